@@ -1,0 +1,154 @@
+"""Seeded synthetic workloads for the sparse MoE layer.
+
+This module only draws and stores inputs; it holds none of the layer's arithmetic. The tests
+feed the same arrays to the CPU oracle and to the HIP library, and the benchmark uses the same
+shapes. numpy and the standard library only (no torch), so it imports anywhere.
+
+Shapes and value distributions follow the five workloads the layer is measured on: the
+decode and speculative-verify rounds of T = batch x (draft + 1) tokens described on the page
+"feat(windows): integrate upstream Qwen3.8 DFlash2 support - #8" (T=4 at batch 1, T=32 at
+batch 8, both with three draft tokens; a prefill chunk of 8192 tokens), with Qwen-family MoE
+sizes: hidden 2048, 256 experts, top-8, expert and shared-expert intermediate 512.
+
+Recipe (all draws from ``numpy.random.default_rng(seed)``, PCG64, ``standard_normal`` in
+float32):
+  1. router weight [E+1][H] (row E is the shared-expert gate row), scaled by 1/sqrt(H);
+  2. only when the workload has a router bias: bias[E] scaled by sqrt(2) (variance 2); the
+     gate row's bias is 0;
+  3. for e = 0..E-1 in order: gate [I][H] and up [I][H] scaled by 1/sqrt(H), then down [H][I]
+     scaled by 1/sqrt(I);
+  4. shared expert: gate [Is][H], up [Is][H] (1/sqrt(H)), down [H][Is] (1/sqrt(Is));
+  5. x [T][H], unscaled N(0, 1).
+bf16 workloads round every draw to bf16 with round-to-nearest-even and store the raw bits as
+uint16. gate and up are stored stacked as gate_up [E][2I][H] (gate rows first); down is
+[E][H][I] (the nn.Linear convention: output rows, input columns contiguous).
+
+Tie tokens: selected tokens have every router score replaced by the nearest multiple of 0.25
+(ties to even), which forces equal logits across experts; those tokens are routed from the given
+logits rather than from x.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    tokens: int
+    hidden: int
+    num_experts: int
+    top_k: int
+    inter: int
+    shared_inter: int
+    dtype: str            # "f32" or "bf16": storage type of x and of every weight
+    bias_std: float = 0.0  # > 0: per-expert router bias ~ N(0, bias_std^2)
+    tie_every: int = 0     # > 0: tokens t with t % tie_every == 0 get tie-quantized logits
+    seed: int = 0
+
+
+WORKLOADS = (
+    Workload("tiny_fp32_t4", 4, 64, 16, 8, 32, 32, "f32", tie_every=2, seed=0),
+    Workload("decode_b1_t4", 4, 2048, 256, 8, 512, 512, "bf16", seed=1),
+    Workload("decode_b8_t32", 32, 2048, 256, 8, 512, 512, "bf16", seed=2),
+    Workload("verify_skewed_t192", 192, 2048, 256, 8, 512, 512, "bf16", bias_std=2.0 ** 0.5,
+             seed=3),
+    Workload("prefill_t8192", 8192, 2048, 256, 8, 512, 512, "bf16", tie_every=10, seed=4),
+)
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return the raw uint16 bits."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounded = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of raw bf16 bits to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _draw(rng, shape, scale, dtype):
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        v *= np.float32(scale)
+    return f32_to_bf16_bits(v) if dtype == "bf16" else v
+
+
+def make_layer(w: Workload, tokens: int | None = None, seed: int | None = None) -> dict:
+    """Draw one layer (weights + x) following the recipe above.
+
+    ``tokens`` overrides T (the weights do not depend on T; x is drawn last).
+    """
+    T = w.tokens if tokens is None else tokens
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    H, E, I, Is = w.hidden, w.num_experts, w.inter, w.shared_inter
+    R = E + (1 if Is > 0 else 0)
+    st = np.uint16 if w.dtype == "bf16" else np.float32
+    layer = {"workload": w, "num_experts": E, "inter": I, "shared_inter": Is, "top_k": w.top_k,
+             "dtype": w.dtype}
+    layer["router_w"] = _draw(rng, (R, H), H ** -0.5, w.dtype)
+    if w.bias_std > 0:
+        b = np.zeros((R,), dtype=np.float32)
+        b[:E] = rng.standard_normal((E,), dtype=np.float32) * np.float32(w.bias_std)
+        layer["router_bias"] = b
+    else:
+        layer["router_bias"] = None
+    gate_up = np.empty((E, 2 * I, H), dtype=st)
+    down = np.empty((E, H, I), dtype=st)
+    for e in range(E):
+        gate_up[e, :I] = _draw(rng, (I, H), H ** -0.5, w.dtype)
+        gate_up[e, I:] = _draw(rng, (I, H), H ** -0.5, w.dtype)
+        down[e] = _draw(rng, (H, I), I ** -0.5, w.dtype)
+    layer["gate_up"] = gate_up
+    layer["down"] = down
+    if Is > 0:
+        sgu = np.empty((2 * Is, H), dtype=st)
+        sgu[:Is] = _draw(rng, (Is, H), H ** -0.5, w.dtype)
+        sgu[Is:] = _draw(rng, (Is, H), H ** -0.5, w.dtype)
+        layer["shared_gate_up"] = sgu
+        layer["shared_down"] = _draw(rng, (H, Is), Is ** -0.5, w.dtype)
+    else:
+        layer["shared_gate_up"] = None
+        layer["shared_down"] = None
+    layer["x"] = _draw(rng, (T, H), 1.0, w.dtype)
+    return layer
+
+
+def draw_x(w: Workload, tokens: int, seed: int) -> np.ndarray:
+    """A fresh activation batch [tokens][H] of the workload's storage type."""
+    rng = np.random.default_rng(seed)
+    return _draw(rng, (tokens, w.hidden), 1.0, w.dtype)
+
+
+def tie_tokens(w: Workload, tokens: int | None = None) -> np.ndarray:
+    """Indices of the tokens whose logits are tie-quantized."""
+    T = w.tokens if tokens is None else tokens
+    if w.tie_every <= 0:
+        return np.zeros((0,), dtype=np.int64)
+    return np.arange(0, T, w.tie_every, dtype=np.int64)
+
+
+def tie_quantize(z: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """Copy of z with the given rows rounded to multiples of 0.25 (ties to even)."""
+    q = np.array(z, dtype=np.float32, copy=True)
+    if len(rows):
+        q[rows] = np.round(q[rows] * np.float32(4.0)) / np.float32(4.0)
+    return q
+
+
+def sample_tokens(T: int, n: int, seed: int = 1234, must=()) -> np.ndarray:
+    """A sorted, seeded sample of min(n, T) distinct token indices including the first and last
+    tokens and any indices in ``must``."""
+    if T <= n:
+        return np.arange(T, dtype=np.int32)
+    rng = np.random.default_rng(seed)
+    pick = set(int(t) for t in must if 0 <= t < T)
+    pick.update((0, T - 1))
+    rest = rng.choice(T, size=max(0, n - len(pick)), replace=False)
+    pick.update(int(t) for t in rest)
+    return np.array(sorted(pick)[:max(n, len(pick))], dtype=np.int32)

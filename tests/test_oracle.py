@@ -1,0 +1,349 @@
+"""Pins for the CPU oracle (no GPU): each check compares the oracle with something other than
+itself - a library sort, closed forms, integer-exact arithmetic, a numpy/scipy SwiGLU, stable
+argsort - and the planted-mistake builds show that every pin rejects a plausible error.
+
+The layer follows the small-T MoE router commit message on the page "feat(windows): integrate
+upstream Qwen3.8 DFlash2 support - #8": top-8 under the order (larger logit first, the lower
+expert id on equal logits), softmax over the eight selected logits, a sigmoid shared-expert gate,
+and a double-precision CPU reference checked at T = 1, 2, 19, 20, 46, 47, 768 and 4097.
+"""
+import math
+import os
+import tempfile
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle as oracle_mod
+from sparse_moe_routing_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- helpers
+def library_order(z_row: np.ndarray, E: int) -> np.ndarray:
+    """Full order of experts by numpy's lexsort: primary key -z ascending (NaN sorts last),
+    secondary key the id ascending. -0.0 and +0.0 compare equal in numpy's sort."""
+    v = z_row[:E].astype(np.float64)
+    return np.lexsort((np.arange(E), -v))
+
+
+def tuple_sort_order(z_row, E):
+    """A second brute force: Python's stable sort over (is_nan, -value, id) tuples."""
+    keys = []
+    for e in range(E):
+        v = float(z_row[e])
+        keys.append((math.isnan(v), 0.0 if math.isnan(v) else -v, e))
+    return [k[2] for k in sorted(keys)]
+
+
+def numpy_swiglu(x64, gu, dn, I):
+    """Independent SwiGLU: np.matmul and scipy's logistic function."""
+    a = x64 @ gu[:I].T
+    u = x64 @ gu[I:].T
+    h = a * scipy.special.expit(a) * u
+    return h @ dn.T
+
+
+def widen(a):
+    if a.dtype == np.uint16:
+        return inputs.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def tiny_layer(rng, T=3, H=16, E=8, I=8, Is=8, dtype="f32"):
+    st = np.uint16 if dtype == "bf16" else np.float32
+
+    def d(shape, s):
+        v = (rng.standard_normal(shape) * s).astype(np.float32)
+        return inputs.f32_to_bf16_bits(v) if dtype == "bf16" else v.astype(st)
+
+    R = E + (1 if Is else 0)
+    layer = {"num_experts": E, "inter": I, "shared_inter": Is, "top_k": 8, "dtype": dtype,
+             "router_w": d((R, H), H ** -0.5), "router_bias": None,
+             "gate_up": d((E, 2 * I, H), H ** -0.5), "down": d((E, H, I), I ** -0.5),
+             "x": d((T, H), 1.0)}
+    if Is:
+        layer["shared_gate_up"] = d((2 * Is, H), H ** -0.5)
+        layer["shared_down"] = d((H, Is), Is ** -0.5)
+    else:
+        layer["shared_gate_up"] = layer["shared_down"] = None
+    return layer
+
+
+def tie_heavy_logits(rng, T, E, gate=True):
+    grid = np.array([-1.0, -0.75, -0.5, -0.25, -0.0, 0.0, 0.25, 0.5, 0.75, 1.0], np.float32)
+    z = grid[rng.integers(0, len(grid), size=(T, E + (1 if gate else 0)))]
+    return z.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- pins
+def pin_select_vs_library_sort(orc):
+    rng = np.random.default_rng(11)
+    for E in (8, 9, 16, 64, 256):
+        for kind in ("normal", "ties", "special"):
+            T = 40
+            if kind == "normal":
+                z = rng.standard_normal((T, E + 1)).astype(np.float32)
+            elif kind == "ties":
+                z = tie_heavy_logits(rng, T, E)
+            else:
+                z = tie_heavy_logits(rng, T, E)
+                specials = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0], np.float32)
+                mask = rng.random((T, E + 1)) < 0.15
+                z[mask] = specials[rng.integers(0, len(specials), size=mask.sum())]
+            ids, w, g = orc.select(z, E, True)
+            for t in range(T):
+                lib = library_order(z[t], E)[:8]
+                tup = tuple_sort_order(z[t], E)[:8]
+                assert list(ids[t]) == list(lib), (E, kind, t, z[t], ids[t], lib)
+                assert list(ids[t]) == tup
+
+
+def pin_select_special_cases(orc):
+    E = 256
+    # all-equal logits: ids 0..7, weights exactly 1/8
+    z = np.full((2, E + 1), 0.3, np.float32)
+    z[1] = -0.0
+    ids, w, g = orc.select(z, E, True)
+    assert (ids == np.arange(8)).all()
+    assert (w == 0.125).all()
+    # distinct ascending logits, then a known permutation of the experts
+    base = np.arange(E, dtype=np.float32) / 16.0
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(E)
+    z = np.zeros((2, E + 1), np.float32)
+    z[0, :E] = base
+    z[1, perm] = base  # expert perm[e] carries value base[e]
+    ids, w, g = orc.select(z, E, True)
+    want0 = np.arange(E - 1, E - 9, -1)
+    assert (ids[0] == want0).all()
+    assert (ids[1] == perm[want0]).all()
+    assert np.array_equal(w[0], w[1])
+
+
+def pin_weights_closed_form(orc):
+    E = 16
+    for L in (0.0, 0.5, 1.0, 3.0, -2.0):
+        z = np.full((1, E + 1), -10.0, np.float32)
+        z[0, 5] = L
+        z[0, [1, 2, 3, 7, 9, 11, 13]] = 0.0
+        ids, w, g = orc.select(z, E, True)
+        if L > 0:
+            assert ids[0, 0] == 5 and list(ids[0, 1:]) == [1, 2, 3, 7, 9, 11, 13]
+            assert abs(w[0, 0] - math.exp(L) / (math.exp(L) + 7)) < 1e-12
+            for k in range(1, 8):
+                assert abs(w[0, k] - 1 / (math.exp(L) + 7)) < 1e-12
+        assert abs(w[0].sum() - 1.0) < 1e-12
+        assert (np.diff(w[0]) <= 1e-15).all()
+    rng = np.random.default_rng(7)
+    z = (rng.standard_normal((64, 257)) * 3).astype(np.float32)
+    ids, w, g = orc.select(z, 256, True)
+    assert np.abs(w.sum(1) - 1).max() < 1e-12
+    assert (np.diff(w, axis=1) <= 1e-15).all()
+    # reference softmax via scipy over the selected logits
+    sel = np.take_along_axis(z[:, :256].astype(np.float64), ids, axis=1)
+    assert np.abs(w - scipy.special.softmax(sel, axis=1)).max() < 1e-14
+    # equivalently: the full softmax over all 256 experts renormalised to the selected eight
+    full = scipy.special.softmax(z[:, :256].astype(np.float64), axis=1)
+    fsel = np.take_along_axis(full, ids, axis=1)
+    assert np.abs(w - fsel / fsel.sum(1, keepdims=True)).max() < 1e-12
+
+
+def pin_gate(orc):
+    E = 16
+    z = np.zeros((4, E + 1), np.float32)
+    z[:, E] = [0.0, np.inf, -np.inf, 2.0]
+    _, _, g = orc.select(z, E, True)
+    assert g[0] == 0.5 and g[1] == 1.0 and g[2] == 0.0
+    assert abs(g[3] - scipy.special.expit(2.0)) < 1e-15
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((32, E + 1)).astype(np.float32)
+    _, _, g = orc.select(z, E, True)
+    assert np.abs(g - scipy.special.expit(z[:, E].astype(np.float64))).max() < 1e-15
+
+
+def pin_logits_integer_exact(orc):
+    rng = np.random.default_rng(9)
+    for dtype in ("f32", "bf16"):
+        T, H, R = 7, 96, 17
+        xi = rng.integers(-8, 9, size=(T, H))
+        wi = rng.integers(-8, 9, size=(R, H))
+        bi = rng.integers(-64, 65, size=(R,))
+        scale_w, scale_b = 2.0 ** -6, 2.0 ** -6
+        xf = xi.astype(np.float32)
+        wf = (wi * scale_w).astype(np.float32)
+        bf = (bi * scale_b).astype(np.float32)
+        if dtype == "bf16":
+            xf, wf = inputs.f32_to_bf16_bits(xf), inputs.f32_to_bf16_bits(wf)
+        z = orc.logits(xf, wf, bf)
+        exact = (xi @ wi.T + bi[None, :]).astype(np.float64) * scale_w  # integers times 2^-6
+        assert np.array_equal(z.astype(np.float64), exact), dtype
+
+
+def pin_logits_random_vs_matmul(orc):
+    rng = np.random.default_rng(10)
+    layer = tiny_layer(rng, T=9, H=64, E=16, I=8, Is=8, dtype="bf16")
+    b = rng.standard_normal(17).astype(np.float32)
+    z = orc.logits(layer["x"], layer["router_w"], b)
+    ref = widen(layer["x"]) @ widen(layer["router_w"]).T + b.astype(np.float64)
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert (np.abs(z - ref) <= ulp).all()
+
+
+def pin_bucket_vs_argsort(orc):
+    rng = np.random.default_rng(12)
+    for T, E in ((1, 16), (5, 16), (47, 256), (300, 256)):
+        ids = np.stack([rng.permutation(E)[:8] for _ in range(T)]).astype(np.int32)
+        counts, offsets, perm = orc.bucket(ids, E)
+        flat = ids.ravel()
+        assert np.array_equal(counts, np.bincount(flat, minlength=E))
+        assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+        assert np.array_equal(perm, np.argsort(flat, kind="stable"))
+
+
+def pin_ffn_dense_equivalence(orc):
+    """E = 8 identical experts: all eight are selected, the weights sum to 1, so the routed part
+    equals one plain SwiGLU; with the shared expert the gate scales a second plain SwiGLU."""
+    rng = np.random.default_rng(13)
+    for dtype in ("f32", "bf16"):
+        layer = tiny_layer(rng, T=5, H=32, E=8, I=12, Is=10, dtype=dtype)
+        layer["gate_up"][:] = layer["gate_up"][0]
+        layer["down"][:] = layer["down"][0]
+        z, ids, w, g = orc.route(layer)
+        assert sorted(ids[0]) == list(range(8))
+        y = orc.forward(layer, ids, w, g)
+        x64 = widen(layer["x"])
+        routed = numpy_swiglu(x64, widen(layer["gate_up"][0]), widen(layer["down"][0]), 12)
+        shared = numpy_swiglu(x64, widen(layer["shared_gate_up"]), widen(layer["shared_down"]), 10)
+        ref = routed + g[:, None] * shared
+        assert np.abs(y - ref).max() < 1e-12 * max(1.0, np.abs(ref).max()), dtype
+
+
+def pin_ffn_shared_alone_and_zero(orc):
+    rng = np.random.default_rng(14)
+    layer = tiny_layer(rng, T=4, H=32, E=16, I=8, Is=8, dtype="f32")
+    layer["down"][:] = 0.0
+    layer["router_w"][16] = 0.0  # gate logit 0 -> g = 1/2
+    z, ids, w, g = orc.route(layer)
+    assert (g == 0.5).all()
+    y = orc.forward(layer, ids, w, g)
+    x64 = widen(layer["x"])
+    ref = 0.5 * numpy_swiglu(x64, widen(layer["shared_gate_up"]), widen(layer["shared_down"]), 8)
+    assert np.abs(y - ref).max() < 1e-12
+    layer["x"][:] = 0.0
+    z, ids, w, g = orc.route(layer)
+    y = orc.forward(layer, ids, w, g)
+    assert (y == 0.0).all()
+
+
+def pin_ffn_routed_mixture(orc):
+    """Distinct experts: y = sum_k w_k SwiGLU_{id_k}(x) + g SwiGLU_s(x) with numpy SwiGLUs."""
+    rng = np.random.default_rng(15)
+    for dtype in ("f32", "bf16"):
+        layer = tiny_layer(rng, T=6, H=24, E=16, I=8, Is=4, dtype=dtype)
+        z, ids, w, g = orc.route(layer)
+        y = orc.forward(layer, ids, w, g, tokens=np.array([5, 0, 3], np.int32))
+        x64 = widen(layer["x"])
+        for j, t in enumerate((5, 0, 3)):
+            ref = np.zeros(24)
+            for k in range(8):
+                e = ids[t, k]
+                ref += w[t, k] * numpy_swiglu(x64[t:t + 1], widen(layer["gate_up"][e]),
+                                              widen(layer["down"][e]), 8)[0]
+            ref += g[t] * numpy_swiglu(x64[t:t + 1], widen(layer["shared_gate_up"]),
+                                       widen(layer["shared_down"]), 4)[0]
+            assert np.abs(y[j] - ref).max() < 1e-12, (dtype, t)
+
+
+def pin_golden_hand_example(orc):
+    path = os.path.join(GOLDEN, "select_hand.txt")
+    rec = {}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, val = line.split(":", 1)
+        rec[key.strip()] = val.strip()
+    z1 = np.array([float(v) for v in rec["logits"].split()], np.float32)
+    z2 = np.array([float(v) for v in rec["logits2"].split()], np.float32)
+    ids, w, g = orc.select(np.stack([z1, z2]), 16, True)
+    assert list(ids[0]) == [int(v) for v in rec["ids"].split()]
+    assert list(ids[1]) == [int(v) for v in rec["ids2"].split()]
+    env = {"exp": math.exp}
+    S = eval(rec["S_expr"], env)
+    env["S"] = S
+    want = [eval(e.strip(), env) for e in rec["w2_exprs"].split(";")]
+    assert np.abs(w[1] - np.array(want)).max() < 1e-12
+    assert abs(g[1] - float(rec["g2_approx"])) < 1e-7
+
+
+PINS = [pin_select_vs_library_sort, pin_select_special_cases, pin_weights_closed_form, pin_gate,
+        pin_logits_integer_exact, pin_logits_random_vs_matmul, pin_bucket_vs_argsort,
+        pin_ffn_dense_equivalence, pin_ffn_shared_alone_and_zero, pin_ffn_routed_mixture,
+        pin_golden_hand_example]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(oracle, pin):
+    pin(oracle)
+
+
+def test_oracle_p2_token_counts(oracle):
+    """The token counts at which the pages' double-precision reference checks the op; the oracle's
+    selection must agree with the library sort at each of them (E = 256, ties included)."""
+    rng = np.random.default_rng(21)
+    for T in (1, 2, 19, 20, 46, 47, 768, 4097):
+        z = tie_heavy_logits(rng, T, 256) if T % 2 else rng.standard_normal((T, 257)).astype(np.float32)
+        ids, w, g = oracle.select(z, 256, True)
+        check = sorted(set([0, T - 1]) | set(rng.integers(0, T, size=min(T, 16)).tolist()))
+        for t in check:
+            assert list(ids[t]) == list(library_order(z[t], 256)[:8])
+        assert np.abs(w.sum(1) - 1).max() < 1e-12
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+PLANTS = {
+    "ORACLE_PLANT_TIE_HIGH_ID": [pin_select_vs_library_sort, pin_select_special_cases,
+                                 pin_golden_hand_example],
+    "ORACLE_PLANT_SHIFT_ID8": [pin_select_vs_library_sort, pin_select_special_cases,
+                               pin_golden_hand_example],
+    "ORACLE_PLANT_SWAP_W67": [pin_weights_closed_form, pin_golden_hand_example],
+    "ORACLE_PLANT_SWAP_GATE_UP": [pin_ffn_dense_equivalence, pin_ffn_routed_mixture],
+    "ORACLE_PLANT_DROP_BIAS": [pin_logits_integer_exact, pin_logits_random_vs_matmul],
+}
+
+
+@pytest.fixture(scope="module")
+def plant_dir():
+    with tempfile.TemporaryDirectory() as d:
+        yield d
+
+
+@pytest.mark.parametrize("plant", sorted(PLANTS))
+def test_planted_mistake_is_caught(plant, plant_dir):
+    path = os.path.join(plant_dir, f"lib_{plant}.so")
+    oracle_mod.build(path, defines=(plant,))
+    bad = oracle_mod.Oracle(oracle_mod.load(path))
+    for pin in PLANTS[plant]:
+        with pytest.raises(AssertionError):
+            pin(bad)
+
+
+def test_workload_recipe_shapes():
+    w = inputs.BY_NAME["tiny_fp32_t4"]
+    layer = inputs.make_layer(w)
+    assert layer["router_w"].shape == (17, 64) and layer["router_w"].dtype == np.float32
+    assert layer["gate_up"].shape == (16, 64, 64)
+    assert layer["down"].shape == (16, 64, 32)
+    assert layer["x"].shape == (4, 64)
+    again = inputs.make_layer(w)
+    assert np.array_equal(layer["gate_up"], again["gate_up"])
+    assert list(inputs.tie_tokens(w)) == [0, 2]
+    # bf16 rounding: nearest-even on a few exact cases
+    v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 0.0], np.float32)
+    back = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(v))
+    assert list(back) == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 0.0]
+    q = inputs.tie_quantize(np.array([[0.1, -0.1, 0.375, 0.125, 1.3]], np.float32), np.array([0]))
+    assert list(q[0]) == [0.0, 0.0, 0.5, 0.0, 1.25] and np.signbit(q[0, 1])
