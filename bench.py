@@ -1,0 +1,243 @@
+"""Benchmark of the sparse MoE layer on one MI355X: tokens/s of the whole hot path.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_b1_t4]
+
+A step is one moe_forward over one batch of T synthetic tokens: router logits, top-8 selection
+with softmax and shared gate, bucketing, the expert gate/up/down stage and the weighted combine.
+Inputs are resident in HBM before the timed region. To time cold weights (the 256 MB Infinity
+Cache would hold a whole T=4 working set), each step uses the next of several independent weight
+sets and the next activation batch of a pool, so consecutive steps share no expert bytes.
+
+Printed: one JSON line with the metric, the dominant kernel's roofline (algorithmic bytes per
+launch over its event-timed average duration) and the oracle's CPU throughput on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="decode_b1_t4")
+    ap.add_argument("--sets", type=int, default=6, help="independent weight sets (cold cache)")
+    ap.add_argument("--pool", type=int, default=16, help="activation batches in the pool")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def make_sets(w, n_sets, torch):
+    """Weight sets drawn on the GPU with the workload's shapes and scales (bench only)."""
+    from sparse_moe_routing_amd import binding
+    H, E, I, Is = w.hidden, w.num_experts, w.inter, w.shared_inter
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda")
+    layers = []
+    for s in range(n_sets):
+        gen.manual_seed(10_000 + s)
+
+        def draw(shape, scale):
+            return (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+                    * scale).to(dt)
+
+        t = {"router_w": draw((E + 1, H), H ** -0.5), "router_bias": None,
+             "gate_up": draw((E, 2 * I, H), H ** -0.5), "down": draw((E, H, I), I ** -0.5),
+             "shared_gate_up": draw((2 * Is, H), H ** -0.5),
+             "shared_down": draw((H, Is), Is ** -0.5)}
+        if w.bias_std > 0:
+            b = torch.zeros(E + 1, device="cuda")
+            b[:E] = torch.randn(E, generator=gen, device="cuda") * w.bias_std
+            t["router_bias"] = b
+        m = binding.MoeLayer(H, E, I, Is, w.tokens, w.dtype, t)
+        layers.append((m, t))
+    return layers
+
+
+def step_bytes(w, U):
+    """Algorithmic HBM bytes of one step: router, shared expert, the U distinct routed experts
+    touched (each read once), x in and y out."""
+    esz = 2 if w.dtype == "bf16" else 4
+    H, I, Is, E, T = w.hidden, w.inter, w.shared_inter, w.num_experts, w.tokens
+    return (esz * (E + 1) * H + 3 * esz * H * Is + U * 3 * esz * H * I + esz * T * H + 4 * T * H)
+
+
+def expert_bytes(w, U):
+    """Algorithmic bytes of one expert-kernel launch: the touched expert weights (routed and
+    shared) and the x rows it stages."""
+    esz = 2 if w.dtype == "bf16" else 4
+    H, I, Is, T = w.hidden, w.inter, w.shared_inter, w.tokens
+    return 3 * esz * H * Is + U * 3 * esz * H * I + esz * T * H
+
+
+def cpu_baseline(w, m_t, seconds):
+    """The oracle (untuned) on the host: route + forward of whole T-token batches until about
+    `seconds` of CPU time have been spent."""
+    import oracle as oracle_mod
+    import torch
+    orc = oracle_mod.default()
+    t = m_t
+
+    def host(a):
+        if a is None:
+            return None
+        if a.dtype == torch.bfloat16:
+            return a.view(torch.int16).cpu().numpy().view(np.uint16)
+        return a.cpu().numpy()
+
+    layer = {"num_experts": w.num_experts, "inter": w.inter, "shared_inter": w.shared_inter,
+             "router_w": host(t["router_w"]), "router_bias": host(t["router_bias"]),
+             "gate_up": host(t["gate_up"]), "down": host(t["down"]),
+             "shared_gate_up": host(t["shared_gate_up"]), "shared_down": host(t["shared_down"])}
+    from sparse_moe_routing_amd import inputs
+    T = min(w.tokens, 64)
+    tokens = 0
+    rounds = 0
+    t0 = time.perf_counter()
+    while True:
+        layer["x"] = inputs.draw_x(w, T, seed=900 + rounds)
+        z = orc.logits(layer["x"], layer["router_w"], layer["router_bias"])
+        ids, wt, g = orc.select(z, w.num_experts, w.shared_inter > 0)
+        orc.forward(layer, ids, wt, g)
+        tokens += T
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    # the oracle parallelises over tokens, so a batch of T tokens keeps at most T threads busy
+    cores = min(T, orc.num_threads())
+    return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rounds} batches of {T} tokens of the {w.name} shapes (fresh x per batch), "
+                      f"fp64 route+forward, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer has no "
+              "multi-GPU path in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_moe_routing_amd import binding, inputs
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    w = inputs.BY_NAME[args.workload]
+    T, H = w.tokens, w.hidden
+    log(f"[bench] workload {w.name}: T={T} H={H} E={w.num_experts} I={w.inter} Is={w.shared_inter}"
+        f" dtype={w.dtype}; {args.sets} weight sets, pool {args.pool}")
+    sets = make_sets(w, args.sets, torch)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    pool = [torch.randn((T, H), generator=gen, device="cuda").to(dt) for _ in range(args.pool)]
+    m0 = sets[0][0]
+    ws = m0.workspace(T)
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    plan = m0.plan(T)
+    n_ev = len(plan) + 1
+    n_pairs = len(sets) * len(pool)
+    # distinct experts per (set, batch) pair, from the library's own routing (outside timing)
+    U = {}
+    for si, (m, _) in enumerate(sets):
+        for pi, x in enumerate(pool):
+            _, ids, _, _ = m.route(x=x, want_logits=False)
+            U[(si, pi)] = int(torch.unique(ids).numel())
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def combo(i):
+        return i % len(sets), (i // len(sets) + i) % len(pool)
+
+    log(f"[bench] plan {plan}; warmup {args.warmup}")
+    for i in range(args.warmup):
+        si, pi = combo(i)
+        sets[si][0].forward(pool[pi], y=y, ws=ws)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel events recorded on the launch stream
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+              for _ in range(args.steps)]
+    used = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        si, pi = combo(args.warmup + i)
+        used.append((si, pi))
+        sets[si][0].forward(pool[pi], y=y, ws=ws, events=events[i], stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = args.steps * T / elapsed
+    per_kernel = {name: [] for name in plan}
+    step_ms = []
+    for ev in events:
+        for k, name in enumerate(plan):
+            per_kernel[name].append(ev[k].elapsed_time(ev[k + 1]))
+        step_ms.append(ev[0].elapsed_time(ev[-1]))
+    mean_U = float(np.mean([U[c] for c in used]))
+    exp_us = float(np.mean(per_kernel["expert"])) * 1e3
+    exp_bytes = float(np.mean([expert_bytes(w, U[c]) for c in used]))
+    achieved = exp_bytes / (exp_us * 1e-6) / 1e9
+    step_b = float(np.mean([step_bytes(w, U[c]) for c in used]))
+    gpu_step_us = float(np.median(step_ms)) * 1e3
+    log("[bench] per-kernel mean us: " + ", ".join(
+        f"{k}={np.mean(v) * 1e3:.2f}" for k, v in per_kernel.items()))
+    log(f"[bench] wall {ms_per_step * 1e3:.2f} us/step, event-timed step median {gpu_step_us:.2f} us,"
+        f" mean U {mean_U:.1f}, step bytes {step_b / 1e6:.1f} MB -> "
+        f"{step_b / (ms_per_step * 1e-3) / 1e9:.0f} GB/s wall")
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done (3 launches)")
+    result = {
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s (% of peak) at T=4, 32, 192",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": w.num_experts,
+                   "top_k": 8, "inter": w.inter, "shared_inter": w.shared_inter,
+                   "weight_sets": len(sets), "x_pool": len(pool)},
+        "hbm_gbs_step": step_b / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_step": step_b / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "mean_distinct_experts": mean_U,
+        "per_kernel_us": {k: float(np.mean(v)) * 1e3 for k, v in per_kernel.items()},
+        "roofline": {"kernel": "expert", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(w, sets[0][1], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

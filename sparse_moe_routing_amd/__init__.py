@@ -2,16 +2,9 @@
 softmax over the selected eight, sigmoid-gated shared expert, SwiGLU experts and the weighted
 combine, behind the C-ABI library ``libmoe.so`` (header ``include/moe.h``).
 
-``inputs`` (seeded synthetic workloads) imports without the library; the binding loads
-``libmoe.so`` on first use and raises if it is missing.
+``inputs`` (seeded synthetic workloads) needs only numpy; ``binding`` loads ``libmoe.so`` on
+first use and raises if it has not been built.
 """
-from . import inputs  # noqa: F401
+from . import binding, inputs  # noqa: F401
 
-__all__ = ["inputs", "binding"]
-
-
-def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
-    raise AttributeError(name)
+__all__ = ["binding", "inputs"]

@@ -1,0 +1,84 @@
+// kernels.h - parameter blocks and host-side launchers of the libmoe kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router partial logits: zpart[ks][t][r] = sum over the ks-th K range of W[r][h] * x[t][h].
+struct RouterParams {
+    const void *x;       // [T][H]
+    const void *w;       // [R][H]
+    float *zpart;        // [KS][T][R]
+    int T, H, R;
+    int KS;              // K split: H / KS is a multiple of the op's k step
+    int n_tt;            // token tiles of 16
+    int n_rg;            // row-tile groups (each covers up to MAXRT row tiles of 16)
+};
+
+// Fold of the router partials + top-8 + softmax + gate (one wave per token).
+struct SelectParams {
+    const float *zpart;  // [KS][T][R] (KS = 1 for given logits)
+    const float *bias;   // [R] or nullptr
+    float *logits_out;   // [T][R] or nullptr
+    int32_t *ids;        // [T][8]
+    float *w;            // [T][8]
+    float *g;            // [T] or nullptr when there is no gate row
+    int T, E, R, KS;
+};
+
+// Dispatch tables written by the bucketing pass.
+struct BucketParams {
+    int T, E;
+    int NG;              // tokens per expert group (rows of the expert kernel's x tile)
+    int has_shared;      // shared-expert groups come first in the group table
+    int chunk_tokens;    // tokens per chunk of the multi-block path (64)
+    int n_chunks;
+    const int32_t *ids_in;  // [T][8] when the selection is not run in the same kernel
+    int32_t *counts;     // [E]
+    int32_t *offsets;    // [E+1]
+    int32_t *perm;       // [T*8]
+    int32_t *hist;       // [n_chunks][E] (multi-block path); becomes per-chunk bases
+    int4 *groups;        // [max_groups]: {expert (E = shared), start, n, 0}
+    int32_t *num_groups; // [1]
+};
+
+// Expert stage: gate/up + SwiGLU + down for (group, slice chunk) units.
+struct ExpertParams {
+    const void *x;
+    const void *gate_up, *down, *sgu, *sdn;
+    const int32_t *perm;
+    const int4 *groups;
+    const int32_t *num_groups;
+    float *ypart;        // [n_sc][slots][H]
+    int T, H, E, I, Is;
+    int s;               // slice width of I per wave group (16 * gate/up waves)
+    int S;               // slices of max(I, Is)
+    int SPU;             // slices per unit (S % SPU == 0); n_sc = S / SPU
+    int NG;              // x-tile rows
+    int slots;           // T*8 (+ T with a shared expert)
+    int x_stride;        // LDS row stride of the x tile in elements
+};
+
+struct CombineParams {
+    const float *ypart;  // [n_sc][slots][H]
+    const float *w;      // [T][8]
+    const float *g;      // [T] or nullptr
+    float *y;            // [T][H]
+    int T, H, slots, n_sc_routed, n_sc_shared, has_shared;
+};
+
+hipError_t launch_router(const RouterParams &p, int dtype, int maxrt, hipStream_t s);
+hipError_t launch_route_small(const SelectParams &sp, const BucketParams &bp, bool do_select,
+                              bool do_bucket, hipStream_t s);
+hipError_t launch_select_hist(const SelectParams &sp, const BucketParams &bp, bool do_select,
+                              bool do_hist, hipStream_t s);
+hipError_t launch_bucket_scan(const BucketParams &bp, hipStream_t s);
+hipError_t launch_bucket_scatter(const BucketParams &bp, hipStream_t s);
+hipError_t launch_expert(const ExpertParams &p, int dtype, int grid, size_t lds_bytes,
+                         hipStream_t s);
+hipError_t prepare_expert_kernels(size_t max_lds_bytes);
+hipError_t launch_combine(const CombineParams &p, hipStream_t s);
+
+}  // namespace moe

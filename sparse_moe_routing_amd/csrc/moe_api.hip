@@ -1,0 +1,475 @@
+// moe_api.hip - the C ABI of libmoe (include/moe.h): validation, workspace layout, kernel plans.
+//
+// Call sequence of moe_forward (all on the caller's stream, no host synchronisation):
+//   router        partial logits (matrix cores), K split at decode sizes
+//   route_small   T <= 64: fold + top-8 + softmax + gate, then the whole bucketing pass, one block
+//   select_hist   T > 64: per 64-token chunk, fold + top-8 + softmax + gate + expert histogram
+//   bucket_scan   T > 64: per-expert chunk bases, counts, offsets, expert-group table
+//   bucket_scatter T > 64: the stable scatter of pair indices
+//   expert        gate/up + SwiGLU + down per (expert group, intermediate slice chunk)
+//   combine       weighted sum of the routed partials plus the gated shared partials
+#include <string.h>
+
+#include <new>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+struct moe_ctx {
+    moe_config cfg;
+    moe_weights w;
+    int R;         // router rows
+    int device;
+    int num_cus;
+    int s;         // intermediate slice width of the expert kernel
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kMaxXTileBytes = 144 * 1024;  // LDS for the expert kernel's x tile
+constexpr size_t kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
+constexpr int kRouterSplit = 8;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+    int T = 0;
+    bool small = false;
+    int KS = 1, n_tt = 1, n_rg = 1, maxrt = 1;
+    int NG = 16, n_chunks = 0, max_groups = 0;
+    int s = 64, S = 1, SPU = 1, n_sc = 1, n_sc_routed = 1, n_sc_shared = 0, slots = 0;
+    int x_stride = 0, grid = 1;
+    size_t lds = 0;
+    size_t o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
+           o_hist = 0, o_groups = 0, o_ngroups = 0, o_ypart = 0, total = 0;
+};
+
+int k_step(int dtype) { return dtype == MOE_BF16 ? 32 : 16; }
+int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+Plan make_plan(const moe_ctx *c, int T) {
+    Plan p;
+    const moe_config &cfg = c->cfg;
+    const int H = cfg.hidden, E = cfg.num_experts, I = cfg.inter, Is = cfg.shared_inter;
+    p.T = T;
+    p.small = T <= 64;
+    const int n_rt = (c->R + 15) / 16;
+    p.n_tt = (T + 15) / 16;
+    // Router K split: 8 partial sums per logit (fewer only when H has fewer k steps). The split
+    // is the same for every T, so a token's logits do not depend on the batch it comes in.
+    p.KS = 1;
+    {
+        const int ksteps = H / k_step(cfg.dtype);
+        while (p.KS < kRouterSplit && ksteps % (p.KS * 2) == 0) p.KS *= 2;
+    }
+    p.maxrt = T > 256 ? 4 : 1;
+    p.n_rg = (n_rt + p.maxrt - 1) / p.maxrt;
+    // bucketing and expert groups
+    // x-tile rows: up to 16 tokens, fewer when a row of H elements would not leave room in LDS
+    const int esz = elem_bytes(cfg.dtype);
+    p.x_stride = H + 16 / esz;
+    const int ng_lds = (int)(kMaxXTileBytes / ((size_t)p.x_stride * esz));
+    p.NG = T < 16 ? T : 16;
+    if (p.NG > ng_lds) p.NG = ng_lds;
+    p.n_chunks = p.small ? 0 : (T + 63) / 64;
+    const int nsh = Is > 0 ? (T + p.NG - 1) / p.NG : 0;
+    const int pairs = T * 8;
+    p.max_groups = nsh + (pairs < E ? pairs : E) + pairs / p.NG + 1;
+    p.s = c->s;
+    const int Imax = I > Is ? I : Is;
+    p.S = Imax / p.s;
+    // Slices per unit: 1 (many small units) or all of them (one unit per group). Both sum the
+    // per-slice partials of a token in the same order, so y does not depend on the choice.
+    p.SPU = T <= 256 ? 1 : p.S;
+    p.n_sc = p.S / p.SPU;
+    p.n_sc_routed = (I / p.s + p.SPU - 1) / p.SPU;
+    p.n_sc_shared = Is > 0 ? (Is / p.s + p.SPU - 1) / p.SPU : 0;
+    p.slots = pairs + (Is > 0 ? T : 0);
+    p.lds = (size_t)p.NG * p.x_stride * esz + (size_t)16 * (p.s + 4) * 4;
+    const long units = (long)p.max_groups * p.n_sc;
+    const long cap = (long)c->num_cus * 4;
+    p.grid = (int)(units < cap ? units : cap);
+    if (p.grid < 1) p.grid = 1;
+    // workspace
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    p.o_zpart = take((size_t)p.KS * T * c->R * 4);
+    p.o_ids = take((size_t)pairs * 4);
+    p.o_w = take((size_t)pairs * 4);
+    p.o_g = take((size_t)T * 4);
+    p.o_counts = take((size_t)E * 4);
+    p.o_offsets = take((size_t)(E + 1) * 4);
+    p.o_perm = take((size_t)pairs * 4);
+    p.o_hist = take((size_t)p.n_chunks * E * 4);
+    p.o_groups = take((size_t)p.max_groups * 16);
+    p.o_ngroups = take(16);
+    p.o_ypart = take((size_t)p.n_sc * p.slots * H * 4);
+    p.total = o;
+    return p;
+}
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int check_call(const moe_ctx *c, int32_t T, void *ws, size_t ws_bytes, const Plan *plan) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || T > c->cfg.max_tokens) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!ws || !aligned(ws, kAlign) || ws_bytes < plan->total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Kernel sequence of one call; `run` false only lists the names.
+struct Launcher {
+    const moe_ctx *c;
+    hipStream_t stream;
+    hipEvent_t *events;
+    int n_events;
+    bool run;
+    int count = 0;
+    const char **names = nullptr;
+    int max_names = 0;
+    hipError_t err = hipSuccess;
+
+    template <class F>
+    void step(const char *name, F &&launch) {
+        if (names && count < max_names) names[count] = name;
+        if (run && err == hipSuccess) {
+            if (events && count < n_events) err = hipEventRecord(events[count], stream);
+            if (err == hipSuccess) err = launch();
+        }
+        ++count;
+    }
+    void finish() {
+        if (run && err == hipSuccess && events && count < n_events)
+            err = hipEventRecord(events[count], stream);
+    }
+};
+
+SelectParams select_params(const moe_ctx *c, const Plan &p, const float *zpart, int KS,
+                           const float *bias, float *logits_out, int32_t *ids, float *w, float *g) {
+    SelectParams sp{};
+    sp.zpart = zpart;
+    sp.bias = bias;
+    sp.logits_out = logits_out;
+    sp.ids = ids;
+    sp.w = w;
+    sp.g = c->cfg.shared_inter > 0 ? g : nullptr;
+    sp.T = p.T;
+    sp.E = c->cfg.num_experts;
+    sp.R = c->R;
+    sp.KS = KS;
+    return sp;
+}
+
+BucketParams bucket_params(const moe_ctx *c, const Plan &p, char *ws, const int32_t *ids_in,
+                           int32_t *counts, int32_t *offsets, int32_t *perm) {
+    BucketParams bp{};
+    bp.T = p.T;
+    bp.E = c->cfg.num_experts;
+    bp.NG = p.NG;
+    bp.has_shared = c->cfg.shared_inter > 0;
+    bp.chunk_tokens = 64;
+    bp.n_chunks = p.n_chunks;
+    bp.ids_in = ids_in;
+    bp.counts = counts;
+    bp.offsets = offsets;
+    bp.perm = perm;
+    bp.hist = reinterpret_cast<int32_t *>(ws + p.o_hist);
+    bp.groups = reinterpret_cast<int4 *>(ws + p.o_groups);
+    bp.num_groups = reinterpret_cast<int32_t *>(ws + p.o_ngroups);
+    return bp;
+}
+
+void enqueue_router(Launcher &L, const moe_ctx *c, const Plan &p, const void *x, float *zpart) {
+    RouterParams rp{};
+    rp.x = x;
+    rp.w = c->w.router_w;
+    rp.zpart = zpart;
+    rp.T = p.T;
+    rp.H = c->cfg.hidden;
+    rp.R = c->R;
+    rp.KS = p.KS;
+    rp.n_tt = p.n_tt;
+    rp.n_rg = p.n_rg;
+    L.step("router", [&] { return launch_router(rp, c->cfg.dtype, p.maxrt, L.stream); });
+}
+
+// Bucketing from ids already in memory (or selection + bucketing when sp is given).
+void enqueue_dispatch(Launcher &L, const Plan &p, const SelectParams *sp, BucketParams bp) {
+    if (p.small) {
+        SelectParams dummy{};
+        const SelectParams &s = sp ? *sp : dummy;
+        L.step("route_small", [&] { return launch_route_small(s, bp, sp != nullptr, true, L.stream); });
+        return;
+    }
+    {
+        SelectParams dummy{};
+        const SelectParams &s = sp ? *sp : dummy;
+        L.step("select_hist", [&] { return launch_select_hist(s, bp, sp != nullptr, true, L.stream); });
+    }
+    if (sp) bp.ids_in = sp->ids;
+    L.step("bucket_scan", [&] { return launch_bucket_scan(bp, L.stream); });
+    L.step("bucket_scatter", [&] { return launch_bucket_scatter(bp, L.stream); });
+}
+
+int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_in,
+                 const float *w_in, const float *gate_in, float *y, void *workspace,
+                 size_t ws_bytes, hipStream_t stream, hipEvent_t *events, int32_t n_events,
+                 const char **names, int32_t max_names, int32_t *n_kernels, bool run,
+                 int routing_given_flag) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || T > c->cfg.max_tokens) return MOE_ERR_INVALID_ARG;
+    const bool has_shared = c->cfg.shared_inter > 0;
+    const bool given = run ? (ids_in || w_in || gate_in) : routing_given_flag != 0;
+    if (run) {
+        if (T == 0) return MOE_OK;
+        if (!x || !y) return MOE_ERR_INVALID_ARG;
+        if (!aligned(x, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+        if (given && (!ids_in || !w_in || (has_shared && !gate_in))) return MOE_ERR_INVALID_ARG;
+    }
+    if (T == 0) {
+        if (n_kernels) *n_kernels = 0;
+        return MOE_OK;
+    }
+    const Plan p = make_plan(c, T);
+    if (run) {
+        const int st = check_call(c, T, workspace, ws_bytes, &p);
+        if (st != MOE_OK) return st;
+    }
+    char *ws = static_cast<char *>(workspace);
+    Launcher L{c, stream, events, n_events, run};
+    L.names = names;
+    L.max_names = max_names;
+
+    int32_t *ids = reinterpret_cast<int32_t *>(ws + p.o_ids);
+    float *wts = reinterpret_cast<float *>(ws + p.o_w);
+    float *g = reinterpret_cast<float *>(ws + p.o_g);
+    int32_t *counts = reinterpret_cast<int32_t *>(ws + p.o_counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(ws + p.o_offsets);
+    int32_t *perm = reinterpret_cast<int32_t *>(ws + p.o_perm);
+    const int32_t *ids_used = ids;
+    const float *w_used = wts;
+    const float *g_used = g;
+    if (!given) {
+        float *zpart = reinterpret_cast<float *>(ws + p.o_zpart);
+        enqueue_router(L, c, p, x, zpart);
+        const SelectParams sp = select_params(c, p, zpart, p.KS, c->w.router_bias, nullptr, ids,
+                                              wts, g);
+        enqueue_dispatch(L, p, &sp, bucket_params(c, p, ws, nullptr, counts, offsets, perm));
+    } else {
+        ids_used = ids_in;
+        w_used = w_in;
+        g_used = gate_in;
+        enqueue_dispatch(L, p, nullptr, bucket_params(c, p, ws, ids_in, counts, offsets, perm));
+    }
+    ExpertParams ep{};
+    ep.x = x;
+    ep.gate_up = c->w.gate_up;
+    ep.down = c->w.down;
+    ep.sgu = c->w.shared_gate_up;
+    ep.sdn = c->w.shared_down;
+    ep.perm = perm;
+    ep.groups = reinterpret_cast<const int4 *>(ws + p.o_groups);
+    ep.num_groups = reinterpret_cast<const int32_t *>(ws + p.o_ngroups);
+    ep.ypart = reinterpret_cast<float *>(ws + p.o_ypart);
+    ep.T = T;
+    ep.H = c->cfg.hidden;
+    ep.E = c->cfg.num_experts;
+    ep.I = c->cfg.inter;
+    ep.Is = c->cfg.shared_inter;
+    ep.s = p.s;
+    ep.S = p.S;
+    ep.SPU = p.SPU;
+    ep.NG = p.NG;
+    ep.slots = p.slots;
+    ep.x_stride = p.x_stride;
+    L.step("expert", [&] { return launch_expert(ep, c->cfg.dtype, p.grid, p.lds, L.stream); });
+    CombineParams cp{};
+    cp.ypart = ep.ypart;
+    cp.w = w_used;
+    cp.g = has_shared ? g_used : nullptr;
+    cp.y = y;
+    cp.T = T;
+    cp.H = c->cfg.hidden;
+    cp.slots = p.slots;
+    cp.n_sc_routed = p.n_sc_routed;
+    cp.n_sc_shared = p.n_sc_shared;
+    cp.has_shared = has_shared ? 1 : 0;
+    L.step("combine", [&] { return launch_combine(cp, L.stream); });
+    (void)ids_used;
+    L.finish();
+    if (n_kernels) *n_kernels = L.count;
+    return hip_status(L.err);
+}
+
+bool valid_inter(int v, int dtype) {
+    const int m = dtype == MOE_BF16 ? 32 : 16;
+    return v >= m && v <= 4096 && v % m == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(int status) {
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out) {
+    if (!out) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!cfg || !weights) return MOE_ERR_INVALID_ARG;
+    if (cfg->dtype != MOE_F32 && cfg->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (cfg->top_k != 8) return MOE_ERR_UNSUPPORTED;
+    if (cfg->num_experts < 8 || cfg->num_experts > 256) return MOE_ERR_UNSUPPORTED;
+    if (cfg->hidden < 64 || cfg->hidden > 16384 || cfg->hidden % 64) return MOE_ERR_UNSUPPORTED;
+    if (!valid_inter(cfg->inter, cfg->dtype)) return MOE_ERR_UNSUPPORTED;
+    if (cfg->shared_inter != 0 && !valid_inter(cfg->shared_inter, cfg->dtype))
+        return MOE_ERR_UNSUPPORTED;
+    if (cfg->max_tokens < 1) return MOE_ERR_INVALID_ARG;
+    if (cfg->max_tokens > 65536) return MOE_ERR_UNSUPPORTED;
+    if (!weights->router_w || !weights->gate_up || !weights->down) return MOE_ERR_INVALID_ARG;
+    const bool has_shared = cfg->shared_inter > 0;
+    if (has_shared != (weights->shared_gate_up != nullptr) ||
+        has_shared != (weights->shared_down != nullptr))
+        return MOE_ERR_INVALID_ARG;
+    const void *ptrs[] = {weights->router_w, weights->gate_up, weights->down,
+                          weights->shared_gate_up, weights->shared_down};
+    for (const void *ptr : ptrs)
+        if (ptr && !aligned(ptr, 16)) return MOE_ERR_INVALID_ARG;
+    if (weights->router_bias && !aligned(weights->router_bias, 4)) return MOE_ERR_INVALID_ARG;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_UNSUPPORTED;
+
+    moe_ctx *c = new (std::nothrow) moe_ctx;
+    if (!c) return MOE_ERR_HIP;
+    c->cfg = *cfg;
+    c->w = *weights;
+    c->R = cfg->num_experts + (has_shared ? 1 : 0);
+    c->device = dev;
+    c->num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+    const int Is = cfg->shared_inter;
+    c->s = (cfg->inter % 64 == 0 && Is % 64 == 0) ? 64 : (cfg->inter % 32 == 0 && Is % 32 == 0) ? 32 : 16;
+    // largest LDS any plan of this context asks for (x tile of up to 16 rows + h tile)
+    const Plan p = make_plan(c, cfg->max_tokens);
+    if (p.NG < 1 || p.lds > kMaxLds) {
+        delete c;
+        return MOE_ERR_UNSUPPORTED;
+    }
+    if (prepare_expert_kernels(p.lds) != hipSuccess) {
+        delete c;
+        return MOE_ERR_HIP;
+    }
+    *out = c;
+    return MOE_OK;
+}
+
+void moe_destroy(moe_ctx *ctx) { delete ctx; }
+
+size_t moe_workspace_bytes(const moe_ctx *ctx, int32_t T) {
+    if (!ctx || T <= 0 || T > ctx->cfg.max_tokens) return 0;
+    return make_plan(ctx, T).total;
+}
+
+int moe_route(const moe_ctx *c, const void *x, const float *logits_in, int32_t T,
+              float *logits_out, int32_t *topk_ids, float *topk_w, float *shared_gate,
+              void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || T > c->cfg.max_tokens) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if ((x == nullptr) == (logits_in == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (!topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (c->cfg.shared_inter > 0 && !shared_gate) return MOE_ERR_INVALID_ARG;
+    if (x && !aligned(x, 16)) return MOE_ERR_INVALID_ARG;
+    const Plan p = make_plan(c, T);
+    const int st = check_call(c, T, workspace, ws_bytes, &p);
+    if (st != MOE_OK) return st;
+    char *ws = static_cast<char *>(workspace);
+    Launcher L{c, stream, nullptr, 0, true};
+    const float *zpart = logits_in;
+    int KS = 1;
+    const float *bias = nullptr;
+    if (x) {
+        float *zp = reinterpret_cast<float *>(ws + p.o_zpart);
+        enqueue_router(L, c, p, x, zp);
+        zpart = zp;
+        KS = p.KS;
+        bias = c->w.router_bias;
+    }
+    const SelectParams sp = select_params(c, p, zpart, KS, bias, logits_out, topk_ids, topk_w,
+                                          shared_gate);
+    BucketParams bp = bucket_params(c, p, ws, nullptr, nullptr, nullptr, nullptr);
+    if (p.small)
+        L.step("route_small", [&] { return launch_route_small(sp, bp, true, false, stream); });
+    else
+        L.step("select_hist", [&] { return launch_select_hist(sp, bp, true, false, stream); });
+    return hip_status(L.err);
+}
+
+int moe_bucket(const moe_ctx *c, const int32_t *ids_in, int32_t T, int32_t *counts,
+               int32_t *offsets, int32_t *perm, void *workspace, size_t ws_bytes,
+               hipStream_t stream) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || T > c->cfg.max_tokens) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!ids_in || !counts || !offsets || !perm) return MOE_ERR_INVALID_ARG;
+    const Plan p = make_plan(c, T);
+    const int st = check_call(c, T, workspace, ws_bytes, &p);
+    if (st != MOE_OK) return st;
+    Launcher L{c, stream, nullptr, 0, true};
+    enqueue_dispatch(L, p, nullptr,
+                     bucket_params(c, p, static_cast<char *>(workspace), ids_in, counts, offsets, perm));
+    return hip_status(L.err);
+}
+
+int moe_forward(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_in,
+                const float *w_in, const float *gate_in, float *y, void *workspace,
+                size_t ws_bytes, hipStream_t stream) {
+    return forward_impl(c, x, T, ids_in, w_in, gate_in, y, workspace, ws_bytes, stream, nullptr,
+                        0, nullptr, 0, nullptr, true, 0);
+}
+
+int moe_forward_timed(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_in,
+                      const float *w_in, const float *gate_in, float *y, void *workspace,
+                      size_t ws_bytes, hipStream_t stream, hipEvent_t *events,
+                      int32_t n_events) {
+    if (!events || n_events < 2) return MOE_ERR_INVALID_ARG;
+    int32_t n = 0;
+    const int given = (ids_in || w_in || gate_in) ? 1 : 0;
+    int st = forward_impl(c, x, T, ids_in, w_in, gate_in, y, workspace, ws_bytes, stream, nullptr,
+                          0, nullptr, 0, &n, false, given);
+    if (st != MOE_OK) return st;
+    if (n_events != n + 1) return MOE_ERR_INVALID_ARG;
+    return forward_impl(c, x, T, ids_in, w_in, gate_in, y, workspace, ws_bytes, stream, events,
+                        n_events, nullptr, 0, nullptr, true, 0);
+}
+
+int moe_forward_plan(const moe_ctx *c, int32_t T, int32_t routing_given, int32_t *n_kernels,
+                     const char **names, int32_t max_names) {
+    if (!c || !n_kernels) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || T > c->cfg.max_tokens) return MOE_ERR_INVALID_ARG;
+    return forward_impl(c, nullptr, T, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr,
+                        nullptr, 0, names, max_names, n_kernels, false, routing_given);
+}
+
+}  // extern "C"

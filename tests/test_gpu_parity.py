@@ -1,0 +1,419 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle, element by element.
+
+Bars: expert ids and their order bit-exact given the same fp32 logits; selection weights and the
+shared gate within 1e-6; logits and y within |gpu - oracle| <= 1e-3 + 1e-2 |oracle|; bucketing
+tables exact. Inputs come from the seeded generators (sparse_moe_routing_amd.inputs) and the
+expected values from the oracle only; no expected value is derived from a GPU result.
+"""
+import numpy as np
+import pytest
+
+import oracle as oracle_mod
+from sparse_moe_routing_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 1e-3, 1e-2
+W_TOL = 1e-6
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle_mod.default()
+
+
+_LAYERS = {}
+MAX_TOKENS = 8192
+
+
+def get_layer(name, max_tokens=None):
+    """(numpy layer, MoeLayer, device tensors) for a named workload, one context per workload
+    with max_tokens = 8192; cached for the process."""
+    torch = _torch()
+    if name not in _LAYERS:
+        layer = inputs.make_layer(inputs.BY_NAME[name])
+        m, t = binding.layer_from_numpy(layer, MAX_TOKENS)
+        torch.cuda.synchronize()
+        _LAYERS[name] = (layer, m, t)
+    return _LAYERS[name]
+
+
+def x_device(layer_np_x):
+    torch = _torch()
+    a = layer_np_x.view(np.int16) if layer_np_x.dtype == np.uint16 else layer_np_x
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def assert_close(gpu, ref, what):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bad = np.abs(gpu - ref) > ATOL + RTOL * np.abs(ref)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first "
+                             f"{[(tuple(i), gpu[tuple(i)], ref[tuple(i)]) for i in idx]}")
+
+
+def check_selection(ids_g, w_g, g_g, ids_o, w_o, g_o, what, finite_rows=None):
+    mism = np.argwhere(ids_g != ids_o)
+    assert mism.size == 0, f"{what}: ids differ at {mism[:5].tolist()}"
+    rows = slice(None) if finite_rows is None else finite_rows
+    assert np.abs(w_g[rows] - w_o[rows]).max(initial=0) <= W_TOL, what
+    if g_o is not None:
+        assert np.abs(g_g[rows] - g_o[rows]).max(initial=0) <= W_TOL, what
+
+
+# ----------------------------------------------------------------------------- selection
+SEL_CASES = [("tiny_fp32_t4", T) for T in (1, 2, 4, 19, 20, 46, 47, 64, 65, 200)] + \
+            [("decode_b1_t4", T) for T in (1, 2, 4, 19, 20, 32, 46, 47, 64, 65, 192, 768, 4097,
+                                           8192)]
+
+
+@pytest.mark.parametrize("name,T", SEL_CASES)
+def test_select_given_logits(orc, name, T):
+    """moe_route from given fp32 logits: random, tie-heavy (multiples of 0.25, both zeros) and
+    special values (NaN, +-inf); ids bit-exact, weights and gate within 1e-6."""
+    torch = _torch()
+    layer, m, _ = get_layer(name, max_tokens=8192)
+    E, R = m.num_experts, m.rows
+    rng = np.random.default_rng(1000 + T)
+    z = (rng.standard_normal((T, R)) * 2).astype(np.float32)
+    third = max(1, T // 3)
+    z[:third] = inputs.tie_quantize(z[:third], np.arange(third))
+    specials = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0], np.float32)
+    sp_rows = np.arange(third, min(T, 2 * third))
+    for r in sp_rows:
+        cols = rng.choice(E, size=6, replace=False)
+        z[r, cols] = specials[rng.integers(0, 5, size=6)]
+    zt = torch.from_numpy(z).cuda()
+    _, ids, w, g = m.route(logits=zt, want_logits=False)
+    torch.cuda.synchronize()
+    ids_o, w_o, g_o = orc.select(z, E, m.shared_inter > 0)
+    sel_vals = np.take_along_axis(z[:, :E], ids_o, axis=1)
+    finite = np.isfinite(sel_vals).all(1)
+    check_selection(ids.cpu().numpy(), w.cpu().numpy(), None if g is None else g.cpu().numpy(),
+                    ids_o, w_o, g_o, f"{name} T={T}", finite_rows=finite)
+
+
+def test_select_all_equal_and_permuted(orc):
+    torch = _torch()
+    layer, m, _ = get_layer("decode_b1_t4", max_tokens=8192)
+    E = m.num_experts
+    z = np.zeros((3, E + 1), np.float32)
+    z[0] = 0.7
+    z[1, :E] = np.arange(E) / 16.0
+    perm = np.random.default_rng(2).permutation(E)
+    z[2, perm] = z[1, :E]
+    _, ids, w, g = m.route(logits=torch.from_numpy(z).cuda(), want_logits=False)
+    ids = ids.cpu().numpy()
+    w = w.cpu().numpy()
+    assert (ids[0] == np.arange(8)).all() and (w[0] == 0.125).all()
+    assert (ids[1] == np.arange(E - 1, E - 9, -1)).all()
+    assert (ids[2] == perm[ids[1]]).all()
+    assert np.abs(g.cpu().numpy() - np.array([1 / (1 + np.exp(-0.7)), 0.5, 0.5])).max() < W_TOL
+
+
+# ----------------------------------------------------------------------------- fused routing
+def dyadic_layer(name, T, seed):
+    """Router inputs whose fp32 sums are exact in any order: small integers times 2^-6."""
+    w = inputs.BY_NAME[name]
+    rng = np.random.default_rng(seed)
+    R = w.num_experts + 1
+    xi = rng.integers(-3, 4, size=(T, w.hidden)).astype(np.float32)
+    wi = (rng.integers(-3, 4, size=(R, w.hidden)) * 2.0 ** -6).astype(np.float32)
+    if w.dtype == "bf16":
+        return inputs.f32_to_bf16_bits(xi), inputs.f32_to_bf16_bits(wi)
+    return xi, wi
+
+
+@pytest.mark.parametrize("name,T", [("tiny_fp32_t4", 4), ("tiny_fp32_t4", 67),
+                                    ("decode_b1_t4", 4), ("decode_b1_t4", 32),
+                                    ("decode_b1_t4", 192), ("decode_b1_t4", 1000)])
+def test_route_exact_dyadic(orc, name, T):
+    """x -> logits -> ids on the fused path with exactly representable logits: GPU and oracle
+    logits are bit-identical whatever the summation order, so ids (ties included) must match."""
+    torch = _torch()
+    layer, _, t = get_layer(name, max_tokens=8192)
+    w = layer["workload"]
+    x_np, wr_np = dyadic_layer(name, T, seed=T)
+    wr = x_device(wr_np)
+    dev_w = dict(t)
+    dev_w["router_w"] = wr
+    dev_w["router_bias"] = None
+    m = binding.MoeLayer(w.hidden, w.num_experts, w.inter, w.shared_inter, 8192, w.dtype, dev_w)
+    z, ids, wt, g = m.route(x=x_device(x_np))
+    torch.cuda.synchronize()
+    z_o = orc.logits(x_np, wr_np)
+    assert np.array_equal(z.cpu().numpy(), z_o)
+    ids_o, w_o, g_o = orc.select(z_o, w.num_experts, True)
+    check_selection(ids.cpu().numpy(), wt.cpu().numpy(), g.cpu().numpy(), ids_o, w_o, g_o,
+                    f"dyadic {name} T={T}")
+    assert (np.diff(np.sort(z_o[:, :w.num_experts], axis=1), axis=1) == 0).any()  # ties occur
+
+
+def oracle_route_sample(orc, layer, rows):
+    """Oracle logits (fp32) and selection for the given token rows."""
+    x = layer["x"][rows]
+    z = orc.logits(x, layer["router_w"], layer["router_bias"])
+    ids, w, g = orc.select(z, layer["num_experts"], layer["shared_inter"] > 0)
+    return z, ids, w, g
+
+
+def tie_gap_ok(z_o_row, ids_g_row, ids_o_row, E, zgap):
+    """A fused-path id mismatch is allowed only at a near-tie: the experts the two sides rank
+    differently must have oracle logits within zgap of each other."""
+    d = np.nonzero(ids_g_row != ids_o_row)[0]
+    k = d[0]
+    a, b = z_o_row[ids_g_row[k]], z_o_row[ids_o_row[k]]
+    return abs(float(a) - float(b)) <= zgap
+
+
+FULL = ["decode_b1_t4", "decode_b8_t32", "verify_skewed_t192", "prefill_t8192"]
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL)
+def test_route_fused(orc, name):
+    torch = _torch()
+    layer, m, t = get_layer(name)
+    w = layer["workload"]
+    T = w.tokens
+    z, ids, wt, g = m.route(x=t["x"])
+    torch.cuda.synchronize()
+    rows = inputs.sample_tokens(T, 96)
+    z_o, ids_o, w_o, g_o = oracle_route_sample(orc, layer, rows)
+    z_g = z.cpu().numpy()[rows]
+    assert_close(z_g, z_o, f"{name} logits")
+    ids_g = ids.cpu().numpy()[rows]
+    bad = [i for i in range(len(rows)) if (ids_g[i] != ids_o[i]).any()]
+    for i in bad:
+        assert tie_gap_ok(z_o[i], ids_g[i], ids_o[i], w.num_experts, 1e-4), (name, rows[i])
+    assert len(bad) <= max(1, len(rows) // 50), (name, bad)
+    good = np.array([i for i in range(len(rows)) if i not in bad], dtype=np.int64)
+    check_selection(ids_g[good], wt.cpu().numpy()[rows][good], g.cpu().numpy()[rows][good],
+                    ids_o[good], w_o[good], g_o[good], name)
+
+
+# ----------------------------------------------------------------------------- bucketing
+@pytest.mark.parametrize("T", [1, 2, 4, 19, 20, 32, 46, 47, 64, 65, 192, 768, 4097, 8192])
+def test_bucket_exact(orc, T):
+    torch = _torch()
+    layer, m, _ = get_layer("decode_b1_t4", max_tokens=8192)
+    E = m.num_experts
+    rng = np.random.default_rng(77 + T)
+    if T == 192:  # skewed: a few experts take most pairs
+        pref = rng.permutation(E)[:12]
+        ids = np.stack([np.concatenate([rng.permutation(pref)[:6], rng.permutation(
+            np.setdiff1d(np.arange(E), pref))[:2]]) for _ in range(T)]).astype(np.int32)
+    else:
+        ids = np.stack([rng.permutation(E)[:8] for _ in range(T)]).astype(np.int32)
+    counts, offsets, perm = m.bucket(torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    c_o, o_o, p_o = orc.bucket(ids, E)
+    assert np.array_equal(counts.cpu().numpy(), c_o)
+    assert np.array_equal(offsets.cpu().numpy(), o_o)
+    assert np.array_equal(perm.cpu().numpy(), p_o)
+
+
+# ----------------------------------------------------------------------------- forward
+def forward_sample(orc, layer, rows, ids_o, w_o, g_o):
+    T = layer["x"].shape[0]
+    full_ids = np.zeros((T, 8), np.int32)
+    full_w = np.zeros((T, 8), np.float64)
+    full_g = np.zeros((T,), np.float64)
+    full_ids[rows], full_w[rows] = ids_o, w_o
+    if g_o is not None:
+        full_g[rows] = g_o
+    return orc.forward(layer, full_ids, full_w, full_g if g_o is not None else None,
+                       tokens=np.asarray(rows, np.int32))
+
+
+def routing_device(ids, w, g):
+    torch = _torch()
+    return (torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda(),
+            torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda(),
+            None if g is None else torch.from_numpy(np.ascontiguousarray(g, np.float32)).cuda())
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL)
+def test_forward_given_oracle_routing(orc, name):
+    """y from the oracle's own routing (all tokens routed by the oracle, tie tokens from their
+    quantized logits), checked on a token sample against the oracle's fp64 forward."""
+    torch = _torch()
+    layer, m, t = get_layer(name)
+    w = layer["workload"]
+    T = w.tokens
+    allrows = np.arange(T)
+    z_o = orc.logits(layer["x"], layer["router_w"], layer["router_bias"])
+    z_q = inputs.tie_quantize(z_o, inputs.tie_tokens(w))
+    ids_o, w_o, g_o = orc.select(z_q, w.num_experts, True)
+    y = m.forward(t["x"], routing=routing_device(ids_o, w_o, g_o))
+    torch.cuda.synchronize()
+    rows = inputs.sample_tokens(T, 48, must=inputs.tie_tokens(w)[:8])
+    y_o = forward_sample(orc, layer, rows, ids_o[rows], w_o[rows], g_o[rows])
+    assert_close(y.cpu().numpy()[rows], y_o, f"{name} y")
+    del allrows
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL)
+def test_forward_tie_tokens_route_then_forward(orc, name):
+    """The tie protocol: quantized logits through moe_route(logits_in), its routing into
+    moe_forward; the oracle routes the same logits itself."""
+    torch = _torch()
+    layer, m, t = get_layer(name)
+    w = layer["workload"]
+    T = w.tokens
+    z_o = orc.logits(layer["x"], layer["router_w"], layer["router_bias"])
+    tie = inputs.tie_tokens(w)
+    z_q = inputs.tie_quantize(z_o, tie)
+    _, ids, wt, g = m.route(logits=torch.from_numpy(z_q).cuda(), want_logits=False)
+    y = m.forward(t["x"], routing=(ids, wt, g))
+    torch.cuda.synchronize()
+    ids_o, w_o, g_o = orc.select(z_q, w.num_experts, True)
+    check_selection(ids.cpu().numpy(), wt.cpu().numpy(), g.cpu().numpy(), ids_o, w_o, g_o, name)
+    rows = inputs.sample_tokens(T, 48, must=tie[:8])
+    y_o = forward_sample(orc, layer, rows, ids_o[rows], w_o[rows], g_o[rows])
+    assert_close(y.cpu().numpy()[rows], y_o, f"{name} y (tie protocol)")
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL)
+def test_forward_internal_routing(orc, name):
+    """The whole hot path from x (the launch configuration the benchmark times)."""
+    torch = _torch()
+    layer, m, t = get_layer(name)
+    w = layer["workload"]
+    T = w.tokens
+    y = m.forward(t["x"])
+    _, ids, _, _ = m.route(x=t["x"], want_logits=False)
+    torch.cuda.synchronize()
+    rows = inputs.sample_tokens(T, 48)
+    z_o, ids_o, w_o, g_o = oracle_route_sample(orc, layer, rows)
+    ids_g = ids.cpu().numpy()[rows]
+    same = np.array([(ids_g[i] == ids_o[i]).all() for i in range(len(rows))])
+    assert same.sum() >= len(rows) - max(1, len(rows) // 50)
+    y_o = forward_sample(orc, layer, rows[same], ids_o[same], w_o[same], g_o[same])
+    assert_close(y.cpu().numpy()[rows[same]], y_o, f"{name} y (internal routing)")
+
+
+def test_forward_small_sizes_all_tokens(orc):
+    """Every output of several small T (ragged token tiles, one to several 16-token groups)."""
+    torch = _torch()
+    layer, m, t = get_layer("decode_b1_t4", max_tokens=8192)
+    for T in (1, 2, 17, 47):
+        x_np = inputs.draw_x(layer["workload"], T, seed=500 + T)
+        x = x_device(x_np)
+        y = m.forward(x)
+        torch.cuda.synchronize()
+        lay = dict(layer)
+        lay["x"] = x_np
+        z_o = orc.logits(x_np, layer["router_w"], None)
+        ids_o, w_o, g_o = orc.select(z_o, 256, True)
+        _, ids, _, _ = m.route(x=x, want_logits=False)
+        ids_g = ids.cpu().numpy()
+        same = (ids_g == ids_o).all(1)
+        assert same.sum() >= T - 1
+        rows = np.nonzero(same)[0].astype(np.int32)
+        y_o = orc.forward(lay, ids_o, w_o, g_o, tokens=rows)
+        assert_close(y.cpu().numpy()[rows], y_o, f"T={T}")
+
+
+# ----------------------------------------------------------------------------- special cases
+def test_dense_expert_reproduces_swiglu():
+    """E = 8 identical experts: every token selects all eight, the weights sum to one, so the
+    routed part is one plain SwiGLU (numpy fp64) plus the gated shared expert."""
+    torch = _torch()
+    import scipy.special
+    rng = np.random.default_rng(31)
+    H, E, I, Is, T = 256, 8, 64, 32, 21
+    def bf(shape, s):
+        return inputs.f32_to_bf16_bits((rng.standard_normal(shape) * s).astype(np.float32))
+    gu1, dn1 = bf((2 * I, H), H ** -0.5), bf((H, I), I ** -0.5)
+    layer = {"router_w": bf((E + 1, H), H ** -0.5), "router_bias": None,
+             "gate_up": np.ascontiguousarray(np.broadcast_to(gu1, (E, 2 * I, H))),
+             "down": np.ascontiguousarray(np.broadcast_to(dn1, (E, H, I))),
+             "shared_gate_up": bf((2 * Is, H), H ** -0.5), "shared_down": bf((H, Is), Is ** -0.5),
+             "x": bf((T, H), 1.0)}
+    t = binding.device_weights(layer)
+    m = binding.MoeLayer(H, E, I, Is, 64, "bf16", t)
+    y = m.forward(t["x"])
+    _, ids, wt, g = m.route(x=t["x"], want_logits=False)
+    torch.cuda.synchronize()
+    assert (np.sort(ids.cpu().numpy(), 1) == np.arange(8)).all()
+    f = lambda a: inputs.bf16_bits_to_f32(a).astype(np.float64)
+    x = f(layer["x"])
+    def swiglu(gu, dn, n):
+        a, u = x @ f(gu[:n]).T, x @ f(gu[n:]).T
+        return (a * scipy.special.expit(a) * u) @ f(dn).T
+    gg = g.cpu().numpy().astype(np.float64)
+    ref = swiglu(gu1, dn1, I) + gg[:, None] * swiglu(layer["shared_gate_up"], layer["shared_down"], Is)
+    assert_close(y.cpu().numpy(), ref, "dense SwiGLU")
+
+
+def test_zero_input_gives_zero_output():
+    torch = _torch()
+    layer, m, t = get_layer("decode_b1_t4", max_tokens=8192)
+    x = torch.zeros((5, 2048), dtype=torch.int16, device="cuda")
+    y = m.forward(x)
+    torch.cuda.synchronize()
+    assert (y.cpu().numpy() == 0).all()
+
+
+def test_batch_invariance_bitwise():
+    """A token's logits, routing and output do not depend on the batch it is computed in."""
+    torch = _torch()
+    layer, m, t = get_layer("decode_b8_t32", max_tokens=8192)
+    x = t["x"]
+    y32 = m.forward(x)
+    y4 = m.forward(x[:4].contiguous())
+    y1 = m.forward(x[7:8].contiguous())
+    big = torch.cat([x] * 12)  # 384 tokens: the large-T launch configuration
+    y384 = m.forward(big)
+    z32, ids32, _, _ = m.route(x=x)
+    z4, ids4, _, _ = m.route(x=x[:4].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(z32[:4], z4) and torch.equal(ids32[:4], ids4)
+    assert torch.equal(y32[:4], y4)
+    assert torch.equal(y32[7:8], y1)
+    assert torch.equal(y384[:32], y32) and torch.equal(y384[352:], y32)
+
+
+def test_token_permutation_equivariance():
+    torch = _torch()
+    layer, m, t = get_layer("decode_b8_t32", max_tokens=8192)
+    x = t["x"]
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(32)).cuda()
+    y = m.forward(x)
+    yp = m.forward(x[perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y[perm])
+
+
+def test_call_errors_and_empty():
+    torch = _torch()
+    layer, m, t = get_layer("decode_b1_t4", max_tokens=8192)
+    lib = m.lib
+    ws = m.workspace(4)
+    y = torch.empty((4, 2048), dtype=torch.float32, device="cuda")
+    s = binding._stream()
+    P = binding._ptr
+    assert lib.moe_forward(m.ctx, P(t["x"]), 0, None, None, None, P(y), None, 0, s) == binding.MOE_OK
+    assert lib.moe_forward(m.ctx, P(t["x"]), 8193, None, None, None, P(y), P(ws), ws.numel(), s) \
+        == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(m.ctx, P(t["x"]), 4, None, None, None, P(y), P(ws), 16, s) \
+        == binding.MOE_ERR_WORKSPACE
+    assert lib.moe_forward(m.ctx, P(t["x"]), 4, None, None, None, None, P(ws), ws.numel(), s) \
+        == binding.MOE_ERR_INVALID_ARG
+    ids = torch.zeros((4, 8), dtype=torch.int32, device="cuda")
+    assert lib.moe_forward(m.ctx, P(t["x"]), 4, P(ids), None, None, P(y), P(ws), ws.numel(), s) \
+        == binding.MOE_ERR_INVALID_ARG  # routing must be all given or all absent
+    assert lib.moe_route(m.ctx, P(t["x"]), P(y), 4, None, P(ids), P(y), P(y), P(ws), ws.numel(),
+                         s) == binding.MOE_ERR_INVALID_ARG  # both x and logits
+    plan = m.plan(4)
+    assert plan == ["router", "route_small", "expert", "combine"]
+    assert m.plan(8192)[:2] == ["router", "select_hist"]

@@ -1,0 +1,132 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every function include/moe.h declares,
+and rejects bad arguments on the host before touching the GPU (no compute call here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_routing_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names += re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_route",
+                     "moe_bucket", "moe_forward", "moe_status_str"):
+        assert required in names
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_no_oracle_code_in_the_library():
+    # the product library must not contain the oracle's entry points
+    data = open(binding.LIB_PATH, "rb").read()
+    assert b"oracle_" not in data
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4):
+        assert lib.moe_status_str(st)
+    assert lib.moe_status_str(12345) == b"unknown status"
+
+
+def good_config():
+    return binding.moe_config(2048, 256, 8, 512, 512, 64, binding.MOE_BF16)
+
+
+def fake_weights(shared=True):
+    # host addresses that are never dereferenced: validation runs before any device access
+    base = 0x10000000
+    return binding.moe_weights(base, None, base + 0x1000000, base + 0x2000000,
+                               base + 0x3000000 if shared else None,
+                               base + 0x4000000 if shared else None)
+
+
+def create(lib, cfg, w):
+    ctx = ctypes.c_void_p()
+    st = lib.moe_create(ctypes.byref(cfg) if cfg is not None else None,
+                        ctypes.byref(w) if w is not None else None, ctypes.byref(ctx))
+    return st, ctx
+
+
+@pytest.mark.parametrize("field,value,want", [
+    ("top_k", 4, binding.MOE_ERR_UNSUPPORTED),
+    ("top_k", 16, binding.MOE_ERR_UNSUPPORTED),
+    ("num_experts", 7, binding.MOE_ERR_UNSUPPORTED),
+    ("num_experts", 257, binding.MOE_ERR_UNSUPPORTED),
+    ("hidden", 100, binding.MOE_ERR_UNSUPPORTED),
+    ("hidden", 0, binding.MOE_ERR_UNSUPPORTED),
+    ("inter", 48, binding.MOE_ERR_UNSUPPORTED),     # bf16 needs a multiple of 32
+    ("shared_inter", 8, binding.MOE_ERR_UNSUPPORTED),
+    ("max_tokens", 0, binding.MOE_ERR_INVALID_ARG),
+    ("max_tokens", 70000, binding.MOE_ERR_UNSUPPORTED),
+    ("dtype", 7, binding.MOE_ERR_INVALID_ARG),
+])
+def test_create_rejects_bad_config(lib, field, value, want):
+    cfg = good_config()
+    setattr(cfg, field, value)
+    st, ctx = create(lib, cfg, fake_weights())
+    assert st == want
+    assert not ctx.value
+
+
+def test_create_rejects_bad_weights(lib):
+    cfg = good_config()
+    assert create(lib, None, fake_weights())[0] == binding.MOE_ERR_INVALID_ARG
+    assert create(lib, cfg, None)[0] == binding.MOE_ERR_INVALID_ARG
+    w = fake_weights()
+    w.router_w = None
+    assert create(lib, cfg, w)[0] == binding.MOE_ERR_INVALID_ARG
+    w = fake_weights(shared=False)  # shared_inter > 0 but no shared weights
+    assert create(lib, cfg, w)[0] == binding.MOE_ERR_INVALID_ARG
+    cfg0 = good_config()
+    cfg0.shared_inter = 0
+    assert create(lib, cfg0, fake_weights(shared=True))[0] == binding.MOE_ERR_INVALID_ARG
+    w = fake_weights()
+    w.gate_up = 0x10000008  # not 16-byte aligned
+    assert create(lib, cfg, w)[0] == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_create(ctypes.byref(cfg), ctypes.byref(fake_weights()), None) == \
+        binding.MOE_ERR_INVALID_ARG
+
+
+def test_calls_reject_null_context(lib):
+    assert lib.moe_workspace_bytes(None, 4) == 0
+    assert lib.moe_route(None, None, None, 4, None, None, None, None, None, 0, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_bucket(None, None, 4, None, None, None, None, 0, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(None, None, 4, None, None, None, None, None, 0, None) == \
+        binding.MOE_ERR_INVALID_ARG
+    n = ctypes.c_int32()
+    assert lib.moe_forward_plan(None, 4, 0, ctypes.byref(n), None, 0) == binding.MOE_ERR_INVALID_ARG
+    lib.moe_destroy(None)
+
+
+def test_create_without_gpu_reports_hip_error(lib):
+    """A valid config on a machine without a usable gfx950 device fails cleanly."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, ctx = create(lib, good_config(), fake_weights())
+    assert st in (binding.MOE_ERR_HIP, binding.MOE_ERR_UNSUPPORTED)
+    assert not ctx.value
