@@ -83,12 +83,19 @@ def step_bytes(w, U):
     return (esz * (E + 1) * H + 3 * esz * H * Is + U * 3 * esz * H * I + esz * T * H + 4 * T * H)
 
 
-def expert_bytes(w, U):
-    """Algorithmic bytes of one expert-kernel launch: the touched expert weights (routed and
-    shared) and the x rows it stages."""
+def kernel_bytes(w, U, name):
+    """Algorithmic bytes of one launch of an expert-stage kernel: the weights it must read (the U
+    distinct routed experts touched, each once, and the shared expert) plus the activations it
+    must read or write. Intermediates (h, partial sums, routing tables) are not counted."""
     esz = 2 if w.dtype == "bf16" else 4
     H, I, Is, T = w.hidden, w.inter, w.shared_inter, w.tokens
-    return 3 * esz * H * Is + U * 3 * esz * H * I + esz * T * H
+    if name == "gateup":
+        return 2 * esz * H * Is + U * 2 * esz * H * I + esz * T * H
+    if name == "down":
+        return esz * H * Is + U * esz * H * I + 4 * T * H
+    if name == "expert":
+        return 3 * esz * H * Is + U * 3 * esz * H * I + esz * T * H
+    raise KeyError(name)
 
 
 def cpu_baseline(w, m_t, seconds):
@@ -180,6 +187,9 @@ def main():
     # timed region: K steps, per-kernel events recorded on the launch stream
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
               for _ in range(args.steps)]
+    for evs in events:  # torch creates the HIP event on its first record
+        for e in evs:
+            e.record(stream)
     used = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -199,9 +209,14 @@ def main():
             per_kernel[name].append(ev[k].elapsed_time(ev[k + 1]))
         step_ms.append(ev[0].elapsed_time(ev[-1]))
     mean_U = float(np.mean([U[c] for c in used]))
-    exp_us = float(np.mean(per_kernel["expert"])) * 1e3
-    exp_bytes = float(np.mean([expert_bytes(w, U[c]) for c in used]))
-    achieved = exp_bytes / (exp_us * 1e-6) / 1e9
+    stage = {}
+    for name in ("gateup", "down", "expert"):
+        if name in per_kernel:
+            us = float(np.mean(per_kernel[name])) * 1e3
+            b = float(np.mean([kernel_bytes(w, U[c], name) for c in used]))
+            stage[name] = {"us": us, "bytes": b, "gbs": b / (us * 1e-6) / 1e9}
+    dom = max(stage, key=lambda k: stage[k]["us"])  # the dominant kernel
+    achieved = stage[dom]["gbs"]
     step_b = float(np.mean([step_bytes(w, U[c]) for c in used]))
     gpu_step_us = float(np.median(step_ms)) * 1e3
     log("[bench] per-kernel mean us: " + ", ".join(
@@ -229,7 +244,8 @@ def main():
         "hbm_frac_step": step_b / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "mean_distinct_experts": mean_U,
         "per_kernel_us": {k: float(np.mean(v)) * 1e3 for k, v in per_kernel.items()},
-        "roofline": {"kernel": "expert", "bound": "hbm", "achieved": achieved,
+        "expert_stage_gbs": {k: v["gbs"] for k, v in stage.items()},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None},
     }

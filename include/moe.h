@@ -24,7 +24,10 @@
  * memory. The context BORROWS the weight pointers (nothing is copied); they must stay valid and
  * unchanged while the context is used. The library allocates no device memory: each call takes a
  * caller-provided workspace of at least moe_workspace_bytes(ctx, T) bytes, 256-byte aligned, that
- * the call owns until its kernels finish. The context is immutable after moe_create, so calls on
+ * the call owns until its kernels finish. The first 256 bytes of a workspace hold arrival
+ * counters: they must be zero before the workspace is first used (e.g. allocate it zeroed), and
+ * every call leaves them zero again, so a workspace can be reused by later calls on any stream as
+ * long as two calls never use it at the same time. The context is immutable after moe_create, so calls on
  * different streams are safe when each uses its own workspace and outputs.
  *
  * Errors: arguments are validated on the host before anything is enqueued; a rejected call

@@ -139,8 +139,11 @@ class MoeLayer:
         return int(self.lib.moe_workspace_bytes(self.ctx, T))
 
     def workspace(self, T: int, device="cuda"):
+        """A workspace for calls of up to T tokens. It starts zeroed: the library keeps arrival
+        counters in its first 256 bytes, which must be zero before the first call and which
+        every call leaves at zero."""
         import torch
-        return torch.empty(max(self.workspace_bytes(T), 256), dtype=torch.uint8, device=device)
+        return torch.zeros(max(self.workspace_bytes(T), 256), dtype=torch.uint8, device=device)
 
     def route(self, x=None, logits=None, T=None, ws=None, want_logits=True, stream=None):
         """(logits [T][R] or None, ids [T][8], w [T][8], g [T] or None) from x or given logits."""

@@ -28,18 +28,23 @@
 namespace moe {
 
 constexpr int kExpertThreads = 256;
-constexpr int kUnroll = 8;
 
 __device__ __forceinline__ uint4 lds16(const void *p) {
     return *reinterpret_cast<const uint4 *>(p);
 }
 
-template <class Op>
+// SW: slice width (intermediate rows per slice, 16 per gate/up wave); Op: element type.
+template <class Op, int SW>
 __global__ __launch_bounds__(kExpertThreads) void expert_kernel(ExpertParams p) {
     using elem_t = typename Op::elem_t;
+    constexpr int kU = Op::kElemBytes == 2 ? 8 : 4;  // k steps / row tiles per load batch
+    constexpr int kNst = SW / Op::kStep;             // k steps of the down product per slice
+    constexpr int kGuWaves = SW / kTile;             // waves computing gate/up tiles
+    static_assert(SW % Op::kStep == 0 && kGuWaves >= 1 && kGuWaves <= 4, "slice width");
+    constexpr int kHs = SW + 4;                      // LDS row stride of h (floats)
+
     extern __shared__ __align__(16) unsigned char smem[];
     elem_t *xs = reinterpret_cast<elem_t *>(smem);
-    const int hs_stride = p.s + 4;
     float *hs = reinterpret_cast<float *>(smem + (size_t)p.NG * p.x_stride * sizeof(elem_t));
 
     const int tid = threadIdx.x;
@@ -49,8 +54,11 @@ __global__ __launch_bounds__(kExpertThreads) void expert_kernel(ExpertParams p) 
     const int nunits = p.num_groups[0] * n_sc;
     const int chunks_per_row = p.H / Op::kPerLane;
     const int n_row_tiles = p.H / kTile;
+    const int tiles_w = (n_row_tiles - wave + 3) / 4;  // down row tiles wave, wave+4, ...
+    const int nfull3 = tiles_w / kU;
+    const int nfull1 = p.H / (kU * Op::kStep);
+    const int rem1 = nfull1 * kU * Op::kStep;
     const elem_t *x = reinterpret_cast<const elem_t *>(p.x);
-    const uint4 zero = {0u, 0u, 0u, 0u};
 
     for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
         const int gi = u / n_sc, sc = u - (u / n_sc) * n_sc;
@@ -59,8 +67,8 @@ __global__ __launch_bounds__(kExpertThreads) void expert_kernel(ExpertParams p) 
         const bool shared = e == p.E;
         const int Ie = shared ? p.Is : p.I;
         const int j_begin = sc * p.SPU;
-        if (j_begin * p.s >= Ie) continue;  // uniform over the block
-        const int j_end = min(j_begin + p.SPU, Ie / p.s);
+        if (j_begin * SW >= Ie) continue;  // uniform over the block
+        const int j_end = min(j_begin + p.SPU, Ie / SW);
 
         __syncthreads();  // the previous unit's readers of xs / hs are done
         for (int idx = tid; idx < n * chunks_per_row; idx += kExpertThreads) {
@@ -71,6 +79,9 @@ __global__ __launch_bounds__(kExpertThreads) void expert_kernel(ExpertParams p) 
                 load16(x + (size_t)tok * p.H + c * Op::kPerLane);
         }
         const bool col_ok = col < n;
+        // Token columns >= n read row 0 of the tiles: matrix-core columns are independent, so
+        // those columns only produce values that are never stored.
+        const int crow = col_ok ? col : 0;
         const int slot = !col_ok ? 0 : (shared ? p.T * kTopK + start + col : p.perm[start + col]);
         const elem_t *gu = reinterpret_cast<const elem_t *>(shared ? p.sgu : p.gate_up) +
                            (shared ? 0 : (size_t)e * 2 * Ie * p.H);
@@ -80,162 +91,224 @@ __global__ __launch_bounds__(kExpertThreads) void expert_kernel(ExpertParams p) 
         __syncthreads();
 
         for (int j = j_begin; j < j_end; ++j) {
-            // ---- gate/up tiles + SwiGLU
-            if (wave < p.s / kTile) {
-                const int i0 = j * p.s + wave * kTile;
+            const elem_t *dcol = dn + (size_t)col * Ie + j * SW + q * Op::kPerLane;
+            uint4 dA[kU][kNst], dB[kU][kNst];
+            // down weights of row-tile batch b: tiles wave + 4 * (b * kU + v)
+            auto load_down = [&](uint4(&d)[kU][kNst], int b) {
+#pragma unroll
+                for (int v = 0; v < kU; ++v) {
+                    const elem_t *src = dcol + (size_t)(wave + 4 * (b * kU + v)) * kTile * Ie;
+#pragma unroll
+                    for (int st = 0; st < kNst; ++st) d[v][st] = load16_stream(src + st * Op::kStep);
+                }
+            };
+
+            // ---- gate/up tiles + SwiGLU: a double-buffered weight stream, then h into LDS
+            if (wave < kGuWaves) {
+                const int i0 = j * SW + wave * kTile;
                 const elem_t *grow = gu + (size_t)(i0 + col) * p.H + q * Op::kPerLane;
                 const elem_t *urow = gu + (size_t)(Ie + i0 + col) * p.H + q * Op::kPerLane;
-                const elem_t *xrow = xs + (col_ok ? col : 0) * p.x_stride + q * Op::kPerLane;
+                const elem_t *xrow = xs + crow * p.x_stride + q * Op::kPerLane;
                 f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-                for (int k0 = 0; k0 < p.H; k0 += kUnroll * Op::kStep) {
-                    uint4 ga[kUnroll], ua[kUnroll], xb[kUnroll];
+                uint4 gA[kU], uA[kU], gB[kU], uB[kU];
+                auto load_gu = [&](uint4(&g)[kU], uint4(&uu)[kU], int b) {
 #pragma unroll
-                    for (int v = 0; v < kUnroll; ++v) {
-                        const int kk = k0 + v * Op::kStep;
-                        if (kk < p.H) {
-                            ga[v] = load16_stream(grow + kk);
-                            ua[v] = load16_stream(urow + kk);
-                        }
+                    for (int v = 0; v < kU; ++v) {
+                        const int kk = (b * kU + v) * Op::kStep;
+                        g[v] = load16_stream(grow + kk);
+                        uu[v] = load16_stream(urow + kk);
                     }
+                };
+                auto mma_gu = [&](const uint4(&g)[kU], const uint4(&uu)[kU], int b) {
 #pragma unroll
-                    for (int v = 0; v < kUnroll; ++v) {
-                        const int kk = k0 + v * Op::kStep;
-                        if (kk < p.H) xb[v] = col_ok ? lds16(xrow + kk) : zero;
+                    for (int v = 0; v < kU; ++v) {
+                        const uint4 xb = lds16(xrow + (b * kU + v) * Op::kStep);
+                        Op::mma(ag, g[v], xb);
+                        Op::mma(au, uu[v], xb);
                     }
-#pragma unroll
-                    for (int v = 0; v < kUnroll; ++v) {
-                        const int kk = k0 + v * Op::kStep;
-                        if (kk < p.H) {
-                            Op::mma(ag, ga[v], xb[v]);
-                            Op::mma(au, ua[v], xb[v]);
-                        }
-                    }
+                };
+                if (nfull1 > 0) load_gu(gA, uA, 0);
+                int b = 0;
+                for (; b + 2 <= nfull1; b += 2) {
+                    load_gu(gB, uB, b + 1);
+                    mma_gu(gA, uA, b);
+                    if (b + 2 < nfull1) load_gu(gA, uA, b + 2);
+                    mma_gu(gB, uB, b + 1);
                 }
+                if (b < nfull1) mma_gu(gA, uA, b);
+                for (int kk = rem1; kk < p.H; kk += Op::kStep) {  // only when H % (kU*step) != 0
+                    const uint4 xb = lds16(xrow + kk);
+                    Op::mma(ag, load16_stream(grow + kk), xb);
+                    Op::mma(au, load16_stream(urow + kk), xb);
+                }
+                if (nfull3 > 0) load_down(dA, 0);  // the down stream does not depend on h
                 f32x4_t hv;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) hv[r] = ag[r] / (1.0f + expf(-ag[r])) * au[r];
                 // lane holds intermediate rows 4q + r of this tile for token column `col`
-                *reinterpret_cast<f32x4_t *>(hs + col * hs_stride + wave * kTile + 4 * q) = hv;
+                *reinterpret_cast<f32x4_t *>(hs + col * kHs + wave * kTile + 4 * q) = hv;
+            } else if (nfull3 > 0) {
+                load_down(dA, 0);
             }
             __syncthreads();
 
-            // ---- B fragments of the down product: h^T for this slice
-            constexpr int kMaxSteps = 64 / Op::kStep;  // s <= 64
-            const int nsteps = p.s / Op::kStep;
-            uint4 bhi[kMaxSteps], blo[kMaxSteps];
+            // ---- B fragments of the down product: h^T of this slice
+            uint4 bhi[kNst], blo[kNst];
 #pragma unroll
-            for (int st = 0; st < kMaxSteps; ++st) {
-                bhi[st] = zero;
-                blo[st] = zero;
-                if (st < nsteps && col_ok) {
-                    const float *hp = hs + col * hs_stride + st * Op::kStep + q * Op::kPerLane;
-                    if constexpr (Op::kElemBytes == 2) {
-                        uint32_t hw[4], lw[4];
+            for (int st = 0; st < kNst; ++st) {
+                const float *hp = hs + crow * kHs + st * Op::kStep + q * Op::kPerLane;
+                if constexpr (Op::kElemBytes == 2) {
+                    uint32_t hw[4], lw[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float h0 = hp[2 * i], h1 = hp[2 * i + 1];
-                            const uint32_t a0 = f32_to_bf16_bits(h0), a1 = f32_to_bf16_bits(h1);
-                            const uint32_t l0 = f32_to_bf16_bits(h0 - bf16_bits_to_f32(a0));
-                            const uint32_t l1 = f32_to_bf16_bits(h1 - bf16_bits_to_f32(a1));
-                            hw[i] = a0 | (a1 << 16);
-                            lw[i] = l0 | (l1 << 16);
-                        }
-                        bhi[st] = uint4{hw[0], hw[1], hw[2], hw[3]};
-                        blo[st] = uint4{lw[0], lw[1], lw[2], lw[3]};
-                    } else {
-                        bhi[st] = uint4{__float_as_uint(hp[0]), __float_as_uint(hp[1]),
-                                        __float_as_uint(hp[2]), __float_as_uint(hp[3])};
+                    for (int i = 0; i < 4; ++i) {
+                        const float h0 = hp[2 * i], h1 = hp[2 * i + 1];
+                        const uint32_t a0 = f32_to_bf16_bits(h0), a1 = f32_to_bf16_bits(h1);
+                        const uint32_t l0 = f32_to_bf16_bits(h0 - bf16_bits_to_f32(a0));
+                        const uint32_t l1 = f32_to_bf16_bits(h1 - bf16_bits_to_f32(a1));
+                        hw[i] = a0 | (a1 << 16);
+                        lw[i] = l0 | (l1 << 16);
                     }
+                    bhi[st] = uint4{hw[0], hw[1], hw[2], hw[3]};
+                    blo[st] = uint4{lw[0], lw[1], lw[2], lw[3]};
+                } else {
+                    bhi[st] = uint4{__float_as_uint(hp[0]), __float_as_uint(hp[1]),
+                                    __float_as_uint(hp[2]), __float_as_uint(hp[3])};
+                    blo[st] = bhi[st];
                 }
             }
             __syncthreads();  // hs may be overwritten by the next slice from here on
 
-            // ---- down tiles: rows rt*16 .. +16 of the [H x s] column block
-            const elem_t *dcol = dn + (size_t)col * Ie + j * p.s + q * Op::kPerLane;
-            for (int rt0 = wave; rt0 < n_row_tiles; rt0 += 4 * kUnroll) {
-                uint4 a[kUnroll][kMaxSteps];
+            // ---- down tiles: rows rt*16 .. +16 of the [H x SW] column block
+            auto tile_out = [&](const uint4(&a)[kNst], int rt) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int v = 0; v < kUnroll; ++v) {
-                    const int rt = rt0 + 4 * v;
-#pragma unroll
-                    for (int st = 0; st < kMaxSteps; ++st)
-                        if (rt < n_row_tiles && st < nsteps)
-                            a[v][st] = load16_stream(dcol + (size_t)rt * kTile * Ie + st * Op::kStep);
+                for (int st = 0; st < kNst; ++st) {
+                    Op::mma(acc, a[st], bhi[st]);
+                    if constexpr (Op::kElemBytes == 2) Op::mma(acc, a[st], blo[st]);
                 }
-#pragma unroll
-                for (int v = 0; v < kUnroll; ++v) {
-                    const int rt = rt0 + 4 * v;
-                    if (rt >= n_row_tiles) break;
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int st = 0; st < kMaxSteps; ++st) {
-                        if (st < nsteps) {
-                            Op::mma(acc, a[v][st], bhi[st]);
-                            if constexpr (Op::kElemBytes == 2) Op::mma(acc, a[v][st], blo[st]);
-                        }
-                    }
-                    if (col_ok) {
-                        f32x4_t *dst = reinterpret_cast<f32x4_t *>(yout + rt * kTile + 4 * q);
-                        if (j == j_begin) *dst = acc;
-                        else *dst = *dst + acc;
-                    }
+                if (col_ok) {
+                    f32x4_t *dst = reinterpret_cast<f32x4_t *>(yout + rt * kTile + 4 * q);
+                    if (j == j_begin) *dst = acc;
+                    else *dst = *dst + acc;
                 }
+            };
+            auto mma_down = [&](const uint4(&d)[kU][kNst], int b) {
+#pragma unroll
+                for (int v = 0; v < kU; ++v) tile_out(d[v], wave + 4 * (b * kU + v));
+            };
+            int b = 0;
+            for (; b + 2 <= nfull3; b += 2) {
+                load_down(dB, b + 1);
+                mma_down(dA, b);
+                if (b + 2 < nfull3) load_down(dA, b + 2);
+                mma_down(dB, b + 1);
+            }
+            if (b < nfull3) mma_down(dA, b);
+            for (int i = nfull3 * kU; i < tiles_w; ++i) {  // tiles past the last full batch
+                const int rt = wave + 4 * i;
+                uint4 a[kNst];
+#pragma unroll
+                for (int st = 0; st < kNst; ++st)
+                    a[st] = load16_stream(dcol + (size_t)rt * kTile * Ie + st * Op::kStep);
+                tile_out(a, rt);
             }
         }
     }
 }
 
-// y[t] = sum_k w[t][k] * (sum of the routed partials of pair t*8+k) + g[t] * (shared partials)
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-    const int hchunks = (p.H / 4 + 255) / 256;
-    const int t = blockIdx.x / hchunks;
-    const int h = ((blockIdx.x - t * hchunks) * 256 + threadIdx.x) * 4;
+// y[t][h..h+4) = sum_k w[t][k] * (sum over slice chunks of the routed partials of pair t*8+k)
+//               + g[t] * (sum over slice chunks of the shared partials of token t).
+// One thread per 4 outputs, 64 threads per block, so even T = 4 spreads over 32 blocks.
+__global__ __launch_bounds__(64) void combine_kernel(CombineParams p) {
+    const int hblocks = (p.H + 255) / 256;
+    const int t = blockIdx.x / hblocks;
+    const int h = ((blockIdx.x - t * hblocks) * 64 + threadIdx.x) * 4;
     if (h >= p.H) return;
     const size_t chunk = (size_t)p.slots * p.H;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    constexpr int kMaxChunks = 8;
+    // partial sums of one slot over its slice chunks: all loads issued before the adds, the
+    // adds in chunk order (the same order an all-slices unit accumulates in)
+    auto slot_sum = [&](int slot, int nch) {
+        const float *src = p.ypart + (size_t)slot * p.H + h;
+        float4 v[kMaxChunks];
 #pragma unroll
-    for (int k = 0; k < kTopK; ++k) {
-        const float *src = p.ypart + (size_t)(t * kTopK + k) * p.H + h;
-        float4 s = *reinterpret_cast<const float4 *>(src);
-        for (int c = 1; c < p.n_sc_routed; ++c) {
-            const float4 v = *reinterpret_cast<const float4 *>(src + c * chunk);
-            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        for (int c = 0; c < kMaxChunks; ++c)  // unconditional loads: chunks past nch re-read one
+            v[c] = *reinterpret_cast<const float4 *>(src + (c < nch ? c : nch - 1) * chunk);
+        float4 s = v[0];
+#pragma unroll
+        for (int c = 1; c < kMaxChunks; ++c) {
+            const bool in = c < nch;
+            s.x = in ? s.x + v[c].x : s.x;
+            s.y = in ? s.y + v[c].y : s.y;
+            s.z = in ? s.z + v[c].z : s.z;
+            s.w = in ? s.w + v[c].w : s.w;
         }
-        const float wk = p.w[t * kTopK + k];
-        acc.x += wk * s.x; acc.y += wk * s.y; acc.z += wk * s.z; acc.w += wk * s.w;
-    }
-    if (p.has_shared) {
-        const float *src = p.ypart + (size_t)(p.T * kTopK + t) * p.H + h;
-        float4 s = *reinterpret_cast<const float4 *>(src);
-        for (int c = 1; c < p.n_sc_shared; ++c) {
-            const float4 v = *reinterpret_cast<const float4 *>(src + c * chunk);
-            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        return s;
+    };
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.w) {
+#pragma unroll
+        for (int k = 0; k < kTopK; ++k) {
+            const float4 s = slot_sum(t * kTopK + k, p.n_sc_routed);
+            const float wk = p.w[t * kTopK + k];
+            acc.x += wk * s.x; acc.y += wk * s.y; acc.z += wk * s.z; acc.w += wk * s.w;
         }
-        const float gt = p.g[t];
-        acc.x += gt * s.x; acc.y += gt * s.y; acc.z += gt * s.z; acc.w += gt * s.w;
+        if (p.has_shared) {
+            const float4 s = slot_sum(p.T * kTopK + t, p.n_sc_shared);
+            const float gt = p.g[t];
+            acc.x += gt * s.x; acc.y += gt * s.y; acc.z += gt * s.z; acc.w += gt * s.w;
+        }
+    } else {  // weighted partials, one chunk each: y = sum_k v_k + v_shared, in rank order
+        float4 v[kTopK + 1];
+#pragma unroll
+        for (int k = 0; k < kTopK; ++k)
+            v[k] = *reinterpret_cast<const float4 *>(p.ypart + (size_t)(t * kTopK + k) * p.H + h);
+        v[kTopK] = p.has_shared
+            ? *reinterpret_cast<const float4 *>(p.ypart + (size_t)(p.T * kTopK + t) * p.H + h)
+            : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < kTopK; ++k) {
+            acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+        }
+        if (p.has_shared) {
+            acc.x += v[kTopK].x; acc.y += v[kTopK].y; acc.z += v[kTopK].z; acc.w += v[kTopK].w;
+        }
     }
     *reinterpret_cast<float4 *>(p.y + (size_t)t * p.H + h) = acc;
 }
 
+template <class Op, int SW>
+hipError_t set_lds_limit(size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&expert_kernel<Op, SW>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 hipError_t prepare_expert_kernels(size_t max_lds_bytes) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&expert_kernel<OpBF16>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)max_lds_bytes);
-    if (err != hipSuccess) return err;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&expert_kernel<OpF32>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds_bytes);
+    hipError_t e;
+    if ((e = set_lds_limit<OpBF16, 32>(max_lds_bytes)) != hipSuccess) return e;
+    if ((e = set_lds_limit<OpBF16, 64>(max_lds_bytes)) != hipSuccess) return e;
+    if ((e = set_lds_limit<OpF32, 16>(max_lds_bytes)) != hipSuccess) return e;
+    if ((e = set_lds_limit<OpF32, 32>(max_lds_bytes)) != hipSuccess) return e;
+    return set_lds_limit<OpF32, 64>(max_lds_bytes);
 }
 
 hipError_t launch_expert(const ExpertParams &p, int dtype, int grid, size_t lds_bytes,
                          hipStream_t s) {
-    if (dtype == 1) expert_kernel<OpBF16><<<grid, kExpertThreads, lds_bytes, s>>>(p);
-    else expert_kernel<OpF32><<<grid, kExpertThreads, lds_bytes, s>>>(p);
+    if (dtype == 1) {
+        if (p.s == 64) expert_kernel<OpBF16, 64><<<grid, kExpertThreads, lds_bytes, s>>>(p);
+        else if (p.s == 32) expert_kernel<OpBF16, 32><<<grid, kExpertThreads, lds_bytes, s>>>(p);
+        else return hipErrorInvalidValue;
+    } else {
+        if (p.s == 64) expert_kernel<OpF32, 64><<<grid, kExpertThreads, lds_bytes, s>>>(p);
+        else if (p.s == 32) expert_kernel<OpF32, 32><<<grid, kExpertThreads, lds_bytes, s>>>(p);
+        else if (p.s == 16) expert_kernel<OpF32, 16><<<grid, kExpertThreads, lds_bytes, s>>>(p);
+        else return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineParams &p, hipStream_t s) {
-    const int hchunks = (p.H / 4 + 255) / 256;
-    combine_kernel<<<hchunks * p.T, 256, 0, s>>>(p);
+    combine_kernel<<<((p.H + 255) / 256) * p.T, 64, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -61,9 +61,36 @@ struct ExpertParams {
     int x_stride;        // LDS row stride of the x tile in elements
 };
 
+// Split expert stage (T <= 256): gate/up + SwiGLU into h, then down + weighted sum into y.
+struct GateUpParams {
+    const void *x;
+    const void *gate_up, *sgu;
+    const int32_t *perm;
+    const int4 *groups;
+    const int32_t *num_groups;
+    void *h;             // bf16: planes hi, lo of [slots][Imax]; fp32: [slots][Imax]
+    size_t plane;        // elements from the hi plane to the lo plane
+    int T, H, E, I, Is, Imax;
+    int S;               // slices of Imax (units per group)
+    int NG, x_stride;
+};
+
+struct DownParams {
+    const void *down, *sdn;
+    const void *h;
+    size_t plane;
+    const int32_t *perm;
+    const int4 *groups;
+    const int32_t *num_groups;
+    const float *w;      // [T][8]
+    const float *g;      // [T] or nullptr
+    float *ybuf;         // [slots][H]: weighted expert outputs per (token, rank) / shared slot
+    int T, H, E, I, Is, Imax;
+};
+
 struct CombineParams {
     const float *ypart;  // [n_sc][slots][H]
-    const float *w;      // [T][8]
+    const float *w;      // [T][8]; nullptr: the partials already carry their weights
     const float *g;      // [T] or nullptr
     float *y;            // [T][H]
     int T, H, slots, n_sc_routed, n_sc_shared, has_shared;
@@ -72,6 +99,9 @@ struct CombineParams {
 hipError_t launch_router(const RouterParams &p, int dtype, int maxrt, hipStream_t s);
 hipError_t launch_route_small(const SelectParams &sp, const BucketParams &bp, bool do_select,
                               bool do_bucket, hipStream_t s);
+hipError_t launch_route_fused(const RouterParams &rp, const SelectParams &sp,
+                              const BucketParams &bp, bool do_bucket, int *arrivals, int dtype,
+                              hipStream_t s);
 hipError_t launch_select_hist(const SelectParams &sp, const BucketParams &bp, bool do_select,
                               bool do_hist, hipStream_t s);
 hipError_t launch_bucket_scan(const BucketParams &bp, hipStream_t s);
@@ -80,5 +110,9 @@ hipError_t launch_expert(const ExpertParams &p, int dtype, int grid, size_t lds_
                          hipStream_t s);
 hipError_t prepare_expert_kernels(size_t max_lds_bytes);
 hipError_t launch_combine(const CombineParams &p, hipStream_t s);
+hipError_t prepare_split_kernels(size_t gateup_lds, size_t down_lds);
+hipError_t launch_gateup(const GateUpParams &p, int dtype, int sw, int grid, size_t lds,
+                         hipStream_t s);
+hipError_t launch_down(const DownParams &p, int dtype, int grid, size_t lds, hipStream_t s);
 
 }  // namespace moe

@@ -32,6 +32,8 @@ constexpr size_t kAlign = 256;
 constexpr size_t kMaxXTileBytes = 144 * 1024;  // LDS for the expert kernel's x tile
 constexpr size_t kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
 constexpr int kRouterSplit = 8;
+constexpr size_t kStateBytes = 256;
+constexpr int kSplitMaxTokens = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -43,8 +45,11 @@ struct Plan {
     int s = 64, S = 1, SPU = 1, n_sc = 1, n_sc_routed = 1, n_sc_shared = 0, slots = 0;
     int x_stride = 0, grid = 1;
     size_t lds = 0;
-    size_t o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
-           o_hist = 0, o_groups = 0, o_ngroups = 0, o_ypart = 0, total = 0;
+    bool split = false;          // T <= 256: gateup + down kernels instead of expert + combine
+    int Imax = 0, gu_grid = 1, down_grid = 1;
+    size_t gu_lds = 0, down_lds = 0;
+    size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
+           o_hist = 0, o_groups = 0, o_ngroups = 0, o_ypart = 0, o_h = 0, total = 0;
 };
 
 int k_step(int dtype) { return dtype == MOE_BF16 ? 32 : 16; }
@@ -89,6 +94,22 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.n_sc_shared = Is > 0 ? (Is / p.s + p.SPU - 1) / p.SPU : 0;
     p.slots = pairs + (Is > 0 ? T : 0);
     p.lds = (size_t)p.NG * p.x_stride * esz + (size_t)16 * (p.s + 4) * 4;
+    p.Imax = Imax;
+    p.gu_lds = (size_t)p.NG * p.x_stride * esz;
+    p.down_lds = (size_t)16 * (Imax + 16 / esz) * esz * (cfg.dtype == MOE_BF16 ? 2 : 1);
+    p.split = T <= kSplitMaxTokens && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds;
+    {
+        const long d_units = (long)p.max_groups * (H / 64);
+        const long d_cap = (long)c->num_cus * 8;
+        p.down_grid = (int)(d_units < d_cap ? d_units : d_cap);
+        if (p.down_grid < 1) p.down_grid = 1;
+    }
+    {
+        const long gu_units = (long)p.max_groups * p.S;
+        const long gu_cap = (long)c->num_cus * 8;
+        p.gu_grid = (int)(gu_units < gu_cap ? gu_units : gu_cap);
+        if (p.gu_grid < 1) p.gu_grid = 1;
+    }
     const long units = (long)p.max_groups * p.n_sc;
     const long cap = (long)c->num_cus * 4;
     p.grid = (int)(units < cap ? units : cap);
@@ -100,6 +121,7 @@ Plan make_plan(const moe_ctx *c, int T) {
         o = align_up(o + bytes);
         return at;
     };
+    p.o_state = take(kStateBytes);  // arrival counters; zero before the first call, left zero
     p.o_zpart = take((size_t)p.KS * T * c->R * 4);
     p.o_ids = take((size_t)pairs * 4);
     p.o_w = take((size_t)pairs * 4);
@@ -110,7 +132,8 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.o_hist = take((size_t)p.n_chunks * E * 4);
     p.o_groups = take((size_t)p.max_groups * 16);
     p.o_ngroups = take(16);
-    p.o_ypart = take((size_t)p.n_sc * p.slots * H * 4);
+    p.o_ypart = take(p.split ? (size_t)p.slots * H * 4 : (size_t)p.n_sc * p.slots * H * 4);
+    p.o_h = take(p.split ? (size_t)p.slots * Imax * 4 : 0);
     p.total = o;
     return p;
 }
@@ -189,7 +212,14 @@ BucketParams bucket_params(const moe_ctx *c, const Plan &p, char *ws, const int3
     return bp;
 }
 
+RouterParams router_params(const moe_ctx *c, const Plan &p, const void *x, float *zpart);
+
 void enqueue_router(Launcher &L, const moe_ctx *c, const Plan &p, const void *x, float *zpart) {
+    const RouterParams rp = router_params(c, p, x, zpart);
+    L.step("router", [&] { return launch_router(rp, c->cfg.dtype, p.maxrt, L.stream); });
+}
+
+RouterParams router_params(const moe_ctx *c, const Plan &p, const void *x, float *zpart) {
     RouterParams rp{};
     rp.x = x;
     rp.w = c->w.router_w;
@@ -200,7 +230,18 @@ void enqueue_router(Launcher &L, const moe_ctx *c, const Plan &p, const void *x,
     rp.KS = p.KS;
     rp.n_tt = p.n_tt;
     rp.n_rg = p.n_rg;
-    L.step("router", [&] { return launch_router(rp, c->cfg.dtype, p.maxrt, L.stream); });
+    return rp;
+}
+
+// T <= 64 from x: router, selection and (optionally) bucketing in one launch.
+void enqueue_route_fused(Launcher &L, const moe_ctx *c, const Plan &p, const void *x,
+                         float *zpart, const SelectParams &sp, const BucketParams &bp,
+                         bool do_bucket, char *ws) {
+    const RouterParams rp = router_params(c, p, x, zpart);
+    int *arrivals = reinterpret_cast<int *>(ws + p.o_state);
+    L.step("route_fused", [&] {
+        return launch_route_fused(rp, sp, bp, do_bucket, arrivals, c->cfg.dtype, L.stream);
+    });
 }
 
 // Bucketing from ids already in memory (or selection + bucketing when sp is given).
@@ -261,15 +302,79 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
     const float *g_used = g;
     if (!given) {
         float *zpart = reinterpret_cast<float *>(ws + p.o_zpart);
-        enqueue_router(L, c, p, x, zpart);
         const SelectParams sp = select_params(c, p, zpart, p.KS, c->w.router_bias, nullptr, ids,
                                               wts, g);
-        enqueue_dispatch(L, p, &sp, bucket_params(c, p, ws, nullptr, counts, offsets, perm));
+        const BucketParams bp = bucket_params(c, p, ws, nullptr, counts, offsets, perm);
+        if (p.small) {
+            enqueue_route_fused(L, c, p, x, zpart, sp, bp, true, ws);
+        } else {
+            enqueue_router(L, c, p, x, zpart);
+            enqueue_dispatch(L, p, &sp, bp);
+        }
     } else {
         ids_used = ids_in;
         w_used = w_in;
         g_used = gate_in;
         enqueue_dispatch(L, p, nullptr, bucket_params(c, p, ws, ids_in, counts, offsets, perm));
+    }
+    if (p.split) {
+        GateUpParams gp{};
+        gp.x = x;
+        gp.gate_up = c->w.gate_up;
+        gp.sgu = c->w.shared_gate_up;
+        gp.perm = perm;
+        gp.groups = reinterpret_cast<const int4 *>(ws + p.o_groups);
+        gp.num_groups = reinterpret_cast<const int32_t *>(ws + p.o_ngroups);
+        gp.h = ws + p.o_h;
+        gp.plane = (size_t)p.slots * p.Imax;
+        gp.T = T;
+        gp.H = c->cfg.hidden;
+        gp.E = c->cfg.num_experts;
+        gp.I = c->cfg.inter;
+        gp.Is = c->cfg.shared_inter;
+        gp.Imax = p.Imax;
+        gp.S = p.S;
+        gp.NG = p.NG;
+        gp.x_stride = p.x_stride;
+        L.step("gateup", [&] {
+            return launch_gateup(gp, c->cfg.dtype, p.s, p.gu_grid, p.gu_lds, L.stream);
+        });
+        DownParams dp{};
+        dp.down = c->w.down;
+        dp.sdn = c->w.shared_down;
+        dp.h = gp.h;
+        dp.plane = gp.plane;
+        dp.perm = perm;
+        dp.groups = gp.groups;
+        dp.num_groups = gp.num_groups;
+        dp.w = w_used;
+        dp.g = has_shared ? g_used : nullptr;
+        dp.ybuf = reinterpret_cast<float *>(ws + p.o_ypart);
+        dp.T = T;
+        dp.H = c->cfg.hidden;
+        dp.E = c->cfg.num_experts;
+        dp.I = c->cfg.inter;
+        dp.Is = c->cfg.shared_inter;
+        dp.Imax = p.Imax;
+        L.step("down", [&] {
+            return launch_down(dp, c->cfg.dtype, p.down_grid, p.down_lds, L.stream);
+        });
+        CombineParams cp{};
+        cp.ypart = dp.ybuf;
+        cp.w = nullptr;
+        cp.g = nullptr;
+        cp.y = y;
+        cp.T = T;
+        cp.H = c->cfg.hidden;
+        cp.slots = p.slots;
+        cp.n_sc_routed = 1;
+        cp.n_sc_shared = has_shared ? 1 : 0;
+        cp.has_shared = has_shared ? 1 : 0;
+        L.step("combine", [&] { return launch_combine(cp, L.stream); });
+        (void)ids_used;
+        L.finish();
+        if (n_kernels) *n_kernels = L.count;
+        return hip_status(L.err);
     }
     ExpertParams ep{};
     ep.x = x;
@@ -376,6 +481,11 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
         delete c;
         return MOE_ERR_UNSUPPORTED;
     }
+    const Plan ps = make_plan(c, cfg->max_tokens < kSplitMaxTokens ? cfg->max_tokens : kSplitMaxTokens);
+    if (ps.split && prepare_split_kernels(ps.gu_lds, ps.down_lds) != hipSuccess) {
+        delete c;
+        return MOE_ERR_HIP;
+    }
     if (prepare_expert_kernels(p.lds) != hipSuccess) {
         delete c;
         return MOE_ERR_HIP;
@@ -409,9 +519,8 @@ int moe_route(const moe_ctx *c, const void *x, const float *logits_in, int32_t T
     const float *zpart = logits_in;
     int KS = 1;
     const float *bias = nullptr;
+    float *zp = reinterpret_cast<float *>(ws + p.o_zpart);
     if (x) {
-        float *zp = reinterpret_cast<float *>(ws + p.o_zpart);
-        enqueue_router(L, c, p, x, zp);
         zpart = zp;
         KS = p.KS;
         bias = c->w.router_bias;
@@ -419,10 +528,15 @@ int moe_route(const moe_ctx *c, const void *x, const float *logits_in, int32_t T
     const SelectParams sp = select_params(c, p, zpart, KS, bias, logits_out, topk_ids, topk_w,
                                           shared_gate);
     BucketParams bp = bucket_params(c, p, ws, nullptr, nullptr, nullptr, nullptr);
-    if (p.small)
-        L.step("route_small", [&] { return launch_route_small(sp, bp, true, false, stream); });
-    else
-        L.step("select_hist", [&] { return launch_select_hist(sp, bp, true, false, stream); });
+    if (x && p.small) {
+        enqueue_route_fused(L, c, p, x, zp, sp, bp, false, ws);
+    } else {
+        if (x) enqueue_router(L, c, p, x, zp);
+        if (p.small)
+            L.step("route_small", [&] { return launch_route_small(sp, bp, true, false, stream); });
+        else
+            L.step("select_hist", [&] { return launch_select_hist(sp, bp, true, false, stream); });
+    }
     return hip_status(L.err);
 }
 

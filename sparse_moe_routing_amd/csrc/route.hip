@@ -16,11 +16,15 @@
 // top eight; lanes 0..7 decode one winner each and form the softmax over the eight chosen logits
 // (reference point: the top logit), and the shared-expert gate is the sigmoid of score E.
 //
-// Bucketing is a stable counting sort of the T*8 (token, rank) pairs by expert id without
-// atomics: per expert, one thread counts and then writes its pairs in pair order; exclusive
-// scans give the offsets and the expert-group table that drives the expert kernel.
-#include "device_common.h"
-#include "kernels.h"
+// Bucketing is a stable counting sort of the T*8 (token, rank) pairs by expert id, without
+// atomics and without per-expert scans over all pairs. For a chunk of 64 consecutive pairs (one
+// per lane), eight wave ballots of the expert-id bits (plus a validity ballot) describe the
+// chunk completely: AND-ing, for each bit, the ballot or its complement gives the set of lanes
+// holding a given expert. Expert e's count in the chunk is the popcount of that set; a pair's
+// stable rank among the pairs of its expert is its rank inside the set (popcount of the lanes
+// below it) plus the counts of e in the earlier chunks. Exclusive scans over experts give the
+// offsets and the expert-group table that drives the expert kernel.
+#include "router_core.h"
 
 namespace moe {
 
@@ -50,27 +54,56 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
     return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-// Folded logit of score e of token t: partials summed in ks order, then the bias.
-__device__ __forceinline__ float fold_logit(const SelectParams &p, int t, int e) {
-    const size_t pstride = (size_t)p.T * p.R;
-    const float *zp = p.zpart + (size_t)t * p.R + e;
-    float v = zp[0];
-    for (int ks = 1; ks < p.KS; ++ks) v += zp[ks * pstride];
-    if (p.bias) v += p.bias[e];
-    return v;
-}
-
 // Select the top eight of token t with the calling wave; lanes 0..7 write rank `lane`.
 // ids_lds (nullable) receives the eight ids as well.
+// Folding: logit = (((p_0 + p_1) + ...) + p_{KS-1}) + bias, the partials in ks order. All
+// partial loads are issued before the first add; loads past KS re-read partial KS-1 (in bounds)
+// and are dropped by a select. Offsets are 32-bit from a wave-uniform base.
 __device__ void select_token(const SelectParams &p, int t, int lane, int32_t *ids_lds) {
+    constexpr int kMaxKS = 8;
+    const float *zt = p.zpart + (size_t)t * p.R;
+    const int pstride = p.T * p.R;
+    int eo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eo[j] = min(lane + kWave * j, p.E - 1);
+    float part[kMaxKS][4];
+    float gpart[kMaxKS];
+#pragma unroll
+    for (int ks = 0; ks < kMaxKS; ++ks) {
+        const int ko = (ks < p.KS ? ks : p.KS - 1) * pstride;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[ks][j] = zt[ko + eo[j]];
+        gpart[ks] = zt[ko + (p.g ? p.E : 0)];
+    }
+    float bj[4] = {0.f, 0.f, 0.f, 0.f}, bg = 0.f;
+    if (p.bias) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bj[j] = p.bias[eo[j]];
+        bg = p.g ? p.bias[p.E] : 0.f;
+    }
+    float zv[4], zg = gpart[0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) zv[j] = part[0][j];
+#pragma unroll
+    for (int ks = 1; ks < kMaxKS; ++ks) {
+        const bool in = ks < p.KS;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zv[j] = in ? zv[j] + part[ks][j] : zv[j];
+        zg = in ? zg + gpart[ks] : zg;
+    }
+    if (p.bias) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zv[j] += bj[j];
+        zg += bg;
+    }
+
     uint64_t c[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = lane + kWave * j;
         if (e < p.E) {
-            const float v = fold_logit(p, t, e);
-            if (p.logits_out) p.logits_out[(size_t)t * p.R + e] = v;
-            c[j] = ((uint64_t)order_key(v) << 32) | (uint32_t)~(uint32_t)e;
+            if (p.logits_out) p.logits_out[(size_t)t * p.R + e] = zv[j];
+            c[j] = ((uint64_t)order_key(zv[j]) << 32) | (uint32_t)~(uint32_t)e;
         } else {
             c[j] = 0;  // padding ranks below every real expert, NaN included
         }
@@ -118,110 +151,235 @@ __device__ void select_token(const SelectParams &p, int t, int lane, int32_t *id
         if (ids_lds) ids_lds[lane] = id;
     }
     if (p.g && lane == kTopK) {
-        const float zg = fold_logit(p, t, p.E);
         if (p.logits_out) p.logits_out[(size_t)t * p.R + p.E] = zg;
         p.g[t] = 1.0f / (1.0f + expf(-zg));
     }
 }
 
-// Exclusive scan of one int per expert over threads 0..255 (every thread of the block calls it).
-__device__ void scan256(int v, int *buf, int &excl, int &total) {
-    const int tid = threadIdx.x;
-    if (tid < 256) buf[tid] = v;
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-        const int add = (tid < 256 && tid >= d) ? buf[tid - d] : 0;
-        __syncthreads();
-        if (tid < 256) buf[tid] += add;
-        __syncthreads();
-    }
-    excl = (tid < 256 ? buf[tid] : 0) - v;
-    total = buf[255];
-    __syncthreads();
+// ----------------------------------------------------------------------------- bucketing
+constexpr int kChunkTokens = 64;                       // tokens per bucketing chunk
+constexpr int kChunkPairs = kChunkTokens * kTopK;      // 512 pairs
+constexpr int kSubs = kChunkPairs / kWave;             // 8 sub-chunks of 64 pairs (one per wave)
+
+// LDS of the bucketing of one chunk of up to 512 pairs.
+struct BucketShared {
+    alignas(16) int32_t ids[kChunkPairs];  // expert id of each pair (any value outside [0,E): none)
+    uint64_t bits[kSubs][8];               // per sub-chunk: ballot of each expert-id bit
+    uint64_t valid[kSubs];                 // per sub-chunk: ballot of the pairs with a valid id
+    int pre[kSubs][256];                   // count of expert e in the sub-chunks before s
+    int a[256], b[256];                    // per-expert counts / group counts, then their scans
+    int tot[2];
+};
+
+// Lanes of sub-chunk sc whose pair holds expert e.
+__device__ __forceinline__ uint64_t lanes_of(const BucketShared &s, int sc, int e) {
+    uint64_t m = s.valid[sc];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) m &= ((e >> b) & 1) ? s.bits[sc][b] : ~s.bits[sc][b];
+    return m;
 }
 
-// Offsets, counts and the group table from per-expert totals (threads 0..E-1 own an expert).
-__device__ void write_tables(const BucketParams &bp, int cnt, int *buf, int &off_out) {
+// Ballots of the n pairs in s.ids (waves 0..7), then per expert (threads 0..255): the counts
+// of the sub-chunks before each sub-chunk (s.pre) and the total. Every thread calls it.
+__device__ int chunk_counts(BucketShared &s, int n, int E) {
     const int tid = threadIdx.x;
-    const int e = tid;
-    const bool own = e < bp.E;
-    const int c = own ? cnt : 0;
-    int off, total;
-    scan256(c, buf, off, total);
-    const int ng = own ? (c + bp.NG - 1) / bp.NG : 0;
-    int gbase, gtotal;
-    scan256(ng, buf, gbase, gtotal);
-    const int nsh = bp.has_shared ? (bp.T + bp.NG - 1) / bp.NG : 0;
-    if (own) {
-        bp.counts[e] = c;
-        bp.offsets[e] = off;
-        for (int gg = 0; gg < ng; ++gg)
-            bp.groups[nsh + gbase + gg] = make_int4(e, off + gg * bp.NG, min(bp.NG, c - gg * bp.NG), 0);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int nsub = (n + kWave - 1) / kWave;
+    if (wave < nsub) {
+        const int pidx = wave * kWave + lane;
+        const int e = pidx < n ? s.ids[pidx] : -1;
+        const bool ok = e >= 0 && e < E;
+        const uint64_t vb = __ballot(ok);
+        uint64_t bb[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) bb[b] = __ballot(ok && ((e >> b) & 1));
+        if (lane == 0) {
+            s.valid[wave] = vb;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) s.bits[wave][b] = bb[b];
+        }
     }
-    if (tid < nsh) bp.groups[tid] = make_int4(bp.E, tid * bp.NG, min(bp.NG, bp.T - tid * bp.NG), 0);
-    if (tid == 0) {
-        bp.offsets[bp.E] = total;
-        bp.num_groups[0] = nsh + gtotal;
-    }
-    off_out = off;
-}
-
-__device__ __forceinline__ int count_in(const int32_t *ids, int n, int e) {
+    __syncthreads();
     int cnt = 0;
-    for (int p = 0; p < n; ++p) cnt += (ids[p] == e);
+    if (tid < E) {
+        for (int sc = 0; sc < nsub; ++sc) {
+            s.pre[sc][tid] = cnt;
+            cnt += __popcll(lanes_of(s, sc, tid));
+        }
+    }
     return cnt;
 }
 
-// T <= 64: selection and the whole bucketing pass in one block of 1024 threads (16 waves).
-__global__ __launch_bounds__(1024) void route_small_kernel(SelectParams sp, BucketParams bp,
-                                                          int do_select, int do_bucket) {
-    __shared__ int32_t s_ids[64 * kTopK];
-    __shared__ int s_buf[256];
+// Writes perm[base_of(e) + stable rank] = p0 + pair index for every valid pair (waves 0..7).
+// base_of(e) gives the destination of expert e's first pair of this chunk. Needs s.pre, i.e.
+// a block barrier after chunk_counts.
+template <class Base>
+__device__ void chunk_scatter(const BucketShared &s, int n, int E, int p0, int32_t *perm,
+                              Base base_of) {
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int nsub = (n + kWave - 1) / kWave;
+    if (wave < nsub) {
+        const int pidx = wave * kWave + lane;
+        const int e = pidx < n ? s.ids[pidx] : -1;
+        if (e >= 0 && e < E) {
+            const uint64_t m = lanes_of(s, wave, e);
+            const int rank = __popcll(m & ((1ull << lane) - 1ull));
+            perm[base_of(e) + s.pre[wave][e] + rank] = p0 + pidx;
+        }
+    }
+}
+
+// Exclusive scans over experts of s.a and s.b (256 entries each, by wave 0 of the block).
+// Every thread of the block calls it.
+__device__ void scan_experts(BucketShared &s) {
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (tid < kWave) {
+        const int l = tid;
+        int a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] = s.a[4 * l + i];
+            b[i] = s.b[4 * l + i];
+        }
+        const int sa = a[0] + a[1] + a[2] + a[3];
+        const int sb = b[0] + b[1] + b[2] + b[3];
+        int ia = sa, ib = sb;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int ua = __shfl_up(ia, d, kWave);
+            const int ub = __shfl_up(ib, d, kWave);
+            if (l >= d) {
+                ia += ua;
+                ib += ub;
+            }
+        }
+        int ea = ia - sa, eb = ib - sb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s.a[4 * l + i] = ea;
+            s.b[4 * l + i] = eb;
+            ea += a[i];
+            eb += b[i];
+        }
+        if (l == kWave - 1) {
+            s.tot[0] = ia;
+            s.tot[1] = ib;
+        }
+    }
+    __syncthreads();
+}
+
+// Offsets, counts and the group table from per-expert totals (thread e < E owns expert e; its
+// offset ends up in s.a[e]). Every thread calls it.
+__device__ void write_tables(const BucketParams &bp, int cnt, BucketShared &s) {
+    const int tid = threadIdx.x;
+    const bool own = tid < bp.E;
+    const int c = own ? cnt : 0;
+    const int ng = (c + bp.NG - 1) / bp.NG;
+    if (tid < 256) {
+        s.a[tid] = c;
+        s.b[tid] = ng;
+    }
+    scan_experts(s);
+    const int off = tid < 256 ? s.a[tid] : 0;
+    const int gbase = tid < 256 ? s.b[tid] : 0;
+    const int nsh = bp.has_shared ? (bp.T + bp.NG - 1) / bp.NG : 0;
+    if (own) {
+        bp.counts[tid] = c;
+        bp.offsets[tid] = off;
+        for (int gg = 0; gg < ng; ++gg)
+            bp.groups[nsh + gbase + gg] =
+                make_int4(tid, off + gg * bp.NG, min(bp.NG, c - gg * bp.NG), 0);
+    }
+    if (tid < nsh) bp.groups[tid] = make_int4(bp.E, tid * bp.NG, min(bp.NG, bp.T - tid * bp.NG), 0);
+    if (tid == 0) {
+        bp.offsets[bp.E] = s.tot[0];
+        bp.num_groups[0] = nsh + s.tot[1];
+    }
+}
+
+// Selection of T <= 64 tokens (one wave per token, 16 waves) and, optionally, the whole
+// bucketing pass, by one block of 1024 threads.
+__device__ void select_bucket_block(const SelectParams &sp, const BucketParams &bp, bool do_select,
+                                    bool do_bucket, BucketShared &s) {
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int T = do_select ? sp.T : bp.T;
     if (do_select) {
-        for (int t = wave; t < T; t += 16) select_token(sp, t, lane, s_ids + t * kTopK);
+#pragma unroll 1
+        for (int t = wave; t < T; t += 16) select_token(sp, t, lane, s.ids + t * kTopK);
     } else {
-        for (int i = tid; i < T * kTopK; i += blockDim.x) s_ids[i] = bp.ids_in[i];
+        for (int i = tid; i < T * kTopK; i += blockDim.x) s.ids[i] = bp.ids_in[i];
     }
     if (!do_bucket) return;  // uniform over the block
     __syncthreads();
     const int n = T * kTopK;
-    const int e = tid;
-    const int cnt = e < bp.E ? count_in(s_ids, n, e) : 0;
-    int off;
-    write_tables(bp, cnt, s_buf, off);
-    if (e < bp.E && cnt > 0) {
-        int c = 0;
-        for (int p = 0; p < n; ++p)
-            if (s_ids[p] == e) bp.perm[off + c++] = p;
+    const int cnt = chunk_counts(s, n, bp.E);
+    write_tables(bp, cnt, s);  // ends with a barrier; s.a[e] = offset of expert e
+    chunk_scatter(s, n, bp.E, 0, bp.perm, [&](int e) { return s.a[e]; });
+}
+
+// T <= 64 with given ids (or selection from given logits): one block.
+__global__ __launch_bounds__(1024) void route_small_kernel(SelectParams sp, BucketParams bp,
+                                                          int do_select, int do_bucket) {
+    __shared__ BucketShared s;
+    select_bucket_block(sp, bp, do_select != 0, do_bucket != 0, s);
+}
+
+// T <= 64 from x: router units on every wave of the grid; the last block to finish (an arrival
+// counter in the workspace state, reset by that block) folds the partial logits and runs the
+// selection and the bucketing. One launch for the whole routing step.
+template <class Op>
+__global__ __launch_bounds__(1024) void route_fused_kernel(RouterParams rp, SelectParams sp,
+                                                          BucketParams bp, int do_bucket,
+                                                          int *arrivals) {
+    __shared__ BucketShared s;
+    __shared__ int s_last;
+    const int tid = threadIdx.x;
+    router_unit<Op, 1>(rp, blockIdx.x * 16 + (tid >> 6), tid & 63);
+    // The barrier waits for every wave's stores; one device-scope fence then publishes them all.
+    __syncthreads();
+    if (tid == 0) {
+        __threadfence();
+        s_last = atomicAdd(arrivals, 1) == (int)gridDim.x - 1;
+        if (s_last) {
+            __threadfence();  // acquire: the other blocks' partial logits (same CU and L2 for all
+            arrivals[0] = 0;  // the waves of this block); every block has arrived, so reset
+        }
     }
+    __syncthreads();
+    if (!s_last) return;  // uniform over the block
+    select_bucket_block(sp, bp, true, do_bucket != 0, s);
 }
 
 // T > 64, pass 1: per 64-token chunk, selection (optional) and the per-expert histogram.
 __global__ __launch_bounds__(1024) void select_hist_kernel(SelectParams sp, BucketParams bp,
                                                           int do_select, int do_hist) {
-    __shared__ int32_t s_ids[64 * kTopK];
+    __shared__ BucketShared s;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int T = do_select ? sp.T : bp.T;
-    const int t0 = blockIdx.x * 64;
-    const int nt = min(64, T - t0);
+    const int t0 = blockIdx.x * kChunkTokens;
+    const int nt = min(kChunkTokens, T - t0);
     if (do_select) {
-        for (int i = wave; i < nt; i += 16) select_token(sp, t0 + i, lane, s_ids + i * kTopK);
+#pragma unroll 1
+        for (int i = wave; i < nt; i += 16) select_token(sp, t0 + i, lane, s.ids + i * kTopK);
     } else {
-        for (int i = tid; i < nt * kTopK; i += blockDim.x) s_ids[i] = bp.ids_in[(size_t)t0 * kTopK + i];
+        for (int i = tid; i < nt * kTopK; i += blockDim.x)
+            s.ids[i] = bp.ids_in[(size_t)t0 * kTopK + i];
     }
     if (!do_hist) return;
     __syncthreads();
-    if (tid < bp.E) bp.hist[(size_t)blockIdx.x * bp.E + tid] = count_in(s_ids, nt * kTopK, tid);
+    const int cnt = chunk_counts(s, nt * kTopK, bp.E);
+    if (tid < bp.E) bp.hist[(size_t)blockIdx.x * bp.E + tid] = cnt;
 }
 
 // T > 64, pass 2 (one block): per-expert running bases over chunks, counts, offsets, groups.
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketParams bp) {
     __shared__ int s_part[4][256];
-    __shared__ int s_buf[256];
+    __shared__ BucketShared s;
     const int tid = threadIdx.x;
     const int e = tid & 255, quarter = tid >> 8;
     const int per = (bp.n_chunks + 3) / 4;
@@ -241,24 +399,22 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketParams bp) {
         }
     }
     const int cnt = (tid < 256) ? s_part[0][e] + s_part[1][e] + s_part[2][e] + s_part[3][e] : 0;
-    int off;
-    write_tables(bp, cnt, s_buf, off);
+    write_tables(bp, cnt, s);
 }
 
-// T > 64, pass 3: per chunk, every expert writes its pairs at offset + chunk base, in pair order.
-__global__ __launch_bounds__(256) void bucket_scatter_kernel(BucketParams bp) {
-    __shared__ int32_t s_ids[64 * kTopK];
+// T > 64, pass 3: per chunk, every pair goes to offset + chunk base + its stable rank.
+__global__ __launch_bounds__(512) void bucket_scatter_kernel(BucketParams bp) {
+    __shared__ BucketShared s;
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * 64;
-    const int nt = min(64, bp.T - t0);
-    for (int i = tid; i < nt * kTopK; i += blockDim.x) s_ids[i] = bp.ids_in[(size_t)t0 * kTopK + i];
+    const int t0 = blockIdx.x * kChunkTokens;
+    const int nt = min(kChunkTokens, bp.T - t0);
+    for (int i = tid; i < nt * kTopK; i += blockDim.x) s.ids[i] = bp.ids_in[(size_t)t0 * kTopK + i];
     __syncthreads();
-    const int e = tid;
-    if (e >= bp.E) return;
-    int dst = bp.offsets[e] + bp.hist[(size_t)blockIdx.x * bp.E + e];
-    const int p0 = t0 * kTopK;
-    for (int p = 0; p < nt * kTopK; ++p)
-        if (s_ids[p] == e) bp.perm[dst++] = p0 + p;
+    chunk_counts(s, nt * kTopK, bp.E);
+    __syncthreads();
+    const int32_t *chunk_base = bp.hist + (size_t)blockIdx.x * bp.E;
+    chunk_scatter(s, nt * kTopK, bp.E, t0 * kTopK, bp.perm,
+                  [&](int e) { return bp.offsets[e] + chunk_base[e]; });
 }
 
 hipError_t launch_route_small(const SelectParams &sp, const BucketParams &bp, bool do_select,
@@ -267,10 +423,23 @@ hipError_t launch_route_small(const SelectParams &sp, const BucketParams &bp, bo
     return hipGetLastError();
 }
 
+hipError_t launch_route_fused(const RouterParams &rp, const SelectParams &sp,
+                              const BucketParams &bp, bool do_bucket, int *arrivals, int dtype,
+                              hipStream_t s) {
+    const int units = rp.n_tt * rp.KS * rp.n_rg;
+    const int grid = (units + 15) / 16;
+    if (dtype == 1)
+        route_fused_kernel<OpBF16><<<grid, 1024, 0, s>>>(rp, sp, bp, do_bucket ? 1 : 0, arrivals);
+    else
+        route_fused_kernel<OpF32><<<grid, 1024, 0, s>>>(rp, sp, bp, do_bucket ? 1 : 0, arrivals);
+    return hipGetLastError();
+}
+
 hipError_t launch_select_hist(const SelectParams &sp, const BucketParams &bp, bool do_select,
                               bool do_hist, hipStream_t s) {
     const int T = do_select ? sp.T : bp.T;
-    select_hist_kernel<<<(T + 63) / 64, 1024, 0, s>>>(sp, bp, do_select ? 1 : 0, do_hist ? 1 : 0);
+    select_hist_kernel<<<(T + kChunkTokens - 1) / kChunkTokens, 1024, 0, s>>>(
+        sp, bp, do_select ? 1 : 0, do_hist ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -280,7 +449,7 @@ hipError_t launch_bucket_scan(const BucketParams &bp, hipStream_t s) {
 }
 
 hipError_t launch_bucket_scatter(const BucketParams &bp, hipStream_t s) {
-    bucket_scatter_kernel<<<bp.n_chunks, 256, 0, s>>>(bp);
+    bucket_scatter_kernel<<<bp.n_chunks, 512, 0, s>>>(bp);
     return hipGetLastError();
 }
 

@@ -372,15 +372,21 @@ def test_batch_invariance_bitwise():
     y32 = m.forward(x)
     y4 = m.forward(x[:4].contiguous())
     y1 = m.forward(x[7:8].contiguous())
-    big = torch.cat([x] * 12)  # 384 tokens: the large-T launch configuration
+    y200 = m.forward(torch.cat([x] * 7)[:200].contiguous())  # several chunks, the T > 64 routing
+    big = torch.cat([x] * 12)  # 384 tokens: the large-T expert kernels (another summation order)
     y384 = m.forward(big)
     z32, ids32, _, _ = m.route(x=x)
     z4, ids4, _, _ = m.route(x=x[:4].contiguous())
+    z384, ids384, _, _ = m.route(x=big)
     torch.cuda.synchronize()
     assert torch.equal(z32[:4], z4) and torch.equal(ids32[:4], ids4)
+    assert torch.equal(z384[:32], z32) and torch.equal(ids384[352:], ids32)
     assert torch.equal(y32[:4], y4)
     assert torch.equal(y32[7:8], y1)
-    assert torch.equal(y384[:32], y32) and torch.equal(y384[352:], y32)
+    assert torch.equal(y200[:32], y32) and torch.equal(y200[192:200], y32[:8])
+    # across the T = 256 boundary the expert arithmetic is grouped differently: equal to rounding
+    assert torch.allclose(y384[:32], y32, rtol=1e-4, atol=1e-5)
+    assert torch.allclose(y384[352:], y32, rtol=1e-4, atol=1e-5)
 
 
 def test_token_permutation_equivariance():
@@ -415,5 +421,20 @@ def test_call_errors_and_empty():
     assert lib.moe_route(m.ctx, P(t["x"]), P(y), 4, None, P(ids), P(y), P(y), P(ws), ws.numel(),
                          s) == binding.MOE_ERR_INVALID_ARG  # both x and logits
     plan = m.plan(4)
-    assert plan == ["router", "route_small", "expert", "combine"]
+    assert plan == ["route_fused", "gateup", "down", "combine"]
     assert m.plan(8192)[:2] == ["router", "select_hist"]
+    assert m.plan(8192)[-2:] == ["expert", "combine"]
+    assert m.plan(4, routing_given=True) == ["route_small", "gateup", "down", "combine"]
+
+
+def test_workspace_state_left_zero():
+    """The arrival counters at the start of the workspace are zero again after every call."""
+    torch = _torch()
+    layer, m, t = get_layer("decode_b1_t4", max_tokens=8192)
+    ws = m.workspace(32)
+    for T in (4, 32, 1, 7):
+        m.forward(t["x"][:T].contiguous() if T <= 4 else torch.cat([t["x"]] * 8)[:T].contiguous(),
+                  ws=ws)
+        m.route(x=t["x"], ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:256].view(torch.int32).abs().sum()) == 0
