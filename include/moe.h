@@ -62,7 +62,7 @@ typedef enum {
 } moe_dtype;
 
 typedef struct {
-    int32_t hidden;       /* H: multiple of 64, 64..16384 */
+    int32_t hidden;       /* H: 64..16384, a multiple of 64 (fp32) or of 128 (bf16) */
     int32_t num_experts;  /* E: 8..256 */
     int32_t top_k;        /* must be 8 */
     int32_t inter;        /* I: expert intermediate size, multiple of 16, 16..4096 */

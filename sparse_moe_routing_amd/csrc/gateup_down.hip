@@ -5,10 +5,11 @@
 // bandwidth-bound: "RELEASE_NOTES_0.9.0" of the 16 GB ninfer fork, the expert-placement
 // paragraphs). It is split so that each weight matrix is streamed in the order that suits it:
 //
-// gateup_kernel - one block per (expert group of <= 16 tokens, 64-row slice of the intermediate
-//   dimension): the group's x rows are staged in LDS; wave w computes the 16x16 gate tile and
-//   the 16x16 up tile of rows j*SW + 16w .. +16 with MFMA, the weight rows streaming from HBM
-//   straight into the A operand; h = silu(gate) * up is written to the workspace, for bf16 as
+// gateup_kernel - one block per (expert group of <= 16 tokens, 32-row slice of the intermediate
+//   dimension): the group's x rows are staged in LDS; two waves compute the 16x16 gate tiles and
+//   two the 16x16 up tiles of the slice with MFMA, each streaming its 16 weight rows from HBM in
+//   long contiguous runs and reordering them through LDS into operand order;
+//   h = silu(gate) * up is written to the workspace, for bf16 as
 //   two bf16 planes hi = bf16(h) and lo = bf16(h - hi) (so that the bf16 down product keeps ~16
 //   mantissa bits of h), for fp32 as is. Row slot of a (token, rank) pair: t*8 + k; of the
 //   shared expert for token t: T*8 + t.
@@ -31,24 +32,40 @@ __device__ __forceinline__ uint4 lds_load16(const void *p) {
     return *reinterpret_cast<const uint4 *>(p);
 }
 
-template <class Op, int SW>
+// Unit = (expert group, 32-row slice j of the intermediate dimension). Waves 0, 1 own the gate
+// rows j*32 + 16w .. +16, waves 2, 3 the matching up rows. Each wave streams its 16 weight rows in
+// chunks of 16 x 256 bytes: one load instruction reads 256 contiguous bytes of each of 4 rows (long
+// runs per row are what keeps HBM near its streaming rate; the matrix-core operand order would
+// read only 64 bytes per row per instruction). The chunk is written to the wave's own LDS buffer
+// with an XOR swizzle of the 16-byte pieces (row r, piece p at r*256 + ((p ^ r) & 15)*16), so that
+// the operand reads - lane (row i, k-group q) takes piece 4s + q of row i for step s - hit 16
+// distinct bank groups. The up waves hand their 16x16 tiles to the gate waves through LDS, which
+// write h = silu(gate) * up.
+template <class Op>
 __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
     using elem_t = typename Op::elem_t;
-    constexpr int kU = Op::kElemBytes == 2 ? 8 : 4;  // k steps per load batch
-    constexpr int kGuWaves = SW / kTile;
-    static_assert(kGuWaves >= 1 && kGuWaves <= 4, "slice width");
+    constexpr int kSW = 32;                           // intermediate rows per unit
+    constexpr int kPieces = 16;                       // 16-byte pieces per row per chunk
+    constexpr int kChunkElems = kPieces * Op::kPerLane;
+    constexpr int kStepsPerChunk = kPieces / 4;       // 4 k-groups of one piece per step
+    constexpr int kDepth = 2;                         // chunks per load batch (double-buffered)
+    constexpr int kStage = kTile * kPieces * 16;      // 4 KB of LDS per chunk per wave
 
     extern __shared__ __align__(16) unsigned char smem[];
     elem_t *xs = reinterpret_cast<elem_t *>(smem);
+    unsigned char *stage_all = smem + (size_t)p.NG * p.x_stride * sizeof(elem_t);
+    float *xchg = reinterpret_cast<float *>(stage_all + 4 * kDepth * kStage);  // [2][16][16] up tiles
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, q = lane >> 4;
+    unsigned char *stage = stage_all + wave * kDepth * kStage;
     const int nunits = p.num_groups[0] * p.S;
     const int chunks_per_row = p.H / Op::kPerLane;
-    const int nfull = p.H / (kU * Op::kStep);
-    const int rem = nfull * kU * Op::kStep;
+    const int nchunks = p.H / kChunkElems;
     const elem_t *x = reinterpret_cast<const elem_t *>(p.x);
+    // loader lane -> (row, piece) of a chunk: 4 instructions of 4 rows x 256 contiguous bytes
+    const int lrow = lane >> 4, lpiece = lane & 15;
 
     for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
         const int gi = u / p.S, j = u - (u / p.S) * p.S;
@@ -56,9 +73,9 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
         const int e = grp.x, start = grp.y, n = grp.z;
         const bool shared = e == p.E;
         const int Ie = shared ? p.Is : p.I;
-        if (j * SW >= Ie) continue;  // uniform over the block
+        if (j * kSW >= Ie) continue;  // uniform over the block
 
-        __syncthreads();  // the previous unit's readers of xs are done
+        __syncthreads();  // the previous unit's readers of xs / xchg are done
         for (int idx = tid; idx < n * chunks_per_row; idx += kThreads) {
             const int row = idx / chunks_per_row;
             const int c = idx - row * chunks_per_row;
@@ -67,56 +84,66 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
                 load16(x + (size_t)tok * p.H + c * Op::kPerLane);
         }
         __syncthreads();
-        if (wave >= kGuWaves) continue;
 
-        const bool col_ok = col < n;
-        // token columns >= n read row 0 of the x tile: matrix-core columns are independent, so
-        // those columns only produce values that are never stored
-        const int crow = col_ok ? col : 0;
-        const int slot = !col_ok ? 0 : (shared ? p.T * kTopK + start + col : p.perm[start + col]);
         const elem_t *gu = reinterpret_cast<const elem_t *>(shared ? p.sgu : p.gate_up) +
                            (shared ? 0 : (size_t)e * 2 * Ie * p.H);
-        const int i0 = j * SW + wave * kTile;
-        const elem_t *grow = gu + (size_t)(i0 + col) * p.H + q * Op::kPerLane;
-        const elem_t *urow = gu + (size_t)(Ie + i0 + col) * p.H + q * Op::kPerLane;
+        const int wrow0 = (wave < 2 ? 0 : Ie) + j * kSW + (wave & 1) * kTile;  // first weight row
+        const elem_t *src = gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
+        const bool col_ok = col < n;
+        const int crow = col_ok ? col : 0;  // columns >= n repeat column 0 (dropped)
         const elem_t *xrow = xs + crow * p.x_stride + q * Op::kPerLane;
-        f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-        uint4 gA[kU], uA[kU], gB[kU], uB[kU];
-        auto load_gu = [&](uint4(&g)[kU], uint4(&uu)[kU], int b) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+
+        uint4 rA[kDepth][4], rB[kDepth][4];
+        auto load = [&](uint4(&r)[kDepth][4], int c0) {
 #pragma unroll
-            for (int v = 0; v < kU; ++v) {
-                const int kk = (b * kU + v) * Op::kStep;
-                g[v] = load16_stream(grow + kk);
-                uu[v] = load16_stream(urow + kk);
+            for (int d = 0; d < kDepth; ++d)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int c = min(c0 + d, nchunks - 1);  // past the end: re-read, unused
+                    r[d][a] = load16_stream(src + (size_t)(4 * a) * p.H + c * kChunkElems);
+                }
+        };
+        auto consume = [&](const uint4(&r)[kDepth][4], int c0) {
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                if (c0 + d >= nchunks) break;  // uniform
+                unsigned char *buf = stage + d * kStage;
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int rr = 4 * a + lrow;
+                    *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) = r[d][a];
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
+                    const int pc = 4 * s2 + q;
+                    const uint4 av = lds_load16(buf + col * 256 + ((pc ^ col) & 15) * 16);
+                    const uint4 xb = lds_load16(xrow + (c0 + d) * kChunkElems + 4 * s2 * Op::kPerLane);
+                    Op::mma(acc, av, xb);
+                }
             }
         };
-        auto mma_gu = [&](const uint4(&g)[kU], const uint4(&uu)[kU], int b) {
-#pragma unroll
-            for (int v = 0; v < kU; ++v) {
-                const uint4 xb = lds_load16(xrow + (b * kU + v) * Op::kStep);
-                Op::mma(ag, g[v], xb);
-                Op::mma(au, uu[v], xb);
-            }
-        };
-        if (nfull > 0) load_gu(gA, uA, 0);
-        int b = 0;
-        for (; b + 2 <= nfull; b += 2) {
-            load_gu(gB, uB, b + 1);
-            mma_gu(gA, uA, b);
-            if (b + 2 < nfull) load_gu(gA, uA, b + 2);
-            mma_gu(gB, uB, b + 1);
+        load(rA, 0);
+        for (int c0 = 0; c0 < nchunks; c0 += 2 * kDepth) {
+            if (c0 + kDepth < nchunks) load(rB, c0 + kDepth);
+            consume(rA, c0);
+            if (c0 + 2 * kDepth < nchunks) load(rA, c0 + 2 * kDepth);
+            if (c0 + kDepth < nchunks) consume(rB, c0 + kDepth);
         }
-        if (b < nfull) mma_gu(gA, uA, b);
-        for (int kk = rem; kk < p.H; kk += Op::kStep) {  // only when H % (kU*step) != 0
-            const uint4 xb = lds_load16(xrow + kk);
-            Op::mma(ag, load16_stream(grow + kk), xb);
-            Op::mma(au, load16_stream(urow + kk), xb);
+
+        // up waves hand their tiles over; gate waves form h
+        if (wave >= 2) {
+            *reinterpret_cast<f32x4_t *>(xchg + ((wave - 2) * kTile + col) * kTile + 4 * q) = acc;
         }
-        if (!col_ok) continue;
+        __syncthreads();
+        if (wave >= 2 || !col_ok) continue;
+        const f32x4_t up = *reinterpret_cast<const f32x4_t *>(xchg + (wave * kTile + col) * kTile + 4 * q);
+        const int slot = shared ? p.T * kTopK + start + col : p.perm[start + col];
+        const int i0 = j * kSW + wave * kTile;
         // lane holds intermediate rows i0 + 4q + r, r = 0..3, of token column `col`
         float hv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hv[r] = ag[r] / (1.0f + expf(-ag[r])) * au[r];
+        for (int r = 0; r < 4; ++r) hv[r] = acc[r] / (1.0f + expf(-acc[r])) * up[r];
         const size_t off = (size_t)slot * p.Imax + i0 + 4 * q;
         if constexpr (Op::kElemBytes == 2) {
             uint32_t hi[4], lo[4];
@@ -139,21 +166,31 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
 // One block per (expert group, 64 rows of y): wave w multiplies rows r0 + 16w .. +16 of the
 // expert's down weight (Ie contiguous elements each, so the block reads one contiguous 64-row
 // block) by the group's h, staged once per unit in LDS, and writes weight * (Wd h) to the row
-// slot of each of the group's (token, rank) pairs.
+// slot of each of the group's (token, rank) pairs. Weight rows stream as in gateup_kernel: each
+// load instruction reads 256 contiguous bytes of each of 4 rows, and a per-wave LDS buffer with
+// the same XOR swizzle turns 16 x 256-byte chunks into matrix-core operands.
 template <class Op>
 __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
     using elem_t = typename Op::elem_t;
     using h_t = typename Op::elem_t;                // h planes share the operand type
     constexpr int kRowsPerUnit = 64;
-    constexpr int kMaxSteps = 32;                   // Ie / kStep <= 32 loads in flight
+    constexpr int kPieces = 16;
+    constexpr int kChunkElems = kPieces * Op::kPerLane;
+    constexpr int kStepsPerChunk = kPieces / 4;
+    constexpr int kBatch = 4;                       // chunks loaded together (16 KB per wave)
+    constexpr int kStage = kTile * kPieces * 16;    // 4 KB of LDS per wave
     extern __shared__ __align__(16) unsigned char smem[];
     const int hstride = p.Imax + 16 / Op::kElemBytes;  // padded row stride of the h tile
     h_t *hs_hi = reinterpret_cast<h_t *>(smem);                 // [16][hstride]
     h_t *hs_lo = hs_hi + (size_t)kTile * hstride;               // bf16 only
+    unsigned char *stage_all = reinterpret_cast<unsigned char *>(
+        hs_hi + (size_t)kTile * hstride * (Op::kElemBytes == 2 ? 2 : 1));
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, q = lane >> 4;
+    const int lrow = lane >> 4, lpiece = lane & 15;
+    unsigned char *stage = stage_all + wave * kStage;
     const int n_rc = p.H / kRowsPerUnit;
     const int nunits = p.num_groups[0] * n_rc;
     const h_t *hg = reinterpret_cast<const h_t *>(p.h);
@@ -164,30 +201,33 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
         const int e = grp.x, start = grp.y, n = grp.z;
         const bool shared = e == p.E;
         const int Ie = shared ? p.Is : p.I;
-        const int nsteps = Ie / Op::kStep;
+        const int nchunks = Ie / kChunkElems;
         const elem_t *dn = reinterpret_cast<const elem_t *>(shared ? p.sdn : p.down) +
                            (shared ? 0 : (size_t)e * p.H * Ie);
-        const int row = rc * kRowsPerUnit + wave * kTile + col;
-        const elem_t *arp = dn + (size_t)row * Ie + q * Op::kPerLane;
-        // the weight stream does not depend on h: issue its first chunk before staging h
-        uint4 a[kMaxSteps];
-        auto load_chunk = [&](int s0) {
+        const elem_t *src =
+            dn + (size_t)(rc * kRowsPerUnit + wave * kTile + lrow) * Ie + lpiece * Op::kPerLane;
+        uint4 a[kBatch][4];
+        auto load = [&](int c0) {
 #pragma unroll
-            for (int st = 0; st < kMaxSteps; ++st)
-                if (s0 + st < nsteps) a[st] = load16_stream(arp + (s0 + st) * Op::kStep);
+            for (int d = 0; d < kBatch; ++d)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int c = min(c0 + d, nchunks - 1);  // past the end: re-read, unused
+                    a[d][r] = load16_stream(src + (size_t)(4 * r) * Ie + c * kChunkElems);
+                }
         };
-        load_chunk(0);
+        load(0);  // the weight stream does not depend on h: start it before staging h
 
         __syncthreads();  // the previous unit's readers of the h tile are done
         const int cpr = Ie / Op::kPerLane;  // 16-byte chunks per h row
         for (int idx = tid; idx < n * cpr; idx += kThreads) {
             const int r = idx / cpr, c = idx - (idx / cpr) * cpr;
             const int slot = shared ? p.T * kTopK + start + r : p.perm[start + r];
-            const size_t src = (size_t)slot * p.Imax + c * Op::kPerLane;
-            *reinterpret_cast<uint4 *>(hs_hi + r * hstride + c * Op::kPerLane) = load16(hg + src);
+            const size_t hsrc = (size_t)slot * p.Imax + c * Op::kPerLane;
+            *reinterpret_cast<uint4 *>(hs_hi + r * hstride + c * Op::kPerLane) = load16(hg + hsrc);
             if constexpr (Op::kElemBytes == 2)
                 *reinterpret_cast<uint4 *>(hs_lo + r * hstride + c * Op::kPerLane) =
-                    load16(hg + p.plane + src);
+                    load16(hg + p.plane + hsrc);
         }
         __syncthreads();
 
@@ -196,14 +236,23 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
         const h_t *bhp = hs_hi + crow * hstride + q * Op::kPerLane;
         const h_t *blp = hs_lo + crow * hstride + q * Op::kPerLane;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < nsteps; s0 += kMaxSteps) {  // one pass unless Ie > kMaxSteps steps
-            if (s0 > 0) load_chunk(s0);
+        for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+            if (c0 > 0) load(c0);
 #pragma unroll
-            for (int st = 0; st < kMaxSteps; ++st) {
-                const int kk = (s0 + st) * Op::kStep;
-                if (s0 + st < nsteps) {  // uniform
-                    Op::mma(acc, a[st], lds_load16(bhp + kk));
-                    if constexpr (Op::kElemBytes == 2) Op::mma(acc, a[st], lds_load16(blp + kk));
+            for (int d = 0; d < kBatch; ++d) {
+                if (c0 + d >= nchunks) break;  // uniform
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int rr = 4 * r + lrow;
+                    *reinterpret_cast<uint4 *>(stage + rr * 256 + ((lpiece ^ rr) & 15) * 16) = a[d][r];
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
+                    const int pc = 4 * s2 + q;
+                    const uint4 av = lds_load16(stage + col * 256 + ((pc ^ col) & 15) * 16);
+                    const int kk = (c0 + d) * kChunkElems + 4 * s2 * Op::kPerLane;
+                    Op::mma(acc, av, lds_load16(bhp + kk));
+                    if constexpr (Op::kElemBytes == 2) Op::mma(acc, av, lds_load16(blp + kk));
                 }
             }
         }
@@ -218,19 +267,16 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
     }
 }
 
-template <class Op, int SW>
-static hipError_t set_gateup_lds(size_t bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_kernel<Op, SW>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
 hipError_t prepare_split_kernels(size_t gateup_lds, size_t down_lds) {
     hipError_t err;
-    if ((err = set_gateup_lds<OpBF16, 32>(gateup_lds)) != hipSuccess) return err;
-    if ((err = set_gateup_lds<OpBF16, 64>(gateup_lds)) != hipSuccess) return err;
-    if ((err = set_gateup_lds<OpF32, 16>(gateup_lds)) != hipSuccess) return err;
-    if ((err = set_gateup_lds<OpF32, 32>(gateup_lds)) != hipSuccess) return err;
-    if ((err = set_gateup_lds<OpF32, 64>(gateup_lds)) != hipSuccess) return err;
+    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_kernel<OpBF16>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)gateup_lds)) !=
+        hipSuccess)
+        return err;
+    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_kernel<OpF32>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)gateup_lds)) !=
+        hipSuccess)
+        return err;
     if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&down_kernel<OpBF16>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)down_lds)) !=
         hipSuccess)
@@ -239,20 +285,14 @@ hipError_t prepare_split_kernels(size_t gateup_lds, size_t down_lds) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)down_lds);
 }
 
-hipError_t launch_gateup(const GateUpParams &p, int dtype, int sw, int grid, size_t lds,
-                         hipStream_t s) {
-    if (dtype == 1) {
-        if (sw == 64) gateup_kernel<OpBF16, 64><<<grid, kThreads, lds, s>>>(p);
-        else if (sw == 32) gateup_kernel<OpBF16, 32><<<grid, kThreads, lds, s>>>(p);
-        else return hipErrorInvalidValue;
-    } else {
-        if (sw == 64) gateup_kernel<OpF32, 64><<<grid, kThreads, lds, s>>>(p);
-        else if (sw == 32) gateup_kernel<OpF32, 32><<<grid, kThreads, lds, s>>>(p);
-        else if (sw == 16) gateup_kernel<OpF32, 16><<<grid, kThreads, lds, s>>>(p);
-        else return hipErrorInvalidValue;
-    }
+hipError_t launch_gateup(const GateUpParams &p, int dtype, int grid, size_t lds, hipStream_t s) {
+    if (dtype == 1) gateup_kernel<OpBF16><<<grid, kThreads, lds, s>>>(p);
+    else gateup_kernel<OpF32><<<grid, kThreads, lds, s>>>(p);
     return hipGetLastError();
 }
+
+size_t gateup_stage_bytes() { return 4 * 2 * 4096 + 2 * 16 * 16 * 4; }
+size_t down_stage_bytes() { return 4 * 4096; }
 
 hipError_t launch_down(const DownParams &p, int dtype, int grid, size_t lds, hipStream_t s) {
     if (dtype == 1) down_kernel<OpBF16><<<grid, kThreads, lds, s>>>(p);

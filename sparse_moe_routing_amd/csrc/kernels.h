@@ -71,7 +71,7 @@ struct GateUpParams {
     void *h;             // bf16: planes hi, lo of [slots][Imax]; fp32: [slots][Imax]
     size_t plane;        // elements from the hi plane to the lo plane
     int T, H, E, I, Is, Imax;
-    int S;               // slices of Imax (units per group)
+    int S;               // 32-row slices of Imax (units per group)
     int NG, x_stride;
 };
 
@@ -111,8 +111,9 @@ hipError_t launch_expert(const ExpertParams &p, int dtype, int grid, size_t lds_
 hipError_t prepare_expert_kernels(size_t max_lds_bytes);
 hipError_t launch_combine(const CombineParams &p, hipStream_t s);
 hipError_t prepare_split_kernels(size_t gateup_lds, size_t down_lds);
-hipError_t launch_gateup(const GateUpParams &p, int dtype, int sw, int grid, size_t lds,
-                         hipStream_t s);
+hipError_t launch_gateup(const GateUpParams &p, int dtype, int grid, size_t lds, hipStream_t s);
+size_t gateup_stage_bytes();  // LDS of gateup_kernel beyond its x tile
+size_t down_stage_bytes();    // LDS of down_kernel beyond its h tile
 hipError_t launch_down(const DownParams &p, int dtype, int grid, size_t lds, hipStream_t s);
 
 }  // namespace moe

@@ -46,7 +46,7 @@ struct Plan {
     int x_stride = 0, grid = 1;
     size_t lds = 0;
     bool split = false;          // T <= 256: gateup + down kernels instead of expert + combine
-    int Imax = 0, gu_grid = 1, down_grid = 1;
+    int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;
     size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
            o_hist = 0, o_groups = 0, o_ngroups = 0, o_ypart = 0, o_h = 0, total = 0;
@@ -95,9 +95,14 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.slots = pairs + (Is > 0 ? T : 0);
     p.lds = (size_t)p.NG * p.x_stride * esz + (size_t)16 * (p.s + 4) * 4;
     p.Imax = Imax;
-    p.gu_lds = (size_t)p.NG * p.x_stride * esz;
-    p.down_lds = (size_t)16 * (Imax + 16 / esz) * esz * (cfg.dtype == MOE_BF16 ? 2 : 1);
-    p.split = T <= kSplitMaxTokens && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds;
+    p.gu_lds = (size_t)p.NG * p.x_stride * esz + gateup_stage_bytes();
+    p.gu_S = Imax / 32;
+    p.down_lds = (size_t)16 * (Imax + 16 / esz) * esz * (cfg.dtype == MOE_BF16 ? 2 : 1) +
+                 down_stage_bytes();
+    // the split kernels stream weight rows in chunks of 16 x 16 bytes (128 bf16 / 64 fp32)
+    const int chunk = cfg.dtype == MOE_BF16 ? 128 : 64;
+    p.split = T <= kSplitMaxTokens && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds &&
+              I % chunk == 0 && Is % chunk == 0;
     {
         const long d_units = (long)p.max_groups * (H / 64);
         const long d_cap = (long)c->num_cus * 8;
@@ -105,7 +110,7 @@ Plan make_plan(const moe_ctx *c, int T) {
         if (p.down_grid < 1) p.down_grid = 1;
     }
     {
-        const long gu_units = (long)p.max_groups * p.S;
+        const long gu_units = (long)p.max_groups * (Imax / 32);
         const long gu_cap = (long)c->num_cus * 8;
         p.gu_grid = (int)(gu_units < gu_cap ? gu_units : gu_cap);
         if (p.gu_grid < 1) p.gu_grid = 1;
@@ -333,11 +338,11 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         gp.I = c->cfg.inter;
         gp.Is = c->cfg.shared_inter;
         gp.Imax = p.Imax;
-        gp.S = p.S;
+        gp.S = p.gu_S;
         gp.NG = p.NG;
         gp.x_stride = p.x_stride;
         L.step("gateup", [&] {
-            return launch_gateup(gp, c->cfg.dtype, p.s, p.gu_grid, p.gu_lds, L.stream);
+            return launch_gateup(gp, c->cfg.dtype, p.gu_grid, p.gu_lds, L.stream);
         });
         DownParams dp{};
         dp.down = c->w.down;
@@ -444,6 +449,7 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
     if (cfg->top_k != 8) return MOE_ERR_UNSUPPORTED;
     if (cfg->num_experts < 8 || cfg->num_experts > 256) return MOE_ERR_UNSUPPORTED;
     if (cfg->hidden < 64 || cfg->hidden > 16384 || cfg->hidden % 64) return MOE_ERR_UNSUPPORTED;
+    if (cfg->dtype == MOE_BF16 && cfg->hidden % 128) return MOE_ERR_UNSUPPORTED;
     if (!valid_inter(cfg->inter, cfg->dtype)) return MOE_ERR_UNSUPPORTED;
     if (cfg->shared_inter != 0 && !valid_inter(cfg->shared_inter, cfg->dtype))
         return MOE_ERR_UNSUPPORTED;

@@ -422,6 +422,8 @@ def test_call_errors_and_empty():
                          s) == binding.MOE_ERR_INVALID_ARG  # both x and logits
     plan = m.plan(4)
     assert plan == ["route_fused", "gateup", "down", "combine"]
+    tiny = get_layer("tiny_fp32_t4")[1]  # I = 32 is below the split kernels' row chunk
+    assert tiny.plan(4) == ["route_fused", "expert", "combine"]
     assert m.plan(8192)[:2] == ["router", "select_hist"]
     assert m.plan(8192)[-2:] == ["expert", "combine"]
     assert m.plan(4, routing_given=True) == ["route_small", "gateup", "down", "combine"]
