@@ -31,7 +31,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxXTileBytes = 144 * 1024;  // LDS for the expert kernel's x tile
 constexpr size_t kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
-constexpr int kRouterSplit = 8;
+constexpr int kRouterSplit = 4;  // the quarters of router_core.h
 constexpr size_t kStateBytes = 256;
 constexpr int kSplitMaxTokens = 256;
 
@@ -52,7 +52,6 @@ struct Plan {
            o_hist = 0, o_groups = 0, o_ngroups = 0, o_ypart = 0, o_h = 0, total = 0;
 };
 
-int k_step(int dtype) { return dtype == MOE_BF16 ? 32 : 16; }
 int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
 Plan make_plan(const moe_ctx *c, int T) {
@@ -63,13 +62,9 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.small = T <= 64;
     const int n_rt = (c->R + 15) / 16;
     p.n_tt = (T + 15) / 16;
-    // Router K split: 8 partial sums per logit (fewer only when H has fewer k steps). The split
-    // is the same for every T, so a token's logits do not depend on the batch it comes in.
-    p.KS = 1;
-    {
-        const int ksteps = H / k_step(cfg.dtype);
-        while (p.KS < kRouterSplit && ksteps % (p.KS * 2) == 0) p.KS *= 2;
-    }
+    // Router: four partial sums per logit for every T (the summation order is fixed, so a
+    // token's logits do not depend on the batch it comes in).
+    p.KS = kRouterSplit;
     p.maxrt = T > 256 ? 4 : 1;
     p.n_rg = (n_rt + p.maxrt - 1) / p.maxrt;
     // bucketing and expert groups

@@ -58,9 +58,9 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
 // ids_lds (nullable) receives the eight ids as well.
 // Folding: logit = (((p_0 + p_1) + ...) + p_{KS-1}) + bias, the partials in ks order. All
 // partial loads are issued before the first add; loads past KS re-read partial KS-1 (in bounds)
-// and are dropped by a select. Offsets are 32-bit from a wave-uniform base.
+// and are dropped by a select (KS <= 4). Offsets are 32-bit from a wave-uniform base.
 __device__ void select_token(const SelectParams &p, int t, int lane, int32_t *ids_lds) {
-    constexpr int kMaxKS = 8;
+    constexpr int kMaxKS = kQuarters;
     const float *zt = p.zpart + (size_t)t * p.R;
     const int pstride = p.T * p.R;
     int eo[4];
@@ -328,17 +328,19 @@ __global__ __launch_bounds__(1024) void route_small_kernel(SelectParams sp, Buck
     select_bucket_block(sp, bp, do_select != 0, do_bucket != 0, s);
 }
 
-// T <= 64 from x: router units on every wave of the grid; the last block to finish (an arrival
-// counter in the workspace state, reset by that block) folds the partial logits and runs the
-// selection and the bucketing. One launch for the whole routing step.
+// T <= 64 from x: one block per (token tile, row tile, quarter) computes that quarter's partial
+// logits; the last block to finish (an arrival counter in the workspace state, reset by that
+// block) folds the partial logits and runs the selection and the bucketing. One launch for the
+// whole routing step, with the 1 MiB router read spread over 4 * 17 blocks (T <= 16).
 template <class Op>
 __global__ __launch_bounds__(1024) void route_fused_kernel(RouterParams rp, SelectParams sp,
                                                           BucketParams bp, int do_bucket,
                                                           int *arrivals) {
     __shared__ BucketShared s;
+    __shared__ float red[16 * 256];
     __shared__ int s_last;
     const int tid = threadIdx.x;
-    router_unit<Op, 1>(rp, blockIdx.x * 16 + (tid >> 6), tid & 63);
+    router_quarter_block<Op>(rp, blockIdx.x, red);
     // The barrier waits for every wave's stores; one device-scope fence then publishes them all.
     __syncthreads();
     if (tid == 0) {
@@ -426,8 +428,7 @@ hipError_t launch_route_small(const SelectParams &sp, const BucketParams &bp, bo
 hipError_t launch_route_fused(const RouterParams &rp, const SelectParams &sp,
                               const BucketParams &bp, bool do_bucket, int *arrivals, int dtype,
                               hipStream_t s) {
-    const int units = rp.n_tt * rp.KS * rp.n_rg;
-    const int grid = (units + 15) / 16;
+    const int grid = rp.n_tt * ((rp.R + kTile - 1) / kTile) * kQuarters;
     if (dtype == 1)
         route_fused_kernel<OpBF16><<<grid, 1024, 0, s>>>(rp, sp, bp, do_bucket ? 1 : 0, arrivals);
     else

@@ -1,13 +1,22 @@
-// router_core.h - one router unit (a wave's share of the router logits) on the matrix cores.
+// router_core.h - router logits on the matrix cores, in one fixed summation order.
 //
 // The router is a [R x H] weight times the [H x T] activations (R = E experts plus the shared
-// gate row). A wave owns one unit = (16-token tile, K range, group of up to MAXRT 16-row tiles)
-// and accumulates fp32 16x16 tiles with MFMA; no LDS is needed because every weight fragment is
-// used by exactly one instruction and the activation fragment is reused across the wave's row
-// tiles from registers. The K dimension is split KS ways so that enough waves stream the 1 MiB
-// router at decode sizes; the selection folds the KS partials in a fixed order. (The page
-// "feat(windows): integrate upstream Qwen3.8 DFlash2 support - #8" describes the same split for
-// its S1 kernel: four partial sums per score over 1028 blocks, folded by S2.)
+// gate row), computed on 16x16 (row, token) tiles with MFMA. The K dimension (H, in MFMA steps
+// of 32 bf16 / 16 fp32 elements) is cut into kQuarters quarters of Sq steps, and each quarter
+// into up to kChains contiguous runs of Sw = ceil(Sq / kChains) steps. A run is one MFMA
+// accumulation chain; a quarter's partial logit is the sum of its runs' tiles in run order; the
+// selection later adds the four partials in order and then the bias. Every kernel that produces
+// logits uses exactly this order, so a token's logits - and therefore its routing - do not
+// depend on the batch it is in or on which kernel computed them.
+//
+// Two ways to evaluate it:
+//   router_quarter_block - 16 waves of a block compute the runs of one (token tile, row tile,
+//     quarter) in parallel and add them through LDS (decode sizes: the 1 MiB router is spread
+//     over many CUs).
+//   router_unit - one wave computes a quarter for up to MAXRT row tiles, running the runs one
+//     after the other (large T).
+// (The page "feat(windows): integrate upstream Qwen3.8 DFlash2 support - #8" describes a K split
+// for its S1 kernel as well: four partial sums per score, folded by S2.)
 #pragma once
 
 #include "device_common.h"
@@ -15,75 +24,156 @@
 
 namespace moe {
 
-// One router unit per wave: unit u = (16-token tile, K range, group of MAXRT 16-row tiles).
-// Waves with u >= the unit count do nothing (callers may place a block barrier after this).
+constexpr int kQuarters = 4;   // partial logits per score
+constexpr int kChains = 16;    // accumulation runs per quarter
+
+struct RouterGeom {
+    int Sq, Sw, nchains;
+    __device__ RouterGeom(int H, int kstep) {
+        Sq = H / kstep / kQuarters;
+        Sw = (Sq + kChains - 1) / kChains;
+        nchains = (Sq + Sw - 1) / Sw;
+    }
+};
+
+// One run: tile += sum over steps [s0, s1) of W[rows] . x[tokens] (MFMA chain), where `wrow` and
+// `xrow` point at the lane's row / token with the lane's k-group offset already applied.
+// Out-of-range rows and tokens read clamped addresses and are zeroed by `wok` / `tok_ok`.
+template <class Op, int MAXRT>
+__device__ __forceinline__ void router_run(f32x4_t (&ch)[MAXRT], const typename Op::elem_t *xrow,
+                                           const typename Op::elem_t *const (&wrow)[MAXRT],
+                                           const bool (&wok)[MAXRT], bool tok_ok, int nrt_here,
+                                           int s0, int s1) {
+    const uint4 zero = {0u, 0u, 0u, 0u};
+    constexpr int kBatch = 8;  // steps whose loads are issued together
+    for (int b0 = s0; b0 < s1; b0 += kBatch) {
+        uint4 xb[kBatch], wa[kBatch][MAXRT];
+#pragma unroll
+        for (int v = 0; v < kBatch; ++v) {
+            const int st = min(b0 + v, s1 - 1);  // past the end: re-read, unused
+            xb[v] = load16(xrow + st * Op::kStep);
+#pragma unroll
+            for (int j = 0; j < MAXRT; ++j) wa[v][j] = load16(wrow[j] + st * Op::kStep);
+        }
+#pragma unroll
+        for (int v = 0; v < kBatch; ++v) {
+            if (b0 + v >= s1) break;  // uniform
+            const uint4 bv = tok_ok ? xb[v] : zero;
+#pragma unroll
+            for (int j = 0; j < MAXRT; ++j)
+                if (j < nrt_here) Op::mma(ch[j], wok[j] ? wa[v][j] : zero, bv);  // uniform j test
+        }
+    }
+}
+
+// Large-T form: wave unit u = (token tile, group of MAXRT row tiles, quarter); writes the
+// quarter's partial logits zpart[quarter][t][r]. Waves with u >= the unit count do nothing.
 template <class Op, int MAXRT>
 __device__ __forceinline__ void router_unit(const RouterParams &p, int u, int lane) {
     using elem_t = typename Op::elem_t;
     const int total = p.n_tt * p.KS * p.n_rg;
     if (u >= total) return;
     const int rg = u % p.n_rg;
-    const int ks = (u / p.n_rg) % p.KS;
+    const int kq = (u / p.n_rg) % p.KS;
     const int tt = u / (p.n_rg * p.KS);
     const int n_rt = (p.R + kTile - 1) / kTile;
     const int rt0 = rg * MAXRT;
-    const int col = lane & 15;
-    const int q = lane >> 4;
+    const int nrt_here = min(MAXRT, n_rt - rt0);
+    const int col = lane & 15, q = lane >> 4;
     const int tok = tt * kTile + col;
     const bool tok_ok = tok < p.T;
-    const int Kc = p.H / p.KS;
-    const int k_begin = ks * Kc;
-    const elem_t *x = reinterpret_cast<const elem_t *>(p.x);
-    const elem_t *w = reinterpret_cast<const elem_t *>(p.w);
-
-    const elem_t *xrow = x + (size_t)(tok_ok ? tok : 0) * p.H;
+    const RouterGeom g(p.H, Op::kStep);
+    const int kbase = kq * g.Sq * Op::kStep + q * Op::kPerLane;
+    const elem_t *xrow = reinterpret_cast<const elem_t *>(p.x) + (size_t)(tok_ok ? tok : 0) * p.H + kbase;
     const elem_t *wrow[MAXRT];
     bool wok[MAXRT];
 #pragma unroll
     for (int j = 0; j < MAXRT; ++j) {
         const int row = (rt0 + j) * kTile + col;
-        wok[j] = (rt0 + j < n_rt) && row < p.R;
-        wrow[j] = w + (size_t)(wok[j] ? row : 0) * p.H;
+        wok[j] = j < nrt_here && row < p.R;
+        wrow[j] = reinterpret_cast<const elem_t *>(p.w) + (size_t)(wok[j] ? row : 0) * p.H + kbase;
     }
-    f32x4_t acc[MAXRT];
-#pragma unroll
-    for (int j = 0; j < MAXRT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
+    // The runs are evaluated one after the other, but the loads of kBatch consecutive steps are
+    // issued together across run boundaries; a run's tile is added to the quarter sum when the
+    // run ends (the first run initialises it), exactly as in router_quarter_block.
     const uint4 zero = {0u, 0u, 0u, 0u};
-    // Loads are unconditional (out-of-range steps, rows and tokens read clamped addresses) and
-    // their values are zeroed by selects, so a batch's loads are all in flight together.
-    constexpr int kBatch = 8;  // k steps whose loads are issued together
-    const int k_end = k_begin + Kc;
-    for (int k0 = k_begin; k0 < k_end; k0 += kBatch * Op::kStep) {
-        uint4 b[kBatch], a[kBatch][MAXRT];
-        bool ok[kBatch];
+    constexpr int kBatch = 8;
+    f32x4_t s[MAXRT], ch[MAXRT];
+#pragma unroll
+    for (int j = 0; j < MAXRT; ++j) ch[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b0 = 0; b0 < g.Sq; b0 += kBatch) {
+        uint4 xb[kBatch], wa[kBatch][MAXRT];
 #pragma unroll
         for (int v = 0; v < kBatch; ++v) {
-            ok[v] = k0 + v * Op::kStep < k_end;
-            const int kk = (ok[v] ? k0 + v * Op::kStep : k_begin) + q * Op::kPerLane;
-            b[v] = load16(xrow + kk);
+            const int st = min(b0 + v, g.Sq - 1);  // past the end: re-read, unused
+            xb[v] = load16(xrow + st * Op::kStep);
 #pragma unroll
-            for (int j = 0; j < MAXRT; ++j) a[v][j] = load16(wrow[j] + kk);
+            for (int j = 0; j < MAXRT; ++j) wa[v][j] = load16(wrow[j] + st * Op::kStep);
         }
 #pragma unroll
         for (int v = 0; v < kBatch; ++v) {
-            const uint4 bv = (ok[v] && tok_ok) ? b[v] : zero;
+            const int st = b0 + v;
+            if (st >= g.Sq) break;  // uniform
+            const uint4 bv = tok_ok ? xb[v] : zero;
 #pragma unroll
-            for (int j = 0; j < MAXRT; ++j) {
-                const uint4 av = wok[j] ? a[v][j] : zero;
-                if (rt0 + j < n_rt) Op::mma(acc[j], av, bv);  // uniform condition
+            for (int j = 0; j < MAXRT; ++j)
+                if (j < nrt_here) Op::mma(ch[j], wok[j] ? wa[v][j] : zero, bv);
+            if ((st + 1) % g.Sw == 0 || st + 1 == g.Sq) {  // run st / Sw ends here (uniform)
+                const bool first = st < g.Sw;
+#pragma unroll
+                for (int j = 0; j < MAXRT; ++j) {
+                    s[j] = first ? ch[j] : s[j] + ch[j];
+                    ch[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
             }
         }
     }
     if (!tok_ok) return;
-    float *out = p.zpart + ((size_t)ks * p.T + tok) * p.R;
+    float *out = p.zpart + ((size_t)kq * p.T + tok) * p.R;
 #pragma unroll
     for (int j = 0; j < MAXRT; ++j) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = (rt0 + j) * kTile + 4 * q + r;
-            if (rt0 + j < n_rt && row < p.R) out[row] = acc[j][r];
+            if (j < nrt_here && row < p.R) out[row] = s[j][r];
         }
+    }
+}
+
+// Decode form: block b = (token tile, row tile, quarter) of 16 waves; wave w computes run w and
+// the runs are added in order through LDS (red: 16 tiles of 256 floats). Every thread of the
+// block calls it; it ends with the partial logits stored (no trailing barrier).
+template <class Op>
+__device__ __forceinline__ void router_quarter_block(const RouterParams &p, int b, float *red) {
+    using elem_t = typename Op::elem_t;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int n_rt = (p.R + kTile - 1) / kTile;
+    const int rt = b % n_rt;
+    const int kq = (b / n_rt) % kQuarters;
+    const int tt = b / (n_rt * kQuarters);
+    const int col = lane & 15, q = lane >> 4;
+    const int tok = tt * kTile + col;
+    const bool tok_ok = tok < p.T;
+    const int row = rt * kTile + col;
+    const bool wok[1] = {row < p.R};
+    const RouterGeom g(p.H, Op::kStep);
+    const int kbase = kq * g.Sq * Op::kStep + q * Op::kPerLane;
+    const elem_t *xrow = reinterpret_cast<const elem_t *>(p.x) + (size_t)(tok_ok ? tok : 0) * p.H + kbase;
+    const elem_t *const wrow[1] = {reinterpret_cast<const elem_t *>(p.w) +
+                                   (size_t)(wok[0] ? row : 0) * p.H + kbase};
+    f32x4_t ch[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    if (wave < g.nchains)
+        router_run<Op, 1>(ch, xrow, wrow, wok, tok_ok, 1, wave * g.Sw, min((wave + 1) * g.Sw, g.Sq));
+    // tile element (row 4q + r, token col) of run `wave`
+    *reinterpret_cast<f32x4_t *>(red + wave * 256 + col * 16 + 4 * q) = ch[0];
+    __syncthreads();
+    if (tid < 256) {
+        const int c = tid >> 4, rr = tid & 15;  // token column, tile row
+        float acc = red[c * 16 + rr];
+        for (int w = 1; w < g.nchains; ++w) acc += red[w * 256 + c * 16 + rr];
+        const int t = tt * kTile + c, r = rt * kTile + rr;
+        if (t < p.T && r < p.R) p.zpart[((size_t)kq * p.T + t) * p.R + r] = acc;
     }
 }
 
