@@ -98,6 +98,37 @@ def kernel_bytes(w, U, name):
     raise KeyError(name)
 
 
+def kernel_sources_hash():
+    """sha256[:16] over the HIP sources, as recorded with the committed counter summaries."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "sparse_moe_routing_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from profiles/pmc_<workload>.txt (FETCH_SIZE + WRITE_SIZE,
+    each scaled by what the counter reads for a plain 256 MiB copy), or None when there is no
+    summary or the kernels have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    sha = None
+    mib = None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 2 and parts[0] == "kernel_sources_sha16":
+            sha = parts[1]
+        if len(parts) >= 6 and parts[0] == "kernel" and parts[1] == f"{kernel}_kernel":
+            mib = float(parts[-1])
+    if sha != kernel_sources_hash() or mib is None:
+        return None
+    return mib * 2 ** 20
+
+
 def cpu_baseline(w, m_t, seconds):
     """The oracle (untuned) on the host: route + forward of whole T-token batches until about
     `seconds` of CPU time have been spent."""
@@ -247,7 +278,8 @@ def main():
         "expert_stage_gbs": {k: v["gbs"] for k, v in stage.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": counter_traffic(w.name, dom),
+                     "algorithmic_bytes": stage[dom]["bytes"], "launch_us": stage[dom]["us"]},
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
