@@ -95,6 +95,8 @@ def kernel_bytes(w, U, name):
         return esz * H * Is + U * esz * H * I + 4 * T * H
     if name == "expert":
         return 3 * esz * H * Is + U * 3 * esz * H * I + esz * T * H
+    if name == "decode":  # the single launch does the whole step
+        return step_bytes(w, U)
     raise KeyError(name)
 
 
@@ -215,24 +217,29 @@ def main():
         sets[si][0].forward(pool[pi], y=y, ws=ws)
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-kernel events recorded on the launch stream
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-              for _ in range(args.steps)]
-    for evs in events:  # torch creates the HIP event on its first record
-        for e in evs:
-            e.record(stream)
-    used = []
+    # timed region: K steps of plain moe_forward calls, synchronized on both sides
+    used = [combo(args.warmup + i) for i in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        si, pi = combo(args.warmup + i)
-        used.append((si, pi))
-        sets[si][0].forward(pool[pi], y=y, ws=ws, events=events[i], stream=stream)
+    for si, pi in used:
+        sets[si][0].forward(pool[pi], y=y, ws=ws, stream=stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / args.steps
     value = args.steps * T / elapsed
+
+    # per-kernel durations: the same K steps again, with HIP events recorded on the launch
+    # stream between the kernels (moe_forward_timed); not part of `value`
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+              for _ in range(args.steps)]
+    for evs in events:  # torch creates the HIP event on its first record
+        for e in evs:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i, (si, pi) in enumerate(used):
+        sets[si][0].forward(pool[pi], y=y, ws=ws, events=events[i], stream=stream)
+    torch.cuda.synchronize()
     per_kernel = {name: [] for name in plan}
     step_ms = []
     for ev in events:
@@ -241,7 +248,7 @@ def main():
         step_ms.append(ev[0].elapsed_time(ev[-1]))
     mean_U = float(np.mean([U[c] for c in used]))
     stage = {}
-    for name in ("gateup", "down", "expert"):
+    for name in ("decode", "gateup", "down", "expert"):
         if name in per_kernel:
             us = float(np.mean(per_kernel[name])) * 1e3
             b = float(np.mean([kernel_bytes(w, U[c], name) for c in used]))

@@ -24,11 +24,12 @@
  * memory. The context BORROWS the weight pointers (nothing is copied); they must stay valid and
  * unchanged while the context is used. The library allocates no device memory: each call takes a
  * caller-provided workspace of at least moe_workspace_bytes(ctx, T) bytes, 256-byte aligned, that
- * the call owns until its kernels finish. The first 256 bytes of a workspace hold arrival
- * counters: they must be zero before the workspace is first used (e.g. allocate it zeroed), and
- * every call leaves them zero again, so a workspace can be reused by later calls on any stream as
- * long as two calls never use it at the same time. The context is immutable after moe_create, so calls on
- * different streams are safe when each uses its own workspace and outputs.
+ * the call owns until its kernels finish. A workspace must be zero-filled before its first use
+ * (e.g. allocate it zeroed): its leading moe_workspace_state_bytes(ctx) bytes hold arrival
+ * counters and work-queue words, and every call, whatever its T, leaves that region zero again,
+ * so a workspace can be reused by later calls on any stream as long as two calls never use it
+ * at the same time. The context is immutable after moe_create, so calls on different
+ * streams are safe when each uses its own workspace and outputs.
  *
  * Errors: arguments are validated on the host before anything is enqueued; a rejected call
  * enqueues nothing and returns a negative moe_status. Unsupported shapes are errors, never a
@@ -93,6 +94,12 @@ void moe_destroy(moe_ctx *ctx);
 /* Bytes of workspace a call with T tokens needs (0 when T <= 0 or ctx is NULL). */
 size_t moe_workspace_bytes(const moe_ctx *ctx, int32_t T);
 
+/* Size of the leading state region of every workspace of ctx (the same for every T; a multiple
+ * of 256; 0 when ctx is NULL). It must be zero before a workspace's first use and every call
+ * leaves it zero. It holds the arrival counters of the kernels whose last block to finish does
+ * the final step of a pass (the routing kernel's selection, the down kernel's combine). */
+size_t moe_workspace_state_bytes(const moe_ctx *ctx);
+
 /* Router logits + top-8 selection + softmax weights + shared gate.
  * Exactly one of x ([T][H], config dtype) and logits_in ([T][R] fp32, final logits: no bias is
  * added) must be non-NULL. Outputs: logits_out [T][R] fp32 (may be NULL; when written it holds
@@ -113,8 +120,8 @@ int moe_bucket(const moe_ctx *ctx, const int32_t *ids_in, int32_t T, int32_t *co
 
 /* The whole layer: y [T][H] fp32 from x [T][H].
  * Routing: ids_in, w_in, gate_in all NULL -> routed internally from x (as moe_route);
- * otherwise ids_in [T][8] and w_in [T][8] are used as given (gate_in [T] required iff I_s > 0),
- * e.g. the output of moe_route called with logits_in. */
+ * otherwise ids_in [T][8] (values in [0, E)) and w_in [T][8] are used as given (gate_in [T]
+ * required iff I_s > 0), e.g. the output of moe_route called with logits_in. */
 int moe_forward(const moe_ctx *ctx, const void *x, int32_t T, const int32_t *ids_in,
                 const float *w_in, const float *gate_in, float *y, void *workspace,
                 size_t ws_bytes, hipStream_t stream);

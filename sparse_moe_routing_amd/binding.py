@@ -21,7 +21,8 @@ MOE_ERR_HIP = -4
 MOE_F32 = 0
 MOE_BF16 = 1
 
-EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_route", "moe_bucket",
+EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_state_bytes",
+           "moe_route", "moe_bucket",
            "moe_forward", "moe_forward_plan", "moe_forward_timed", "moe_status_str")
 
 
@@ -58,6 +59,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_destroy.restype = None
     lib.moe_workspace_bytes.argtypes = [P, I32]
     lib.moe_workspace_bytes.restype = SZ
+    lib.moe_workspace_state_bytes.argtypes = [P]
+    lib.moe_workspace_state_bytes.restype = SZ
     lib.moe_route.argtypes = [P, P, P, I32, P, P, P, P, P, SZ, P]
     lib.moe_route.restype = ctypes.c_int
     lib.moe_bucket.argtypes = [P, P, I32, P, P, P, P, SZ, P]
@@ -138,10 +141,15 @@ class MoeLayer:
     def workspace_bytes(self, T: int) -> int:
         return int(self.lib.moe_workspace_bytes(self.ctx, T))
 
+    def state_bytes(self) -> int:
+        """Size of the workspace's leading state region (zero before the first call, left zero
+        by every call)."""
+        return int(self.lib.moe_workspace_state_bytes(self.ctx))
+
     def workspace(self, T: int, device="cuda"):
         """A workspace for calls of up to T tokens. It starts zeroed: the library keeps arrival
-        counters in its first 256 bytes, which must be zero before the first call and which
-        every call leaves at zero."""
+        counters and work-queue words in its leading state region, which must be zero before the
+        first call and which every call leaves at zero."""
         import torch
         return torch.zeros(max(self.workspace_bytes(T), 256), dtype=torch.uint8, device=device)
 

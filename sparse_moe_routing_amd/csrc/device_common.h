@@ -74,4 +74,35 @@ __device__ __forceinline__ uint4 load16_stream(const void *p) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Device-coherent access for data that one wave writes and a wave on another XCD reads inside the
+// same launch: relaxed agent-scope atomic loads and stores (on gfx950 these carry the device
+// scope bit: stores write through the XCD's L2, loads do not hit a stale L2 line), so a producer
+// publishes by waiting for its stores (vmcnt) before a counter update and the consumer needs no
+// L2 invalidation. Element types of at most 8 bytes.
+template <class T>
+__device__ __forceinline__ T ld_dev(const T *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ void st_dev(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint4 ld_dev16(const void *p) {
+    const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+    const uint64_t a = ld_dev(q), b = ld_dev(q + 1);
+    return uint4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+__device__ __forceinline__ void st_dev16(void *p, uint4 v) {
+    uint64_t *q = reinterpret_cast<uint64_t *>(p);
+    st_dev(q, (uint64_t)v.x | ((uint64_t)v.y << 32));
+    st_dev(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32));
+}
+// Wait until every memory operation this wave issued has completed (its device-scope stores are
+// then visible device-wide); a compiler barrier on both sides keeps them on their side.
+__device__ __forceinline__ void wait_own_stores() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt not waited for
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 }  // namespace moe

@@ -18,9 +18,10 @@
 //   expert's 64 down-weight rows (one contiguous block of 64 * I elements) and the group's h rows
 //   (staged once in LDS) and writes w * (Wd h) for each of the group's (token, rank) pairs into
 //   that pair's row of a [slots][H] buffer (w = the pair's routing weight, or the shared gate).
-//   Every element of the buffer has exactly one writer; the combine kernel then sums a token's
-//   eight ranks in rank order plus its shared slot. No atomics, and a token's bits do not depend
-//   on the batch it came in.
+//   Every element of the buffer has exactly one writer. The last unit to finish a 64-row block
+//   (an arrival count per row block) then sums each token's eight ranks in rank order plus its
+//   shared slot into y. No floating-point atomics, and a token's bits do not depend on the batch
+//   it came in.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -163,6 +164,35 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
     }
 }
 
+// y rows h0 .. h0 + 64 of every token from the weighted per-slot outputs: the eight ranks in
+// rank order, then the shared slot (one float4 of one token per thread and step).
+__device__ void combine_rows(const DownParams &p, int h0, int tid) {
+    const bool has_shared = p.g != nullptr;
+    for (int i = tid; i < p.T * 16; i += kThreads) {
+        const int t = i >> 4;
+        const int h = h0 + (i & 15) * 4;
+        auto ld4 = [](const float *a) {
+            const uint4 b = ld_dev16(a);
+            return make_float4(__uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z),
+                               __uint_as_float(b.w));
+        };
+        float4 v[kTopK + 1];
+#pragma unroll
+        for (int k = 0; k < kTopK; ++k) v[k] = ld4(p.ybuf + (size_t)(t * kTopK + k) * p.H + h);
+        v[kTopK] = has_shared ? ld4(p.ybuf + (size_t)(p.T * kTopK + t) * p.H + h)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < kTopK; ++k) {
+            acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+        }
+        if (has_shared) {
+            acc.x += v[kTopK].x; acc.y += v[kTopK].y; acc.z += v[kTopK].z; acc.w += v[kTopK].w;
+        }
+        *reinterpret_cast<float4 *>(p.y + (size_t)t * p.H + h) = acc;
+    }
+}
+
 // One block per (expert group, 64 rows of y): wave w multiplies rows r0 + 16w .. +16 of the
 // expert's down weight (Ie contiguous elements each, so the block reads one contiguous 64-row
 // block) by the group's h, staged once per unit in LDS, and writes weight * (Wd h) to the row
@@ -182,9 +212,10 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int hstride = p.Imax + 16 / Op::kElemBytes;  // padded row stride of the h tile
     h_t *hs_hi = reinterpret_cast<h_t *>(smem);                 // [16][hstride]
-    h_t *hs_lo = hs_hi + (size_t)kTile * hstride;               // bf16 only
+    h_t *hs_lo = hs_hi + (size_t)p.NG * hstride;                // [NG][hstride], bf16 only
     unsigned char *stage_all = reinterpret_cast<unsigned char *>(
-        hs_hi + (size_t)kTile * hstride * (Op::kElemBytes == 2 ? 2 : 1));
+        hs_hi + (size_t)p.NG * hstride * (Op::kElemBytes == 2 ? 2 : 1));
+    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -192,7 +223,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
     const int lrow = lane >> 4, lpiece = lane & 15;
     unsigned char *stage = stage_all + wave * kStage;
     const int n_rc = p.H / kRowsPerUnit;
-    const int nunits = p.num_groups[0] * n_rc;
+    const int ngroups = p.num_groups[0];
+    const int nunits = ngroups * n_rc;
     const h_t *hg = reinterpret_cast<const h_t *>(p.h);
 
     for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
@@ -259,11 +291,23 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
         if (col_ok) {
             const int slot = shared ? p.T * kTopK + start + col : p.perm[start + col];
             const float wt = shared ? p.g[start + col] : p.w[slot];
-            // lane holds rows 4q + r of the wave's 16 rows for token column col
-            *reinterpret_cast<float4 *>(p.ybuf + (size_t)slot * p.H + rc * kRowsPerUnit +
-                                        wave * kTile + 4 * q) =
-                make_float4(wt * acc[0], wt * acc[1], wt * acc[2], wt * acc[3]);
+            // lane holds rows 4q + r of the wave's 16 rows for token column col; the combine of
+            // this row block may run in another block of this launch: device-coherent store
+            st_dev16(p.ybuf + (size_t)slot * p.H + rc * kRowsPerUnit + wave * kTile + 4 * q,
+                     uint4{__float_as_uint(wt * acc[0]), __float_as_uint(wt * acc[1]),
+                           __float_as_uint(wt * acc[2]), __float_as_uint(wt * acc[3])});
         }
+        // The last unit to finish row block rc (of the num_groups units that write it) sums, for
+        // every token, the eight weighted rank outputs in rank order and then the gated shared
+        // output: the combine, without a kernel of its own.
+        wait_own_stores();
+        __syncthreads();
+        if (tid == 0) {
+            s_last = atomicAdd(p.rb_arrivals + rc, 1) == ngroups - 1;
+            if (s_last) p.rb_arrivals[rc] = 0;  // all units of rc arrived: reset for the next call
+        }
+        __syncthreads();
+        if (s_last) combine_rows(p, rc * kRowsPerUnit, tid);
     }
 }
 

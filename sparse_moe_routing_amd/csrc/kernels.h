@@ -33,7 +33,7 @@ struct BucketParams {
     int T, E;
     int NG;              // tokens per expert group (rows of the expert kernel's x tile)
     int has_shared;      // shared-expert groups come first in the group table
-    int chunk_tokens;    // tokens per chunk of the multi-block path (64)
+    int chunk_tokens;    // tokens per chunk of the multi-block path (16; at most 64)
     int n_chunks;
     const int32_t *ids_in;  // [T][8] when the selection is not run in the same kernel
     int32_t *counts;     // [E]
@@ -85,7 +85,9 @@ struct DownParams {
     const float *w;      // [T][8]
     const float *g;      // [T] or nullptr
     float *ybuf;         // [slots][H]: weighted expert outputs per (token, rank) / shared slot
-    int T, H, E, I, Is, Imax;
+    float *y;            // [T][H]
+    int *rb_arrivals;    // [H / 64] zero at entry; left zero
+    int T, H, E, I, Is, Imax, NG;
 };
 
 struct CombineParams {

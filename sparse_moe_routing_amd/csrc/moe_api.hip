@@ -3,11 +3,14 @@
 // Call sequence of moe_forward (all on the caller's stream, no host synchronisation):
 //   router        partial logits (matrix cores), K split at decode sizes
 //   route_small   T <= 64: fold + top-8 + softmax + gate, then the whole bucketing pass, one block
-//   select_hist   T > 64: per 64-token chunk, fold + top-8 + softmax + gate + expert histogram
+//   select_hist   T > 64: per 16-token chunk, fold + top-8 + softmax + gate + expert histogram
 //   bucket_scan   T > 64: per-expert chunk bases, counts, offsets, expert-group table
 //   bucket_scatter T > 64: the stable scatter of pair indices
-//   expert        gate/up + SwiGLU + down per (expert group, intermediate slice chunk)
-//   combine       weighted sum of the routed partials plus the gated shared partials
+//   gateup        T <= 256: gate/up + SwiGLU into h per (expert group, 32 intermediate rows)
+//   down          T <= 256: down product per (expert group, 64 rows of y), weighted per slot;
+//                 the last unit of each 64-row block sums the slots into y
+//   expert        T > 256: gate/up + SwiGLU + down per (expert group, intermediate slice chunk)
+//   combine       T > 256: weighted sum of the routed partials plus the gated shared partials
 #include <string.h>
 
 #include <new>
@@ -32,7 +35,9 @@ constexpr size_t kAlign = 256;
 constexpr size_t kMaxXTileBytes = 144 * 1024;  // LDS for the expert kernel's x tile
 constexpr size_t kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
 constexpr int kRouterSplit = 4;  // the quarters of router_core.h
-constexpr size_t kStateBytes = 256;
+constexpr int kStateRowBlocks = 64;  // state ints before the per-row-block counters
+// T > 64: tokens per selection / histogram block (one wave per token in a 1024-thread block)
+constexpr int kHistChunk = 16;
 constexpr int kSplitMaxTokens = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -54,6 +59,29 @@ struct Plan {
 
 int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
+int max_groups_for(const moe_ctx *c, int T, int NG) {
+    const int nsh = c->cfg.shared_inter > 0 ? (T + NG - 1) / NG : 0;
+    const int pairs = T * 8;
+    return nsh + (pairs < c->cfg.num_experts ? pairs : c->cfg.num_experts) + pairs / NG + 1;
+}
+
+// Leading state region of every workspace of the context (the same size for every T, so that a
+// workspace reused across token counts keeps it zero): the route kernel's arrival counter, then
+// one arrival counter per 64-row block of y for the down kernel.
+size_t state_bytes(const moe_ctx *c) {
+    return align_up((size_t)(kStateRowBlocks + c->cfg.hidden / 64) * 4);
+}
+
+// Rows of an expert group: up to 16 tokens, fewer when the x tile would not fit in LDS.
+int group_rows(const moe_ctx *c, int T) {
+    const int esz = elem_bytes(c->cfg.dtype);
+    const int x_stride = c->cfg.hidden + 16 / esz;
+    const int ng_lds = (int)(kMaxXTileBytes / ((size_t)x_stride * esz));
+    int NG = T < 16 ? T : 16;
+    if (NG > ng_lds) NG = ng_lds;
+    return NG;
+}
+
 Plan make_plan(const moe_ctx *c, int T) {
     Plan p;
     const moe_config &cfg = c->cfg;
@@ -71,13 +99,10 @@ Plan make_plan(const moe_ctx *c, int T) {
     // x-tile rows: up to 16 tokens, fewer when a row of H elements would not leave room in LDS
     const int esz = elem_bytes(cfg.dtype);
     p.x_stride = H + 16 / esz;
-    const int ng_lds = (int)(kMaxXTileBytes / ((size_t)p.x_stride * esz));
-    p.NG = T < 16 ? T : 16;
-    if (p.NG > ng_lds) p.NG = ng_lds;
-    p.n_chunks = p.small ? 0 : (T + 63) / 64;
-    const int nsh = Is > 0 ? (T + p.NG - 1) / p.NG : 0;
+    p.NG = group_rows(c, T);
+    p.n_chunks = p.small ? 0 : (T + kHistChunk - 1) / kHistChunk;
     const int pairs = T * 8;
-    p.max_groups = nsh + (pairs < E ? pairs : E) + pairs / p.NG + 1;
+    p.max_groups = max_groups_for(c, T, p.NG);
     p.s = c->s;
     const int Imax = I > Is ? I : Is;
     p.S = Imax / p.s;
@@ -92,7 +117,7 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.Imax = Imax;
     p.gu_lds = (size_t)p.NG * p.x_stride * esz + gateup_stage_bytes();
     p.gu_S = Imax / 32;
-    p.down_lds = (size_t)16 * (Imax + 16 / esz) * esz * (cfg.dtype == MOE_BF16 ? 2 : 1) +
+    p.down_lds = (size_t)p.NG * (Imax + 16 / esz) * esz * (cfg.dtype == MOE_BF16 ? 2 : 1) +
                  down_stage_bytes();
     // the split kernels stream weight rows in chunks of 16 x 16 bytes (128 bf16 / 64 fp32)
     const int chunk = cfg.dtype == MOE_BF16 ? 128 : 64;
@@ -121,7 +146,7 @@ Plan make_plan(const moe_ctx *c, int T) {
         o = align_up(o + bytes);
         return at;
     };
-    p.o_state = take(kStateBytes);  // arrival counters; zero before the first call, left zero
+    p.o_state = take(state_bytes(c));  // zero before the first call, left zero by every call
     p.o_zpart = take((size_t)p.KS * T * c->R * 4);
     p.o_ids = take((size_t)pairs * 4);
     p.o_w = take((size_t)pairs * 4);
@@ -200,7 +225,7 @@ BucketParams bucket_params(const moe_ctx *c, const Plan &p, char *ws, const int3
     bp.E = c->cfg.num_experts;
     bp.NG = p.NG;
     bp.has_shared = c->cfg.shared_inter > 0;
-    bp.chunk_tokens = 64;
+    bp.chunk_tokens = kHistChunk;
     bp.n_chunks = p.n_chunks;
     bp.ids_in = ids_in;
     bp.counts = counts;
@@ -350,6 +375,9 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         dp.w = w_used;
         dp.g = has_shared ? g_used : nullptr;
         dp.ybuf = reinterpret_cast<float *>(ws + p.o_ypart);
+        dp.y = y;
+        dp.rb_arrivals = reinterpret_cast<int *>(ws + p.o_state) + kStateRowBlocks;
+        dp.NG = p.NG;
         dp.T = T;
         dp.H = c->cfg.hidden;
         dp.E = c->cfg.num_experts;
@@ -359,18 +387,6 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         L.step("down", [&] {
             return launch_down(dp, c->cfg.dtype, p.down_grid, p.down_lds, L.stream);
         });
-        CombineParams cp{};
-        cp.ypart = dp.ybuf;
-        cp.w = nullptr;
-        cp.g = nullptr;
-        cp.y = y;
-        cp.T = T;
-        cp.H = c->cfg.hidden;
-        cp.slots = p.slots;
-        cp.n_sc_routed = 1;
-        cp.n_sc_shared = has_shared ? 1 : 0;
-        cp.has_shared = has_shared ? 1 : 0;
-        L.step("combine", [&] { return launch_combine(cp, L.stream); });
         (void)ids_used;
         L.finish();
         if (n_kernels) *n_kernels = L.count;
@@ -501,6 +517,8 @@ size_t moe_workspace_bytes(const moe_ctx *ctx, int32_t T) {
     if (!ctx || T <= 0 || T > ctx->cfg.max_tokens) return 0;
     return make_plan(ctx, T).total;
 }
+
+size_t moe_workspace_state_bytes(const moe_ctx *ctx) { return ctx ? state_bytes(ctx) : 0; }
 
 int moe_route(const moe_ctx *c, const void *x, const float *logits_in, int32_t T,
               float *logits_out, int32_t *topk_ids, float *topk_w, float *shared_gate,

@@ -8,11 +8,12 @@
 //   high 32 bits: the fp32 logit mapped monotonically to an unsigned integer, with -0 and +0
 //                 sharing one key and every NaN mapped to 0 (below -inf);
 //   low 32 bits : the complement of the expert id (a lower id gives a larger key).
-// A lane sorts its (up to four) keys, then six xor-exchange levels (partners 1, 2, 4, 8, 16, 32)
-// merge sorted runs of eight: keep the larger of a[i] and partner[7-i] (a bitonic sequence that
-// holds the top eight of the sixteen) and sort it with three compare-exchange stages. That is
-// the page's pairwise merge of sorted per-lane runs, widened from its 32-lane warp (five levels)
-// to the 64-lane wavefront (six levels). After the last level every lane holds the same sorted
+// A lane sorts its (up to four) keys, then six exchange levels - each pairing the two halves of
+// groups of 2, 4, 8, 16, 32, 64 lanes through register-to-register lane moves - merge sorted
+// runs of eight: keep the larger of a[i] and partner[7-i] (a bitonic sequence that holds the top
+// eight of the sixteen) and sort it with three compare-exchange stages. That is the page's
+// pairwise merge of sorted per-lane runs, widened from its 32-lane warp (five levels) to the
+// 64-lane wavefront (six levels). After the last level every lane holds the same sorted
 // top eight; lanes 0..7 decode one winner each and form the softmax over the eight chosen logits
 // (reference point: the top logit), and the shared-expert gate is the sigmoid of score E.
 //
@@ -24,140 +25,12 @@
 // stable rank among the pairs of its expert is its rank inside the set (popcount of the lanes
 // below it) plus the counts of e in the earlier chunks. Exclusive scans over experts give the
 // offsets and the expert-group table that drives the expert kernel.
-#include "router_core.h"
+#include "select_core.h"
 
 namespace moe {
 
-__device__ __forceinline__ uint32_t order_key(float v) {
-    const uint32_t b = __float_as_uint(v);
-    const uint32_t mag = b & 0x7fffffffu;
-    if (mag > 0x7f800000u) return 0u;      // NaN: below every number
-    if (mag == 0u) return 0x80000000u;     // -0 and +0 compare equal
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_value(uint32_t k) {
-    if (k == 0u) return __uint_as_float(0x7fc00000u);
-    return (k & 0x80000000u) ? __uint_as_float(k & 0x7fffffffu) : __uint_as_float(~k);
-}
-
-__device__ __forceinline__ void cex(uint64_t &a, uint64_t &b) {  // a gets the larger key
-    const uint64_t hi = a > b ? a : b;
-    const uint64_t lo = a > b ? b : a;
-    a = hi;
-    b = lo;
-}
-
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-    const int lo = __shfl_xor((int)(uint32_t)v, m, kWave);
-    const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m, kWave);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-// Select the top eight of token t with the calling wave; lanes 0..7 write rank `lane`.
-// ids_lds (nullable) receives the eight ids as well.
-// Folding: logit = (((p_0 + p_1) + ...) + p_{KS-1}) + bias, the partials in ks order. All
-// partial loads are issued before the first add; loads past KS re-read partial KS-1 (in bounds)
-// and are dropped by a select (KS <= 4). Offsets are 32-bit from a wave-uniform base.
-__device__ void select_token(const SelectParams &p, int t, int lane, int32_t *ids_lds) {
-    constexpr int kMaxKS = kQuarters;
-    const float *zt = p.zpart + (size_t)t * p.R;
-    const int pstride = p.T * p.R;
-    int eo[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) eo[j] = min(lane + kWave * j, p.E - 1);
-    float part[kMaxKS][4];
-    float gpart[kMaxKS];
-#pragma unroll
-    for (int ks = 0; ks < kMaxKS; ++ks) {
-        const int ko = (ks < p.KS ? ks : p.KS - 1) * pstride;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) part[ks][j] = zt[ko + eo[j]];
-        gpart[ks] = zt[ko + (p.g ? p.E : 0)];
-    }
-    float bj[4] = {0.f, 0.f, 0.f, 0.f}, bg = 0.f;
-    if (p.bias) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bj[j] = p.bias[eo[j]];
-        bg = p.g ? p.bias[p.E] : 0.f;
-    }
-    float zv[4], zg = gpart[0];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) zv[j] = part[0][j];
-#pragma unroll
-    for (int ks = 1; ks < kMaxKS; ++ks) {
-        const bool in = ks < p.KS;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) zv[j] = in ? zv[j] + part[ks][j] : zv[j];
-        zg = in ? zg + gpart[ks] : zg;
-    }
-    if (p.bias) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) zv[j] += bj[j];
-        zg += bg;
-    }
-
-    uint64_t c[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = lane + kWave * j;
-        if (e < p.E) {
-            if (p.logits_out) p.logits_out[(size_t)t * p.R + e] = zv[j];
-            c[j] = ((uint64_t)order_key(zv[j]) << 32) | (uint32_t)~(uint32_t)e;
-        } else {
-            c[j] = 0;  // padding ranks below every real expert, NaN included
-        }
-    }
-    // sort the lane's four keys, largest first
-    cex(c[0], c[1]);
-    cex(c[2], c[3]);
-    cex(c[0], c[2]);
-    cex(c[1], c[3]);
-    cex(c[1], c[2]);
-    uint64_t r[8] = {c[0], c[1], c[2], c[3], 0, 0, 0, 0};
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        uint64_t o[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = shfl_xor64(r[i], m);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r[i] = r[i] > o[7 - i] ? r[i] : o[7 - i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cex(r[i], r[i + 4]);
-        cex(r[0], r[2]);
-        cex(r[1], r[3]);
-        cex(r[4], r[6]);
-        cex(r[5], r[7]);
-        cex(r[0], r[1]);
-        cex(r[2], r[3]);
-        cex(r[4], r[5]);
-        cex(r[6], r[7]);
-    }
-    uint64_t mine = r[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i)
-        if (lane == i) mine = r[i];
-    const float top = key_value((uint32_t)(r[0] >> 32));
-    const float v = key_value((uint32_t)(mine >> 32));
-    const float ex = expf(v - top);
-    float sum = ex;
-    sum += __shfl_xor(sum, 1, kWave);
-    sum += __shfl_xor(sum, 2, kWave);
-    sum += __shfl_xor(sum, 4, kWave);
-    if (lane < kTopK) {
-        const int id = (int)~(uint32_t)mine;
-        p.ids[(size_t)t * kTopK + lane] = id;
-        p.w[(size_t)t * kTopK + lane] = ex / sum;
-        if (ids_lds) ids_lds[lane] = id;
-    }
-    if (p.g && lane == kTopK) {
-        if (p.logits_out) p.logits_out[(size_t)t * p.R + p.E] = zg;
-        p.g[t] = 1.0f / (1.0f + expf(-zg));
-    }
-}
-
 // ----------------------------------------------------------------------------- bucketing
-constexpr int kChunkTokens = 64;                       // tokens per bucketing chunk
+constexpr int kChunkTokens = 64;                       // most tokens one bucketing block takes
 constexpr int kChunkPairs = kChunkTokens * kTopK;      // 512 pairs
 constexpr int kSubs = kChunkPairs / kWave;             // 8 sub-chunks of 64 pairs (one per wave)
 
@@ -302,6 +175,7 @@ __device__ void write_tables(const BucketParams &bp, int cnt, BucketShared &s) {
 
 // Selection of T <= 64 tokens (one wave per token, 16 waves) and, optionally, the whole
 // bucketing pass, by one block of 1024 threads.
+template <bool kDev = false>
 __device__ void select_bucket_block(const SelectParams &sp, const BucketParams &bp, bool do_select,
                                     bool do_bucket, BucketShared &s) {
     const int tid = threadIdx.x;
@@ -309,7 +183,7 @@ __device__ void select_bucket_block(const SelectParams &sp, const BucketParams &
     const int T = do_select ? sp.T : bp.T;
     if (do_select) {
 #pragma unroll 1
-        for (int t = wave; t < T; t += 16) select_token(sp, t, lane, s.ids + t * kTopK);
+        for (int t = wave; t < T; t += 16) select_token<kDev>(sp, t, lane, s.ids + t * kTopK);
     } else {
         for (int i = tid; i < T * kTopK; i += blockDim.x) s.ids[i] = bp.ids_in[i];
     }
@@ -332,6 +206,9 @@ __global__ __launch_bounds__(1024) void route_small_kernel(SelectParams sp, Buck
 // logits; the last block to finish (an arrival counter in the workspace state, reset by that
 // block) folds the partial logits and runs the selection and the bucketing. One launch for the
 // whole routing step, with the 1 MiB router read spread over 4 * 17 blocks (T <= 16).
+// The partial logits cross blocks inside the launch, so they are stored and loaded device-
+// coherently: a block waits for its own stores before it arrives, and no L2 write-back or
+// invalidation is needed (each would flush or drop an XCD's whole L2).
 template <class Op>
 __global__ __launch_bounds__(1024) void route_fused_kernel(RouterParams rp, SelectParams sp,
                                                           BucketParams bp, int do_bucket,
@@ -340,31 +217,28 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(RouterParams rp, Sele
     __shared__ float red[16 * 256];
     __shared__ int s_last;
     const int tid = threadIdx.x;
-    router_quarter_block<Op>(rp, blockIdx.x, red);
-    // The barrier waits for every wave's stores; one device-scope fence then publishes them all.
+    router_quarter_block<Op, true>(rp, blockIdx.x, red);
+    wait_own_stores();  // every wave: its partial-logit stores are complete
     __syncthreads();
     if (tid == 0) {
-        __threadfence();
         s_last = atomicAdd(arrivals, 1) == (int)gridDim.x - 1;
-        if (s_last) {
-            __threadfence();  // acquire: the other blocks' partial logits (same CU and L2 for all
-            arrivals[0] = 0;  // the waves of this block); every block has arrived, so reset
-        }
+        if (s_last) arrivals[0] = 0;  // every block has arrived: reset for the next call
     }
     __syncthreads();
     if (!s_last) return;  // uniform over the block
-    select_bucket_block(sp, bp, true, do_bucket != 0, s);
+    select_bucket_block<true>(sp, bp, true, do_bucket != 0, s);
 }
 
-// T > 64, pass 1: per 64-token chunk, selection (optional) and the per-expert histogram.
+// T > 64, pass 1: per chunk of chunk_tokens tokens (one wave each), selection (optional) and
+// the per-expert histogram.
 __global__ __launch_bounds__(1024) void select_hist_kernel(SelectParams sp, BucketParams bp,
                                                           int do_select, int do_hist) {
     __shared__ BucketShared s;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int T = do_select ? sp.T : bp.T;
-    const int t0 = blockIdx.x * kChunkTokens;
-    const int nt = min(kChunkTokens, T - t0);
+    const int t0 = blockIdx.x * bp.chunk_tokens;
+    const int nt = min(bp.chunk_tokens, T - t0);
     if (do_select) {
 #pragma unroll 1
         for (int i = wave; i < nt; i += 16) select_token(sp, t0 + i, lane, s.ids + i * kTopK);
@@ -408,8 +282,8 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketParams bp) {
 __global__ __launch_bounds__(512) void bucket_scatter_kernel(BucketParams bp) {
     __shared__ BucketShared s;
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * kChunkTokens;
-    const int nt = min(kChunkTokens, bp.T - t0);
+    const int t0 = blockIdx.x * bp.chunk_tokens;
+    const int nt = min(bp.chunk_tokens, bp.T - t0);
     for (int i = tid; i < nt * kTopK; i += blockDim.x) s.ids[i] = bp.ids_in[(size_t)t0 * kTopK + i];
     __syncthreads();
     chunk_counts(s, nt * kTopK, bp.E);
@@ -439,7 +313,7 @@ hipError_t launch_route_fused(const RouterParams &rp, const SelectParams &sp,
 hipError_t launch_select_hist(const SelectParams &sp, const BucketParams &bp, bool do_select,
                               bool do_hist, hipStream_t s) {
     const int T = do_select ? sp.T : bp.T;
-    select_hist_kernel<<<(T + kChunkTokens - 1) / kChunkTokens, 1024, 0, s>>>(
+    select_hist_kernel<<<(T + bp.chunk_tokens - 1) / bp.chunk_tokens, 1024, 0, s>>>(
         sp, bp, do_select ? 1 : 0, do_hist ? 1 : 0);
     return hipGetLastError();
 }

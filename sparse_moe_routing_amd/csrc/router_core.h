@@ -68,7 +68,8 @@ __device__ __forceinline__ void router_run(f32x4_t (&ch)[MAXRT], const typename 
 
 // Large-T form: wave unit u = (token tile, group of MAXRT row tiles, quarter); writes the
 // quarter's partial logits zpart[quarter][t][r]. Waves with u >= the unit count do nothing.
-template <class Op, int MAXRT>
+// kDev: store them device-coherently (read by another wave of the same launch).
+template <class Op, int MAXRT, bool kDev = false>
 __device__ __forceinline__ void router_unit(const RouterParams &p, int u, int lane) {
     using elem_t = typename Op::elem_t;
     const int total = p.n_tt * p.KS * p.n_rg;
@@ -135,15 +136,19 @@ __device__ __forceinline__ void router_unit(const RouterParams &p, int u, int la
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = (rt0 + j) * kTile + 4 * q + r;
-            if (j < nrt_here && row < p.R) out[row] = s[j][r];
+            if (j < nrt_here && row < p.R) {
+                if constexpr (kDev) st_dev(out + row, s[j][r]);
+                else out[row] = s[j][r];
+            }
         }
     }
 }
 
 // Decode form: block b = (token tile, row tile, quarter) of 16 waves; wave w computes run w and
 // the runs are added in order through LDS (red: 16 tiles of 256 floats). Every thread of the
-// block calls it; it ends with the partial logits stored (no trailing barrier).
-template <class Op>
+// block calls it; it ends with the partial logits stored (no trailing barrier). kDev: stored
+// device-coherently (read by another block of the same launch).
+template <class Op, bool kDev = false>
 __device__ __forceinline__ void router_quarter_block(const RouterParams &p, int b, float *red) {
     using elem_t = typename Op::elem_t;
     const int tid = threadIdx.x;
@@ -173,7 +178,11 @@ __device__ __forceinline__ void router_quarter_block(const RouterParams &p, int 
         float acc = red[c * 16 + rr];
         for (int w = 1; w < g.nchains; ++w) acc += red[w * 256 + c * 16 + rr];
         const int t = tt * kTile + c, r = rt * kTile + rr;
-        if (t < p.T && r < p.R) p.zpart[((size_t)kq * p.T + t) * p.R + r] = acc;
+        if (t < p.T && r < p.R) {
+            float *dst = p.zpart + ((size_t)kq * p.T + t) * p.R + r;
+            if constexpr (kDev) st_dev(dst, acc);
+            else *dst = acc;
+        }
     }
 }
 

@@ -1,0 +1,178 @@
+// select_core.h - per-token top-8 selection on one wave64 (device code shared by the kernels
+// that select). The method and the key encoding are described in route.hip.
+#pragma once
+
+#include "router_core.h"
+
+namespace moe {
+
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t mag = b & 0x7fffffffu;
+    if (mag > 0x7f800000u) return 0u;      // NaN: below every number
+    if (mag == 0u) return 0x80000000u;     // -0 and +0 compare equal
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+    if (k == 0u) return __uint_as_float(0x7fc00000u);
+    return (k & 0x80000000u) ? __uint_as_float(k & 0x7fffffffu) : __uint_as_float(~k);
+}
+
+__device__ __forceinline__ void cex(uint64_t &a, uint64_t &b) {  // a gets the larger key
+    const uint64_t hi = a > b ? a : b;
+    const uint64_t lo = a > b ? b : a;
+    a = hi;
+    b = lo;
+}
+
+// The value of v held by this lane's partner at merge level L (0..5). The partners pair the two
+// halves of every group of 2^(L+1) lanes: lane ^ 1 and lane ^ 2 (DPP quad permutations), the
+// mirror lane within 8 and within 16 lanes (DPP half-row / row mirror), then the other row of a
+// row pair and the other half of the wave (gfx950 permlane swaps). All of them are register-to-
+// register moves: no LDS round trip. A permlane swap returns the lane's own value in one of its
+// two results and the partner's in the other, so their xor with the own value is the partner's.
+template <int L>
+__device__ __forceinline__ uint32_t partner32(uint32_t v) {
+    if constexpr (L == 0) return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, false);
+    else if constexpr (L == 1) return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, false);
+    else if constexpr (L == 2) return __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, false);
+    else if constexpr (L == 3) return __builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, false);
+    else if constexpr (L == 4) {
+        const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return s[0] ^ s[1] ^ v;
+    } else {
+        const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return s[0] ^ s[1] ^ v;
+    }
+}
+
+template <int L>
+__device__ __forceinline__ uint64_t partner64(uint64_t v) {
+    const uint32_t lo = partner32<L>((uint32_t)v), hi = partner32<L>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One merge level: r (sorted, largest first) becomes the sorted top eight of r and the partner's
+// list: max(r[i], partner[7 - i]) is a bitonic sequence holding them, sorted by three stages.
+template <int L>
+__device__ __forceinline__ void merge_level(uint64_t (&r)[8]) {
+    uint64_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = partner64<L>(r[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = r[i] > o[7 - i] ? r[i] : o[7 - i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cex(r[i], r[i + 4]);
+    cex(r[0], r[2]);
+    cex(r[1], r[3]);
+    cex(r[4], r[6]);
+    cex(r[5], r[7]);
+    cex(r[0], r[1]);
+    cex(r[2], r[3]);
+    cex(r[4], r[5]);
+    cex(r[6], r[7]);
+}
+
+// Select the top eight of token t with the calling wave; lanes 0..7 write rank `lane`.
+// ids_lds (nullable) receives the eight ids as well.
+// Folding: logit = (((p_0 + p_1) + ...) + p_{KS-1}) + bias, the partials in ks order. All
+// partial loads are issued before the first add; loads past KS re-read partial KS-1 (in bounds)
+// and are dropped by a select (KS <= 4). Offsets are 32-bit from a wave-uniform base.
+// kDev: partial logits read, and ids / w / g written, device-coherently (producer and consumer
+// waves of the same launch).
+template <bool kDev = false>
+__device__ inline void select_token(const SelectParams &p, int t, int lane, int32_t *ids_lds) {
+    constexpr int kMaxKS = kQuarters;
+    const float *zt = p.zpart + (size_t)t * p.R;
+    const int pstride = p.T * p.R;
+    int eo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eo[j] = min(lane + kWave * j, p.E - 1);
+    float part[kMaxKS][4];
+    float gpart[kMaxKS];
+#pragma unroll
+    for (int ks = 0; ks < kMaxKS; ++ks) {
+        const int ko = (ks < p.KS ? ks : p.KS - 1) * pstride;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[ks][j] = kDev ? ld_dev(zt + ko + eo[j]) : zt[ko + eo[j]];
+        const int gi = ko + (p.g ? p.E : 0);
+        gpart[ks] = kDev ? ld_dev(zt + gi) : zt[gi];
+    }
+    float bj[4] = {0.f, 0.f, 0.f, 0.f}, bg = 0.f;
+    if (p.bias) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bj[j] = p.bias[eo[j]];
+        bg = p.g ? p.bias[p.E] : 0.f;
+    }
+    float zv[4], zg = gpart[0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) zv[j] = part[0][j];
+#pragma unroll
+    for (int ks = 1; ks < kMaxKS; ++ks) {
+        const bool in = ks < p.KS;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zv[j] = in ? zv[j] + part[ks][j] : zv[j];
+        zg = in ? zg + gpart[ks] : zg;
+    }
+    if (p.bias) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zv[j] += bj[j];
+        zg += bg;
+    }
+
+    uint64_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + kWave * j;
+        if (e < p.E) {
+            if (p.logits_out) p.logits_out[(size_t)t * p.R + e] = zv[j];
+            c[j] = ((uint64_t)order_key(zv[j]) << 32) | (uint32_t)~(uint32_t)e;
+        } else {
+            c[j] = 0;  // padding ranks below every real expert, NaN included
+        }
+    }
+    // sort the lane's four keys, largest first
+    cex(c[0], c[1]);
+    cex(c[2], c[3]);
+    cex(c[0], c[2]);
+    cex(c[1], c[3]);
+    cex(c[1], c[2]);
+    uint64_t r[8] = {c[0], c[1], c[2], c[3], 0, 0, 0, 0};
+    merge_level<0>(r);
+    merge_level<1>(r);
+    merge_level<2>(r);
+    merge_level<3>(r);
+    merge_level<4>(r);
+    merge_level<5>(r);
+    uint64_t mine = r[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+        if (lane == i) mine = r[i];
+    const float top = key_value((uint32_t)(r[0] >> 32));
+    const float v = key_value((uint32_t)(mine >> 32));
+    const float ex = expf(v - top);
+    float sum = ex;
+    sum += __shfl_xor(sum, 1, kWave);
+    sum += __shfl_xor(sum, 2, kWave);
+    sum += __shfl_xor(sum, 4, kWave);
+    if (lane < kTopK) {
+        const int id = (int)~(uint32_t)mine;
+        if constexpr (kDev) {
+            st_dev(p.ids + (size_t)t * kTopK + lane, id);
+            st_dev(p.w + (size_t)t * kTopK + lane, ex / sum);
+        } else {
+            p.ids[(size_t)t * kTopK + lane] = id;
+            p.w[(size_t)t * kTopK + lane] = ex / sum;
+        }
+        if (ids_lds) ids_lds[lane] = id;
+    }
+    if (p.g && lane == kTopK) {
+        if (p.logits_out) p.logits_out[(size_t)t * p.R + p.E] = zg;
+        const float gv = 1.0f / (1.0f + expf(-zg));
+        if constexpr (kDev) st_dev(p.g + t, gv);
+        else p.g[t] = gv;
+    }
+}
+
+}  // namespace moe

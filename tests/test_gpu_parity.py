@@ -323,6 +323,80 @@ def test_forward_small_sizes_all_tokens(orc):
         assert_close(y.cpu().numpy()[rows], y_o, f"T={T}")
 
 
+# ----------------------------------------------------------------------------- small-T shapes
+# (dtype, H, E, I, Is, token counts): shapes of the fused routing + split expert path (T <= 64)
+SMALL_SHAPES = [
+    ("bf16", 256, 32, 128, 128, (1, 5, 16, 33, 64)),
+    ("bf16", 384, 16, 256, 0, (3, 64)),        # no shared expert
+    ("bf16", 128, 256, 128, 256, (2, 64)),     # shared expert wider than the routed ones
+    ("f32", 128, 16, 64, 64, (1, 8, 64)),
+]
+
+
+def small_layer(dtype, H, E, I, Is, T, seed):
+    rng = np.random.default_rng(seed)
+
+    def draw(shape, scale):
+        a = (rng.standard_normal(shape) * scale).astype(np.float32)
+        return inputs.f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+    layer = {"num_experts": E, "inter": I, "shared_inter": Is,
+             "router_w": draw((E + (1 if Is else 0), H), H ** -0.5), "router_bias": None,
+             "gate_up": draw((E, 2 * I, H), H ** -0.5), "down": draw((E, H, I), I ** -0.5),
+             "shared_gate_up": draw((2 * Is, H), H ** -0.5) if Is else None,
+             "shared_down": draw((H, Is), Is ** -0.5) if Is else None,
+             "x": draw((T, H), 1.0)}
+    return layer
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: f"{s[0]}-H{s[1]}-E{s[2]}-I{s[3]}-Is{s[4]}")
+def test_small_batch_shapes(orc, shape):
+    """Every output of the small-T path, against the oracle, for several shapes and token counts:
+    from x (the routing checked against the oracle's), and from the oracle's routing."""
+    torch = _torch()
+    dtype, H, E, I, Is, Ts = shape
+    layer = small_layer(dtype, H, E, I, Is, 64, seed=H + E + I + Is)
+    t = binding.device_weights(layer)
+    m = binding.MoeLayer(H, E, I, Is, 64, dtype, t)
+    ws = m.workspace(64)
+    for T in Ts:
+        assert m.plan(T) == ["route_fused", "gateup", "down"]
+        lay = dict(layer)
+        lay["x"] = layer["x"][:T]
+        x = t["x"][:T].contiguous()
+        y = m.forward(x, ws=ws)
+        _, ids, _, _ = m.route(x=x, want_logits=False, ws=ws)
+        z_o = orc.logits(lay["x"], layer["router_w"], None)
+        ids_o, w_o, g_o = orc.select(z_o, E, Is > 0)
+        y2 = m.forward(x, routing=routing_device(ids_o, w_o, g_o), ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:m.state_bytes()].view(torch.int32).abs().sum()) == 0
+        y_o = orc.forward(lay, ids_o, w_o, g_o)
+        assert_close(y2.cpu().numpy(), y_o, f"{shape} T={T} (oracle routing)")
+        same = (ids.cpu().numpy() == ids_o).all(1)
+        assert same.sum() >= T - max(1, T // 50), f"T={T}: routing differs on {T - same.sum()} tokens"
+        assert_close(y.cpu().numpy()[same], y_o[same], f"{shape} T={T} (from x)")
+
+
+def test_fused_and_chunked_routing_agree():
+    """T <= 64 routes in one fused launch, T = 65..256 in the chunked multi-kernel routing: the
+    same token gets the same bits from both (same summation orders), and a given routing gives
+    the same y as the internal one."""
+    torch = _torch()
+    layer, m, t = get_layer("decode_b8_t32", max_tokens=8192)
+    x = t["x"]
+    xs = torch.cat([x] * 3)[:96].contiguous()
+    assert m.plan(64)[0] == "route_fused" and m.plan(96)[0] == "router"
+    y64 = m.forward(xs[:64].contiguous())
+    y96 = m.forward(xs)
+    ids, w, g = m.route(x=xs, want_logits=False)[1:]
+    y64g = m.forward(xs[:64].contiguous(), routing=(ids[:64].contiguous(), w[:64].contiguous(),
+                                                    g[:64].contiguous()))
+    torch.cuda.synchronize()
+    assert torch.equal(y64, y96[:64])
+    assert torch.equal(y64g, y64)
+
+
 # ----------------------------------------------------------------------------- special cases
 def test_dense_expert_reproduces_swiglu():
     """E = 8 identical experts: every token selects all eight, the weights sum to one, so the
@@ -420,23 +494,29 @@ def test_call_errors_and_empty():
         == binding.MOE_ERR_INVALID_ARG  # routing must be all given or all absent
     assert lib.moe_route(m.ctx, P(t["x"]), P(y), 4, None, P(ids), P(y), P(y), P(ws), ws.numel(),
                          s) == binding.MOE_ERR_INVALID_ARG  # both x and logits
-    plan = m.plan(4)
-    assert plan == ["route_fused", "gateup", "down", "combine"]
-    tiny = get_layer("tiny_fp32_t4")[1]  # I = 32 is below the split kernels' row chunk
+    assert m.plan(4) == ["route_fused", "gateup", "down"] and m.plan(64) == m.plan(4)
+    assert m.plan(4, routing_given=True) == ["route_small", "gateup", "down"]
+    tiny = get_layer("tiny_fp32_t4")[1]  # I = 32 is below the weight-row chunk of the split path
     assert tiny.plan(4) == ["route_fused", "expert", "combine"]
+    assert m.plan(65) == ["router", "select_hist", "bucket_scan", "bucket_scatter", "gateup",
+                          "down"]
     assert m.plan(8192)[:2] == ["router", "select_hist"]
     assert m.plan(8192)[-2:] == ["expert", "combine"]
-    assert m.plan(4, routing_given=True) == ["route_small", "gateup", "down", "combine"]
 
 
 def test_workspace_state_left_zero():
-    """The arrival counters at the start of the workspace are zero again after every call."""
+    """The state region at the start of the workspace (arrival counters, work-queue words,
+    flags, the sticky spin-limit word) is zero again after every call, whatever T."""
     torch = _torch()
     layer, m, t = get_layer("decode_b1_t4", max_tokens=8192)
-    ws = m.workspace(32)
-    for T in (4, 32, 1, 7):
-        m.forward(t["x"][:T].contiguous() if T <= 4 else torch.cat([t["x"]] * 8)[:T].contiguous(),
-                  ws=ws)
+    ws = m.workspace(200)
+    n_state = m.state_bytes()
+    assert 0 < n_state <= 64 * 1024 and n_state % 256 == 0
+    xs = torch.cat([t["x"]] * 64)
+    for T in (4, 32, 1, 7, 64, 200, 3):
+        m.forward(xs[:T].contiguous(), ws=ws)
         m.route(x=t["x"], ws=ws)
+        ids, wt, g = m.route(x=xs[:T].contiguous(), want_logits=False, ws=ws)[1:]
+        m.forward(xs[:T].contiguous(), routing=(ids, wt, g), ws=ws)
         torch.cuda.synchronize()
-        assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+        assert int(ws[:n_state].view(torch.int32).abs().sum()) == 0, T
