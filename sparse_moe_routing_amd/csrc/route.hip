@@ -42,6 +42,7 @@ struct BucketShared {
     int pre[kSubs][256];                   // count of expert e in the sub-chunks before s
     int a[256], b[256];                    // per-expert counts / group counts, then their scans
     int tot[2];
+    uint64_t sel[16][kSelScratch];         // selection scratch of each of up to 16 waves
 };
 
 // Lanes of sub-chunk sc whose pair holds expert e.
@@ -183,7 +184,8 @@ __device__ void select_bucket_block(const SelectParams &sp, const BucketParams &
     const int T = do_select ? sp.T : bp.T;
     if (do_select) {
 #pragma unroll 1
-        for (int t = wave; t < T; t += 16) select_token<kDev>(sp, t, lane, s.ids + t * kTopK);
+        for (int t = wave; t < T; t += 16)
+            select_token<kDev>(sp, t, lane, s.ids + t * kTopK, s.sel[wave]);
     } else {
         for (int i = tid; i < T * kTopK; i += blockDim.x) s.ids[i] = bp.ids_in[i];
     }
@@ -241,7 +243,8 @@ __global__ __launch_bounds__(1024) void select_hist_kernel(SelectParams sp, Buck
     const int nt = min(bp.chunk_tokens, T - t0);
     if (do_select) {
 #pragma unroll 1
-        for (int i = wave; i < nt; i += 16) select_token(sp, t0 + i, lane, s.ids + i * kTopK);
+        for (int i = wave; i < nt; i += 16)
+            select_token(sp, t0 + i, lane, s.ids + i * kTopK, s.sel[wave]);
     } else {
         for (int i = tid; i < nt * kTopK; i += blockDim.x)
             s.ids[i] = bp.ids_in[(size_t)t0 * kTopK + i];

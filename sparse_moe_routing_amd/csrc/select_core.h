@@ -79,10 +79,74 @@ __device__ __forceinline__ void merge_level(uint64_t (&r)[8]) {
 // Folding: logit = (((p_0 + p_1) + ...) + p_{KS-1}) + bias, the partials in ks order. All
 // partial loads are issued before the first add; loads past KS re-read partial KS-1 (in bounds)
 // and are dropped by a select (KS <= 4). Offsets are 32-bit from a wave-uniform base.
-// kDev: partial logits read, and ids / w / g written, device-coherently (producer and consumer
-// waves of the same launch).
+// kDev: the partial logits are read device-coherently (written by other blocks of the same
+// launch). The outputs are plain stores: they are read by later launches.
+// Per-wave LDS scratch of select_token: up to 64 candidate keys, then the eight winners.
+constexpr int kSelScratch = kWave + kTopK;
+
+// The eight largest keys of the wave (each lane holds four, sorted), largest first: lane i < 8
+// gets the i-th in `mine`; `top` is the largest on every lane.
+//
+// Most keys cannot be among the eight, so the exact answer is taken from a short candidate list:
+// let v8 be the 8th largest of the lane maxima's value halves (a bitwise search with wave
+// ballots); at least eight keys have a value half >= v8, so every one of the eight winners does
+// too, and only lanes whose maximum reaches v8 - at most eight lanes unless values tie - hold such
+// keys. The candidates are packed into LDS; each one's rank is the number of candidates above it,
+// and a candidate's rank among them is its rank among all keys (every key above a winner is a
+// winner). With more than 64 candidates (heavy ties) the merge network runs instead.
+__device__ __forceinline__ void top8_of_wave(const uint64_t (&c)[4], int lane, uint64_t *scr,
+                                             uint64_t &mine, uint64_t &top) {
+    const uint32_t hmax = (uint32_t)(c[0] >> 32);
+    uint32_t v8 = 0;
+#pragma unroll
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = v8 | (1u << b);
+        if (__popcll(__ballot(hmax >= cand)) >= kTopK) v8 = cand;
+    }
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) n += (uint32_t)(c[j] >> 32) >= v8 ? 1 : 0;
+    const uint64_t b0 = __ballot(n & 1), b1 = __ballot(n & 2), b2 = __ballot(n & 4);
+    const int total = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+    if (total <= kWave) {  // uniform
+        const uint64_t below = (1ull << lane) - 1ull;
+        const int off = __popcll(b0 & below) + 2 * __popcll(b1 & below) + 4 * __popcll(b2 & below);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (j < n) scr[off + j] = c[j];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < total) {
+            const uint64_t key = scr[lane];
+            int rank = 0;
+            for (int k = 0; k < total; ++k) rank += scr[k] > key ? 1 : 0;
+            if (rank < kTopK) scr[kWave + rank] = key;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        mine = scr[kWave + (lane < kTopK ? lane : 0)];
+        top = scr[kWave];
+        return;
+    }
+    uint64_t r[8] = {c[0], c[1], c[2], c[3], 0, 0, 0, 0};
+    merge_level<0>(r);
+    merge_level<1>(r);
+    merge_level<2>(r);
+    merge_level<3>(r);
+    merge_level<4>(r);
+    merge_level<5>(r);
+    mine = r[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+        if (lane == i) mine = r[i];
+    top = r[0];
+}
+
 template <bool kDev = false>
-__device__ inline void select_token(const SelectParams &p, int t, int lane, int32_t *ids_lds) {
+__device__ inline void select_token(const SelectParams &p, int t, int lane, int32_t *ids_lds,
+                                    uint64_t *scr) {
     constexpr int kMaxKS = kQuarters;
     const float *zt = p.zpart + (size_t)t * p.R;
     const int pstride = p.T * p.R;
@@ -138,18 +202,9 @@ __device__ inline void select_token(const SelectParams &p, int t, int lane, int3
     cex(c[0], c[2]);
     cex(c[1], c[3]);
     cex(c[1], c[2]);
-    uint64_t r[8] = {c[0], c[1], c[2], c[3], 0, 0, 0, 0};
-    merge_level<0>(r);
-    merge_level<1>(r);
-    merge_level<2>(r);
-    merge_level<3>(r);
-    merge_level<4>(r);
-    merge_level<5>(r);
-    uint64_t mine = r[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i)
-        if (lane == i) mine = r[i];
-    const float top = key_value((uint32_t)(r[0] >> 32));
+    uint64_t mine, topkey;
+    top8_of_wave(c, lane, scr, mine, topkey);
+    const float top = key_value((uint32_t)(topkey >> 32));
     const float v = key_value((uint32_t)(mine >> 32));
     const float ex = expf(v - top);
     float sum = ex;
@@ -158,20 +213,13 @@ __device__ inline void select_token(const SelectParams &p, int t, int lane, int3
     sum += __shfl_xor(sum, 4, kWave);
     if (lane < kTopK) {
         const int id = (int)~(uint32_t)mine;
-        if constexpr (kDev) {
-            st_dev(p.ids + (size_t)t * kTopK + lane, id);
-            st_dev(p.w + (size_t)t * kTopK + lane, ex / sum);
-        } else {
-            p.ids[(size_t)t * kTopK + lane] = id;
-            p.w[(size_t)t * kTopK + lane] = ex / sum;
-        }
+        p.ids[(size_t)t * kTopK + lane] = id;
+        p.w[(size_t)t * kTopK + lane] = ex / sum;
         if (ids_lds) ids_lds[lane] = id;
     }
     if (p.g && lane == kTopK) {
         if (p.logits_out) p.logits_out[(size_t)t * p.R + p.E] = zg;
-        const float gv = 1.0f / (1.0f + expf(-zg));
-        if constexpr (kDev) st_dev(p.g + t, gv);
-        else p.g[t] = gv;
+        p.g[t] = 1.0f / (1.0f + expf(-zg));
     }
 }
 
