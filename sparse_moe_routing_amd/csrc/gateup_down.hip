@@ -76,16 +76,6 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
         const int Ie = shared ? p.Is : p.I;
         if (j * kSW >= Ie) continue;  // uniform over the block
 
-        __syncthreads();  // the previous unit's readers of xs / xchg are done
-        for (int idx = tid; idx < n * chunks_per_row; idx += kThreads) {
-            const int row = idx / chunks_per_row;
-            const int c = idx - row * chunks_per_row;
-            const int tok = shared ? start + row : (p.perm[start + row] >> 3);
-            *reinterpret_cast<uint4 *>(xs + row * p.x_stride + c * Op::kPerLane) =
-                load16(x + (size_t)tok * p.H + c * Op::kPerLane);
-        }
-        __syncthreads();
-
         const elem_t *gu = reinterpret_cast<const elem_t *>(shared ? p.sgu : p.gate_up) +
                            (shared ? 0 : (size_t)e * 2 * Ie * p.H);
         const int wrow0 = (wave < 2 ? 0 : Ie) + j * kSW + (wave & 1) * kTile;  // first weight row
@@ -124,12 +114,26 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
                 }
             }
         };
+        // the weight stream does not depend on x: both buffers are requested before staging x
         load(rA, 0);
+        if (kDepth < nchunks) load(rB, kDepth);
+        __syncthreads();  // the previous unit's readers of xs / xchg are done
+        for (int idx = tid; idx < n * chunks_per_row; idx += kThreads) {
+            const int row = idx / chunks_per_row;
+            const int c = idx - row * chunks_per_row;
+            const int tok = shared ? start + row : (p.perm[start + row] >> 3);
+            *reinterpret_cast<uint4 *>(xs + row * p.x_stride + c * Op::kPerLane) =
+                load16(x + (size_t)tok * p.H + c * Op::kPerLane);
+        }
+        __syncthreads();
+
         for (int c0 = 0; c0 < nchunks; c0 += 2 * kDepth) {
-            if (c0 + kDepth < nchunks) load(rB, c0 + kDepth);
             consume(rA, c0);
             if (c0 + 2 * kDepth < nchunks) load(rA, c0 + 2 * kDepth);
-            if (c0 + kDepth < nchunks) consume(rB, c0 + kDepth);
+            if (c0 + kDepth < nchunks) {
+                consume(rB, c0 + kDepth);
+                if (c0 + 3 * kDepth < nchunks) load(rB, c0 + 3 * kDepth);
+            }
         }
 
         // up waves hand their tiles over; gate waves form h
@@ -307,7 +311,11 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
             if (s_last) p.rb_arrivals[rc] = 0;  // all units of rc arrived: reset for the next call
         }
         __syncthreads();
-        if (s_last) combine_rows(p, rc * kRowsPerUnit, tid);
+        if (s_last) {
+            int t2 = tid;
+            asm volatile("" : "+v"(t2));  // keeps the combine's addressing out of the unit loop
+            combine_rows(p, rc * kRowsPerUnit, t2);
+        }
     }
 }
 
