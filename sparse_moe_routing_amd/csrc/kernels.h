@@ -117,5 +117,9 @@ hipError_t launch_gateup(const GateUpParams &p, int dtype, int grid, size_t lds,
 size_t gateup_stage_bytes();  // LDS of gateup_kernel beyond its x tile
 size_t down_stage_bytes();    // LDS of down_kernel beyond its h tile
 hipError_t launch_down(const DownParams &p, int dtype, int grid, size_t lds, hipStream_t s);
+hipError_t prepare_wide_kernels();
+hipError_t launch_gateup_wide(const GateUpParams &p, int dtype, int grid, hipStream_t s);
+hipError_t launch_down_wide(const DownParams &p, int dtype, int grid, hipStream_t s);
+int wide_group_tokens();  // tokens per expert group of the wide kernels
 
 }  // namespace moe

@@ -6,11 +6,14 @@
 //   select_hist   T > 64: per 16-token chunk, fold + top-8 + softmax + gate + expert histogram
 //   bucket_scan   T > 64: per-expert chunk bases, counts, offsets, expert-group table
 //   bucket_scatter T > 64: the stable scatter of pair indices
-//   gateup        T <= 256: gate/up + SwiGLU into h per (expert group, 32 intermediate rows)
-//   down          T <= 256: down product per (expert group, 64 rows of y), weighted per slot;
+//   gateup        T <= 64: gate/up + SwiGLU into h per (16-token expert group, 32 inter. rows)
+//   down          T <= 64: down product per (expert group, 64 rows of y), weighted per slot;
 //                 the last unit of each 64-row block sums the slots into y
-//   expert        T > 256: gate/up + SwiGLU + down per (expert group, intermediate slice chunk)
-//   combine       T > 256: weighted sum of the routed partials plus the gated shared partials
+//   gateup_wide   T > 64: as gateup for 64-token expert groups (wide.hip)
+//   down_wide     T > 64: as down for 64-token groups, slot outputs only
+//   combine       sum of the weighted slot outputs (or partials) into y
+//   expert        shapes outside the chunked kernels: fused gate/up + SwiGLU + down per (group,
+//                 intermediate slice chunk), then combine
 #include <string.h>
 
 #include <new>
@@ -38,7 +41,7 @@ constexpr int kRouterSplit = 4;  // the quarters of router_core.h
 constexpr int kStateRowBlocks = 64;  // state ints before the per-row-block counters
 // T > 64: tokens per selection / histogram block (one wave per token in a 1024-thread block)
 constexpr int kHistChunk = 16;
-constexpr int kSplitMaxTokens = 256;
+constexpr int kSplitMaxTokens = 64;   // 16-token groups up to here, 64-token groups above
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -50,7 +53,8 @@ struct Plan {
     int s = 64, S = 1, SPU = 1, n_sc = 1, n_sc_routed = 1, n_sc_shared = 0, slots = 0;
     int x_stride = 0, grid = 1;
     size_t lds = 0;
-    bool split = false;          // T <= 256: gateup + down kernels instead of expert + combine
+    bool split = false;          // T <= 64: gateup + down kernels, 16-token groups
+    bool wide = false;           // T > 64: gateup_wide + down_wide + combine, 64-token groups
     int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;
     size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
@@ -99,7 +103,12 @@ Plan make_plan(const moe_ctx *c, int T) {
     // x-tile rows: up to 16 tokens, fewer when a row of H elements would not leave room in LDS
     const int esz = elem_bytes(cfg.dtype);
     p.x_stride = H + 16 / esz;
-    p.NG = group_rows(c, T);
+    const int ng_x = group_rows(c, T);  // x-tile rows of the split and fused expert kernels
+    // the split and wide kernels stream weight rows in chunks of 16 x 16 bytes (128 bf16 / 64 fp32)
+    const int chunk = cfg.dtype == MOE_BF16 ? 128 : 64;
+    const bool chunk_ok = I % chunk == 0 && Is % chunk == 0;
+    p.wide = T > kSplitMaxTokens && chunk_ok;
+    p.NG = p.wide ? wide_group_tokens() : ng_x;
     p.n_chunks = p.small ? 0 : (T + kHistChunk - 1) / kHistChunk;
     const int pairs = T * 8;
     p.max_groups = max_groups_for(c, T, p.NG);
@@ -113,16 +122,13 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.n_sc_routed = (I / p.s + p.SPU - 1) / p.SPU;
     p.n_sc_shared = Is > 0 ? (Is / p.s + p.SPU - 1) / p.SPU : 0;
     p.slots = pairs + (Is > 0 ? T : 0);
-    p.lds = (size_t)p.NG * p.x_stride * esz + (size_t)16 * (p.s + 4) * 4;
+    p.lds = (size_t)ng_x * p.x_stride * esz + (size_t)16 * (p.s + 4) * 4;
     p.Imax = Imax;
-    p.gu_lds = (size_t)p.NG * p.x_stride * esz + gateup_stage_bytes();
+    p.gu_lds = (size_t)ng_x * p.x_stride * esz + gateup_stage_bytes();
     p.gu_S = Imax / 32;
-    p.down_lds = (size_t)p.NG * (Imax + 16 / esz) * esz * (cfg.dtype == MOE_BF16 ? 2 : 1) +
+    p.down_lds = (size_t)ng_x * (Imax + 16 / esz) * esz * (cfg.dtype == MOE_BF16 ? 2 : 1) +
                  down_stage_bytes();
-    // the split kernels stream weight rows in chunks of 16 x 16 bytes (128 bf16 / 64 fp32)
-    const int chunk = cfg.dtype == MOE_BF16 ? 128 : 64;
-    p.split = T <= kSplitMaxTokens && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds &&
-              I % chunk == 0 && Is % chunk == 0;
+    p.split = T <= kSplitMaxTokens && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds && chunk_ok;
     {
         const long d_units = (long)p.max_groups * (H / 64);
         const long d_cap = (long)c->num_cus * 8;
@@ -157,8 +163,9 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.o_hist = take((size_t)p.n_chunks * E * 4);
     p.o_groups = take((size_t)p.max_groups * 16);
     p.o_ngroups = take(16);
-    p.o_ypart = take(p.split ? (size_t)p.slots * H * 4 : (size_t)p.n_sc * p.slots * H * 4);
-    p.o_h = take(p.split ? (size_t)p.slots * Imax * 4 : 0);
+    const bool per_slot = p.split || p.wide;  // [slots][H] weighted outputs and an h buffer
+    p.o_ypart = take(per_slot ? (size_t)p.slots * H * 4 : (size_t)p.n_sc * p.slots * H * 4);
+    p.o_h = take(per_slot ? (size_t)p.slots * Imax * 4 : 0);
     p.total = o;
     return p;
 }
@@ -342,7 +349,7 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         g_used = gate_in;
         enqueue_dispatch(L, p, nullptr, bucket_params(c, p, ws, ids_in, counts, offsets, perm));
     }
-    if (p.split) {
+    if (p.split || p.wide) {
         GateUpParams gp{};
         gp.x = x;
         gp.gate_up = c->w.gate_up;
@@ -361,9 +368,14 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         gp.S = p.gu_S;
         gp.NG = p.NG;
         gp.x_stride = p.x_stride;
-        L.step("gateup", [&] {
-            return launch_gateup(gp, c->cfg.dtype, p.gu_grid, p.gu_lds, L.stream);
-        });
+        if (p.wide)
+            L.step("gateup_wide", [&] {
+                return launch_gateup_wide(gp, c->cfg.dtype, p.gu_grid, L.stream);
+            });
+        else
+            L.step("gateup", [&] {
+                return launch_gateup(gp, c->cfg.dtype, p.gu_grid, p.gu_lds, L.stream);
+            });
         DownParams dp{};
         dp.down = c->w.down;
         dp.sdn = c->w.shared_down;
@@ -384,9 +396,27 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         dp.I = c->cfg.inter;
         dp.Is = c->cfg.shared_inter;
         dp.Imax = p.Imax;
-        L.step("down", [&] {
-            return launch_down(dp, c->cfg.dtype, p.down_grid, p.down_lds, L.stream);
-        });
+        if (p.wide) {
+            L.step("down_wide", [&] {
+                return launch_down_wide(dp, c->cfg.dtype, p.down_grid, L.stream);
+            });
+            CombineParams cp{};
+            cp.ypart = dp.ybuf;
+            cp.w = nullptr;  // the slot outputs already carry their routing weight / gate
+            cp.g = nullptr;
+            cp.y = y;
+            cp.T = T;
+            cp.H = c->cfg.hidden;
+            cp.slots = p.slots;
+            cp.n_sc_routed = 1;
+            cp.n_sc_shared = has_shared ? 1 : 0;
+            cp.has_shared = has_shared ? 1 : 0;
+            L.step("combine", [&] { return launch_combine(cp, L.stream); });
+        } else {
+            L.step("down", [&] {
+                return launch_down(dp, c->cfg.dtype, p.down_grid, p.down_lds, L.stream);
+            });
+        }
         (void)ids_used;
         L.finish();
         if (n_kernels) *n_kernels = L.count;
@@ -503,7 +533,7 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
         delete c;
         return MOE_ERR_HIP;
     }
-    if (prepare_expert_kernels(p.lds) != hipSuccess) {
+    if (prepare_expert_kernels(p.lds) != hipSuccess || prepare_wide_kernels() != hipSuccess) {
         delete c;
         return MOE_ERR_HIP;
     }

@@ -1,0 +1,327 @@
+// wide.hip - the expert stage for larger rounds (T > 64): expert groups of up to 64 tokens.
+//
+// With 16-token groups an expert that draws 150 tokens (the skewed verify workload) has its
+// weights read ten times. Here a group holds up to 64 tokens, so every weight fragment that a wave
+// stages feeds four 16-token matrix-core tiles and an expert's weights are read once per 64 of
+// its tokens. The token operands no longer fit in LDS for the whole K range, so they are staged
+// one 256-byte K chunk at a time, double-buffered, with one block barrier per chunk:
+//
+// gateup_wide_kernel - unit = (expert group, 32 intermediate rows): waves 0, 1 stream the 16-row
+//   gate tiles, waves 2, 3 the matching up tiles (each load instruction reads 256 contiguous bytes
+//   of 4 rows, reordered into operands through a swizzled per-wave LDS buffer, as in
+//   gateup_down.hip); the group's x chunk is staged cooperatively; h = silu(gate) * up goes to the
+//   workspace (bf16: hi/lo planes).
+// down_wide_kernel - unit = (expert group, 64 rows of y): four 16-row tiles of the contiguous
+//   64-row block of the down weight against the group's h (hi and lo planes staged per chunk);
+//   w * (Wd h) goes to the (token, rank) slot rows of the [slots][H] buffer, which the combine
+//   kernel sums in rank order.
+//
+// Per output element the arithmetic is that of gateup_down.hip (the same matrix instruction, the
+// same k order over chunks and steps, the same SiLU and split of h), so a token's bits do not
+// depend on which of the two paths computed it.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kWThreads = 256;
+constexpr int kWPieces = 16;                  // 16-byte pieces per row per chunk (256 bytes)
+constexpr int kWStage = kTile * kWPieces * 16;  // one wave's 16 x 256-byte weight chunk
+constexpr int kXRow = kWPieces * 16 + 16;     // LDS row of a staged token chunk (+16 B: no bank
+                                              // conflicts across the 16 rows of an operand read)
+
+__device__ __forceinline__ uint4 lds_read16(const unsigned char *p) {
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+// Weight chunk of one wave: rows lrow + 4a (a = 0..3) of the wave's 16, 256 bytes each.
+template <class Op>
+__device__ __forceinline__ void load_wchunk(uint4 (&r)[4], const typename Op::elem_t *src,
+                                            size_t row_stride, int c) {
+    constexpr int kCE = kWPieces * Op::kPerLane;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) r[a] = load16_stream(src + (size_t)(4 * a) * row_stride + c * kCE);
+}
+
+// Swizzled staging (row rr, piece p at rr * 256 + ((p ^ rr) & 15) * 16) and operand read of
+// step s (piece 4s + q of row col).
+__device__ __forceinline__ void stage_w(unsigned char *buf, const uint4 (&r)[4], int lrow,
+                                        int lpiece) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int rr = 4 * a + lrow;
+        *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) = r[a];
+    }
+}
+__device__ __forceinline__ uint4 w_operand(const unsigned char *buf, int s, int col, int q) {
+    const int pc = 4 * s + q;
+    return lds_read16(buf + col * 256 + ((pc ^ col) & 15) * 16);
+}
+
+}  // namespace
+
+template <class Op, int NT>
+__global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) {
+    using elem_t = typename Op::elem_t;
+    constexpr int TG = NT * kTile;
+    constexpr int kCE = kWPieces * Op::kPerLane;
+    constexpr int kSteps = kWPieces / 4;
+    constexpr int kSW = 32;  // intermediate rows per unit
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char *xs = smem;                                  // [2][TG][kXRow]
+    unsigned char *stage_all = smem + 2 * TG * kXRow;          // [4 waves][4 KB]
+    float *xchg = reinterpret_cast<float *>(stage_all + 4 * kWStage);  // [2][NT][16][16]
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 15, q = lane >> 4, lrow = lane >> 4, lpiece = lane & 15;
+    unsigned char *stage = stage_all + wave * kWStage;
+    const int nunits = p.num_groups[0] * p.S;
+    const int nchunks = p.H / kCE;
+    const elem_t *x = reinterpret_cast<const elem_t *>(p.x);
+    const int xp = tid & 15, xr0 = tid >> 4;  // x loader: piece xp of rows xr0 + 16 i
+
+    for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
+        const int gi = u / p.S, j = u - (u / p.S) * p.S;
+        const int4 grp = p.groups[gi];
+        const int e = grp.x, start = grp.y, n = grp.z;
+        const bool shared = e == p.E;
+        const int Ie = shared ? p.Is : p.I;
+        if (j * kSW >= Ie) continue;  // uniform over the block
+        const int nt_used = (n + kTile - 1) / kTile;
+
+        const elem_t *gu = reinterpret_cast<const elem_t *>(shared ? p.sgu : p.gate_up) +
+                           (shared ? 0 : (size_t)e * 2 * Ie * p.H);
+        const int wrow0 = (wave < 2 ? 0 : Ie) + j * kSW + (wave & 1) * kTile;
+        const elem_t *src = gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
+        const elem_t *xsrc[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int r = xr0 + kTile * i;
+            const int rr = r < n ? r : 0;  // rows >= n repeat row 0 (their columns are dropped)
+            const int tok = shared ? start + rr : (p.perm[start + rr] >> 3);
+            xsrc[i] = x + (size_t)tok * p.H + xp * Op::kPerLane;
+        }
+        uint4 wA[4], wB[4], xv[NT];
+        auto load_x = [&](int c) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) xv[i] = load16(xsrc[i] + c * kCE);
+        };
+        auto store_x = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+                *reinterpret_cast<uint4 *>(xs + (buf * TG + xr0 + kTile * i) * kXRow + xp * 16) = xv[i];
+        };
+        f32x4_t acc[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        load_wchunk<Op>(wA, src, p.H, 0);
+        if (1 < nchunks) load_wchunk<Op>(wB, src, p.H, 1);
+        load_x(0);
+        __syncthreads();  // the previous unit's readers of xs / xchg are done
+        store_x(0);
+        auto step = [&](uint4 (&wcur)[4], int c) {
+            if (c + 1 < nchunks) load_x(c + 1);
+            __syncthreads();  // x chunk c is staged; chunk c - 1's readers are done
+            stage_w(stage, wcur, lrow, lpiece);
+            if (c + 2 < nchunks) load_wchunk<Op>(wcur, src, p.H, c + 2);
+            const unsigned char *xb = xs + (c & 1) * TG * kXRow;
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                const uint4 a = w_operand(stage, s, col, q);
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+                    if (tt < nt_used)  // uniform
+                        Op::mma(acc[tt], a, lds_read16(xb + (tt * kTile + col) * kXRow + (4 * s + q) * 16));
+            }
+            if (c + 1 < nchunks) store_x((c + 1) & 1);
+        };
+        for (int c = 0; c < nchunks; c += 2) {
+            step(wA, c);
+            if (c + 1 < nchunks) step(wB, c + 1);
+        }
+
+        // up waves hand their tiles over; gate waves form h
+        if (wave >= 2) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+                *reinterpret_cast<f32x4_t *>(xchg + (((wave - 2) * NT + tt) * kTile + col) * kTile + 4 * q) =
+                    acc[tt];
+        }
+        __syncthreads();
+        if (wave >= 2) continue;
+        const int i0 = j * kSW + wave * kTile + 4 * q;  // intermediate rows i0 + r of this lane
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int cc = tt * kTile + col;  // group row of this lane's token column
+            if (cc >= n) continue;
+            const f32x4_t up = *reinterpret_cast<const f32x4_t *>(
+                xchg + ((wave * NT + tt) * kTile + col) * kTile + 4 * q);
+            const int slot = shared ? p.T * kTopK + start + cc : p.perm[start + cc];
+            float hv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hv[r] = acc[tt][r] / (1.0f + expf(-acc[tt][r])) * up[r];
+            const size_t off = (size_t)slot * p.Imax + i0;
+            if constexpr (Op::kElemBytes == 2) {
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    hi[r] = f32_to_bf16_bits(hv[r]);
+                    lo[r] = f32_to_bf16_bits(hv[r] - bf16_bits_to_f32(hi[r]));
+                }
+                uint16_t *hp = reinterpret_cast<uint16_t *>(p.h);
+                *reinterpret_cast<uint2 *>(hp + off) = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+                *reinterpret_cast<uint2 *>(hp + p.plane + off) =
+                    uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+            } else {
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.h) + off) =
+                    make_float4(hv[0], hv[1], hv[2], hv[3]);
+            }
+        }
+    }
+}
+
+template <class Op, int NT>
+__global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
+    using elem_t = typename Op::elem_t;
+    constexpr int TG = NT * kTile;
+    constexpr int kCE = kWPieces * Op::kPerLane;
+    constexpr int kSteps = kWPieces / 4;
+    constexpr int kRowsPerUnit = 64;
+    constexpr int kPlanes = Op::kElemBytes == 2 ? 2 : 1;  // h as hi + lo bf16, or fp32
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char *hs = smem;                                      // [2][planes][TG][kXRow]
+    unsigned char *stage_all = smem + 2 * kPlanes * TG * kXRow;    // [4 waves][4 KB]
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 15, q = lane >> 4, lrow = lane >> 4, lpiece = lane & 15;
+    unsigned char *stage = stage_all + wave * kWStage;
+    const int n_rc = p.H / kRowsPerUnit;
+    const int nunits = p.num_groups[0] * n_rc;
+    const elem_t *hg = reinterpret_cast<const elem_t *>(p.h);
+    const int hp = tid & 15, hr0 = tid >> 4;  // h loader: piece hp of rows hr0 + 16 i
+
+    for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
+        const int gi = u / n_rc, rc = u - (u / n_rc) * n_rc;
+        const int4 grp = p.groups[gi];
+        const int e = grp.x, start = grp.y, n = grp.z;
+        const bool shared = e == p.E;
+        const int Ie = shared ? p.Is : p.I;
+        const int nchunks = Ie / kCE;
+        const int nt_used = (n + kTile - 1) / kTile;
+        const elem_t *dn = reinterpret_cast<const elem_t *>(shared ? p.sdn : p.down) +
+                           (shared ? 0 : (size_t)e * p.H * Ie);
+        const elem_t *src =
+            dn + (size_t)(rc * kRowsPerUnit + wave * kTile + lrow) * Ie + lpiece * Op::kPerLane;
+        const elem_t *hsrc[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int r = hr0 + kTile * i;
+            const int rr = r < n ? r : 0;
+            const int slot = shared ? p.T * kTopK + start + rr : p.perm[start + rr];
+            hsrc[i] = hg + (size_t)slot * p.Imax + hp * Op::kPerLane;
+        }
+        uint4 wA[4], wB[4], hv[kPlanes][NT];
+        auto load_h = [&](int c) {
+#pragma unroll
+            for (int pl = 0; pl < kPlanes; ++pl)
+#pragma unroll
+                for (int i = 0; i < NT; ++i) hv[pl][i] = load16(hsrc[i] + pl * p.plane + c * kCE);
+        };
+        auto store_h = [&](int buf) {
+#pragma unroll
+            for (int pl = 0; pl < kPlanes; ++pl)
+#pragma unroll
+                for (int i = 0; i < NT; ++i)
+                    *reinterpret_cast<uint4 *>(hs + ((buf * kPlanes + pl) * TG + hr0 + kTile * i) * kXRow +
+                                               hp * 16) = hv[pl][i];
+        };
+        f32x4_t acc[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        load_wchunk<Op>(wA, src, Ie, 0);
+        if (1 < nchunks) load_wchunk<Op>(wB, src, Ie, 1);
+        load_h(0);
+        __syncthreads();  // the previous unit's readers of hs are done
+        store_h(0);
+        auto step = [&](uint4 (&wcur)[4], int c) {
+            if (c + 1 < nchunks) load_h(c + 1);
+            __syncthreads();  // h chunk c is staged; chunk c - 1's readers are done
+            stage_w(stage, wcur, lrow, lpiece);
+            if (c + 2 < nchunks) load_wchunk<Op>(wcur, src, Ie, c + 2);
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+                const uint4 a = w_operand(stage, s, col, q);
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    if (tt >= nt_used) continue;  // uniform
+#pragma unroll
+                    for (int pl = 0; pl < kPlanes; ++pl)
+                        Op::mma(acc[tt], a,
+                                lds_read16(hs + (((c & 1) * kPlanes + pl) * TG + tt * kTile + col) * kXRow +
+                                           (4 * s + q) * 16));
+                }
+            }
+            if (c + 1 < nchunks) store_h((c + 1) & 1);
+        };
+        for (int c = 0; c < nchunks; c += 2) {
+            step(wA, c);
+            if (c + 1 < nchunks) step(wB, c + 1);
+        }
+
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int cc = tt * kTile + col;
+            if (cc >= n) continue;
+            const int slot = shared ? p.T * kTopK + start + cc : p.perm[start + cc];
+            const float wt = shared ? p.g[start + cc] : p.w[slot];
+            // lane holds rows 4q + r of the wave's 16 rows for its token column
+            *reinterpret_cast<float4 *>(p.ybuf + (size_t)slot * p.H + rc * kRowsPerUnit +
+                                        wave * kTile + 4 * q) =
+                make_float4(wt * acc[tt][0], wt * acc[tt][1], wt * acc[tt][2], wt * acc[tt][3]);
+        }
+    }
+}
+
+constexpr int kWideNT = 4;  // 64-token groups
+
+size_t gateup_wide_lds() { return 2 * kWideNT * kTile * kXRow + 4 * kWStage + 2 * kWideNT * kTile * kTile * 4; }
+size_t down_wide_lds(int dtype) {
+    return 2 * (dtype == 1 ? 2 : 1) * kWideNT * kTile * kXRow + 4 * kWStage;
+}
+int wide_group_tokens() { return kWideNT * kTile; }
+
+hipError_t prepare_wide_kernels() {
+    hipError_t err;
+    const void *gk[] = {reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT>),
+                        reinterpret_cast<const void *>(&gateup_wide_kernel<OpF32, kWideNT>)};
+    for (const void *k : gk)
+        if ((err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)gateup_wide_lds())) != hipSuccess)
+            return err;
+    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&down_wide_kernel<OpBF16, kWideNT>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)down_wide_lds(1))) != hipSuccess)
+        return err;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&down_wide_kernel<OpF32, kWideNT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)down_wide_lds(0));
+}
+
+hipError_t launch_gateup_wide(const GateUpParams &p, int dtype, int grid, hipStream_t s) {
+    if (dtype == 1) gateup_wide_kernel<OpBF16, kWideNT><<<grid, kWThreads, gateup_wide_lds(), s>>>(p);
+    else gateup_wide_kernel<OpF32, kWideNT><<<grid, kWThreads, gateup_wide_lds(), s>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_wide(const DownParams &p, int dtype, int grid, hipStream_t s) {
+    if (dtype == 1) down_wide_kernel<OpBF16, kWideNT><<<grid, kWThreads, down_wide_lds(1), s>>>(p);
+    else down_wide_kernel<OpF32, kWideNT><<<grid, kWThreads, down_wide_lds(0), s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -378,6 +378,36 @@ def test_small_batch_shapes(orc, shape):
         assert_close(y.cpu().numpy()[same], y_o[same], f"{shape} T={T} (from x)")
 
 
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: f"{s[0]}-H{s[1]}-E{s[2]}-I{s[3]}-Is{s[4]}")
+def test_wide_group_shapes(orc, shape):
+    """Every output of the T > 64 path (64-token expert groups, chunked routing), against the
+    oracle, including groups that hold one token, a ragged tail and full 64-token groups."""
+    torch = _torch()
+    dtype, H, E, I, Is, _ = shape
+    layer = small_layer(dtype, H, E, I, Is, 200, seed=7 + H + E + I + Is)
+    t = binding.device_weights(layer)
+    m = binding.MoeLayer(H, E, I, Is, 200, dtype, t)
+    ws = m.workspace(200)
+    for T in (65, 200):
+        assert m.plan(T)[-3:] == ["gateup_wide", "down_wide", "combine"]
+        lay = dict(layer)
+        lay["x"] = layer["x"][:T]
+        x = t["x"][:T].contiguous()
+        z_o = orc.logits(lay["x"], layer["router_w"], None)
+        ids_o, w_o, g_o = orc.select(z_o, E, Is > 0)
+        if E <= 16 and T == 200:  # few experts: more than 64 tokens per expert
+            assert np.bincount(ids_o.ravel(), minlength=E).max() > 64
+        y = m.forward(x, routing=routing_device(ids_o, w_o, g_o), ws=ws)
+        y2 = m.forward(x, ws=ws)
+        _, ids, _, _ = m.route(x=x, want_logits=False, ws=ws)
+        torch.cuda.synchronize()
+        y_o = orc.forward(lay, ids_o, w_o, g_o)
+        assert_close(y.cpu().numpy(), y_o, f"{shape} T={T} (oracle routing)")
+        same = (ids.cpu().numpy() == ids_o).all(1)
+        assert same.sum() >= T - max(1, T // 50)
+        assert_close(y2.cpu().numpy()[same], y_o[same], f"{shape} T={T} (from x)")
+
+
 def test_fused_and_chunked_routing_agree():
     """T <= 64 routes in one fused launch, T = 65..256 in the chunked multi-kernel routing: the
     same token gets the same bits from both (same summation orders), and a given routing gives
@@ -446,8 +476,8 @@ def test_batch_invariance_bitwise():
     y32 = m.forward(x)
     y4 = m.forward(x[:4].contiguous())
     y1 = m.forward(x[7:8].contiguous())
-    y200 = m.forward(torch.cat([x] * 7)[:200].contiguous())  # several chunks, the T > 64 routing
-    big = torch.cat([x] * 12)  # 384 tokens: the large-T expert kernels (another summation order)
+    y200 = m.forward(torch.cat([x] * 7)[:200].contiguous())  # T > 64: chunked routing, 64-token groups
+    big = torch.cat([x] * 12)  # 384 tokens
     y384 = m.forward(big)
     z32, ids32, _, _ = m.route(x=x)
     z4, ids4, _, _ = m.route(x=x[:4].contiguous())
@@ -458,9 +488,7 @@ def test_batch_invariance_bitwise():
     assert torch.equal(y32[:4], y4)
     assert torch.equal(y32[7:8], y1)
     assert torch.equal(y200[:32], y32) and torch.equal(y200[192:200], y32[:8])
-    # across the T = 256 boundary the expert arithmetic is grouped differently: equal to rounding
-    assert torch.allclose(y384[:32], y32, rtol=1e-4, atol=1e-5)
-    assert torch.allclose(y384[352:], y32, rtol=1e-4, atol=1e-5)
+    assert torch.equal(y384[:32], y32) and torch.equal(y384[352:], y32)
 
 
 def test_token_permutation_equivariance():
@@ -498,10 +526,11 @@ def test_call_errors_and_empty():
     assert m.plan(4, routing_given=True) == ["route_small", "gateup", "down"]
     tiny = get_layer("tiny_fp32_t4")[1]  # I = 32 is below the weight-row chunk of the split path
     assert tiny.plan(4) == ["route_fused", "expert", "combine"]
-    assert m.plan(65) == ["router", "select_hist", "bucket_scan", "bucket_scatter", "gateup",
-                          "down"]
-    assert m.plan(8192)[:2] == ["router", "select_hist"]
-    assert m.plan(8192)[-2:] == ["expert", "combine"]
+    wide = ["router", "select_hist", "bucket_scan", "bucket_scatter", "gateup_wide", "down_wide",
+            "combine"]
+    assert m.plan(65) == wide and m.plan(8192) == wide
+    assert tiny.plan(200) == ["router", "select_hist", "bucket_scan", "bucket_scatter", "expert",
+                              "combine"]
 
 
 def test_workspace_state_left_zero():
