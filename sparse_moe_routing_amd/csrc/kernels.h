@@ -120,6 +120,8 @@ hipError_t launch_down(const DownParams &p, int dtype, int grid, size_t lds, hip
 hipError_t prepare_wide_kernels();
 hipError_t launch_gateup_wide(const GateUpParams &p, int dtype, int grid, hipStream_t s);
 hipError_t launch_down_wide(const DownParams &p, int dtype, int grid, hipStream_t s);
-int wide_group_tokens();  // tokens per expert group of the wide kernels
+int wide_group_tokens();          // tokens per expert group of the wide kernels
+int wide_rows_per_down_unit();    // rows of y per down_wide unit
+int wide_rows_per_gateup_unit();  // intermediate rows per gateup_wide unit
 
 }  // namespace moe

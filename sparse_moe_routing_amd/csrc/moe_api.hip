@@ -129,13 +129,21 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.down_lds = (size_t)ng_x * (Imax + 16 / esz) * esz * (cfg.dtype == MOE_BF16 ? 2 : 1) +
                  down_stage_bytes();
     p.split = T <= kSplitMaxTokens && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds && chunk_ok;
-    {
+    if (p.wide) {
+        const int dr = wide_rows_per_down_unit(), gr = wide_rows_per_gateup_unit();
+        const long d_units = (long)p.max_groups * ((H + dr - 1) / dr);
+        const long g_units = (long)p.max_groups * (Imax / gr);
+        const long cap = (long)c->num_cus * 4;
+        p.down_grid = (int)(d_units < cap ? d_units : cap);
+        p.gu_grid = (int)(g_units < cap ? g_units : cap);
+        p.gu_S = Imax / gr;
+    } else {
         const long d_units = (long)p.max_groups * (H / 64);
         const long d_cap = (long)c->num_cus * 8;
         p.down_grid = (int)(d_units < d_cap ? d_units : d_cap);
         if (p.down_grid < 1) p.down_grid = 1;
     }
-    {
+    if (!p.wide) {
         const long gu_units = (long)p.max_groups * (Imax / 32);
         const long gu_cap = (long)c->num_cus * 8;
         p.gu_grid = (int)(gu_units < gu_cap ? gu_units : gu_cap);

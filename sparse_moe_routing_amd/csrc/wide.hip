@@ -6,13 +6,14 @@
 // its tokens. The token operands no longer fit in LDS for the whole K range, so they are staged
 // one 256-byte K chunk at a time, double-buffered, with one block barrier per chunk:
 //
-// gateup_wide_kernel - unit = (expert group, 32 intermediate rows): waves 0, 1 stream the 16-row
-//   gate tiles, waves 2, 3 the matching up tiles (each load instruction reads 256 contiguous bytes
-//   of 4 rows, reordered into operands through a swizzled per-wave LDS buffer, as in
-//   gateup_down.hip); the group's x chunk is staged cooperatively; h = silu(gate) * up goes to the
-//   workspace (bf16: hi/lo planes).
-// down_wide_kernel - unit = (expert group, 64 rows of y): four 16-row tiles of the contiguous
-//   64-row block of the down weight against the group's h (hi and lo planes staged per chunk);
+// gateup_wide_kernel - unit = (expert group, 64 intermediate rows), 8 waves: waves 0-3 stream
+//   the 16-row gate tiles, waves 4-7 the matching up tiles (each load instruction reads 256
+//   contiguous bytes of 4 rows, reordered into operands through a swizzled per-wave LDS buffer,
+//   as in gateup_down.hip); the group's x chunk is staged cooperatively and shared by all eight
+//   tiles; h = silu(gate) * up goes to the workspace (bf16: hi/lo planes).
+// down_wide_kernel - unit = (expert group, 256 rows of y), 8 waves of two 16-row tiles each over
+//   the contiguous 256-row block of the down weight, against the group's h (hi and lo planes
+//   staged per chunk and shared by the sixteen tiles: h bytes per unit stay below weight bytes);
 //   w * (Wd h) goes to the (token, rank) slot rows of the [slots][H] buffer, which the combine
 //   kernel sums in rank order.
 //
@@ -26,7 +27,9 @@ namespace moe {
 
 namespace {
 
-constexpr int kWThreads = 256;
+constexpr int kWWaves = 8;                    // waves per block
+constexpr int kWThreads = kWWaves * kWave;
+constexpr int kDownTiles = 2;                 // 16-row tiles of the down weight per wave
 constexpr int kWPieces = 16;                  // 16-byte pieces per row per chunk (256 bytes)
 constexpr int kWStage = kTile * kWPieces * 16;  // one wave's 16 x 256-byte weight chunk
 constexpr int kXRow = kWPieces * 16 + 16;     // LDS row of a staged token chunk (+16 B: no bank
@@ -68,11 +71,13 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
     constexpr int TG = NT * kTile;
     constexpr int kCE = kWPieces * Op::kPerLane;
     constexpr int kSteps = kWPieces / 4;
-    constexpr int kSW = 32;  // intermediate rows per unit
+    constexpr int kGW = kWWaves / 2;   // gate waves (and up waves)
+    constexpr int kSW = kGW * kTile;   // intermediate rows per unit
+    constexpr int kXPasses = TG * kWPieces / kWThreads;  // x chunk loads per thread
     extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char *xs = smem;                                  // [2][TG][kXRow]
-    unsigned char *stage_all = smem + 2 * TG * kXRow;          // [4 waves][4 KB]
-    float *xchg = reinterpret_cast<float *>(stage_all + 4 * kWStage);  // [2][NT][16][16]
+    unsigned char *xs = smem;                                       // [2][TG][kXRow]
+    unsigned char *stage_all = smem + 2 * TG * kXRow;               // [waves][4 KB]
+    float *xchg = reinterpret_cast<float *>(stage_all + kWWaves * kWStage);  // [kGW][NT][16][16]
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -81,7 +86,8 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
     const int nunits = p.num_groups[0] * p.S;
     const int nchunks = p.H / kCE;
     const elem_t *x = reinterpret_cast<const elem_t *>(p.x);
-    const int xp = tid & 15, xr0 = tid >> 4;  // x loader: piece xp of rows xr0 + 16 i
+    const int xp = tid & 15, xr0 = tid >> 4;  // x loader: piece xp of rows xr0 + (threads/16) i
+    constexpr int kXRowsPerPass = kWThreads / kWPieces;
 
     for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
         const int gi = u / p.S, j = u - (u / p.S) * p.S;
@@ -94,25 +100,26 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
 
         const elem_t *gu = reinterpret_cast<const elem_t *>(shared ? p.sgu : p.gate_up) +
                            (shared ? 0 : (size_t)e * 2 * Ie * p.H);
-        const int wrow0 = (wave < 2 ? 0 : Ie) + j * kSW + (wave & 1) * kTile;
+        const int wrow0 = (wave < kGW ? 0 : Ie) + j * kSW + (wave % kGW) * kTile;
         const elem_t *src = gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
-        const elem_t *xsrc[NT];
+        const elem_t *xsrc[kXPasses];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const int r = xr0 + kTile * i;
+        for (int i = 0; i < kXPasses; ++i) {
+            const int r = xr0 + kXRowsPerPass * i;
             const int rr = r < n ? r : 0;  // rows >= n repeat row 0 (their columns are dropped)
             const int tok = shared ? start + rr : (p.perm[start + rr] >> 3);
             xsrc[i] = x + (size_t)tok * p.H + xp * Op::kPerLane;
         }
-        uint4 wA[4], wB[4], xv[NT];
+        uint4 wA[4], wB[4], xv[kXPasses];
         auto load_x = [&](int c) {
 #pragma unroll
-            for (int i = 0; i < NT; ++i) xv[i] = load16(xsrc[i] + c * kCE);
+            for (int i = 0; i < kXPasses; ++i) xv[i] = load16(xsrc[i] + c * kCE);
         };
         auto store_x = [&](int buf) {
 #pragma unroll
-            for (int i = 0; i < NT; ++i)
-                *reinterpret_cast<uint4 *>(xs + (buf * TG + xr0 + kTile * i) * kXRow + xp * 16) = xv[i];
+            for (int i = 0; i < kXPasses; ++i)
+                *reinterpret_cast<uint4 *>(xs + (buf * TG + xr0 + kXRowsPerPass * i) * kXRow + xp * 16) =
+                    xv[i];
         };
         f32x4_t acc[NT];
 #pragma unroll
@@ -145,14 +152,14 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
         }
 
         // up waves hand their tiles over; gate waves form h
-        if (wave >= 2) {
+        if (wave >= kGW) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
-                *reinterpret_cast<f32x4_t *>(xchg + (((wave - 2) * NT + tt) * kTile + col) * kTile + 4 * q) =
+                *reinterpret_cast<f32x4_t *>(xchg + (((wave - kGW) * NT + tt) * kTile + col) * kTile + 4 * q) =
                     acc[tt];
         }
         __syncthreads();
-        if (wave >= 2) continue;
+        if (wave >= kGW) continue;
         const int i0 = j * kSW + wave * kTile + 4 * q;  // intermediate rows i0 + r of this lane
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -190,17 +197,19 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
     constexpr int TG = NT * kTile;
     constexpr int kCE = kWPieces * Op::kPerLane;
     constexpr int kSteps = kWPieces / 4;
-    constexpr int kRowsPerUnit = 64;
+    constexpr int kRowsPerUnit = kWWaves * kDownTiles * kTile;  // 256
     constexpr int kPlanes = Op::kElemBytes == 2 ? 2 : 1;  // h as hi + lo bf16, or fp32
+    constexpr int kHPasses = TG * kWPieces / kWThreads;
+    constexpr int kHRowsPerPass = kWThreads / kWPieces;
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char *hs = smem;                                      // [2][planes][TG][kXRow]
-    unsigned char *stage_all = smem + 2 * kPlanes * TG * kXRow;    // [4 waves][4 KB]
+    unsigned char *stage_all = smem + 2 * kPlanes * TG * kXRow;    // [waves][tiles][4 KB]
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, q = lane >> 4, lrow = lane >> 4, lpiece = lane & 15;
-    unsigned char *stage = stage_all + wave * kWStage;
-    const int n_rc = p.H / kRowsPerUnit;
+    unsigned char *stage = stage_all + wave * kDownTiles * kWStage;
+    const int n_rc = (p.H + kRowsPerUnit - 1) / kRowsPerUnit;  // the last block may be partial
     const int nunits = p.num_groups[0] * n_rc;
     const elem_t *hg = reinterpret_cast<const elem_t *>(p.h);
     const int hp = tid & 15, hr0 = tid >> 4;  // h loader: piece hp of rows hr0 + 16 i
@@ -215,56 +224,75 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
         const int nt_used = (n + kTile - 1) / kTile;
         const elem_t *dn = reinterpret_cast<const elem_t *>(shared ? p.sdn : p.down) +
                            (shared ? 0 : (size_t)e * p.H * Ie);
-        const elem_t *src =
-            dn + (size_t)(rc * kRowsPerUnit + wave * kTile + lrow) * Ie + lpiece * Op::kPerLane;
-        const elem_t *hsrc[NT];
+        // rows rc * 256 + wave * 32 + tile * 16 + ...: one contiguous 32-row block per wave; a wave
+        // past H (H is a multiple of 32) only joins the block barriers
+        const int wrow = rc * kRowsPerUnit + wave * kDownTiles * kTile;
+        const bool rows_ok = wrow < p.H;  // uniform over the wave
+        const elem_t *src = dn + (size_t)((rows_ok ? wrow : 0) + lrow) * Ie + lpiece * Op::kPerLane;
+        const elem_t *hsrc[kHPasses];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const int r = hr0 + kTile * i;
+        for (int i = 0; i < kHPasses; ++i) {
+            const int r = hr0 + kHRowsPerPass * i;
             const int rr = r < n ? r : 0;
             const int slot = shared ? p.T * kTopK + start + rr : p.perm[start + rr];
             hsrc[i] = hg + (size_t)slot * p.Imax + hp * Op::kPerLane;
         }
-        uint4 wA[4], wB[4], hv[kPlanes][NT];
+        uint4 wA[kDownTiles][4], wB[kDownTiles][4], hv[kPlanes][kHPasses];
+        auto load_w = [&](uint4 (&w)[kDownTiles][4], int c) {
+#pragma unroll
+            for (int t = 0; t < kDownTiles; ++t)
+                load_wchunk<Op>(w[t], src + (size_t)(t * kTile) * Ie, Ie, c);
+        };
         auto load_h = [&](int c) {
 #pragma unroll
             for (int pl = 0; pl < kPlanes; ++pl)
 #pragma unroll
-                for (int i = 0; i < NT; ++i) hv[pl][i] = load16(hsrc[i] + pl * p.plane + c * kCE);
+                for (int i = 0; i < kHPasses; ++i) hv[pl][i] = load16(hsrc[i] + pl * p.plane + c * kCE);
         };
         auto store_h = [&](int buf) {
 #pragma unroll
             for (int pl = 0; pl < kPlanes; ++pl)
 #pragma unroll
-                for (int i = 0; i < NT; ++i)
-                    *reinterpret_cast<uint4 *>(hs + ((buf * kPlanes + pl) * TG + hr0 + kTile * i) * kXRow +
-                                               hp * 16) = hv[pl][i];
+                for (int i = 0; i < kHPasses; ++i)
+                    *reinterpret_cast<uint4 *>(hs + ((buf * kPlanes + pl) * TG + hr0 + kHRowsPerPass * i) *
+                                                        kXRow + hp * 16) = hv[pl][i];
         };
-        f32x4_t acc[NT];
+        f32x4_t acc[kDownTiles][NT];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < kDownTiles; ++t)
+#pragma unroll
+            for (int i = 0; i < NT; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        load_wchunk<Op>(wA, src, Ie, 0);
-        if (1 < nchunks) load_wchunk<Op>(wB, src, Ie, 1);
+        if (rows_ok) {
+            load_w(wA, 0);
+            if (1 < nchunks) load_w(wB, 1);
+        }
         load_h(0);
         __syncthreads();  // the previous unit's readers of hs are done
         store_h(0);
-        auto step = [&](uint4 (&wcur)[4], int c) {
+        auto step = [&](uint4 (&wcur)[kDownTiles][4], int c) {
             if (c + 1 < nchunks) load_h(c + 1);
             __syncthreads();  // h chunk c is staged; chunk c - 1's readers are done
-            stage_w(stage, wcur, lrow, lpiece);
-            if (c + 2 < nchunks) load_wchunk<Op>(wcur, src, Ie, c + 2);
+            if (rows_ok) {
 #pragma unroll
-            for (int s = 0; s < kSteps; ++s) {
-                const uint4 a = w_operand(stage, s, col, q);
+                for (int t = 0; t < kDownTiles; ++t) stage_w(stage + t * kWStage, wcur[t], lrow, lpiece);
+                if (c + 2 < nchunks) load_w(wcur, c + 2);
+            }
+#pragma unroll
+            for (int s = 0; s < kSteps && rows_ok; ++s) {
+                uint4 a[kDownTiles];
+#pragma unroll
+                for (int t = 0; t < kDownTiles; ++t) a[t] = w_operand(stage + t * kWStage, s, col, q);
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
                     if (tt >= nt_used) continue;  // uniform
 #pragma unroll
-                    for (int pl = 0; pl < kPlanes; ++pl)
-                        Op::mma(acc[tt], a,
-                                lds_read16(hs + (((c & 1) * kPlanes + pl) * TG + tt * kTile + col) * kXRow +
-                                           (4 * s + q) * 16));
+                    for (int pl = 0; pl < kPlanes; ++pl) {
+                        const uint4 b = lds_read16(hs + (((c & 1) * kPlanes + pl) * TG + tt * kTile + col) *
+                                                            kXRow + (4 * s + q) * 16);
+#pragma unroll
+                        for (int t = 0; t < kDownTiles; ++t) Op::mma(acc[t][tt], a[t], b);
+                    }
                 }
             }
             if (c + 1 < nchunks) store_h((c + 1) & 1);
@@ -277,23 +305,30 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             const int cc = tt * kTile + col;
-            if (cc >= n) continue;
+            if (cc >= n || !rows_ok) continue;
             const int slot = shared ? p.T * kTopK + start + cc : p.perm[start + cc];
             const float wt = shared ? p.g[start + cc] : p.w[slot];
-            // lane holds rows 4q + r of the wave's 16 rows for its token column
-            *reinterpret_cast<float4 *>(p.ybuf + (size_t)slot * p.H + rc * kRowsPerUnit +
-                                        wave * kTile + 4 * q) =
-                make_float4(wt * acc[tt][0], wt * acc[tt][1], wt * acc[tt][2], wt * acc[tt][3]);
+            // lane holds rows 4q + r of each of the wave's 16-row tiles for its token column
+#pragma unroll
+            for (int t = 0; t < kDownTiles; ++t)
+                *reinterpret_cast<float4 *>(p.ybuf + (size_t)slot * p.H + rc * kRowsPerUnit +
+                                            (wave * kDownTiles + t) * kTile + 4 * q) =
+                    make_float4(wt * acc[t][tt][0], wt * acc[t][tt][1], wt * acc[t][tt][2],
+                                wt * acc[t][tt][3]);
         }
     }
 }
 
 constexpr int kWideNT = 4;  // 64-token groups
 
-size_t gateup_wide_lds() { return 2 * kWideNT * kTile * kXRow + 4 * kWStage + 2 * kWideNT * kTile * kTile * 4; }
-size_t down_wide_lds(int dtype) {
-    return 2 * (dtype == 1 ? 2 : 1) * kWideNT * kTile * kXRow + 4 * kWStage;
+size_t gateup_wide_lds() {
+    return 2 * kWideNT * kTile * kXRow + kWWaves * kWStage + (kWWaves / 2) * kWideNT * kTile * kTile * 4;
 }
+size_t down_wide_lds(int dtype) {
+    return 2 * (dtype == 1 ? 2 : 1) * kWideNT * kTile * kXRow + kWWaves * kDownTiles * kWStage;
+}
+int wide_rows_per_down_unit() { return kWWaves * kDownTiles * kTile; }
+int wide_rows_per_gateup_unit() { return kWWaves / 2 * kTile; }
 int wide_group_tokens() { return kWideNT * kTile; }
 
 hipError_t prepare_wide_kernels() {
