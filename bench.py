@@ -198,7 +198,7 @@ def main():
     ws = m0.workspace(T)
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     plan = m0.plan(T)
-    n_ev = len(plan) + 1
+    n_ev = 2 * len(plan)  # each kernel's own start and end
     n_pairs = len(sets) * len(pool)
     # distinct experts per (set, batch) pair, from the library's own routing (outside timing)
     U = {}
@@ -230,8 +230,8 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     value = args.steps * T / elapsed
 
-    # per-kernel durations: the same K steps again, with HIP events recorded on the launch
-    # stream between the kernels (moe_forward_timed); not part of `value`
+    # per-kernel durations: the same K steps again, each kernel launched with a start and a stop
+    # event that its dispatch records (moe_forward_timed); not part of `value`
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
               for _ in range(args.steps)]
     for evs in events:  # torch creates the HIP event on its first record
@@ -245,7 +245,7 @@ def main():
     step_ms = []
     for ev in events:
         for k, name in enumerate(plan):
-            per_kernel[name].append(ev[k].elapsed_time(ev[k + 1]))
+            per_kernel[name].append(ev[2 * k].elapsed_time(ev[2 * k + 1]))
         step_ms.append(ev[0].elapsed_time(ev[-1]))
     mean_U = float(np.mean([U[c] for c in used]))
     stage = {}
@@ -260,7 +260,7 @@ def main():
     gpu_step_us = float(np.median(step_ms)) * 1e3
     log("[bench] per-kernel mean us: " + ", ".join(
         f"{k}={np.mean(v) * 1e3:.2f}" for k, v in per_kernel.items()))
-    log(f"[bench] wall {ms_per_step * 1e3:.2f} us/step, event-timed step median {gpu_step_us:.2f} us,"
+    log(f"[bench] wall {ms_per_step * 1e3:.2f} us/step, timed pass step median {gpu_step_us:.2f} us (with per-kernel events),"
         f" mean U {mean_U:.1f}, step bytes {step_b / 1e6:.1f} MB -> "
         f"{step_b / (ms_per_step * 1e-3) / 1e9:.0f} GB/s wall")
     if args.calib_copy_mib:

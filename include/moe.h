@@ -132,9 +132,10 @@ int moe_forward(const moe_ctx *ctx, const void *x, int32_t T, const int32_t *ids
 int moe_forward_plan(const moe_ctx *ctx, int32_t T, int32_t routing_given, int32_t *n_kernels,
                      const char **names, int32_t max_names);
 
-/* moe_forward that also records events[i] on `stream` immediately before kernel i of the plan
- * and events[n_kernels] after the last one (n_events must equal n_kernels + 1; the events are
- * created by the caller). For per-kernel timing. */
+/* moe_forward whose kernel i of the plan records its own start time in events[2i] and its end
+ * time in events[2i + 1] (timestamps of the kernel's dispatch, launch gaps excluded; n_events
+ * must equal 2 * n_kernels; the events are created by the caller). For per-kernel timing:
+ * hipEventElapsedTime(events[2i], events[2i + 1]) is kernel i's duration. */
 int moe_forward_timed(const moe_ctx *ctx, const void *x, int32_t T, const int32_t *ids_in,
                       const float *w_in, const float *gate_in, float *y, void *workspace,
                       size_t ws_bytes, hipStream_t stream, hipEvent_t *events,

@@ -295,20 +295,20 @@ hipError_t prepare_expert_kernels(size_t max_lds_bytes) {
 hipError_t launch_expert(const ExpertParams &p, int dtype, int grid, size_t lds_bytes,
                          hipStream_t s) {
     if (dtype == 1) {
-        if (p.s == 64) expert_kernel<OpBF16, 64><<<grid, kExpertThreads, lds_bytes, s>>>(p);
-        else if (p.s == 32) expert_kernel<OpBF16, 32><<<grid, kExpertThreads, lds_bytes, s>>>(p);
+        if (p.s == 64) launch_k(expert_kernel<OpBF16, 64>, grid, kExpertThreads, lds_bytes, s, p);
+        else if (p.s == 32) launch_k(expert_kernel<OpBF16, 32>, grid, kExpertThreads, lds_bytes, s, p);
         else return hipErrorInvalidValue;
     } else {
-        if (p.s == 64) expert_kernel<OpF32, 64><<<grid, kExpertThreads, lds_bytes, s>>>(p);
-        else if (p.s == 32) expert_kernel<OpF32, 32><<<grid, kExpertThreads, lds_bytes, s>>>(p);
-        else if (p.s == 16) expert_kernel<OpF32, 16><<<grid, kExpertThreads, lds_bytes, s>>>(p);
+        if (p.s == 64) launch_k(expert_kernel<OpF32, 64>, grid, kExpertThreads, lds_bytes, s, p);
+        else if (p.s == 32) launch_k(expert_kernel<OpF32, 32>, grid, kExpertThreads, lds_bytes, s, p);
+        else if (p.s == 16) launch_k(expert_kernel<OpF32, 16>, grid, kExpertThreads, lds_bytes, s, p);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineParams &p, hipStream_t s) {
-    combine_kernel<<<((p.H + 255) / 256) * p.T, 64, 0, s>>>(p);
+    launch_k(combine_kernel, ((p.H + 255) / 256) * p.T, 64, 0, s, p);
     return hipGetLastError();
 }
 

@@ -338,8 +338,8 @@ hipError_t prepare_split_kernels(size_t gateup_lds, size_t down_lds) {
 }
 
 hipError_t launch_gateup(const GateUpParams &p, int dtype, int grid, size_t lds, hipStream_t s) {
-    if (dtype == 1) gateup_kernel<OpBF16><<<grid, kThreads, lds, s>>>(p);
-    else gateup_kernel<OpF32><<<grid, kThreads, lds, s>>>(p);
+    if (dtype == 1) launch_k(gateup_kernel<OpBF16>, grid, kThreads, lds, s, p);
+    else launch_k(gateup_kernel<OpF32>, grid, kThreads, lds, s, p);
     return hipGetLastError();
 }
 
@@ -347,8 +347,8 @@ size_t gateup_stage_bytes() { return 4 * 2 * 4096 + 2 * 16 * 16 * 4; }
 size_t down_stage_bytes() { return 4 * 4096; }
 
 hipError_t launch_down(const DownParams &p, int dtype, int grid, size_t lds, hipStream_t s) {
-    if (dtype == 1) down_kernel<OpBF16><<<grid, kThreads, lds, s>>>(p);
-    else down_kernel<OpF32><<<grid, kThreads, lds, s>>>(p);
+    if (dtype == 1) launch_k(down_kernel<OpBF16>, grid, kThreads, lds, s, p);
+    else launch_k(down_kernel<OpF32>, grid, kThreads, lds, s, p);
     return hipGetLastError();
 }
 

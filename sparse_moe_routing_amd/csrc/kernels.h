@@ -1,10 +1,22 @@
 // kernels.h - parameter blocks and host-side launchers of the libmoe kernels (internal).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Events the next launch records its own start and end in (the timed entry point sets them
+// around each kernel; null otherwise). Kernel-own timestamps: no launch gap inside the interval.
+extern thread_local hipEvent_t g_launch_start, g_launch_stop;
+
+template <typename... KArgs, typename... Args>
+inline void launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                     Args &&...args) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)lds, s, g_launch_start, g_launch_stop,
+                          0u, KArgs(args)...);
+}
 
 // Router partial logits: zpart[ks][t][r] = sum over the ks-th K range of W[r][h] * x[t][h].
 struct RouterParams {

@@ -23,6 +23,10 @@
 
 using namespace moe;
 
+namespace moe {
+thread_local hipEvent_t g_launch_start = nullptr, g_launch_stop = nullptr;
+}
+
 struct moe_ctx {
     moe_config cfg;
     moe_weights w;
@@ -202,19 +206,21 @@ struct Launcher {
     int max_names = 0;
     hipError_t err = hipSuccess;
 
+    // With events, kernel i records its own start in events[2i] and its end in events[2i + 1]
+    // (timestamps taken by the dispatch itself, so a launch gap is not counted).
     template <class F>
     void step(const char *name, F &&launch) {
         if (names && count < max_names) names[count] = name;
         if (run && err == hipSuccess) {
-            if (events && count < n_events) err = hipEventRecord(events[count], stream);
-            if (err == hipSuccess) err = launch();
+            const bool timed = events && 2 * count + 1 < n_events;
+            g_launch_start = timed ? events[2 * count] : nullptr;
+            g_launch_stop = timed ? events[2 * count + 1] : nullptr;
+            err = launch();
+            g_launch_start = g_launch_stop = nullptr;
         }
         ++count;
     }
-    void finish() {
-        if (run && err == hipSuccess && events && count < n_events)
-            err = hipEventRecord(events[count], stream);
-    }
+    void finish() {}
 };
 
 SelectParams select_params(const moe_ctx *c, const Plan &p, const float *zpart, int KS,
@@ -630,7 +636,7 @@ int moe_forward_timed(const moe_ctx *c, const void *x, int32_t T, const int32_t 
     int st = forward_impl(c, x, T, ids_in, w_in, gate_in, y, workspace, ws_bytes, stream, nullptr,
                           0, nullptr, 0, &n, false, given);
     if (st != MOE_OK) return st;
-    if (n_events != n + 1) return MOE_ERR_INVALID_ARG;
+    if (n_events != 2 * n) return MOE_ERR_INVALID_ARG;
     return forward_impl(c, x, T, ids_in, w_in, gate_in, y, workspace, ws_bytes, stream, events,
                         n_events, nullptr, 0, nullptr, true, 0);
 }

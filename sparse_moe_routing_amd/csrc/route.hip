@@ -298,7 +298,7 @@ __global__ __launch_bounds__(512) void bucket_scatter_kernel(BucketParams bp) {
 
 hipError_t launch_route_small(const SelectParams &sp, const BucketParams &bp, bool do_select,
                               bool do_bucket, hipStream_t s) {
-    route_small_kernel<<<1, 1024, 0, s>>>(sp, bp, do_select ? 1 : 0, do_bucket ? 1 : 0);
+    launch_k(route_small_kernel, 1, 1024, 0, s, sp, bp, do_select ? 1 : 0, do_bucket ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -307,27 +307,27 @@ hipError_t launch_route_fused(const RouterParams &rp, const SelectParams &sp,
                               hipStream_t s) {
     const int grid = rp.n_tt * ((rp.R + kTile - 1) / kTile) * kQuarters;
     if (dtype == 1)
-        route_fused_kernel<OpBF16><<<grid, 1024, 0, s>>>(rp, sp, bp, do_bucket ? 1 : 0, arrivals);
+        launch_k(route_fused_kernel<OpBF16>, grid, 1024, 0, s, rp, sp, bp, do_bucket ? 1 : 0, arrivals);
     else
-        route_fused_kernel<OpF32><<<grid, 1024, 0, s>>>(rp, sp, bp, do_bucket ? 1 : 0, arrivals);
+        launch_k(route_fused_kernel<OpF32>, grid, 1024, 0, s, rp, sp, bp, do_bucket ? 1 : 0, arrivals);
     return hipGetLastError();
 }
 
 hipError_t launch_select_hist(const SelectParams &sp, const BucketParams &bp, bool do_select,
                               bool do_hist, hipStream_t s) {
     const int T = do_select ? sp.T : bp.T;
-    select_hist_kernel<<<(T + bp.chunk_tokens - 1) / bp.chunk_tokens, 1024, 0, s>>>(
+    launch_k(select_hist_kernel, (T + bp.chunk_tokens - 1) / bp.chunk_tokens, 1024, 0, s, 
         sp, bp, do_select ? 1 : 0, do_hist ? 1 : 0);
     return hipGetLastError();
 }
 
 hipError_t launch_bucket_scan(const BucketParams &bp, hipStream_t s) {
-    bucket_scan_kernel<<<1, 1024, 0, s>>>(bp);
+    launch_k(bucket_scan_kernel, 1, 1024, 0, s, bp);
     return hipGetLastError();
 }
 
 hipError_t launch_bucket_scatter(const BucketParams &bp, hipStream_t s) {
-    bucket_scatter_kernel<<<bp.n_chunks, 512, 0, s>>>(bp);
+    launch_k(bucket_scatter_kernel, bp.n_chunks, 512, 0, s, bp);
     return hipGetLastError();
 }
 

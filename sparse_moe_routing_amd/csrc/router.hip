@@ -12,11 +12,11 @@ hipError_t launch_router(const RouterParams &p, int dtype, int maxrt, hipStream_
     const int units = p.n_tt * p.KS * p.n_rg;
     const dim3 grid((units + 3) / 4), block(256);
     if (dtype == 1) {
-        if (maxrt == 1) router_kernel<OpBF16, 1><<<grid, block, 0, s>>>(p);
-        else router_kernel<OpBF16, 4><<<grid, block, 0, s>>>(p);
+        if (maxrt == 1) launch_k(router_kernel<OpBF16, 1>, grid, block, 0, s, p);
+        else launch_k(router_kernel<OpBF16, 4>, grid, block, 0, s, p);
     } else {
-        if (maxrt == 1) router_kernel<OpF32, 1><<<grid, block, 0, s>>>(p);
-        else router_kernel<OpF32, 4><<<grid, block, 0, s>>>(p);
+        if (maxrt == 1) launch_k(router_kernel<OpF32, 1>, grid, block, 0, s, p);
+        else launch_k(router_kernel<OpF32, 4>, grid, block, 0, s, p);
     }
     return hipGetLastError();
 }

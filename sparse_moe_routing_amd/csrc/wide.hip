@@ -348,14 +348,14 @@ hipError_t prepare_wide_kernels() {
 }
 
 hipError_t launch_gateup_wide(const GateUpParams &p, int dtype, int grid, hipStream_t s) {
-    if (dtype == 1) gateup_wide_kernel<OpBF16, kWideNT><<<grid, kWThreads, gateup_wide_lds(), s>>>(p);
-    else gateup_wide_kernel<OpF32, kWideNT><<<grid, kWThreads, gateup_wide_lds(), s>>>(p);
+    if (dtype == 1) launch_k(gateup_wide_kernel<OpBF16, kWideNT>, grid, kWThreads, gateup_wide_lds(), s, p);
+    else launch_k(gateup_wide_kernel<OpF32, kWideNT>, grid, kWThreads, gateup_wide_lds(), s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_down_wide(const DownParams &p, int dtype, int grid, hipStream_t s) {
-    if (dtype == 1) down_wide_kernel<OpBF16, kWideNT><<<grid, kWThreads, down_wide_lds(1), s>>>(p);
-    else down_wide_kernel<OpF32, kWideNT><<<grid, kWThreads, down_wide_lds(0), s>>>(p);
+    if (dtype == 1) launch_k(down_wide_kernel<OpBF16, kWideNT>, grid, kWThreads, down_wide_lds(1), s, p);
+    else launch_k(down_wide_kernel<OpF32, kWideNT>, grid, kWThreads, down_wide_lds(0), s, p);
     return hipGetLastError();
 }
 

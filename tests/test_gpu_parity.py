@@ -533,6 +533,29 @@ def test_call_errors_and_empty():
                               "combine"]
 
 
+def test_forward_timed_events():
+    """moe_forward_timed computes the same y as moe_forward and fills a start / stop event pair
+    per kernel of the plan; a wrong event count is rejected before anything is enqueued."""
+    torch = _torch()
+    layer, m, t = get_layer("decode_b1_t4", max_tokens=8192)
+    for T in (4, 200):
+        x = torch.cat([t["x"]] * 64)[:T].contiguous()
+        plan = m.plan(T)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(plan))]
+        for e in evs:
+            e.record()
+        y = m.forward(x)
+        y2 = m.forward(x, events=evs)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2)
+        dur = [evs[2 * k].elapsed_time(evs[2 * k + 1]) for k in range(len(plan))]
+        assert all(d > 0 for d in dur), dur
+        # kernels run in plan order: each starts after the previous one ended
+        assert all(evs[2 * k + 1].elapsed_time(evs[2 * k + 2]) >= 0 for k in range(len(plan) - 1))
+        with pytest.raises(binding.MoeError):
+            m.forward(x, events=evs[:-1])
+
+
 def test_workspace_state_left_zero():
     """The state region at the start of the workspace (arrival counters, work-queue words,
     flags, the sticky spin-limit word) is zero again after every call, whatever T."""
