@@ -77,7 +77,8 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char *xs = smem;                                       // [2][TG][kXRow]
     unsigned char *stage_all = smem + 2 * TG * kXRow;               // [waves][4 KB]
-    float *xchg = reinterpret_cast<float *>(stage_all + kWWaves * kWStage);  // [kGW][NT][16][16]
+    // [kGW][NT][16][16] up tiles, in the stage area of the up waves once their K loop is done
+    float *xchg = reinterpret_cast<float *>(stage_all + kGW * kWStage);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -111,15 +112,19 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
             xsrc[i] = x + (size_t)tok * p.H + xp * Op::kPerLane;
         }
         uint4 wA[4], wB[4], xv[kXPasses];
+        // a pass whose rows all lie past n is skipped (uniform): the columns those rows feed are
+        // dropped, whatever the stale LDS holds
         auto load_x = [&](int c) {
 #pragma unroll
-            for (int i = 0; i < kXPasses; ++i) xv[i] = load16(xsrc[i] + c * kCE);
+            for (int i = 0; i < kXPasses; ++i)
+                if (kXRowsPerPass * i < n) xv[i] = load16(xsrc[i] + c * kCE);
         };
         auto store_x = [&](int buf) {
 #pragma unroll
             for (int i = 0; i < kXPasses; ++i)
-                *reinterpret_cast<uint4 *>(xs + (buf * TG + xr0 + kXRowsPerPass * i) * kXRow + xp * 16) =
-                    xv[i];
+                if (kXRowsPerPass * i < n)
+                    *reinterpret_cast<uint4 *>(xs + (buf * TG + xr0 + kXRowsPerPass * i) * kXRow +
+                                               xp * 16) = xv[i];
         };
         f32x4_t acc[NT];
 #pragma unroll
@@ -151,7 +156,9 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
             if (c + 1 < nchunks) step(wB, c + 1);
         }
 
-        // up waves hand their tiles over; gate waves form h
+        // up waves hand their tiles over (into their own stage buffers, free now); gate waves
+        // form h
+        static_assert(kGW * NT * kTile * kTile * 4 <= kGW * kWStage, "exchange exceeds the up stages");
         if (wave >= kGW) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
@@ -243,6 +250,8 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
             for (int t = 0; t < kDownTiles; ++t)
                 load_wchunk<Op>(w[t], src + (size_t)(t * kTile) * Ie, Ie, c);
         };
+        // (unlike x, every pass is loaded: skipping passes here measured slower - the branches
+        // break the load pipelining across chunks)
         auto load_h = [&](int c) {
 #pragma unroll
             for (int pl = 0; pl < kPlanes; ++pl)
@@ -321,9 +330,7 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
 
 constexpr int kWideNT = 4;  // 64-token groups
 
-size_t gateup_wide_lds() {
-    return 2 * kWideNT * kTile * kXRow + kWWaves * kWStage + (kWWaves / 2) * kWideNT * kTile * kTile * 4;
-}
+size_t gateup_wide_lds() { return 2 * kWideNT * kTile * kXRow + kWWaves * kWStage; }
 size_t down_wide_lds(int dtype) {
     return 2 * (dtype == 1 ? 2 : 1) * kWideNT * kTile * kXRow + kWWaves * kDownTiles * kWStage;
 }
