@@ -116,6 +116,9 @@ hipError_t launch_route_small(const SelectParams &sp, const BucketParams &bp, bo
 hipError_t launch_route_fused(const RouterParams &rp, const SelectParams &sp,
                               const BucketParams &bp, bool do_bucket, int *arrivals, int dtype,
                               hipStream_t s);
+hipError_t launch_route_tiles(const RouterParams &rp, const SelectParams &sp,
+                              const BucketParams &bp, bool do_bucket, int *tile_arrivals,
+                              int *tiles_done, int dtype, hipStream_t s);
 hipError_t launch_select_hist(const SelectParams &sp, const BucketParams &bp, bool do_select,
                               bool do_hist, hipStream_t s);
 hipError_t launch_bucket_scan(const BucketParams &bp, hipStream_t s);

@@ -1,11 +1,14 @@
 // moe_api.hip - the C ABI of libmoe (include/moe.h): validation, workspace layout, kernel plans.
 //
 // Call sequence of moe_forward (all on the caller's stream, no host synchronisation):
-//   router        partial logits (matrix cores), K split at decode sizes
-//   route_small   T <= 64: fold + top-8 + softmax + gate, then the whole bucketing pass, one block
-//   select_hist   T > 64: per 16-token chunk, fold + top-8 + softmax + gate + expert histogram
-//   bucket_scan   T > 64: per-expert chunk bases, counts, offsets, expert-group table
-//   bucket_scatter T > 64: the stable scatter of pair indices
+//   router        T > 64: partial logits (matrix cores)
+//   route_fused   T <= 16 from x: router partials; the last block selects and buckets
+//   route_tiles   16 < T <= 64 from x: as route_fused per 16-token tile; the last tile buckets
+//   route_small   T <= 64, routing given: the whole bucketing pass, one block
+//   select_hist   T > 64: per 16-token chunk, fold + top-8 + softmax + gate
+//                 + expert histogram
+//   bucket_scan   per-expert chunk bases, counts, offsets, expert-group table
+//   bucket_scatter the stable scatter of pair indices
 //   gateup        T <= 64: gate/up + SwiGLU into h per (16-token expert group, 32 inter. rows)
 //   down          T <= 64: down product per (expert group, 64 rows of y), weighted per slot;
 //                 the last unit of each 64-row block sums the slots into y
@@ -42,7 +45,16 @@ constexpr size_t kAlign = 256;
 constexpr size_t kMaxXTileBytes = 144 * 1024;  // LDS for the expert kernel's x tile
 constexpr size_t kMaxLds = 160 * 1024;         // LDS per workgroup on gfx950
 constexpr int kRouterSplit = 4;  // the quarters of router_core.h
-constexpr int kStateRowBlocks = 64;  // state ints before the per-row-block counters
+// workspace state words (32-bit): route_fused's arrival counter, route_tiles' counter of
+// finished tiles and its per-tile arrival counters (up to 16 tiles), then (from word 64) the
+// down kernel's per-64-row-block arrival counters
+constexpr int kStateRouteArrival = 0;
+constexpr int kStateTilesDone = 4;
+constexpr int kStateTileArrivals = 8;
+constexpr int kStateRowBlocks = 64;
+// route_tiles: up to 4 token tiles (512 pairs). Above, its 68 blocks per tile no longer fit the
+// chip in one round and the chained kernels are faster (measured at T = 192).
+constexpr int kTileRouteMaxTokens = 64;
 // T > 64: tokens per selection / histogram block (one wave per token in a 1024-thread block)
 constexpr int kHistChunk = 16;
 constexpr int kSplitMaxTokens = 64;   // 16-token groups up to here, 64-token groups above
@@ -279,15 +291,25 @@ RouterParams router_params(const moe_ctx *c, const Plan &p, const void *x, float
     return rp;
 }
 
-// T <= 64 from x: router, selection and (optionally) bucketing in one launch.
+// T <= 64 from x: router, selection and (optionally) bucketing in one launch - one token tile:
+// route_fused (its last block selects and buckets); several tiles: route_tiles (the last block of
+// each tile selects the tile, the last tile buckets).
 void enqueue_route_fused(Launcher &L, const moe_ctx *c, const Plan &p, const void *x,
                          float *zpart, const SelectParams &sp, const BucketParams &bp,
                          bool do_bucket, char *ws) {
     const RouterParams rp = router_params(c, p, x, zpart);
-    int *arrivals = reinterpret_cast<int *>(ws + p.o_state);
-    L.step("route_fused", [&] {
-        return launch_route_fused(rp, sp, bp, do_bucket, arrivals, c->cfg.dtype, L.stream);
-    });
+    int *state = reinterpret_cast<int *>(ws + p.o_state);
+    if (p.n_tt == 1) {
+        L.step("route_fused", [&] {
+            return launch_route_fused(rp, sp, bp, do_bucket, state + kStateRouteArrival,
+                                      c->cfg.dtype, L.stream);
+        });
+    } else {
+        L.step("route_tiles", [&] {
+            return launch_route_tiles(rp, sp, bp, do_bucket, state + kStateTileArrivals,
+                                      state + kStateTilesDone, c->cfg.dtype, L.stream);
+        });
+    }
 }
 
 // Bucketing from ids already in memory (or selection + bucketing when sp is given).
@@ -351,7 +373,7 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         const SelectParams sp = select_params(c, p, zpart, p.KS, c->w.router_bias, nullptr, ids,
                                               wts, g);
         const BucketParams bp = bucket_params(c, p, ws, nullptr, counts, offsets, perm);
-        if (p.small) {
+        if (T <= kTileRouteMaxTokens) {
             enqueue_route_fused(L, c, p, x, zpart, sp, bp, true, ws);
         } else {
             enqueue_router(L, c, p, x, zpart);
@@ -591,7 +613,7 @@ int moe_route(const moe_ctx *c, const void *x, const float *logits_in, int32_t T
     const SelectParams sp = select_params(c, p, zpart, KS, bias, logits_out, topk_ids, topk_w,
                                           shared_gate);
     BucketParams bp = bucket_params(c, p, ws, nullptr, nullptr, nullptr, nullptr);
-    if (x && p.small) {
+    if (x && T <= kTileRouteMaxTokens) {
         enqueue_route_fused(L, c, p, x, zp, sp, bp, false, ws);
     } else {
         if (x) enqueue_router(L, c, p, x, zp);

@@ -32,35 +32,41 @@ namespace moe {
 // ----------------------------------------------------------------------------- bucketing
 constexpr int kChunkTokens = 64;                       // most tokens one bucketing block takes
 constexpr int kChunkPairs = kChunkTokens * kTopK;      // 512 pairs
-constexpr int kSubs = kChunkPairs / kWave;             // 8 sub-chunks of 64 pairs (one per wave)
 
-// LDS of the bucketing of one chunk of up to 512 pairs.
-struct BucketShared {
-    alignas(16) int32_t ids[kChunkPairs];  // expert id of each pair (any value outside [0,E): none)
-    uint64_t bits[kSubs][8];               // per sub-chunk: ballot of each expert-id bit
-    uint64_t valid[kSubs];                 // per sub-chunk: ballot of the pairs with a valid id
-    int pre[kSubs][256];                   // count of expert e in the sub-chunks before s
-    int a[256], b[256];                    // per-expert counts / group counts, then their scans
+// LDS of the bucketing of up to kPairs pairs (sub-chunks of 64 pairs, one wave ballot each).
+template <int kPairs>
+struct BucketSharedT {
+    static constexpr int kSub = kPairs / kWave;
+    alignas(16) int32_t ids[kPairs];  // expert id of each pair (any value outside [0,E): none)
+    uint64_t bits[kSub][8];           // per sub-chunk: ballot of each expert-id bit
+    uint64_t valid[kSub];             // per sub-chunk: ballot of the pairs with a valid id
+    int pre[kSub][256];               // count of expert e in the sub-chunks before s
+    int a[256], b[256];               // per-expert counts / group counts, then their scans
     int tot[2];
-    uint64_t sel[16][kSelScratch];         // selection scratch of each of up to 16 waves
+    uint64_t sel[16][kSelScratch];    // selection scratch of each of up to 16 waves
 };
+using BucketShared = BucketSharedT<kChunkPairs>;
 
 // Lanes of sub-chunk sc whose pair holds expert e.
-__device__ __forceinline__ uint64_t lanes_of(const BucketShared &s, int sc, int e) {
+template <class S>
+__device__ __forceinline__ uint64_t lanes_of(const S &s, int sc, int e) {
     uint64_t m = s.valid[sc];
 #pragma unroll
     for (int b = 0; b < 8; ++b) m &= ((e >> b) & 1) ? s.bits[sc][b] : ~s.bits[sc][b];
     return m;
 }
 
-// Ballots of the n pairs in s.ids (waves 0..7), then per expert (threads 0..255): the counts
-// of the sub-chunks before each sub-chunk (s.pre) and the total. Every thread calls it.
-__device__ int chunk_counts(BucketShared &s, int n, int E) {
+// Ballots of the n pairs in s.ids (wave w takes sub-chunks w, w + waves, ...), then per expert
+// (threads 0..255): the counts of the sub-chunks before each sub-chunk (s.pre) and the total.
+// Every thread calls it.
+template <class S>
+__device__ int chunk_counts(S &s, int n, int E) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int nw = blockDim.x / kWave;
     const int nsub = (n + kWave - 1) / kWave;
-    if (wave < nsub) {
-        const int pidx = wave * kWave + lane;
+    for (int sc = wave; sc < nsub; sc += nw) {
+        const int pidx = sc * kWave + lane;
         const int e = pidx < n ? s.ids[pidx] : -1;
         const bool ok = e >= 0 && e < E;
         const uint64_t vb = __ballot(ok);
@@ -68,9 +74,9 @@ __device__ int chunk_counts(BucketShared &s, int n, int E) {
 #pragma unroll
         for (int b = 0; b < 8; ++b) bb[b] = __ballot(ok && ((e >> b) & 1));
         if (lane == 0) {
-            s.valid[wave] = vb;
+            s.valid[sc] = vb;
 #pragma unroll
-            for (int b = 0; b < 8; ++b) s.bits[wave][b] = bb[b];
+            for (int b = 0; b < 8; ++b) s.bits[sc][b] = bb[b];
         }
     }
     __syncthreads();
@@ -84,29 +90,30 @@ __device__ int chunk_counts(BucketShared &s, int n, int E) {
     return cnt;
 }
 
-// Writes perm[base_of(e) + stable rank] = p0 + pair index for every valid pair (waves 0..7).
-// base_of(e) gives the destination of expert e's first pair of this chunk. Needs s.pre, i.e.
-// a block barrier after chunk_counts.
-template <class Base>
-__device__ void chunk_scatter(const BucketShared &s, int n, int E, int p0, int32_t *perm,
-                              Base base_of) {
+// Writes perm[base_of(e) + stable rank] = p0 + pair index for every valid pair (sub-chunks as
+// in chunk_counts). base_of(e) gives the destination of expert e's first pair of this chunk.
+// Needs s.pre, i.e. a block barrier after chunk_counts.
+template <class S, class Base>
+__device__ void chunk_scatter(const S &s, int n, int E, int p0, int32_t *perm, Base base_of) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int nw = blockDim.x / kWave;
     const int nsub = (n + kWave - 1) / kWave;
-    if (wave < nsub) {
-        const int pidx = wave * kWave + lane;
+    for (int sc = wave; sc < nsub; sc += nw) {
+        const int pidx = sc * kWave + lane;
         const int e = pidx < n ? s.ids[pidx] : -1;
         if (e >= 0 && e < E) {
-            const uint64_t m = lanes_of(s, wave, e);
+            const uint64_t m = lanes_of(s, sc, e);
             const int rank = __popcll(m & ((1ull << lane) - 1ull));
-            perm[base_of(e) + s.pre[wave][e] + rank] = p0 + pidx;
+            perm[base_of(e) + s.pre[sc][e] + rank] = p0 + pidx;
         }
     }
 }
 
 // Exclusive scans over experts of s.a and s.b (256 entries each, by wave 0 of the block).
 // Every thread of the block calls it.
-__device__ void scan_experts(BucketShared &s) {
+template <class S>
+__device__ void scan_experts(S &s) {
     __syncthreads();
     const int tid = threadIdx.x;
     if (tid < kWave) {
@@ -147,7 +154,8 @@ __device__ void scan_experts(BucketShared &s) {
 
 // Offsets, counts and the group table from per-expert totals (thread e < E owns expert e; its
 // offset ends up in s.a[e]). Every thread calls it.
-__device__ void write_tables(const BucketParams &bp, int cnt, BucketShared &s) {
+template <class S>
+__device__ void write_tables(const BucketParams &bp, int cnt, S &s) {
     const int tid = threadIdx.x;
     const bool own = tid < bp.E;
     const int c = own ? cnt : 0;
@@ -231,6 +239,52 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(RouterParams rp, Sele
     select_bucket_block<true>(sp, bp, true, do_bucket != 0, s);
 }
 
+// 16 < T <= 64 from x: the blocks of route_fused_kernel for every token tile; the last block of
+// a tile (one arrival counter per tile) selects that tile's tokens, one wave each; the last tile
+// to finish (a second counter) runs the bucketing of all T*8 pairs. The selections of different
+// tiles run on different CUs, and one launch replaces router, selection and three bucketing
+// passes. The tile's ids reach the last block device-coherently.
+template <class Op>
+__global__ __launch_bounds__(1024) void route_tiles_kernel(RouterParams rp, SelectParams sp,
+                                                          BucketParams bp, int do_bucket,
+                                                          int *tile_arrivals, int *tiles_done) {
+    __shared__ BucketShared s;
+    __shared__ float red[16 * 256];
+    __shared__ int s_last;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int per_tile = ((rp.R + kTile - 1) / kTile) * kQuarters;
+    const int tt = blockIdx.x / per_tile;
+    router_quarter_block<Op, true>(rp, blockIdx.x, red);
+    wait_own_stores();
+    __syncthreads();
+    if (tid == 0) {
+        s_last = atomicAdd(tile_arrivals + tt, 1) == per_tile - 1;
+        if (s_last) tile_arrivals[tt] = 0;  // the tile's blocks have all arrived
+    }
+    __syncthreads();
+    if (!s_last) return;  // uniform over the block
+    const int t0 = tt * kTile, nt = min(kTile, sp.T - t0);
+    if (wave < nt) select_token<true>(sp, t0 + wave, lane, s.ids + wave * kTopK, s.sel[wave]);
+    if (!do_bucket) return;  // uniform
+    __syncthreads();
+    for (int i = tid; i < nt * kTopK; i += blockDim.x) st_dev(sp.ids + t0 * kTopK + i, s.ids[i]);
+    wait_own_stores();
+    __syncthreads();
+    if (tid == 0) {
+        s_last = atomicAdd(tiles_done, 1) == rp.n_tt - 1;
+        if (s_last) tiles_done[0] = 0;  // every tile has arrived
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const int n = sp.T * kTopK;
+    for (int i = tid; i < n; i += blockDim.x) s.ids[i] = ld_dev(sp.ids + i);
+    __syncthreads();
+    const int cnt = chunk_counts(s, n, bp.E);
+    write_tables(bp, cnt, s);  // ends with a barrier; s.a[e] = offset of expert e
+    chunk_scatter(s, n, bp.E, 0, bp.perm, [&](int e) { return s.a[e]; });
+}
+
 // T > 64, pass 1: per chunk of chunk_tokens tokens (one wave each), selection (optional) and
 // the per-expert histogram.
 __global__ __launch_bounds__(1024) void select_hist_kernel(SelectParams sp, BucketParams bp,
@@ -310,6 +364,19 @@ hipError_t launch_route_fused(const RouterParams &rp, const SelectParams &sp,
         launch_k(route_fused_kernel<OpBF16>, grid, 1024, 0, s, rp, sp, bp, do_bucket ? 1 : 0, arrivals);
     else
         launch_k(route_fused_kernel<OpF32>, grid, 1024, 0, s, rp, sp, bp, do_bucket ? 1 : 0, arrivals);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_tiles(const RouterParams &rp, const SelectParams &sp,
+                              const BucketParams &bp, bool do_bucket, int *tile_arrivals,
+                              int *tiles_done, int dtype, hipStream_t s) {
+    const int grid = rp.n_tt * ((rp.R + kTile - 1) / kTile) * kQuarters;
+    if (dtype == 1)
+        launch_k(route_tiles_kernel<OpBF16>, grid, 1024, 0, s, rp, sp, bp, do_bucket ? 1 : 0,
+                 tile_arrivals, tiles_done);
+    else
+        launch_k(route_tiles_kernel<OpF32>, grid, 1024, 0, s, rp, sp, bp, do_bucket ? 1 : 0,
+                 tile_arrivals, tiles_done);
     return hipGetLastError();
 }
 

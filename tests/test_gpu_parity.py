@@ -360,7 +360,7 @@ def test_small_batch_shapes(orc, shape):
     m = binding.MoeLayer(H, E, I, Is, 64, dtype, t)
     ws = m.workspace(64)
     for T in Ts:
-        assert m.plan(T) == ["route_fused", "gateup", "down"]
+        assert m.plan(T)[1:] == ["gateup", "down"]
         lay = dict(layer)
         lay["x"] = layer["x"][:T]
         x = t["x"][:T].contiguous()
@@ -409,21 +409,26 @@ def test_wide_group_shapes(orc, shape):
 
 
 def test_fused_and_chunked_routing_agree():
-    """T <= 64 routes in one fused launch, T = 65..256 in the chunked multi-kernel routing: the
-    same token gets the same bits from both (same summation orders), and a given routing gives
-    the same y as the internal one."""
+    """T <= 16 routes in one launch whose last block selects, 16 < T <= 64 per 16-token tile,
+    T > 64 in the chunked multi-kernel routing: the same token gets the same logits, routing and
+    output bits from all three (same summation orders), and a given routing gives the same y as
+    the internal one."""
     torch = _torch()
     layer, m, t = get_layer("decode_b8_t32", max_tokens=8192)
     x = t["x"]
-    xs = torch.cat([x] * 3)[:96].contiguous()
-    assert m.plan(64)[0] == "route_fused" and m.plan(96)[0] == "router"
+    xs = torch.cat([x] * 10)[:300].contiguous()
+    assert m.plan(16)[0] == "route_fused" and m.plan(64)[0] == "route_tiles"
+    assert m.plan(300)[0] == "router"
+    y16 = m.forward(xs[:16].contiguous())
     y64 = m.forward(xs[:64].contiguous())
-    y96 = m.forward(xs)
-    ids, w, g = m.route(x=xs, want_logits=False)[1:]
+    y300 = m.forward(xs)
+    z64, ids64, _, _ = m.route(x=xs[:64].contiguous())
+    z300, ids, w, g = m.route(x=xs)
     y64g = m.forward(xs[:64].contiguous(), routing=(ids[:64].contiguous(), w[:64].contiguous(),
                                                     g[:64].contiguous()))
     torch.cuda.synchronize()
-    assert torch.equal(y64, y96[:64])
+    assert torch.equal(z64, z300[:64]) and torch.equal(ids64, ids[:64])
+    assert torch.equal(y16, y64[:16]) and torch.equal(y64, y300[:64])
     assert torch.equal(y64g, y64)
 
 
@@ -522,13 +527,15 @@ def test_call_errors_and_empty():
         == binding.MOE_ERR_INVALID_ARG  # routing must be all given or all absent
     assert lib.moe_route(m.ctx, P(t["x"]), P(y), 4, None, P(ids), P(y), P(y), P(ws), ws.numel(),
                          s) == binding.MOE_ERR_INVALID_ARG  # both x and logits
-    assert m.plan(4) == ["route_fused", "gateup", "down"] and m.plan(64) == m.plan(4)
+    assert m.plan(4) == ["route_fused", "gateup", "down"]
+    assert m.plan(64) == ["route_tiles", "gateup", "down"]
     assert m.plan(4, routing_given=True) == ["route_small", "gateup", "down"]
     tiny = get_layer("tiny_fp32_t4")[1]  # I = 32 is below the weight-row chunk of the split path
     assert tiny.plan(4) == ["route_fused", "expert", "combine"]
-    wide = ["router", "select_hist", "bucket_scan", "bucket_scatter", "gateup_wide", "down_wide",
-            "combine"]
-    assert m.plan(65) == wide and m.plan(8192) == wide
+    wide = ["gateup_wide", "down_wide", "combine"]
+    assert m.plan(65) == ["router", "select_hist", "bucket_scan", "bucket_scatter"] + wide
+    assert m.plan(8192) == m.plan(65)
+    assert m.plan(200, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
     assert tiny.plan(200) == ["router", "select_hist", "bucket_scan", "bucket_scatter", "expert",
                               "combine"]
 
