@@ -317,18 +317,34 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketParams bp) {
     const int e = tid & 255, quarter = tid >> 8;
     const int per = (bp.n_chunks + 3) / 4;
     const int c0 = quarter * per, c1 = min(bp.n_chunks, c0 + per);
+    // loads in batches of 8 chunks issued together (clamped past the end, dropped)
+    constexpr int kB = 8;
     int sum = 0;
-    if (e < bp.E)
-        for (int c = c0; c < c1; ++c) sum += bp.hist[(size_t)c * bp.E + e];
+    if (e < bp.E) {
+        for (int c = c0; c < c1; c += kB) {
+            int v[kB];
+#pragma unroll
+            for (int j = 0; j < kB; ++j) v[j] = bp.hist[(size_t)min(c + j, c1 - 1) * bp.E + e];
+#pragma unroll
+            for (int j = 0; j < kB; ++j) sum += c + j < c1 ? v[j] : 0;
+        }
+    }
     s_part[quarter][e] = sum;
     __syncthreads();
     int base = 0;
     for (int qq = 0; qq < quarter; ++qq) base += s_part[qq][e];
     if (e < bp.E) {
-        for (int c = c0; c < c1; ++c) {
-            const int v = bp.hist[(size_t)c * bp.E + e];
-            bp.hist[(size_t)c * bp.E + e] = base;
-            base += v;
+        for (int c = c0; c < c1; c += kB) {
+            int v[kB];
+#pragma unroll
+            for (int j = 0; j < kB; ++j) v[j] = bp.hist[(size_t)min(c + j, c1 - 1) * bp.E + e];
+#pragma unroll
+            for (int j = 0; j < kB; ++j) {
+                if (c + j < c1) {
+                    bp.hist[(size_t)(c + j) * bp.E + e] = base;
+                    base += v[j];
+                }
+            }
         }
     }
     const int cnt = (tid < 256) ? s_part[0][e] + s_part[1][e] + s_part[2][e] + s_part[3][e] : 0;

@@ -8,9 +8,23 @@ __global__ __launch_bounds__(256) void router_kernel(RouterParams p) {
     router_unit<Op, MAXRT>(p, blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
 }
 
+// Large T: each wave covers 4 row tiles x 4 token tiles of a quarter.
+constexpr int kRouterTT = 4;
+template <class Op>
+__global__ __launch_bounds__(256) void router_tt_kernel(RouterParams p) {
+    router_unit_tt<Op, 4, kRouterTT>(p, blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+}
+
 hipError_t launch_router(const RouterParams &p, int dtype, int maxrt, hipStream_t s) {
     const int units = p.n_tt * p.KS * p.n_rg;
     const dim3 grid((units + 3) / 4), block(256);
+    if (maxrt == 4) {  // token-tile blocked form
+        const int tunits = (p.n_tt + kRouterTT - 1) / kRouterTT * p.KS * p.n_rg;
+        const dim3 tgrid((tunits + 3) / 4);
+        if (dtype == 1) launch_k(router_tt_kernel<OpBF16>, tgrid, block, 0, s, p);
+        else launch_k(router_tt_kernel<OpF32>, tgrid, block, 0, s, p);
+        return hipGetLastError();
+    }
     if (dtype == 1) {
         if (maxrt == 1) launch_k(router_kernel<OpBF16, 1>, grid, block, 0, s, p);
         else launch_k(router_kernel<OpBF16, 4>, grid, block, 0, s, p);

@@ -144,6 +144,97 @@ __device__ __forceinline__ void router_unit(const RouterParams &p, int u, int la
     }
 }
 
+// Prefill form: wave unit u = (group of MAXTT token tiles, group of MAXRT row tiles, quarter):
+// every weight fragment feeds MAXTT token tiles and every x fragment MAXRT row tiles, so the
+// router weight is read from cache once per MAXTT token tiles. Per output element the steps,
+// runs and their order are those of router_unit (the result is bitwise the same).
+template <class Op, int MAXRT, int MAXTT>
+__device__ __forceinline__ void router_unit_tt(const RouterParams &p, int u, int lane) {
+    using elem_t = typename Op::elem_t;
+    const int n_tg = (p.n_tt + MAXTT - 1) / MAXTT;
+    const int total = n_tg * p.KS * p.n_rg;
+    if (u >= total) return;
+    const int rg = u % p.n_rg;
+    const int kq = (u / p.n_rg) % p.KS;
+    const int tg = u / (p.n_rg * p.KS);
+    const int n_rt = (p.R + kTile - 1) / kTile;
+    const int rt0 = rg * MAXRT, tt0 = tg * MAXTT;
+    const int nrt_here = min(MAXRT, n_rt - rt0);
+    const int ntt_here = min(MAXTT, p.n_tt - tt0);
+    const int col = lane & 15, q = lane >> 4;
+    const RouterGeom g(p.H, Op::kStep);
+    const int kbase = kq * g.Sq * Op::kStep + q * Op::kPerLane;
+    const elem_t *xrow[MAXTT];
+    bool tok_ok[MAXTT];
+#pragma unroll
+    for (int i = 0; i < MAXTT; ++i) {
+        const int tok = (tt0 + i) * kTile + col;
+        tok_ok[i] = i < ntt_here && tok < p.T;
+        xrow[i] = reinterpret_cast<const elem_t *>(p.x) + (size_t)(tok_ok[i] ? tok : 0) * p.H + kbase;
+    }
+    const elem_t *wrow[MAXRT];
+    bool wok[MAXRT];
+#pragma unroll
+    for (int j = 0; j < MAXRT; ++j) {
+        const int row = (rt0 + j) * kTile + col;
+        wok[j] = j < nrt_here && row < p.R;
+        wrow[j] = reinterpret_cast<const elem_t *>(p.w) + (size_t)(wok[j] ? row : 0) * p.H + kbase;
+    }
+    const uint4 zero = {0u, 0u, 0u, 0u};
+    constexpr int kBatch = 2;
+    f32x4_t s[MAXRT][MAXTT], ch[MAXRT][MAXTT];
+#pragma unroll
+    for (int j = 0; j < MAXRT; ++j)
+#pragma unroll
+        for (int i = 0; i < MAXTT; ++i) ch[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b0 = 0; b0 < g.Sq; b0 += kBatch) {
+        uint4 xb[kBatch][MAXTT], wa[kBatch][MAXRT];
+#pragma unroll
+        for (int v = 0; v < kBatch; ++v) {
+            const int st = min(b0 + v, g.Sq - 1);  // past the end: re-read, unused
+#pragma unroll
+            for (int i = 0; i < MAXTT; ++i) xb[v][i] = load16(xrow[i] + st * Op::kStep);
+#pragma unroll
+            for (int j = 0; j < MAXRT; ++j) wa[v][j] = load16(wrow[j] + st * Op::kStep);
+        }
+#pragma unroll
+        for (int v = 0; v < kBatch; ++v) {
+            const int st = b0 + v;
+            if (st >= g.Sq) break;  // uniform
+#pragma unroll
+            for (int j = 0; j < MAXRT; ++j)
+#pragma unroll
+                for (int i = 0; i < MAXTT; ++i)
+                    if (j < nrt_here && i < ntt_here)  // uniform
+                        Op::mma(ch[j][i], wok[j] ? wa[v][j] : zero, tok_ok[i] ? xb[v][i] : zero);
+            if ((st + 1) % g.Sw == 0 || st + 1 == g.Sq) {  // run st / Sw ends here (uniform)
+                const bool first = st < g.Sw;
+#pragma unroll
+                for (int j = 0; j < MAXRT; ++j)
+#pragma unroll
+                    for (int i = 0; i < MAXTT; ++i) {
+                        s[j][i] = first ? ch[j][i] : s[j][i] + ch[j][i];
+                        ch[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXTT; ++i) {
+        if (!tok_ok[i]) continue;
+        const int tok = (tt0 + i) * kTile + col;
+        float *out = p.zpart + ((size_t)kq * p.T + tok) * p.R;
+#pragma unroll
+        for (int j = 0; j < MAXRT; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = (rt0 + j) * kTile + 4 * q + r;
+                if (j < nrt_here && row < p.R) out[row] = s[j][i][r];
+            }
+        }
+    }
+}
+
 // Decode form: block b = (token tile, row tile, quarter) of 16 waves; wave w computes run w and
 // the runs are added in order through LDS (red: 16 tiles of 256 floats). Every thread of the
 // block calls it; it ends with the partial logits stored (no trailing barrier). kDev: stored
