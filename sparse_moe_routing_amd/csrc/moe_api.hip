@@ -58,6 +58,7 @@ constexpr int kTileRouteMaxTokens = 64;
 // T > 64: tokens per selection / histogram block (one wave per token in a 1024-thread block)
 constexpr int kHistChunk = 16;
 constexpr int kSplitMaxTokens = 64;   // 16-token groups up to here, 64-token groups above
+constexpr int kBigMinTokens = 3072;     // bf16 from here: gateup_big in place of gateup_wide
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -71,6 +72,7 @@ struct Plan {
     size_t lds = 0;
     bool split = false;          // T <= 64: gateup + down kernels, 16-token groups
     bool wide = false;           // T > 64: gateup_wide + down_wide + combine, 64-token groups
+    bool big = false;            // wide, bf16, T >= kBigMinTokens: gateup_big for gateup_wide
     int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;
     size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
@@ -153,6 +155,14 @@ Plan make_plan(const moe_ctx *c, int T) {
         p.down_grid = (int)(d_units < cap ? d_units : cap);
         p.gu_grid = (int)(g_units < cap ? g_units : cap);
         p.gu_S = Imax / gr;
+        p.big = cfg.dtype == MOE_BF16 && T >= kBigMinTokens && Imax % big_rows_per_gateup_unit() == 0;
+        if (p.big) {
+            p.gu_S = Imax / big_rows_per_gateup_unit();
+            const long b_units = (long)p.max_groups * p.gu_S;
+            const long b_cap = (long)c->num_cus * 8;
+            p.gu_grid = (int)(b_units < b_cap ? b_units : b_cap);
+            if (p.gu_grid >= 8) p.gu_grid -= p.gu_grid % 8;  // whole rounds over the 8 XCDs
+        }
     } else {
         const long d_units = (long)p.max_groups * (H / 64);
         const long d_cap = (long)c->num_cus * 8;
@@ -404,7 +414,9 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         gp.S = p.gu_S;
         gp.NG = p.NG;
         gp.x_stride = p.x_stride;
-        if (p.wide)
+        if (p.big)
+            L.step("gateup_big", [&] { return launch_gateup_big(gp, p.gu_grid, L.stream); });
+        else if (p.wide)
             L.step("gateup_wide", [&] {
                 return launch_gateup_wide(gp, c->cfg.dtype, p.gu_grid, L.stream);
             });

@@ -328,6 +328,160 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
     }
 }
 
+// gateup_big_kernel (bf16, large T) - the same unit arithmetic as gateup_wide_kernel with the
+// operand traffic cut for the matrix-core-bound regime. Unit = (expert group of <= 64 tokens,
+// kBigRows * waves intermediate rows); wave w owns rows i0 .. i0 + kBigRows of BOTH the gate and
+// the up matrix (kBigRows / 16 tiles each) against the group's four 16-token tiles, so h is formed
+// in registers. Weight fragments are read from global memory straight in matrix-core order (one
+// fragment feeds four token tiles; an expert's other groups find it in the caches) through a ring
+// of two K chunks of registers; the group's x chunk is staged in LDS per 256-byte K chunk
+// (double-buffered) and each of its fragments feeds every weight tile of the wave.
+constexpr int kBigWaves = 4;
+constexpr int kXcds = 8;      // accelerator complex dies of the chip, each with its own L2
+constexpr int kBigThreads = kBigWaves * kWave;
+constexpr int kBigRows = 32;  // intermediate rows per wave (two 16-row tiles of gate and of up)
+
+template <int NT>
+__global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_big_kernel(GateUpParams p) {
+    using Op = OpBF16;
+    using elem_t = uint16_t;
+    constexpr int TG = NT * kTile;
+    constexpr int kCE = kWPieces * Op::kPerLane;          // elements per chunk (128)
+    constexpr int kSteps = kWPieces / 4;                  // matrix-core steps per chunk
+    constexpr int kRT = 2 * kBigRows / kTile;             // weight tiles per wave (gate, up)
+    constexpr int kSW = kBigWaves * kBigRows;             // intermediate rows per unit
+    constexpr int kXPasses = TG * kWPieces / kBigThreads;
+    constexpr int kXRowsPerPass = kBigThreads / kWPieces;
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char *xs = smem;  // [2][TG][kXRow]
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 15, q = lane >> 4;
+    const int ngroups = p.num_groups[0];
+    const int nunits = ngroups * p.S;
+    const int nchunks = p.H / kCE;
+    const elem_t *x = reinterpret_cast<const elem_t *>(p.x);
+    const int xp = tid & 15, xr0 = tid >> 4;  // x loader: piece xp of rows xr0 + 16 i
+    // XCD-aware schedule: units are numbered slice-major (u = j * groups + g), so the groups of
+    // one expert that use the same weight slice are neighbours; blocks b, b + 8, ... share an XCD
+    // (and its L2) and together take one contiguous eighth of the units, so those neighbours run
+    // side by side on one XCD and read the slice from its L2 after the first miss.
+    const bool xmap = gridDim.x % kXcds == 0;
+    const int xcd = blockIdx.x % kXcds;
+    const int per = xmap ? (nunits + kXcds - 1) / kXcds : nunits;
+    const int u_end = xmap ? min(nunits, (xcd + 1) * per) : nunits;
+    const int u_step = xmap ? gridDim.x / kXcds : gridDim.x;
+
+    for (int u = xmap ? xcd * per + blockIdx.x / kXcds : blockIdx.x; u < u_end; u += u_step) {
+        const int j = u / ngroups, gi = u - j * ngroups;
+        const int4 grp = p.groups[gi];
+        const int e = grp.x, start = grp.y, n = grp.z;
+        const bool shared = e == p.E;
+        const int Ie = shared ? p.Is : p.I;
+        if (j * kSW >= Ie) continue;  // uniform over the block
+        const int nt_used = (n + kTile - 1) / kTile;
+        const int i0 = j * kSW + wave * kBigRows;
+        const bool rows_ok = i0 < Ie;  // uniform over the wave (Ie is a multiple of 32)
+        const elem_t *gu = reinterpret_cast<const elem_t *>(shared ? p.sgu : p.gate_up) +
+                           (shared ? 0 : (size_t)e * 2 * Ie * p.H);
+        // tile t: gate rows (t < kRT/2) or up rows, i0 + 16 (t % (kRT/2)) + col; k-group q
+        const elem_t *arow[kRT];
+#pragma unroll
+        for (int t = 0; t < kRT; ++t) {
+            const int row = (t < kRT / 2 ? 0 : Ie) + i0 + kTile * (t % (kRT / 2)) + col;
+            arow[t] = gu + (size_t)(rows_ok ? row : 0) * p.H + q * Op::kPerLane;
+        }
+        const elem_t *xsrc[kXPasses];
+#pragma unroll
+        for (int i = 0; i < kXPasses; ++i) {
+            const int r = xr0 + kXRowsPerPass * i;
+            const int rr = r < n ? r : 0;  // rows >= n repeat row 0 (their columns are dropped)
+            const int tok = shared ? start + rr : (p.perm[start + rr] >> 3);
+            xsrc[i] = x + (size_t)tok * p.H + xp * Op::kPerLane;
+        }
+        uint4 xv[kXPasses];
+        auto load_x = [&](int c) {
+#pragma unroll
+            for (int i = 0; i < kXPasses; ++i)
+                if (kXRowsPerPass * i < n) xv[i] = load16(xsrc[i] + c * kCE);
+        };
+        auto store_x = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < kXPasses; ++i)
+                if (kXRowsPerPass * i < n)
+                    *reinterpret_cast<uint4 *>(xs + (buf * TG + xr0 + kXRowsPerPass * i) * kXRow +
+                                               xp * 16) = xv[i];
+        };
+        // weight ring: slot s holds step s of the current chunk and is refilled with step s of the
+        // next chunk as soon as its four token tiles have used it
+        uint4 ar[kSteps][kRT];
+        auto load_a = [&](int s2, int c) {
+            if (!rows_ok || c >= nchunks) return;  // uniform
+#pragma unroll
+            for (int t = 0; t < kRT; ++t) ar[s2][t] = load16(arow[t] + c * kCE + s2 * 4 * Op::kPerLane);
+        };
+        f32x4_t acc[kRT][NT];
+#pragma unroll
+        for (int t = 0; t < kRT; ++t)
+#pragma unroll
+            for (int i = 0; i < NT; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+        for (int s2 = 0; s2 < kSteps; ++s2) load_a(s2, 0);
+        load_x(0);
+        __syncthreads();  // the previous unit's readers of xs are done
+        store_x(0);
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) load_x(c + 1);
+            __syncthreads();  // x chunk c is staged; chunk c - 1's readers are done
+            const unsigned char *xb = xs + (c & 1) * TG * kXRow;
+#pragma unroll
+            for (int s2 = 0; s2 < kSteps; ++s2) {
+                uint4 b[NT];
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+                    if (tt < nt_used)  // uniform
+                        b[tt] = lds_read16(xb + (tt * kTile + col) * kXRow + (4 * s2 + q) * 16);
+                if (rows_ok) {
+#pragma unroll
+                    for (int t = 0; t < kRT; ++t)
+#pragma unroll
+                        for (int tt = 0; tt < NT; ++tt)
+                            if (tt < nt_used) Op::mma(acc[t][tt], ar[s2][t], b[tt]);
+                }
+                load_a(s2, c + 1);
+            }
+            if (c + 1 < nchunks) store_x((c + 1) & 1);
+        }
+        if (!rows_ok) continue;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int cc = tt * kTile + col;  // group row of this lane's token column
+            if (cc >= n) continue;
+            const int slot = shared ? p.T * kTopK + start + cc : p.perm[start + cc];
+#pragma unroll
+            for (int g2 = 0; g2 < kRT / 2; ++g2) {
+                const f32x4_t ga = acc[g2][tt], up = acc[kRT / 2 + g2][tt];
+                float hv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) hv[r] = ga[r] / (1.0f + expf(-ga[r])) * up[r];
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    hi[r] = f32_to_bf16_bits(hv[r]);
+                    lo[r] = f32_to_bf16_bits(hv[r] - bf16_bits_to_f32(hi[r]));
+                }
+                const size_t off = (size_t)slot * p.Imax + i0 + g2 * kTile + 4 * q;
+                uint16_t *hp = reinterpret_cast<uint16_t *>(p.h);
+                *reinterpret_cast<uint2 *>(hp + off) = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+                *reinterpret_cast<uint2 *>(hp + p.plane + off) =
+                    uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+            }
+        }
+    }
+}
+
 constexpr int kWideNT = 4;  // 64-token groups
 
 size_t gateup_wide_lds() { return 2 * kWideNT * kTile * kXRow + kWWaves * kWStage; }
@@ -337,6 +491,13 @@ size_t down_wide_lds(int dtype) {
 int wide_rows_per_down_unit() { return kWWaves * kDownTiles * kTile; }
 int wide_rows_per_gateup_unit() { return kWWaves / 2 * kTile; }
 int wide_group_tokens() { return kWideNT * kTile; }
+int big_rows_per_gateup_unit() { return kBigWaves * kBigRows; }
+size_t gateup_big_lds() { return 2 * kWideNT * kTile * kXRow; }
+
+hipError_t launch_gateup_big(const GateUpParams &p, int grid, hipStream_t s) {
+    launch_k(gateup_big_kernel<kWideNT>, grid, kBigThreads, gateup_big_lds(), s, p);
+    return hipGetLastError();
+}
 
 hipError_t prepare_wide_kernels() {
     hipError_t err;

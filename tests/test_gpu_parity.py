@@ -494,6 +494,11 @@ def test_batch_invariance_bitwise():
     assert torch.equal(y32[7:8], y1)
     assert torch.equal(y200[:32], y32) and torch.equal(y200[192:200], y32[:8])
     assert torch.equal(y384[:32], y32) and torch.equal(y384[352:], y32)
+    # T >= 3072: the register-blocked gate/up kernel, the same bits
+    y4097 = m.forward(torch.cat([x] * 129)[:4097].contiguous())
+    torch.cuda.synchronize()
+    assert m.plan(4097)[4] == "gateup_big"
+    assert torch.equal(y4097[:32], y32) and torch.equal(y4097[4064:4096], y32)
 
 
 def test_token_permutation_equivariance():
@@ -534,7 +539,10 @@ def test_call_errors_and_empty():
     assert tiny.plan(4) == ["route_fused", "expert", "combine"]
     wide = ["gateup_wide", "down_wide", "combine"]
     assert m.plan(65) == ["router", "select_hist", "bucket_scan", "bucket_scatter"] + wide
-    assert m.plan(8192) == m.plan(65)
+    assert m.plan(3071) == m.plan(65)
+    big = ["gateup_big", "down_wide", "combine"]  # bf16 from 3072 tokens
+    assert m.plan(3072) == m.plan(8192) == ["router", "select_hist", "bucket_scan",
+                                             "bucket_scatter"] + big
     assert m.plan(200, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
     assert tiny.plan(200) == ["router", "select_hist", "bucket_scan", "bucket_scatter", "expert",
                               "combine"]
