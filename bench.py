@@ -52,7 +52,7 @@ def make_sets(w, n_sets, torch):
     """Weight sets drawn on the GPU with the workload's shapes and scales (bench only)."""
     from sparse_moe_routing_amd import binding
     H, E, I, Is = w.hidden, w.num_experts, w.inter, w.shared_inter
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16  # x and router (fp8: bf16)
     gen = torch.Generator(device="cuda")
     layers = []
     for s in range(n_sets):
@@ -62,10 +62,23 @@ def make_sets(w, n_sets, torch):
             return (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
                     * scale).to(dt)
 
+        def draw_w(shape, scale):
+            """An expert weight block; fp8: per-row E4M3 codes (uint8) and fp32 row scales."""
+            if w.dtype != "fp8":
+                return draw(shape, scale), None
+            v = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * scale
+            rs = v.abs().amax(dim=-1).clamp_min(1e-30) / 448.0
+            q = (v / rs.unsqueeze(-1)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+            return q.view(torch.uint8), rs.contiguous()
+
+        gu, gus = draw_w((E, 2 * I, H), H ** -0.5)
+        dn, dns = draw_w((E, H, I), I ** -0.5)
+        sgu, sgus = draw_w((2 * Is, H), H ** -0.5)
+        sdn, sdns = draw_w((H, Is), Is ** -0.5)
         t = {"router_w": draw((E + 1, H), H ** -0.5), "router_bias": None,
-             "gate_up": draw((E, 2 * I, H), H ** -0.5), "down": draw((E, H, I), I ** -0.5),
-             "shared_gate_up": draw((2 * Is, H), H ** -0.5),
-             "shared_down": draw((H, Is), Is ** -0.5)}
+             "gate_up": gu, "down": dn, "shared_gate_up": sgu, "shared_down": sdn,
+             "gate_up_scale": gus, "down_scale": dns, "shared_gate_up_scale": sgus,
+             "shared_down_scale": sdns}
         if w.bias_std > 0:
             b = torch.zeros(E + 1, device="cuda")
             b[:E] = torch.randn(E, generator=gen, device="cuda") * w.bias_std
@@ -75,25 +88,34 @@ def make_sets(w, n_sets, torch):
     return layers
 
 
+def sizes(w):
+    """(activation bytes, expert weight bytes, row-scale bytes) per element / row."""
+    if w.dtype == "fp8":
+        return 2, 1, 4
+    esz = 2 if w.dtype == "bf16" else 4
+    return esz, esz, 0
+
+
 def step_bytes(w, U):
     """Algorithmic HBM bytes of one step: router, shared expert, the U distinct routed experts
-    touched (each read once), x in and y out."""
-    esz = 2 if w.dtype == "bf16" else 4
+    touched (each read once, with their row scales for fp8), x in and y out."""
+    esz, wsz, ssz = sizes(w)
     H, I, Is, E, T = w.hidden, w.inter, w.shared_inter, w.num_experts, w.tokens
-    return (esz * (E + 1) * H + 3 * esz * H * Is + U * 3 * esz * H * I + esz * T * H + 4 * T * H)
+    return (esz * (E + 1) * H + 3 * wsz * H * Is + ssz * (2 * Is + H) +
+            U * (3 * wsz * H * I + ssz * (2 * I + H)) + esz * T * H + 4 * T * H)
 
 
 def kernel_bytes(w, U, name):
     """Algorithmic bytes of one launch of an expert-stage kernel: the weights it must read (the U
     distinct routed experts touched, each once, and the shared expert) plus the activations it
     must read or write. Intermediates (h, partial sums, routing tables) are not counted."""
-    esz = 2 if w.dtype == "bf16" else 4
+    esz, wsz, ssz = sizes(w)
     H, I, Is, T = w.hidden, w.inter, w.shared_inter, w.tokens
     name = {"gateup_wide": "gateup", "gateup_big": "gateup", "down_wide": "down"}.get(name, name)
     if name == "gateup":
-        return 2 * esz * H * Is + U * 2 * esz * H * I + esz * T * H
+        return 2 * wsz * H * Is + 2 * ssz * Is + U * (2 * wsz * H * I + 2 * ssz * I) + esz * T * H
     if name == "down":
-        return esz * H * Is + U * esz * H * I + 4 * T * H
+        return wsz * H * Is + ssz * H + U * (wsz * H * I + ssz * H) + 4 * T * H
     if name == "expert":
         return 3 * esz * H * Is + U * 3 * esz * H * I + esz * T * H
     if name == "decode":  # the single launch does the whole step
@@ -147,10 +169,10 @@ def cpu_baseline(w, m_t, seconds):
             return a.view(torch.int16).cpu().numpy().view(np.uint16)
         return a.cpu().numpy()
 
-    layer = {"num_experts": w.num_experts, "inter": w.inter, "shared_inter": w.shared_inter,
-             "router_w": host(t["router_w"]), "router_bias": host(t["router_bias"]),
-             "gate_up": host(t["gate_up"]), "down": host(t["down"]),
-             "shared_gate_up": host(t["shared_gate_up"]), "shared_down": host(t["shared_down"])}
+    layer = {"num_experts": w.num_experts, "inter": w.inter, "shared_inter": w.shared_inter}
+    for k in ("router_w", "router_bias", "gate_up", "down", "shared_gate_up", "shared_down",
+              "gate_up_scale", "down_scale", "shared_gate_up_scale", "shared_down_scale"):
+        layer[k] = host(t.get(k))
     from sparse_moe_routing_amd import inputs
     T = min(w.tokens, 64)
     tokens = 0
@@ -190,7 +212,7 @@ def main():
     log(f"[bench] workload {w.name}: T={T} H={H} E={w.num_experts} I={w.inter} Is={w.shared_inter}"
         f" dtype={w.dtype}; {args.sets} weight sets, pool {args.pool}")
     sets = make_sets(w, args.sets, torch)
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16  # x (fp8 workloads: bf16)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(77)
     pool = [torch.randn((T, H), generator=gen, device="cuda").to(dt) for _ in range(args.pool)]

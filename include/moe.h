@@ -58,21 +58,28 @@ typedef enum {
 } moe_status;
 
 typedef enum {
-    MOE_F32 = 0,  /* x and every weight stored as fp32 */
-    MOE_BF16 = 1  /* x and every weight stored as bf16 (raw 16-bit patterns) */
+    MOE_F32 = 0,      /* x and every weight stored as fp32 */
+    MOE_BF16 = 1,     /* x and every weight stored as bf16 (raw 16-bit patterns) */
+    MOE_FP8_E4M3 = 2  /* x and router_w bf16; the routed and shared expert weights stored as
+                         OCP FP8 E4M3 codes (one byte each) with one fp32 scale per weight row:
+                         weight = value(code) * scale[row]. The quantized expert formats the
+                         pages name (groupwise integers, FP8, NVFP4) are not fixed by them; this
+                         is the per-row-scaled FP8 reading (see the scale fields below). */
 } moe_dtype;
 
 typedef struct {
-    int32_t hidden;       /* H: 64..16384, a multiple of 64 (fp32) or of 128 (bf16) */
+    int32_t hidden;       /* H: 64..16384, a multiple of 64 (fp32) or of 128 (bf16, FP8) */
     int32_t num_experts;  /* E: 8..256 */
     int32_t top_k;        /* must be 8 */
-    int32_t inter;        /* I: expert intermediate size, multiple of 16, 16..4096 */
-    int32_t shared_inter; /* I_s: 0 (no shared expert) or a multiple of 16, 16..4096 */
+    int32_t inter;        /* I: expert intermediate size, 16..4096, a multiple of 16 (fp32), of
+                             32 (bf16) or of 128 (FP8) */
+    int32_t shared_inter; /* I_s: 0 (no shared expert) or as I */
     int32_t max_tokens;   /* largest T any call on this context may pass, 1..65536 */
     int32_t dtype;        /* moe_dtype */
 } moe_config;
 
-/* Weight buffers, all row-major, element type = config.dtype. R = E + (I_s > 0 ? 1 : 0). */
+/* Weight buffers, all row-major, element type = config.dtype (for MOE_FP8_E4M3: router_w bf16,
+ * the four expert matrices FP8 E4M3 codes). R = E + (I_s > 0 ? 1 : 0). */
 typedef struct {
     const void *router_w;       /* [R][H]; row E is the shared-expert gate row when I_s > 0 */
     const float *router_bias;   /* [R] fp32, added to the logits, or NULL */
@@ -80,6 +87,13 @@ typedef struct {
     const void *down;           /* [E][H][I] */
     const void *shared_gate_up; /* [2 I_s][H] (gate rows first); NULL iff I_s == 0 */
     const void *shared_down;    /* [H][I_s]; NULL iff I_s == 0 */
+    /* MOE_FP8_E4M3 only (NULL otherwise), fp32, one scale per row of the matrix above:
+     * gate_up_scale [E][2I], down_scale [E][H], shared_gate_up_scale [2 I_s] and
+     * shared_down_scale [H] (the last two NULL iff I_s == 0). 16-byte aligned. */
+    const float *gate_up_scale;
+    const float *down_scale;
+    const float *shared_gate_up_scale;
+    const float *shared_down_scale;
 } moe_weights;
 
 typedef struct moe_ctx moe_ctx;

@@ -24,6 +24,7 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 
 F32 = 0
 BF16 = 1
+FP8 = 2  # expert weights only: OCP FP8 E4M3 codes (numpy.uint8) with fp32 per-row scales
 
 _lock = threading.Lock()
 _lib = None
@@ -62,9 +63,13 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_select.argtypes = [i, i, i, P, i, i, P, P, P]
     lib.oracle_bucket.argtypes = [i, i, P, P, P, P]
     lib.oracle_forward.argtypes = [i, P, i, i, i, i, i, i, i, P, P, P, P, P, P, P, P, P]
+    lib.oracle_forward_w.argtypes = [i, P, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P, P, P, P,
+                                     P, P, P]
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
     for f in (lib.oracle_logits, lib.oracle_select, lib.oracle_bucket, lib.oracle_forward,
-              lib.oracle_num_threads):
+              lib.oracle_forward_w, lib.oracle_num_threads):
         f.restype = ctypes.c_int
     return lib
 
@@ -154,12 +159,27 @@ class Oracle:
         y = np.empty((tokens.size, H), dtype=np.float64)
         sgu = layer.get("shared_gate_up") if Is > 0 else None
         sdn = layer.get("shared_down") if Is > 0 else None
-        rc = self.lib.oracle_forward(tokens.size, _ptr(tokens), T, H, E, I, Is, k, dt, _ptr(x),
-                                     _ptr(layer["gate_up"]), _ptr(layer["down"]), _ptr(sgu),
-                                     _ptr(sdn), _ptr(ids), _ptr(w), _ptr(g), _ptr(y))
+        if layer["gate_up"].dtype == np.uint8:  # FP8 E4M3 codes with per-row scales
+            def f32(a):
+                return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+            sc = [f32(layer.get(n)) for n in ("gate_up_scale", "down_scale",
+                                              "shared_gate_up_scale", "shared_down_scale")]
+            rc = self.lib.oracle_forward_w(tokens.size, _ptr(tokens), T, H, E, I, Is, k, dt, FP8,
+                                           _ptr(x), _ptr(layer["gate_up"]), _ptr(layer["down"]),
+                                           _ptr(sgu), _ptr(sdn), *[_ptr(a) for a in sc],
+                                           _ptr(ids), _ptr(w), _ptr(g), _ptr(y))
+        else:
+            rc = self.lib.oracle_forward(tokens.size, _ptr(tokens), T, H, E, I, Is, k, dt,
+                                         _ptr(x), _ptr(layer["gate_up"]), _ptr(layer["down"]),
+                                         _ptr(sgu), _ptr(sdn), _ptr(ids), _ptr(w), _ptr(g),
+                                         _ptr(y))
         if rc:
             raise ValueError("oracle_forward rejected its arguments")
         return y
+
+    def e4m3_value(self, code: int) -> float:
+        """The value of one OCP FP8 E4M3 code (NaN for the two NaN codes)."""
+        return float(self.lib.oracle_e4m3_value(int(code)))
 
     def route(self, layer, logits_override=None):
         """Logits (fp32), then selection on them: the plain path from x to (ids, w, g)."""

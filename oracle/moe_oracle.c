@@ -31,6 +31,10 @@
  *   oracle_forward  for each requested token: sum over the eight ranks of w_k * FFN_{id_k}(x) plus
  *                   g * FFN_shared(x), where FFN(x) = Wd (silu(Wg x) * (Wu x)) and
  *                   silu(a) = a / (1 + exp(-a)); every step in fp64 with no intermediate rounding.
+ *   oracle_forward_w the same with FP8 expert weights: each weight is its E4M3 code's value times
+ *                   its row's fp32 scale, taken exactly in fp64 before the products (the pages
+ *                   name quantized expert formats - groupwise integers, FP8, NVFP4 - without
+ *                   fixing one; per-row scales over OCP E4M3 codes are the reading here).
  *
  * Comparison semantics: IEEE-754 fp32 values compared as values, so -0 equals +0 (a tie, decided
  * by the id). NaN ranks below every non-NaN value, -inf included; NaNs tie among themselves and
@@ -49,15 +53,40 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_FP8 2 /* weights only: OCP FP8 E4M3 codes, each row times its own fp32 scale */
+
+/* Value of one OCP FP8 E4M3 code (the 8-bit floating-point format of the Open Compute Project
+ * specification: sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, and
+ * S.1111.111 is NaN). Exponent field 0 holds the subnormals m * 2^-9; otherwise the value is
+ * 2^(e - 7) * (1 + m / 8). Exact in double. */
+double oracle_e4m3_value(uint8_t code) {
+    const int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+#ifdef ORACLE_PLANT_E4M3_BIAS8
+    if (e == 0) v = ldexp((double)m, -10); /* planted mistake: the other FP8 family's bias 8 */
+    else v = ldexp(1.0 + m / 8.0, e - 8);
+#else
+    if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp(1.0 + m / 8.0, e - 7);
+#endif
+    return s ? -v : v;
+}
 
 /* Widen one stored element to double. bf16 is the top half of an fp32 word, so the value is the
- * 16 stored bits shifted into the high half; the conversion is exact. */
+ * 16 stored bits shifted into the high half; the conversion is exact. An FP8 element is its
+ * code's value times the fp32 scale of its row (given by the caller). */
 static double load_elem(const void *base, int dtype, size_t i) {
     if (dtype == ORACLE_F32) return (double)((const float *)base)[i];
+    if (dtype == ORACLE_FP8) return oracle_e4m3_value(((const uint8_t *)base)[i]);
     uint32_t bits = ((uint32_t)((const uint16_t *)base)[i]) << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+static size_t elem_size(int dtype) {
+    return dtype == ORACLE_F32 ? 4 : dtype == ORACLE_FP8 ? 1 : 2;
 }
 
 /* ---------------------------------------------------------------- router logits */
@@ -160,13 +189,22 @@ int oracle_bucket(int n, int E, const int32_t *ids, int32_t *counts, int32_t *of
 
 /* ---------------------------------------------------------------- one SwiGLU FFN */
 /* o[H] = Wd (silu(Wg x) * (Wu x)); gate_up is [2*I][H] with the gate rows first, down is [H][I]. */
+/* With scales (FP8 weights): element (row, col) of a matrix is value(code) * scale[row]; gu_scale
+ * has 2I entries (gate rows, then up rows), dn_scale H. Without, the scales are 1. */
 static void swiglu_ffn(int H, int I, int dtype, const double *x, const void *gate_up,
-                       const void *down, double *hbuf, double *o) {
+                       const void *down, const float *gu_scale, const float *dn_scale,
+                       double *hbuf, double *o) {
     for (int i = 0; i < I; ++i) {
         double a = 0.0, u = 0.0;
+        const double sg = gu_scale ? (double)gu_scale[i] : 1.0;
+#ifdef ORACLE_PLANT_UP_SCALE_ROW
+        const double su = gu_scale ? (double)gu_scale[i] : 1.0; /* planted: the gate row's scale */
+#else
+        const double su = gu_scale ? (double)gu_scale[I + i] : 1.0;
+#endif
         for (int h = 0; h < H; ++h) {
-            a += load_elem(gate_up, dtype, (size_t)i * H + h) * x[h];
-            u += load_elem(gate_up, dtype, (size_t)(I + i) * H + h) * x[h];
+            a += load_elem(gate_up, dtype, (size_t)i * H + h) * sg * x[h];
+            u += load_elem(gate_up, dtype, (size_t)(I + i) * H + h) * su * x[h];
         }
 #ifdef ORACLE_PLANT_SWAP_GATE_UP
         { double tmp = a; a = u; u = tmp; } /* planted mistake: gate and up rows exchanged */
@@ -175,7 +213,8 @@ static void swiglu_ffn(int H, int I, int dtype, const double *x, const void *gat
     }
     for (int h = 0; h < H; ++h) {
         double acc = 0.0;
-        for (int i = 0; i < I; ++i) acc += load_elem(down, dtype, (size_t)h * I + i) * hbuf[i];
+        const double sd = dn_scale ? (double)dn_scale[h] : 1.0;
+        for (int i = 0; i < I; ++i) acc += load_elem(down, dtype, (size_t)h * I + i) * sd * hbuf[i];
         o[h] = acc;
     }
 }
@@ -183,16 +222,22 @@ static void swiglu_ffn(int H, int I, int dtype, const double *x, const void *gat
 /* ---------------------------------------------------------------- the layer output */
 /* For each token t = tokens[j] (j < n_tok): y[j][:] = sum_r w[t][r] * FFN_{ids[t][r]}(x_t)
  * + g[t] * FFN_shared(x_t). gate_up is [E][2I][H], down is [E][H][I]; the shared expert is
- * skipped when Is == 0. ids/w hold k entries per token; g may be NULL iff Is == 0. */
-int oracle_forward(int n_tok, const int32_t *tokens, int T, int H, int E, int I, int Is, int k,
-                   int dtype, const void *x, const void *gate_up, const void *down,
-                   const void *shared_gate_up, const void *shared_down, const int32_t *ids,
-                   const double *w, const double *g, double *y) {
+ * skipped when Is == 0. ids/w hold k entries per token; g may be NULL iff Is == 0. x has element
+ * type xdtype, the expert weights wdtype; with wdtype FP8 the four scale arrays give each weight
+ * row's scale: gu_scale [E][2I], dn_scale [E][H], sgu_scale [2Is], sdn_scale [H]. */
+int oracle_forward_w(int n_tok, const int32_t *tokens, int T, int H, int E, int I, int Is, int k,
+                     int xdtype, int wdtype, const void *x, const void *gate_up, const void *down,
+                     const void *shared_gate_up, const void *shared_down, const float *gu_scale,
+                     const float *dn_scale, const float *sgu_scale, const float *sdn_scale,
+                     const int32_t *ids, const double *w, const double *g, double *y) {
     if (n_tok < 0 || H <= 0 || E <= 0 || I <= 0 || Is < 0 || k <= 0) return -1;
+    if (xdtype != ORACLE_F32 && xdtype != ORACLE_BF16) return -1;
     if (Is > 0 && (!shared_gate_up || !shared_down || !g)) return -1;
+    const int scaled = wdtype == ORACLE_FP8;
+    if (scaled && (!gu_scale || !dn_scale || (Is > 0 && (!sgu_scale || !sdn_scale)))) return -1;
     for (int j = 0; j < n_tok; ++j)
         if (tokens[j] < 0 || tokens[j] >= T) return -1;
-    const size_t esz = dtype == ORACLE_F32 ? 4 : 2;
+    const size_t esz = elem_size(wdtype);
     const int Imax = I > Is ? I : Is;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
@@ -202,19 +247,21 @@ int oracle_forward(int n_tok, const int32_t *tokens, int T, int H, int E, int I,
         double *hb = (double *)malloc(sizeof(double) * (size_t)Imax);
         double *o = (double *)malloc(sizeof(double) * (size_t)H);
         double *yj = y + (size_t)j * H;
-        for (int h = 0; h < H; ++h) xt[h] = load_elem(x, dtype, (size_t)t * H + h);
+        for (int h = 0; h < H; ++h) xt[h] = load_elem(x, xdtype, (size_t)t * H + h);
         for (int h = 0; h < H; ++h) yj[h] = 0.0;
         for (int r = 0; r < k; ++r) {
             const int e = ids[(size_t)t * k + r];
             if (e < 0 || e >= E) { bad = 1; break; }
             const char *gu = (const char *)gate_up + (size_t)e * 2 * I * H * esz;
             const char *dn = (const char *)down + (size_t)e * H * I * esz;
-            swiglu_ffn(H, I, dtype, xt, gu, dn, hb, o);
+            swiglu_ffn(H, I, wdtype, xt, gu, dn, scaled ? gu_scale + (size_t)e * 2 * I : NULL,
+                       scaled ? dn_scale + (size_t)e * H : NULL, hb, o);
             const double wk = w[(size_t)t * k + r];
             for (int h = 0; h < H; ++h) yj[h] += wk * o[h];
         }
         if (Is > 0) {
-            swiglu_ffn(H, Is, dtype, xt, shared_gate_up, shared_down, hb, o);
+            swiglu_ffn(H, Is, wdtype, xt, shared_gate_up, shared_down, scaled ? sgu_scale : NULL,
+                       scaled ? sdn_scale : NULL, hb, o);
             for (int h = 0; h < H; ++h) yj[h] += g[t] * o[h];
         }
         free(xt);
@@ -222,6 +269,16 @@ int oracle_forward(int n_tok, const int32_t *tokens, int T, int H, int E, int I,
         free(o);
     }
     return bad ? -1 : 0;
+}
+
+/* The same with one element type for x and the weights (no scales). */
+int oracle_forward(int n_tok, const int32_t *tokens, int T, int H, int E, int I, int Is, int k,
+                   int dtype, const void *x, const void *gate_up, const void *down,
+                   const void *shared_gate_up, const void *shared_down, const int32_t *ids,
+                   const double *w, const double *g, double *y) {
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    return oracle_forward_w(n_tok, tokens, T, H, E, I, Is, k, dtype, dtype, x, gate_up, down,
+                            shared_gate_up, shared_down, NULL, NULL, NULL, NULL, ids, w, g, y);
 }
 
 /* Number of OpenMP threads a parallel region of this library uses (for reporting). */

@@ -20,6 +20,10 @@ MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_FP8_E4M3 = 2  # bf16 x and router; FP8 E4M3 expert weights with fp32 per-row scales
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+WEIGHT_KEYS = ("router_w", "router_bias", "gate_up", "down", "shared_gate_up", "shared_down",
+               "gate_up_scale", "down_scale", "shared_gate_up_scale", "shared_down_scale")
 
 EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_state_bytes",
            "moe_route", "moe_bucket",
@@ -34,9 +38,7 @@ class moe_config(ctypes.Structure):
 
 
 class moe_weights(ctypes.Structure):
-    _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
-                ("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p),
-                ("shared_gate_up", ctypes.c_void_p), ("shared_down", ctypes.c_void_p)]
+    _fields_ = [(k, ctypes.c_void_p) for k in WEIGHT_KEYS]
 
 
 _lib = None
@@ -105,7 +107,9 @@ class MoeLayer:
     """A context over device weight tensors (borrowed: the tensors are kept alive here).
 
     weights: dict with router_w [R][H], router_bias [R] fp32 or None, gate_up [E][2I][H],
-    down [E][H][I], shared_gate_up [2Is][H] or None, shared_down [H][Is] or None; bf16 weights
+    down [E][H][I], shared_gate_up [2Is][H] or None, shared_down [H][Is] or None, and for "fp8"
+    the row scales gate_up_scale [E][2I], down_scale [E][H], shared_gate_up_scale [2Is] and
+    shared_down_scale [H] (fp32) next to uint8 FP8 E4M3 codes; bf16 weights
     may be torch.bfloat16 or 16-bit integer tensors holding the bf16 bits.
     """
 
@@ -113,12 +117,10 @@ class MoeLayer:
                  top_k=8):
         self.lib = load()
         self.cfg = moe_config(hidden, num_experts, top_k, inter, shared_inter, max_tokens,
-                              MOE_BF16 if dtype == "bf16" else MOE_F32)
+                              DTYPES[dtype])
         self._keep = dict(weights)
-        w = moe_weights(*(
-            (None if weights.get(k) is None else weights[k].data_ptr())
-            for k in ("router_w", "router_bias", "gate_up", "down", "shared_gate_up",
-                      "shared_down")))
+        w = moe_weights(*((None if weights.get(k) is None else weights[k].data_ptr())
+                          for k in WEIGHT_KEYS))
         ctx = ctypes.c_void_p()
         _check(self.lib.moe_create(ctypes.byref(self.cfg), ctypes.byref(w), ctypes.byref(ctx)),
                "moe_create")
@@ -225,8 +227,7 @@ def device_weights(layer: dict, device="cuda") -> dict:
             a = a.view(np.int16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
-    return {k: dev(layer.get(k)) for k in ("router_w", "router_bias", "gate_up", "down",
-                                           "shared_gate_up", "shared_down", "x")}
+    return {k: dev(layer.get(k)) for k in WEIGHT_KEYS + ("x",)}
 
 
 def layer_from_numpy(layer: dict, max_tokens: int, device="cuda"):

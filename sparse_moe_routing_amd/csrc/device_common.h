@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -70,6 +72,73 @@ __device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cas
 __device__ __forceinline__ uint4 load16_stream(const void *p) {
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
     return uint4{v.x, v.y, v.z, v.w};
+}
+
+// Expert-weight storage formats. A weight "piece" is the Op::kPerLane elements one lane feeds to
+// one matrix-core fragment (16 bytes of operand data). WeightFmt<Op, false> stores the operand
+// type itself; WeightFmt<OpBF16, true> stores OCP FP8 E4M3 codes (8 bytes per piece) that are
+// widened to bf16 exactly on load (every E4M3 value is a bf16 value; gfx950 converts two codes
+// per instruction) and whose per-row scale is applied to the fp32 product afterwards:
+// sum_k (code_k * s) x_k = s * sum_k code_k x_k.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Codes of bytes 2*kHi and 2*kHi + 1 of w as two bf16 (low half: the lower byte).
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    const bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    return uint4{e4m3x2_to_bf16x2<false>(lo), e4m3x2_to_bf16x2<true>(lo),
+                 e4m3x2_to_bf16x2<false>(hi), e4m3x2_to_bf16x2<true>(hi)};
+}
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <class Op, bool kFp8>
+struct WeightFmt {
+    static_assert(!kFp8 || Op::kElemBytes == 2, "FP8 weights feed bf16 matrix-core operands");
+    using wt_t = typename std::conditional<kFp8, uint8_t, typename Op::elem_t>::type;
+    // a piece as stored (8 bytes of FP8 codes, 16 bytes otherwise), kept in registers until it
+    // is staged, so that FP8 holds twice the elements in flight in the same registers
+    using raw_t = typename std::conditional<kFp8, u32x2_t, uint4>::type;
+    static constexpr bool kScaled = kFp8;
+    __device__ static __forceinline__ raw_t load_raw(const wt_t *p) {
+        if constexpr (kFp8) return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+        else return load16_stream(p);
+    }
+    __device__ static __forceinline__ uint4 to_operand(const raw_t &r) {
+        if constexpr (kFp8) return e4m3x8_to_bf16x8(r.x, r.y);
+        else return r;
+    }
+    // one piece from p (element address), streamed (read once per call)
+    __device__ static __forceinline__ uint4 piece(const wt_t *p) {
+        if constexpr (kFp8) {
+            const u32x2_t c = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+            return e4m3x8_to_bf16x8(c.x, c.y);
+        } else {
+            return load16_stream(p);
+        }
+    }
+    // the same through the caches (weights other units re-read)
+    __device__ static __forceinline__ uint4 piece_cached(const wt_t *p) {
+        if constexpr (kFp8) {
+            const uint2 c = *reinterpret_cast<const uint2 *>(p);
+            return e4m3x8_to_bf16x8(c.x, c.y);
+        } else {
+            return load16(p);
+        }
+    }
+};
+
+// acc rows 4q + r (r = 0..3) of a tile times their row scales scale[0..3] (FP8 weights).
+__device__ __forceinline__ void scale_rows(f32x4_t &acc, const float *scale) {
+    const float4 s = *reinterpret_cast<const float4 *>(scale);
+    acc[0] *= s.x;
+    acc[1] *= s.y;
+    acc[2] *= s.z;
+    acc[3] *= s.w;
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

@@ -42,25 +42,30 @@ __device__ __forceinline__ uint4 lds_load16(const void *p) {
 // the operand reads - lane (row i, k-group q) takes piece 4s + q of row i for step s - hit 16
 // distinct bank groups. The up waves hand their 16x16 tiles to the gate waves through LDS, which
 // write h = silu(gate) * up.
-template <class Op>
+template <class Op, bool kFp8>
 __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
     using elem_t = typename Op::elem_t;
+    using WF = WeightFmt<Op, kFp8>;
+    using wt_t = typename WF::wt_t;
     constexpr int kSW = 32;                           // intermediate rows per unit
     constexpr int kPieces = 16;                       // 16-byte pieces per row per chunk
     constexpr int kChunkElems = kPieces * Op::kPerLane;
     constexpr int kStepsPerChunk = kPieces / 4;       // 4 k-groups of one piece per step
-    constexpr int kDepth = 2;                         // chunks per load batch (double-buffered)
+    // chunks per load batch (two batches in flight); FP8 codes are half the bytes, so twice the
+    // chunks fill the same registers
+    constexpr int kDepth = kFp8 ? 4 : 2;
+    constexpr int kStageBufs = 2;                     // LDS chunk buffers per wave
     constexpr int kStage = kTile * kPieces * 16;      // 4 KB of LDS per chunk per wave
 
     extern __shared__ __align__(16) unsigned char smem[];
     elem_t *xs = reinterpret_cast<elem_t *>(smem);
     unsigned char *stage_all = smem + (size_t)p.NG * p.x_stride * sizeof(elem_t);
-    float *xchg = reinterpret_cast<float *>(stage_all + 4 * kDepth * kStage);  // [2][16][16] up tiles
+    float *xchg = reinterpret_cast<float *>(stage_all + 4 * kStageBufs * kStage);  // [2][16][16] up tiles
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, q = lane >> 4;
-    unsigned char *stage = stage_all + wave * kDepth * kStage;
+    unsigned char *stage = stage_all + wave * kStageBufs * kStage;
     const int nunits = p.num_groups[0] * p.S;
     const int chunks_per_row = p.H / Op::kPerLane;
     const int nchunks = p.H / kChunkElems;
@@ -76,34 +81,36 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
         const int Ie = shared ? p.Is : p.I;
         if (j * kSW >= Ie) continue;  // uniform over the block
 
-        const elem_t *gu = reinterpret_cast<const elem_t *>(shared ? p.sgu : p.gate_up) +
-                           (shared ? 0 : (size_t)e * 2 * Ie * p.H);
+        const wt_t *gu = reinterpret_cast<const wt_t *>(shared ? p.sgu : p.gate_up) +
+                         (shared ? 0 : (size_t)e * 2 * Ie * p.H);
         const int wrow0 = (wave < 2 ? 0 : Ie) + j * kSW + (wave & 1) * kTile;  // first weight row
-        const elem_t *src = gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
+        const wt_t *src = gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
         const bool col_ok = col < n;
         const int crow = col_ok ? col : 0;  // columns >= n repeat column 0 (dropped)
         const elem_t *xrow = xs + crow * p.x_stride + q * Op::kPerLane;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 
-        uint4 rA[kDepth][4], rB[kDepth][4];
-        auto load = [&](uint4(&r)[kDepth][4], int c0) {
+        using raw_t = typename WF::raw_t;
+        raw_t rA[kDepth][4], rB[kDepth][4];
+        auto load = [&](raw_t(&r)[kDepth][4], int c0) {
 #pragma unroll
             for (int d = 0; d < kDepth; ++d)
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     const int c = min(c0 + d, nchunks - 1);  // past the end: re-read, unused
-                    r[d][a] = load16_stream(src + (size_t)(4 * a) * p.H + c * kChunkElems);
+                    r[d][a] = WF::load_raw(src + (size_t)(4 * a) * p.H + c * kChunkElems);
                 }
         };
-        auto consume = [&](const uint4(&r)[kDepth][4], int c0) {
+        auto consume = [&](const raw_t(&r)[kDepth][4], int c0) {
 #pragma unroll
             for (int d = 0; d < kDepth; ++d) {
                 if (c0 + d >= nchunks) break;  // uniform
-                unsigned char *buf = stage + d * kStage;
+                unsigned char *buf = stage + (d % kStageBufs) * kStage;  // a wave's LDS ops stay in order
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     const int rr = 4 * a + lrow;
-                    *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) = r[d][a];
+                    *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) =
+                        WF::to_operand(r[d][a]);
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
@@ -136,6 +143,8 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
             }
         }
 
+        if constexpr (WF::kScaled)  // the rows' dequantization scales (gate rows, then up rows)
+            scale_rows(acc, (shared ? p.sgu_scale : p.gu_scale + (size_t)e * 2 * Ie) + wrow0 + 4 * q);
         // up waves hand their tiles over; gate waves form h
         if (wave >= 2) {
             *reinterpret_cast<f32x4_t *>(xchg + ((wave - 2) * kTile + col) * kTile + 4 * q) = acc;
@@ -203,9 +212,11 @@ __device__ void combine_rows(const DownParams &p, int h0, int tid) {
 // slot of each of the group's (token, rank) pairs. Weight rows stream as in gateup_kernel: each
 // load instruction reads 256 contiguous bytes of each of 4 rows, and a per-wave LDS buffer with
 // the same XOR swizzle turns 16 x 256-byte chunks into matrix-core operands.
-template <class Op>
+template <class Op, bool kFp8>
 __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
     using elem_t = typename Op::elem_t;
+    using WF = WeightFmt<Op, kFp8>;
+    using wt_t = typename WF::wt_t;
     using h_t = typename Op::elem_t;                // h planes share the operand type
     constexpr int kRowsPerUnit = 64;
     constexpr int kPieces = 16;
@@ -238,18 +249,18 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
         const bool shared = e == p.E;
         const int Ie = shared ? p.Is : p.I;
         const int nchunks = Ie / kChunkElems;
-        const elem_t *dn = reinterpret_cast<const elem_t *>(shared ? p.sdn : p.down) +
-                           (shared ? 0 : (size_t)e * p.H * Ie);
-        const elem_t *src =
+        const wt_t *dn = reinterpret_cast<const wt_t *>(shared ? p.sdn : p.down) +
+                         (shared ? 0 : (size_t)e * p.H * Ie);
+        const wt_t *src =
             dn + (size_t)(rc * kRowsPerUnit + wave * kTile + lrow) * Ie + lpiece * Op::kPerLane;
-        uint4 a[kBatch][4];
+        typename WF::raw_t a[kBatch][4];
         auto load = [&](int c0) {
 #pragma unroll
             for (int d = 0; d < kBatch; ++d)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int c = min(c0 + d, nchunks - 1);  // past the end: re-read, unused
-                    a[d][r] = load16_stream(src + (size_t)(4 * r) * Ie + c * kChunkElems);
+                    a[d][r] = WF::load_raw(src + (size_t)(4 * r) * Ie + c * kChunkElems);
                 }
         };
         load(0);  // the weight stream does not depend on h: start it before staging h
@@ -280,7 +291,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int rr = 4 * r + lrow;
-                    *reinterpret_cast<uint4 *>(stage + rr * 256 + ((lpiece ^ rr) & 15) * 16) = a[d][r];
+                    *reinterpret_cast<uint4 *>(stage + rr * 256 + ((lpiece ^ rr) & 15) * 16) =
+                        WF::to_operand(a[d][r]);
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
@@ -292,6 +304,9 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
                 }
             }
         }
+        if constexpr (WF::kScaled)  // the output rows' dequantization scales
+            scale_rows(acc, (shared ? p.sdn_scale : p.dn_scale + (size_t)e * p.H) + rc * kRowsPerUnit +
+                                wave * kTile + 4 * q);
         if (col_ok) {
             const int slot = shared ? p.T * kTopK + start + col : p.perm[start + col];
             const float wt = shared ? p.g[start + col] : p.w[slot];
@@ -320,26 +335,29 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
 }
 
 hipError_t prepare_split_kernels(size_t gateup_lds, size_t down_lds) {
+    const void *gk[] = {reinterpret_cast<const void *>(&gateup_kernel<OpBF16, false>),
+                        reinterpret_cast<const void *>(&gateup_kernel<OpF32, false>),
+                        reinterpret_cast<const void *>(&gateup_kernel<OpBF16, true>)};
+    const void *dk[] = {reinterpret_cast<const void *>(&down_kernel<OpBF16, false>),
+                        reinterpret_cast<const void *>(&down_kernel<OpF32, false>),
+                        reinterpret_cast<const void *>(&down_kernel<OpBF16, true>)};
     hipError_t err;
-    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_kernel<OpBF16>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)gateup_lds)) !=
-        hipSuccess)
-        return err;
-    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_kernel<OpF32>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)gateup_lds)) !=
-        hipSuccess)
-        return err;
-    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&down_kernel<OpBF16>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)down_lds)) !=
-        hipSuccess)
-        return err;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&down_kernel<OpF32>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)down_lds);
+    for (const void *k : gk)
+        if ((err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)gateup_lds)) != hipSuccess)
+            return err;
+    for (const void *k : dk)
+        if ((err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)down_lds)) != hipSuccess)
+            return err;
+    return hipSuccess;
 }
 
+// dtype: 0 fp32, 1 bf16, 2 bf16 activations with FP8 E4M3 weights
 hipError_t launch_gateup(const GateUpParams &p, int dtype, int grid, size_t lds, hipStream_t s) {
-    if (dtype == 1) launch_k(gateup_kernel<OpBF16>, grid, kThreads, lds, s, p);
-    else launch_k(gateup_kernel<OpF32>, grid, kThreads, lds, s, p);
+    if (dtype == 2) launch_k(gateup_kernel<OpBF16, true>, grid, kThreads, lds, s, p);
+    else if (dtype == 1) launch_k(gateup_kernel<OpBF16, false>, grid, kThreads, lds, s, p);
+    else launch_k(gateup_kernel<OpF32, false>, grid, kThreads, lds, s, p);
     return hipGetLastError();
 }
 
@@ -347,8 +365,9 @@ size_t gateup_stage_bytes() { return 4 * 2 * 4096 + 2 * 16 * 16 * 4; }
 size_t down_stage_bytes() { return 4 * 4096; }
 
 hipError_t launch_down(const DownParams &p, int dtype, int grid, size_t lds, hipStream_t s) {
-    if (dtype == 1) launch_k(down_kernel<OpBF16>, grid, kThreads, lds, s, p);
-    else launch_k(down_kernel<OpF32>, grid, kThreads, lds, s, p);
+    if (dtype == 2) launch_k(down_kernel<OpBF16, true>, grid, kThreads, lds, s, p);
+    else if (dtype == 1) launch_k(down_kernel<OpBF16, false>, grid, kThreads, lds, s, p);
+    else launch_k(down_kernel<OpF32, false>, grid, kThreads, lds, s, p);
     return hipGetLastError();
 }
 

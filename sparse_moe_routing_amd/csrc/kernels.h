@@ -85,6 +85,7 @@ struct GateUpParams {
     int T, H, E, I, Is, Imax;
     int S;               // 32-row slices of Imax (units per group)
     int NG, x_stride;
+    const float *gu_scale, *sgu_scale;  // FP8 weights: per-row scales [E][2I], [2Is]; else null
 };
 
 struct DownParams {
@@ -100,6 +101,7 @@ struct DownParams {
     float *y;            // [T][H]
     int *rb_arrivals;    // [H / 64] zero at entry; left zero
     int T, H, E, I, Is, Imax, NG;
+    const float *dn_scale, *sdn_scale;  // FP8 weights: per-row scales [E][H], [H]; else null
 };
 
 struct CombineParams {

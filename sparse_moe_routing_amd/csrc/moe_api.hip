@@ -79,7 +79,14 @@ struct Plan {
            o_hist = 0, o_groups = 0, o_ngroups = 0, o_ypart = 0, o_h = 0, total = 0;
 };
 
-int elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+// Activation (x, router) element type of a config: bf16 for FP8 expert weights.
+int act_dtype(int dtype) { return dtype == MOE_F32 ? MOE_F32 : MOE_BF16; }
+// Bytes of one activation element.
+int elem_bytes(int dtype) { return act_dtype(dtype) == MOE_BF16 ? 2 : 4; }
+// Kernel variant of the router and routing kernels (0 fp32, 1 bf16) and of the expert kernels
+// (2: bf16 operands with FP8 E4M3 weights).
+int route_kdt(const moe_ctx *c);
+int expert_kdt(const moe_ctx *c);
 
 int max_groups_for(const moe_ctx *c, int T, int NG) {
     const int nsh = c->cfg.shared_inter > 0 ? (T + NG - 1) / NG : 0;
@@ -123,7 +130,7 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.x_stride = H + 16 / esz;
     const int ng_x = group_rows(c, T);  // x-tile rows of the split and fused expert kernels
     // the split and wide kernels stream weight rows in chunks of 16 x 16 bytes (128 bf16 / 64 fp32)
-    const int chunk = cfg.dtype == MOE_BF16 ? 128 : 64;
+    const int chunk = act_dtype(cfg.dtype) == MOE_BF16 ? 128 : 64;
     const bool chunk_ok = I % chunk == 0 && Is % chunk == 0;
     p.wide = T > kSplitMaxTokens && chunk_ok;
     p.NG = p.wide ? wide_group_tokens() : ng_x;
@@ -144,7 +151,7 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.Imax = Imax;
     p.gu_lds = (size_t)ng_x * p.x_stride * esz + gateup_stage_bytes();
     p.gu_S = Imax / 32;
-    p.down_lds = (size_t)ng_x * (Imax + 16 / esz) * esz * (cfg.dtype == MOE_BF16 ? 2 : 1) +
+    p.down_lds = (size_t)ng_x * (Imax + 16 / esz) * esz * (esz == 2 ? 2 : 1) +
                  down_stage_bytes();
     p.split = T <= kSplitMaxTokens && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds && chunk_ok;
     if (p.wide) {
@@ -284,7 +291,7 @@ RouterParams router_params(const moe_ctx *c, const Plan &p, const void *x, float
 
 void enqueue_router(Launcher &L, const moe_ctx *c, const Plan &p, const void *x, float *zpart) {
     const RouterParams rp = router_params(c, p, x, zpart);
-    L.step("router", [&] { return launch_router(rp, c->cfg.dtype, p.maxrt, L.stream); });
+    L.step("router", [&] { return launch_router(rp, route_kdt(c), p.maxrt, L.stream); });
 }
 
 RouterParams router_params(const moe_ctx *c, const Plan &p, const void *x, float *zpart) {
@@ -312,12 +319,12 @@ void enqueue_route_fused(Launcher &L, const moe_ctx *c, const Plan &p, const voi
     if (p.n_tt == 1) {
         L.step("route_fused", [&] {
             return launch_route_fused(rp, sp, bp, do_bucket, state + kStateRouteArrival,
-                                      c->cfg.dtype, L.stream);
+                                      route_kdt(c), L.stream);
         });
     } else {
         L.step("route_tiles", [&] {
             return launch_route_tiles(rp, sp, bp, do_bucket, state + kStateTileArrivals,
-                                      state + kStateTilesDone, c->cfg.dtype, L.stream);
+                                      state + kStateTilesDone, route_kdt(c), L.stream);
         });
     }
 }
@@ -414,15 +421,17 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         gp.S = p.gu_S;
         gp.NG = p.NG;
         gp.x_stride = p.x_stride;
+        gp.gu_scale = c->w.gate_up_scale;
+        gp.sgu_scale = c->w.shared_gate_up_scale;
         if (p.big)
             L.step("gateup_big", [&] { return launch_gateup_big(gp, p.gu_grid, L.stream); });
         else if (p.wide)
             L.step("gateup_wide", [&] {
-                return launch_gateup_wide(gp, c->cfg.dtype, p.gu_grid, L.stream);
+                return launch_gateup_wide(gp, expert_kdt(c), p.gu_grid, L.stream);
             });
         else
             L.step("gateup", [&] {
-                return launch_gateup(gp, c->cfg.dtype, p.gu_grid, p.gu_lds, L.stream);
+                return launch_gateup(gp, expert_kdt(c), p.gu_grid, p.gu_lds, L.stream);
             });
         DownParams dp{};
         dp.down = c->w.down;
@@ -444,9 +453,11 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         dp.I = c->cfg.inter;
         dp.Is = c->cfg.shared_inter;
         dp.Imax = p.Imax;
+        dp.dn_scale = c->w.down_scale;
+        dp.sdn_scale = c->w.shared_down_scale;
         if (p.wide) {
             L.step("down_wide", [&] {
-                return launch_down_wide(dp, c->cfg.dtype, p.down_grid, L.stream);
+                return launch_down_wide(dp, expert_kdt(c), p.down_grid, L.stream);
             });
             CombineParams cp{};
             cp.ypart = dp.ybuf;
@@ -462,7 +473,7 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
             L.step("combine", [&] { return launch_combine(cp, L.stream); });
         } else {
             L.step("down", [&] {
-                return launch_down(dp, c->cfg.dtype, p.down_grid, p.down_lds, L.stream);
+                return launch_down(dp, expert_kdt(c), p.down_grid, p.down_lds, L.stream);
             });
         }
         (void)ids_used;
@@ -511,8 +522,14 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
 }
 
 bool valid_inter(int v, int dtype) {
-    const int m = dtype == MOE_BF16 ? 32 : 16;
+    // FP8 weights run only the chunked expert kernels: 128-element weight-row chunks
+    const int m = dtype == MOE_FP8_E4M3 ? 128 : dtype == MOE_BF16 ? 32 : 16;
     return v >= m && v <= 4096 && v % m == 0;
+}
+
+int route_kdt(const moe_ctx *c) { return act_dtype(c->cfg.dtype) == MOE_BF16 ? 1 : 0; }
+int expert_kdt(const moe_ctx *c) {
+    return c->cfg.dtype == MOE_FP8_E4M3 ? 2 : c->cfg.dtype == MOE_BF16 ? 1 : 0;
 }
 
 }  // namespace
@@ -534,11 +551,12 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
     if (!out) return MOE_ERR_INVALID_ARG;
     *out = nullptr;
     if (!cfg || !weights) return MOE_ERR_INVALID_ARG;
-    if (cfg->dtype != MOE_F32 && cfg->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (cfg->dtype != MOE_F32 && cfg->dtype != MOE_BF16 && cfg->dtype != MOE_FP8_E4M3)
+        return MOE_ERR_INVALID_ARG;
     if (cfg->top_k != 8) return MOE_ERR_UNSUPPORTED;
     if (cfg->num_experts < 8 || cfg->num_experts > 256) return MOE_ERR_UNSUPPORTED;
     if (cfg->hidden < 64 || cfg->hidden > 16384 || cfg->hidden % 64) return MOE_ERR_UNSUPPORTED;
-    if (cfg->dtype == MOE_BF16 && cfg->hidden % 128) return MOE_ERR_UNSUPPORTED;
+    if (cfg->dtype != MOE_F32 && cfg->hidden % 128) return MOE_ERR_UNSUPPORTED;
     if (!valid_inter(cfg->inter, cfg->dtype)) return MOE_ERR_UNSUPPORTED;
     if (cfg->shared_inter != 0 && !valid_inter(cfg->shared_inter, cfg->dtype))
         return MOE_ERR_UNSUPPORTED;
@@ -554,6 +572,15 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
     for (const void *ptr : ptrs)
         if (ptr && !aligned(ptr, 16)) return MOE_ERR_INVALID_ARG;
     if (weights->router_bias && !aligned(weights->router_bias, 4)) return MOE_ERR_INVALID_ARG;
+    // row scales: all present (16-byte aligned) with FP8 weights, all absent otherwise
+    const float *scales[] = {weights->gate_up_scale, weights->down_scale,
+                             weights->shared_gate_up_scale, weights->shared_down_scale};
+    const bool fp8 = cfg->dtype == MOE_FP8_E4M3;
+    for (int i = 0; i < 4; ++i) {
+        const bool need = fp8 && (i < 2 || has_shared);
+        if (need != (scales[i] != nullptr)) return MOE_ERR_INVALID_ARG;
+        if (scales[i] && !aligned(scales[i], 16)) return MOE_ERR_INVALID_ARG;
+    }
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;

@@ -39,23 +39,24 @@ __device__ __forceinline__ uint4 lds_read16(const unsigned char *p) {
     return *reinterpret_cast<const uint4 *>(p);
 }
 
-// Weight chunk of one wave: rows lrow + 4a (a = 0..3) of the wave's 16, 256 bytes each.
-template <class Op>
-__device__ __forceinline__ void load_wchunk(uint4 (&r)[4], const typename Op::elem_t *src,
+// Weight chunk of one wave: rows lrow + 4a (a = 0..3) of the wave's 16, 16 pieces each (256
+// bytes of bf16 or fp32, 128 bytes of FP8 codes widened to bf16).
+template <class WF, int kCE>
+__device__ __forceinline__ void load_wchunk(typename WF::raw_t (&r)[4], const typename WF::wt_t *src,
                                             size_t row_stride, int c) {
-    constexpr int kCE = kWPieces * Op::kPerLane;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) r[a] = load16_stream(src + (size_t)(4 * a) * row_stride + c * kCE);
+    for (int a = 0; a < 4; ++a) r[a] = WF::load_raw(src + (size_t)(4 * a) * row_stride + c * kCE);
 }
 
 // Swizzled staging (row rr, piece p at rr * 256 + ((p ^ rr) & 15) * 16) and operand read of
 // step s (piece 4s + q of row col).
-__device__ __forceinline__ void stage_w(unsigned char *buf, const uint4 (&r)[4], int lrow,
-                                        int lpiece) {
+template <class WF>
+__device__ __forceinline__ void stage_w(unsigned char *buf, const typename WF::raw_t (&r)[4],
+                                        int lrow, int lpiece) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int rr = 4 * a + lrow;
-        *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) = r[a];
+        *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) = WF::to_operand(r[a]);
     }
 }
 __device__ __forceinline__ uint4 w_operand(const unsigned char *buf, int s, int col, int q) {
@@ -65,9 +66,11 @@ __device__ __forceinline__ uint4 w_operand(const unsigned char *buf, int s, int 
 
 }  // namespace
 
-template <class Op, int NT>
+template <class Op, int NT, bool kFp8>
 __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) {
     using elem_t = typename Op::elem_t;
+    using WF = WeightFmt<Op, kFp8>;
+    using wt_t = typename WF::wt_t;
     constexpr int TG = NT * kTile;
     constexpr int kCE = kWPieces * Op::kPerLane;
     constexpr int kSteps = kWPieces / 4;
@@ -99,10 +102,10 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
         if (j * kSW >= Ie) continue;  // uniform over the block
         const int nt_used = (n + kTile - 1) / kTile;
 
-        const elem_t *gu = reinterpret_cast<const elem_t *>(shared ? p.sgu : p.gate_up) +
-                           (shared ? 0 : (size_t)e * 2 * Ie * p.H);
+        const wt_t *gu = reinterpret_cast<const wt_t *>(shared ? p.sgu : p.gate_up) +
+                         (shared ? 0 : (size_t)e * 2 * Ie * p.H);
         const int wrow0 = (wave < kGW ? 0 : Ie) + j * kSW + (wave % kGW) * kTile;
-        const elem_t *src = gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
+        const wt_t *src = gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
         const elem_t *xsrc[kXPasses];
 #pragma unroll
         for (int i = 0; i < kXPasses; ++i) {
@@ -111,7 +114,11 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
             const int tok = shared ? start + rr : (p.perm[start + rr] >> 3);
             xsrc[i] = x + (size_t)tok * p.H + xp * Op::kPerLane;
         }
-        uint4 wA[4], wB[4], xv[kXPasses];
+        // weight chunks in flight: a ring of kWD register buffers (FP8 codes are half the bytes,
+        // so twice the chunks fill the same registers)
+        constexpr int kWD = kFp8 ? 4 : 2;
+        typename WF::raw_t wr[kWD][4];
+        uint4 xv[kXPasses];
         // a pass whose rows all lie past n is skipped (uniform): the columns those rows feed are
         // dropped, whatever the stale LDS holds
         auto load_x = [&](int c) {
@@ -130,16 +137,17 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
 #pragma unroll
         for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        load_wchunk<Op>(wA, src, p.H, 0);
-        if (1 < nchunks) load_wchunk<Op>(wB, src, p.H, 1);
+#pragma unroll
+        for (int d = 0; d < kWD; ++d)
+            if (d < nchunks) load_wchunk<WF, kCE>(wr[d], src, p.H, d);
         load_x(0);
         __syncthreads();  // the previous unit's readers of xs / xchg are done
         store_x(0);
-        auto step = [&](uint4 (&wcur)[4], int c) {
+        auto step = [&](typename WF::raw_t (&wcur)[4], int c) {
             if (c + 1 < nchunks) load_x(c + 1);
             __syncthreads();  // x chunk c is staged; chunk c - 1's readers are done
-            stage_w(stage, wcur, lrow, lpiece);
-            if (c + 2 < nchunks) load_wchunk<Op>(wcur, src, p.H, c + 2);
+            stage_w<WF>(stage, wcur, lrow, lpiece);
+            if (c + kWD < nchunks) load_wchunk<WF, kCE>(wcur, src, p.H, c + kWD);
             const unsigned char *xb = xs + (c & 1) * TG * kXRow;
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
@@ -151,11 +159,17 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
             }
             if (c + 1 < nchunks) store_x((c + 1) & 1);
         };
-        for (int c = 0; c < nchunks; c += 2) {
-            step(wA, c);
-            if (c + 1 < nchunks) step(wB, c + 1);
+        for (int c = 0; c < nchunks; c += kWD) {
+#pragma unroll
+            for (int d = 0; d < kWD; ++d)
+                if (c + d < nchunks) step(wr[d], c + d);  // uniform
         }
 
+        if constexpr (WF::kScaled) {  // the rows' dequantization scales (gate rows, then up rows)
+            const float *sc = (shared ? p.sgu_scale : p.gu_scale + (size_t)e * 2 * Ie) + wrow0 + 4 * q;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) scale_rows(acc[tt], sc);
+        }
         // up waves hand their tiles over (into their own stage buffers, free now); gate waves
         // form h
         static_assert(kGW * NT * kTile * kTile * 4 <= kGW * kWStage, "exchange exceeds the up stages");
@@ -198,9 +212,11 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
     }
 }
 
-template <class Op, int NT>
+template <class Op, int NT, bool kFp8>
 __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
     using elem_t = typename Op::elem_t;
+    using WF = WeightFmt<Op, kFp8>;
+    using wt_t = typename WF::wt_t;
     constexpr int TG = NT * kTile;
     constexpr int kCE = kWPieces * Op::kPerLane;
     constexpr int kSteps = kWPieces / 4;
@@ -229,13 +245,13 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
         const int Ie = shared ? p.Is : p.I;
         const int nchunks = Ie / kCE;
         const int nt_used = (n + kTile - 1) / kTile;
-        const elem_t *dn = reinterpret_cast<const elem_t *>(shared ? p.sdn : p.down) +
-                           (shared ? 0 : (size_t)e * p.H * Ie);
+        const wt_t *dn = reinterpret_cast<const wt_t *>(shared ? p.sdn : p.down) +
+                         (shared ? 0 : (size_t)e * p.H * Ie);
         // rows rc * 256 + wave * 32 + tile * 16 + ...: one contiguous 32-row block per wave; a wave
         // past H (H is a multiple of 32) only joins the block barriers
         const int wrow = rc * kRowsPerUnit + wave * kDownTiles * kTile;
         const bool rows_ok = wrow < p.H;  // uniform over the wave
-        const elem_t *src = dn + (size_t)((rows_ok ? wrow : 0) + lrow) * Ie + lpiece * Op::kPerLane;
+        const wt_t *src = dn + (size_t)((rows_ok ? wrow : 0) + lrow) * Ie + lpiece * Op::kPerLane;
         const elem_t *hsrc[kHPasses];
 #pragma unroll
         for (int i = 0; i < kHPasses; ++i) {
@@ -244,11 +260,13 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
             const int slot = shared ? p.T * kTopK + start + rr : p.perm[start + rr];
             hsrc[i] = hg + (size_t)slot * p.Imax + hp * Op::kPerLane;
         }
-        uint4 wA[kDownTiles][4], wB[kDownTiles][4], hv[kPlanes][kHPasses];
-        auto load_w = [&](uint4 (&w)[kDownTiles][4], int c) {
+        constexpr int kWD = kFp8 ? 4 : 2;  // weight chunks in flight (ring of register buffers)
+        typename WF::raw_t wr[kWD][kDownTiles][4];
+        uint4 hv[kPlanes][kHPasses];
+        auto load_w = [&](typename WF::raw_t (&w)[kDownTiles][4], int c) {
 #pragma unroll
             for (int t = 0; t < kDownTiles; ++t)
-                load_wchunk<Op>(w[t], src + (size_t)(t * kTile) * Ie, Ie, c);
+                load_wchunk<WF, kCE>(w[t], src + (size_t)(t * kTile) * Ie, Ie, c);
         };
         // (unlike x, every pass is loaded: skipping passes here measured slower - the branches
         // break the load pipelining across chunks)
@@ -273,19 +291,20 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
             for (int i = 0; i < NT; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         if (rows_ok) {
-            load_w(wA, 0);
-            if (1 < nchunks) load_w(wB, 1);
+#pragma unroll
+            for (int d = 0; d < kWD; ++d)
+                if (d < nchunks) load_w(wr[d], d);
         }
         load_h(0);
         __syncthreads();  // the previous unit's readers of hs are done
         store_h(0);
-        auto step = [&](uint4 (&wcur)[kDownTiles][4], int c) {
+        auto step = [&](typename WF::raw_t (&wcur)[kDownTiles][4], int c) {
             if (c + 1 < nchunks) load_h(c + 1);
             __syncthreads();  // h chunk c is staged; chunk c - 1's readers are done
             if (rows_ok) {
 #pragma unroll
-                for (int t = 0; t < kDownTiles; ++t) stage_w(stage + t * kWStage, wcur[t], lrow, lpiece);
-                if (c + 2 < nchunks) load_w(wcur, c + 2);
+                for (int t = 0; t < kDownTiles; ++t) stage_w<WF>(stage + t * kWStage, wcur[t], lrow, lpiece);
+                if (c + kWD < nchunks) load_w(wcur, c + kWD);
             }
 #pragma unroll
             for (int s = 0; s < kSteps && rows_ok; ++s) {
@@ -306,11 +325,21 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
             }
             if (c + 1 < nchunks) store_h((c + 1) & 1);
         };
-        for (int c = 0; c < nchunks; c += 2) {
-            step(wA, c);
-            if (c + 1 < nchunks) step(wB, c + 1);
+        for (int c = 0; c < nchunks; c += kWD) {
+#pragma unroll
+            for (int d = 0; d < kWD; ++d)
+                if (c + d < nchunks) step(wr[d], c + d);  // uniform
         }
 
+        if constexpr (WF::kScaled) {  // the output rows' dequantization scales
+            if (rows_ok) {
+                const float *sc = (shared ? p.sdn_scale : p.dn_scale + (size_t)e * p.H) + wrow + 4 * q;
+#pragma unroll
+                for (int t = 0; t < kDownTiles; ++t)
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) scale_rows(acc[t][tt], sc + t * kTile);
+            }
+        }
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             const int cc = tt * kTile + col;
@@ -501,29 +530,35 @@ hipError_t launch_gateup_big(const GateUpParams &p, int grid, hipStream_t s) {
 
 hipError_t prepare_wide_kernels() {
     hipError_t err;
-    const void *gk[] = {reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT>),
-                        reinterpret_cast<const void *>(&gateup_wide_kernel<OpF32, kWideNT>)};
+    const void *gk[] = {reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT, false>),
+                        reinterpret_cast<const void *>(&gateup_wide_kernel<OpF32, kWideNT, false>),
+                        reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT, true>)};
     for (const void *k : gk)
         if ((err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)gateup_wide_lds())) != hipSuccess)
             return err;
-    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&down_wide_kernel<OpBF16, kWideNT>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)down_wide_lds(1))) != hipSuccess)
-        return err;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&down_wide_kernel<OpF32, kWideNT>),
+    const void *dk16[] = {reinterpret_cast<const void *>(&down_wide_kernel<OpBF16, kWideNT, false>),
+                          reinterpret_cast<const void *>(&down_wide_kernel<OpBF16, kWideNT, true>)};
+    for (const void *k : dk16)
+        if ((err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)down_wide_lds(1))) != hipSuccess)
+            return err;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&down_wide_kernel<OpF32, kWideNT, false>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)down_wide_lds(0));
 }
 
+// dtype: 0 fp32, 1 bf16, 2 bf16 activations with FP8 E4M3 weights
 hipError_t launch_gateup_wide(const GateUpParams &p, int dtype, int grid, hipStream_t s) {
-    if (dtype == 1) launch_k(gateup_wide_kernel<OpBF16, kWideNT>, grid, kWThreads, gateup_wide_lds(), s, p);
-    else launch_k(gateup_wide_kernel<OpF32, kWideNT>, grid, kWThreads, gateup_wide_lds(), s, p);
+    if (dtype == 2) launch_k(gateup_wide_kernel<OpBF16, kWideNT, true>, grid, kWThreads, gateup_wide_lds(), s, p);
+    else if (dtype == 1) launch_k(gateup_wide_kernel<OpBF16, kWideNT, false>, grid, kWThreads, gateup_wide_lds(), s, p);
+    else launch_k(gateup_wide_kernel<OpF32, kWideNT, false>, grid, kWThreads, gateup_wide_lds(), s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_down_wide(const DownParams &p, int dtype, int grid, hipStream_t s) {
-    if (dtype == 1) launch_k(down_wide_kernel<OpBF16, kWideNT>, grid, kWThreads, down_wide_lds(1), s, p);
-    else launch_k(down_wide_kernel<OpF32, kWideNT>, grid, kWThreads, down_wide_lds(0), s, p);
+    if (dtype == 2) launch_k(down_wide_kernel<OpBF16, kWideNT, true>, grid, kWThreads, down_wide_lds(1), s, p);
+    else if (dtype == 1) launch_k(down_wide_kernel<OpBF16, kWideNT, false>, grid, kWThreads, down_wide_lds(1), s, p);
+    else launch_k(down_wide_kernel<OpF32, kWideNT, false>, grid, kWThreads, down_wide_lds(0), s, p);
     return hipGetLastError();
 }
 

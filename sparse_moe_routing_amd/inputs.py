@@ -20,7 +20,12 @@ float32):
   4. shared expert: gate [Is][H], up [Is][H] (1/sqrt(H)), down [H][Is] (1/sqrt(Is));
   5. x [T][H], unscaled N(0, 1).
 bf16 workloads round every draw to bf16 with round-to-nearest-even and store the raw bits as
-uint16. gate and up are stored stacked as gate_up [E][2I][H] (gate rows first); down is
+uint16. fp8 workloads store x and the router weight as bf16 and quantize each expert weight row
+(routed and shared, gate, up and down alike) to OCP FP8 E4M3 codes (uint8) with one float32
+scale per row: scale = max|row| / 448 (1 for an all-zero row), code = the E4M3 value nearest to
+v / scale (ties to the even code), so the row's largest magnitude becomes 448; the scales are
+stored next to the codes as gate_up_scale [E][2I], down_scale [E][H], shared_gate_up_scale
+[2Is], shared_down_scale [H]. gate and up are stored stacked as gate_up [E][2I][H] (gate rows first); down is
 [E][H][I] (the nn.Linear convention: output rows, input columns contiguous).
 
 Tie tokens: selected tokens have every router score replaced by the nearest multiple of 0.25
@@ -43,7 +48,8 @@ class Workload:
     top_k: int
     inter: int
     shared_inter: int
-    dtype: str            # "f32" or "bf16": storage type of x and of every weight
+    dtype: str            # "f32" or "bf16": storage type of x and of every weight; "fp8": x and
+                          # the router in bf16, expert weights as FP8 E4M3 codes + row scales
     bias_std: float = 0.0  # > 0: per-expert router bias ~ N(0, bias_std^2)
     tie_every: int = 0     # > 0: tokens t with t % tie_every == 0 get tie-quantized logits
     seed: int = 0
@@ -56,6 +62,12 @@ WORKLOADS = (
     Workload("verify_skewed_t192", 192, 2048, 256, 8, 512, 512, "bf16", bias_std=2.0 ** 0.5,
              seed=3),
     Workload("prefill_t8192", 8192, 2048, 256, 8, 512, 512, "bf16", tie_every=10, seed=4),
+    # the same rounds with FP8 E4M3 expert weights (x and router in bf16)
+    Workload("decode_b1_t4_fp8", 4, 2048, 256, 8, 512, 512, "fp8", seed=11),
+    Workload("decode_b8_t32_fp8", 32, 2048, 256, 8, 512, 512, "fp8", seed=12),
+    Workload("verify_skewed_t192_fp8", 192, 2048, 256, 8, 512, 512, "fp8",
+             bias_std=2.0 ** 0.5, seed=13),
+    Workload("prefill_t8192_fp8", 8192, 2048, 256, 8, 512, 512, "fp8", tie_every=10, seed=14),
 )
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -72,11 +84,47 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def f32_to_e4m3_codes(a: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes of float32 values (nearest, ties to the even code; magnitudes above the
+    largest finite value 448 saturate to it). Sign bit, then 4 exponent bits (bias 7) and 3
+    mantissa bits; exponent field 0 holds the subnormal multiples of 2^-9."""
+    a = np.asarray(a, dtype=np.float32)
+    sign = (a.view(np.uint32) >> np.uint32(24)).astype(np.uint8) & np.uint8(0x80)
+    v = np.minimum(np.abs(a), np.float32(448.0))
+    # normal range (v >= 2^-6): round the float32 significand to 3 bits, nearest-even; a carry
+    # into the exponent falls out of the integer add
+    b = v.view(np.uint32)
+    b = b + np.uint32(0x7FFFF) + ((b >> np.uint32(20)) & np.uint32(1))
+    ex = (b >> np.uint32(23)).astype(np.int32) - 127
+    code_n = ((ex + 7) << 3) | ((b >> np.uint32(20)) & np.uint32(7)).astype(np.int32)
+    # subnormal range: multiples of 2^-9 (8 * 2^-9 is 2^-6, whose code is 8)
+    code_s = np.rint(v * np.float32(512.0)).astype(np.int32)
+    code = np.where(v >= np.float32(2.0 ** -6), code_n, code_s)
+    return code.astype(np.uint8) | sign
+
+
+def quantize_rows_e4m3(v: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row FP8 E4M3 quantization of a float32 matrix [..., rows, cols]: (codes, scales)."""
+    v = np.asarray(v, dtype=np.float32)
+    amax = np.max(np.abs(v), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return f32_to_e4m3_codes(v / scale[..., None]), scale
+
+
 def _draw(rng, shape, scale, dtype):
     v = rng.standard_normal(shape, dtype=np.float32)
     if scale != 1.0:
         v *= np.float32(scale)
+    if dtype == "fp8":  # activations and the router stay bf16 in fp8 workloads
+        dtype = "bf16"
     return f32_to_bf16_bits(v) if dtype == "bf16" else v
+
+
+def _draw_w(rng, shape, scale, dtype):
+    """An expert weight block: as _draw, or (codes, per-row scales) for fp8."""
+    if dtype != "fp8":
+        return _draw(rng, shape, scale, dtype), None
+    return quantize_rows_e4m3(_draw(rng, shape, scale, "f32"))
 
 
 def make_layer(w: Workload, tokens: int | None = None, seed: int | None = None) -> dict:
@@ -98,23 +146,36 @@ def make_layer(w: Workload, tokens: int | None = None, seed: int | None = None) 
         layer["router_bias"] = b
     else:
         layer["router_bias"] = None
+    fp8 = w.dtype == "fp8"
+    if fp8:
+        st = np.uint8
     gate_up = np.empty((E, 2 * I, H), dtype=st)
     down = np.empty((E, H, I), dtype=st)
+    gu_s = np.empty((E, 2 * I), dtype=np.float32) if fp8 else None
+    dn_s = np.empty((E, H), dtype=np.float32) if fp8 else None
     for e in range(E):
-        gate_up[e, :I] = _draw(rng, (I, H), H ** -0.5, w.dtype)
-        gate_up[e, I:] = _draw(rng, (I, H), H ** -0.5, w.dtype)
-        down[e] = _draw(rng, (H, I), I ** -0.5, w.dtype)
+        gate_up[e, :I], sg = _draw_w(rng, (I, H), H ** -0.5, w.dtype)
+        gate_up[e, I:], su = _draw_w(rng, (I, H), H ** -0.5, w.dtype)
+        down[e], sd = _draw_w(rng, (H, I), I ** -0.5, w.dtype)
+        if fp8:
+            gu_s[e, :I], gu_s[e, I:], dn_s[e] = sg, su, sd
     layer["gate_up"] = gate_up
     layer["down"] = down
+    layer["gate_up_scale"] = gu_s
+    layer["down_scale"] = dn_s
     if Is > 0:
         sgu = np.empty((2 * Is, H), dtype=st)
-        sgu[:Is] = _draw(rng, (Is, H), H ** -0.5, w.dtype)
-        sgu[Is:] = _draw(rng, (Is, H), H ** -0.5, w.dtype)
+        sgu[:Is], sg = _draw_w(rng, (Is, H), H ** -0.5, w.dtype)
+        sgu[Is:], su = _draw_w(rng, (Is, H), H ** -0.5, w.dtype)
         layer["shared_gate_up"] = sgu
-        layer["shared_down"] = _draw(rng, (H, Is), Is ** -0.5, w.dtype)
+        layer["shared_down"], sd = _draw_w(rng, (H, Is), Is ** -0.5, w.dtype)
+        layer["shared_gate_up_scale"] = np.concatenate([sg, su]) if fp8 else None
+        layer["shared_down_scale"] = sd
     else:
         layer["shared_gate_up"] = None
         layer["shared_down"] = None
+        layer["shared_gate_up_scale"] = None
+        layer["shared_down_scale"] = None
     layer["x"] = _draw(rng, (T, H), 1.0, w.dtype)
     return layer
 

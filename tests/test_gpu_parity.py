@@ -176,9 +176,12 @@ def tie_gap_ok(z_o_row, ids_g_row, ids_o_row, E, zgap):
 
 
 FULL = ["decode_b1_t4", "decode_b8_t32", "verify_skewed_t192", "prefill_t8192"]
+# FP8 E4M3 expert weights (bf16 x and router): the split path (T = 4), the 64-token-group path
+# (T = 192, skewed) and the prefill chunk with tie tokens
+FULL8 = ["decode_b1_t4_fp8", "verify_skewed_t192_fp8", "prefill_t8192_fp8"]
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL)
+@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL + FULL8)
 def test_route_fused(orc, name):
     torch = _torch()
     layer, m, t = get_layer(name)
@@ -241,7 +244,7 @@ def routing_device(ids, w, g):
             None if g is None else torch.from_numpy(np.ascontiguousarray(g, np.float32)).cuda())
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL)
+@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL + FULL8)
 def test_forward_given_oracle_routing(orc, name):
     """y from the oracle's own routing (all tokens routed by the oracle, tie tokens from their
     quantized logits), checked on a token sample against the oracle's fp64 forward."""
@@ -261,7 +264,7 @@ def test_forward_given_oracle_routing(orc, name):
     del allrows
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL)
+@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL + FULL8)
 def test_forward_tie_tokens_route_then_forward(orc, name):
     """The tie protocol: quantized logits through moe_route(logits_in), its routing into
     moe_forward; the oracle routes the same logits itself."""
@@ -282,7 +285,7 @@ def test_forward_tie_tokens_route_then_forward(orc, name):
     assert_close(y.cpu().numpy()[rows], y_o, f"{name} y (tie protocol)")
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL)
+@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL + FULL8)
 def test_forward_internal_routing(orc, name):
     """The whole hot path from x (the launch configuration the benchmark times)."""
     torch = _torch()
@@ -499,6 +502,21 @@ def test_batch_invariance_bitwise():
     torch.cuda.synchronize()
     assert m.plan(4097)[4] == "gateup_big"
     assert torch.equal(y4097[:32], y32) and torch.equal(y4097[4064:4096], y32)
+
+
+def test_fp8_batch_invariance_bitwise():
+    """FP8 weights: a token's output bits do not depend on its batch, across the split path
+    (T <= 64) and the 64-token-group path (T > 64)."""
+    torch = _torch()
+    layer, m, t = get_layer("decode_b1_t4_fp8")
+    x = torch.cat([t["x"]] * 8)  # 32 tokens
+    y32 = m.forward(x)
+    y4 = m.forward(x[:4].contiguous())
+    y200 = m.forward(torch.cat([x] * 7)[:200].contiguous())
+    torch.cuda.synchronize()
+    assert m.plan(32)[-1] == "down" and m.plan(200)[-3:] == ["gateup_wide", "down_wide", "combine"]
+    assert torch.equal(y32[:4], y4)
+    assert torch.equal(y200[:32], y32) and torch.equal(y200[192:200], y32[:8])
 
 
 def test_token_permutation_equivariance():

@@ -109,6 +109,43 @@ def test_create_rejects_bad_weights(lib):
         binding.MOE_ERR_INVALID_ARG
 
 
+def test_create_checks_fp8_weights(lib):
+    """FP8 E4M3 expert weights need every row-scale array (16-byte aligned) and 128-element
+    multiples for I and I_s; other dtypes must not pass scales."""
+    cfg = good_config()
+    cfg.dtype = binding.MOE_FP8_E4M3
+    base = 0x20000000
+
+    def fp8_weights(shared=True):
+        w = fake_weights(shared)
+        w.gate_up_scale = base
+        w.down_scale = base + 0x100000
+        w.shared_gate_up_scale = base + 0x200000 if shared else None
+        w.shared_down_scale = base + 0x300000 if shared else None
+        return w
+
+    for name in ("gate_up_scale", "down_scale", "shared_gate_up_scale", "shared_down_scale"):
+        w = fp8_weights()
+        setattr(w, name, None)
+        assert create(lib, cfg, w)[0] == binding.MOE_ERR_INVALID_ARG, name
+        w = fp8_weights()
+        setattr(w, name, getattr(w, name) + 4)  # 4-byte but not 16-byte aligned
+        assert create(lib, cfg, w)[0] == binding.MOE_ERR_INVALID_ARG, name
+    cfg0 = good_config()
+    cfg0.dtype = binding.MOE_FP8_E4M3
+    cfg0.shared_inter = 0  # no shared expert: no shared scales either
+    w = fp8_weights(shared=False)
+    w.shared_down_scale = base + 0x300000
+    assert create(lib, cfg0, w)[0] == binding.MOE_ERR_INVALID_ARG
+    bf = good_config()  # bf16 weights take no scales
+    assert create(lib, bf, fp8_weights())[0] == binding.MOE_ERR_INVALID_ARG
+    for field, value in (("inter", 96), ("shared_inter", 160), ("hidden", 192)):
+        c = good_config()
+        c.dtype = binding.MOE_FP8_E4M3
+        setattr(c, field, value)
+        assert create(lib, c, fp8_weights())[0] == binding.MOE_ERR_UNSUPPORTED, field
+
+
 def test_calls_reject_null_context(lib):
     assert lib.moe_workspace_bytes(None, 4) == 0
     assert lib.moe_route(None, None, None, 4, None, None, None, None, None, 0, None) == \

@@ -279,10 +279,80 @@ def pin_golden_hand_example(orc):
     assert abs(g[1] - float(rec["g2_approx"])) < 1e-7
 
 
+def pin_e4m3_values(orc):
+    """The OCP FP8 E4M3 code points that the format's definition fixes: zero and negative zero,
+    the smallest subnormal 2^-9, the smallest normal 2^-6, 1, 2, 1.875, the largest finite 448,
+    NaN at S.1111.111 and no infinities; positive codes 0x00..0x7E strictly increasing and the
+    negative half their mirror."""
+    v = orc.e4m3_value
+    assert v(0x00) == 0.0 and math.copysign(1.0, v(0x00)) == 1.0
+    assert v(0x80) == 0.0 and math.copysign(1.0, v(0x80)) == -1.0
+    assert v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9
+    assert v(0x08) == 2.0 ** -6 and v(0x38) == 1.0 and v(0x40) == 2.0 and v(0x3F) == 1.875
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0
+    assert math.isnan(v(0x7F)) and math.isnan(v(0xFF))
+    pos = [v(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(pos, pos[1:]))
+    assert all(v(0x80 | c) == -pos[c] for c in range(1, 0x7F))
+    assert len(set(pos)) == 127 and all(math.isfinite(x) for x in pos)
+
+
+def pin_e4m3_quantizer_round_trip(orc):
+    """The input quantizer (nearest code, ties to the even code) maps every finite code value
+    back to its code and every midpoint between neighbours to the even one of the two."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    vals = np.array([orc.e4m3_value(int(c)) for c in codes], np.float32)
+    assert np.array_equal(inputs.f32_to_e4m3_codes(vals), codes)
+    pos = np.array([orc.e4m3_value(c) for c in range(0x7F)], np.float64)
+    mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    got = inputs.f32_to_e4m3_codes(mid).astype(np.int64)
+    lo = np.arange(126)
+    assert np.all((got == lo) | (got == lo + 1)) and np.all(got % 2 == 0)
+    assert inputs.f32_to_e4m3_codes(np.array([1e6, -1e6], np.float32)).tolist() == [0x7E, 0xFE]
+
+
+def pin_fp8_forward_equals_bf16(orc):
+    """FP8 weights with power-of-two row scales are exactly bf16 values (E4M3 has 3 mantissa bits),
+    so the oracle's FP8 forward must equal its bf16 forward on those values, with every row's
+    own scale (each row of gate, up and down gets a different power of two)."""
+    rng = np.random.default_rng(31)
+    T, H, E, I, Is = 3, 32, 8, 16, 24
+    lay16 = {"num_experts": E, "inter": I, "shared_inter": Is, "top_k": 8, "dtype": "bf16"}
+    lay8 = dict(lay16, dtype="fp8")
+
+    def block(rows, cols):
+        codes = rng.integers(0, 256, size=(rows, cols)).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x38  # no NaN codes
+        scale = (2.0 ** rng.integers(-12, -4, size=rows)).astype(np.float32)
+        vals = np.array([[orc.e4m3_value(int(c)) for c in r] for r in codes], np.float64)
+        bits = inputs.f32_to_bf16_bits((vals * scale[:, None]).astype(np.float32))
+        assert np.array_equal(inputs.bf16_bits_to_f32(bits), (vals * scale[:, None]).astype(np.float32))
+        return codes, scale, bits
+
+    gu8, gus, gu16 = zip(*[block(2 * I, H) for _ in range(E)])
+    dn8, dns, dn16 = zip(*[block(H, I) for _ in range(E)])
+    sgu8, sgus, sgu16 = block(2 * Is, H)
+    sdn8, sdns, sdn16 = block(H, Is)
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    lay16.update(x=x, gate_up=np.stack(gu16), down=np.stack(dn16), shared_gate_up=sgu16,
+                 shared_down=sdn16)
+    lay8.update(x=x, gate_up=np.stack(gu8), down=np.stack(dn8), shared_gate_up=sgu8,
+                shared_down=sdn8, gate_up_scale=np.stack(gus), down_scale=np.stack(dns),
+                shared_gate_up_scale=sgus, shared_down_scale=sdns)
+    ids = np.stack([rng.permutation(E) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, E))
+    w /= w.sum(1, keepdims=True)
+    g = rng.random(T)
+    y16 = orc.forward(lay16, ids, w, g)
+    y8 = orc.forward(lay8, ids, w, g)
+    assert np.abs(y8 - y16).max() <= 1e-12 * max(1.0, np.abs(y16).max())
+
+
 PINS = [pin_select_vs_library_sort, pin_select_special_cases, pin_weights_closed_form, pin_gate,
         pin_logits_integer_exact, pin_logits_random_vs_matmul, pin_bucket_vs_argsort,
         pin_ffn_dense_equivalence, pin_ffn_shared_alone_and_zero, pin_ffn_routed_mixture,
-        pin_golden_hand_example]
+        pin_golden_hand_example, pin_e4m3_values, pin_e4m3_quantizer_round_trip,
+        pin_fp8_forward_equals_bf16]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -312,6 +382,8 @@ PLANTS = {
     "ORACLE_PLANT_SWAP_W67": [pin_weights_closed_form, pin_golden_hand_example],
     "ORACLE_PLANT_SWAP_GATE_UP": [pin_ffn_dense_equivalence, pin_ffn_routed_mixture],
     "ORACLE_PLANT_DROP_BIAS": [pin_logits_integer_exact, pin_logits_random_vs_matmul],
+    "ORACLE_PLANT_E4M3_BIAS8": [pin_e4m3_values, pin_e4m3_quantizer_round_trip],
+    "ORACLE_PLANT_UP_SCALE_ROW": [pin_fp8_forward_equals_bf16],
 }
 
 
