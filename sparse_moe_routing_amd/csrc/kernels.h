@@ -124,6 +124,10 @@ hipError_t launch_route_tiles(const RouterParams &rp, const SelectParams &sp,
 hipError_t launch_select_hist(const SelectParams &sp, const BucketParams &bp, bool do_select,
                               bool do_hist, hipStream_t s);
 hipError_t launch_bucket_scan(const BucketParams &bp, hipStream_t s);
+// 64 < T <= 256: selection (optional) and the whole bucketing in one launch; arrivals: a zeroed
+// workspace state word, left zero
+hipError_t launch_select_bucket(const SelectParams &sp, const BucketParams &bp, bool do_select,
+                                int *arrivals, hipStream_t s);
 hipError_t launch_bucket_scatter(const BucketParams &bp, hipStream_t s);
 hipError_t launch_expert(const ExpertParams &p, int dtype, int grid, size_t lds_bytes,
                          hipStream_t s);

@@ -49,6 +49,7 @@ constexpr int kRouterSplit = 4;  // the quarters of router_core.h
 // finished tiles and its per-tile arrival counters (up to 16 tiles), then (from word 64) the
 // down kernel's per-64-row-block arrival counters
 constexpr int kStateRouteArrival = 0;
+constexpr int kStateSelectArrival = 1;  // select_bucket's arrival counter
 constexpr int kStateTilesDone = 4;
 constexpr int kStateTileArrivals = 8;
 constexpr int kStateRowBlocks = 64;
@@ -57,6 +58,8 @@ constexpr int kStateRowBlocks = 64;
 constexpr int kTileRouteMaxTokens = 64;
 // T > 64: tokens per selection / histogram block (one wave per token in a 1024-thread block)
 constexpr int kHistChunk = 16;
+// 64 < T <= 256: selection and bucketing in one launch (select_bucket)
+constexpr int kSelBucketMaxTokens = 256;
 constexpr int kSplitMaxTokens = 64;   // 16-token groups up to here, 64-token groups above
 constexpr int kBigMinTokens = 3072;     // bf16 from here: gateup_big in place of gateup_wide
 
@@ -330,7 +333,17 @@ void enqueue_route_fused(Launcher &L, const moe_ctx *c, const Plan &p, const voi
 }
 
 // Bucketing from ids already in memory (or selection + bucketing when sp is given).
-void enqueue_dispatch(Launcher &L, const Plan &p, const SelectParams *sp, BucketParams bp) {
+void enqueue_dispatch(Launcher &L, const Plan &p, const SelectParams *sp, BucketParams bp,
+                      char *ws) {
+    if (!p.small && p.T <= kSelBucketMaxTokens) {
+        SelectParams dummy{};
+        const SelectParams &s = sp ? *sp : dummy;
+        int *arrivals = reinterpret_cast<int *>(ws + p.o_state) + kStateSelectArrival;
+        L.step("select_bucket", [&] {
+            return launch_select_bucket(s, bp, sp != nullptr, arrivals, L.stream);
+        });
+        return;
+    }
     if (p.small) {
         SelectParams dummy{};
         const SelectParams &s = sp ? *sp : dummy;
@@ -394,13 +407,13 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
             enqueue_route_fused(L, c, p, x, zpart, sp, bp, true, ws);
         } else {
             enqueue_router(L, c, p, x, zpart);
-            enqueue_dispatch(L, p, &sp, bp);
+            enqueue_dispatch(L, p, &sp, bp, ws);
         }
     } else {
         ids_used = ids_in;
         w_used = w_in;
         g_used = gate_in;
-        enqueue_dispatch(L, p, nullptr, bucket_params(c, p, ws, ids_in, counts, offsets, perm));
+        enqueue_dispatch(L, p, nullptr, bucket_params(c, p, ws, ids_in, counts, offsets, perm), ws);
     }
     if (p.split || p.wide) {
         GateUpParams gp{};
@@ -675,8 +688,8 @@ int moe_bucket(const moe_ctx *c, const int32_t *ids_in, int32_t T, int32_t *coun
     const int st = check_call(c, T, workspace, ws_bytes, &p);
     if (st != MOE_OK) return st;
     Launcher L{c, stream, nullptr, 0, true};
-    enqueue_dispatch(L, p, nullptr,
-                     bucket_params(c, p, static_cast<char *>(workspace), ids_in, counts, offsets, perm));
+    char *ws = static_cast<char *>(workspace);
+    enqueue_dispatch(L, p, nullptr, bucket_params(c, p, ws, ids_in, counts, offsets, perm), ws);
     return hip_status(L.err);
 }
 

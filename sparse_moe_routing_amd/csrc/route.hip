@@ -32,6 +32,7 @@ namespace moe {
 // ----------------------------------------------------------------------------- bucketing
 constexpr int kChunkTokens = 64;                       // most tokens one bucketing block takes
 constexpr int kChunkPairs = kChunkTokens * kTopK;      // 512 pairs
+constexpr int kSelBucketPairs = 256 * kTopK;           // select_bucket_kernel: T <= 256
 
 // LDS of the bucketing of up to kPairs pairs (sub-chunks of 64 pairs, one wave ballot each).
 template <int kPairs>
@@ -309,6 +310,44 @@ __global__ __launch_bounds__(1024) void select_hist_kernel(SelectParams sp, Buck
     if (tid < bp.E) bp.hist[(size_t)blockIdx.x * bp.E + tid] = cnt;
 }
 
+// 64 < T <= 256: per 16-token chunk (one wave per token) the selection (optional); the chunk's
+// ids are published device-coherently and the last chunk block to finish (an arrival counter in
+// the workspace state, reset by that block) buckets all T*8 pairs in one pass, as route_small
+// does: one launch in place of the histogram, scan and scatter passes.
+using BucketWide = BucketSharedT<kSelBucketPairs>;
+__global__ __launch_bounds__(1024) void select_bucket_kernel(SelectParams sp, BucketParams bp,
+                                                            int do_select, int *arrivals) {
+    __shared__ BucketWide s;
+    __shared__ int s_last;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int T = bp.T;
+    const int t0 = blockIdx.x * bp.chunk_tokens;
+    const int nt = min(bp.chunk_tokens, T - t0);
+    if (do_select) {
+#pragma unroll 1
+        for (int i = wave; i < nt; i += 16)
+            select_token(sp, t0 + i, lane, s.ids + i * kTopK, s.sel[wave]);
+        __syncthreads();
+        for (int i = tid; i < nt * kTopK; i += blockDim.x)
+            st_dev(sp.ids + (size_t)t0 * kTopK + i, s.ids[i]);  // read by the last block below
+        wait_own_stores();
+    }
+    __syncthreads();
+    if (tid == 0) {
+        s_last = atomicAdd(arrivals, 1) == (int)gridDim.x - 1;
+        if (s_last) arrivals[0] = 0;  // every chunk has arrived: reset for the next call
+    }
+    __syncthreads();
+    if (!s_last) return;  // uniform over the block
+    const int n = T * kTopK;
+    for (int i = tid; i < n; i += blockDim.x) s.ids[i] = do_select ? ld_dev(sp.ids + i) : bp.ids_in[i];
+    __syncthreads();
+    const int cnt = chunk_counts(s, n, bp.E);
+    write_tables(bp, cnt, s);  // ends with a barrier; s.a[e] = offset of expert e
+    chunk_scatter(s, n, bp.E, 0, bp.perm, [&](int e) { return s.a[e]; });
+}
+
 // T > 64, pass 2 (one block): per-expert running bases over chunks, counts, offsets, groups.
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketParams bp) {
     __shared__ int s_part[4][256];
@@ -401,6 +440,14 @@ hipError_t launch_select_hist(const SelectParams &sp, const BucketParams &bp, bo
     const int T = do_select ? sp.T : bp.T;
     launch_k(select_hist_kernel, (T + bp.chunk_tokens - 1) / bp.chunk_tokens, 1024, 0, s, 
         sp, bp, do_select ? 1 : 0, do_hist ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_bucket(const SelectParams &sp, const BucketParams &bp, bool do_select,
+                                int *arrivals, hipStream_t s) {
+    if (bp.T > kSelBucketPairs / kTopK) return hipErrorInvalidValue;  // a caller bug
+    const int grid = (bp.T + bp.chunk_tokens - 1) / bp.chunk_tokens;
+    launch_k(select_bucket_kernel, grid, 1024, 0, s, sp, bp, do_select ? 1 : 0, arrivals);
     return hipGetLastError();
 }
 

@@ -556,14 +556,15 @@ def test_call_errors_and_empty():
     tiny = get_layer("tiny_fp32_t4")[1]  # I = 32 is below the weight-row chunk of the split path
     assert tiny.plan(4) == ["route_fused", "expert", "combine"]
     wide = ["gateup_wide", "down_wide", "combine"]
-    assert m.plan(65) == ["router", "select_hist", "bucket_scan", "bucket_scatter"] + wide
-    assert m.plan(3071) == m.plan(65)
+    # 64 < T <= 256: selection and bucketing in one launch; above, histogram / scan / scatter
+    assert m.plan(65) == m.plan(256) == ["router", "select_bucket"] + wide
+    chained = ["router", "select_hist", "bucket_scan", "bucket_scatter"]
+    assert m.plan(257) == m.plan(3071) == chained + wide
     big = ["gateup_big", "down_wide", "combine"]  # bf16 from 3072 tokens
-    assert m.plan(3072) == m.plan(8192) == ["router", "select_hist", "bucket_scan",
-                                             "bucket_scatter"] + big
-    assert m.plan(200, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
-    assert tiny.plan(200) == ["router", "select_hist", "bucket_scan", "bucket_scatter", "expert",
-                              "combine"]
+    assert m.plan(3072) == m.plan(8192) == chained + big
+    assert m.plan(200, routing_given=True) == ["select_bucket"] + wide
+    assert m.plan(300, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
+    assert tiny.plan(200) == ["router", "select_bucket", "expert", "combine"]
 
 
 def test_forward_timed_events():
