@@ -84,25 +84,32 @@ __device__ __forceinline__ void merge_level(uint64_t (&r)[8]) {
 // Per-wave LDS scratch of select_token: up to 64 candidate keys, then the eight winners.
 constexpr int kSelScratch = kWave + kTopK;
 
+// Lower bound of the wave's 8th largest lane maximum (value halves): the smallest of the maxima
+// of the eight groups of 8 lanes. Those are eight keys of distinct lanes, all >= the bound, so
+// the 8th largest key is >= it too. Register-to-register lane moves only: maxima within 8 lanes
+// (quad permutations, half-row mirror), then minima across the groups (row mirror, then the
+// row-pair and half-wave swaps).
+__device__ __forceinline__ uint32_t eighth_bound(uint32_t h) {
+    h = max(h, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0xB1, 0xF, 0xF, false));
+    h = max(h, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0x4E, 0xF, 0xF, false));
+    h = max(h, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0x141, 0xF, 0xF, false));
+    h = min(h, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0x140, 0xF, 0xF, false));
+    h = min(h, partner32<4>(h));
+    return min(h, partner32<5>(h));
+}
+
 // The eight largest keys of the wave (each lane holds four, sorted), largest first: lane i < 8
 // gets the i-th in `mine`; `top` is the largest on every lane.
 //
 // Most keys cannot be among the eight, so the exact answer is taken from a short candidate list:
-// let v8 be the 8th largest of the lane maxima's value halves (a bitwise search with wave
-// ballots); at least eight keys have a value half >= v8, so every one of the eight winners does
-// too, and only lanes whose maximum reaches v8 - at most eight lanes unless values tie - hold such
-// keys. The candidates are packed into LDS; each one's rank is the number of candidates above it,
+// let v8 be a lower bound of the 8th largest key's value half (eighth_bound); every one of the
+// eight winners has a value half >= v8, so the keys reaching v8 - about twenty for untied logits -
+// are candidates. They are packed into LDS; each one's rank is the number of candidates above it,
 // and a candidate's rank among them is its rank among all keys (every key above a winner is a
 // winner). With more than 64 candidates (heavy ties) the merge network runs instead.
 __device__ __forceinline__ void top8_of_wave(const uint64_t (&c)[4], int lane, uint64_t *scr,
                                              uint64_t &mine, uint64_t &top) {
-    const uint32_t hmax = (uint32_t)(c[0] >> 32);
-    uint32_t v8 = 0;
-#pragma unroll
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = v8 | (1u << b);
-        if (__popcll(__ballot(hmax >= cand)) >= kTopK) v8 = cand;
-    }
+    const uint32_t v8 = eighth_bound((uint32_t)(c[0] >> 32));
     int n = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) n += (uint32_t)(c[j] >> 32) >= v8 ? 1 : 0;
