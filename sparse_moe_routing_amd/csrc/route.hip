@@ -111,6 +111,19 @@ __device__ void chunk_scatter(const S &s, int n, int E, int p0, int32_t *perm, B
     }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves (no LDS round trips):
+// shifts by 1, 2, 4, 8 inside each 16-lane row, then each row adds the total of the row before
+// (broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 to rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 to rows 2, 3
+    return v;
+}
+
 // Exclusive scans over experts of s.a and s.b (256 entries each, by wave 0 of the block).
 // Every thread of the block calls it.
 template <class S>
@@ -127,16 +140,7 @@ __device__ void scan_experts(S &s) {
         }
         const int sa = a[0] + a[1] + a[2] + a[3];
         const int sb = b[0] + b[1] + b[2] + b[3];
-        int ia = sa, ib = sb;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int ua = __shfl_up(ia, d, kWave);
-            const int ub = __shfl_up(ib, d, kWave);
-            if (l >= d) {
-                ia += ua;
-                ib += ub;
-            }
-        }
+        const int ia = wave_inclusive_sum(sa), ib = wave_inclusive_sum(sb);
         int ea = ia - sa, eb = ib - sb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -214,10 +214,12 @@ __device__ inline void select_token(const SelectParams &p, int t, int lane, int3
     const float top = key_value((uint32_t)(topkey >> 32));
     const float v = key_value((uint32_t)(mine >> 32));
     const float ex = expf(v - top);
+    // the sum over lanes 0..7 (pairs, then quads, then the two quads of the half row): every
+    // lane of the eight gets the same bits
     float sum = ex;
-    sum += __shfl_xor(sum, 1, kWave);
-    sum += __shfl_xor(sum, 2, kWave);
-    sum += __shfl_xor(sum, 4, kWave);
+    sum += __uint_as_float(__builtin_amdgcn_update_dpp(0, __float_as_uint(sum), 0xB1, 0xF, 0xF, false));
+    sum += __uint_as_float(__builtin_amdgcn_update_dpp(0, __float_as_uint(sum), 0x4E, 0xF, 0xF, false));
+    sum += __uint_as_float(__builtin_amdgcn_update_dpp(0, __float_as_uint(sum), 0x141, 0xF, 0xF, false));
     if (lane < kTopK) {
         const int id = (int)~(uint32_t)mine;
         p.ids[(size_t)t * kTopK + lane] = id;
