@@ -105,7 +105,8 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
 /* Release a context (NULL is ignored). Does not free the borrowed weights. */
 void moe_destroy(moe_ctx *ctx);
 
-/* Bytes of workspace a call with T tokens needs (0 when T <= 0 or ctx is NULL). */
+/* Bytes of workspace that serve every call with 1..T tokens (0 when T <= 0 or ctx is NULL): a
+ * workspace sized for T can be reused for any smaller token count. */
 size_t moe_workspace_bytes(const moe_ctx *ctx, int32_t T);
 
 /* Size of the leading state region of every workspace of ctx (the same for every T; a multiple

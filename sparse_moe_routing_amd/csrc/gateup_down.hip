@@ -214,7 +214,6 @@ __device__ void combine_rows(const DownParams &p, int h0, int tid) {
 // the same XOR swizzle turns 16 x 256-byte chunks into matrix-core operands.
 template <class Op, bool kFp8>
 __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
-    using elem_t = typename Op::elem_t;
     using WF = WeightFmt<Op, kFp8>;
     using wt_t = typename WF::wt_t;
     using h_t = typename Op::elem_t;                // h planes share the operand type

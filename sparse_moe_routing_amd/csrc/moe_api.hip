@@ -633,7 +633,11 @@ void moe_destroy(moe_ctx *ctx) { delete ctx; }
 
 size_t moe_workspace_bytes(const moe_ctx *ctx, int32_t T) {
     if (!ctx || T <= 0 || T > ctx->cfg.max_tokens) return 0;
-    return make_plan(ctx, T).total;
+    // the plans' needs grow with T inside each regime; should the decode regime's largest ever
+    // exceed the next regime's smallest, the larger of the two keeps the size monotone in T
+    const size_t need = make_plan(ctx, T).total;
+    const size_t decode = make_plan(ctx, T < kSplitMaxTokens ? T : kSplitMaxTokens).total;
+    return need > decode ? need : decode;
 }
 
 size_t moe_workspace_state_bytes(const moe_ctx *ctx) { return ctx ? state_bytes(ctx) : 0; }

@@ -590,6 +590,16 @@ def test_forward_timed_events():
             m.forward(x, events=evs[:-1])
 
 
+def test_workspace_bytes_monotone():
+    """A workspace sized for T serves every smaller token count: the size never decreases with T,
+    across the decode, 64-token-group and large-T plans."""
+    for name in ("decode_b1_t4", "decode_b1_t4_fp8", "tiny_fp32_t4"):
+        m = get_layer(name)[1]
+        sizes = [m.lib.moe_workspace_bytes(m.ctx, T) for T in list(range(1, 300)) + [3071, 3072, 8192]]
+        assert all(b > 0 for b in sizes)
+        assert all(a <= b for a, b in zip(sizes, sizes[1:])), name
+
+
 def test_workspace_state_left_zero():
     """The state region at the start of the workspace (arrival counters, work-queue words,
     flags, the sticky spin-limit word) is zero again after every call, whatever T."""
