@@ -123,7 +123,9 @@ hipError_t launch_route_tiles(const RouterParams &rp, const SelectParams &sp,
                               int *tiles_done, int dtype, hipStream_t s);
 hipError_t launch_select_hist(const SelectParams &sp, const BucketParams &bp, bool do_select,
                               bool do_hist, hipStream_t s);
-hipError_t launch_bucket_scan(const BucketParams &bp, hipStream_t s);
+// T > 256: per-expert chunk bases and the tables; arrivals: a zeroed workspace state word, left
+// zero
+hipError_t launch_bucket_scan(const BucketParams &bp, int *arrivals, hipStream_t s);
 // 64 < T <= 256: selection (optional) and the whole bucketing in one launch; arrivals: a zeroed
 // workspace state word, left zero
 hipError_t launch_select_bucket(const SelectParams &sp, const BucketParams &bp, bool do_select,

@@ -50,6 +50,7 @@ constexpr int kRouterSplit = 4;  // the quarters of router_core.h
 // down kernel's per-64-row-block arrival counters
 constexpr int kStateRouteArrival = 0;
 constexpr int kStateSelectArrival = 1;  // select_bucket's arrival counter
+constexpr int kStateScanArrival = 2;    // bucket_scan's arrival counter
 constexpr int kStateTilesDone = 4;
 constexpr int kStateTileArrivals = 8;
 constexpr int kStateRowBlocks = 64;
@@ -356,7 +357,8 @@ void enqueue_dispatch(Launcher &L, const Plan &p, const SelectParams *sp, Bucket
         L.step("select_hist", [&] { return launch_select_hist(s, bp, sp != nullptr, true, L.stream); });
     }
     if (sp) bp.ids_in = sp->ids;
-    L.step("bucket_scan", [&] { return launch_bucket_scan(bp, L.stream); });
+    int *scan_arrivals = reinterpret_cast<int *>(ws + p.o_state) + kStateScanArrival;
+    L.step("bucket_scan", [&] { return launch_bucket_scan(bp, scan_arrivals, L.stream); });
     L.step("bucket_scatter", [&] { return launch_bucket_scatter(bp, L.stream); });
 }
 

@@ -352,18 +352,25 @@ __global__ __launch_bounds__(1024) void select_bucket_kernel(SelectParams sp, Bu
     chunk_scatter(s, n, bp.E, 0, bp.perm, [&](int e) { return s.a[e]; });
 }
 
-// T > 64, pass 2 (one block): per-expert running bases over chunks, counts, offsets, groups.
-__global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketParams bp) {
-    __shared__ int s_part[4][256];
+// T > 256, pass 2: per-expert running bases over the chunks, then counts, offsets and the group
+// table. Wave w of block b owns expert e = 16 b + w: lane l takes a contiguous run of the
+// expert's chunks, the lanes' run sums are scanned with lane moves, and each lane rewrites its
+// chunks' histogram entries with their exclusive bases (chunk order). The expert's total goes to
+// counts[e] device-coherently; the last block to finish (an arrival counter in the workspace
+// state, reset by that block) builds the tables from all the totals, as the single-block form
+// did - spread over E / 16 blocks, the histogram reads no longer queue behind one CU.
+constexpr int kScanWaves = 16;
+__global__ __launch_bounds__(kScanWaves * kWave) void bucket_scan_kernel(BucketParams bp, int *arrivals) {
     __shared__ BucketShared s;
+    __shared__ int s_last;
     const int tid = threadIdx.x;
-    const int e = tid & 255, quarter = tid >> 8;
-    const int per = (bp.n_chunks + 3) / 4;
-    const int c0 = quarter * per, c1 = min(bp.n_chunks, c0 + per);
-    // loads in batches of 8 chunks issued together (clamped past the end, dropped)
-    constexpr int kB = 8;
-    int sum = 0;
-    if (e < bp.E) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int e = blockIdx.x * kScanWaves + wave;
+    if (e < bp.E) {  // uniform over the wave
+        const int per = (bp.n_chunks + kWave - 1) / kWave;
+        const int c0 = min(lane * per, bp.n_chunks), c1 = min(c0 + per, bp.n_chunks);
+        constexpr int kB = 8;  // loads issued together (clamped past the end, dropped)
+        int sum = 0;
         for (int c = c0; c < c1; c += kB) {
             int v[kB];
 #pragma unroll
@@ -371,12 +378,8 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketParams bp) {
 #pragma unroll
             for (int j = 0; j < kB; ++j) sum += c + j < c1 ? v[j] : 0;
         }
-    }
-    s_part[quarter][e] = sum;
-    __syncthreads();
-    int base = 0;
-    for (int qq = 0; qq < quarter; ++qq) base += s_part[qq][e];
-    if (e < bp.E) {
+        const int incl = wave_inclusive_sum(sum);
+        int base = incl - sum;
         for (int c = c0; c < c1; c += kB) {
             int v[kB];
 #pragma unroll
@@ -389,8 +392,17 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(BucketParams bp) {
                 }
             }
         }
+        if (lane == kWave - 1) st_dev(bp.counts + e, incl);  // the expert's total
     }
-    const int cnt = (tid < 256) ? s_part[0][e] + s_part[1][e] + s_part[2][e] + s_part[3][e] : 0;
+    wait_own_stores();
+    __syncthreads();
+    if (tid == 0) {
+        s_last = atomicAdd(arrivals, 1) == (int)gridDim.x - 1;
+        if (s_last) arrivals[0] = 0;  // every block has arrived: reset for the next call
+    }
+    __syncthreads();
+    if (!s_last) return;  // uniform over the block
+    const int cnt = tid < bp.E ? ld_dev(bp.counts + tid) : 0;
     write_tables(bp, cnt, s);
 }
 
@@ -455,8 +467,9 @@ hipError_t launch_select_bucket(const SelectParams &sp, const BucketParams &bp, 
     return hipGetLastError();
 }
 
-hipError_t launch_bucket_scan(const BucketParams &bp, hipStream_t s) {
-    launch_k(bucket_scan_kernel, 1, 1024, 0, s, bp);
+hipError_t launch_bucket_scan(const BucketParams &bp, int *arrivals, hipStream_t s) {
+    launch_k(bucket_scan_kernel, (bp.E + kScanWaves - 1) / kScanWaves, kScanWaves * kWave, 0, s, bp,
+             arrivals);
     return hipGetLastError();
 }
 

@@ -605,11 +605,11 @@ def test_workspace_state_left_zero():
     flags, the sticky spin-limit word) is zero again after every call, whatever T."""
     torch = _torch()
     layer, m, t = get_layer("decode_b1_t4", max_tokens=8192)
-    ws = m.workspace(200)
+    ws = m.workspace(300)
     n_state = m.state_bytes()
     assert 0 < n_state <= 64 * 1024 and n_state % 256 == 0
-    xs = torch.cat([t["x"]] * 64)
-    for T in (4, 32, 1, 7, 64, 200, 3):
+    xs = torch.cat([t["x"]] * 80)
+    for T in (4, 32, 1, 7, 64, 200, 3, 300):
         m.forward(xs[:T].contiguous(), ws=ws)
         m.route(x=t["x"], ws=ws)
         ids, wt, g = m.route(x=xs[:T].contiguous(), want_logits=False, ws=ws)[1:]
