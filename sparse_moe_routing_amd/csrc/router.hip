@@ -8,8 +8,9 @@ __global__ __launch_bounds__(256) void router_kernel(RouterParams p) {
     router_unit<Op, MAXRT>(p, blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
 }
 
-// Large T: each wave covers 4 row tiles x 4 token tiles of a quarter.
-constexpr int kRouterTT = 4;
+// Large T: each wave covers 4 row tiles x 2 token tiles of a quarter (two waves per SIMD, four
+// k steps of loads in flight per wave).
+constexpr int kRouterTT = 2;
 template <class Op>
 __global__ __launch_bounds__(256) void router_tt_kernel(RouterParams p) {
     router_unit_tt<Op, 4, kRouterTT>(p, blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);

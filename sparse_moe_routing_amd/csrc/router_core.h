@@ -181,7 +181,7 @@ __device__ __forceinline__ void router_unit_tt(const RouterParams &p, int u, int
         wrow[j] = reinterpret_cast<const elem_t *>(p.w) + (size_t)(wok[j] ? row : 0) * p.H + kbase;
     }
     const uint4 zero = {0u, 0u, 0u, 0u};
-    constexpr int kBatch = 2;
+    constexpr int kBatch = MAXTT >= 4 ? 2 : 4;  // k steps whose loads are issued together
     f32x4_t s[MAXRT][MAXTT], ch[MAXRT][MAXTT];
 #pragma unroll
     for (int j = 0; j < MAXRT; ++j)
