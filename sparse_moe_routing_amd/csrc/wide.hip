@@ -361,14 +361,16 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
 // operand traffic cut for the matrix-core-bound regime. Unit = (expert group of <= 64 tokens,
 // kBigRows * waves intermediate rows); wave w owns rows i0 .. i0 + kBigRows of BOTH the gate and
 // the up matrix (kBigRows / 16 tiles each) against the group's four 16-token tiles, so h is formed
-// in registers. Weight fragments are read from global memory straight in matrix-core order (one
-// fragment feeds four token tiles; an expert's other groups find it in the caches) through a ring
-// of two K chunks of registers; the group's x chunk is staged in LDS per 256-byte K chunk
-// (double-buffered) and each of its fragments feeds every weight tile of the wave.
+// in registers. Weight rows are read in whole 128-byte cache lines (8 rows x 128 bytes per load;
+// an expert's other groups find them in the caches) into a ring of two half chunks of registers
+// and staged per half chunk in the wave's own LDS area, from which each operand fragment feeds
+// four token tiles; the group's x chunk is staged in LDS per 256-byte K chunk (double-buffered)
+// and each of its fragments feeds every weight tile of the wave.
 constexpr int kBigWaves = 4;
 constexpr int kXcds = 8;      // accelerator complex dies of the chip, each with its own L2
 constexpr int kBigThreads = kBigWaves * kWave;
 constexpr int kBigRows = 32;  // intermediate rows per wave (two 16-row tiles of gate and of up)
+constexpr int kBigTile = kTile * 128;  // LDS of one staged 16-row x 128-byte weight tile
 
 template <int NT>
 __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_big_kernel(GateUpParams p) {
@@ -387,6 +389,8 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, q = lane >> 4;
+    const int drow = lane >> 3, dpiece = lane & 7;  // weight loader: 8 rows x 128 B per load
+    unsigned char *wst = smem + 2 * TG * kXRow + wave * kRT * kBigTile;  // the wave's weight tiles
     const int ngroups = p.num_groups[0];
     const int nunits = ngroups * p.S;
     const int nchunks = p.H / kCE;
@@ -414,12 +418,13 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
         const bool rows_ok = i0 < Ie;  // uniform over the wave (Ie is a multiple of 32)
         const elem_t *gu = reinterpret_cast<const elem_t *>(shared ? p.sgu : p.gate_up) +
                            (shared ? 0 : (size_t)e * 2 * Ie * p.H);
-        // tile t: gate rows (t < kRT/2) or up rows, i0 + 16 (t % (kRT/2)) + col; k-group q
+        // tile t: gate rows (t < kRT/2) or up rows i0 + 16 (t % (kRT/2)) .. + 16; the loader lane
+        // takes row drow (+ 8) and 16-byte piece dpiece of each 128-byte half chunk
         const elem_t *arow[kRT];
 #pragma unroll
         for (int t = 0; t < kRT; ++t) {
-            const int row = (t < kRT / 2 ? 0 : Ie) + i0 + kTile * (t % (kRT / 2)) + col;
-            arow[t] = gu + (size_t)(rows_ok ? row : 0) * p.H + q * Op::kPerLane;
+            const int row = (t < kRT / 2 ? 0 : Ie) + i0 + kTile * (t % (kRT / 2)) + drow;
+            arow[t] = gu + (size_t)(rows_ok ? row : 0) * p.H + dpiece * Op::kPerLane;
         }
         const elem_t *xsrc[kXPasses];
 #pragma unroll
@@ -442,13 +447,17 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
                     *reinterpret_cast<uint4 *>(xs + (buf * TG + xr0 + kXRowsPerPass * i) * kXRow +
                                                xp * 16) = xv[i];
         };
-        // weight ring: slot s holds step s of the current chunk and is refilled with step s of the
-        // next chunk as soon as its four token tiles have used it
-        uint4 ar[kSteps][kRT];
-        auto load_a = [&](int s2, int c) {
+        // weight ring: rA / rB hold the first / second 128-byte half of a chunk's rows for every
+        // tile (two loads of 8 rows x 128 contiguous bytes per tile: whole cache lines), refilled
+        // with the same half of the next chunk as soon as it is staged
+        uint4 rA[kRT][2], rB[kRT][2];
+        auto load_a = [&](uint4 (&r)[kRT][2], int hh, int c) {
             if (!rows_ok || c >= nchunks) return;  // uniform
 #pragma unroll
-            for (int t = 0; t < kRT; ++t) ar[s2][t] = load16(arow[t] + c * kCE + s2 * 4 * Op::kPerLane);
+            for (int t = 0; t < kRT; ++t)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    r[t][i] = load16(arow[t] + (size_t)(8 * i) * p.H + c * kCE + hh * (kCE / 2));
         };
         f32x4_t acc[kRT][NT];
 #pragma unroll
@@ -456,31 +465,52 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
             for (int i = 0; i < NT; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-        for (int s2 = 0; s2 < kSteps; ++s2) load_a(s2, 0);
+        load_a(rA, 0, 0);
+        load_a(rB, 1, 0);
         load_x(0);
         __syncthreads();  // the previous unit's readers of xs are done
         store_x(0);
-        for (int c = 0; c < nchunks; ++c) {
-            if (c + 1 < nchunks) load_x(c + 1);
-            __syncthreads();  // x chunk c is staged; chunk c - 1's readers are done
-            const unsigned char *xb = xs + (c & 1) * TG * kXRow;
+        // one half chunk (two k steps) of the wave's tiles: stage the 16 rows x 128 bytes of each
+        // tile in the wave's LDS area (row rr, piece pc at rr * 128 + ((pc ^ (rr & 7)) * 16)),
+        // refill the ring, then the two steps' operands in matrix-core order
+        auto half = [&](uint4 (&r)[kRT][2], int hh, int c, const unsigned char *xb) {
+            if (rows_ok) {
 #pragma unroll
-            for (int s2 = 0; s2 < kSteps; ++s2) {
+                for (int t = 0; t < kRT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int rr = 8 * i + drow;
+                        *reinterpret_cast<uint4 *>(wst + t * kBigTile + rr * 128 + ((dpiece ^ (rr & 7)) * 16)) = r[t][i];
+                    }
+            }
+            load_a(r, hh, c + 1);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int s2 = 2 * hh + s;  // step within the chunk
                 uint4 b[NT];
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt)
                     if (tt < nt_used)  // uniform
                         b[tt] = lds_read16(xb + (tt * kTile + col) * kXRow + (4 * s2 + q) * 16);
                 if (rows_ok) {
+                    uint4 a[kRT];
+#pragma unroll
+                    for (int t = 0; t < kRT; ++t)
+                        a[t] = lds_read16(wst + t * kBigTile + col * 128 + (((4 * s + q) ^ (col & 7)) * 16));
 #pragma unroll
                     for (int t = 0; t < kRT; ++t)
 #pragma unroll
                         for (int tt = 0; tt < NT; ++tt)
-                            if (tt < nt_used) Op::mma(acc[t][tt], ar[s2][t], b[tt]);
+                            if (tt < nt_used) Op::mma(acc[t][tt], a[t], b[tt]);
                 }
-                load_a(s2, c + 1);
             }
+        };
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) load_x(c + 1);
+            __syncthreads();  // x chunk c is staged; chunk c - 1's readers are done
+            const unsigned char *xb = xs + (c & 1) * TG * kXRow;
+            half(rA, 0, c, xb);
+            half(rB, 1, c, xb);
             if (c + 1 < nchunks) store_x((c + 1) & 1);
         }
         if (!rows_ok) continue;
@@ -521,7 +551,9 @@ int wide_rows_per_down_unit() { return kWWaves * kDownTiles * kTile; }
 int wide_rows_per_gateup_unit() { return kWWaves / 2 * kTile; }
 int wide_group_tokens() { return kWideNT * kTile; }
 int big_rows_per_gateup_unit() { return kBigWaves * kBigRows; }
-size_t gateup_big_lds() { return 2 * kWideNT * kTile * kXRow; }
+size_t gateup_big_lds() {
+    return 2 * kWideNT * kTile * kXRow + kBigWaves * (2 * kBigRows / kTile) * kBigTile;
+}
 
 hipError_t launch_gateup_big(const GateUpParams &p, int grid, hipStream_t s) {
     launch_k(gateup_big_kernel<kWideNT>, grid, kBigThreads, gateup_big_lds(), s, p);
@@ -530,6 +562,10 @@ hipError_t launch_gateup_big(const GateUpParams &p, int grid, hipStream_t s) {
 
 hipError_t prepare_wide_kernels() {
     hipError_t err;
+    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_big_kernel<kWideNT>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)gateup_big_lds())) != hipSuccess)
+        return err;
     const void *gk[] = {reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT, false>),
                         reinterpret_cast<const void *>(&gateup_wide_kernel<OpF32, kWideNT, false>),
                         reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT, true>)};
