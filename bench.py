@@ -111,7 +111,8 @@ def kernel_bytes(w, U, name):
     must read or write. Intermediates (h, partial sums, routing tables) are not counted."""
     esz, wsz, ssz = sizes(w)
     H, I, Is, T = w.hidden, w.inter, w.shared_inter, w.tokens
-    name = {"gateup_wide": "gateup", "gateup_big": "gateup", "down_wide": "down"}.get(name, name)
+    name = {"gateup_wide": "gateup", "gateup_big": "gateup", "down_wide": "down",
+            "down_big": "down"}.get(name, name)
     if name == "gateup":
         return 2 * wsz * H * Is + 2 * ssz * Is + U * (2 * wsz * H * I + 2 * ssz * I) + esz * T * H
     if name == "down":
@@ -271,7 +272,7 @@ def main():
         step_ms.append(ev[0].elapsed_time(ev[-1]))
     mean_U = float(np.mean([U[c] for c in used]))
     stage = {}
-    for name in ("gateup", "down", "gateup_wide", "gateup_big", "down_wide", "expert"):
+    for name in ("gateup", "down", "gateup_wide", "gateup_big", "down_wide", "down_big", "expert"):
         if name in per_kernel:
             us = float(np.mean(per_kernel[name])) * 1e3
             b = float(np.mean([kernel_bytes(w, U[c], name) for c in used]))

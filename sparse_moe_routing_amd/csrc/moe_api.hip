@@ -77,6 +77,7 @@ struct Plan {
     bool split = false;          // T <= 64: gateup + down kernels, 16-token groups
     bool wide = false;           // T > 64: gateup_wide + down_wide + combine, 64-token groups
     bool big = false;            // wide, bf16, T >= kBigMinTokens: gateup_big for gateup_wide
+    bool down_big = false;       // big and H a multiple of 512: down_big for down_wide
     int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;
     size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
@@ -173,6 +174,12 @@ Plan make_plan(const moe_ctx *c, int T) {
             const long b_cap = (long)c->num_cus * 8;
             p.gu_grid = (int)(b_units < b_cap ? b_units : b_cap);
             if (p.gu_grid >= 8) p.gu_grid -= p.gu_grid % 8;  // whole rounds over the 8 XCDs
+        }
+        p.down_big = p.big && H % big_rows_per_down_unit() == 0;
+        if (p.down_big) {
+            const long db_units = (long)p.max_groups * (H / big_rows_per_down_unit());
+            const long db_cap = (long)c->num_cus * 4;
+            p.down_grid = (int)(db_units < db_cap ? db_units : db_cap);
         }
     } else {
         const long d_units = (long)p.max_groups * (H / 64);
@@ -470,10 +477,14 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         dp.Imax = p.Imax;
         dp.dn_scale = c->w.down_scale;
         dp.sdn_scale = c->w.shared_down_scale;
-        if (p.wide) {
+        if (p.down_big) {
+            L.step("down_big", [&] { return launch_down_big(dp, p.down_grid, L.stream); });
+        } else if (p.wide) {
             L.step("down_wide", [&] {
                 return launch_down_wide(dp, expert_kdt(c), p.down_grid, L.stream);
             });
+        }
+        if (p.wide) {
             CombineParams cp{};
             cp.ypart = dp.ybuf;
             cp.w = nullptr;  // the slot outputs already carry their routing weight / gate

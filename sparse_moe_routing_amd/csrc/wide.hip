@@ -541,6 +541,150 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
 }
 
+// down_big_kernel (bf16, large T) - the down product of the 64-token groups with the layout of
+// gateup_big: unit = (expert group, kDBRows = 512 rows of y), so a group's h is staged 4 times
+// per token instead of 8; wave w owns rows w * 64 .. + 64 of the unit (four 16-row tiles) against
+// the group's four 16-token tiles. Weight rows are read in whole 128-byte lines (8 rows x 128 B
+// per load; an expert's other groups find them in the caches) into a ring of two half chunks of
+// registers and staged per half chunk in the wave's own LDS area; h (hi and lo planes) is staged
+// per 256-byte chunk as in down_wide_kernel. Per
+// output element the steps, planes and their order are those of down_wide_kernel (bitwise equal).
+constexpr int kDBWaves = 8;
+constexpr int kDBThreads = kDBWaves * kWave;
+constexpr int kDBTiles = 4;                              // 16-row tiles per wave
+constexpr int kDBRows = kDBWaves * kDBTiles * kTile;     // rows of y per unit (512)
+
+template <int NT>
+__global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_big_kernel(DownParams p) {
+    using Op = OpBF16;
+    using elem_t = uint16_t;
+    constexpr int TG = NT * kTile;
+    constexpr int kCE = kWPieces * Op::kPerLane;     // 128 elements per chunk
+    constexpr int kPlanes = 2;                       // h as hi + lo bf16
+    constexpr int kHPasses = TG * kWPieces / kDBThreads;
+    constexpr int kHRowsPerPass = kDBThreads / kWPieces;
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char *hs = smem;                        // [2][planes][TG][kXRow]
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 15, q = lane >> 4;
+    const int drow = lane >> 3, dpiece = lane & 7;   // weight loader: 8 rows x 128 B per load
+    unsigned char *wst = smem + 2 * kPlanes * TG * kXRow + wave * kDBTiles * kBigTile;
+    const int n_rc = p.H / kDBRows;
+    const int nunits = p.num_groups[0] * n_rc;
+    const elem_t *hg = reinterpret_cast<const elem_t *>(p.h);
+    const int hp = tid & 15, hr0 = tid >> 4;         // h loader: piece hp of rows hr0 + 32 i
+
+    for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
+        const int gi = u / n_rc, rc = u - (u / n_rc) * n_rc;
+        const int4 grp = p.groups[gi];
+        const int e = grp.x, start = grp.y, n = grp.z;
+        const bool shared = e == p.E;
+        const int Ie = shared ? p.Is : p.I;
+        const int nchunks = Ie / kCE;
+        const int nt_used = (n + kTile - 1) / kTile;
+        const elem_t *dn = reinterpret_cast<const elem_t *>(shared ? p.sdn : p.down) +
+                           (shared ? 0 : (size_t)e * p.H * Ie);
+        const int wrow = rc * kDBRows + wave * kDBTiles * kTile;  // the wave's first row
+        const elem_t *src = dn + (size_t)(wrow + drow) * Ie + dpiece * Op::kPerLane;
+        uint32_t hoff[kHPasses];  // element offsets of the h rows this thread stages
+#pragma unroll
+        for (int i = 0; i < kHPasses; ++i) {
+            const int r = hr0 + kHRowsPerPass * i;
+            const int rr = r < n ? r : 0;
+            const int slot = shared ? p.T * kTopK + start + rr : p.perm[start + rr];
+            hoff[i] = (uint32_t)slot * (uint32_t)p.Imax + hp * Op::kPerLane;
+        }
+        uint4 hv[kPlanes][kHPasses];
+        auto load_h = [&](int c) {
+#pragma unroll
+            for (int pl = 0; pl < kPlanes; ++pl)
+#pragma unroll
+                for (int i = 0; i < kHPasses; ++i) hv[pl][i] = load16(hg + pl * p.plane + hoff[i] + c * kCE);
+        };
+        auto store_h = [&](int buf) {
+#pragma unroll
+            for (int pl = 0; pl < kPlanes; ++pl)
+#pragma unroll
+                for (int i = 0; i < kHPasses; ++i)
+                    *reinterpret_cast<uint4 *>(hs + ((buf * kPlanes + pl) * TG + hr0 + kHRowsPerPass * i) *
+                                                        kXRow + hp * 16) = hv[pl][i];
+        };
+        // weight ring: rA / rB hold the first / second 128-byte half of a chunk's rows of every
+        // tile (two loads of 8 rows x 128 bytes per tile), refilled with the same half of the next
+        // chunk as soon as it is staged
+        uint4 rA[kDBTiles][2], rB[kDBTiles][2];
+        auto load_w = [&](uint4 (&r)[kDBTiles][2], int hh, int c) {
+            if (c >= nchunks) return;  // uniform
+#pragma unroll
+            for (int t = 0; t < kDBTiles; ++t)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    r[t][i] = load16(src + (size_t)(t * kTile + 8 * i) * Ie + c * kCE + hh * (kCE / 2));
+        };
+        f32x4_t acc[kDBTiles][NT];
+#pragma unroll
+        for (int t = 0; t < kDBTiles; ++t)
+#pragma unroll
+            for (int i = 0; i < NT; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        load_w(rA, 0, 0);
+        load_w(rB, 1, 0);
+        load_h(0);
+        __syncthreads();  // the previous unit's readers of hs are done
+        store_h(0);
+        auto half = [&](uint4 (&r)[kDBTiles][2], int hh, int c, const unsigned char *hb) {
+#pragma unroll
+            for (int t = 0; t < kDBTiles; ++t)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int rr = 8 * i + drow;
+                    *reinterpret_cast<uint4 *>(wst + t * kBigTile + rr * 128 + ((dpiece ^ (rr & 7)) * 16)) = r[t][i];
+                }
+            load_w(r, hh, c + 1);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int s2 = 2 * hh + s;  // step within the chunk
+                uint4 a[kDBTiles];
+#pragma unroll
+                for (int t = 0; t < kDBTiles; ++t)
+                    a[t] = lds_read16(wst + t * kBigTile + col * 128 + (((4 * s + q) ^ (col & 7)) * 16));
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    if (tt >= nt_used) continue;  // uniform
+#pragma unroll
+                    for (int pl = 0; pl < kPlanes; ++pl) {
+                        const uint4 b = lds_read16(hb + (pl * TG + tt * kTile + col) * kXRow + (4 * s2 + q) * 16);
+#pragma unroll
+                        for (int t = 0; t < kDBTiles; ++t) Op::mma(acc[t][tt], a[t], b);
+                    }
+                }
+            }
+        };
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) load_h(c + 1);
+            __syncthreads();  // h chunk c is staged; chunk c - 1's readers are done
+            const unsigned char *hb = hs + (c & 1) * kPlanes * TG * kXRow;
+            half(rA, 0, c, hb);
+            half(rB, 1, c, hb);
+            if (c + 1 < nchunks) store_h((c + 1) & 1);
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int cc = tt * kTile + col;
+            if (cc >= n) continue;
+            const int slot = shared ? p.T * kTopK + start + cc : p.perm[start + cc];
+            const float wt = shared ? p.g[start + cc] : p.w[slot];
+            // lane holds rows 4q + r of each of the wave's 16-row tiles for its token column
+#pragma unroll
+            for (int t = 0; t < kDBTiles; ++t)
+                *reinterpret_cast<float4 *>(p.ybuf + (size_t)slot * p.H + wrow + t * kTile + 4 * q) =
+                    make_float4(wt * acc[t][tt][0], wt * acc[t][tt][1], wt * acc[t][tt][2],
+                                wt * acc[t][tt][3]);
+        }
+    }
+}
+
 constexpr int kWideNT = 4;  // 64-token groups
 
 size_t gateup_wide_lds() { return 2 * kWideNT * kTile * kXRow + kWWaves * kWStage; }
@@ -560,8 +704,21 @@ hipError_t launch_gateup_big(const GateUpParams &p, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+size_t down_big_lds() { return 2 * 2 * kWideNT * kTile * kXRow + kDBWaves * kDBTiles * kBigTile; }
+int big_rows_per_down_unit() { return kDBRows; }
+
+hipError_t launch_down_big(const DownParams &p, int grid, hipStream_t s) {
+    if (p.NG != kWideNT * kTile || p.H % kDBRows) return hipErrorInvalidValue;  // a caller bug
+    launch_k(down_big_kernel<kWideNT>, grid, kDBThreads, down_big_lds(), s, p);
+    return hipGetLastError();
+}
+
 hipError_t prepare_wide_kernels() {
     hipError_t err;
+    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&down_big_kernel<kWideNT>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)down_big_lds())) != hipSuccess)
+        return err;
     if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_big_kernel<kWideNT>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)gateup_big_lds())) != hipSuccess)

@@ -500,7 +500,7 @@ def test_batch_invariance_bitwise():
     # T >= 3072: the register-blocked gate/up kernel, the same bits
     y4097 = m.forward(torch.cat([x] * 129)[:4097].contiguous())
     torch.cuda.synchronize()
-    assert m.plan(4097)[4] == "gateup_big"
+    assert m.plan(4097)[4:6] == ["gateup_big", "down_big"]
     assert torch.equal(y4097[:32], y32) and torch.equal(y4097[4064:4096], y32)
 
 
@@ -560,7 +560,7 @@ def test_call_errors_and_empty():
     assert m.plan(65) == m.plan(256) == ["router", "select_bucket"] + wide
     chained = ["router", "select_hist", "bucket_scan", "bucket_scatter"]
     assert m.plan(257) == m.plan(3071) == chained + wide
-    big = ["gateup_big", "down_wide", "combine"]  # bf16 from 3072 tokens
+    big = ["gateup_big", "down_big", "combine"]  # bf16 from 3072 tokens
     assert m.plan(3072) == m.plan(8192) == chained + big
     assert m.plan(200, routing_given=True) == ["select_bucket"] + wide
     assert m.plan(300, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
