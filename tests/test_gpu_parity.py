@@ -556,13 +556,14 @@ def test_call_errors_and_empty():
     tiny = get_layer("tiny_fp32_t4")[1]  # I = 32 is below the weight-row chunk of the split path
     assert tiny.plan(4) == ["route_fused", "expert", "combine"]
     wide = ["gateup_wide", "down_wide", "combine"]
+    wide_db = ["gateup_wide", "down_big", "combine"]  # bf16, T <= 256: 512-row down units
     # 64 < T <= 256: selection and bucketing in one launch; above, histogram / scan / scatter
-    assert m.plan(65) == m.plan(256) == ["router", "select_bucket"] + wide
+    assert m.plan(65) == m.plan(256) == ["router", "select_bucket"] + wide_db
     chained = ["router", "select_hist", "bucket_scan", "bucket_scatter"]
     assert m.plan(257) == m.plan(3071) == chained + wide
     big = ["gateup_big", "down_big", "combine"]  # bf16 from 3072 tokens
     assert m.plan(3072) == m.plan(8192) == chained + big
-    assert m.plan(200, routing_given=True) == ["select_bucket"] + wide
+    assert m.plan(200, routing_given=True) == ["select_bucket"] + wide_db
     assert m.plan(300, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
     assert tiny.plan(200) == ["router", "select_bucket", "expert", "combine"]
 
