@@ -62,7 +62,7 @@ constexpr int kHistChunk = 16;
 // 64 < T <= 256: selection and bucketing in one launch (select_bucket)
 constexpr int kSelBucketMaxTokens = 256;
 constexpr int kSplitMaxTokens = 64;   // 16-token groups up to here, 64-token groups above
-constexpr int kBigMinTokens = 3072;     // bf16 from here: gateup_big in place of gateup_wide
+constexpr int kBigMinTokens = 1536;     // bf16 from here: gateup_big in place of gateup_wide
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -77,7 +77,7 @@ struct Plan {
     bool split = false;          // T <= 64: gateup + down kernels, 16-token groups
     bool wide = false;           // T > 64: gateup_wide + down_wide + combine, 64-token groups
     bool big = false;            // wide, bf16, T >= kBigMinTokens: gateup_big for gateup_wide
-    bool down_big = false;       // wide, bf16, H a multiple of 512, T <= 256 or >= 3072
+    bool down_big = false;       // wide, bf16, H a multiple of 512, T <= 256 or big
     int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;
     size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
@@ -175,8 +175,9 @@ Plan make_plan(const moe_ctx *c, int T) {
             p.gu_grid = (int)(b_units < b_cap ? b_units : b_cap);
             if (p.gu_grid >= 8) p.gu_grid -= p.gu_grid % 8;  // whole rounds over the 8 XCDs
         }
-        // down_big from 3072 tokens and up to 256 (measured: skewed T = 192 51.1 against 53.8 us;
-        // T = 768 140.1 against 137.1 us for down_wide)
+        // down_big with gateup_big and up to 256 tokens (measured: skewed T = 192 51.1 against
+        // 53.8 us; T = 768 140.1 against 137.1 us for down_wide). The big pair from 1536 tokens:
+        // T = 2048 step 527 against 611 us, T = 1024 430 against 403 us.
         p.down_big = cfg.dtype == MOE_BF16 && H % big_rows_per_down_unit() == 0 &&
                      (T >= kBigMinTokens || T <= kSelBucketMaxTokens);
         if (p.down_big) {

@@ -497,7 +497,7 @@ def test_batch_invariance_bitwise():
     assert torch.equal(y32[7:8], y1)
     assert torch.equal(y200[:32], y32) and torch.equal(y200[192:200], y32[:8])
     assert torch.equal(y384[:32], y32) and torch.equal(y384[352:], y32)
-    # T >= 3072: the register-blocked gate/up kernel, the same bits
+    # T >= 1536: the large-T gate/up and down kernels, the same bits
     y4097 = m.forward(torch.cat([x] * 129)[:4097].contiguous())
     torch.cuda.synchronize()
     assert m.plan(4097)[4:6] == ["gateup_big", "down_big"]
@@ -560,9 +560,9 @@ def test_call_errors_and_empty():
     # 64 < T <= 256: selection and bucketing in one launch; above, histogram / scan / scatter
     assert m.plan(65) == m.plan(256) == ["router", "select_bucket"] + wide_db
     chained = ["router", "select_hist", "bucket_scan", "bucket_scatter"]
-    assert m.plan(257) == m.plan(3071) == chained + wide
-    big = ["gateup_big", "down_big", "combine"]  # bf16 from 3072 tokens
-    assert m.plan(3072) == m.plan(8192) == chained + big
+    assert m.plan(257) == m.plan(1535) == chained + wide
+    big = ["gateup_big", "down_big", "combine"]  # bf16 from 1536 tokens
+    assert m.plan(1536) == m.plan(8192) == chained + big
     assert m.plan(200, routing_given=True) == ["select_bucket"] + wide_db
     assert m.plan(300, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
     assert tiny.plan(200) == ["router", "select_bucket", "expert", "combine"]
@@ -596,7 +596,7 @@ def test_workspace_bytes_monotone():
     across the decode, 64-token-group and large-T plans."""
     for name in ("decode_b1_t4", "decode_b1_t4_fp8", "tiny_fp32_t4"):
         m = get_layer(name)[1]
-        sizes = [m.lib.moe_workspace_bytes(m.ctx, T) for T in list(range(1, 300)) + [3071, 3072, 8192]]
+        sizes = [m.lib.moe_workspace_bytes(m.ctx, T) for T in list(range(1, 300)) + [1535, 1536, 3071, 3072, 8192]]
         assert all(b > 0 for b in sizes)
         assert all(a <= b for a, b in zip(sizes, sizes[1:])), name
 
