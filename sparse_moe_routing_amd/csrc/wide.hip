@@ -471,8 +471,9 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
         __syncthreads();  // the previous unit's readers of xs are done
         store_x(0);
         // one half chunk (two k steps) of the wave's tiles: stage the 16 rows x 128 bytes of each
-        // tile in the wave's LDS area (row rr, piece pc at rr * 128 + ((pc ^ (rr & 7)) * 16)),
-        // refill the ring, then the two steps' operands in matrix-core order
+        // tile in the wave's LDS area (row rr, piece pc at rr * 128 + ((pc ^ (rr >> 1)) & 7) * 16:
+        // the 16 rows of an operand read fall on 16 distinct 16-byte bank groups), refill the ring,
+        // then the two steps' operands in matrix-core order
         auto half = [&](uint4 (&r)[kRT][2], int hh, int c, const unsigned char *xb) {
             if (rows_ok) {
 #pragma unroll
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         const int rr = 8 * i + drow;
-                        *reinterpret_cast<uint4 *>(wst + t * kBigTile + rr * 128 + ((dpiece ^ (rr & 7)) * 16)) = r[t][i];
+                        *reinterpret_cast<uint4 *>(wst + t * kBigTile + rr * 128 + ((dpiece ^ ((rr >> 1) & 7)) * 16)) = r[t][i];
                     }
             }
             load_a(r, hh, c + 1);
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
                     uint4 a[kRT];
 #pragma unroll
                     for (int t = 0; t < kRT; ++t)
-                        a[t] = lds_read16(wst + t * kBigTile + col * 128 + (((4 * s + q) ^ (col & 7)) * 16));
+                        a[t] = lds_read16(wst + t * kBigTile + col * 128 + (((4 * s + q) ^ ((col >> 1) & 7)) * 16));
 #pragma unroll
                     for (int t = 0; t < kRT; ++t)
 #pragma unroll
@@ -639,7 +640,7 @@ __global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int rr = 8 * i + drow;
-                    *reinterpret_cast<uint4 *>(wst + t * kBigTile + rr * 128 + ((dpiece ^ (rr & 7)) * 16)) = r[t][i];
+                    *reinterpret_cast<uint4 *>(wst + t * kBigTile + rr * 128 + ((dpiece ^ ((rr >> 1) & 7)) * 16)) = r[t][i];
                 }
             load_w(r, hh, c + 1);
 #pragma unroll
@@ -648,7 +649,7 @@ __global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 uint4 a[kDBTiles];
 #pragma unroll
                 for (int t = 0; t < kDBTiles; ++t)
-                    a[t] = lds_read16(wst + t * kBigTile + col * 128 + (((4 * s + q) ^ (col & 7)) * 16));
+                    a[t] = lds_read16(wst + t * kBigTile + col * 128 + (((4 * s + q) ^ ((col >> 1) & 7)) * 16));
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
                     if (tt >= nt_used) continue;  // uniform
