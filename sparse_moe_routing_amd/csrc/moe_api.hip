@@ -184,6 +184,7 @@ Plan make_plan(const moe_ctx *c, int T) {
             const long db_units = (long)p.max_groups * (H / big_rows_per_down_unit());
             const long db_cap = (long)c->num_cus * 4;
             p.down_grid = (int)(db_units < db_cap ? db_units : db_cap);
+            if (p.down_grid >= 8) p.down_grid -= p.down_grid % 8;  // whole rounds over the 8 XCDs
         }
     } else {
         const long d_units = (long)p.max_groups * (H / 64);

@@ -235,6 +235,124 @@ __device__ __forceinline__ void router_unit_tt(const RouterParams &p, int u, int
     }
 }
 
+// Prefill form with whole cache lines: as router_unit_tt, but every 16-row weight tile and
+// 16-token x tile is read 128 contiguous bytes per row (8 rows x 128 B per load) for two k steps
+// at a time and staged in the wave's own LDS area `wst` ((MAXRT + MAXTT) x 2 KiB; row rr, piece
+// pc at rr * 128 + ((pc ^ (rr >> 1)) & 7) * 16), from which the operand fragments are read in
+// matrix-core order. Per output element the steps, runs and their order are those of router_unit
+// (the result is bitwise the same). Needs an even number of steps per quarter.
+template <class Op, int MAXRT, int MAXTT>
+__device__ __forceinline__ void router_unit_tt_lds(const RouterParams &p, int u, int lane,
+                                                   unsigned char *wst) {
+    using elem_t = typename Op::elem_t;
+    constexpr int NTL = MAXRT + MAXTT;    // staged tiles: weights first, then x
+    constexpr int kTileBytes = kTile * 128;
+    constexpr int kHalf = 2 * Op::kStep;  // elements of a half chunk (128 bytes)
+    const int n_tg = (p.n_tt + MAXTT - 1) / MAXTT;
+    const int total = n_tg * p.KS * p.n_rg;
+    if (u >= total) return;
+    const int rg = u % p.n_rg;
+    const int kq = (u / p.n_rg) % p.KS;
+    const int tg = u / (p.n_rg * p.KS);
+    const int n_rt = (p.R + kTile - 1) / kTile;
+    const int rt0 = rg * MAXRT, tt0 = tg * MAXTT;
+    const int nrt_here = min(MAXRT, n_rt - rt0);
+    const int ntt_here = min(MAXTT, p.n_tt - tt0);
+    const int col = lane & 15, q = lane >> 4;
+    const int drow = lane >> 3, dpiece = lane & 7;
+    const RouterGeom g(p.H, Op::kStep);
+    const int nhalf = g.Sq / 2;
+    const elem_t *x = reinterpret_cast<const elem_t *>(p.x);
+    const elem_t *w = reinterpret_cast<const elem_t *>(p.w);
+    // loader: element offsets (quarter start and piece included) of rows drow and drow + 8 of
+    // every tile, clamped to a valid row (an out-of-range row is zeroed at its use)
+    uint32_t off[NTL][2];
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = (t < MAXRT ? (rt0 + t) : (tt0 + t - MAXRT)) * kTile + 8 * i + drow;
+            const int lim = t < MAXRT ? p.R : p.T;
+            off[t][i] = (uint32_t)(r < lim ? r : lim - 1) * (uint32_t)p.H + kq * g.Sq * Op::kStep +
+                        dpiece * Op::kPerLane;
+        }
+    bool wok[MAXRT], tok_ok[MAXTT];
+#pragma unroll
+    for (int j = 0; j < MAXRT; ++j) wok[j] = j < nrt_here && (rt0 + j) * kTile + col < p.R;
+#pragma unroll
+    for (int i = 0; i < MAXTT; ++i) tok_ok[i] = i < ntt_here && (tt0 + i) * kTile + col < p.T;
+    uint4 rA[NTL][2], rB[NTL][2];
+    auto load = [&](uint4 (&r)[NTL][2], int hc) {
+        if (hc >= nhalf) return;  // uniform
+#pragma unroll
+        for (int t = 0; t < NTL; ++t)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) r[t][i] = load16((t < MAXRT ? w : x) + off[t][i] + hc * kHalf);
+    };
+    const uint4 zero = {0u, 0u, 0u, 0u};
+    f32x4_t s[MAXRT][MAXTT], ch[MAXRT][MAXTT];
+#pragma unroll
+    for (int j = 0; j < MAXRT; ++j)
+#pragma unroll
+        for (int i = 0; i < MAXTT; ++i) ch[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto half = [&](uint4 (&r)[NTL][2], int hc) {
+#pragma unroll
+        for (int t = 0; t < NTL; ++t)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int rr = 8 * i + drow;
+                *reinterpret_cast<uint4 *>(wst + t * kTileBytes + rr * 128 + ((dpiece ^ ((rr >> 1) & 7)) * 16)) = r[t][i];
+            }
+        load(r, hc + 2);
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+            const int st = 2 * hc + sh;
+            const int po = col * 128 + (((4 * sh + q) ^ ((col >> 1) & 7)) * 16);
+            uint4 a[MAXRT], b[MAXTT];
+#pragma unroll
+            for (int j = 0; j < MAXRT; ++j) a[j] = *reinterpret_cast<const uint4 *>(wst + j * kTileBytes + po);
+#pragma unroll
+            for (int i = 0; i < MAXTT; ++i) b[i] = *reinterpret_cast<const uint4 *>(wst + (MAXRT + i) * kTileBytes + po);
+#pragma unroll
+            for (int j = 0; j < MAXRT; ++j)
+#pragma unroll
+                for (int i = 0; i < MAXTT; ++i)
+                    if (j < nrt_here && i < ntt_here)  // uniform
+                        Op::mma(ch[j][i], wok[j] ? a[j] : zero, tok_ok[i] ? b[i] : zero);
+            if ((st + 1) % g.Sw == 0 || st + 1 == g.Sq) {  // run st / Sw ends here (uniform)
+                const bool first = st < g.Sw;
+#pragma unroll
+                for (int j = 0; j < MAXRT; ++j)
+#pragma unroll
+                    for (int i = 0; i < MAXTT; ++i) {
+                        s[j][i] = first ? ch[j][i] : s[j][i] + ch[j][i];
+                        ch[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    }
+            }
+        }
+    };
+    load(rA, 0);
+    load(rB, 1);
+    for (int hc = 0; hc < nhalf; hc += 2) {
+        half(rA, hc);
+        if (hc + 1 < nhalf) half(rB, hc + 1);
+    }
+#pragma unroll
+    for (int i = 0; i < MAXTT; ++i) {
+        const int tok = (tt0 + i) * kTile + col;
+        if (!(i < ntt_here && tok < p.T)) continue;
+        float *out = p.zpart + ((size_t)kq * p.T + tok) * p.R;
+#pragma unroll
+        for (int j = 0; j < MAXRT; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = (rt0 + j) * kTile + 4 * q + r;
+                if (j < nrt_here && row < p.R) out[row] = s[j][i][r];
+            }
+        }
+    }
+}
+
 // Decode form: block b = (token tile, row tile, quarter) of 16 waves; wave w computes run w and
 // the runs are added in order through LDS (red: 16 tiles of 256 floats). Every thread of the
 // block calls it; it ends with the partial logits stored (no trailing barrier). kDev: stored

@@ -572,12 +572,21 @@ __global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int drow = lane >> 3, dpiece = lane & 7;   // weight loader: 8 rows x 128 B per load
     unsigned char *wst = smem + 2 * kPlanes * TG * kXRow + wave * kDBTiles * kBigTile;
     const int n_rc = p.H / kDBRows;
-    const int nunits = p.num_groups[0] * n_rc;
+    const int ngroups = p.num_groups[0];
+    const int nunits = ngroups * n_rc;
     const elem_t *hg = reinterpret_cast<const elem_t *>(p.h);
     const int hp = tid & 15, hr0 = tid >> 4;         // h loader: piece hp of rows hr0 + 32 i
+    // XCD-aware schedule (as in gateup_big_kernel): units numbered row-block-major
+    // (u = rc * groups + g), so an expert's groups, which read the same down rows, are neighbours;
+    // blocks b, b + 8, ... share an XCD and take one contiguous eighth of the units
+    const bool xmap = gridDim.x % kXcds == 0;
+    const int xcd = blockIdx.x % kXcds;
+    const int per = xmap ? (nunits + kXcds - 1) / kXcds : nunits;
+    const int u_end = xmap ? min(nunits, (xcd + 1) * per) : nunits;
+    const int u_step = xmap ? gridDim.x / kXcds : gridDim.x;
 
-    for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
-        const int gi = u / n_rc, rc = u - (u / n_rc) * n_rc;
+    for (int u = xmap ? xcd * per + blockIdx.x / kXcds : blockIdx.x; u < u_end; u += u_step) {
+        const int rc = u / ngroups, gi = u - rc * ngroups;
         const int4 grp = p.groups[gi];
         const int e = grp.x, start = grp.y, n = grp.z;
         const bool shared = e == p.E;
