@@ -145,9 +145,9 @@ hipError_t launch_gateup_wide(const GateUpParams &p, int dtype, int grid, hipStr
 hipError_t launch_down_wide(const DownParams &p, int dtype, int grid, hipStream_t s);
 int wide_group_tokens();          // tokens per expert group of the wide kernels
 int big_rows_per_gateup_unit();   // intermediate rows per gateup_big unit
-hipError_t launch_gateup_big(const GateUpParams &p, int grid, hipStream_t s);  // bf16 only
+hipError_t launch_gateup_big(const GateUpParams &p, int dtype, int grid, hipStream_t s);  // bf16 / FP8
 int big_rows_per_down_unit();     // rows of y per down_big unit
-hipError_t launch_down_big(const DownParams &p, int grid, hipStream_t s);      // bf16 only
+hipError_t launch_down_big(const DownParams &p, int dtype, int grid, hipStream_t s);  // bf16 / FP8
 int wide_rows_per_down_unit();    // rows of y per down_wide unit
 int wide_rows_per_gateup_unit();  // intermediate rows per gateup_wide unit
 

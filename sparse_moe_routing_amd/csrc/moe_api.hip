@@ -76,8 +76,8 @@ struct Plan {
     size_t lds = 0;
     bool split = false;          // T <= 64: gateup + down kernels, 16-token groups
     bool wide = false;           // T > 64: gateup_wide + down_wide + combine, 64-token groups
-    bool big = false;            // wide, bf16, T >= kBigMinTokens: gateup_big for gateup_wide
-    bool down_big = false;       // wide, bf16, H a multiple of 512, T <= 256 or big
+    bool big = false;            // wide, bf16 or FP8, T >= kBigMinTokens: gateup_big for gateup_wide
+    bool down_big = false;       // wide, bf16 or FP8, H a multiple of 512, T <= 256 or big
     int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;
     size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
@@ -167,7 +167,8 @@ Plan make_plan(const moe_ctx *c, int T) {
         p.down_grid = (int)(d_units < cap ? d_units : cap);
         p.gu_grid = (int)(g_units < cap ? g_units : cap);
         p.gu_S = Imax / gr;
-        p.big = cfg.dtype == MOE_BF16 && T >= kBigMinTokens && Imax % big_rows_per_gateup_unit() == 0;
+        const bool big_dtype = cfg.dtype == MOE_BF16 || cfg.dtype == MOE_FP8_E4M3;
+        p.big = big_dtype && T >= kBigMinTokens && Imax % big_rows_per_gateup_unit() == 0;
         if (p.big) {
             p.gu_S = Imax / big_rows_per_gateup_unit();
             const long b_units = (long)p.max_groups * p.gu_S;
@@ -178,7 +179,7 @@ Plan make_plan(const moe_ctx *c, int T) {
         // down_big with gateup_big and up to 256 tokens (measured: skewed T = 192 51.1 against
         // 53.8 us; T = 768 140.1 against 137.1 us for down_wide). The big pair from 1536 tokens:
         // T = 2048 step 527 against 611 us, T = 1024 430 against 403 us.
-        p.down_big = cfg.dtype == MOE_BF16 && H % big_rows_per_down_unit() == 0 &&
+        p.down_big = big_dtype && H % big_rows_per_down_unit() == 0 &&
                      (T >= kBigMinTokens || T <= kSelBucketMaxTokens);
         if (p.down_big) {
             const long db_units = (long)p.max_groups * (H / big_rows_per_down_unit());
@@ -451,7 +452,7 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         gp.gu_scale = c->w.gate_up_scale;
         gp.sgu_scale = c->w.shared_gate_up_scale;
         if (p.big)
-            L.step("gateup_big", [&] { return launch_gateup_big(gp, p.gu_grid, L.stream); });
+            L.step("gateup_big", [&] { return launch_gateup_big(gp, expert_kdt(c), p.gu_grid, L.stream); });
         else if (p.wide)
             L.step("gateup_wide", [&] {
                 return launch_gateup_wide(gp, expert_kdt(c), p.gu_grid, L.stream);
@@ -483,7 +484,7 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         dp.dn_scale = c->w.down_scale;
         dp.sdn_scale = c->w.shared_down_scale;
         if (p.down_big) {
-            L.step("down_big", [&] { return launch_down_big(dp, p.down_grid, L.stream); });
+            L.step("down_big", [&] { return launch_down_big(dp, expert_kdt(c), p.down_grid, L.stream); });
         } else if (p.wide) {
             L.step("down_wide", [&] {
                 return launch_down_wide(dp, expert_kdt(c), p.down_grid, L.stream);

@@ -372,10 +372,11 @@ constexpr int kBigThreads = kBigWaves * kWave;
 constexpr int kBigRows = 32;  // intermediate rows per wave (two 16-row tiles of gate and of up)
 constexpr int kBigTile = kTile * 128;  // LDS of one staged 16-row x 128-byte weight tile
 
-template <int NT>
+template <int NT, bool kFp8>
 __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_big_kernel(GateUpParams p) {
     using Op = OpBF16;
     using elem_t = uint16_t;
+    using wt_t = typename WeightFmt<Op, kFp8>::wt_t;  // bf16, or one-byte E4M3 codes
     constexpr int TG = NT * kTile;
     constexpr int kCE = kWPieces * Op::kPerLane;          // elements per chunk (128)
     constexpr int kSteps = kWPieces / 4;                  // matrix-core steps per chunk
@@ -416,15 +417,17 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
         const int nt_used = (n + kTile - 1) / kTile;
         const int i0 = j * kSW + wave * kBigRows;
         const bool rows_ok = i0 < Ie;  // uniform over the wave (Ie is a multiple of 32)
-        const elem_t *gu = reinterpret_cast<const elem_t *>(shared ? p.sgu : p.gate_up) +
-                           (shared ? 0 : (size_t)e * 2 * Ie * p.H);
+        const wt_t *gu = reinterpret_cast<const wt_t *>(shared ? p.sgu : p.gate_up) +
+                         (shared ? 0 : (size_t)e * 2 * Ie * p.H);
         // tile t: gate rows (t < kRT/2) or up rows i0 + 16 (t % (kRT/2)) .. + 16; the loader lane
-        // takes row drow (+ 8) and 16-byte piece dpiece of each 128-byte half chunk
-        const elem_t *arow[kRT];
+        // takes row drow (+ 8) and 16-byte piece dpiece of each 128-byte line: of a half chunk
+        // (bf16), of a whole chunk (FP8 codes, 16 per lane)
+        constexpr int kLaneElems = kFp8 ? 16 : Op::kPerLane;
+        const wt_t *arow[kRT];
 #pragma unroll
         for (int t = 0; t < kRT; ++t) {
             const int row = (t < kRT / 2 ? 0 : Ie) + i0 + kTile * (t % (kRT / 2)) + drow;
-            arow[t] = gu + (size_t)(rows_ok ? row : 0) * p.H + dpiece * Op::kPerLane;
+            arow[t] = gu + (size_t)(rows_ok ? row : 0) * p.H + dpiece * kLaneElems;
         }
         const elem_t *xsrc[kXPasses];
 #pragma unroll
@@ -447,9 +450,10 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
                     *reinterpret_cast<uint4 *>(xs + (buf * TG + xr0 + kXRowsPerPass * i) * kXRow +
                                                xp * 16) = xv[i];
         };
-        // weight ring: rA / rB hold the first / second 128-byte half of a chunk's rows for every
-        // tile (two loads of 8 rows x 128 contiguous bytes per tile: whole cache lines), refilled
-        // with the same half of the next chunk as soon as it is staged
+        // weight ring (two loads of 8 rows x 128 contiguous bytes per tile: whole cache lines).
+        // bf16: rA / rB hold the first / second half of a chunk's rows, refilled with the same
+        // half of the next chunk as soon as it is staged. FP8: rA / rB hold whole chunks (even /
+        // odd), refilled two chunks later once both halves are staged.
         uint4 rA[kRT][2], rB[kRT][2];
         auto load_a = [&](uint4 (&r)[kRT][2], int hh, int c) {
             if (!rows_ok || c >= nchunks) return;  // uniform
@@ -457,7 +461,7 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
             for (int t = 0; t < kRT; ++t)
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    r[t][i] = load16(arow[t] + (size_t)(8 * i) * p.H + c * kCE + hh * (kCE / 2));
+                    r[t][i] = load16(arow[t] + (size_t)(8 * i) * p.H + c * kCE + (kFp8 ? 0 : hh * (kCE / 2)));
         };
         f32x4_t acc[kRT][NT];
 #pragma unroll
@@ -466,7 +470,7 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
             for (int i = 0; i < NT; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         load_a(rA, 0, 0);
-        load_a(rB, 1, 0);
+        load_a(rB, 1, kFp8 ? 1 : 0);
         load_x(0);
         __syncthreads();  // the previous unit's readers of xs are done
         store_x(0);
@@ -481,10 +485,27 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         const int rr = 8 * i + drow;
-                        *reinterpret_cast<uint4 *>(wst + t * kBigTile + rr * 128 + ((dpiece ^ ((rr >> 1) & 7)) * 16)) = r[t][i];
+                        unsigned char *row = wst + t * kBigTile + rr * 128;
+                        if constexpr (kFp8) {
+                            // lanes holding codes of this half widen their 16 codes to two
+                            // 16-byte bf16 pieces (exact)
+                            if ((dpiece >> 2) == hh) {
+                                const int pc = 2 * (dpiece & 3);
+                                *reinterpret_cast<uint4 *>(row + ((pc ^ ((rr >> 1) & 7)) * 16)) =
+                                    e4m3x8_to_bf16x8(r[t][i].x, r[t][i].y);
+                                *reinterpret_cast<uint4 *>(row + (((pc + 1) ^ ((rr >> 1) & 7)) * 16)) =
+                                    e4m3x8_to_bf16x8(r[t][i].z, r[t][i].w);
+                            }
+                        } else {
+                            *reinterpret_cast<uint4 *>(row + ((dpiece ^ ((rr >> 1) & 7)) * 16)) = r[t][i];
+                        }
                     }
             }
-            load_a(r, hh, c + 1);
+            if constexpr (kFp8) {
+                if (hh == 1) load_a(r, 0, c + 2);
+            } else {
+                load_a(r, hh, c + 1);
+            }
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int s2 = 2 * hh + s;  // step within the chunk
@@ -506,15 +527,31 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
                 }
             }
         };
-        for (int c = 0; c < nchunks; ++c) {
+        auto chunk = [&](uint4 (&r0)[kRT][2], uint4 (&r1)[kRT][2], int c) {
             if (c + 1 < nchunks) load_x(c + 1);
             __syncthreads();  // x chunk c is staged; chunk c - 1's readers are done
             const unsigned char *xb = xs + (c & 1) * TG * kXRow;
-            half(rA, 0, c, xb);
-            half(rB, 1, c, xb);
+            half(r0, 0, c, xb);
+            half(r1, 1, c, xb);
             if (c + 1 < nchunks) store_x((c + 1) & 1);
+        };
+        if constexpr (kFp8) {
+            for (int c = 0; c < nchunks; c += 2) {
+                chunk(rA, rA, c);
+                if (c + 1 < nchunks) chunk(rB, rB, c + 1);
+            }
+        } else {
+            for (int c = 0; c < nchunks; ++c) chunk(rA, rB, c);
         }
         if (!rows_ok) continue;
+        if constexpr (kFp8) {  // the rows' dequantization scales (gate rows, then up rows)
+            const float *sc = shared ? p.sgu_scale : p.gu_scale + (size_t)e * 2 * Ie;
+#pragma unroll
+            for (int t = 0; t < kRT; ++t)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+                    scale_rows(acc[t][tt], sc + (t < kRT / 2 ? 0 : Ie) + i0 + kTile * (t % (kRT / 2)) + 4 * q);
+        }
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             const int cc = tt * kTile + col;  // group row of this lane's token column
@@ -555,10 +592,11 @@ constexpr int kDBThreads = kDBWaves * kWave;
 constexpr int kDBTiles = 4;                              // 16-row tiles per wave
 constexpr int kDBRows = kDBWaves * kDBTiles * kTile;     // rows of y per unit (512)
 
-template <int NT>
+template <int NT, bool kFp8>
 __global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_big_kernel(DownParams p) {
     using Op = OpBF16;
     using elem_t = uint16_t;
+    using wt_t = typename WeightFmt<Op, kFp8>::wt_t;  // bf16, or one-byte E4M3 codes
     constexpr int TG = NT * kTile;
     constexpr int kCE = kWPieces * Op::kPerLane;     // 128 elements per chunk
     constexpr int kPlanes = 2;                       // h as hi + lo bf16
@@ -593,10 +631,10 @@ __global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const int Ie = shared ? p.Is : p.I;
         const int nchunks = Ie / kCE;
         const int nt_used = (n + kTile - 1) / kTile;
-        const elem_t *dn = reinterpret_cast<const elem_t *>(shared ? p.sdn : p.down) +
-                           (shared ? 0 : (size_t)e * p.H * Ie);
+        const wt_t *dn = reinterpret_cast<const wt_t *>(shared ? p.sdn : p.down) +
+                         (shared ? 0 : (size_t)e * p.H * Ie);
         const int wrow = rc * kDBRows + wave * kDBTiles * kTile;  // the wave's first row
-        const elem_t *src = dn + (size_t)(wrow + drow) * Ie + dpiece * Op::kPerLane;
+        const wt_t *src = dn + (size_t)(wrow + drow) * Ie + dpiece * (kFp8 ? 16 : Op::kPerLane);
         uint32_t hoff[kHPasses];  // element offsets of the h rows this thread stages
 #pragma unroll
         for (int i = 0; i < kHPasses; ++i) {
@@ -620,9 +658,9 @@ __global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                     *reinterpret_cast<uint4 *>(hs + ((buf * kPlanes + pl) * TG + hr0 + kHRowsPerPass * i) *
                                                         kXRow + hp * 16) = hv[pl][i];
         };
-        // weight ring: rA / rB hold the first / second 128-byte half of a chunk's rows of every
-        // tile (two loads of 8 rows x 128 bytes per tile), refilled with the same half of the next
-        // chunk as soon as it is staged
+        // weight ring (two loads of 8 rows x 128 bytes per tile): bf16 - rA / rB hold the first /
+        // second half of a chunk's rows, refilled with the same half of the next chunk as soon as
+        // it is staged; FP8 - whole chunks (even / odd), refilled two chunks later
         uint4 rA[kDBTiles][2], rB[kDBTiles][2];
         auto load_w = [&](uint4 (&r)[kDBTiles][2], int hh, int c) {
             if (c >= nchunks) return;  // uniform
@@ -630,7 +668,7 @@ __global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             for (int t = 0; t < kDBTiles; ++t)
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    r[t][i] = load16(src + (size_t)(t * kTile + 8 * i) * Ie + c * kCE + hh * (kCE / 2));
+                    r[t][i] = load16(src + (size_t)(t * kTile + 8 * i) * Ie + c * kCE + (kFp8 ? 0 : hh * (kCE / 2)));
         };
         f32x4_t acc[kDBTiles][NT];
 #pragma unroll
@@ -639,7 +677,7 @@ __global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             for (int i = 0; i < NT; ++i) acc[t][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         load_w(rA, 0, 0);
-        load_w(rB, 1, 0);
+        load_w(rB, 1, kFp8 ? 1 : 0);
         load_h(0);
         __syncthreads();  // the previous unit's readers of hs are done
         store_h(0);
@@ -671,13 +709,64 @@ __global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 }
             }
         };
-        for (int c = 0; c < nchunks; ++c) {
+        // FP8: a whole chunk of raw codes (16 rows x 128 bytes per tile) is staged at once, same
+        // swizzle, and each operand fragment (8 codes) is widened to bf16 right before its use:
+        // step s2, k-group q takes bytes 32 s2 + 8 q .. + 8 of the row
+        auto chunk8 = [&](uint4 (&r)[kDBTiles][2], int c) {
             if (c + 1 < nchunks) load_h(c + 1);
             __syncthreads();  // h chunk c is staged; chunk c - 1's readers are done
             const unsigned char *hb = hs + (c & 1) * kPlanes * TG * kXRow;
-            half(rA, 0, c, hb);
-            half(rB, 1, c, hb);
+#pragma unroll
+            for (int t = 0; t < kDBTiles; ++t)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int rr = 8 * i + drow;
+                    *reinterpret_cast<uint4 *>(wst + t * kBigTile + rr * 128 + ((dpiece ^ ((rr >> 1) & 7)) * 16)) = r[t][i];
+                }
+            load_w(r, 0, c + 2);
+#pragma unroll
+            for (int s2 = 0; s2 < kWPieces / 4; ++s2) {
+                const int po = col * 128 + (((2 * s2 + (q >> 1)) ^ ((col >> 1) & 7)) * 16) + (q & 1) * 8;
+                uint4 a[kDBTiles];
+#pragma unroll
+                for (int t = 0; t < kDBTiles; ++t) {
+                    const uint2 cd = *reinterpret_cast<const uint2 *>(wst + t * kBigTile + po);
+                    a[t] = e4m3x8_to_bf16x8(cd.x, cd.y);
+                }
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    if (tt >= nt_used) continue;  // uniform
+#pragma unroll
+                    for (int pl = 0; pl < kPlanes; ++pl) {
+                        const uint4 b = lds_read16(hb + (pl * TG + tt * kTile + col) * kXRow + (4 * s2 + q) * 16);
+#pragma unroll
+                        for (int t = 0; t < kDBTiles; ++t) Op::mma(acc[t][tt], a[t], b);
+                    }
+                }
+            }
             if (c + 1 < nchunks) store_h((c + 1) & 1);
+        };
+        if constexpr (kFp8) {
+            for (int c = 0; c < nchunks; c += 2) {
+                chunk8(rA, c);
+                if (c + 1 < nchunks) chunk8(rB, c + 1);
+            }
+        } else {
+            for (int c = 0; c < nchunks; ++c) {
+                if (c + 1 < nchunks) load_h(c + 1);
+                __syncthreads();  // h chunk c is staged; chunk c - 1's readers are done
+                const unsigned char *hb = hs + (c & 1) * kPlanes * TG * kXRow;
+                half(rA, 0, c, hb);
+                half(rB, 1, c, hb);
+                if (c + 1 < nchunks) store_h((c + 1) & 1);
+            }
+        }
+        if constexpr (kFp8) {  // the output rows' dequantization scales
+            const float *sc = (shared ? p.sdn_scale : p.dn_scale + (size_t)e * p.H) + wrow + 4 * q;
+#pragma unroll
+            for (int t = 0; t < kDBTiles; ++t)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) scale_rows(acc[t][tt], sc + t * kTile);
         }
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -709,30 +798,35 @@ size_t gateup_big_lds() {
     return 2 * kWideNT * kTile * kXRow + kBigWaves * (2 * kBigRows / kTile) * kBigTile;
 }
 
-hipError_t launch_gateup_big(const GateUpParams &p, int grid, hipStream_t s) {
-    launch_k(gateup_big_kernel<kWideNT>, grid, kBigThreads, gateup_big_lds(), s, p);
+// dtype: 1 bf16, 2 bf16 activations with FP8 E4M3 weights
+hipError_t launch_gateup_big(const GateUpParams &p, int dtype, int grid, hipStream_t s) {
+    if (dtype == 2) launch_k(gateup_big_kernel<kWideNT, true>, grid, kBigThreads, gateup_big_lds(), s, p);
+    else launch_k(gateup_big_kernel<kWideNT, false>, grid, kBigThreads, gateup_big_lds(), s, p);
     return hipGetLastError();
 }
 
 size_t down_big_lds() { return 2 * 2 * kWideNT * kTile * kXRow + kDBWaves * kDBTiles * kBigTile; }
 int big_rows_per_down_unit() { return kDBRows; }
 
-hipError_t launch_down_big(const DownParams &p, int grid, hipStream_t s) {
+// dtype: 1 bf16, 2 bf16 activations with FP8 E4M3 weights
+hipError_t launch_down_big(const DownParams &p, int dtype, int grid, hipStream_t s) {
     if (p.NG != kWideNT * kTile || p.H % kDBRows) return hipErrorInvalidValue;  // a caller bug
-    launch_k(down_big_kernel<kWideNT>, grid, kDBThreads, down_big_lds(), s, p);
+    if (dtype == 2) launch_k(down_big_kernel<kWideNT, true>, grid, kDBThreads, down_big_lds(), s, p);
+    else launch_k(down_big_kernel<kWideNT, false>, grid, kDBThreads, down_big_lds(), s, p);
     return hipGetLastError();
 }
 
 hipError_t prepare_wide_kernels() {
     hipError_t err;
-    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&down_big_kernel<kWideNT>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)down_big_lds())) != hipSuccess)
-        return err;
-    if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_big_kernel<kWideNT>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)gateup_big_lds())) != hipSuccess)
-        return err;
+    const void *big[] = {reinterpret_cast<const void *>(&down_big_kernel<kWideNT, false>),
+                         reinterpret_cast<const void *>(&down_big_kernel<kWideNT, true>),
+                         reinterpret_cast<const void *>(&gateup_big_kernel<kWideNT, false>),
+                         reinterpret_cast<const void *>(&gateup_big_kernel<kWideNT, true>)};
+    const size_t big_lds[] = {down_big_lds(), down_big_lds(), gateup_big_lds(), gateup_big_lds()};
+    for (int i = 0; i < 4; ++i)
+        if ((err = hipFuncSetAttribute(big[i], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)big_lds[i])) != hipSuccess)
+            return err;
     const void *gk[] = {reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT, false>),
                         reinterpret_cast<const void *>(&gateup_wide_kernel<OpF32, kWideNT, false>),
                         reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT, true>)};

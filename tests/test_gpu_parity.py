@@ -506,17 +506,23 @@ def test_batch_invariance_bitwise():
 
 def test_fp8_batch_invariance_bitwise():
     """FP8 weights: a token's output bits do not depend on its batch, across the split path
-    (T <= 64) and the 64-token-group path (T > 64)."""
+    (T <= 64), the 64-token-group path (T > 64) and the large-T kernels (T >= 1536)."""
     torch = _torch()
     layer, m, t = get_layer("decode_b1_t4_fp8")
     x = torch.cat([t["x"]] * 8)  # 32 tokens
     y32 = m.forward(x)
     y4 = m.forward(x[:4].contiguous())
     y200 = m.forward(torch.cat([x] * 7)[:200].contiguous())
+    y300 = m.forward(torch.cat([x] * 10)[:300].contiguous())
+    y1600 = m.forward(torch.cat([x] * 50).contiguous())
     torch.cuda.synchronize()
-    assert m.plan(32)[-1] == "down" and m.plan(200)[-3:] == ["gateup_wide", "down_wide", "combine"]
+    assert m.plan(32)[-1] == "down" and m.plan(200)[-3:] == ["gateup_wide", "down_big", "combine"]
+    assert m.plan(300)[-3:] == ["gateup_wide", "down_wide", "combine"]
+    assert m.plan(1600)[-3:] == ["gateup_big", "down_big", "combine"]
     assert torch.equal(y32[:4], y4)
     assert torch.equal(y200[:32], y32) and torch.equal(y200[192:200], y32[:8])
+    assert torch.equal(y300[:32], y32) and torch.equal(y300[288:300], y32[:12])
+    assert torch.equal(y1600[:32], y32) and torch.equal(y1600[1568:], y32)
 
 
 def test_token_permutation_equivariance():
