@@ -70,8 +70,11 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
     const int chunks_per_row = p.H / Op::kPerLane;
     const int nchunks = p.H / kChunkElems;
     const elem_t *x = reinterpret_cast<const elem_t *>(p.x);
-    // loader lane -> (row, piece) of a chunk: 4 instructions of 4 rows x 256 contiguous bytes
+    // loader lane -> (row, piece) of a chunk: 4 instructions of 4 rows x 256 contiguous bytes;
+    // FP8 codes (128 bytes per row and chunk): 2 instructions of 8 rows x 128 bytes, 16 codes a lane
     const int lrow = lane >> 4, lpiece = lane & 15;
+    const int lrow8 = lane >> 3, lpiece8 = lane & 7;
+    constexpr int kLoads = kFp8 ? 2 : 4;  // load instructions per chunk
 
     for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
         const int gi = u / p.S, j = u - (u / p.S) * p.S;
@@ -84,33 +87,46 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
         const wt_t *gu = reinterpret_cast<const wt_t *>(shared ? p.sgu : p.gate_up) +
                          (shared ? 0 : (size_t)e * 2 * Ie * p.H);
         const int wrow0 = (wave < 2 ? 0 : Ie) + j * kSW + (wave & 1) * kTile;  // first weight row
-        const wt_t *src = gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
+        const wt_t *src = kFp8 ? gu + (size_t)(wrow0 + lrow8) * p.H + lpiece8 * 16
+                               : gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
         const bool col_ok = col < n;
         const int crow = col_ok ? col : 0;  // columns >= n repeat column 0 (dropped)
         const elem_t *xrow = xs + crow * p.x_stride + q * Op::kPerLane;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 
-        using raw_t = typename WF::raw_t;
-        raw_t rA[kDepth][4], rB[kDepth][4];
-        auto load = [&](raw_t(&r)[kDepth][4], int c0) {
+        using raw_t = typename std::conditional<kFp8, uint4, typename WF::raw_t>::type;
+        raw_t rA[kDepth][kLoads], rB[kDepth][kLoads];
+        auto load = [&](raw_t(&r)[kDepth][kLoads], int c0) {
 #pragma unroll
             for (int d = 0; d < kDepth; ++d)
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
+                for (int a = 0; a < kLoads; ++a) {
                     const int c = min(c0 + d, nchunks - 1);  // past the end: re-read, unused
-                    r[d][a] = WF::load_raw(src + (size_t)(4 * a) * p.H + c * kChunkElems);
+                    if constexpr (kFp8)
+                        r[d][a] = load16_stream(src + (size_t)(8 * a) * p.H + c * kChunkElems);
+                    else
+                        r[d][a] = WF::load_raw(src + (size_t)(4 * a) * p.H + c * kChunkElems);
                 }
         };
-        auto consume = [&](const raw_t(&r)[kDepth][4], int c0) {
+        auto consume = [&](const raw_t(&r)[kDepth][kLoads], int c0) {
 #pragma unroll
             for (int d = 0; d < kDepth; ++d) {
                 if (c0 + d >= nchunks) break;  // uniform
                 unsigned char *buf = stage + (d % kStageBufs) * kStage;  // a wave's LDS ops stay in order
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int rr = 4 * a + lrow;
-                    *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) =
-                        WF::to_operand(r[d][a]);
+                for (int a = 0; a < kLoads; ++a) {
+                    if constexpr (kFp8) {  // 16 codes widened to two bf16 pieces (exact)
+                        const int rr = 8 * a + lrow8;
+                        const int p0 = 2 * lpiece8;
+                        *reinterpret_cast<uint4 *>(buf + rr * 256 + ((p0 ^ rr) & 15) * 16) =
+                            e4m3x8_to_bf16x8(r[d][a].x, r[d][a].y);
+                        *reinterpret_cast<uint4 *>(buf + rr * 256 + (((p0 + 1) ^ rr) & 15) * 16) =
+                            e4m3x8_to_bf16x8(r[d][a].z, r[d][a].w);
+                    } else {
+                        const int rr = 4 * a + lrow;
+                        *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) =
+                            WF::to_operand(r[d][a]);
+                    }
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
@@ -250,16 +266,25 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
         const int nchunks = Ie / kChunkElems;
         const wt_t *dn = reinterpret_cast<const wt_t *>(shared ? p.sdn : p.down) +
                          (shared ? 0 : (size_t)e * p.H * Ie);
+        // FP8 codes: 2 loads of 8 rows x 128 bytes per chunk (16 codes a lane) in place of 4 of
+        // 4 rows x 128 bytes
+        const int lrow8 = lane >> 3, lpiece8 = lane & 7;
+        constexpr int kLoads = kFp8 ? 2 : 4;
         const wt_t *src =
-            dn + (size_t)(rc * kRowsPerUnit + wave * kTile + lrow) * Ie + lpiece * Op::kPerLane;
-        typename WF::raw_t a[kBatch][4];
+            kFp8 ? dn + (size_t)(rc * kRowsPerUnit + wave * kTile + lrow8) * Ie + lpiece8 * 16
+                 : dn + (size_t)(rc * kRowsPerUnit + wave * kTile + lrow) * Ie + lpiece * Op::kPerLane;
+        using raw_t = typename std::conditional<kFp8, uint4, typename WF::raw_t>::type;
+        raw_t a[kBatch][kLoads];
         auto load = [&](int c0) {
 #pragma unroll
             for (int d = 0; d < kBatch; ++d)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                for (int r = 0; r < kLoads; ++r) {
                     const int c = min(c0 + d, nchunks - 1);  // past the end: re-read, unused
-                    a[d][r] = WF::load_raw(src + (size_t)(4 * r) * Ie + c * kChunkElems);
+                    if constexpr (kFp8)
+                        a[d][r] = load16_stream(src + (size_t)(8 * r) * Ie + c * kChunkElems);
+                    else
+                        a[d][r] = WF::load_raw(src + (size_t)(4 * r) * Ie + c * kChunkElems);
                 }
         };
         load(0);  // the weight stream does not depend on h: start it before staging h
@@ -288,10 +313,19 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
             for (int d = 0; d < kBatch; ++d) {
                 if (c0 + d >= nchunks) break;  // uniform
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int rr = 4 * r + lrow;
-                    *reinterpret_cast<uint4 *>(stage + rr * 256 + ((lpiece ^ rr) & 15) * 16) =
-                        WF::to_operand(a[d][r]);
+                for (int r = 0; r < kLoads; ++r) {
+                    if constexpr (kFp8) {  // 16 codes widened to two bf16 pieces (exact)
+                        const int rr = 8 * r + lrow8;
+                        const int p0 = 2 * lpiece8;
+                        *reinterpret_cast<uint4 *>(stage + rr * 256 + ((p0 ^ rr) & 15) * 16) =
+                            e4m3x8_to_bf16x8(a[d][r].x, a[d][r].y);
+                        *reinterpret_cast<uint4 *>(stage + rr * 256 + (((p0 + 1) ^ rr) & 15) * 16) =
+                            e4m3x8_to_bf16x8(a[d][r].z, a[d][r].w);
+                    } else {
+                        const int rr = 4 * r + lrow;
+                        *reinterpret_cast<uint4 *>(stage + rr * 256 + ((lpiece ^ rr) & 15) * 16) =
+                            WF::to_operand(a[d][r]);
+                    }
                 }
 #pragma unroll
                 for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
