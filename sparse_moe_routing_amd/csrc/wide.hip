@@ -39,24 +39,55 @@ __device__ __forceinline__ uint4 lds_read16(const unsigned char *p) {
     return *reinterpret_cast<const uint4 *>(p);
 }
 
-// Weight chunk of one wave: rows lrow + 4a (a = 0..3) of the wave's 16, 16 pieces each (256
-// bytes of bf16 or fp32, 128 bytes of FP8 codes widened to bf16).
+// Weight chunk of one wave (16 rows x 256 bytes of operands). bf16 / fp32: 4 loads of 4 rows x
+// 256 bytes (lane: row lane / 16 + 4a, 16-byte piece lane % 16). FP8 codes (128 bytes per row):
+// 2 loads of 8 rows x 128 bytes (lane: row lane / 8 + 8a, 16 codes at lane % 8), widened to bf16
+// when staged.
+template <class WF>
+struct WChunk {
+    static constexpr bool k8 = WF::kScaled;
+    static constexpr int kLoads = k8 ? 2 : 4;
+    static constexpr int kRowStep = k8 ? 8 : 4;
+    using raw_t = typename std::conditional<k8, uint4, typename WF::raw_t>::type;
+    // the lane's first row and its element offset in a chunk
+    __device__ static __forceinline__ int row(int lane) { return k8 ? lane >> 3 : lane >> 4; }
+    __device__ static __forceinline__ int elem(int lane) {
+        return k8 ? (lane & 7) * 16 : (lane & 15) * (int)(16 / sizeof(typename WF::wt_t));
+    }
+};
+
 template <class WF, int kCE>
-__device__ __forceinline__ void load_wchunk(typename WF::raw_t (&r)[4], const typename WF::wt_t *src,
-                                            size_t row_stride, int c) {
+__device__ __forceinline__ void load_wchunk(typename WChunk<WF>::raw_t (&r)[WChunk<WF>::kLoads],
+                                            const typename WF::wt_t *src, size_t row_stride, int c) {
+    using W = WChunk<WF>;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) r[a] = WF::load_raw(src + (size_t)(4 * a) * row_stride + c * kCE);
+    for (int a = 0; a < W::kLoads; ++a) {
+        const typename WF::wt_t *ptr = src + (size_t)(W::kRowStep * a) * row_stride + c * kCE;
+        if constexpr (W::k8) r[a] = load16_stream(ptr);
+        else r[a] = WF::load_raw(ptr);
+    }
 }
 
 // Swizzled staging (row rr, piece p at rr * 256 + ((p ^ rr) & 15) * 16) and operand read of
 // step s (piece 4s + q of row col).
 template <class WF>
-__device__ __forceinline__ void stage_w(unsigned char *buf, const typename WF::raw_t (&r)[4],
-                                        int lrow, int lpiece) {
+__device__ __forceinline__ void stage_w(unsigned char *buf,
+                                        const typename WChunk<WF>::raw_t (&r)[WChunk<WF>::kLoads],
+                                        int lane) {
+    using W = WChunk<WF>;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int rr = 4 * a + lrow;
-        *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) = WF::to_operand(r[a]);
+    for (int a = 0; a < W::kLoads; ++a) {
+        const int rr = W::kRowStep * a + W::row(lane);
+        if constexpr (W::k8) {  // 16 codes widened to two bf16 pieces (exact)
+            const int p0 = 2 * (lane & 7);
+            *reinterpret_cast<uint4 *>(buf + rr * 256 + ((p0 ^ rr) & 15) * 16) =
+                e4m3x8_to_bf16x8(r[a].x, r[a].y);
+            *reinterpret_cast<uint4 *>(buf + rr * 256 + (((p0 + 1) ^ rr) & 15) * 16) =
+                e4m3x8_to_bf16x8(r[a].z, r[a].w);
+        } else {
+            const int lpiece = lane & 15;
+            *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) = WF::to_operand(r[a]);
+        }
     }
 }
 __device__ __forceinline__ uint4 w_operand(const unsigned char *buf, int s, int col, int q) {
@@ -85,7 +116,7 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int col = lane & 15, q = lane >> 4, lrow = lane >> 4, lpiece = lane & 15;
+    const int col = lane & 15, q = lane >> 4;
     unsigned char *stage = stage_all + wave * kWStage;
     const int nunits = p.num_groups[0] * p.S;
     const int nchunks = p.H / kCE;
@@ -105,7 +136,8 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
         const wt_t *gu = reinterpret_cast<const wt_t *>(shared ? p.sgu : p.gate_up) +
                          (shared ? 0 : (size_t)e * 2 * Ie * p.H);
         const int wrow0 = (wave < kGW ? 0 : Ie) + j * kSW + (wave % kGW) * kTile;
-        const wt_t *src = gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
+        using W = WChunk<WF>;
+        const wt_t *src = gu + (size_t)(wrow0 + W::row(lane)) * p.H + W::elem(lane);
         const elem_t *xsrc[kXPasses];
 #pragma unroll
         for (int i = 0; i < kXPasses; ++i) {
@@ -117,7 +149,7 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
         // weight chunks in flight: a ring of kWD register buffers (FP8 codes are half the bytes,
         // so twice the chunks fill the same registers)
         constexpr int kWD = kFp8 ? 4 : 2;
-        typename WF::raw_t wr[kWD][4];
+        typename W::raw_t wr[kWD][W::kLoads];
         uint4 xv[kXPasses];
         // a pass whose rows all lie past n is skipped (uniform): the columns those rows feed are
         // dropped, whatever the stale LDS holds
@@ -143,10 +175,10 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
         load_x(0);
         __syncthreads();  // the previous unit's readers of xs / xchg are done
         store_x(0);
-        auto step = [&](typename WF::raw_t (&wcur)[4], int c) {
+        auto step = [&](typename W::raw_t (&wcur)[W::kLoads], int c) {
             if (c + 1 < nchunks) load_x(c + 1);
             __syncthreads();  // x chunk c is staged; chunk c - 1's readers are done
-            stage_w<WF>(stage, wcur, lrow, lpiece);
+            stage_w<WF>(stage, wcur, lane);
             if (c + kWD < nchunks) load_wchunk<WF, kCE>(wcur, src, p.H, c + kWD);
             const unsigned char *xb = xs + (c & 1) * TG * kXRow;
 #pragma unroll
@@ -230,7 +262,7 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int col = lane & 15, q = lane >> 4, lrow = lane >> 4, lpiece = lane & 15;
+    const int col = lane & 15, q = lane >> 4;
     unsigned char *stage = stage_all + wave * kDownTiles * kWStage;
     const int n_rc = (p.H + kRowsPerUnit - 1) / kRowsPerUnit;  // the last block may be partial
     const int nunits = p.num_groups[0] * n_rc;
@@ -251,7 +283,8 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
         // past H (H is a multiple of 32) only joins the block barriers
         const int wrow = rc * kRowsPerUnit + wave * kDownTiles * kTile;
         const bool rows_ok = wrow < p.H;  // uniform over the wave
-        const wt_t *src = dn + (size_t)((rows_ok ? wrow : 0) + lrow) * Ie + lpiece * Op::kPerLane;
+        using W = WChunk<WF>;
+        const wt_t *src = dn + (size_t)((rows_ok ? wrow : 0) + W::row(lane)) * Ie + W::elem(lane);
         const elem_t *hsrc[kHPasses];
 #pragma unroll
         for (int i = 0; i < kHPasses; ++i) {
@@ -261,9 +294,9 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
             hsrc[i] = hg + (size_t)slot * p.Imax + hp * Op::kPerLane;
         }
         constexpr int kWD = kFp8 ? 4 : 2;  // weight chunks in flight (ring of register buffers)
-        typename WF::raw_t wr[kWD][kDownTiles][4];
+        typename W::raw_t wr[kWD][kDownTiles][W::kLoads];
         uint4 hv[kPlanes][kHPasses];
-        auto load_w = [&](typename WF::raw_t (&w)[kDownTiles][4], int c) {
+        auto load_w = [&](typename W::raw_t (&w)[kDownTiles][W::kLoads], int c) {
 #pragma unroll
             for (int t = 0; t < kDownTiles; ++t)
                 load_wchunk<WF, kCE>(w[t], src + (size_t)(t * kTile) * Ie, Ie, c);
@@ -298,12 +331,12 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
         load_h(0);
         __syncthreads();  // the previous unit's readers of hs are done
         store_h(0);
-        auto step = [&](typename WF::raw_t (&wcur)[kDownTiles][4], int c) {
+        auto step = [&](typename W::raw_t (&wcur)[kDownTiles][W::kLoads], int c) {
             if (c + 1 < nchunks) load_h(c + 1);
             __syncthreads();  // h chunk c is staged; chunk c - 1's readers are done
             if (rows_ok) {
 #pragma unroll
-                for (int t = 0; t < kDownTiles; ++t) stage_w<WF>(stage + t * kWStage, wcur[t], lrow, lpiece);
+                for (int t = 0; t < kDownTiles; ++t) stage_w<WF>(stage + t * kWStage, wcur[t], lane);
                 if (c + kWD < nchunks) load_w(wcur, c + kWD);
             }
 #pragma unroll
@@ -379,7 +412,6 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
     using wt_t = typename WeightFmt<Op, kFp8>::wt_t;  // bf16, or one-byte E4M3 codes
     constexpr int TG = NT * kTile;
     constexpr int kCE = kWPieces * Op::kPerLane;          // elements per chunk (128)
-    constexpr int kSteps = kWPieces / 4;                  // matrix-core steps per chunk
     constexpr int kRT = 2 * kBigRows / kTile;             // weight tiles per wave (gate, up)
     constexpr int kSW = kBigWaves * kBigRows;             // intermediate rows per unit
     constexpr int kXPasses = TG * kWPieces / kBigThreads;
