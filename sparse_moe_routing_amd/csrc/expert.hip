@@ -259,13 +259,16 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineParams p) {
             acc.x += gt * s.x; acc.y += gt * s.y; acc.z += gt * s.z; acc.w += gt * s.w;
         }
     } else {  // weighted partials, one chunk each: y = sum_k v_k + v_shared, in rank order
+        // (each slot output is read exactly once: non-temporal loads keep it out of the caches)
+        auto ld4 = [](const float *a) {
+            const f32x4_t r = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(a));
+            return make_float4(r[0], r[1], r[2], r[3]);
+        };
         float4 v[kTopK + 1];
 #pragma unroll
-        for (int k = 0; k < kTopK; ++k)
-            v[k] = *reinterpret_cast<const float4 *>(p.ypart + (size_t)(t * kTopK + k) * p.H + h);
-        v[kTopK] = p.has_shared
-            ? *reinterpret_cast<const float4 *>(p.ypart + (size_t)(p.T * kTopK + t) * p.H + h)
-            : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int k = 0; k < kTopK; ++k) v[k] = ld4(p.ypart + (size_t)(t * kTopK + k) * p.H + h);
+        v[kTopK] = p.has_shared ? ld4(p.ypart + (size_t)(p.T * kTopK + t) * p.H + h)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int k = 0; k < kTopK; ++k) {
             acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
