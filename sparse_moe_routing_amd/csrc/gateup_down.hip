@@ -256,6 +256,11 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
     const int ngroups = p.num_groups[0];
     const int nunits = ngroups * n_rc;
     const h_t *hg = reinterpret_cast<const h_t *>(p.h);
+    // With a grid that is a multiple of the row-block count every unit of this block has row
+    // block blockIdx.x % n_rc: the block then waits for its stores and arrives once, after its
+    // last unit, adding its unit count (one store-acknowledge wait per block, not per unit).
+    const bool defer = gridDim.x % n_rc == 0;
+    int my_units = 0;
 
     for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
         const int gi = u / n_rc, rc = u - (u / n_rc) * n_rc;
@@ -352,6 +357,10 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
         // The last unit to finish row block rc (of the num_groups units that write it) sums, for
         // every token, the eight weighted rank outputs in rank order and then the gated shared
         // output: the combine, without a kernel of its own.
+        if (defer) {
+            ++my_units;
+            continue;
+        }
         wait_own_stores();
         __syncthreads();
         if (tid == 0) {
@@ -364,6 +373,17 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
             asm volatile("" : "+v"(t2));  // keeps the combine's addressing out of the unit loop
             combine_rows(p, rc * kRowsPerUnit, t2);
         }
+    }
+    if (defer && my_units > 0) {  // uniform over the block
+        const int rc = blockIdx.x % n_rc;
+        wait_own_stores();
+        __syncthreads();
+        if (tid == 0) {
+            s_last = atomicAdd(p.rb_arrivals + rc, my_units) + my_units == ngroups;
+            if (s_last) p.rb_arrivals[rc] = 0;  // all units of rc arrived: reset for the next call
+        }
+        __syncthreads();
+        if (s_last) combine_rows(p, rc * kRowsPerUnit, tid);
     }
 }
 
