@@ -4,7 +4,7 @@
 // Decode rounds touch each selected expert with one or two tokens, so the stage is a stream of
 // expert weights read once from HBM (the expert block dominates a MoE model's bytes and decode is
 // bandwidth-bound: "RELEASE_NOTES_0.9.0" of the 16 GB ninfer fork, the expert-placement
-// paragraphs). A unit of work is (group of up to 16 tokens routed to one expert, chunk of
+// paragraphs). A unit of work is (group of up to 8 tokens routed to one expert, chunk of
 // 16-wide slices of the intermediate dimension):
 //   1. the group's x rows are staged in LDS (bf16 or fp32, row stride padded by 16 bytes so the
 //      16 rows fall in different banks);

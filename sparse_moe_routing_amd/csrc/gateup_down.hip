@@ -5,7 +5,7 @@
 // bandwidth-bound: "RELEASE_NOTES_0.9.0" of the 16 GB ninfer fork, the expert-placement
 // paragraphs). It is split so that each weight matrix is streamed in the order that suits it:
 //
-// gateup_kernel - one block per (expert group of <= 16 tokens, 32-row slice of the intermediate
+// gateup_kernel - one block per (expert group of <= 8 tokens, 32-row slice of the intermediate
 //   dimension): the group's x rows are staged in LDS; two waves compute the 16x16 gate tiles and
 //   two the 16x16 up tiles of the slice with MFMA, each streaming its 16 weight rows from HBM in
 //   long contiguous runs and reordering them through LDS into operand order;

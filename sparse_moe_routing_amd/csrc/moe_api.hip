@@ -9,7 +9,7 @@
 //                 + expert histogram
 //   bucket_scan   per-expert chunk bases, counts, offsets, expert-group table
 //   bucket_scatter the stable scatter of pair indices
-//   gateup        T <= 64: gate/up + SwiGLU into h per (16-token expert group, 32 inter. rows)
+//   gateup        T <= 64: gate/up + SwiGLU into h per (8-token expert group, 32 inter. rows)
 //   down          T <= 64: down product per (expert group, 64 rows of y), weighted per slot;
 //                 the last unit of each 64-row block sums the slots into y
 //   gateup_wide   T > 64: as gateup for 64-token expert groups (wide.hip)
@@ -61,7 +61,7 @@ constexpr int kTileRouteMaxTokens = 64;
 constexpr int kHistChunk = 16;
 // 64 < T <= 256: selection and bucketing in one launch (select_bucket)
 constexpr int kSelBucketMaxTokens = 256;
-constexpr int kSplitMaxTokens = 64;   // 16-token groups up to here, 64-token groups above
+constexpr int kSplitMaxTokens = 64;   // 8-token groups up to here, 64-token groups above
 constexpr int kBigMinTokens = 1536;     // bf16 from here: gateup_big in place of gateup_wide
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -74,7 +74,7 @@ struct Plan {
     int s = 64, S = 1, SPU = 1, n_sc = 1, n_sc_routed = 1, n_sc_shared = 0, slots = 0;
     int x_stride = 0, grid = 1;
     size_t lds = 0;
-    bool split = false;          // T <= 64: gateup + down kernels, 16-token groups
+    bool split = false;          // T <= 64: gateup + down kernels, 8-token groups
     bool wide = false;           // T > 64: gateup_wide + down_wide + combine, 64-token groups
     bool big = false;            // wide, bf16 or FP8, T >= kBigMinTokens: gateup_big for gateup_wide
     bool down_big = false;       // wide, bf16 or FP8, H a multiple of 512, T <= 256 or big
@@ -106,12 +106,15 @@ size_t state_bytes(const moe_ctx *c) {
     return align_up((size_t)(kStateRowBlocks + c->cfg.hidden / 64) * 4);
 }
 
-// Rows of an expert group: up to 16 tokens, fewer when the x tile would not fit in LDS.
+// Rows of an expert group: up to 8 tokens, fewer when the x tile would not fit in LDS. The x tile
+// is sized for a full group, so the cap sets the gate/up kernel's blocks per CU: measured at the
+// decode shapes, 8 rows against 16: T = 16 125.6 vs 134.5 us per step, T = 32 186.2 vs 200.0,
+// T = 64 254.0 vs 270.8 (4 and 6 rows within 1 % of 8 below T = 64, worse at 64).
 int group_rows(const moe_ctx *c, int T) {
     const int esz = elem_bytes(c->cfg.dtype);
     const int x_stride = c->cfg.hidden + 16 / esz;
     const int ng_lds = (int)(kMaxXTileBytes / ((size_t)x_stride * esz));
-    int NG = T < 16 ? T : 16;
+    int NG = T < 8 ? T : 8;
     if (NG > ng_lds) NG = ng_lds;
     return NG;
 }
@@ -130,7 +133,7 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.maxrt = T > 256 ? 4 : 1;
     p.n_rg = (n_rt + p.maxrt - 1) / p.maxrt;
     // bucketing and expert groups
-    // x-tile rows: up to 16 tokens, fewer when a row of H elements would not leave room in LDS
+    // x-tile rows: up to 8 tokens, fewer when a row of H elements would not leave room in LDS
     const int esz = elem_bytes(cfg.dtype);
     p.x_stride = H + 16 / esz;
     const int ng_x = group_rows(c, T);  // x-tile rows of the split and fused expert kernels

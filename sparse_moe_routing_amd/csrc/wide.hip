@@ -1,7 +1,7 @@
 // wide.hip - the expert stage for larger rounds (T > 64): expert groups of up to 64 tokens.
 //
-// With 16-token groups an expert that draws 150 tokens (the skewed verify workload) has its
-// weights read ten times. Here a group holds up to 64 tokens, so every weight fragment that a wave
+// With the decode path's 8-token groups an expert that draws 150 tokens (the skewed verify
+// workload) would have its weights read nineteen times. Here a group holds up to 64 tokens, so every weight fragment that a wave
 // stages feeds four 16-token matrix-core tiles and an expert's weights are read once per 64 of
 // its tokens. The token operands no longer fit in LDS for the whole K range, so they are staged
 // one 256-byte K chunk at a time, double-buffered, with one block barrier per chunk:
