@@ -147,8 +147,9 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
             xsrc[i] = x + (size_t)tok * p.H + xp * Op::kPerLane;
         }
         // weight chunks in flight: a ring of kWD register buffers (FP8 codes are half the bytes,
-        // so twice the chunks fill the same registers)
-        constexpr int kWD = kFp8 ? 4 : 2;
+        // so more chunks fill the same registers); bf16: 3 measured best (uniform T = 192 gate/up
+        // 196.9 us against 202.9 with 2; 4 drops to three waves per SIMD: 206.8)
+        constexpr int kWD = kFp8 ? 4 : 3;
         typename W::raw_t wr[kWD][W::kLoads];
         uint4 xv[kXPasses];
         // a pass whose rows all lie past n is skipped (uniform): the columns those rows feed are
