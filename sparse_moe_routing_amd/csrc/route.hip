@@ -345,7 +345,12 @@ __global__ __launch_bounds__(1024) void select_bucket_kernel(SelectParams sp, Bu
     __syncthreads();
     if (!s_last) return;  // uniform over the block
     const int n = T * kTopK;
-    for (int i = tid; i < n; i += blockDim.x) s.ids[i] = do_select ? ld_dev(sp.ids + i) : bp.ids_in[i];
+    // both loads of a thread are issued before either is used (n <= 2 * 1024)
+    const int i1 = tid + (int)blockDim.x;
+    const int v0 = tid < n ? (do_select ? ld_dev(sp.ids + tid) : bp.ids_in[tid]) : 0;
+    const int v1 = i1 < n ? (do_select ? ld_dev(sp.ids + i1) : bp.ids_in[i1]) : 0;
+    if (tid < n) s.ids[tid] = v0;
+    if (i1 < n) s.ids[i1] = v1;
     __syncthreads();
     const int cnt = chunk_counts(s, n, bp.E);
     write_tables(bp, cnt, s);  // ends with a barrier; s.a[e] = offset of expert e
