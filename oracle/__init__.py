@@ -25,6 +25,7 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 F32 = 0
 BF16 = 1
 FP8 = 2  # expert weights only: OCP FP8 E4M3 codes (numpy.uint8) with fp32 per-row scales
+MXFP4 = 3  # expert weights only: OCP MXFP4, packed E2M1 codes with E8M0 scale bytes per 32
 
 _lock = threading.Lock()
 _lib = None
@@ -68,6 +69,9 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_num_threads.argtypes = []
     lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_value.restype = ctypes.c_double
+    for f in (lib.oracle_e2m1_value, lib.oracle_e8m0_value):
+        f.argtypes = [ctypes.c_uint8]
+        f.restype = ctypes.c_double
     for f in (lib.oracle_logits, lib.oracle_select, lib.oracle_bucket, lib.oracle_forward,
               lib.oracle_forward_w, lib.oracle_num_threads):
         f.restype = ctypes.c_int
@@ -159,12 +163,17 @@ class Oracle:
         y = np.empty((tokens.size, H), dtype=np.float64)
         sgu = layer.get("shared_gate_up") if Is > 0 else None
         sdn = layer.get("shared_down") if Is > 0 else None
-        if layer["gate_up"].dtype == np.uint8:  # FP8 E4M3 codes with per-row scales
-            def f32(a):
-                return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
-            sc = [f32(layer.get(n)) for n in ("gate_up_scale", "down_scale",
-                                              "shared_gate_up_scale", "shared_down_scale")]
-            rc = self.lib.oracle_forward_w(tokens.size, _ptr(tokens), T, H, E, I, Is, k, dt, FP8,
+        if layer["gate_up"].dtype == np.uint8:
+            # FP8 E4M3 codes with fp32 per-row scales, or MXFP4 packed codes with E8M0 scale bytes
+            mx = layer.get("dtype") == "mxfp4"
+            st = np.uint8 if mx else np.float32
+
+            def sc_arr(a):
+                return None if a is None else np.ascontiguousarray(a, dtype=st)
+            sc = [sc_arr(layer.get(n)) for n in ("gate_up_scale", "down_scale",
+                                                 "shared_gate_up_scale", "shared_down_scale")]
+            rc = self.lib.oracle_forward_w(tokens.size, _ptr(tokens), T, H, E, I, Is, k, dt,
+                                           MXFP4 if mx else FP8,
                                            _ptr(x), _ptr(layer["gate_up"]), _ptr(layer["down"]),
                                            _ptr(sgu), _ptr(sdn), *[_ptr(a) for a in sc],
                                            _ptr(ids), _ptr(w), _ptr(g), _ptr(y))
@@ -180,6 +189,14 @@ class Oracle:
     def e4m3_value(self, code: int) -> float:
         """The value of one OCP FP8 E4M3 code (NaN for the two NaN codes)."""
         return float(self.lib.oracle_e4m3_value(int(code)))
+
+    def e2m1_value(self, code: int) -> float:
+        """The value of one FP4 E2M1 code (the low four bits of `code`)."""
+        return float(self.lib.oracle_e2m1_value(int(code)))
+
+    def e8m0_value(self, b: int) -> float:
+        """The value of one E8M0 scale byte (NaN for 0xFF)."""
+        return float(self.lib.oracle_e8m0_value(int(b)))
 
     def route(self, layer, logits_override=None):
         """Logits (fp32), then selection on them: the plain path from x to (ids, w, g)."""

@@ -31,10 +31,12 @@
  *   oracle_forward  for each requested token: sum over the eight ranks of w_k * FFN_{id_k}(x) plus
  *                   g * FFN_shared(x), where FFN(x) = Wd (silu(Wg x) * (Wu x)) and
  *                   silu(a) = a / (1 + exp(-a)); every step in fp64 with no intermediate rounding.
- *   oracle_forward_w the same with FP8 expert weights: each weight is its E4M3 code's value times
- *                   its row's fp32 scale, taken exactly in fp64 before the products (the pages
- *                   name quantized expert formats - groupwise integers, FP8, NVFP4 - without
- *                   fixing one; per-row scales over OCP E4M3 codes are the reading here).
+ *   oracle_forward_w the same with quantized expert weights, each weight's value taken exactly in
+ *                   fp64 before the products: FP8 - its E4M3 code's value times its row's fp32
+ *                   scale; MXFP4 - its E2M1 code's value times the E8M0 scale of its block of 32
+ *                   consecutive weights along the row (the pages name quantized expert formats -
+ *                   groupwise integers, FP8, NVFP4 - without fixing one; these two, per-row-scaled
+ *                   E4M3 and the Open Compute Project's MXFP4, are the readings here).
  *
  * Comparison semantics: IEEE-754 fp32 values compared as values, so -0 equals +0 (a tie, decided
  * by the id). NaN ranks below every non-NaN value, -inf included; NaNs tie among themselves and
@@ -54,6 +56,9 @@
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
 #define ORACLE_FP8 2 /* weights only: OCP FP8 E4M3 codes, each row times its own fp32 scale */
+#define ORACLE_MXFP4 3 /* weights only: OCP MXFP4 - E2M1 codes, two per byte (the even column in
+                          the low nibble), each block of 32 columns times its E8M0 scale byte */
+#define MX_BLOCK 32    /* weights per shared scale in MXFP4 */
 
 /* Value of one OCP FP8 E4M3 code (the 8-bit floating-point format of the Open Compute Project
  * specification: sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, and
@@ -73,6 +78,31 @@ double oracle_e4m3_value(uint8_t code) {
     return s ? -v : v;
 }
 
+/* Value of one FP4 E2M1 code (the 4-bit element type of the Open Compute Project's Microscaling
+ * (MX) formats specification): sign bit, 2 exponent bits with bias 1, 1 mantissa bit; exponent
+ * field 0 holds zero and the subnormal 0.5, otherwise the value is 2^(e - 1) * (1 + m / 2). No
+ * infinities or NaN: the eight magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6. Exact in double. */
+double oracle_e2m1_value(uint8_t code) {
+    const int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+#ifdef ORACLE_PLANT_E2M1_BIAS2
+    const double v = e == 0 ? 0.25 * m : ldexp(1.0 + 0.5 * m, e - 2); /* planted: bias 2 */
+#else
+    const double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+#endif
+    return s ? -v : v;
+}
+
+/* Value of one E8M0 scale byte (the MX formats' shared scale: an unsigned exponent with bias 127
+ * and no mantissa): 2^(b - 127); the byte 0xFF is NaN. Exact in double. */
+double oracle_e8m0_value(uint8_t b) {
+    if (b == 0xFF) return NAN;
+#ifdef ORACLE_PLANT_E8M0_BIAS128
+    return ldexp(1.0, (int)b - 128); /* planted mistake: bias off by one */
+#else
+    return ldexp(1.0, (int)b - 127);
+#endif
+}
+
 /* Widen one stored element to double. bf16 is the top half of an fp32 word, so the value is the
  * 16 stored bits shifted into the high half; the conversion is exact. An FP8 element is its
  * code's value times the fp32 scale of its row (given by the caller). */
@@ -87,6 +117,39 @@ static double load_elem(const void *base, int dtype, size_t i) {
 
 static size_t elem_size(int dtype) {
     return dtype == ORACLE_F32 ? 4 : dtype == ORACLE_FP8 ? 1 : 2;
+}
+
+/* Weight (row, col) of a matrix with `cols` columns in weight format wdtype, as a double, with
+ * the scales of row srow (always row itself, except in one planted-mistake build). FP8: the
+ * code's value times the row's fp32 scale (scale[srow]; 1 without scales). MXFP4: codes packed
+ * two per byte along the row (column 2j in the low nibble of byte j, 2j + 1 in the high one),
+ * scale bytes [rows][cols / 32]; the weight is the code's value times its block's scale. */
+static double weight_at(const void *m, const void *scale, int wdtype, int row, int col, int cols,
+                        int srow) {
+    if (wdtype == ORACLE_MXFP4) {
+        const uint8_t b = ((const uint8_t *)m)[(size_t)row * (cols / 2) + col / 2];
+#ifdef ORACLE_PLANT_FP4_HIGH_FIRST
+        const uint8_t code = (col & 1) ? (b & 15) : (b >> 4); /* planted: nibble order swapped */
+#else
+        const uint8_t code = (col & 1) ? (b >> 4) : (b & 15);
+#endif
+        const uint8_t sb = ((const uint8_t *)scale)[(size_t)srow * (cols / MX_BLOCK) + col / MX_BLOCK];
+        return oracle_e2m1_value(code) * oracle_e8m0_value(sb);
+    }
+    const double v = load_elem(m, wdtype, (size_t)row * cols + col);
+    if (wdtype == ORACLE_FP8 && scale) return v * (double)((const float *)scale)[srow];
+    return v;
+}
+
+/* Bytes of one stored [rows][cols] weight matrix, and of its scales (0 without). */
+static size_t matrix_bytes(int wdtype, int rows, int cols) {
+    if (wdtype == ORACLE_MXFP4) return (size_t)rows * (cols / 2);
+    return (size_t)rows * cols * elem_size(wdtype);
+}
+static size_t scale_bytes(int wdtype, int rows, int cols) {
+    if (wdtype == ORACLE_FP8) return (size_t)rows * sizeof(float);
+    if (wdtype == ORACLE_MXFP4) return (size_t)rows * (cols / MX_BLOCK);
+    return 0;
 }
 
 /* ---------------------------------------------------------------- router logits */
@@ -188,23 +251,22 @@ int oracle_bucket(int n, int E, const int32_t *ids, int32_t *counts, int32_t *of
 }
 
 /* ---------------------------------------------------------------- one SwiGLU FFN */
-/* o[H] = Wd (silu(Wg x) * (Wu x)); gate_up is [2*I][H] with the gate rows first, down is [H][I]. */
-/* With scales (FP8 weights): element (row, col) of a matrix is value(code) * scale[row]; gu_scale
- * has 2I entries (gate rows, then up rows), dn_scale H. Without, the scales are 1. */
+/* o[H] = Wd (silu(Wg x) * (Wu x)); gate_up is [2*I][H] with the gate rows first, down is [H][I].
+ * Quantized weights take their scales as weight_at states: gu_scale covers the 2I gate and up
+ * rows, dn_scale the H down rows (NULL without scales). */
 static void swiglu_ffn(int H, int I, int dtype, const double *x, const void *gate_up,
-                       const void *down, const float *gu_scale, const float *dn_scale,
+                       const void *down, const void *gu_scale, const void *dn_scale,
                        double *hbuf, double *o) {
     for (int i = 0; i < I; ++i) {
         double a = 0.0, u = 0.0;
-        const double sg = gu_scale ? (double)gu_scale[i] : 1.0;
 #ifdef ORACLE_PLANT_UP_SCALE_ROW
-        const double su = gu_scale ? (double)gu_scale[i] : 1.0; /* planted: the gate row's scale */
+        const int su = i; /* planted mistake: the up row takes its gate row's scales */
 #else
-        const double su = gu_scale ? (double)gu_scale[I + i] : 1.0;
+        const int su = I + i;
 #endif
         for (int h = 0; h < H; ++h) {
-            a += load_elem(gate_up, dtype, (size_t)i * H + h) * sg * x[h];
-            u += load_elem(gate_up, dtype, (size_t)(I + i) * H + h) * su * x[h];
+            a += weight_at(gate_up, gu_scale, dtype, i, h, H, i) * x[h];
+            u += weight_at(gate_up, gu_scale, dtype, I + i, h, H, su) * x[h];
         }
 #ifdef ORACLE_PLANT_SWAP_GATE_UP
         { double tmp = a; a = u; u = tmp; } /* planted mistake: gate and up rows exchanged */
@@ -213,8 +275,7 @@ static void swiglu_ffn(int H, int I, int dtype, const double *x, const void *gat
     }
     for (int h = 0; h < H; ++h) {
         double acc = 0.0;
-        const double sd = dn_scale ? (double)dn_scale[h] : 1.0;
-        for (int i = 0; i < I; ++i) acc += load_elem(down, dtype, (size_t)h * I + i) * sd * hbuf[i];
+        for (int i = 0; i < I; ++i) acc += weight_at(down, dn_scale, dtype, h, i, I, h) * hbuf[i];
         o[h] = acc;
     }
 }
@@ -223,21 +284,27 @@ static void swiglu_ffn(int H, int I, int dtype, const double *x, const void *gat
 /* For each token t = tokens[j] (j < n_tok): y[j][:] = sum_r w[t][r] * FFN_{ids[t][r]}(x_t)
  * + g[t] * FFN_shared(x_t). gate_up is [E][2I][H], down is [E][H][I]; the shared expert is
  * skipped when Is == 0. ids/w hold k entries per token; g may be NULL iff Is == 0. x has element
- * type xdtype, the expert weights wdtype; with wdtype FP8 the four scale arrays give each weight
- * row's scale: gu_scale [E][2I], dn_scale [E][H], sgu_scale [2Is], sdn_scale [H]. */
+ * type xdtype, the expert weights wdtype. With wdtype FP8 the four scale arrays (fp32) give each
+ * weight row's scale: gu_scale [E][2I], dn_scale [E][H], sgu_scale [2Is], sdn_scale [H]; with
+ * MXFP4 the matrices hold packed codes ([E][2I][H/2], [E][H][I/2], [2Is][H/2], [H][Is/2] bytes)
+ * and the scale arrays E8M0 bytes, one per 32 weights of a row: [E][2I][H/32], [E][H][I/32],
+ * [2Is][H/32], [H][Is/32]. */
 int oracle_forward_w(int n_tok, const int32_t *tokens, int T, int H, int E, int I, int Is, int k,
                      int xdtype, int wdtype, const void *x, const void *gate_up, const void *down,
-                     const void *shared_gate_up, const void *shared_down, const float *gu_scale,
-                     const float *dn_scale, const float *sgu_scale, const float *sdn_scale,
+                     const void *shared_gate_up, const void *shared_down, const void *gu_scale,
+                     const void *dn_scale, const void *sgu_scale, const void *sdn_scale,
                      const int32_t *ids, const double *w, const double *g, double *y) {
     if (n_tok < 0 || H <= 0 || E <= 0 || I <= 0 || Is < 0 || k <= 0) return -1;
     if (xdtype != ORACLE_F32 && xdtype != ORACLE_BF16) return -1;
+    if (wdtype < ORACLE_F32 || wdtype > ORACLE_MXFP4) return -1;
     if (Is > 0 && (!shared_gate_up || !shared_down || !g)) return -1;
-    const int scaled = wdtype == ORACLE_FP8;
+    const int scaled = wdtype == ORACLE_FP8 || wdtype == ORACLE_MXFP4;
     if (scaled && (!gu_scale || !dn_scale || (Is > 0 && (!sgu_scale || !sdn_scale)))) return -1;
+    if (wdtype == ORACLE_MXFP4 && (H % MX_BLOCK || I % MX_BLOCK || Is % MX_BLOCK)) return -1;
     for (int j = 0; j < n_tok; ++j)
         if (tokens[j] < 0 || tokens[j] >= T) return -1;
-    const size_t esz = elem_size(wdtype);
+    const size_t gu_b = matrix_bytes(wdtype, 2 * I, H), dn_b = matrix_bytes(wdtype, H, I);
+    const size_t gus_b = scale_bytes(wdtype, 2 * I, H), dns_b = scale_bytes(wdtype, H, I);
     const int Imax = I > Is ? I : Is;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
@@ -252,10 +319,11 @@ int oracle_forward_w(int n_tok, const int32_t *tokens, int T, int H, int E, int 
         for (int r = 0; r < k; ++r) {
             const int e = ids[(size_t)t * k + r];
             if (e < 0 || e >= E) { bad = 1; break; }
-            const char *gu = (const char *)gate_up + (size_t)e * 2 * I * H * esz;
-            const char *dn = (const char *)down + (size_t)e * H * I * esz;
-            swiglu_ffn(H, I, wdtype, xt, gu, dn, scaled ? gu_scale + (size_t)e * 2 * I : NULL,
-                       scaled ? dn_scale + (size_t)e * H : NULL, hb, o);
+            const char *gu = (const char *)gate_up + (size_t)e * gu_b;
+            const char *dn = (const char *)down + (size_t)e * dn_b;
+            swiglu_ffn(H, I, wdtype, xt, gu, dn,
+                       scaled ? (const char *)gu_scale + (size_t)e * gus_b : NULL,
+                       scaled ? (const char *)dn_scale + (size_t)e * dns_b : NULL, hb, o);
             const double wk = w[(size_t)t * k + r];
             for (int h = 0; h < H; ++h) yj[h] += wk * o[h];
         }

@@ -27,6 +27,14 @@ v / scale (ties to the even code), so the row's largest magnitude becomes 448; t
 stored next to the codes as gate_up_scale [E][2I], down_scale [E][H], shared_gate_up_scale
 [2Is], shared_down_scale [H]. gate and up are stored stacked as gate_up [E][2I][H] (gate rows first); down is
 [E][H][I] (the nn.Linear convention: output rows, input columns contiguous).
+mxfp4 workloads quantize the same expert weight rows to OCP MXFP4 (the Open Compute Project's
+Microscaling formats): each block of 32 consecutive weights of a row shares one E8M0 scale byte
+b (scale 2^(b - 127)), chosen as 2^(floor(log2(max|block|)) - 2) (the largest E2M1 magnitude is
+6 = 1.5 * 2^2; an all-zero block takes b = 127), and each weight becomes the FP4 E2M1 code nearest
+to v / scale (ties to the even code, magnitudes above 6 saturate to 6). Codes are packed two per
+byte along the row, the even column in the low nibble: gate_up [E][2I][H/2], down [E][H][I/2],
+shared [2Is][H/2], [H][Is/2]; the scale bytes are gate_up_scale [E][2I][H/32], down_scale
+[E][H][I/32], shared_gate_up_scale [2Is][H/32], shared_down_scale [H][Is/32].
 
 Tie tokens: selected tokens have every router score replaced by the nearest multiple of 0.25
 (ties to even), which forces equal logits across experts; those tokens are routed from the given
@@ -49,7 +57,8 @@ class Workload:
     inter: int
     shared_inter: int
     dtype: str            # "f32" or "bf16": storage type of x and of every weight; "fp8": x and
-                          # the router in bf16, expert weights as FP8 E4M3 codes + row scales
+                          # the router in bf16, expert weights as FP8 E4M3 codes + row scales;
+                          # "mxfp4": as fp8 with MXFP4 expert weights (E2M1 + E8M0 per 32)
     bias_std: float = 0.0  # > 0: per-expert router bias ~ N(0, bias_std^2)
     tie_every: int = 0     # > 0: tokens t with t % tie_every == 0 get tie-quantized logits
     seed: int = 0
@@ -68,6 +77,13 @@ WORKLOADS = (
     Workload("verify_skewed_t192_fp8", 192, 2048, 256, 8, 512, 512, "fp8",
              bias_std=2.0 ** 0.5, seed=13),
     Workload("prefill_t8192_fp8", 8192, 2048, 256, 8, 512, 512, "fp8", tie_every=10, seed=14),
+    # and with MXFP4 expert weights
+    Workload("decode_b1_t4_mxfp4", 4, 2048, 256, 8, 512, 512, "mxfp4", seed=21),
+    Workload("decode_b8_t32_mxfp4", 32, 2048, 256, 8, 512, 512, "mxfp4", seed=22),
+    Workload("verify_skewed_t192_mxfp4", 192, 2048, 256, 8, 512, 512, "mxfp4",
+             bias_std=2.0 ** 0.5, seed=23),
+    Workload("prefill_t8192_mxfp4", 8192, 2048, 256, 8, 512, 512, "mxfp4", tie_every=10,
+             seed=24),
 )
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -111,17 +127,54 @@ def quantize_rows_e4m3(v: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return f32_to_e4m3_codes(v / scale[..., None]), scale
 
 
+def f32_to_e2m1_codes(a: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 codes (uint8, 0..15) of float32 values: the nearest of the eight magnitudes
+    0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code, magnitudes above 6 saturated to 6; the sign
+    in bit 3 (zero is code 0). Sign bit, 2 exponent bits (bias 1), 1 mantissa bit; exponent
+    field 0 holds 0 and the subnormal 0.5."""
+    a = np.asarray(a, dtype=np.float32)
+    v = np.abs(a)
+    # from 1 up: round the float32 significand to 1 bit, nearest-even (a carry moves the exponent)
+    b = v.view(np.uint32)
+    b = b + np.uint32(0x1FFFFF) + ((b >> np.uint32(22)) & np.uint32(1))
+    ex = (b >> np.uint32(23)).astype(np.int32) - 127
+    code_n = np.where(ex > 2, 7, ((ex + 1) << 1) | ((b >> np.uint32(22)) & np.uint32(1)).astype(np.int32))
+    # below 1: multiples of 0.5 (2 * 0.5 is 1.0, whose code is 2); rint rounds ties to even
+    code_s = np.rint(v * np.float32(2.0)).astype(np.int32)
+    code = np.where(v >= np.float32(1.0), code_n, code_s)
+    return (code | np.where(np.signbit(a) & (code > 0), 8, 0)).astype(np.uint8)
+
+
+def quantize_blocks_mxfp4(v: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP4 quantization of a float32 matrix [..., rows, cols] (cols a multiple of 32):
+    (packed codes [..., rows, cols / 2], E8M0 scale bytes [..., rows, cols / 32])."""
+    v = np.asarray(v, dtype=np.float32)
+    blocks = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
+    amax = np.max(np.abs(blocks), axis=-1)
+    _, ex = np.frexp(amax)  # amax = m * 2^ex with m in [0.5, 1): floor(log2(amax)) = ex - 1
+    e = np.clip(ex.astype(np.int32) - 1 - 2, -127, 127)
+    e = np.where(amax > 0, e, 0)
+    scale_b = (e + 127).astype(np.uint8)
+    x = np.ldexp(blocks, -e[..., None]).astype(np.float32)  # exact: a power-of-two scale
+    codes = f32_to_e2m1_codes(x).reshape(v.shape)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, scale_b
+
+
 def _draw(rng, shape, scale, dtype):
     v = rng.standard_normal(shape, dtype=np.float32)
     if scale != 1.0:
         v *= np.float32(scale)
-    if dtype == "fp8":  # activations and the router stay bf16 in fp8 workloads
+    if dtype in ("fp8", "mxfp4"):  # activations and the router stay bf16 in these workloads
         dtype = "bf16"
     return f32_to_bf16_bits(v) if dtype == "bf16" else v
 
 
 def _draw_w(rng, shape, scale, dtype):
-    """An expert weight block: as _draw, or (codes, per-row scales) for fp8."""
+    """An expert weight block: as _draw, or (codes, per-row scales) for fp8, or (packed codes,
+    block scale bytes) for mxfp4."""
+    if dtype == "mxfp4":
+        return quantize_blocks_mxfp4(_draw(rng, shape, scale, "f32"))
     if dtype != "fp8":
         return _draw(rng, shape, scale, dtype), None
     return quantize_rows_e4m3(_draw(rng, shape, scale, "f32"))
@@ -146,13 +199,17 @@ def make_layer(w: Workload, tokens: int | None = None, seed: int | None = None) 
         layer["router_bias"] = b
     else:
         layer["router_bias"] = None
-    fp8 = w.dtype == "fp8"
+    mx = w.dtype == "mxfp4"
+    fp8 = w.dtype == "fp8" or mx  # scaled one-byte storage
     if fp8:
         st = np.uint8
-    gate_up = np.empty((E, 2 * I, H), dtype=st)
-    down = np.empty((E, H, I), dtype=st)
-    gu_s = np.empty((E, 2 * I), dtype=np.float32) if fp8 else None
-    dn_s = np.empty((E, H), dtype=np.float32) if fp8 else None
+    pk = 2 if mx else 1  # elements per stored byte
+    gate_up = np.empty((E, 2 * I, H // pk), dtype=st)
+    down = np.empty((E, H, I // pk), dtype=st)
+    gu_s = (np.empty((E, 2 * I, H // 32), np.uint8) if mx else
+            np.empty((E, 2 * I), np.float32) if fp8 else None)
+    dn_s = (np.empty((E, H, I // 32), np.uint8) if mx else
+            np.empty((E, H), np.float32) if fp8 else None)
     for e in range(E):
         gate_up[e, :I], sg = _draw_w(rng, (I, H), H ** -0.5, w.dtype)
         gate_up[e, I:], su = _draw_w(rng, (I, H), H ** -0.5, w.dtype)
@@ -164,7 +221,7 @@ def make_layer(w: Workload, tokens: int | None = None, seed: int | None = None) 
     layer["gate_up_scale"] = gu_s
     layer["down_scale"] = dn_s
     if Is > 0:
-        sgu = np.empty((2 * Is, H), dtype=st)
+        sgu = np.empty((2 * Is, H // pk), dtype=st)
         sgu[:Is], sg = _draw_w(rng, (Is, H), H ** -0.5, w.dtype)
         sgu[Is:], su = _draw_w(rng, (Is, H), H ** -0.5, w.dtype)
         layer["shared_gate_up"] = sgu

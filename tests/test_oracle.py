@@ -348,11 +348,109 @@ def pin_fp8_forward_equals_bf16(orc):
     assert np.abs(y8 - y16).max() <= 1e-12 * max(1.0, np.abs(y16).max())
 
 
+# FP4 E2M1 magnitudes of codes 0..7 as the Open Compute Project's Microscaling (MX) formats
+# specification lists them for its FP4 element type (codes 8..15: the same with the sign bit set)
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def pin_e2m1_values(orc):
+    """Every FP4 E2M1 code against the MX specification's table: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+    their negatives (code 8 is negative zero); no infinities or NaN."""
+    for c in range(16):
+        v = orc.e2m1_value(c)
+        want = E2M1_TABLE[c & 7] * (-1.0 if c & 8 else 1.0)
+        assert v == want and math.copysign(1.0, v) == (-1.0 if c & 8 else 1.0), (c, v, want)
+
+
+def pin_e8m0_values(orc):
+    """E8M0 scale bytes: an exponent with bias 127 and no mantissa (0x7F is 1, 0x80 is 2, 0x00 the
+    smallest 2^-127, 0xFE the largest 2^127), and 0xFF is NaN."""
+    assert orc.e8m0_value(0x7F) == 1.0 and orc.e8m0_value(0x80) == 2.0
+    assert orc.e8m0_value(0x7E) == 0.5 and orc.e8m0_value(0x7C) == 0.125
+    assert orc.e8m0_value(0x00) == math.ldexp(1.0, -127)
+    assert orc.e8m0_value(0xFE) == math.ldexp(1.0, 127)
+    assert math.isnan(orc.e8m0_value(0xFF))
+
+
+def pin_mxfp4_quantizer_nearest(orc):
+    """The MXFP4 input quantizer against brute force on small blocks: each block's scale is
+    2^(floor(log2 max|block|) - 2), and each weight's code is, of all sixteen codes, the one whose
+    value times that scale is nearest to the weight (ties to the even code, beyond 6 saturated);
+    the packing puts the even column in the low nibble."""
+    rng = np.random.default_rng(41)
+    v = (rng.standard_normal((6, 64)) * 2.0 ** rng.integers(-8, 3, size=(6, 1))).astype(np.float32)
+    v[1, :32] = 0.0  # an all-zero block
+    v[2, 5] = 0.0  # a zero inside a block
+    # exact midpoints between neighbouring magnitudes (times the block's scale)
+    sc3 = 2.0 ** (math.frexp(float(np.abs(v[3, :32]).max()))[1] - 1 - 2)
+    v[3, 1:8] = (np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]) * sc3).astype(np.float32)
+    packed, sb = inputs.quantize_blocks_mxfp4(v)
+    assert packed.shape == (6, 32) and sb.shape == (6, 2)
+    codes = np.stack([packed & 15, packed >> 4], axis=-1).reshape(6, 64)
+    for r in range(6):
+        for blk in range(2):
+            seg = v[r, 32 * blk:32 * blk + 32].astype(np.float64)
+            amax = np.abs(seg).max()
+            want_b = 127 if amax == 0 else math.frexp(amax)[1] - 1 - 2 + 127
+            assert sb[r, blk] == want_b, (r, blk, sb[r, blk], want_b)
+            scale = orc.e8m0_value(int(sb[r, blk]))
+            vals = [orc.e2m1_value(c) * scale for c in range(16)]
+            for i, x in enumerate(seg):
+                d = [abs(x - q) for q in vals]
+                best = min(d)
+                cands = [c for c in range(16) if d[c] == best]
+                mags = sorted(set(c & 7 for c in cands))
+                # the even magnitude code on a tie; zero is code 0
+                m = mags[0] if len(mags) == 1 else [c for c in mags if c % 2 == 0][0]
+                want = 0 if m == 0 else (m | (8 if x < 0 else 0))
+                assert codes[r, 32 * blk + i] == want, (r, blk, i, x, codes[r, 32 * blk + i], want)
+
+
+def pin_mxfp4_forward_equals_bf16(orc):
+    """MXFP4 weights are bf16 values (E2M1 has one mantissa bit, E8M0 is a power of two), so the
+    oracle's MXFP4 forward must equal its bf16 forward on the same values. The codes and scale
+    bytes are encoded here from the specification's table, independently of the oracle, with a
+    different scale on every block of every gate, up and down row."""
+    rng = np.random.default_rng(43)
+    T, H, E, I, Is = 3, 64, 8, 32, 64
+    lay16 = {"num_experts": E, "inter": I, "shared_inter": Is, "top_k": 8, "dtype": "bf16"}
+    lay4 = dict(lay16, dtype="mxfp4")
+    table = np.array(E2M1_TABLE + [-t for t in E2M1_TABLE])
+
+    def block(rows, cols):
+        codes = rng.integers(0, 16, size=(rows, cols)).astype(np.uint8)
+        sbytes = rng.integers(127 - 12, 127 - 2, size=(rows, cols // 32)).astype(np.uint8)
+        vals = table[codes] * np.ldexp(1.0, sbytes.astype(np.int64) - 127).repeat(32, axis=1)
+        bits = inputs.f32_to_bf16_bits(vals.astype(np.float32))
+        assert np.array_equal(inputs.bf16_bits_to_f32(bits).astype(np.float64), vals)
+        packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+        return packed, sbytes, bits
+
+    gu4, gus, gu16 = zip(*[block(2 * I, H) for _ in range(E)])
+    dn4, dns, dn16 = zip(*[block(H, I) for _ in range(E)])
+    sgu4, sgus, sgu16 = block(2 * Is, H)
+    sdn4, sdns, sdn16 = block(H, Is)
+    x = inputs.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    lay16.update(x=x, gate_up=np.stack(gu16), down=np.stack(dn16), shared_gate_up=sgu16,
+                 shared_down=sdn16)
+    lay4.update(x=x, gate_up=np.stack(gu4), down=np.stack(dn4), shared_gate_up=sgu4,
+                shared_down=sdn4, gate_up_scale=np.stack(gus), down_scale=np.stack(dns),
+                shared_gate_up_scale=sgus, shared_down_scale=sdns)
+    ids = np.stack([rng.permutation(E) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, E))
+    w /= w.sum(1, keepdims=True)
+    g = rng.random(T)
+    y16 = orc.forward(lay16, ids, w, g)
+    y4 = orc.forward(lay4, ids, w, g)
+    assert np.abs(y4 - y16).max() <= 1e-12 * max(1.0, np.abs(y16).max())
+
+
 PINS = [pin_select_vs_library_sort, pin_select_special_cases, pin_weights_closed_form, pin_gate,
         pin_logits_integer_exact, pin_logits_random_vs_matmul, pin_bucket_vs_argsort,
         pin_ffn_dense_equivalence, pin_ffn_shared_alone_and_zero, pin_ffn_routed_mixture,
         pin_golden_hand_example, pin_e4m3_values, pin_e4m3_quantizer_round_trip,
-        pin_fp8_forward_equals_bf16]
+        pin_fp8_forward_equals_bf16, pin_e2m1_values, pin_e8m0_values,
+        pin_mxfp4_quantizer_nearest, pin_mxfp4_forward_equals_bf16]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -383,7 +481,10 @@ PLANTS = {
     "ORACLE_PLANT_SWAP_GATE_UP": [pin_ffn_dense_equivalence, pin_ffn_routed_mixture],
     "ORACLE_PLANT_DROP_BIAS": [pin_logits_integer_exact, pin_logits_random_vs_matmul],
     "ORACLE_PLANT_E4M3_BIAS8": [pin_e4m3_values, pin_e4m3_quantizer_round_trip],
-    "ORACLE_PLANT_UP_SCALE_ROW": [pin_fp8_forward_equals_bf16],
+    "ORACLE_PLANT_UP_SCALE_ROW": [pin_fp8_forward_equals_bf16, pin_mxfp4_forward_equals_bf16],
+    "ORACLE_PLANT_E8M0_BIAS128": [pin_e8m0_values, pin_mxfp4_forward_equals_bf16],
+    "ORACLE_PLANT_FP4_HIGH_FIRST": [pin_mxfp4_forward_equals_bf16],
+    "ORACLE_PLANT_E2M1_BIAS2": [pin_e2m1_values, pin_mxfp4_forward_equals_bf16],
 }
 
 
