@@ -63,7 +63,16 @@ def make_sets(w, n_sets, torch):
                     * scale).to(dt)
 
         def draw_w(shape, scale):
-            """An expert weight block; fp8: per-row E4M3 codes (uint8) and fp32 row scales."""
+            """An expert weight block; fp8: per-row E4M3 codes (uint8) and fp32 row scales;
+            mxfp4: random packed E2M1 codes with E8M0 scale bytes near what the input quantizer
+            gives for these scales (amax of 32 normal draws ~2.5 sigma, over 6: 2^-7 .. 2^-5)."""
+            if w.dtype == "mxfp4":
+                rows, cols = shape[:-1], shape[-1]
+                codes = torch.randint(0, 256, (*rows, cols // 2), generator=gen, device="cuda",
+                                      dtype=torch.uint8)
+                sb = torch.randint(118, 123, (*rows, cols // 32), generator=gen, device="cuda",
+                                   dtype=torch.uint8)
+                return codes, sb
             if w.dtype != "fp8":
                 return draw(shape, scale), None
             v = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * scale
@@ -92,6 +101,8 @@ def sizes(w):
     """(activation bytes, expert weight bytes, row-scale bytes) per element / row."""
     if w.dtype == "fp8":
         return 2, 1, 4
+    if w.dtype == "mxfp4":  # half a byte of code plus a scale byte per 32 weights
+        return 2, 0.5 + 1 / 32, 0
     esz = 2 if w.dtype == "bf16" else 4
     return esz, esz, 0
 
@@ -170,7 +181,8 @@ def cpu_baseline(w, m_t, seconds):
             return a.view(torch.int16).cpu().numpy().view(np.uint16)
         return a.cpu().numpy()
 
-    layer = {"num_experts": w.num_experts, "inter": w.inter, "shared_inter": w.shared_inter}
+    layer = {"num_experts": w.num_experts, "inter": w.inter, "shared_inter": w.shared_inter,
+             "dtype": w.dtype}
     for k in ("router_w", "router_bias", "gate_up", "down", "shared_gate_up", "shared_down",
               "gate_up_scale", "down_scale", "shared_gate_up_scale", "shared_down_scale"):
         layer[k] = host(t.get(k))

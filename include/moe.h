@@ -60,26 +60,37 @@ typedef enum {
 typedef enum {
     MOE_F32 = 0,      /* x and every weight stored as fp32 */
     MOE_BF16 = 1,     /* x and every weight stored as bf16 (raw 16-bit patterns) */
-    MOE_FP8_E4M3 = 2  /* x and router_w bf16; the routed and shared expert weights stored as
+    MOE_FP8_E4M3 = 2, /* x and router_w bf16; the routed and shared expert weights stored as
                          OCP FP8 E4M3 codes (one byte each) with one fp32 scale per weight row:
                          weight = value(code) * scale[row]. The quantized expert formats the
                          pages name (groupwise integers, FP8, NVFP4) are not fixed by them; this
                          is the per-row-scaled FP8 reading (see the scale fields below). */
+    MOE_MXFP4 = 3     /* x and router_w bf16; the expert weights in the Open Compute Project's
+                         MXFP4 (Microscaling formats specification): FP4 E2M1 codes packed two
+                         per byte along each row (the even column in the low nibble, so a row of
+                         n weights is n/2 bytes) and one E8M0 scale byte per 32 consecutive
+                         weights of a row: weight = value(code) * 2^(scale byte - 127), byte 0xFF
+                         NaN. Exact while every product lies in bf16's finite range (scale bytes
+                         up to 252 always do); a product beyond it becomes +-inf. The group-scaled
+                         4-bit reading of the pages' quantized expert formats. */
 } moe_dtype;
 
 typedef struct {
-    int32_t hidden;       /* H: 64..16384, a multiple of 64 (fp32) or of 128 (bf16, FP8) */
+    int32_t hidden;       /* H: 64..16384, a multiple of 64 (fp32), of 128 (bf16, FP8) or of
+                             256 (MXFP4) */
     int32_t num_experts;  /* E: 8..256 */
     int32_t top_k;        /* must be 8 */
     int32_t inter;        /* I: expert intermediate size, 16..4096, a multiple of 16 (fp32), of
-                             32 (bf16) or of 128 (FP8) */
+                             32 (bf16), of 128 (FP8) or of 256 (MXFP4) */
     int32_t shared_inter; /* I_s: 0 (no shared expert) or as I */
     int32_t max_tokens;   /* largest T any call on this context may pass, 1..65536 */
     int32_t dtype;        /* moe_dtype */
 } moe_config;
 
 /* Weight buffers, all row-major, element type = config.dtype (for MOE_FP8_E4M3: router_w bf16,
- * the four expert matrices FP8 E4M3 codes). R = E + (I_s > 0 ? 1 : 0). */
+ * the four expert matrices FP8 E4M3 codes; for MOE_MXFP4: router_w bf16, the four expert
+ * matrices packed E2M1 codes, so their last dimension is halved in bytes: [E][2I][H/2],
+ * [E][H][I/2], [2 I_s][H/2], [H][I_s/2]). R = E + (I_s > 0 ? 1 : 0). */
 typedef struct {
     const void *router_w;       /* [R][H]; row E is the shared-expert gate row when I_s > 0 */
     const float *router_bias;   /* [R] fp32, added to the logits, or NULL */
@@ -87,13 +98,15 @@ typedef struct {
     const void *down;           /* [E][H][I] */
     const void *shared_gate_up; /* [2 I_s][H] (gate rows first); NULL iff I_s == 0 */
     const void *shared_down;    /* [H][I_s]; NULL iff I_s == 0 */
-    /* MOE_FP8_E4M3 only (NULL otherwise), fp32, one scale per row of the matrix above:
-     * gate_up_scale [E][2I], down_scale [E][H], shared_gate_up_scale [2 I_s] and
-     * shared_down_scale [H] (the last two NULL iff I_s == 0). 16-byte aligned. */
-    const float *gate_up_scale;
-    const float *down_scale;
-    const float *shared_gate_up_scale;
-    const float *shared_down_scale;
+    /* Scales of the quantized formats (NULL for MOE_F32 and MOE_BF16; the shared ones NULL iff
+     * I_s == 0). MOE_FP8_E4M3: fp32, one per row of the matrix above, 16-byte aligned:
+     * gate_up_scale [E][2I], down_scale [E][H], shared_gate_up_scale [2 I_s],
+     * shared_down_scale [H]. MOE_MXFP4: E8M0 bytes, one per 32 weights of a row, any
+     * alignment: [E][2I][H/32], [E][H][I/32], [2 I_s][H/32], [H][I_s/32]. */
+    const void *gate_up_scale;
+    const void *down_scale;
+    const void *shared_gate_up_scale;
+    const void *shared_down_scale;
 } moe_weights;
 
 typedef struct moe_ctx moe_ctx;

@@ -21,7 +21,8 @@ MOE_ERR_HIP = -4
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_FP8_E4M3 = 2  # bf16 x and router; FP8 E4M3 expert weights with fp32 per-row scales
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+MOE_MXFP4 = 3  # bf16 x and router; MXFP4 expert weights (packed E2M1 codes, E8M0 bytes per 32)
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4}
 WEIGHT_KEYS = ("router_w", "router_bias", "gate_up", "down", "shared_gate_up", "shared_down",
                "gate_up_scale", "down_scale", "shared_gate_up_scale", "shared_down_scale")
 
@@ -109,7 +110,9 @@ class MoeLayer:
     weights: dict with router_w [R][H], router_bias [R] fp32 or None, gate_up [E][2I][H],
     down [E][H][I], shared_gate_up [2Is][H] or None, shared_down [H][Is] or None, and for "fp8"
     the row scales gate_up_scale [E][2I], down_scale [E][H], shared_gate_up_scale [2Is] and
-    shared_down_scale [H] (fp32) next to uint8 FP8 E4M3 codes; bf16 weights
+    shared_down_scale [H] (fp32) next to uint8 FP8 E4M3 codes, for "mxfp4" packed E2M1 codes
+    ([E][2I][H/2] ...) with E8M0 scale bytes gate_up_scale [E][2I][H/32], down_scale
+    [E][H][I/32], shared_gate_up_scale [2Is][H/32], shared_down_scale [H][Is/32]; bf16 weights
     may be torch.bfloat16 or 16-bit integer tensors holding the bf16 bits.
     """
 

@@ -94,6 +94,38 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
                  e4m3x2_to_bf16x2<false>(hi), e4m3x2_to_bf16x2<true>(hi)};
 }
 
+// MXFP4 (the Open Compute Project's Microscaling FP4): E2M1 codes two per byte (the even weight
+// in the low nibble) and one E8M0 scale byte per 32 consecutive weights. The scale byte as the
+// fp32 2^(b - 127) (b = 0: the subnormal 2^-127; b = 255: NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+    return __uint_as_float(b == 0 ? 0x00400000u : b == 255 ? 0x7FC00000u : b << 23);
+}
+
+// The two codes of byte kByte of w times s as two bf16 (low half: the low nibble). gfx950
+// converts and scales in one instruction, exactly while the product is a finite bf16.
+template <int kByte>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w, float s) {
+    const bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, kByte);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight codes (one 32-bit word, weights 8j .. 8j + 7 of a scale block) as one bf16 operand piece.
+__device__ __forceinline__ uint4 e2m1x8_to_bf16x8(uint32_t w, float s) {
+    return uint4{e2m1x2_to_bf16x2<0>(w, s), e2m1x2_to_bf16x2<1>(w, s),
+                 e2m1x2_to_bf16x2<2>(w, s), e2m1x2_to_bf16x2<3>(w, s)};
+}
+
+// Wait states between the matrix instructions of one chunk and the FP4 conversions of the next:
+// a matrix instruction still reads its A/B registers for several cycles after it issues, and the
+// scaled FP4 conversions may be allocated those registers; without this gap the last matrix
+// steps before a conversion block read the new values (measured on gfx950: exactly those steps'
+// products were wrong). The scheduling barriers keep every instruction on its side.
+__device__ __forceinline__ void mfma_operand_guard() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <class Op, bool kFp8>

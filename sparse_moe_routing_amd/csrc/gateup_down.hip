@@ -42,7 +42,12 @@ __device__ __forceinline__ uint4 lds_load16(const void *p) {
 // the operand reads - lane (row i, k-group q) takes piece 4s + q of row i for step s - hit 16
 // distinct bank groups. The up waves hand their 16x16 tiles to the gate waves through LDS, which
 // write h = silu(gate) * up.
-template <class Op, bool kFp8>
+// MXFP4 weights (kMx): a ring slot is a pair of chunks, 16 rows x 128 bytes of packed codes read
+// as 8 rows x 128 bytes per instruction like FP8; each lane's 16 bytes are one scale block of 32
+// weights, widened with its E8M0 scale into four bf16 pieces of one of the two chunks. The two
+// chunks go to the wave's two LDS buffers and feed the matrix instructions in chunk order, so
+// every accumulator sees the k order of the other formats.
+template <class Op, bool kFp8, bool kMx = false>
 __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
     using elem_t = typename Op::elem_t;
     using WF = WeightFmt<Op, kFp8>;
@@ -53,7 +58,9 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
     constexpr int kStepsPerChunk = kPieces / 4;       // 4 k-groups of one piece per step
     // chunks per load batch (two batches in flight); FP8 codes are half the bytes, so twice the
     // chunks fill the same registers
-    constexpr int kDepth = kFp8 ? 4 : 2;
+    // (MXFP4: chunk pairs per batch, a quarter of the bf16 bytes per chunk)
+    constexpr int kDepth = kFp8 || kMx ? 4 : 2;
+    constexpr bool k8 = kFp8 || kMx;                  // one-byte storage: 8 rows x 128 B loads
     constexpr int kStageBufs = 2;                     // LDS chunk buffers per wave
     constexpr int kStage = kTile * kPieces * 16;      // 4 KB of LDS per chunk per wave
 
@@ -69,12 +76,14 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
     const int nunits = p.num_groups[0] * p.S;
     const int chunks_per_row = p.H / Op::kPerLane;
     const int nchunks = p.H / kChunkElems;
+    const int nslots = kMx ? nchunks / 2 : nchunks;  // ring slots along K (H % 256 == 0 for MXFP4)
     const elem_t *x = reinterpret_cast<const elem_t *>(p.x);
     // loader lane -> (row, piece) of a chunk: 4 instructions of 4 rows x 256 contiguous bytes;
     // FP8 codes (128 bytes per row and chunk): 2 instructions of 8 rows x 128 bytes, 16 codes a lane
     const int lrow = lane >> 4, lpiece = lane & 15;
     const int lrow8 = lane >> 3, lpiece8 = lane & 7;
-    constexpr int kLoads = kFp8 ? 2 : 4;  // load instructions per chunk
+    constexpr int kLoads = k8 ? 2 : 4;  // load instructions per ring slot
+    const int mx_row = p.H / 2, mx_srow = p.H / 32;  // MXFP4 bytes per row: codes, scales
 
     for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
         const int gi = u / p.S, j = u - (u / p.S) * p.S;
@@ -89,29 +98,71 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
         const int wrow0 = (wave < 2 ? 0 : Ie) + j * kSW + (wave & 1) * kTile;  // first weight row
         const wt_t *src = kFp8 ? gu + (size_t)(wrow0 + lrow8) * p.H + lpiece8 * 16
                                : gu + (size_t)(wrow0 + lrow) * p.H + lpiece * Op::kPerLane;
+        // MXFP4: the lane's codes (16 bytes of a 128-byte pair of chunks) and their scale byte
+        const unsigned char *msrc =
+            reinterpret_cast<const unsigned char *>(shared ? p.sgu : p.gate_up) +
+            (shared ? 0 : (size_t)e * 2 * Ie * mx_row) + (size_t)(wrow0 + lrow8) * mx_row + lpiece8 * 16;
+        const uint8_t *ssrc = kMx ? (shared ? p.sgu_mx : p.gu_mx + (size_t)e * 2 * Ie * mx_srow) +
+                                        (size_t)(wrow0 + lrow8) * mx_srow + lpiece8
+                                  : nullptr;
         const bool col_ok = col < n;
         const int crow = col_ok ? col : 0;  // columns >= n repeat column 0 (dropped)
         const elem_t *xrow = xs + crow * p.x_stride + q * Op::kPerLane;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 
-        using raw_t = typename std::conditional<kFp8, uint4, typename WF::raw_t>::type;
+        using raw_t = typename std::conditional<k8, uint4, typename WF::raw_t>::type;
         raw_t rA[kDepth][kLoads], rB[kDepth][kLoads];
-        auto load = [&](raw_t(&r)[kDepth][kLoads], int c0) {
+        uint32_t sA[kDepth][kLoads], sB[kDepth][kLoads];  // MXFP4 scale bytes (else unused)
+        auto load = [&](raw_t(&r)[kDepth][kLoads], uint32_t(&sc)[kDepth][kLoads], int c0) {
 #pragma unroll
             for (int d = 0; d < kDepth; ++d)
 #pragma unroll
                 for (int a = 0; a < kLoads; ++a) {
-                    const int c = min(c0 + d, nchunks - 1);  // past the end: re-read, unused
-                    if constexpr (kFp8)
+                    const int c = min(c0 + d, nslots - 1);  // past the end: re-read, unused
+                    if constexpr (kMx) {
+                        r[d][a] = load16_stream(msrc + (size_t)(8 * a) * mx_row + c * 128);
+                        sc[d][a] = ssrc[(size_t)(8 * a) * mx_srow + c * 8];
+                    } else if constexpr (kFp8) {
                         r[d][a] = load16_stream(src + (size_t)(8 * a) * p.H + c * kChunkElems);
-                    else
+                    } else {
                         r[d][a] = WF::load_raw(src + (size_t)(4 * a) * p.H + c * kChunkElems);
+                    }
                 }
         };
-        auto consume = [&](const raw_t(&r)[kDepth][kLoads], int c0) {
+        auto mma_chunk = [&](const unsigned char *buf, int c) {
+#pragma unroll
+            for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
+                const int pc = 4 * s2 + q;
+                const uint4 av = lds_load16(buf + col * 256 + ((pc ^ col) & 15) * 16);
+                const uint4 xb = lds_load16(xrow + c * kChunkElems + 4 * s2 * Op::kPerLane);
+                Op::mma(acc, av, xb);
+            }
+        };
+        auto consume = [&](const raw_t(&r)[kDepth][kLoads], const uint32_t(&sc)[kDepth][kLoads],
+                           int c0) {
 #pragma unroll
             for (int d = 0; d < kDepth; ++d) {
-                if (c0 + d >= nchunks) break;  // uniform
+                if (c0 + d >= nslots) break;  // uniform
+                if constexpr (kMx) {
+                    // lanes 0-3 of a row hold chunk 2(c0 + d), lanes 4-7 the next one; each lane's
+                    // 32 weights are four consecutive pieces of its chunk
+                    unsigned char *buf = stage + (lpiece8 >> 2) * kStage;
+                    const int pb = 4 * (lpiece8 & 3);
+                    mfma_operand_guard();
+#pragma unroll
+                    for (int a = 0; a < kLoads; ++a) {
+                        const int rr = 8 * a + lrow8;
+                        const float sf = e8m0_to_f32(sc[d][a]);
+                        const uint32_t w4[4] = {r[d][a].x, r[d][a].y, r[d][a].z, r[d][a].w};
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            *reinterpret_cast<uint4 *>(buf + rr * 256 + (((pb + k) ^ rr) & 15) * 16) =
+                                e2m1x8_to_bf16x8(w4[k], sf);
+                    }
+                    mma_chunk(stage, 2 * (c0 + d));  // a wave's LDS ops stay in order
+                    mma_chunk(stage + kStage, 2 * (c0 + d) + 1);
+                    continue;
+                }
                 unsigned char *buf = stage + (d % kStageBufs) * kStage;  // a wave's LDS ops stay in order
 #pragma unroll
                 for (int a = 0; a < kLoads; ++a) {
@@ -128,18 +179,12 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
                             WF::to_operand(r[d][a]);
                     }
                 }
-#pragma unroll
-                for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
-                    const int pc = 4 * s2 + q;
-                    const uint4 av = lds_load16(buf + col * 256 + ((pc ^ col) & 15) * 16);
-                    const uint4 xb = lds_load16(xrow + (c0 + d) * kChunkElems + 4 * s2 * Op::kPerLane);
-                    Op::mma(acc, av, xb);
-                }
+                mma_chunk(buf, c0 + d);
             }
         };
         // the weight stream does not depend on x: both buffers are requested before staging x
-        load(rA, 0);
-        if (kDepth < nchunks) load(rB, kDepth);
+        load(rA, sA, 0);
+        if (kDepth < nslots) load(rB, sB, kDepth);
         __syncthreads();  // the previous unit's readers of xs / xchg are done
         for (int idx = tid; idx < n * chunks_per_row; idx += kThreads) {
             const int row = idx / chunks_per_row;
@@ -150,12 +195,12 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
         }
         __syncthreads();
 
-        for (int c0 = 0; c0 < nchunks; c0 += 2 * kDepth) {
-            consume(rA, c0);
-            if (c0 + 2 * kDepth < nchunks) load(rA, c0 + 2 * kDepth);
-            if (c0 + kDepth < nchunks) {
-                consume(rB, c0 + kDepth);
-                if (c0 + 3 * kDepth < nchunks) load(rB, c0 + 3 * kDepth);
+        for (int c0 = 0; c0 < nslots; c0 += 2 * kDepth) {
+            consume(rA, sA, c0);
+            if (c0 + 2 * kDepth < nslots) load(rA, sA, c0 + 2 * kDepth);
+            if (c0 + kDepth < nslots) {
+                consume(rB, sB, c0 + kDepth);
+                if (c0 + 3 * kDepth < nslots) load(rB, sB, c0 + 3 * kDepth);
             }
         }
 
@@ -228,7 +273,10 @@ __device__ void combine_rows(const DownParams &p, int h0, int tid) {
 // slot of each of the group's (token, rank) pairs. Weight rows stream as in gateup_kernel: each
 // load instruction reads 256 contiguous bytes of each of 4 rows, and a per-wave LDS buffer with
 // the same XOR swizzle turns 16 x 256-byte chunks into matrix-core operands.
-template <class Op, bool kFp8>
+// MXFP4 weights (kMx): ring slots are chunk pairs as in gateup_kernel; the wave's one LDS buffer
+// takes the pair's first chunk (written by the lanes that hold it), feeds its matrix
+// instructions, then takes the second.
+template <class Op, bool kFp8, bool kMx = false>
 __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
     using WF = WeightFmt<Op, kFp8>;
     using wt_t = typename WF::wt_t;
@@ -269,27 +317,42 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
         const bool shared = e == p.E;
         const int Ie = shared ? p.Is : p.I;
         const int nchunks = Ie / kChunkElems;
+        const int nslots = kMx ? nchunks / 2 : nchunks;  // ring slots (MXFP4: chunk pairs)
         const wt_t *dn = reinterpret_cast<const wt_t *>(shared ? p.sdn : p.down) +
                          (shared ? 0 : (size_t)e * p.H * Ie);
         // FP8 codes: 2 loads of 8 rows x 128 bytes per chunk (16 codes a lane) in place of 4 of
-        // 4 rows x 128 bytes
+        // 4 rows x 128 bytes; MXFP4: the same shape per chunk pair
         const int lrow8 = lane >> 3, lpiece8 = lane & 7;
-        constexpr int kLoads = kFp8 ? 2 : 4;
+        constexpr bool k8 = kFp8 || kMx;
+        constexpr int kLoads = k8 ? 2 : 4;
+        const int wr0 = rc * kRowsPerUnit + wave * kTile;  // the wave's first weight row
         const wt_t *src =
-            kFp8 ? dn + (size_t)(rc * kRowsPerUnit + wave * kTile + lrow8) * Ie + lpiece8 * 16
-                 : dn + (size_t)(rc * kRowsPerUnit + wave * kTile + lrow) * Ie + lpiece * Op::kPerLane;
-        using raw_t = typename std::conditional<kFp8, uint4, typename WF::raw_t>::type;
+            kFp8 ? dn + (size_t)(wr0 + lrow8) * Ie + lpiece8 * 16
+                 : dn + (size_t)(wr0 + lrow) * Ie + lpiece * Op::kPerLane;
+        const int mx_row = Ie / 2, mx_srow = Ie / 32;  // MXFP4 bytes per row: codes, scales
+        const unsigned char *msrc = reinterpret_cast<const unsigned char *>(shared ? p.sdn : p.down) +
+                                    (shared ? 0 : (size_t)e * p.H * mx_row) +
+                                    (size_t)(wr0 + lrow8) * mx_row + lpiece8 * 16;
+        const uint8_t *ssrc = kMx ? (shared ? p.sdn_mx : p.dn_mx + (size_t)e * p.H * mx_srow) +
+                                        (size_t)(wr0 + lrow8) * mx_srow + lpiece8
+                                  : nullptr;
+        using raw_t = typename std::conditional<k8, uint4, typename WF::raw_t>::type;
         raw_t a[kBatch][kLoads];
+        uint32_t sc[kBatch][kLoads];  // MXFP4 scale bytes (else unused)
         auto load = [&](int c0) {
 #pragma unroll
             for (int d = 0; d < kBatch; ++d)
 #pragma unroll
                 for (int r = 0; r < kLoads; ++r) {
-                    const int c = min(c0 + d, nchunks - 1);  // past the end: re-read, unused
-                    if constexpr (kFp8)
+                    const int c = min(c0 + d, nslots - 1);  // past the end: re-read, unused
+                    if constexpr (kMx) {
+                        a[d][r] = load16_stream(msrc + (size_t)(8 * r) * mx_row + c * 128);
+                        sc[d][r] = ssrc[(size_t)(8 * r) * mx_srow + c * 8];
+                    } else if constexpr (kFp8) {
                         a[d][r] = load16_stream(src + (size_t)(8 * r) * Ie + c * kChunkElems);
-                    else
+                    } else {
                         a[d][r] = WF::load_raw(src + (size_t)(4 * r) * Ie + c * kChunkElems);
+                    }
                 }
         };
         load(0);  // the weight stream does not depend on h: start it before staging h
@@ -312,11 +375,43 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
         const h_t *bhp = hs_hi + crow * hstride + q * Op::kPerLane;
         const h_t *blp = hs_lo + crow * hstride + q * Op::kPerLane;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+        auto mma_chunk = [&](int c) {
+#pragma unroll
+            for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
+                const int pc = 4 * s2 + q;
+                const uint4 av = lds_load16(stage + col * 256 + ((pc ^ col) & 15) * 16);
+                const int kk = c * kChunkElems + 4 * s2 * Op::kPerLane;
+                Op::mma(acc, av, lds_load16(bhp + kk));
+                if constexpr (Op::kElemBytes == 2) Op::mma(acc, av, lds_load16(blp + kk));
+            }
+        };
+        for (int c0 = 0; c0 < nslots; c0 += kBatch) {
             if (c0 > 0) load(c0);
 #pragma unroll
             for (int d = 0; d < kBatch; ++d) {
-                if (c0 + d >= nchunks) break;  // uniform
+                if (c0 + d >= nslots) break;  // uniform
+                if constexpr (kMx) {
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        mfma_operand_guard();
+                        if ((lpiece8 >> 2) == half) {  // this lane's 32 weights are in chunk half
+                            const int pb = 4 * (lpiece8 & 3);
+#pragma unroll
+                            for (int r = 0; r < kLoads; ++r) {
+                                const int rr = 8 * r + lrow8;
+                                const float sf = e8m0_to_f32(sc[d][r]);
+                                const uint32_t w4[4] = {a[d][r].x, a[d][r].y, a[d][r].z, a[d][r].w};
+#pragma unroll
+                                for (int k = 0; k < 4; ++k)
+                                    *reinterpret_cast<uint4 *>(stage + rr * 256 +
+                                                               (((pb + k) ^ rr) & 15) * 16) =
+                                        e2m1x8_to_bf16x8(w4[k], sf);
+                            }
+                        }
+                        mma_chunk(2 * (c0 + d) + half);  // a wave's LDS ops stay in order
+                    }
+                    continue;
+                }
 #pragma unroll
                 for (int r = 0; r < kLoads; ++r) {
                     if constexpr (kFp8) {  // 16 codes widened to two bf16 pieces (exact)
@@ -332,14 +427,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
                             WF::to_operand(a[d][r]);
                     }
                 }
-#pragma unroll
-                for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
-                    const int pc = 4 * s2 + q;
-                    const uint4 av = lds_load16(stage + col * 256 + ((pc ^ col) & 15) * 16);
-                    const int kk = (c0 + d) * kChunkElems + 4 * s2 * Op::kPerLane;
-                    Op::mma(acc, av, lds_load16(bhp + kk));
-                    if constexpr (Op::kElemBytes == 2) Op::mma(acc, av, lds_load16(blp + kk));
-                }
+                mma_chunk(c0 + d);
             }
         }
         if constexpr (WF::kScaled)  // the output rows' dequantization scales
@@ -390,10 +478,12 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
 hipError_t prepare_split_kernels(size_t gateup_lds, size_t down_lds) {
     const void *gk[] = {reinterpret_cast<const void *>(&gateup_kernel<OpBF16, false>),
                         reinterpret_cast<const void *>(&gateup_kernel<OpF32, false>),
-                        reinterpret_cast<const void *>(&gateup_kernel<OpBF16, true>)};
+                        reinterpret_cast<const void *>(&gateup_kernel<OpBF16, true>),
+                        reinterpret_cast<const void *>(&gateup_kernel<OpBF16, false, true>)};
     const void *dk[] = {reinterpret_cast<const void *>(&down_kernel<OpBF16, false>),
                         reinterpret_cast<const void *>(&down_kernel<OpF32, false>),
-                        reinterpret_cast<const void *>(&down_kernel<OpBF16, true>)};
+                        reinterpret_cast<const void *>(&down_kernel<OpBF16, true>),
+                        reinterpret_cast<const void *>(&down_kernel<OpBF16, false, true>)};
     hipError_t err;
     for (const void *k : gk)
         if ((err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -408,7 +498,8 @@ hipError_t prepare_split_kernels(size_t gateup_lds, size_t down_lds) {
 
 // dtype: 0 fp32, 1 bf16, 2 bf16 activations with FP8 E4M3 weights
 hipError_t launch_gateup(const GateUpParams &p, int dtype, int grid, size_t lds, hipStream_t s) {
-    if (dtype == 2) launch_k(gateup_kernel<OpBF16, true>, grid, kThreads, lds, s, p);
+    if (dtype == 3) launch_k(gateup_kernel<OpBF16, false, true>, grid, kThreads, lds, s, p);
+    else if (dtype == 2) launch_k(gateup_kernel<OpBF16, true>, grid, kThreads, lds, s, p);
     else if (dtype == 1) launch_k(gateup_kernel<OpBF16, false>, grid, kThreads, lds, s, p);
     else launch_k(gateup_kernel<OpF32, false>, grid, kThreads, lds, s, p);
     return hipGetLastError();
@@ -418,7 +509,8 @@ size_t gateup_stage_bytes() { return 4 * 2 * 4096 + 2 * 16 * 16 * 4; }
 size_t down_stage_bytes() { return 4 * 4096; }
 
 hipError_t launch_down(const DownParams &p, int dtype, int grid, size_t lds, hipStream_t s) {
-    if (dtype == 2) launch_k(down_kernel<OpBF16, true>, grid, kThreads, lds, s, p);
+    if (dtype == 3) launch_k(down_kernel<OpBF16, false, true>, grid, kThreads, lds, s, p);
+    else if (dtype == 2) launch_k(down_kernel<OpBF16, true>, grid, kThreads, lds, s, p);
     else if (dtype == 1) launch_k(down_kernel<OpBF16, false>, grid, kThreads, lds, s, p);
     else launch_k(down_kernel<OpF32, false>, grid, kThreads, lds, s, p);
     return hipGetLastError();

@@ -86,6 +86,7 @@ struct GateUpParams {
     int S;               // 32-row slices of Imax (units per group)
     int NG, x_stride;
     const float *gu_scale, *sgu_scale;  // FP8 weights: per-row scales [E][2I], [2Is]; else null
+    const uint8_t *gu_mx, *sgu_mx;      // MXFP4 weights: E8M0 bytes [E][2I][H/32], [2Is][H/32]
 };
 
 struct DownParams {
@@ -102,6 +103,7 @@ struct DownParams {
     int *rb_arrivals;    // [H / 64] zero at entry; left zero
     int T, H, E, I, Is, Imax, NG;
     const float *dn_scale, *sdn_scale;  // FP8 weights: per-row scales [E][H], [H]; else null
+    const uint8_t *dn_mx, *sdn_mx;      // MXFP4 weights: E8M0 bytes [E][H][I/32], [H][Is/32]
 };
 
 struct CombineParams {

@@ -89,7 +89,7 @@ int act_dtype(int dtype) { return dtype == MOE_F32 ? MOE_F32 : MOE_BF16; }
 // Bytes of one activation element.
 int elem_bytes(int dtype) { return act_dtype(dtype) == MOE_BF16 ? 2 : 4; }
 // Kernel variant of the router and routing kernels (0 fp32, 1 bf16) and of the expert kernels
-// (2: bf16 operands with FP8 E4M3 weights).
+// (2: bf16 operands with FP8 E4M3 weights, 3: with MXFP4 weights).
 int route_kdt(const moe_ctx *c);
 int expert_kdt(const moe_ctx *c);
 
@@ -140,7 +140,9 @@ Plan make_plan(const moe_ctx *c, int T) {
     // the split and wide kernels stream weight rows in chunks of 16 x 16 bytes (128 bf16 / 64 fp32)
     const int chunk = act_dtype(cfg.dtype) == MOE_BF16 ? 128 : 64;
     const bool chunk_ok = I % chunk == 0 && Is % chunk == 0;
-    p.wide = T > kSplitMaxTokens && chunk_ok;
+    // MXFP4 weights run the 8-token-group kernels at every T (no 64-token-group variant)
+    const bool mx = cfg.dtype == MOE_MXFP4;
+    p.wide = T > kSplitMaxTokens && chunk_ok && !mx;
     p.NG = p.wide ? wide_group_tokens() : ng_x;
     p.n_chunks = p.small ? 0 : (T + kHistChunk - 1) / kHistChunk;
     const int pairs = T * 8;
@@ -161,7 +163,8 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.gu_S = Imax / 32;
     p.down_lds = (size_t)ng_x * (Imax + 16 / esz) * esz * (esz == 2 ? 2 : 1) +
                  down_stage_bytes();
-    p.split = T <= kSplitMaxTokens && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds && chunk_ok;
+    p.split = (T <= kSplitMaxTokens || mx) && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds &&
+              chunk_ok;
     if (p.wide) {
         const int dr = wide_rows_per_down_unit(), gr = wide_rows_per_gateup_unit();
         const long d_units = (long)p.max_groups * ((H + dr - 1) / dr);
@@ -452,8 +455,11 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         gp.S = p.gu_S;
         gp.NG = p.NG;
         gp.x_stride = p.x_stride;
-        gp.gu_scale = c->w.gate_up_scale;
-        gp.sgu_scale = c->w.shared_gate_up_scale;
+        const bool mx = c->cfg.dtype == MOE_MXFP4;
+        gp.gu_scale = mx ? nullptr : static_cast<const float *>(c->w.gate_up_scale);
+        gp.sgu_scale = mx ? nullptr : static_cast<const float *>(c->w.shared_gate_up_scale);
+        gp.gu_mx = mx ? static_cast<const uint8_t *>(c->w.gate_up_scale) : nullptr;
+        gp.sgu_mx = mx ? static_cast<const uint8_t *>(c->w.shared_gate_up_scale) : nullptr;
         if (p.big)
             L.step("gateup_big", [&] { return launch_gateup_big(gp, expert_kdt(c), p.gu_grid, L.stream); });
         else if (p.wide)
@@ -484,8 +490,10 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         dp.I = c->cfg.inter;
         dp.Is = c->cfg.shared_inter;
         dp.Imax = p.Imax;
-        dp.dn_scale = c->w.down_scale;
-        dp.sdn_scale = c->w.shared_down_scale;
+        dp.dn_scale = mx ? nullptr : static_cast<const float *>(c->w.down_scale);
+        dp.sdn_scale = mx ? nullptr : static_cast<const float *>(c->w.shared_down_scale);
+        dp.dn_mx = mx ? static_cast<const uint8_t *>(c->w.down_scale) : nullptr;
+        dp.sdn_mx = mx ? static_cast<const uint8_t *>(c->w.shared_down_scale) : nullptr;
         if (p.down_big) {
             L.step("down_big", [&] { return launch_down_big(dp, expert_kdt(c), p.down_grid, L.stream); });
         } else if (p.wide) {
@@ -557,14 +565,16 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
 }
 
 bool valid_inter(int v, int dtype) {
-    // FP8 weights run only the chunked expert kernels: 128-element weight-row chunks
-    const int m = dtype == MOE_FP8_E4M3 ? 128 : dtype == MOE_BF16 ? 32 : 16;
+    // FP8 weights run only the chunked expert kernels: 128-element weight-row chunks; MXFP4
+    // weights stream chunk pairs (256 weights, 128 bytes of codes per row)
+    const int m = dtype == MOE_MXFP4 ? 256 : dtype == MOE_FP8_E4M3 ? 128 : dtype == MOE_BF16 ? 32 : 16;
     return v >= m && v <= 4096 && v % m == 0;
 }
 
 int route_kdt(const moe_ctx *c) { return act_dtype(c->cfg.dtype) == MOE_BF16 ? 1 : 0; }
 int expert_kdt(const moe_ctx *c) {
-    return c->cfg.dtype == MOE_FP8_E4M3 ? 2 : c->cfg.dtype == MOE_BF16 ? 1 : 0;
+    return c->cfg.dtype == MOE_MXFP4 ? 3 : c->cfg.dtype == MOE_FP8_E4M3 ? 2
+                                         : c->cfg.dtype == MOE_BF16 ? 1 : 0;
 }
 
 }  // namespace
@@ -586,12 +596,14 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
     if (!out) return MOE_ERR_INVALID_ARG;
     *out = nullptr;
     if (!cfg || !weights) return MOE_ERR_INVALID_ARG;
-    if (cfg->dtype != MOE_F32 && cfg->dtype != MOE_BF16 && cfg->dtype != MOE_FP8_E4M3)
+    if (cfg->dtype != MOE_F32 && cfg->dtype != MOE_BF16 && cfg->dtype != MOE_FP8_E4M3 &&
+        cfg->dtype != MOE_MXFP4)
         return MOE_ERR_INVALID_ARG;
     if (cfg->top_k != 8) return MOE_ERR_UNSUPPORTED;
     if (cfg->num_experts < 8 || cfg->num_experts > 256) return MOE_ERR_UNSUPPORTED;
     if (cfg->hidden < 64 || cfg->hidden > 16384 || cfg->hidden % 64) return MOE_ERR_UNSUPPORTED;
     if (cfg->dtype != MOE_F32 && cfg->hidden % 128) return MOE_ERR_UNSUPPORTED;
+    if (cfg->dtype == MOE_MXFP4 && cfg->hidden % 256) return MOE_ERR_UNSUPPORTED;
     if (!valid_inter(cfg->inter, cfg->dtype)) return MOE_ERR_UNSUPPORTED;
     if (cfg->shared_inter != 0 && !valid_inter(cfg->shared_inter, cfg->dtype))
         return MOE_ERR_UNSUPPORTED;
@@ -607,14 +619,16 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
     for (const void *ptr : ptrs)
         if (ptr && !aligned(ptr, 16)) return MOE_ERR_INVALID_ARG;
     if (weights->router_bias && !aligned(weights->router_bias, 4)) return MOE_ERR_INVALID_ARG;
-    // row scales: all present (16-byte aligned) with FP8 weights, all absent otherwise
-    const float *scales[] = {weights->gate_up_scale, weights->down_scale,
-                             weights->shared_gate_up_scale, weights->shared_down_scale};
+    // scales: all present with quantized weights (FP8 row scales 16-byte aligned; MXFP4 scale
+    // bytes at any address), all absent otherwise
+    const void *scales[] = {weights->gate_up_scale, weights->down_scale,
+                            weights->shared_gate_up_scale, weights->shared_down_scale};
     const bool fp8 = cfg->dtype == MOE_FP8_E4M3;
+    const bool quant = fp8 || cfg->dtype == MOE_MXFP4;
     for (int i = 0; i < 4; ++i) {
-        const bool need = fp8 && (i < 2 || has_shared);
+        const bool need = quant && (i < 2 || has_shared);
         if (need != (scales[i] != nullptr)) return MOE_ERR_INVALID_ARG;
-        if (scales[i] && !aligned(scales[i], 16)) return MOE_ERR_INVALID_ARG;
+        if (fp8 && scales[i] && !aligned(scales[i], 16)) return MOE_ERR_INVALID_ARG;
     }
 
     int dev = 0;

@@ -179,6 +179,9 @@ FULL = ["decode_b1_t4", "decode_b8_t32", "verify_skewed_t192", "prefill_t8192"]
 # FP8 E4M3 expert weights (bf16 x and router): the split path (T = 4), the 64-token-group path
 # (T = 192, skewed) and the prefill chunk with tie tokens
 FULL8 = ["decode_b1_t4_fp8", "verify_skewed_t192_fp8", "prefill_t8192_fp8"]
+# MXFP4 expert weights: the 8-token-group kernels at every T
+FULL4 = ["decode_b1_t4_mxfp4", "decode_b8_t32_mxfp4", "verify_skewed_t192_mxfp4",
+         "prefill_t8192_mxfp4"]
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL + FULL8)
@@ -244,7 +247,7 @@ def routing_device(ids, w, g):
             None if g is None else torch.from_numpy(np.ascontiguousarray(g, np.float32)).cuda())
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL + FULL8)
+@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL + FULL8 + FULL4)
 def test_forward_given_oracle_routing(orc, name):
     """y from the oracle's own routing (all tokens routed by the oracle, tie tokens from their
     quantized logits), checked on a token sample against the oracle's fp64 forward."""
@@ -285,7 +288,7 @@ def test_forward_tie_tokens_route_then_forward(orc, name):
     assert_close(y.cpu().numpy()[rows], y_o, f"{name} y (tie protocol)")
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL + FULL8)
+@pytest.mark.parametrize("name", ["tiny_fp32_t4"] + FULL + FULL8 + FULL4)
 def test_forward_internal_routing(orc, name):
     """The whole hot path from x (the launch configuration the benchmark times)."""
     torch = _torch()
@@ -523,6 +526,92 @@ def test_fp8_batch_invariance_bitwise():
     assert torch.equal(y200[:32], y32) and torch.equal(y200[192:200], y32[:8])
     assert torch.equal(y300[:32], y32) and torch.equal(y300[288:300], y32[:12])
     assert torch.equal(y1600[:32], y32) and torch.equal(y1600[1568:], y32)
+
+
+def test_mxfp4_batch_invariance_bitwise():
+    """MXFP4 weights: a token's output bits do not depend on its batch (the 8-token-group kernels
+    at T = 4, 32, 200 and 1600, with the routing kernels of each size)."""
+    torch = _torch()
+    layer, m, t = get_layer("decode_b1_t4_mxfp4")
+    x = torch.cat([t["x"]] * 8)  # 32 tokens
+    y32 = m.forward(x)
+    y4 = m.forward(x[:4].contiguous())
+    y200 = m.forward(torch.cat([x] * 7)[:200].contiguous())
+    y1600 = m.forward(torch.cat([x] * 50).contiguous())
+    torch.cuda.synchronize()
+    for T in (4, 32, 200, 1600):
+        assert m.plan(T)[-2:] == ["gateup", "down"], (T, m.plan(T))
+    assert torch.equal(y32[:4], y4)
+    assert torch.equal(y200[:32], y32) and torch.equal(y200[192:200], y32[:8])
+    assert torch.equal(y1600[:32], y32) and torch.equal(y1600[1568:], y32)
+
+
+def mxfp4_small_layer(H, E, I, Is, T, seed, lo, hi):
+    """Random E2M1 codes with random E8M0 scale bytes in [lo, hi] per block (bf16 x, router)."""
+    rng = np.random.default_rng(seed)
+
+    def mx(rows, cols):
+        codes = rng.integers(0, 16, size=(rows, cols)).astype(np.uint8)
+        return ((codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8),
+                rng.integers(lo, hi + 1, size=(rows, cols // 32)).astype(np.uint8))
+
+    def bf(shape, scale):
+        return inputs.f32_to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
+
+    gu = [mx(2 * I, H) for _ in range(E)]
+    dn = [mx(H, I) for _ in range(E)]
+    layer = {"num_experts": E, "inter": I, "shared_inter": Is, "dtype": "mxfp4",
+             "router_w": bf((E + (1 if Is else 0), H), H ** -0.5), "router_bias": None,
+             "gate_up": np.stack([a for a, _ in gu]), "gate_up_scale": np.stack([b for _, b in gu]),
+             "down": np.stack([a for a, _ in dn]), "down_scale": np.stack([b for _, b in dn]),
+             "x": bf((T, H), 1.0)}
+    if Is:
+        (layer["shared_gate_up"], layer["shared_gate_up_scale"]) = mx(2 * Is, H)
+        (layer["shared_down"], layer["shared_down_scale"]) = mx(H, Is)
+    else:
+        for k in ("shared_gate_up", "shared_gate_up_scale", "shared_down", "shared_down_scale"):
+            layer[k] = None
+    return layer
+
+
+# (H, E, I, Is, scale-byte range, token counts)
+MX_SHAPES = [
+    (256, 32, 256, 256, (112, 124), (1, 5, 33, 64, 65, 200)),
+    (512, 16, 512, 0, (96, 132), (3, 64, 130)),      # no shared expert, scales over 2^36
+    (256, 64, 256, 512, (120, 126), (2, 64, 97)),    # shared expert wider than the routed ones
+]
+
+
+@pytest.mark.parametrize("shape", MX_SHAPES, ids=lambda s: f"H{s[0]}-E{s[1]}-I{s[2]}-Is{s[3]}")
+def test_mxfp4_small_shapes(orc, shape):
+    """Every output of the MXFP4 path against the oracle for several shapes and token counts
+    (ragged 8-token groups, T above 64), with a different scale byte on every block of 32
+    weights, from the oracle's routing and from x."""
+    torch = _torch()
+    H, E, I, Is, (lo, hi), Ts = shape
+    Tmax = max(Ts)
+    layer = mxfp4_small_layer(H, E, I, Is, Tmax, seed=H + E + I + Is, lo=lo, hi=hi)
+    t = binding.device_weights(layer)
+    m = binding.MoeLayer(H, E, I, Is, Tmax, "mxfp4", t)
+    ws = m.workspace(Tmax)
+    for T in Ts:
+        assert m.plan(T)[-2:] == ["gateup", "down"]
+        lay = dict(layer)
+        lay["x"] = layer["x"][:T]
+        x = t["x"][:T].contiguous()
+        z_o = orc.logits(lay["x"], layer["router_w"], None)
+        ids_o, w_o, g_o = orc.select(z_o, E, Is > 0)
+        y2 = m.forward(x, routing=routing_device(ids_o, w_o, g_o), ws=ws)
+        y = m.forward(x, ws=ws)
+        _, ids, _, _ = m.route(x=x, want_logits=False, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:m.state_bytes()].view(torch.int32).abs().sum()) == 0
+        y_o = orc.forward(lay, ids_o, w_o, g_o)
+        scale = max(1.0, float(np.abs(y_o).max()))
+        assert_close(y2.cpu().numpy() / scale, y_o / scale, f"{shape} T={T} (oracle routing)")
+        same = (ids.cpu().numpy() == ids_o).all(1)
+        assert same.sum() >= T - max(1, T // 50), f"T={T}: routing differs on {T - same.sum()} tokens"
+        assert_close(y.cpu().numpy()[same] / scale, y_o[same] / scale, f"{shape} T={T} (from x)")
 
 
 def test_token_permutation_equivariance():

@@ -146,6 +146,38 @@ def test_create_checks_fp8_weights(lib):
         assert create(lib, c, fp8_weights())[0] == binding.MOE_ERR_UNSUPPORTED, field
 
 
+def test_create_checks_mxfp4_weights(lib):
+    """MXFP4 expert weights need every scale-byte array (at any address) and 256-weight
+    multiples for H, I and I_s."""
+    base = 0x20000000
+
+    def mx_cfg():
+        c = good_config()
+        c.dtype = binding.MOE_MXFP4
+        return c
+
+    def mx_weights():
+        w = fake_weights(True)
+        w.gate_up_scale = base + 1  # byte arrays: no alignment asked for
+        w.down_scale = base + 0x100003
+        w.shared_gate_up_scale = base + 0x200005
+        w.shared_down_scale = base + 0x300007
+        return w
+
+    for name in ("gate_up_scale", "down_scale", "shared_gate_up_scale", "shared_down_scale"):
+        w = mx_weights()
+        setattr(w, name, None)
+        assert create(lib, mx_cfg(), w)[0] == binding.MOE_ERR_INVALID_ARG, name
+    st, ctx = create(lib, mx_cfg(), mx_weights())  # valid: fails only for want of a GPU here
+    assert st in (binding.MOE_OK, binding.MOE_ERR_HIP, binding.MOE_ERR_UNSUPPORTED)
+    if st == binding.MOE_OK:
+        lib.moe_destroy(ctx)
+    for field, value in (("inter", 384), ("shared_inter", 128), ("hidden", 384)):
+        c = mx_cfg()
+        setattr(c, field, value)
+        assert create(lib, c, mx_weights())[0] == binding.MOE_ERR_UNSUPPORTED, field
+
+
 def test_calls_reject_null_context(lib):
     assert lib.moe_workspace_bytes(None, 4) == 0
     assert lib.moe_route(None, None, None, 4, None, None, None, None, None, 0, None) == \
