@@ -140,9 +140,7 @@ Plan make_plan(const moe_ctx *c, int T) {
     // the split and wide kernels stream weight rows in chunks of 16 x 16 bytes (128 bf16 / 64 fp32)
     const int chunk = act_dtype(cfg.dtype) == MOE_BF16 ? 128 : 64;
     const bool chunk_ok = I % chunk == 0 && Is % chunk == 0;
-    // MXFP4 weights run the 8-token-group kernels at every T (no 64-token-group variant)
-    const bool mx = cfg.dtype == MOE_MXFP4;
-    p.wide = T > kSplitMaxTokens && chunk_ok && !mx;
+    p.wide = T > kSplitMaxTokens && chunk_ok;
     p.NG = p.wide ? wide_group_tokens() : ng_x;
     p.n_chunks = p.small ? 0 : (T + kHistChunk - 1) / kHistChunk;
     const int pairs = T * 8;
@@ -163,8 +161,7 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.gu_S = Imax / 32;
     p.down_lds = (size_t)ng_x * (Imax + 16 / esz) * esz * (esz == 2 ? 2 : 1) +
                  down_stage_bytes();
-    p.split = (T <= kSplitMaxTokens || mx) && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds &&
-              chunk_ok;
+    p.split = T <= kSplitMaxTokens && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds && chunk_ok;
     if (p.wide) {
         const int dr = wide_rows_per_down_unit(), gr = wide_rows_per_gateup_unit();
         const long d_units = (long)p.max_groups * ((H + dr - 1) / dr);

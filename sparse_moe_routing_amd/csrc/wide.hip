@@ -43,8 +43,20 @@ __device__ __forceinline__ uint4 lds_read16(const unsigned char *p) {
 // 256 bytes (lane: row lane / 16 + 4a, 16-byte piece lane % 16). FP8 codes (128 bytes per row):
 // 2 loads of 8 rows x 128 bytes (lane: row lane / 8 + 8a, 16 codes at lane % 8), widened to bf16
 // when staged.
+// MXFP4 storage (packed E2M1 codes, an E8M0 scale byte per 32 weights) as a weight format of the
+// wide kernels: a loaded piece carries its 32 codes and their scale byte.
+struct MxFmt {
+    using wt_t = uint8_t;
+    struct raw_t {
+        uint4 c;
+        uint32_t s;
+    };
+    static constexpr bool kScaled = false;  // no row scales: the block scales act on load
+};
+
 template <class WF>
 struct WChunk {
+    static constexpr bool kMx = false;
     static constexpr bool k8 = WF::kScaled;
     static constexpr int kLoads = k8 ? 2 : 4;
     static constexpr int kRowStep = k8 ? 8 : 4;
@@ -56,15 +68,35 @@ struct WChunk {
     }
 };
 
+// MXFP4 chunk of one wave (16 rows x 64 bytes of codes): one load, lane: row lane / 4, the 32
+// codes of scale block lane % 4 of the chunk, and that block's scale byte.
+template <>
+struct WChunk<MxFmt> {
+    static constexpr bool kMx = true;
+    static constexpr bool k8 = false;
+    static constexpr int kLoads = 1;
+    static constexpr int kRowStep = 16;
+    using raw_t = MxFmt::raw_t;
+    __device__ static __forceinline__ int row(int lane) { return lane >> 2; }
+    __device__ static __forceinline__ int elem(int lane) { return (lane & 3) * 16; }  // bytes
+};
+
+// ssrc: the lane's scale byte of chunk 0 (MXFP4 only; the chunk's four blocks follow it)
 template <class WF, int kCE>
 __device__ __forceinline__ void load_wchunk(typename WChunk<WF>::raw_t (&r)[WChunk<WF>::kLoads],
-                                            const typename WF::wt_t *src, size_t row_stride, int c) {
+                                            const typename WF::wt_t *src, size_t row_stride, int c,
+                                            const uint8_t *ssrc = nullptr) {
     using W = WChunk<WF>;
+    if constexpr (W::kMx) {
+        r[0].c = load16_stream(src + c * (kCE / 2));
+        r[0].s = ssrc[c * 4];
+    } else {
 #pragma unroll
-    for (int a = 0; a < W::kLoads; ++a) {
-        const typename WF::wt_t *ptr = src + (size_t)(W::kRowStep * a) * row_stride + c * kCE;
-        if constexpr (W::k8) r[a] = load16_stream(ptr);
-        else r[a] = WF::load_raw(ptr);
+        for (int a = 0; a < W::kLoads; ++a) {
+            const typename WF::wt_t *ptr = src + (size_t)(W::kRowStep * a) * row_stride + c * kCE;
+            if constexpr (W::k8) r[a] = load16_stream(ptr);
+            else r[a] = WF::load_raw(ptr);
+        }
     }
 }
 
@@ -75,18 +107,30 @@ __device__ __forceinline__ void stage_w(unsigned char *buf,
                                         const typename WChunk<WF>::raw_t (&r)[WChunk<WF>::kLoads],
                                         int lane) {
     using W = WChunk<WF>;
+    if constexpr (W::kMx) {  // 32 codes times their block scale as four bf16 pieces (exact)
+        const int rr = W::row(lane), pb = 4 * (lane & 3);
+        const float sf = e8m0_to_f32(r[0].s);
+        const uint32_t w4[4] = {r[0].c.x, r[0].c.y, r[0].c.z, r[0].c.w};
+        mfma_operand_guard();
 #pragma unroll
-    for (int a = 0; a < W::kLoads; ++a) {
-        const int rr = W::kRowStep * a + W::row(lane);
-        if constexpr (W::k8) {  // 16 codes widened to two bf16 pieces (exact)
-            const int p0 = 2 * (lane & 7);
-            *reinterpret_cast<uint4 *>(buf + rr * 256 + ((p0 ^ rr) & 15) * 16) =
-                e4m3x8_to_bf16x8(r[a].x, r[a].y);
-            *reinterpret_cast<uint4 *>(buf + rr * 256 + (((p0 + 1) ^ rr) & 15) * 16) =
-                e4m3x8_to_bf16x8(r[a].z, r[a].w);
-        } else {
-            const int lpiece = lane & 15;
-            *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) = WF::to_operand(r[a]);
+        for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<uint4 *>(buf + rr * 256 + (((pb + k) ^ rr) & 15) * 16) =
+                e2m1x8_to_bf16x8(w4[k], sf);
+    } else {
+#pragma unroll
+        for (int a = 0; a < W::kLoads; ++a) {
+            const int rr = W::kRowStep * a + W::row(lane);
+            if constexpr (W::k8) {  // 16 codes widened to two bf16 pieces (exact)
+                const int p0 = 2 * (lane & 7);
+                *reinterpret_cast<uint4 *>(buf + rr * 256 + ((p0 ^ rr) & 15) * 16) =
+                    e4m3x8_to_bf16x8(r[a].x, r[a].y);
+                *reinterpret_cast<uint4 *>(buf + rr * 256 + (((p0 + 1) ^ rr) & 15) * 16) =
+                    e4m3x8_to_bf16x8(r[a].z, r[a].w);
+            } else {
+                const int lpiece = lane & 15;
+                *reinterpret_cast<uint4 *>(buf + rr * 256 + ((lpiece ^ rr) & 15) * 16) =
+                    WF::to_operand(r[a]);
+            }
         }
     }
 }
@@ -97,10 +141,11 @@ __device__ __forceinline__ uint4 w_operand(const unsigned char *buf, int s, int 
 
 }  // namespace
 
-template <class Op, int NT, bool kFp8>
+template <class Op, int NT, bool kFp8, bool kMx = false>
 __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) {
     using elem_t = typename Op::elem_t;
-    using WF = WeightFmt<Op, kFp8>;
+    using WF = typename std::conditional<kMx, MxFmt, WeightFmt<Op, kFp8>>::type;
+    constexpr int kPack = kMx ? 2 : 1;  // weights per stored element
     using wt_t = typename WF::wt_t;
     constexpr int TG = NT * kTile;
     constexpr int kCE = kWPieces * Op::kPerLane;
@@ -134,10 +179,14 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
         const int nt_used = (n + kTile - 1) / kTile;
 
         const wt_t *gu = reinterpret_cast<const wt_t *>(shared ? p.sgu : p.gate_up) +
-                         (shared ? 0 : (size_t)e * 2 * Ie * p.H);
+                         (shared ? 0 : (size_t)e * 2 * Ie * (p.H / kPack));
         const int wrow0 = (wave < kGW ? 0 : Ie) + j * kSW + (wave % kGW) * kTile;
         using W = WChunk<WF>;
-        const wt_t *src = gu + (size_t)(wrow0 + W::row(lane)) * p.H + W::elem(lane);
+        const wt_t *src = gu + (size_t)(wrow0 + W::row(lane)) * (p.H / kPack) + W::elem(lane);
+        const int srow = p.H / 32;  // MXFP4 scale bytes per row
+        const uint8_t *ssrc = kMx ? (shared ? p.sgu_mx : p.gu_mx + (size_t)e * 2 * Ie * srow) +
+                                        (size_t)(wrow0 + W::row(lane)) * srow + (lane & 3)
+                                  : nullptr;
         const elem_t *xsrc[kXPasses];
 #pragma unroll
         for (int i = 0; i < kXPasses; ++i) {
@@ -149,7 +198,7 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
         // weight chunks in flight: a ring of kWD register buffers (FP8 codes are half the bytes,
         // so more chunks fill the same registers); bf16: 3 measured best (uniform T = 192 gate/up
         // 196.9 us against 202.9 with 2; 4 drops to three waves per SIMD: 206.8)
-        constexpr int kWD = kFp8 ? 4 : 3;
+        constexpr int kWD = kMx ? 8 : kFp8 ? 4 : 3;
         typename W::raw_t wr[kWD][W::kLoads];
         uint4 xv[kXPasses];
         // a pass whose rows all lie past n is skipped (uniform): the columns those rows feed are
@@ -172,7 +221,7 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
 
 #pragma unroll
         for (int d = 0; d < kWD; ++d)
-            if (d < nchunks) load_wchunk<WF, kCE>(wr[d], src, p.H, d);
+            if (d < nchunks) load_wchunk<WF, kCE>(wr[d], src, p.H, d, ssrc);
         load_x(0);
         __syncthreads();  // the previous unit's readers of xs / xchg are done
         store_x(0);
@@ -180,7 +229,7 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
             if (c + 1 < nchunks) load_x(c + 1);
             __syncthreads();  // x chunk c is staged; chunk c - 1's readers are done
             stage_w<WF>(stage, wcur, lane);
-            if (c + kWD < nchunks) load_wchunk<WF, kCE>(wcur, src, p.H, c + kWD);
+            if (c + kWD < nchunks) load_wchunk<WF, kCE>(wcur, src, p.H, c + kWD, ssrc);
             const unsigned char *xb = xs + (c & 1) * TG * kXRow;
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
@@ -245,10 +294,11 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
     }
 }
 
-template <class Op, int NT, bool kFp8>
+template <class Op, int NT, bool kFp8, bool kMx = false>
 __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
     using elem_t = typename Op::elem_t;
-    using WF = WeightFmt<Op, kFp8>;
+    using WF = typename std::conditional<kMx, MxFmt, WeightFmt<Op, kFp8>>::type;
+    constexpr int kPack = kMx ? 2 : 1;  // weights per stored element
     using wt_t = typename WF::wt_t;
     constexpr int TG = NT * kTile;
     constexpr int kCE = kWPieces * Op::kPerLane;
@@ -278,14 +328,19 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
         const int Ie = shared ? p.Is : p.I;
         const int nchunks = Ie / kCE;
         const int nt_used = (n + kTile - 1) / kTile;
+        const int rowe = Ie / kPack;  // stored elements per weight row
         const wt_t *dn = reinterpret_cast<const wt_t *>(shared ? p.sdn : p.down) +
-                         (shared ? 0 : (size_t)e * p.H * Ie);
+                         (shared ? 0 : (size_t)e * p.H * rowe);
         // rows rc * 256 + wave * 32 + tile * 16 + ...: one contiguous 32-row block per wave; a wave
         // past H (H is a multiple of 32) only joins the block barriers
         const int wrow = rc * kRowsPerUnit + wave * kDownTiles * kTile;
         const bool rows_ok = wrow < p.H;  // uniform over the wave
         using W = WChunk<WF>;
-        const wt_t *src = dn + (size_t)((rows_ok ? wrow : 0) + W::row(lane)) * Ie + W::elem(lane);
+        const wt_t *src = dn + (size_t)((rows_ok ? wrow : 0) + W::row(lane)) * rowe + W::elem(lane);
+        const int srow = Ie / 32;  // MXFP4 scale bytes per row
+        const uint8_t *ssrc = kMx ? (shared ? p.sdn_mx : p.dn_mx + (size_t)e * p.H * srow) +
+                                        (size_t)((rows_ok ? wrow : 0) + W::row(lane)) * srow + (lane & 3)
+                                  : nullptr;
         const elem_t *hsrc[kHPasses];
 #pragma unroll
         for (int i = 0; i < kHPasses; ++i) {
@@ -294,13 +349,14 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
             const int slot = shared ? p.T * kTopK + start + rr : p.perm[start + rr];
             hsrc[i] = hg + (size_t)slot * p.Imax + hp * Op::kPerLane;
         }
-        constexpr int kWD = kFp8 ? 4 : 2;  // weight chunks in flight (ring of register buffers)
+        constexpr int kWD = kFp8 || kMx ? 4 : 2;  // weight chunks in flight (ring of register buffers)
         typename W::raw_t wr[kWD][kDownTiles][W::kLoads];
         uint4 hv[kPlanes][kHPasses];
         auto load_w = [&](typename W::raw_t (&w)[kDownTiles][W::kLoads], int c) {
 #pragma unroll
             for (int t = 0; t < kDownTiles; ++t)
-                load_wchunk<WF, kCE>(w[t], src + (size_t)(t * kTile) * Ie, Ie, c);
+                load_wchunk<WF, kCE>(w[t], src + (size_t)(t * kTile) * rowe, rowe, c,
+                                     kMx ? ssrc + (size_t)(t * kTile) * srow : nullptr);
         };
         // (unlike x, every pass is loaded: skipping passes here measured slower - the branches
         // break the load pipelining across chunks)
@@ -862,13 +918,15 @@ hipError_t prepare_wide_kernels() {
             return err;
     const void *gk[] = {reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT, false>),
                         reinterpret_cast<const void *>(&gateup_wide_kernel<OpF32, kWideNT, false>),
-                        reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT, true>)};
+                        reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT, true>),
+                        reinterpret_cast<const void *>(&gateup_wide_kernel<OpBF16, kWideNT, false, true>)};
     for (const void *k : gk)
         if ((err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)gateup_wide_lds())) != hipSuccess)
             return err;
     const void *dk16[] = {reinterpret_cast<const void *>(&down_wide_kernel<OpBF16, kWideNT, false>),
-                          reinterpret_cast<const void *>(&down_wide_kernel<OpBF16, kWideNT, true>)};
+                          reinterpret_cast<const void *>(&down_wide_kernel<OpBF16, kWideNT, true>),
+                          reinterpret_cast<const void *>(&down_wide_kernel<OpBF16, kWideNT, false, true>)};
     for (const void *k : dk16)
         if ((err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)down_wide_lds(1))) != hipSuccess)
@@ -877,16 +935,18 @@ hipError_t prepare_wide_kernels() {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)down_wide_lds(0));
 }
 
-// dtype: 0 fp32, 1 bf16, 2 bf16 activations with FP8 E4M3 weights
+// dtype: 0 fp32, 1 bf16, 2 bf16 activations with FP8 E4M3 weights, 3 with MXFP4 weights
 hipError_t launch_gateup_wide(const GateUpParams &p, int dtype, int grid, hipStream_t s) {
-    if (dtype == 2) launch_k(gateup_wide_kernel<OpBF16, kWideNT, true>, grid, kWThreads, gateup_wide_lds(), s, p);
+    if (dtype == 3) launch_k(gateup_wide_kernel<OpBF16, kWideNT, false, true>, grid, kWThreads, gateup_wide_lds(), s, p);
+    else if (dtype == 2) launch_k(gateup_wide_kernel<OpBF16, kWideNT, true>, grid, kWThreads, gateup_wide_lds(), s, p);
     else if (dtype == 1) launch_k(gateup_wide_kernel<OpBF16, kWideNT, false>, grid, kWThreads, gateup_wide_lds(), s, p);
     else launch_k(gateup_wide_kernel<OpF32, kWideNT, false>, grid, kWThreads, gateup_wide_lds(), s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_down_wide(const DownParams &p, int dtype, int grid, hipStream_t s) {
-    if (dtype == 2) launch_k(down_wide_kernel<OpBF16, kWideNT, true>, grid, kWThreads, down_wide_lds(1), s, p);
+    if (dtype == 3) launch_k(down_wide_kernel<OpBF16, kWideNT, false, true>, grid, kWThreads, down_wide_lds(1), s, p);
+    else if (dtype == 2) launch_k(down_wide_kernel<OpBF16, kWideNT, true>, grid, kWThreads, down_wide_lds(1), s, p);
     else if (dtype == 1) launch_k(down_wide_kernel<OpBF16, kWideNT, false>, grid, kWThreads, down_wide_lds(1), s, p);
     else launch_k(down_wide_kernel<OpF32, kWideNT, false>, grid, kWThreads, down_wide_lds(0), s, p);
     return hipGetLastError();

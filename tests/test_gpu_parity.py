@@ -529,8 +529,8 @@ def test_fp8_batch_invariance_bitwise():
 
 
 def test_mxfp4_batch_invariance_bitwise():
-    """MXFP4 weights: a token's output bits do not depend on its batch (the 8-token-group kernels
-    at T = 4, 32, 200 and 1600, with the routing kernels of each size)."""
+    """MXFP4 weights: a token's output bits do not depend on its batch, across the 8-token-group
+    kernels (T = 4, 32) and the 64-token-group kernels (T = 200, 1600)."""
     torch = _torch()
     layer, m, t = get_layer("decode_b1_t4_mxfp4")
     x = torch.cat([t["x"]] * 8)  # 32 tokens
@@ -539,8 +539,10 @@ def test_mxfp4_batch_invariance_bitwise():
     y200 = m.forward(torch.cat([x] * 7)[:200].contiguous())
     y1600 = m.forward(torch.cat([x] * 50).contiguous())
     torch.cuda.synchronize()
-    for T in (4, 32, 200, 1600):
+    for T in (4, 32):
         assert m.plan(T)[-2:] == ["gateup", "down"], (T, m.plan(T))
+    for T in (200, 1600):
+        assert m.plan(T)[-3:] == ["gateup_wide", "down_wide", "combine"], (T, m.plan(T))
     assert torch.equal(y32[:4], y4)
     assert torch.equal(y200[:32], y32) and torch.equal(y200[192:200], y32[:8])
     assert torch.equal(y1600[:32], y32) and torch.equal(y1600[1568:], y32)
@@ -584,9 +586,9 @@ MX_SHAPES = [
 
 @pytest.mark.parametrize("shape", MX_SHAPES, ids=lambda s: f"H{s[0]}-E{s[1]}-I{s[2]}-Is{s[3]}")
 def test_mxfp4_small_shapes(orc, shape):
-    """Every output of the MXFP4 path against the oracle for several shapes and token counts
-    (ragged 8-token groups, T above 64), with a different scale byte on every block of 32
-    weights, from the oracle's routing and from x."""
+    """Every output of the MXFP4 paths against the oracle for several shapes and token counts
+    (ragged 8-token groups up to T = 64, 64-token groups above), with a different scale byte on
+    every block of 32 weights, from the oracle's routing and from x."""
     torch = _torch()
     H, E, I, Is, (lo, hi), Ts = shape
     Tmax = max(Ts)
@@ -595,7 +597,8 @@ def test_mxfp4_small_shapes(orc, shape):
     m = binding.MoeLayer(H, E, I, Is, Tmax, "mxfp4", t)
     ws = m.workspace(Tmax)
     for T in Ts:
-        assert m.plan(T)[-2:] == ["gateup", "down"]
+        want = ["gateup", "down"] if T <= 64 else ["gateup_wide", "down_wide", "combine"]
+        assert m.plan(T)[-len(want):] == want, (T, m.plan(T))
         lay = dict(layer)
         lay["x"] = layer["x"][:T]
         x = t["x"][:T].contiguous()
