@@ -106,7 +106,7 @@ double oracle_e8m0_value(uint8_t b) {
 /* Widen one stored element to double. bf16 is the top half of an fp32 word, so the value is the
  * 16 stored bits shifted into the high half; the conversion is exact. An FP8 element is its
  * code's value times the fp32 scale of its row (given by the caller). */
-static double load_elem(const void *base, int dtype, size_t i) {
+static inline __attribute__((always_inline)) double load_elem(const void *base, int dtype, size_t i) {
     if (dtype == ORACLE_F32) return (double)((const float *)base)[i];
     if (dtype == ORACLE_FP8) return oracle_e4m3_value(((const uint8_t *)base)[i]);
     uint32_t bits = ((uint32_t)((const uint16_t *)base)[i]) << 16;
@@ -124,8 +124,9 @@ static size_t elem_size(int dtype) {
  * code's value times the row's fp32 scale (scale[srow]; 1 without scales). MXFP4: codes packed
  * two per byte along the row (column 2j in the low nibble of byte j, 2j + 1 in the high one),
  * scale bytes [rows][cols / 32]; the weight is the code's value times its block's scale. */
-static double weight_at(const void *m, const void *scale, int wdtype, int row, int col, int cols,
-                        int srow) {
+static inline __attribute__((always_inline)) double weight_at(const void *m, const void *scale,
+                                                               int wdtype, int row, int col,
+                                                               int cols, int srow) {
     if (wdtype == ORACLE_MXFP4) {
         const uint8_t b = ((const uint8_t *)m)[(size_t)row * (cols / 2) + col / 2];
 #ifdef ORACLE_PLANT_FP4_HIGH_FIRST
