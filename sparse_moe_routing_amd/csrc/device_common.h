@@ -126,6 +126,14 @@ __device__ __forceinline__ void mfma_operand_guard() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Stage position of operand piece p (0..15) of an MXFP4 chunk row, before the row swizzle: each
+// group of four pieces (one lane's scale block) is rotated by its group index and by the stage
+// buffer b, so that the eight lanes that write one row in one LDS instruction (one piece each)
+// hit eight distinct 16-byte bank groups. Writer and operand reader use the same map.
+__device__ __forceinline__ int mx_piece_pos(int p, int b) {
+    return (p & 12) | (((p & 3) + (p >> 2) + b) & 3);
+}
+
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <class Op, bool kFp8>

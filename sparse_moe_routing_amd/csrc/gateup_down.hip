@@ -129,10 +129,10 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
                     }
                 }
         };
-        auto mma_chunk = [&](const unsigned char *buf, int c) {
+        auto mma_chunk = [&](const unsigned char *buf, int c, int mb) {  // mb: MXFP4 buffer
 #pragma unroll
             for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
-                const int pc = 4 * s2 + q;
+                const int pc = kMx ? mx_piece_pos(4 * s2 + q, mb) : 4 * s2 + q;
                 const uint4 av = lds_load16(buf + col * 256 + ((pc ^ col) & 15) * 16);
                 const uint4 xb = lds_load16(xrow + c * kChunkElems + 4 * s2 * Op::kPerLane);
                 Op::mma(acc, av, xb);
@@ -156,11 +156,12 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
                         const uint32_t w4[4] = {r[d][a].x, r[d][a].y, r[d][a].z, r[d][a].w};
 #pragma unroll
                         for (int k = 0; k < 4; ++k)
-                            *reinterpret_cast<uint4 *>(buf + rr * 256 + (((pb + k) ^ rr) & 15) * 16) =
+                            *reinterpret_cast<uint4 *>(
+                                buf + rr * 256 + ((mx_piece_pos(pb + k, lpiece8 >> 2) ^ rr) & 15) * 16) =
                                 e2m1x8_to_bf16x8(w4[k], sf);
                     }
-                    mma_chunk(stage, 2 * (c0 + d));  // a wave's LDS ops stay in order
-                    mma_chunk(stage + kStage, 2 * (c0 + d) + 1);
+                    mma_chunk(stage, 2 * (c0 + d), 0);  // a wave's LDS ops stay in order
+                    mma_chunk(stage + kStage, 2 * (c0 + d) + 1, 1);
                     continue;
                 }
                 unsigned char *buf = stage + (d % kStageBufs) * kStage;  // a wave's LDS ops stay in order
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
                             WF::to_operand(r[d][a]);
                     }
                 }
-                mma_chunk(buf, c0 + d);
+                mma_chunk(buf, c0 + d, 0);
             }
         };
         // the weight stream does not depend on x: both buffers are requested before staging x
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
         auto mma_chunk = [&](int c) {
 #pragma unroll
             for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
-                const int pc = 4 * s2 + q;
+                const int pc = kMx ? mx_piece_pos(4 * s2 + q, 0) : 4 * s2 + q;
                 const uint4 av = lds_load16(stage + col * 256 + ((pc ^ col) & 15) * 16);
                 const int kk = c * kChunkElems + 4 * s2 * Op::kPerLane;
                 Op::mma(acc, av, lds_load16(bhp + kk));
@@ -403,8 +404,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
                                 const uint32_t w4[4] = {a[d][r].x, a[d][r].y, a[d][r].z, a[d][r].w};
 #pragma unroll
                                 for (int k = 0; k < 4; ++k)
-                                    *reinterpret_cast<uint4 *>(stage + rr * 256 +
-                                                               (((pb + k) ^ rr) & 15) * 16) =
+                                    *reinterpret_cast<uint4 *>(
+                                        stage + rr * 256 + ((mx_piece_pos(pb + k, 0) ^ rr) & 15) * 16) =
                                         e2m1x8_to_bf16x8(w4[k], sf);
                             }
                         }

@@ -114,7 +114,7 @@ __device__ __forceinline__ void stage_w(unsigned char *buf,
         mfma_operand_guard();
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            *reinterpret_cast<uint4 *>(buf + rr * 256 + (((pb + k) ^ rr) & 15) * 16) =
+            *reinterpret_cast<uint4 *>(buf + rr * 256 + ((mx_piece_pos(pb + k, 0) ^ rr) & 15) * 16) =
                 e2m1x8_to_bf16x8(w4[k], sf);
     } else {
 #pragma unroll
@@ -134,8 +134,9 @@ __device__ __forceinline__ void stage_w(unsigned char *buf,
         }
     }
 }
+template <bool kMx = false>
 __device__ __forceinline__ uint4 w_operand(const unsigned char *buf, int s, int col, int q) {
-    const int pc = 4 * s + q;
+    const int pc = kMx ? mx_piece_pos(4 * s + q, 0) : 4 * s + q;
     return lds_read16(buf + col * 256 + ((pc ^ col) & 15) * 16);
 }
 
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
             const unsigned char *xb = xs + (c & 1) * TG * kXRow;
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
-                const uint4 a = w_operand(stage, s, col, q);
+                const uint4 a = w_operand<kMx>(stage, s, col, q);
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt)
                     if (tt < nt_used)  // uniform
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
             for (int s = 0; s < kSteps && rows_ok; ++s) {
                 uint4 a[kDownTiles];
 #pragma unroll
-                for (int t = 0; t < kDownTiles; ++t) a[t] = w_operand(stage + t * kWStage, s, col, q);
+                for (int t = 0; t < kDownTiles; ++t) a[t] = w_operand<kMx>(stage + t * kWStage, s, col, q);
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
                     if (tt >= nt_used) continue;  // uniform
