@@ -134,6 +134,11 @@ __device__ __forceinline__ int mx_piece_pos(int p, int b) {
     return (p & 12) | (((p & 3) + (p >> 2) + b) & 3);
 }
 
+// The same for FP8 E4M3 chunks, where each of a row's 8 lanes writes pieces 2j and 2j + 1: the
+// upper half of the row's pieces swaps pairs, so that one LDS instruction's 8 pieces are 8
+// distinct bank groups.
+__device__ __forceinline__ int fp8_piece_pos(int p) { return p ^ ((p >> 3) & 1); }
+
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <class Op, bool kFp8>

@@ -132,7 +132,8 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
         auto mma_chunk = [&](const unsigned char *buf, int c, int mb) {  // mb: MXFP4 buffer
 #pragma unroll
             for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
-                const int pc = kMx ? mx_piece_pos(4 * s2 + q, mb) : 4 * s2 + q;
+                const int pc = kMx ? mx_piece_pos(4 * s2 + q, mb) : kFp8 ? fp8_piece_pos(4 * s2 + q)
+                                                                       : 4 * s2 + q;
                 const uint4 av = lds_load16(buf + col * 256 + ((pc ^ col) & 15) * 16);
                 const uint4 xb = lds_load16(xrow + c * kChunkElems + 4 * s2 * Op::kPerLane);
                 Op::mma(acc, av, xb);
@@ -170,9 +171,9 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
                     if constexpr (kFp8) {  // 16 codes widened to two bf16 pieces (exact)
                         const int rr = 8 * a + lrow8;
                         const int p0 = 2 * lpiece8;
-                        *reinterpret_cast<uint4 *>(buf + rr * 256 + ((p0 ^ rr) & 15) * 16) =
+                        *reinterpret_cast<uint4 *>(buf + rr * 256 + ((fp8_piece_pos(p0) ^ rr) & 15) * 16) =
                             e4m3x8_to_bf16x8(r[d][a].x, r[d][a].y);
-                        *reinterpret_cast<uint4 *>(buf + rr * 256 + (((p0 + 1) ^ rr) & 15) * 16) =
+                        *reinterpret_cast<uint4 *>(buf + rr * 256 + ((fp8_piece_pos(p0 + 1) ^ rr) & 15) * 16) =
                             e4m3x8_to_bf16x8(r[d][a].z, r[d][a].w);
                     } else {
                         const int rr = 4 * a + lrow;
@@ -379,7 +380,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
         auto mma_chunk = [&](int c) {
 #pragma unroll
             for (int s2 = 0; s2 < kStepsPerChunk; ++s2) {
-                const int pc = kMx ? mx_piece_pos(4 * s2 + q, 0) : 4 * s2 + q;
+                const int pc = kMx ? mx_piece_pos(4 * s2 + q, 0) : kFp8 ? fp8_piece_pos(4 * s2 + q)
+                                                                      : 4 * s2 + q;
                 const uint4 av = lds_load16(stage + col * 256 + ((pc ^ col) & 15) * 16);
                 const int kk = c * kChunkElems + 4 * s2 * Op::kPerLane;
                 Op::mma(acc, av, lds_load16(bhp + kk));
@@ -418,9 +420,9 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
                     if constexpr (kFp8) {  // 16 codes widened to two bf16 pieces (exact)
                         const int rr = 8 * r + lrow8;
                         const int p0 = 2 * lpiece8;
-                        *reinterpret_cast<uint4 *>(stage + rr * 256 + ((p0 ^ rr) & 15) * 16) =
+                        *reinterpret_cast<uint4 *>(stage + rr * 256 + ((fp8_piece_pos(p0) ^ rr) & 15) * 16) =
                             e4m3x8_to_bf16x8(a[d][r].x, a[d][r].y);
-                        *reinterpret_cast<uint4 *>(stage + rr * 256 + (((p0 + 1) ^ rr) & 15) * 16) =
+                        *reinterpret_cast<uint4 *>(stage + rr * 256 + ((fp8_piece_pos(p0 + 1) ^ rr) & 15) * 16) =
                             e4m3x8_to_bf16x8(a[d][r].z, a[d][r].w);
                     } else {
                         const int rr = 4 * r + lrow;

@@ -122,9 +122,9 @@ __device__ __forceinline__ void stage_w(unsigned char *buf,
             const int rr = W::kRowStep * a + W::row(lane);
             if constexpr (W::k8) {  // 16 codes widened to two bf16 pieces (exact)
                 const int p0 = 2 * (lane & 7);
-                *reinterpret_cast<uint4 *>(buf + rr * 256 + ((p0 ^ rr) & 15) * 16) =
+                *reinterpret_cast<uint4 *>(buf + rr * 256 + ((fp8_piece_pos(p0) ^ rr) & 15) * 16) =
                     e4m3x8_to_bf16x8(r[a].x, r[a].y);
-                *reinterpret_cast<uint4 *>(buf + rr * 256 + (((p0 + 1) ^ rr) & 15) * 16) =
+                *reinterpret_cast<uint4 *>(buf + rr * 256 + ((fp8_piece_pos(p0 + 1) ^ rr) & 15) * 16) =
                     e4m3x8_to_bf16x8(r[a].z, r[a].w);
             } else {
                 const int lpiece = lane & 15;
@@ -134,9 +134,11 @@ __device__ __forceinline__ void stage_w(unsigned char *buf,
         }
     }
 }
-template <bool kMx = false>
+// kMap: 0 plain, 1 MXFP4, 2 FP8 piece positions (as staged by stage_w)
+template <int kMap = 0>
 __device__ __forceinline__ uint4 w_operand(const unsigned char *buf, int s, int col, int q) {
-    const int pc = kMx ? mx_piece_pos(4 * s + q, 0) : 4 * s + q;
+    const int pc = kMap == 1 ? mx_piece_pos(4 * s + q, 0) : kMap == 2 ? fp8_piece_pos(4 * s + q)
+                                                                      : 4 * s + q;
     return lds_read16(buf + col * 256 + ((pc ^ col) & 15) * 16);
 }
 
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(kWThreads) void gateup_wide_kernel(GateUpParams p) 
             const unsigned char *xb = xs + (c & 1) * TG * kXRow;
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
-                const uint4 a = w_operand<kMx>(stage, s, col, q);
+                const uint4 a = w_operand<kMx ? 1 : kFp8 ? 2 : 0>(stage, s, col, q);
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt)
                     if (tt < nt_used)  // uniform
@@ -401,7 +403,8 @@ __global__ __launch_bounds__(kWThreads) void down_wide_kernel(DownParams p) {
             for (int s = 0; s < kSteps && rows_ok; ++s) {
                 uint4 a[kDownTiles];
 #pragma unroll
-                for (int t = 0; t < kDownTiles; ++t) a[t] = w_operand<kMx>(stage + t * kWStage, s, col, q);
+                for (int t = 0; t < kDownTiles; ++t)
+                    a[t] = w_operand<kMx ? 1 : kFp8 ? 2 : 0>(stage + t * kWStage, s, col, q);
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
                     if (tt >= nt_used) continue;  // uniform
