@@ -211,8 +211,8 @@ def cpu_baseline(w, m_t, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer has no "
-              "multi-GPU path in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
+              "multi-GPU path (expert parallelism is a design, not code)", file=sys.stderr)
         sys.exit(2)
     import torch
     from sparse_moe_routing_amd import binding, inputs

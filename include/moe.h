@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1, /* NULL where a pointer is required, T out of range, bad enum */
-    MOE_ERR_UNSUPPORTED = -2, /* a shape or parameter this build does not implement */
+    MOE_ERR_UNSUPPORTED = -2, /* a shape or parameter the library does not implement */
     MOE_ERR_WORKSPACE = -3,   /* workspace NULL, misaligned or smaller than required */
     MOE_ERR_HIP = -4          /* the HIP runtime reported an error */
 } moe_status;
