@@ -8,9 +8,11 @@ Inputs are resident in HBM before the timed region. To time cold weights (the 25
 Cache would hold a whole T=4 working set), each step uses the next of several independent weight
 sets and the next activation batch of a pool, so consecutive steps share no expert bytes.
 
-Printed: one JSON line with the metric, the dominant kernel's roofline (algorithmic bytes per
-launch over its event-timed average duration) and the oracle's CPU throughput on a bounded
-sample of the same workload.
+Printed: one JSON line with the metric for --workload (default: the T=4 decode round), its
+dominant kernel's roofline (algorithmic bytes per launch over its event-timed average duration)
+and the oracle's CPU throughput on a bounded sample of the same workload (all threads and one).
+The metric is quoted at T=4, 32 and 192, so the same line carries `sub_results` for the T=32
+decode round and the skewed T=192 verify round, each timed the same way after the main one.
 """
 from __future__ import annotations
 
@@ -41,8 +43,10 @@ def parse():
     ap.add_argument("--workload", default="decode_b1_t4")
     ap.add_argument("--sets", type=int, default=6, help="independent weight sets (cold cache)")
     ap.add_argument("--pool", type=int, default=16, help="activation batches in the pool")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="time only --workload (not the T=32 and skewed T=192 rounds as well)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -166,13 +170,23 @@ def counter_traffic(workload, kernel):
     return mib * 2 ** 20
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, m_t, seconds):
-    """The oracle (untuned) on the host: route + forward of whole T-token batches until about
-    `seconds` of CPU time have been spent."""
+    """The oracle (untuned) on the host: route + forward of fresh token batches of the workload's
+    shapes, timed on every thread the process may use (OpenMP over tokens, so each batch holds
+    at least one token per thread) and on one thread, about `seconds` each."""
     import oracle as oracle_mod
     import torch
     orc = oracle_mod.default()
-    t = m_t
 
     def host(a):
         if a is None:
@@ -185,45 +199,51 @@ def cpu_baseline(w, m_t, seconds):
              "dtype": w.dtype}
     for k in ("router_w", "router_bias", "gate_up", "down", "shared_gate_up", "shared_down",
               "gate_up_scale", "down_scale", "shared_gate_up_scale", "shared_down_scale"):
-        layer[k] = host(t.get(k))
+        layer[k] = host(m_t.get(k))
     from sparse_moe_routing_amd import inputs
-    T = min(w.tokens, 64)
-    tokens = 0
-    rounds = 0
-    t0 = time.perf_counter()
-    while True:
-        layer["x"] = inputs.draw_x(w, T, seed=900 + rounds)
-        z = orc.logits(layer["x"], layer["router_w"], layer["router_bias"])
-        ids, wt, g = orc.select(z, w.num_experts, w.shared_inter > 0)
-        orc.forward(layer, ids, wt, g)
-        tokens += T
-        rounds += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    # the oracle parallelises over tokens, so a batch of T tokens keeps at most T threads busy
-    cores = min(T, orc.num_threads())
-    return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rounds} batches of {T} tokens of the {w.name} shapes (fresh x per batch), "
-                      f"fp64 route+forward, {el:.1f} s"}
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count() or 1
+    default_threads = orc.num_threads()  # OMP_NUM_THREADS, else the cores the process may use
+
+    def run(threads, secs):
+        orc.set_num_threads(threads)
+        T = max(w.tokens, threads) if w.tokens <= 64 else 64
+        T = (T + threads - 1) // threads * threads
+        tokens = rounds = 0
+        t0 = time.perf_counter()
+        while True:
+            layer["x"] = inputs.draw_x(w, T, seed=900 + rounds)
+            z = orc.logits(layer["x"], layer["router_w"], layer["router_bias"])
+            ids, wt, g = orc.select(z, w.num_experts, w.shared_inter > 0)
+            orc.forward(layer, ids, wt, g)
+            tokens += T
+            rounds += 1
+            el = time.perf_counter() - t0
+            if el >= secs:
+                break
+        return tokens / el, rounds, T, el
+
+    v_all, r_all, T_all, el_all = run(default_threads, seconds)
+    v_one, r_one, T_one, el_one = run(1, max(2.0, seconds / 3))
+    orc.set_num_threads(default_threads)
+    return {"value": v_all, "unit": "tokens/s", "cores": default_threads, "kind": "oracle",
+            "sample": f"{r_all} batches of {T_all} tokens of the {w.name} shapes (fresh x per "
+                      f"batch, weight set 0), fp64 route+forward, {el_all:.1f} s on "
+                      f"{default_threads} threads",
+            "nproc": os.cpu_count(), "cpus_allowed": allowed, "cpu_model": _cpu_model(),
+            "one_core": {"value": v_one, "unit": "tokens/s", "cores": 1,
+                         "sample": f"{r_one} batches of {T_one} tokens, {el_one:.1f} s"}}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
-              "multi-GPU path (expert parallelism is a design, not code)", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    from sparse_moe_routing_amd import binding, inputs
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    binding.load()
-    w = inputs.BY_NAME[args.workload]
+def measure(w, args, torch, log_prefix):
+    """Warm-up, then K timed steps of plain moe_forward calls (wall clock, synchronized on both
+    sides), then the same K steps once more with per-kernel events. Returns (result dict, the
+    layer tensors of weight set 0)."""
     T, H = w.tokens, w.hidden
-    log(f"[bench] workload {w.name}: T={T} H={H} E={w.num_experts} I={w.inter} Is={w.shared_inter}"
-        f" dtype={w.dtype}; {args.sets} weight sets, pool {args.pool}")
+    log(f"[{log_prefix}] workload {w.name}: T={T} H={H} E={w.num_experts} I={w.inter} "
+        f"Is={w.shared_inter} dtype={w.dtype}; {args.sets} weight sets, pool {args.pool}")
     sets = make_sets(w, args.sets, torch)
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16  # x (fp8 workloads: bf16)
     gen = torch.Generator(device="cuda")
@@ -234,7 +254,6 @@ def main():
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     plan = m0.plan(T)
     n_ev = 2 * len(plan)  # each kernel's own start and end
-    n_pairs = len(sets) * len(pool)
     # distinct experts per (set, batch) pair, from the library's own routing (outside timing)
     U = {}
     for si, (m, _) in enumerate(sets):
@@ -247,7 +266,7 @@ def main():
     def combo(i):
         return i % len(sets), (i // len(sets) + i) % len(pool)
 
-    log(f"[bench] plan {plan}; warmup {args.warmup}")
+    log(f"[{log_prefix}] plan {plan}; warmup {args.warmup}")
     for i in range(args.warmup):
         si, pi = combo(i)
         sets[si][0].forward(pool[pi], y=y, ws=ws)
@@ -259,6 +278,7 @@ def main():
     t0 = time.perf_counter()
     for si, pi in used:
         sets[si][0].forward(pool[pi], y=y, ws=ws, stream=stream)
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -293,11 +313,64 @@ def main():
     achieved = stage[dom]["gbs"]
     step_b = float(np.mean([step_bytes(w, U[c]) for c in used]))
     gpu_step_us = float(np.median(step_ms)) * 1e3
-    log("[bench] per-kernel mean us: " + ", ".join(
+    log(f"[{log_prefix}] per-kernel mean us: " + ", ".join(
         f"{k}={np.mean(v) * 1e3:.2f}" for k, v in per_kernel.items()))
-    log(f"[bench] wall {ms_per_step * 1e3:.2f} us/step, timed pass step median {gpu_step_us:.2f} us (with per-kernel events),"
-        f" mean U {mean_U:.1f}, step bytes {step_b / 1e6:.1f} MB -> "
+    log(f"[{log_prefix}] wall {ms_per_step * 1e3:.2f} us/step (host enqueue "
+        f"{(t_enq - t0) * 1e6 / args.steps:.1f} us/step), event-timed step median "
+        f"{gpu_step_us:.2f} us, mean U {mean_U:.1f}, step bytes {step_b / 1e6:.1f} MB -> "
         f"{step_b / (ms_per_step * 1e-3) / 1e9:.0f} GB/s wall")
+    res = {
+        "value": value, "unit": "tokens/s", "ms_per_step": ms_per_step, "dtype": w.dtype,
+        "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": w.num_experts,
+                   "top_k": 8, "inter": w.inter, "shared_inter": w.shared_inter,
+                   "router_bias_std": w.bias_std, "weight_sets": len(sets),
+                   "x_pool": len(pool)},
+        "hbm_gbs_step": step_b / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_step": step_b / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_bytes": step_b,
+        "mean_distinct_experts": mean_U,
+        "host_enqueue_us_per_step": (t_enq - t0) * 1e6 / args.steps,
+        "event_step_us_median": gpu_step_us,
+        "per_kernel_us": {k: float(np.mean(v)) * 1e3 for k, v in per_kernel.items()},
+        "expert_stage_gbs": {k: v["gbs"] for k, v in stage.items()},
+        "roofline": {"scope": "kernel", "kernel": dom, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counter_traffic(w.name, dom),
+                     "algorithmic_bytes": stage[dom]["bytes"], "launch_us": stage[dom]["us"]},
+    }
+    keep = sets[0][1]
+    for m, _ in sets:
+        m.close()
+    del sets, pool, ws, y, events
+    return res, keep
+
+
+SUB_WORKLOADS = ("decode_b8_t32", "verify_skewed_t192")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
+              "multi-GPU path (expert parallelism is a design, not code)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_moe_routing_amd import binding, inputs
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    w = inputs.BY_NAME[args.workload]
+    main_res, set0 = measure(w, args, torch, "bench")
+    subs = {}
+    if not args.no_sub:
+        for name in SUB_WORKLOADS:
+            if name == w.name:
+                continue
+            sub_w = inputs.BY_NAME[name]
+            r, _ = measure(sub_w, args, torch, "sub")
+            subs[name] = r
+            torch.cuda.empty_cache()
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -308,25 +381,19 @@ def main():
         log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done (3 launches)")
     result = {
         "metric": "MoE-layer tokens/s + achieved HBM GB/s (% of peak) at T=4, 32, 192",
-        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "value": main_res["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": w.num_experts,
-                   "top_k": 8, "inter": w.inter, "shared_inter": w.shared_inter,
-                   "weight_sets": len(sets), "x_pool": len(pool)},
-        "hbm_gbs_step": step_b / (ms_per_step * 1e-3) / 1e9,
-        "hbm_frac_step": step_b / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "mean_distinct_experts": mean_U,
-        "per_kernel_us": {k: float(np.mean(v)) * 1e3 for k, v in per_kernel.items()},
-        "expert_stage_gbs": {k: v["gbs"] for k, v in stage.items()},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counter_traffic(w.name, dom),
-                     "algorithmic_bytes": stage[dom]["bytes"], "launch_us": stage[dom]["us"]},
     }
+    for k in ("config", "hbm_gbs_step", "hbm_frac_step", "step_bytes", "mean_distinct_experts",
+              "host_enqueue_us_per_step", "event_step_us_median", "per_kernel_us",
+              "expert_stage_gbs", "roofline"):
+        result[k] = main_res[k]
+    if subs:
+        result["sub_results"] = subs
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(w, sets[0][1], args.cpu_seconds)
+        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s on all threads, then one)")
+        result["cpu_baseline"] = cpu_baseline(w, set0, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

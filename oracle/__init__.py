@@ -67,6 +67,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_forward_w.argtypes = [i, P, i, i, i, i, i, i, i, i, P, P, P, P, P, P, P, P, P, P,
                                      P, P, P]
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_value.restype = ctypes.c_double
     for f in (lib.oracle_e2m1_value, lib.oracle_e8m0_value):
@@ -98,6 +100,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads of the oracle's later parallel regions (the baseline timing only)."""
+        self.lib.oracle_set_num_threads(int(n))
 
     def logits(self, x: np.ndarray, router_w: np.ndarray, bias: np.ndarray | None = None):
         """z[t][r] = fp32(sum_h W[r][h] x[t][h] + b[r]) with fp64 accumulation."""

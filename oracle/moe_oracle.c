@@ -365,3 +365,14 @@ int oracle_num_threads(void) {
     }
     return n;
 }
+
+/* Thread count of the parallel regions that follow (n > 0); the host baseline times the oracle
+ * on one thread and on every thread the process may use. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -32,7 +32,7 @@ def hipcc() -> str:
 def compile_flags() -> list[str]:
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wextra", "-Wno-unused-parameter", "-Werror=implicit-fallthrough",
+            "-Wall", "-Wextra", "-Wno-unused-parameter", "-Werror",
             "-I" + os.path.join(ROOT, "include")]
 
 

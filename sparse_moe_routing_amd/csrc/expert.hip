@@ -245,10 +245,16 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineParams p) {
         }
         return s;
     };
+    // a pair whose given id lies outside [0, E) was dropped by the bucketing: it adds zero
+    auto valid = [&](int k) {
+        const int e = p.ids[t * kTopK + k];
+        return e >= 0 && e < p.E;
+    };
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p.w) {
 #pragma unroll
         for (int k = 0; k < kTopK; ++k) {
+            if (!valid(k)) continue;
             const float4 s = slot_sum(t * kTopK + k, p.n_sc_routed);
             const float wk = p.w[t * kTopK + k];
             acc.x += wk * s.x; acc.y += wk * s.y; acc.z += wk * s.z; acc.w += wk * s.w;
@@ -266,7 +272,9 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineParams p) {
         };
         float4 v[kTopK + 1];
 #pragma unroll
-        for (int k = 0; k < kTopK; ++k) v[k] = ld4(p.ypart + (size_t)(t * kTopK + k) * p.H + h);
+        for (int k = 0; k < kTopK; ++k)
+            v[k] = valid(k) ? ld4(p.ypart + (size_t)(t * kTopK + k) * p.H + h)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
         v[kTopK] = p.has_shared ? ld4(p.ypart + (size_t)(p.T * kTopK + t) * p.H + h)
                                 : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -297,6 +305,8 @@ hipError_t prepare_expert_kernels(size_t max_lds_bytes) {
 
 hipError_t launch_expert(const ExpertParams &p, int dtype, int grid, size_t lds_bytes,
                          hipStream_t s) {
+    // dtype: 0 fp32, 1 bf16; the quantized weight formats have no variant of this kernel
+    if (dtype != 0 && dtype != 1) return hipErrorInvalidValue;
     if (dtype == 1) {
         if (p.s == 64) launch_k(expert_kernel<OpBF16, 64>, grid, kExpertThreads, lds_bytes, s, p);
         else if (p.s == 32) launch_k(expert_kernel<OpBF16, 32>, grid, kExpertThreads, lds_bytes, s, p);

@@ -241,7 +241,9 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
 }
 
 // y rows h0 .. h0 + 64 of every token from the weighted per-slot outputs: the eight ranks in
-// rank order, then the shared slot (one float4 of one token per thread and step).
+// rank order, then the shared slot (one float4 of one token per thread and step). A pair whose
+// given id lies outside [0, E) was dropped by the bucketing, so its slot holds nothing of this
+// call: it adds zero.
 __device__ void combine_rows(const DownParams &p, int h0, int tid) {
     const bool has_shared = p.g != nullptr;
     for (int i = tid; i < p.T * 16; i += kThreads) {
@@ -254,7 +256,11 @@ __device__ void combine_rows(const DownParams &p, int h0, int tid) {
         };
         float4 v[kTopK + 1];
 #pragma unroll
-        for (int k = 0; k < kTopK; ++k) v[k] = ld4(p.ybuf + (size_t)(t * kTopK + k) * p.H + h);
+        for (int k = 0; k < kTopK; ++k) {
+            const int e = p.ids[t * kTopK + k];
+            v[k] = e >= 0 && e < p.E ? ld4(p.ybuf + (size_t)(t * kTopK + k) * p.H + h)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         v[kTopK] = has_shared ? ld4(p.ybuf + (size_t)(p.T * kTopK + t) * p.H + h)
                               : make_float4(0.f, 0.f, 0.f, 0.f);
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);

@@ -100,6 +100,7 @@ struct DownParams {
     const float *g;      // [T] or nullptr
     float *ybuf;         // [slots][H]: weighted expert outputs per (token, rank) / shared slot
     float *y;            // [T][H]
+    const int32_t *ids;  // [T][8] routing ids: a pair whose id is outside [0, E) adds nothing
     int *rb_arrivals;    // [H / 64] zero at entry; left zero
     int T, H, E, I, Is, Imax, NG;
     const float *dn_scale, *sdn_scale;  // FP8 weights: per-row scales [E][H], [H]; else null
@@ -110,8 +111,9 @@ struct CombineParams {
     const float *ypart;  // [n_sc][slots][H]
     const float *w;      // [T][8]; nullptr: the partials already carry their weights
     const float *g;      // [T] or nullptr
+    const int32_t *ids;  // [T][8] routing ids: a pair whose id is outside [0, E) adds nothing
     float *y;            // [T][H]
-    int T, H, slots, n_sc_routed, n_sc_shared, has_shared;
+    int T, H, E, slots, n_sc_routed, n_sc_shared, has_shared;
 };
 
 hipError_t launch_router(const RouterParams &p, int dtype, int maxrt, hipStream_t s);

@@ -110,12 +110,23 @@ size_t state_bytes(const moe_ctx *c) {
 // is sized for a full group, so the cap sets the gate/up kernel's blocks per CU: measured at the
 // decode shapes, 8 rows against 16: T = 16 125.6 vs 134.5 us per step, T = 32 186.2 vs 200.0,
 // T = 64 254.0 vs 270.8 (4 and 6 rows within 1 % of 8 below T = 64, worse at 64).
+// Rows are also capped so that the split kernels' LDS (the gate/up x tile plus its weight
+// stage, the down h tile plus its stage) fits the workgroup limit at every hidden size: the
+// quantized formats run only the chunked kernels, so their plan must never fall through to the
+// fused fallback kernel.
 int group_rows(const moe_ctx *c, int T) {
     const int esz = elem_bytes(c->cfg.dtype);
     const int x_stride = c->cfg.hidden + 16 / esz;
-    const int ng_lds = (int)(kMaxXTileBytes / ((size_t)x_stride * esz));
+    const size_t xrow = (size_t)x_stride * esz;
+    const int Imax = c->cfg.inter > c->cfg.shared_inter ? c->cfg.inter : c->cfg.shared_inter;
+    const size_t hrow = (size_t)(Imax + 16 / esz) * esz * (esz == 2 ? 2 : 1);
     int NG = T < 8 ? T : 8;
-    if (NG > ng_lds) NG = ng_lds;
+    const int ng_x = (int)(kMaxXTileBytes / xrow);
+    const int ng_gu = (int)((kMaxLds - gateup_stage_bytes()) / xrow);
+    const int ng_dn = (int)((kMaxLds - down_stage_bytes()) / hrow);
+    if (NG > ng_x) NG = ng_x;
+    if (NG > ng_gu) NG = ng_gu;
+    if (NG > ng_dn) NG = ng_dn;
     return NG;
 }
 
@@ -479,6 +490,7 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         dp.g = has_shared ? g_used : nullptr;
         dp.ybuf = reinterpret_cast<float *>(ws + p.o_ypart);
         dp.y = y;
+        dp.ids = ids_used;
         dp.rb_arrivals = reinterpret_cast<int *>(ws + p.o_state) + kStateRowBlocks;
         dp.NG = p.NG;
         dp.T = T;
@@ -503,9 +515,11 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
             cp.ypart = dp.ybuf;
             cp.w = nullptr;  // the slot outputs already carry their routing weight / gate
             cp.g = nullptr;
+            cp.ids = ids_used;
             cp.y = y;
             cp.T = T;
             cp.H = c->cfg.hidden;
+            cp.E = c->cfg.num_experts;
             cp.slots = p.slots;
             cp.n_sc_routed = 1;
             cp.n_sc_shared = has_shared ? 1 : 0;
@@ -516,7 +530,6 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
                 return launch_down(dp, expert_kdt(c), p.down_grid, p.down_lds, L.stream);
             });
         }
-        (void)ids_used;
         L.finish();
         if (n_kernels) *n_kernels = L.count;
         return hip_status(L.err);
@@ -547,15 +560,16 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
     cp.ypart = ep.ypart;
     cp.w = w_used;
     cp.g = has_shared ? g_used : nullptr;
+    cp.ids = ids_used;
     cp.y = y;
     cp.T = T;
     cp.H = c->cfg.hidden;
+    cp.E = c->cfg.num_experts;
     cp.slots = p.slots;
     cp.n_sc_routed = p.n_sc_routed;
     cp.n_sc_shared = p.n_sc_shared;
     cp.has_shared = has_shared ? 1 : 0;
     L.step("combine", [&] { return launch_combine(cp, L.stream); });
-    (void)ids_used;
     L.finish();
     if (n_kernels) *n_kernels = L.count;
     return hip_status(L.err);
@@ -648,6 +662,17 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
     if (p.NG < 1 || p.lds > kMaxLds) {
         delete c;
         return MOE_ERR_UNSUPPORTED;
+    }
+    // The quantized formats have no fused fallback kernel: every token count the context takes
+    // must plan the chunked kernels (8-token groups up to 64 tokens, 64-token groups above).
+    if (quant) {
+        const int t_small = cfg->max_tokens < kSplitMaxTokens ? cfg->max_tokens : kSplitMaxTokens;
+        const bool small_ok = make_plan(c, t_small).split && make_plan(c, 1).split;
+        const bool wide_ok = cfg->max_tokens <= kSplitMaxTokens || p.wide;
+        if (!small_ok || !wide_ok) {
+            delete c;
+            return MOE_ERR_UNSUPPORTED;
+        }
     }
     const Plan ps = make_plan(c, cfg->max_tokens < kSplitMaxTokens ? cfg->max_tokens : kSplitMaxTokens);
     if (ps.split && prepare_split_kernels(ps.gu_lds, ps.down_lds) != hipSuccess) {

@@ -73,9 +73,7 @@ struct WChunk {
 template <>
 struct WChunk<MxFmt> {
     static constexpr bool kMx = true;
-    static constexpr bool k8 = false;
     static constexpr int kLoads = 1;
-    static constexpr int kRowStep = 16;
     using raw_t = MxFmt::raw_t;
     __device__ static __forceinline__ int row(int lane) { return lane >> 2; }
     __device__ static __forceinline__ int elem(int lane) { return (lane & 3) * 16; }  // bytes
