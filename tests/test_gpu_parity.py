@@ -766,8 +766,10 @@ def test_quantized_large_hidden(orc, fmt, I):
     for T in (8, 64, 96):
         plan = m.plan(T)
         assert "expert" not in plan, plan
-        assert plan[-2:] == ["gateup", "down"] if T <= 64 else plan[-3:] == [
-            "gateup_wide", "down_wide", "combine"], plan
+        if T <= 64:
+            assert plan[-2:] == ["gateup", "down"], plan
+        else:
+            assert plan[-3] == "gateup_wide" and plan[-2] in ("down_wide", "down_big"), plan
         lay = dict(layer)
         lay["x"] = layer["x"][:T]
         z_o = orc.logits(lay["x"], layer["router_w"], None)
