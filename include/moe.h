@@ -154,6 +154,20 @@ int moe_forward(const moe_ctx *ctx, const void *x, int32_t T, const int32_t *ids
                 const float *w_in, const float *gate_in, float *y, void *workspace,
                 size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same kernels and results, with the
+ * workspace taken from a static device array of 8 MiB (8388608 bytes) that each GPU holds from
+ * the library's load until the process ends, in place of a caller workspace. The caller still
+ * passes x, y and the optional routing as in moe_forward. The call allocates nothing; it enqueues
+ * a zero fill of the array's state region (a kernel, so that it can be captured) before the
+ * layer's kernels. Calls whose workspace would exceed the array - moe_workspace_bytes(ctx, T)
+ * > 8 MiB, e.g. T > 64 at H = 2048, I = 512 - return MOE_ERR_WORKSPACE and enqueue nothing.
+ * Every call on one GPU shares that GPU's array (it keeps the last call's contents): calls that
+ * overlap in time on one GPU, on any streams or contexts, race and give wrong results; serialize
+ * them (one stream, or events). */
+int moe_forward_noalloc(const moe_ctx *ctx, const void *x, int32_t T, const int32_t *ids_in,
+                        const float *w_in, const float *gate_in, float *y, hipStream_t stream);
+
 /* Kernel plan of moe_forward for T tokens (routing internal iff routing_given == 0): the number
  * of kernels it enqueues, in order, and their names (static strings; up to max_names written).
  * Host-only; enqueues nothing. */

@@ -28,7 +28,8 @@ WEIGHT_KEYS = ("router_w", "router_bias", "gate_up", "down", "shared_gate_up", "
 
 EXPORTS = ("moe_create", "moe_destroy", "moe_workspace_bytes", "moe_workspace_state_bytes",
            "moe_route", "moe_bucket",
-           "moe_forward", "moe_forward_plan", "moe_forward_timed", "moe_status_str")
+           "moe_forward", "moe_forward_noalloc", "moe_forward_plan", "moe_forward_timed",
+           "moe_status_str")
 
 
 class moe_config(ctypes.Structure):
@@ -70,6 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_bucket.restype = ctypes.c_int
     lib.moe_forward.argtypes = [P, P, I32, P, P, P, P, P, SZ, P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [P, P, I32, P, P, P, P, P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_forward_plan.argtypes = [P, I32, I32, ctypes.POINTER(I32),
                                      ctypes.POINTER(ctypes.c_char_p), I32]
     lib.moe_forward_plan.restype = ctypes.c_int
@@ -207,6 +210,18 @@ class MoeLayer:
             _check(self.lib.moe_forward_timed(self.ctx, _ptr(x), T, _ptr(ids), _ptr(w), _ptr(g),
                                               _ptr(y), _ptr(ws), ws.numel(), _stream(stream),
                                               arr, len(events)), "moe_forward_timed")
+        return y
+
+    def forward_noalloc(self, x, routing=None, y=None, stream=None):
+        """moe_forward_noalloc: as forward, with the library's static scratch as workspace."""
+        import torch
+        T = x.shape[0]
+        y = torch.empty((T, self.hidden), dtype=torch.float32, device=x.device) if y is None else y
+        ids = w = g = None
+        if routing is not None:
+            ids, w, g = routing
+        _check(self.lib.moe_forward_noalloc(self.ctx, _ptr(x), T, _ptr(ids), _ptr(w), _ptr(g),
+                                            _ptr(y), _stream(stream)), "moe_forward_noalloc")
         return y
 
     def plan(self, T: int, routing_given: bool = False):

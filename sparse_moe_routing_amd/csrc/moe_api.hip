@@ -19,6 +19,7 @@
 //                 intermediate slice chunk), then combine
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/moe.h"
@@ -37,7 +38,15 @@ struct moe_ctx {
     int device;
     int num_cus;
     int s;         // intermediate slice width of the expert kernel
+    void *scratch; // device address of the static scratch array on this context's device
 };
+
+// Workspace of moe_forward_noalloc: a static device array, one copy per GPU the library runs on,
+// held until the process ends. Its name is only a host-side stand-in for the symbol: host code
+// uses the device address hipGetSymbolAddress returns for it (resolved once per device), never
+// the name itself.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -65,6 +74,29 @@ constexpr int kSplitMaxTokens = 64;   // 8-token groups up to here, 64-token gro
 constexpr int kBigMinTokens = 1536;     // bf16 from here: gateup_big in place of gateup_wide
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Device address of `scratch` on each device, resolved with that device current (moe_create).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int resolve_scratch(int dev, void **out) {
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+// Zero fill of the first n 32-bit words at p (the state region of the static scratch; a kernel
+// rather than a memset so that the call can be captured into a graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *p, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
 
 struct Plan {
     int T = 0;
@@ -393,7 +425,7 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
                  const float *w_in, const float *gate_in, float *y, void *workspace,
                  size_t ws_bytes, hipStream_t stream, hipEvent_t *events, int32_t n_events,
                  const char **names, int32_t max_names, int32_t *n_kernels, bool run,
-                 int routing_given_flag) {
+                 int routing_given_flag, bool clear_state = false) {
     if (!c) return MOE_ERR_INVALID_ARG;
     if (T < 0 || T > c->cfg.max_tokens) return MOE_ERR_INVALID_ARG;
     const bool has_shared = c->cfg.shared_inter > 0;
@@ -412,6 +444,11 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
     if (run) {
         const int st = check_call(c, T, workspace, ws_bytes, &p);
         if (st != MOE_OK) return st;
+        if (clear_state) {  // the arguments are valid: the state region starts at zero
+            const int words = (int)(state_bytes(c) / 4);
+            zero_words_kernel<<<1, 256, 0, stream>>>(static_cast<uint32_t *>(workspace), words);
+            if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+        }
     }
     char *ws = static_cast<char *>(workspace);
     Launcher L{c, stream, events, n_events, run};
@@ -674,6 +711,10 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
             return MOE_ERR_UNSUPPORTED;
         }
     }
+    if (resolve_scratch(dev, &c->scratch) != MOE_OK) {
+        delete c;
+        return MOE_ERR_HIP;
+    }
     const Plan ps = make_plan(c, cfg->max_tokens < kSplitMaxTokens ? cfg->max_tokens : kSplitMaxTokens);
     if (ps.split && prepare_split_kernels(ps.gu_lds, ps.down_lds) != hipSuccess) {
         delete c;
@@ -760,6 +801,18 @@ int moe_forward(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_i
                 size_t ws_bytes, hipStream_t stream) {
     return forward_impl(c, x, T, ids_in, w_in, gate_in, y, workspace, ws_bytes, stream, nullptr,
                         0, nullptr, 0, nullptr, true, 0);
+}
+
+int moe_forward_noalloc(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_in,
+                        const float *w_in, const float *gate_in, float *y, hipStream_t stream) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || T > c->cfg.max_tokens) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!c->scratch) return MOE_ERR_HIP;
+    // the scratch must hold this call's workspace (forward_impl checks the call's own plan too)
+    if (moe_workspace_bytes(c, T) > kScratchBytes) return MOE_ERR_WORKSPACE;
+    return forward_impl(c, x, T, ids_in, w_in, gate_in, y, c->scratch, kScratchBytes, stream,
+                        nullptr, 0, nullptr, 0, nullptr, true, 0, true);
 }
 
 int moe_forward_timed(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_in,
