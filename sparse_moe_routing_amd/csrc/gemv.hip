@@ -1,0 +1,414 @@
+// gemv.hip - the decode expert stage on the vector ALUs (matrix-vector products).
+//
+// At decode sizes each selected expert serves one or two tokens, so its gate/up and down products
+// are matrix-vector products and streaming the expert weights once from HBM is the whole cost
+// (the expert block is most of a MoE model's bytes and decode at concurrency is bandwidth-bound:
+// "RELEASE_NOTES_0.9.0" of the 16 GB ninfer fork, the expert-placement paragraphs; the lucebox
+// pull request #652 log, on decode streaming every weight byte once). Here every weight load
+// reads 1 KB of one row contiguously (lane l: bytes 16 l .. 16 l + 15 of the kilobyte), each
+// lane multiplies its eight bf16 weights by the matching activations with v_dot2_f32_bf16 (bf16
+// products, fp32 accumulation), and the 64 lane partials of a row are summed with lane moves. No
+// matrix instruction and no LDS staging of the weights.
+//
+// gateup_gemv_kernel - a wave unit is (expert group, intermediate rows 2j and 2j + 1): it reads
+//   gate rows 2j, 2j + 1 and up rows I + 2j, I + 2j + 1 (4 x H bf16, two units' rows in flight
+//   per wave) and forms h = silu(gate) * up for each token of the group, written as the two bf16
+//   planes hi = bf16(h), lo = bf16(h - hi) the down products read. The group's tokens are taken
+//   kNB at a time with the weights kept in registers. The grid's waves split the group list:
+//   with fewer groups than waves each group's units are cut into contiguous runs, one per wave
+//   (a wave loads its group's activations once); otherwise each wave takes whole groups.
+// down_rows_kernel - a block owns 4 consecutive rows of y for every token: its waves take the
+//   groups in turn, read those 4 rows of each group's down weight (4 x I bf16; the next group's
+//   rows and h are requested before the current one is computed), multiply them by the group's
+//   h and keep every (slot, row) product in LDS; the block then sums each token's eight ranks in
+//   rank order, weighted, plus its gated shared slot into y. Every output element has one writer
+//   and no step crosses blocks.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kGemvWaves = 8;
+constexpr int kGemvThreads = kGemvWaves * kWave;
+// tokens per expert group on this path (the plan's group size): the gate/up kernel keeps
+// their activations in registers, the down kernel their h rows
+constexpr int kGuNB = 4;
+constexpr int kDnNB = 4;
+constexpr int kDownRows = 8;
+
+__device__ __forceinline__ float dot8(const uint4 &w, const uint4 &x, float c) {
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x),
+                                        __builtin_bit_cast(bf16x2_t, x.x), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y),
+                                        __builtin_bit_cast(bf16x2_t, x.y), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z),
+                                        __builtin_bit_cast(bf16x2_t, x.z), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w),
+                                        __builtin_bit_cast(bf16x2_t, x.w), c, false);
+    return c;
+}
+
+// The value v of lane ^ 16 (kXor == 16) or lane ^ 32 (kXor == 32): a gfx950 permlane swap
+// returns the lane's own value in one result and the partner's in the other.
+template <int kXor>
+__device__ __forceinline__ float lane_xor(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if constexpr (kXor == 16) {
+        const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __uint_as_float(s[0] ^ s[1] ^ u);
+    } else {
+        const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float(s[0] ^ s[1] ^ u);
+    }
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), kCtrl, 0xF, 0xF,
+                                                           false));
+}
+
+// Sums over the 64 lanes of four per-lane values a0..a3: on return every lane of row group
+// g = lane / 16 holds the total of a_g (the same bits in all 16 lanes). The halves of the wave
+// first exchange the pairs they do not keep (lane ^ 32), then the rows of a pair (lane ^ 16), then
+// each 16-lane row sums with DPP moves (xor 1, xor 2, mirror in 8, mirror in 16).
+__device__ __forceinline__ float wave_sum4(float a0, float a1, float a2, float a3, int lane) {
+    const bool upper = lane >= 32;
+    float k0 = upper ? a2 : a0, k1 = upper ? a3 : a1;
+    const float s0 = upper ? a0 : a2, s1 = upper ? a1 : a3;
+    k0 += lane_xor<32>(s0);
+    k1 += lane_xor<32>(s1);
+    const bool odd = (lane & 16) != 0;
+    float k = odd ? k1 : k0;
+    k += lane_xor<16>(odd ? k0 : k1);
+    k = dpp_add<0xB1>(k);   // quad_perm [1, 0, 3, 2]
+    k = dpp_add<0x4E>(k);   // quad_perm [2, 3, 0, 1]
+    k = dpp_add<0x141>(k);  // row_half_mirror
+    k = dpp_add<0x140>(k);  // row_mirror
+    return k;
+}
+
+// Wave unit split of the group list (see the file comment): the range of groups a wave takes and,
+// for each, its range of units [j0, j1) out of S.
+struct WaveShare {
+    int g0, gstep, j0, j1;
+    __device__ WaveShare(int gw, int W, int ng, int S) {
+        if (ng <= W) {
+            const int wpg = W / ng;      // waves per group (>= 1)
+            const int gi = gw / wpg, k = gw - gi * wpg;
+            g0 = gi < ng ? gi : ng;      // past the last group: no work
+            gstep = ng;                  // one group only
+            j0 = (int)((long)k * S / wpg);
+            j1 = (int)((long)(k + 1) * S / wpg);
+        } else {
+            g0 = gw;
+            gstep = W;
+            j0 = 0;
+            j1 = S;
+        }
+    }
+};
+
+template <int KC>
+__global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(GateUpParams p) {
+    const int lane = threadIdx.x & 63;
+    // wave-uniform indices live in scalar registers, so the group table and pair indices are
+    // read through the scalar cache and never wait behind the weight stream
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = gridDim.x * kGemvWaves;
+    const int gw = blockIdx.x * kGemvWaves + wave;
+    const int ng = p.num_groups[0];
+    if (ng <= 0) return;       // no valid pair and no shared expert
+    const int S = p.Imax / 2;  // units per group (two intermediate rows each)
+    const WaveShare share(gw, W, ng, S);
+    const uint16_t *x = reinterpret_cast<const uint16_t *>(p.x);
+    uint16_t *hp = reinterpret_cast<uint16_t *>(p.h);
+
+    for (int gi = share.g0; gi < ng; gi += share.gstep) {
+        const int4 grp = p.groups[gi];
+        const int e = grp.x, start = grp.y, n = grp.z;  // n <= kGuNB (the plan's group size)
+        const bool shared = e == p.E;
+        const int Ie = shared ? p.Is : p.I;
+        const int j0 = share.j0, j1 = min(share.j1, Ie / 2);
+        if (j0 >= j1) continue;  // uniform over the wave
+        int slot[kGuNB], tok[kGuNB];
+#pragma unroll
+        for (int t = 0; t < kGuNB; ++t) {
+            const int m = t < n ? t : 0;  // past the group: a repeat of member 0, unused
+            slot[t] = shared ? p.T * kTopK + start + m : p.perm[start + m];
+            tok[t] = shared ? slot[t] - p.T * kTopK : slot[t] >> 3;
+        }
+        const uint16_t *gu = reinterpret_cast<const uint16_t *>(shared ? p.sgu : p.gate_up) +
+                             (shared ? 0 : (size_t)e * 2 * Ie * p.H) + 8 * lane;
+        // a unit past the wave's range reads the first token's x row in place of the weights
+        // (hot in cache, never used): every iteration issues the same loads, so the compiler's
+        // wait counts stay exact and two units stay in flight
+        const uint16_t *dummy = x + (size_t)tok[0] * p.H + 8 * lane;
+        // the weights of unit j: gate rows 2j, 2j + 1, up rows Ie + 2j, Ie + 2j + 1
+        auto load_w = [&](uint4 (&w)[4][KC], int j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint16_t *row =
+                    j < j1 ? gu + (size_t)((r < 2 ? 0 : Ie) + 2 * j + (r & 1)) * p.H : dummy;
+#pragma unroll
+                for (int c = 0; c < KC; ++c) w[r][c] = load16_stream(row + 512 * c);
+            }
+        };
+        uint4 xr[kGuNB][KC];
+#pragma unroll
+        for (int t = 0; t < kGuNB; ++t)
+#pragma unroll
+            for (int c = 0; c < KC; ++c) xr[t][c] = load16(x + (size_t)tok[t] * p.H + 8 * lane + 512 * c);
+        auto compute = [&](const uint4 (&w)[4][KC], int j) {
+#pragma unroll
+            for (int t = 0; t < kGuNB; ++t) {
+                if (t >= n) break;  // uniform
+                float a[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int c = 0; c < KC; ++c) s = dot8(w[r][c], xr[t][c], s);
+                    a[r] = s;
+                }
+                const float v = wave_sum4(a[0], a[1], a[2], a[3], lane);
+                // row group 0: gate 2j, 1: gate 2j + 1, 2: up 2j, 3: up 2j + 1
+                const float ga = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+                const float gb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+                const float ua = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+                const float ub = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+                if (lane == 0) {
+                    const float h0 = ga / (1.0f + expf(-ga)) * ua;
+                    const float h1 = gb / (1.0f + expf(-gb)) * ub;
+                    const uint32_t hi0 = f32_to_bf16_bits(h0), hi1 = f32_to_bf16_bits(h1);
+                    const uint32_t lo0 = f32_to_bf16_bits(h0 - bf16_bits_to_f32(hi0));
+                    const uint32_t lo1 = f32_to_bf16_bits(h1 - bf16_bits_to_f32(hi1));
+                    const size_t off = (size_t)slot[t] * p.Imax + 2 * j;
+                    *reinterpret_cast<uint32_t *>(hp + off) = hi0 | (hi1 << 16);
+                    *reinterpret_cast<uint32_t *>(hp + p.plane + off) = lo0 | (lo1 << 16);
+                }
+            }
+        };
+        uint4 wA[4][KC], wB[4][KC];
+        load_w(wA, j0);
+        load_w(wB, j0 + 1);
+        for (int j = j0; j < j1; j += 2) {
+            compute(wA, j);
+            load_w(wA, j + 2);
+            if (j + 1 < j1) compute(wB, j + 1);  // uniform; no loads inside
+            load_w(wB, j + 3);
+        }
+    }
+}
+
+// Weight formats of down_rows_kernel. A lane's piece of a row chunk is the 8 weights
+// 512 c + 8 lane .. + 7 of the row (c: the chunk of 512 weights), held as stored until the
+// compute step widens it to eight bf16 operands, exactly:
+//   kBF16  - 16 bytes of bf16 (the operands themselves);
+//   kFP8   - 8 bytes of OCP FP8 E4M3 codes (every E4M3 value is a bf16 value); the row's fp32
+//            scale multiplies the row's reduced product (scale * sum(code * h));
+//   kMXFP4 - 4 bytes of E2M1 codes (two per byte, the even weight in the low nibble) with their
+//            block's E8M0 scale byte (block (512 c + 8 lane) / 32 of the row), widened and scaled
+//            in one gfx950 conversion (exact while the product is a finite bf16).
+enum { kBF16 = 0, kFP8 = 1, kMXFP4 = 2 };
+
+template <int FMT, int KD>
+__global__ __launch_bounds__(kGemvThreads) void down_rows_kernel(DownParams p) {
+    extern __shared__ __align__(16) float obuf[];  // [slots][kDownRows]: (Wd h)[row] per slot
+    constexpr int kRing = KD == 1 ? 3 : 1;         // groups in flight per wave
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // wave-uniform indices live in scalar registers: the group table and pair indices are read
+    // through the scalar cache, so the only vector-memory loads are the weights and h rows
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r0 = blockIdx.x * kDownRows;
+    const int ng = p.num_groups[0];
+    const uint16_t *hg = reinterpret_cast<const uint16_t *>(p.h);
+
+    struct Stage {
+        uint4 w[kDownRows][KD];   // bf16: 4 words; FP8: words x, y; MXFP4: word x, scale byte y
+        uint4 hh[kDnNB][KD], hl[kDnNB][KD];
+        float s0, s1;             // FP8: the scales of rows lane / 16 and lane / 16 + 4
+    };
+    auto slot_of = [&](int e, int start, int m) {
+        return e == p.E ? p.T * kTopK + start + m : p.perm[start + m];
+    };
+    // Group gi's kDownRows rows of its down weight and the h rows of its members. Every load is
+    // issued whatever the group (so the compiler's wait counts stay exact and kRing groups stay
+    // in flight): past the last group, past the group's members, or past a narrower expert's
+    // chunks, the lanes all read the same bytes at the start of h (one cached line), and the
+    // compute step never uses those registers.
+    auto load = [&](Stage &st, int gi) {
+        const bool ok = gi < ng;
+        const int4 grp = p.groups[ok ? gi : 0];
+        const int e = grp.x, start = grp.y, n = ok ? grp.z : 0;
+        const bool shared = e == p.E;
+        const int Ie = shared ? p.Is : p.I;
+        const int kd = ok ? Ie / 512 : 0;
+        const unsigned char *base = static_cast<const unsigned char *>(shared ? p.sdn : p.down);
+        const unsigned char *dummy = reinterpret_cast<const unsigned char *>(hg);
+#pragma unroll
+        for (int r = 0; r < kDownRows; ++r)
+#pragma unroll
+            for (int c = 0; c < KD; ++c) {
+                const bool in = c < kd;
+                const size_t row = (shared ? 0 : (size_t)e * p.H) + r0 + r;  // row of [E][H]
+                if constexpr (FMT == kBF16) {
+                    const unsigned char *a = base + (row * Ie + 512 * c + 8 * lane) * 2;
+                    st.w[r][c] = load16_stream(in ? a : dummy);
+                } else if constexpr (FMT == kFP8) {
+                    const unsigned char *a = base + row * Ie + 512 * c + 8 * lane;
+                    const u32x2_t v = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x2_t *>(in ? a : dummy));
+                    st.w[r][c] = uint4{v.x, v.y, 0u, 0u};
+                } else {
+                    const unsigned char *a = base + row * (Ie / 2) + 256 * c + 4 * lane;
+                    const uint8_t *sb = (shared ? p.sdn_mx : p.dn_mx) + row * (Ie / 32) + 16 * c + lane / 4;
+                    const uint32_t v = __builtin_nontemporal_load(
+                        reinterpret_cast<const uint32_t *>(in ? a : dummy));
+                    const uint8_t *sp = in ? sb : dummy;  // one load from a selected address
+                    st.w[r][c] = uint4{v, (uint32_t)*sp, 0u, 0u};
+                }
+            }
+        if constexpr (FMT == kFP8) {
+            const float *sp = ok ? (shared ? p.sdn_scale : p.dn_scale + (size_t)e * p.H) + r0 + (lane >> 4)
+                                 : reinterpret_cast<const float *>(hg);
+            st.s0 = sp[0];
+            st.s1 = sp[ok ? 4 : 0];
+        }
+#pragma unroll
+        for (int m = 0; m < kDnNB; ++m) {
+            const bool mok = m < n;
+            const uint16_t *hs = mok ? hg + (size_t)slot_of(e, start, m) * p.Imax + 8 * lane : hg;
+#pragma unroll
+            for (int c = 0; c < KD; ++c) {
+                const bool in = mok && c < kd;
+                st.hh[m][c] = load16(in ? hs + 512 * c : hg);
+                st.hl[m][c] = load16(in ? hs + p.plane + 512 * c : hg);
+            }
+        }
+    };
+    // the eight bf16 operands of a stored piece
+    auto widen = [](const uint4 &w) -> uint4 {
+        if constexpr (FMT == kBF16) return w;
+        else if constexpr (FMT == kFP8) return e4m3x8_to_bf16x8(w.x, w.y);
+        else return e2m1x8_to_bf16x8(w.x, e8m0_to_f32(w.y));
+    };
+    // the kDownRows row products of one member's h (hi and lo planes) over the expert's kd
+    // chunks, summed over the wave: rows g and g + 4 land in row group g, which writes them
+    // (times the rows' FP8 scales)
+    auto emit = [&](const uint4 (&w)[kDownRows][KD], const uint4 (&hh)[KD], const uint4 (&hl)[KD],
+                    int kd, float s0, float s1, int slot) {
+        float a[kDownRows];
+#pragma unroll
+        for (int r = 0; r < kDownRows; ++r) {
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < KD; ++c) {
+                if (c >= kd) break;  // uniform
+                const uint4 wv = widen(w[r][c]);
+                s = dot8(wv, hh[c], s);
+                s = dot8(wv, hl[c], s);
+            }
+            a[r] = s;
+        }
+        float v0 = wave_sum4(a[0], a[1], a[2], a[3], lane);
+        float v1 = wave_sum4(a[4], a[5], a[6], a[7], lane);
+        if ((lane & 15) == 0) {
+            const int g = lane >> 4;
+            if constexpr (FMT == kFP8) {  // the row scales, read with the stage
+                v0 *= s0;
+                v1 *= s1;
+            }
+            obuf[slot * kDownRows + g] = v0;
+            obuf[slot * kDownRows + 4 + g] = v1;
+        }
+    };
+    auto compute = [&](const Stage &st, int gi) {  // no vector-memory loads: the stage holds them
+        const int4 grp = p.groups[gi];
+        const int e = grp.x, start = grp.y, n = grp.z;  // n <= kDnNB (the plan's group size)
+        const int kd = (e == p.E ? p.Is : p.I) / 512;
+#pragma unroll
+        for (int m = 0; m < kDnNB; ++m)
+            if (m < n) emit(st.w, st.hh[m], st.hl[m], kd, st.s0, st.s1, slot_of(e, start, m));
+    };
+    // a ring of kRing groups per wave: group k + kRing is requested right after group k is done
+    Stage st[kRing];
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) load(st[d], wave + d * kGemvWaves);
+    for (int k = 0; wave + k * kGemvWaves < ng; k += kRing) {
+#pragma unroll
+        for (int d = 0; d < kRing; ++d) {
+            const int gi = wave + (k + d) * kGemvWaves;
+            if (gi < ng) compute(st[d], gi);  // uniform
+            load(st[d], gi + kRing * kGemvWaves);
+        }
+    }
+    __syncthreads();
+    // y rows r0 .. r0 + kDownRows - 1: the eight ranks in rank order (weighted; a pair whose id
+    // lies outside [0, E) was dropped by the bucketing and adds nothing), then the gated shared
+    // slot
+    for (int i = tid; i < p.T * kDownRows; i += kGemvThreads) {
+        const int t = i / kDownRows, r = i - t * kDownRows;
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < kTopK; ++k) {
+            const int e = p.ids[t * kTopK + k];
+            if (e >= 0 && e < p.E) acc += p.w[t * kTopK + k] * obuf[(t * kTopK + k) * kDownRows + r];
+        }
+        if (p.g) acc += p.g[t] * obuf[(p.T * kTopK + t) * kDownRows + r];
+        p.y[(size_t)t * p.H + r0 + r] = acc;
+    }
+}
+
+int gemv_group_tokens() { return kGuNB; }
+
+// GEMV-path shapes: bf16, H a multiple of 512 up to 2048 (weight rows in whole kilobytes, at most
+// four per row held per lane), I and I_s multiples of 512 up to 1024.
+bool gemv_supported(int H, int I, int Is) {
+    const int Imax = I > Is ? I : Is;
+    return H % 512 == 0 && H <= 2048 && I % 512 == 0 && (Is == 0 || Is % 512 == 0) &&
+           Imax <= 1024;
+}
+
+// down_rows shapes: rows of y in blocks of 8, intermediate rows of whole kilobytes (bf16), at
+// most two of them per lane.
+bool down_rows_supported(int H, int I, int Is) {
+    const int Imax = I > Is ? I : Is;
+    return H % kDownRows == 0 && I % 512 == 0 && (Is == 0 || Is % 512 == 0) && Imax <= 1024;
+}
+
+// LDS of down_rows_kernel: 32 bytes per slot (at most 64 tokens: 18 KB, under the default
+// dynamic LDS limit)
+size_t down_rows_lds(int slots) { return (size_t)slots * kDownRows * sizeof(float); }
+
+hipError_t launch_gateup_gemv(const GateUpParams &p, int grid, hipStream_t s) {
+    switch (p.H / 512) {
+    case 1: launch_k(gateup_gemv_kernel<1>, grid, kGemvThreads, 0, s, p); break;
+    case 2: launch_k(gateup_gemv_kernel<2>, grid, kGemvThreads, 0, s, p); break;
+    case 3: launch_k(gateup_gemv_kernel<3>, grid, kGemvThreads, 0, s, p); break;
+    case 4: launch_k(gateup_gemv_kernel<4>, grid, kGemvThreads, 0, s, p); break;
+    default: return hipErrorInvalidValue;  // a caller bug: the plan checks gemv_supported
+    }
+    return hipGetLastError();
+}
+
+// dtype: 1 bf16, 2 FP8 E4M3, 3 MXFP4 weights (bf16 activations)
+template <int FMT>
+void launch_down_rows_fmt(const DownParams &p, int grid, size_t lds, hipStream_t s) {
+    if (p.Imax <= 512) launch_k(down_rows_kernel<FMT, 1>, grid, kGemvThreads, lds, s, p);
+    else launch_k(down_rows_kernel<FMT, 2>, grid, kGemvThreads, lds, s, p);
+}
+
+hipError_t launch_down_rows(const DownParams &p, int dtype, hipStream_t s) {
+    if (p.H % kDownRows || p.Imax > 1024) return hipErrorInvalidValue;  // a caller bug
+    const size_t lds = down_rows_lds(p.T * kTopK + (p.g ? p.T : 0));
+    const int grid = p.H / kDownRows;
+    if (dtype == 1) launch_down_rows_fmt<kBF16>(p, grid, lds, s);
+    else if (dtype == 2) launch_down_rows_fmt<kFP8>(p, grid, lds, s);
+    else if (dtype == 3) launch_down_rows_fmt<kMXFP4>(p, grid, lds, s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -17,6 +17,7 @@
 //   combine       sum of the weighted slot outputs (or partials) into y
 //   expert        shapes outside the chunked kernels: fused gate/up + SwiGLU + down per (group,
 //                 intermediate slice chunk), then combine
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -38,6 +39,7 @@ struct moe_ctx {
     int device;
     int num_cus;
     int s;         // intermediate slice width of the expert kernel
+    int gemv_max_tokens;  // decode rounds up to this T run the vector-ALU expert kernels
     void *scratch; // device address of the static scratch array on this context's device
 };
 
@@ -72,6 +74,7 @@ constexpr int kHistChunk = 16;
 constexpr int kSelBucketMaxTokens = 256;
 constexpr int kSplitMaxTokens = 64;   // 8-token groups up to here, 64-token groups above
 constexpr int kBigMinTokens = 1536;     // bf16 from here: gateup_big in place of gateup_wide
+
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -110,6 +113,8 @@ struct Plan {
     bool wide = false;           // T > 64: gateup_wide + down_wide + combine, 64-token groups
     bool big = false;            // wide, bf16 or FP8, T >= kBigMinTokens: gateup_big for gateup_wide
     bool down_big = false;       // wide, bf16 or FP8, H a multiple of 512, T <= 256 or big
+    bool gemv = false;           // split, bf16: gateup_gemv in place of gateup
+    bool down_rows = false;      // split, bf16: down_rows in place of down
     int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;
     size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
@@ -179,11 +184,21 @@ Plan make_plan(const moe_ctx *c, int T) {
     // x-tile rows: up to 8 tokens, fewer when a row of H elements would not leave room in LDS
     const int esz = elem_bytes(cfg.dtype);
     p.x_stride = H + 16 / esz;
-    const int ng_x = group_rows(c, T);  // x-tile rows of the split and fused expert kernels
     // the split and wide kernels stream weight rows in chunks of 16 x 16 bytes (128 bf16 / 64 fp32)
     const int chunk = act_dtype(cfg.dtype) == MOE_BF16 ? 128 : 64;
     const bool chunk_ok = I % chunk == 0 && Is % chunk == 0;
     p.wide = T > kSplitMaxTokens && chunk_ok;
+    // bf16 decode rounds (T <= 64) end with down_rows (vector-ALU down products of the rows a
+    // block owns, combined in the block: no per-slot buffer, no arrival counters; measured
+    // faster than the matrix-core down kernel at every T from 1 to 32), whose groups hold at most
+    // 4 tokens (their h rows stay in registers); the vector-ALU gate/up kernel is used up to
+    // gemv_max_tokens (0 unless MOE_GEMV_MAX_TOKENS sets it: the matrix-core gate/up kernel is as
+    // fast or faster from 3 tokens up, and one gate/up kernel for every decode T keeps a token's
+    // bits independent of its batch)
+    p.gemv = cfg.dtype == MOE_BF16 && T <= c->gemv_max_tokens && gemv_supported(H, I, Is);
+    p.down_rows = cfg.dtype != MOE_F32 && T <= kSplitMaxTokens && down_rows_supported(H, I, Is);
+    int ng_x = group_rows(c, T);  // x-tile rows of the split and fused expert kernels
+    if ((p.gemv || p.down_rows) && ng_x > gemv_group_tokens()) ng_x = gemv_group_tokens();
     p.NG = p.wide ? wide_group_tokens() : ng_x;
     p.n_chunks = p.small ? 0 : (T + kHistChunk - 1) / kHistChunk;
     const int pairs = T * 8;
@@ -205,6 +220,8 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.down_lds = (size_t)ng_x * (Imax + 16 / esz) * esz * (esz == 2 ? 2 : 1) +
                  down_stage_bytes();
     p.split = T <= kSplitMaxTokens && p.gu_lds <= kMaxLds && p.down_lds <= kMaxLds && chunk_ok;
+    if (p.gemv) p.split = true;
+    if (!p.split) p.gemv = p.down_rows = false;
     if (p.wide) {
         const int dr = wide_rows_per_down_unit(), gr = wide_rows_per_gateup_unit();
         const long d_units = (long)p.max_groups * ((H + dr - 1) / dr);
@@ -268,7 +285,8 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.o_groups = take((size_t)p.max_groups * 16);
     p.o_ngroups = take(16);
     const bool per_slot = p.split || p.wide;  // [slots][H] weighted outputs and an h buffer
-    p.o_ypart = take(per_slot ? (size_t)p.slots * H * 4 : (size_t)p.n_sc * p.slots * H * 4);
+    p.o_ypart = take(p.down_rows ? 0 : per_slot ? (size_t)p.slots * H * 4
+                                                : (size_t)p.n_sc * p.slots * H * 4);
     p.o_h = take(per_slot ? (size_t)p.slots * Imax * 4 : 0);
     p.total = o;
     return p;
@@ -505,7 +523,9 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         gp.sgu_scale = mx ? nullptr : static_cast<const float *>(c->w.shared_gate_up_scale);
         gp.gu_mx = mx ? static_cast<const uint8_t *>(c->w.gate_up_scale) : nullptr;
         gp.sgu_mx = mx ? static_cast<const uint8_t *>(c->w.shared_gate_up_scale) : nullptr;
-        if (p.big)
+        if (p.gemv)
+            L.step("gateup_gemv", [&] { return launch_gateup_gemv(gp, c->num_cus, L.stream); });
+        else if (p.big)
             L.step("gateup_big", [&] { return launch_gateup_big(gp, expert_kdt(c), p.gu_grid, L.stream); });
         else if (p.wide)
             L.step("gateup_wide", [&] {
@@ -540,6 +560,12 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         dp.sdn_scale = mx ? nullptr : static_cast<const float *>(c->w.shared_down_scale);
         dp.dn_mx = mx ? static_cast<const uint8_t *>(c->w.down_scale) : nullptr;
         dp.sdn_mx = mx ? static_cast<const uint8_t *>(c->w.shared_down_scale) : nullptr;
+        if (p.down_rows) {
+            L.step("down_rows", [&] { return launch_down_rows(dp, expert_kdt(c), L.stream); });
+            L.finish();
+            if (n_kernels) *n_kernels = L.count;
+            return hip_status(L.err);
+        }
         if (p.down_big) {
             L.step("down_big", [&] { return launch_down_big(dp, expert_kdt(c), p.down_grid, L.stream); });
         } else if (p.wide) {
@@ -625,6 +651,44 @@ int expert_kdt(const moe_ctx *c) {
                                          : c->cfg.dtype == MOE_BF16 ? 1 : 0;
 }
 
+// The kernels' dynamic-LDS caps (hipFuncAttributeMaxDynamicSharedMemorySize) are process-wide:
+// they only ever grow, to the largest any context has needed, so that creating a context never
+// lowers a cap another context's launches rely on.
+std::mutex g_lds_mu;
+size_t g_split_gu_lds, g_split_down_lds, g_expert_lds;
+bool g_wide_ready;
+
+hipError_t raise_lds_caps(const moe_ctx *c, const Plan &p_max) {
+    std::lock_guard<std::mutex> lock(g_lds_mu);
+    hipError_t err = hipSuccess;
+    size_t gu = 0, dn = 0;
+    const int tmax = c->cfg.max_tokens < kSplitMaxTokens ? c->cfg.max_tokens : kSplitMaxTokens;
+    for (int T : {1, 4, 8, tmax}) {  // the decode plans' LDS needs grow with T up to 8 tokens
+        if (T > tmax) continue;
+        const Plan q = make_plan(c, T);
+        if (q.split) {
+            gu = q.gu_lds > gu ? q.gu_lds : gu;
+            dn = q.down_lds > dn ? q.down_lds : dn;
+        }
+    }
+    if (gu > g_split_gu_lds || dn > g_split_down_lds) {
+        const size_t ngu = gu > g_split_gu_lds ? gu : g_split_gu_lds;
+        const size_t ndn = dn > g_split_down_lds ? dn : g_split_down_lds;
+        if ((err = prepare_split_kernels(ngu, ndn)) != hipSuccess) return err;
+        g_split_gu_lds = ngu;
+        g_split_down_lds = ndn;
+    }
+    if (p_max.lds > g_expert_lds) {
+        if ((err = prepare_expert_kernels(p_max.lds)) != hipSuccess) return err;
+        g_expert_lds = p_max.lds;
+    }
+    if (!g_wide_ready) {
+        if ((err = prepare_wide_kernels()) != hipSuccess) return err;
+        g_wide_ready = true;
+    }
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -692,6 +756,16 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
     c->R = cfg->num_experts + (has_shared ? 1 : 0);
     c->device = dev;
     c->num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+    c->gemv_max_tokens = 0;
+    if (const char *env = getenv("MOE_GEMV_MAX_TOKENS")) {
+        char *end = nullptr;
+        const long v = strtol(env, &end, 10);
+        if (end == env || *end != '\0' || v < 0 || v > kSplitMaxTokens) {
+            delete c;
+            return MOE_ERR_INVALID_ARG;
+        }
+        c->gemv_max_tokens = (int)v;
+    }
     const int Is = cfg->shared_inter;
     c->s = (cfg->inter % 64 == 0 && Is % 64 == 0) ? 64 : (cfg->inter % 32 == 0 && Is % 32 == 0) ? 32 : 16;
     // largest LDS any plan of this context asks for (x tile of up to 16 rows + h tile)
@@ -715,12 +789,7 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
         delete c;
         return MOE_ERR_HIP;
     }
-    const Plan ps = make_plan(c, cfg->max_tokens < kSplitMaxTokens ? cfg->max_tokens : kSplitMaxTokens);
-    if (ps.split && prepare_split_kernels(ps.gu_lds, ps.down_lds) != hipSuccess) {
-        delete c;
-        return MOE_ERR_HIP;
-    }
-    if (prepare_expert_kernels(p.lds) != hipSuccess || prepare_wide_kernels() != hipSuccess) {
+    if (raise_lds_caps(c, p) != hipSuccess) {
         delete c;
         return MOE_ERR_HIP;
     }

@@ -49,6 +49,10 @@ def main():
     ap.add_argument("--pool", type=int, default=8)
     ap.add_argument("--skewed", action="store_true",
                     help="per-expert router bias ~ N(0, 2) (the verify workload's routing)")
+    ap.add_argument("--paths", default="default",
+                    help="comma list of decode expert paths to time per T: default (the "
+                         "library's plan), gemv (vector-ALU kernels up to 64 tokens), mfma "
+                         "(matrix-core kernels only)")
     args = ap.parse_args()
     import torch
     from sparse_moe_routing_amd import binding, inputs
@@ -66,8 +70,22 @@ def main():
     pool = [torch.randn((w.tokens, H), generator=gen, device="cuda").to(torch.bfloat16)
             for _ in range(args.pool)]
     stream = torch.cuda.current_stream()
+    # contexts over the same weight sets per decode path: the plan boundary is read from
+    # MOE_GEMV_MAX_TOKENS when a context is created
+    limits = {"default": None, "gemv": "64", "mfma": "0"}
+    path_sets = {}
+    for name in args.paths.split(","):
+        old = os.environ.pop("MOE_GEMV_MAX_TOKENS", None)
+        if limits[name] is not None:
+            os.environ["MOE_GEMV_MAX_TOKENS"] = limits[name]
+        path_sets[name] = [(binding.MoeLayer(H, w.num_experts, w.inter, w.shared_inter, w.tokens,
+                                             w.dtype, t), t) for _, t in sets]
+        os.environ.pop("MOE_GEMV_MAX_TOKENS", None)
+        if old is not None:
+            os.environ["MOE_GEMV_MAX_TOKENS"] = old
     rows = []
-    for T in Ts:
+    for T, path in [(T, path) for T in Ts for path in path_sets]:
+        sets = path_sets[path]
         wt = dataclasses.replace(w, tokens=T)
         m0 = sets[0][0]
         ws = m0.workspace(T)
@@ -107,7 +125,7 @@ def main():
                       * 1e3 for k, name in enumerate(plan)}
         mean_U = float(np.mean([U[c] for c in used]))
         step_b = float(np.mean([bench.step_bytes(wt, U[c]) for c in used]))
-        row = {"T": T, "plan": plan, "us_per_step": us, "tokens_per_s": T / (us * 1e-6),
+        row = {"T": T, "path": path, "plan": plan, "us_per_step": us, "tokens_per_s": T / (us * 1e-6),
                "mean_U": mean_U, "step_bytes": step_b, "gbs": step_b / (us * 1e-6) / 1e9,
                "hbm_frac": step_b / (us * 1e-6) / 1e9 / bench.HBM_PEAK_GBS,
                "per_kernel_us": per_kernel}
@@ -118,7 +136,8 @@ def main():
     print("|---|---|---|---|---|---|---|---|---|")
     for r in rows:
         ks = ", ".join(f"{k} {v:.1f}" for k, v in r["per_kernel_us"].items())
-        print(f"| {r['T']} | {'+'.join(r['plan'])} | {r['us_per_step']:.1f} | "
+        print(f"| {r['T']} | {'+'.join(r['plan'][-2:] if len(r['plan']) > 2 else r['plan'])} | "
+              f"{r['us_per_step']:.1f} | "
               f"{r['tokens_per_s'] / 1e3:.1f} k | {r['mean_U']:.1f} | {r['step_bytes'] / 1e6:.1f} | "
               f"{r['gbs']:.0f} | {100 * r['hbm_frac']:.1f} | {ks} |")
 
