@@ -109,14 +109,9 @@ struct WaveShare {
     }
 };
 
+// The gate/up units of wave gw of W.
 template <int KC>
-__global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(GateUpParams p) {
-    const int lane = threadIdx.x & 63;
-    // wave-uniform indices live in scalar registers, so the group table and pair indices are
-    // read through the scalar cache and never wait behind the weight stream
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int W = gridDim.x * kGemvWaves;
-    const int gw = blockIdx.x * kGemvWaves + wave;
+__device__ __forceinline__ void gateup_gemv_waves(const GateUpParams &p, int gw, int W, int lane) {
     const int ng = p.num_groups[0];
     if (ng <= 0) return;       // no valid pair and no shared expert
     const int S = p.Imax / 2;  // units per group (two intermediate rows each)
@@ -184,8 +179,10 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(GateUpParams 
                     const uint32_t lo0 = f32_to_bf16_bits(h0 - bf16_bits_to_f32(hi0));
                     const uint32_t lo1 = f32_to_bf16_bits(h1 - bf16_bits_to_f32(hi1));
                     const size_t off = (size_t)slot[t] * p.Imax + 2 * j;
-                    *reinterpret_cast<uint32_t *>(hp + off) = hi0 | (hi1 << 16);
-                    *reinterpret_cast<uint32_t *>(hp + p.plane + off) = lo0 | (lo1 << 16);
+                    uint32_t *h_hi = reinterpret_cast<uint32_t *>(hp + off);
+                    uint32_t *h_lo = reinterpret_cast<uint32_t *>(hp + p.plane + off);
+                    *h_hi = hi0 | (hi1 << 16);
+                    *h_lo = lo0 | (lo1 << 16);
                 }
             }
         };
@@ -201,6 +198,15 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(GateUpParams 
     }
 }
 
+template <int KC>
+__global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(GateUpParams p) {
+    // wave-uniform indices live in scalar registers, so the group table and pair indices are
+    // read through the scalar cache and never wait behind the weight stream
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    gateup_gemv_waves<KC>(p, blockIdx.x * kGemvWaves + wave, gridDim.x * kGemvWaves,
+                          threadIdx.x & 63);
+}
+
 // Weight formats of down_rows_kernel. A lane's piece of a row chunk is the 8 weights
 // 512 c + 8 lane .. + 7 of the row (c: the chunk of 512 weights), held as stored until the
 // compute step widens it to eight bf16 operands, exactly:
@@ -212,16 +218,17 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(GateUpParams 
 //            in one gfx950 conversion (exact while the product is a finite bf16).
 enum { kBF16 = 0, kFP8 = 1, kMXFP4 = 2 };
 
-template <int FMT, int KD>
-__global__ __launch_bounds__(kGemvThreads) void down_rows_kernel(DownParams p) {
-    extern __shared__ __align__(16) float obuf[];  // [slots][kDownRows]: (Wd h)[row] per slot
+// The down rows of block blk (rows 8 blk .. 8 blk + 7 of y for every token) into LDS obuf, then
+// y, with NW waves.
+template <int FMT, int KD, int NW = kGemvWaves>
+__device__ __forceinline__ void down_rows_block(const DownParams &p, int blk, float *obuf) {
     constexpr int kRing = KD == 1 ? 3 : 1;         // groups in flight per wave
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // wave-uniform indices live in scalar registers: the group table and pair indices are read
     // through the scalar cache, so the only vector-memory loads are the weights and h rows
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r0 = blockIdx.x * kDownRows;
+    const int r0 = blk * kDownRows;
     const int ng = p.num_groups[0];
     const uint16_t *hg = reinterpret_cast<const uint16_t *>(p.h);
 
@@ -233,15 +240,14 @@ __global__ __launch_bounds__(kGemvThreads) void down_rows_kernel(DownParams p) {
     auto slot_of = [&](int e, int start, int m) {
         return e == p.E ? p.T * kTopK + start + m : p.perm[start + m];
     };
-    // Group gi's kDownRows rows of its down weight and the h rows of its members. Every load is
-    // issued whatever the group (so the compiler's wait counts stay exact and kRing groups stay
-    // in flight): past the last group, past the group's members, or past a narrower expert's
-    // chunks, the lanes all read the same bytes at the start of h (one cached line), and the
-    // compute step never uses those registers.
-    auto load = [&](Stage &st, int gi) {
+    // Group gi's kDownRows rows of its down weight (with FP8 row scales). Every weight load is
+    // issued whatever the group, so that the compiler's wait counts stay exact and kRing groups
+    // stay in flight: past the last group or past a narrower expert's chunks the lanes all read
+    // the same bytes at the start of h (one cached line), and the compute step never uses them.
+    auto load_w = [&](Stage &st, int gi) {
         const bool ok = gi < ng;
         const int4 grp = p.groups[ok ? gi : 0];
-        const int e = grp.x, start = grp.y, n = ok ? grp.z : 0;
+        const int e = grp.x;
         const bool shared = e == p.E;
         const int Ie = shared ? p.Is : p.I;
         const int kd = ok ? Ie / 512 : 0;
@@ -276,15 +282,24 @@ __global__ __launch_bounds__(kGemvThreads) void down_rows_kernel(DownParams p) {
             st.s0 = sp[0];
             st.s1 = sp[ok ? 4 : 0];
         }
+    };
+    // The h rows of the group's members: only those the group has (a uniform condition; dummy
+    // reads for the absent members measured 2.5 us of the T = 4 down pass). A stage issues these
+    // before its weight loads, which are unconditional, so the wait counts still cover the ring.
+    auto load_h = [&](Stage &st, int gi) {
+        const bool ok = gi < ng;
+        const int4 grp = p.groups[ok ? gi : 0];
+        const int e = grp.x, start = grp.y, n = ok ? grp.z : 0;
+        const int kd = ok ? (e == p.E ? p.Is : p.I) / 512 : 0;
 #pragma unroll
         for (int m = 0; m < kDnNB; ++m) {
-            const bool mok = m < n;
-            const uint16_t *hs = mok ? hg + (size_t)slot_of(e, start, m) * p.Imax + 8 * lane : hg;
+            if (m >= n) break;  // uniform
+            const uint16_t *hs = hg + (size_t)slot_of(e, start, m) * p.Imax + 8 * lane;
 #pragma unroll
             for (int c = 0; c < KD; ++c) {
-                const bool in = mok && c < kd;
-                st.hh[m][c] = load16(in ? hs + 512 * c : hg);
-                st.hl[m][c] = load16(in ? hs + p.plane + 512 * c : hg);
+                if (c >= kd) break;  // uniform
+                st.hh[m][c] = load16(hs + 512 * c);
+                st.hl[m][c] = load16(hs + p.plane + 512 * c);
             }
         }
     };
@@ -335,20 +350,24 @@ __global__ __launch_bounds__(kGemvThreads) void down_rows_kernel(DownParams p) {
     // a ring of kRing groups per wave: group k + kRing is requested right after group k is done
     Stage st[kRing];
 #pragma unroll
-    for (int d = 0; d < kRing; ++d) load(st[d], wave + d * kGemvWaves);
-    for (int k = 0; wave + k * kGemvWaves < ng; k += kRing) {
+    for (int d = 0; d < kRing; ++d) {
+        load_h(st[d], wave + d * NW);
+        load_w(st[d], wave + d * NW);
+    }
+    for (int k = 0; wave + k * NW < ng; k += kRing) {
 #pragma unroll
         for (int d = 0; d < kRing; ++d) {
-            const int gi = wave + (k + d) * kGemvWaves;
+            const int gi = wave + (k + d) * NW;
             if (gi < ng) compute(st[d], gi);  // uniform
-            load(st[d], gi + kRing * kGemvWaves);
+            load_h(st[d], gi + kRing * NW);
+            load_w(st[d], gi + kRing * NW);
         }
     }
     __syncthreads();
     // y rows r0 .. r0 + kDownRows - 1: the eight ranks in rank order (weighted; a pair whose id
     // lies outside [0, E) was dropped by the bucketing and adds nothing), then the gated shared
     // slot
-    for (int i = tid; i < p.T * kDownRows; i += kGemvThreads) {
+    for (int i = tid; i < p.T * kDownRows; i += NW * kWave) {
         const int t = i / kDownRows, r = i - t * kDownRows;
         float acc = 0.f;
 #pragma unroll
@@ -360,6 +379,13 @@ __global__ __launch_bounds__(kGemvThreads) void down_rows_kernel(DownParams p) {
         p.y[(size_t)t * p.H + r0 + r] = acc;
     }
 }
+
+template <int FMT, int KD>
+__global__ __launch_bounds__(kGemvThreads) void down_rows_kernel(DownParams p) {
+    extern __shared__ __align__(16) float obuf[];  // [slots][kDownRows]: (Wd h)[row] per slot
+    down_rows_block<FMT, KD>(p, blockIdx.x, obuf);
+}
+
 
 int gemv_group_tokens() { return kGuNB; }
 

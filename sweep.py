@@ -51,8 +51,8 @@ def main():
                     help="per-expert router bias ~ N(0, 2) (the verify workload's routing)")
     ap.add_argument("--paths", default="default",
                     help="comma list of decode expert paths to time per T: default (the "
-                         "library's plan), gemv (vector-ALU kernels up to 64 tokens), mfma "
-                         "(matrix-core kernels only)")
+                         "library's plan), gemv (vector-ALU gate/up and down), mfma "
+                         "(matrix-core gate/up, vector-ALU down)")
     args = ap.parse_args()
     import torch
     from sparse_moe_routing_amd import binding, inputs
@@ -72,17 +72,19 @@ def main():
     stream = torch.cuda.current_stream()
     # contexts over the same weight sets per decode path: the plan boundary is read from
     # MOE_GEMV_MAX_TOKENS when a context is created
-    limits = {"default": None, "gemv": "64", "mfma": "0"}
+    # the plan knob each path sets: MOE_GEMV_MAX_TOKENS (vector-ALU gate/up up to that T)
+    knobs = {"default": {}, "gemv": {"MOE_GEMV_MAX_TOKENS": "64"},
+             "mfma": {"MOE_GEMV_MAX_TOKENS": "0"}}
     path_sets = {}
     for name in args.paths.split(","):
-        old = os.environ.pop("MOE_GEMV_MAX_TOKENS", None)
-        if limits[name] is not None:
-            os.environ["MOE_GEMV_MAX_TOKENS"] = limits[name]
+        saved = {k: os.environ.pop(k, None) for k in ("MOE_GEMV_MAX_TOKENS",)}
+        os.environ.update(knobs[name])
         path_sets[name] = [(binding.MoeLayer(H, w.num_experts, w.inter, w.shared_inter, w.tokens,
                                              w.dtype, t), t) for _, t in sets]
-        os.environ.pop("MOE_GEMV_MAX_TOKENS", None)
-        if old is not None:
-            os.environ["MOE_GEMV_MAX_TOKENS"] = old
+        for k, v in saved.items():
+            os.environ.pop(k, None)
+            if v is not None:
+                os.environ[k] = v
     rows = []
     for T, path in [(T, path) for T in Ts for path in path_sets]:
         sets = path_sets[path]

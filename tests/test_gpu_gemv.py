@@ -36,15 +36,17 @@ def orc():
 
 @contextlib.contextmanager
 def gemv_limit(value):
-    old = os.environ.get("MOE_GEMV_MAX_TOKENS")
+    """Contexts created inside take the vector-ALU gate/up up to `value` tokens."""
+    saved = {k: os.environ.get(k) for k in ("MOE_GEMV_MAX_TOKENS",)}
     os.environ["MOE_GEMV_MAX_TOKENS"] = str(value)
     try:
         yield
     finally:
-        if old is None:
-            del os.environ["MOE_GEMV_MAX_TOKENS"]
-        else:
-            os.environ["MOE_GEMV_MAX_TOKENS"] = old
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def assert_close(gpu, ref, what):

@@ -524,7 +524,7 @@ def test_batch_invariance_bitwise():
     z4, ids4, _, _ = m.route(x=x[:4].contiguous())
     z384, ids384, _, _ = m.route(x=big)
     torch.cuda.synchronize()
-    assert m.plan(64)[-1] == "down_rows" and m.plan(65)[-1] != "down_rows"
+    assert m.plan(64)[-1] == "down_rows" and m.plan(65)[-1] == "combine"
     assert torch.equal(z32[:4], z4) and torch.equal(ids32[:4], ids4)
     assert torch.equal(z384[:32], z32) and torch.equal(ids384[352:], ids32)
     assert torch.equal(y32[:4], y4)
