@@ -109,8 +109,52 @@ struct WaveShare {
     }
 };
 
+// Weight formats of the vector-ALU kernels. A lane's piece of a row chunk is the 8 weights
+// 512 c + 8 lane .. + 7 of the row (c: the chunk of 512 weights), held as stored until the
+// compute step widens it to eight bf16 operands, exactly:
+//   kBF16  - 16 bytes of bf16 (the operands themselves);
+//   kFP8   - 8 bytes of OCP FP8 E4M3 codes (every E4M3 value is a bf16 value); the row's fp32
+//            scale multiplies the row's reduced product (scale * sum(code * operand));
+//   kMXFP4 - 4 bytes of E2M1 codes (two per byte, the even weight in the low nibble) with their
+//            block's E8M0 scale byte (block (512 c + 8 lane) / 32 of the row), widened and scaled
+//            in one gfx950 conversion (exact while the product is a finite bf16).
+// Every format gives each lane the same weights, so the products and their order are the bf16
+// kernel's: on weights a bf16 context holds exactly (every MXFP4 weight; FP8 under power-of-two
+// row scales) the outputs are the same bits.
+enum { kBF16 = 0, kFP8 = 1, kMXFP4 = 2 };
+
+// The stored piece of row `row` (element offset of the row in its matrix) and chunk c for this
+// lane; `dummy` (cached, never used) in place of a piece past the range.
+template <int FMT>
+__device__ __forceinline__ uint4 load_piece(const void *mat, const uint8_t *mx, size_t row, int cols,
+                                            int c, int lane, bool in, const void *dummy) {
+    const unsigned char *d = static_cast<const unsigned char *>(dummy);
+    if constexpr (FMT == kBF16) {
+        const unsigned char *a = static_cast<const unsigned char *>(mat) + (row * cols + 512 * c + 8 * lane) * 2;
+        return load16_stream(in ? a : d);
+    } else if constexpr (FMT == kFP8) {
+        const unsigned char *a = static_cast<const unsigned char *>(mat) + row * cols + 512 * c + 8 * lane;
+        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(in ? a : d));
+        return uint4{v.x, v.y, 0u, 0u};
+    } else {
+        const unsigned char *a = static_cast<const unsigned char *>(mat) + row * (cols / 2) + 256 * c + 4 * lane;
+        const uint8_t *sb = mx + row * (cols / 32) + 16 * c + lane / 4;
+        const uint32_t v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(in ? a : d));
+        const uint8_t *sp = in ? sb : d;  // one load from a selected address
+        return uint4{v, (uint32_t)*sp, 0u, 0u};
+    }
+}
+
+// The eight bf16 operands of a stored piece.
+template <int FMT>
+__device__ __forceinline__ uint4 widen(const uint4 &w) {
+    if constexpr (FMT == kBF16) return w;
+    else if constexpr (FMT == kFP8) return e4m3x8_to_bf16x8(w.x, w.y);
+    else return e2m1x8_to_bf16x8(w.x, e8m0_to_f32(w.y));
+}
+
 // The gate/up units of wave gw of W.
-template <int KC>
+template <int FMT, int KC>
 __device__ __forceinline__ void gateup_gemv_waves(const GateUpParams &p, int gw, int W, int lane) {
     const int ng = p.num_groups[0];
     if (ng <= 0) return;       // no valid pair and no shared expert
@@ -133,20 +177,30 @@ __device__ __forceinline__ void gateup_gemv_waves(const GateUpParams &p, int gw,
             slot[t] = shared ? p.T * kTopK + start + m : p.perm[start + m];
             tok[t] = shared ? slot[t] - p.T * kTopK : slot[t] >> 3;
         }
-        const uint16_t *gu = reinterpret_cast<const uint16_t *>(shared ? p.sgu : p.gate_up) +
-                             (shared ? 0 : (size_t)e * 2 * Ie * p.H) + 8 * lane;
+        const void *gu = shared ? p.sgu : p.gate_up;
+        const uint8_t *gmx = shared ? p.sgu_mx : p.gu_mx;
+        const size_t row0 = shared ? 0 : (size_t)e * 2 * Ie;  // the expert's first row
         // a unit past the wave's range reads the first token's x row in place of the weights
         // (hot in cache, never used): every iteration issues the same loads, so the compiler's
         // wait counts stay exact and two units stay in flight
         const uint16_t *dummy = x + (size_t)tok[0] * p.H + 8 * lane;
         // the weights of unit j: gate rows 2j, 2j + 1, up rows Ie + 2j, Ie + 2j + 1
-        auto load_w = [&](uint4 (&w)[4][KC], int j) {
+        // FP8: lane l also reads the scale of row l & 3 of the unit, a vector load in the same
+        // queue as the weights (scalar loads of the scales would each wait for every scalar
+        // load in flight)
+        const float *gsc = shared ? p.sgu_scale : p.gu_scale + row0;
+        auto load_w = [&](uint4 (&w)[4][KC], float &sc, int j) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const uint16_t *row =
-                    j < j1 ? gu + (size_t)((r < 2 ? 0 : Ie) + 2 * j + (r & 1)) * p.H : dummy;
+                const size_t row = row0 + (r < 2 ? 0 : Ie) + 2 * j + (r & 1);
 #pragma unroll
-                for (int c = 0; c < KC; ++c) w[r][c] = load16_stream(row + 512 * c);
+                for (int c = 0; c < KC; ++c)
+                    w[r][c] = load_piece<FMT>(gu, gmx, row, p.H, c, lane, j < j1, dummy);
+            }
+            if constexpr (FMT == kFP8) {
+                const int r = lane & 3;
+                const float *a = gsc + ((r < 2 ? 0 : Ie) + 2 * j + (r & 1));
+                sc = *(j < j1 ? a : reinterpret_cast<const float *>(dummy));
             }
         };
         uint4 xr[kGuNB][KC];
@@ -154,7 +208,7 @@ __device__ __forceinline__ void gateup_gemv_waves(const GateUpParams &p, int gw,
         for (int t = 0; t < kGuNB; ++t)
 #pragma unroll
             for (int c = 0; c < KC; ++c) xr[t][c] = load16(x + (size_t)tok[t] * p.H + 8 * lane + 512 * c);
-        auto compute = [&](const uint4 (&w)[4][KC], int j) {
+        auto compute = [&](const uint4 (&w)[4][KC], float scv, int j) {
 #pragma unroll
             for (int t = 0; t < kGuNB; ++t) {
                 if (t >= n) break;  // uniform
@@ -163,15 +217,21 @@ __device__ __forceinline__ void gateup_gemv_waves(const GateUpParams &p, int gw,
                 for (int r = 0; r < 4; ++r) {
                     float s = 0.f;
 #pragma unroll
-                    for (int c = 0; c < KC; ++c) s = dot8(w[r][c], xr[t][c], s);
+                    for (int c = 0; c < KC; ++c) s = dot8(widen<FMT>(w[r][c]), xr[t][c], s);
                     a[r] = s;
                 }
                 const float v = wave_sum4(a[0], a[1], a[2], a[3], lane);
                 // row group 0: gate 2j, 1: gate 2j + 1, 2: up 2j, 3: up 2j + 1
-                const float ga = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-                const float gb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-                const float ua = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-                const float ub = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+                float ga = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+                float gb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+                float ua = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+                float ub = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+                if constexpr (FMT == kFP8) {  // the rows' scales, from lanes 0 .. 3
+                    ga *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv), 0));
+                    gb *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv), 1));
+                    ua *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv), 2));
+                    ub *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scv), 3));
+                }
                 if (lane == 0) {
                     const float h0 = ga / (1.0f + expf(-ga)) * ua;
                     const float h1 = gb / (1.0f + expf(-gb)) * ub;
@@ -179,44 +239,33 @@ __device__ __forceinline__ void gateup_gemv_waves(const GateUpParams &p, int gw,
                     const uint32_t lo0 = f32_to_bf16_bits(h0 - bf16_bits_to_f32(hi0));
                     const uint32_t lo1 = f32_to_bf16_bits(h1 - bf16_bits_to_f32(hi1));
                     const size_t off = (size_t)slot[t] * p.Imax + 2 * j;
-                    uint32_t *h_hi = reinterpret_cast<uint32_t *>(hp + off);
-                    uint32_t *h_lo = reinterpret_cast<uint32_t *>(hp + p.plane + off);
-                    *h_hi = hi0 | (hi1 << 16);
-                    *h_lo = lo0 | (lo1 << 16);
+                    *reinterpret_cast<uint32_t *>(hp + off) = hi0 | (hi1 << 16);
+                    *reinterpret_cast<uint32_t *>(hp + p.plane + off) = lo0 | (lo1 << 16);
                 }
             }
         };
         uint4 wA[4][KC], wB[4][KC];
-        load_w(wA, j0);
-        load_w(wB, j0 + 1);
+        float sA = 1.f, sB = 1.f;
+        load_w(wA, sA, j0);
+        load_w(wB, sB, j0 + 1);
         for (int j = j0; j < j1; j += 2) {
-            compute(wA, j);
-            load_w(wA, j + 2);
-            if (j + 1 < j1) compute(wB, j + 1);  // uniform; no loads inside
-            load_w(wB, j + 3);
+            compute(wA, sA, j);
+            load_w(wA, sA, j + 2);
+            if (j + 1 < j1) compute(wB, sB, j + 1);  // uniform; no vector-memory loads inside
+            load_w(wB, sB, j + 3);
         }
     }
 }
 
-template <int KC>
+template <int FMT, int KC>
 __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(GateUpParams p) {
     // wave-uniform indices live in scalar registers, so the group table and pair indices are
     // read through the scalar cache and never wait behind the weight stream
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    gateup_gemv_waves<KC>(p, blockIdx.x * kGemvWaves + wave, gridDim.x * kGemvWaves,
-                          threadIdx.x & 63);
+    gateup_gemv_waves<FMT, KC>(p, blockIdx.x * kGemvWaves + wave, gridDim.x * kGemvWaves,
+                               threadIdx.x & 63);
 }
 
-// Weight formats of down_rows_kernel. A lane's piece of a row chunk is the 8 weights
-// 512 c + 8 lane .. + 7 of the row (c: the chunk of 512 weights), held as stored until the
-// compute step widens it to eight bf16 operands, exactly:
-//   kBF16  - 16 bytes of bf16 (the operands themselves);
-//   kFP8   - 8 bytes of OCP FP8 E4M3 codes (every E4M3 value is a bf16 value); the row's fp32
-//            scale multiplies the row's reduced product (scale * sum(code * h));
-//   kMXFP4 - 4 bytes of E2M1 codes (two per byte, the even weight in the low nibble) with their
-//            block's E8M0 scale byte (block (512 c + 8 lane) / 32 of the row), widened and scaled
-//            in one gfx950 conversion (exact while the product is a finite bf16).
-enum { kBF16 = 0, kFP8 = 1, kMXFP4 = 2 };
 
 // The down rows of block blk (rows 8 blk .. 8 blk + 7 of y for every token) into LDS obuf, then
 // y, with NW waves.
@@ -251,31 +300,14 @@ __device__ __forceinline__ void down_rows_block(const DownParams &p, int blk, fl
         const bool shared = e == p.E;
         const int Ie = shared ? p.Is : p.I;
         const int kd = ok ? Ie / 512 : 0;
-        const unsigned char *base = static_cast<const unsigned char *>(shared ? p.sdn : p.down);
-        const unsigned char *dummy = reinterpret_cast<const unsigned char *>(hg);
+        const void *base = shared ? p.sdn : p.down;
+        const uint8_t *mx = shared ? p.sdn_mx : p.dn_mx;
 #pragma unroll
-        for (int r = 0; r < kDownRows; ++r)
+        for (int r = 0; r < kDownRows; ++r) {
+            const size_t row = (shared ? 0 : (size_t)e * p.H) + r0 + r;  // row of [E][H]
 #pragma unroll
-            for (int c = 0; c < KD; ++c) {
-                const bool in = c < kd;
-                const size_t row = (shared ? 0 : (size_t)e * p.H) + r0 + r;  // row of [E][H]
-                if constexpr (FMT == kBF16) {
-                    const unsigned char *a = base + (row * Ie + 512 * c + 8 * lane) * 2;
-                    st.w[r][c] = load16_stream(in ? a : dummy);
-                } else if constexpr (FMT == kFP8) {
-                    const unsigned char *a = base + row * Ie + 512 * c + 8 * lane;
-                    const u32x2_t v = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x2_t *>(in ? a : dummy));
-                    st.w[r][c] = uint4{v.x, v.y, 0u, 0u};
-                } else {
-                    const unsigned char *a = base + row * (Ie / 2) + 256 * c + 4 * lane;
-                    const uint8_t *sb = (shared ? p.sdn_mx : p.dn_mx) + row * (Ie / 32) + 16 * c + lane / 4;
-                    const uint32_t v = __builtin_nontemporal_load(
-                        reinterpret_cast<const uint32_t *>(in ? a : dummy));
-                    const uint8_t *sp = in ? sb : dummy;  // one load from a selected address
-                    st.w[r][c] = uint4{v, (uint32_t)*sp, 0u, 0u};
-                }
-            }
+            for (int c = 0; c < KD; ++c) st.w[r][c] = load_piece<FMT>(base, mx, row, Ie, c, lane, c < kd, hg);
+        }
         if constexpr (FMT == kFP8) {
             const float *sp = ok ? (shared ? p.sdn_scale : p.dn_scale + (size_t)e * p.H) + r0 + (lane >> 4)
                                  : reinterpret_cast<const float *>(hg);
@@ -303,12 +335,6 @@ __device__ __forceinline__ void down_rows_block(const DownParams &p, int blk, fl
             }
         }
     };
-    // the eight bf16 operands of a stored piece
-    auto widen = [](const uint4 &w) -> uint4 {
-        if constexpr (FMT == kBF16) return w;
-        else if constexpr (FMT == kFP8) return e4m3x8_to_bf16x8(w.x, w.y);
-        else return e2m1x8_to_bf16x8(w.x, e8m0_to_f32(w.y));
-    };
     // the kDownRows row products of one member's h (hi and lo planes) over the expert's kd
     // chunks, summed over the wave: rows g and g + 4 land in row group g, which writes them
     // (times the rows' FP8 scales)
@@ -321,7 +347,7 @@ __device__ __forceinline__ void down_rows_block(const DownParams &p, int blk, fl
 #pragma unroll
             for (int c = 0; c < KD; ++c) {
                 if (c >= kd) break;  // uniform
-                const uint4 wv = widen(w[r][c]);
+                const uint4 wv = widen<FMT>(w[r][c]);
                 s = dot8(wv, hh[c], s);
                 s = dot8(wv, hl[c], s);
             }
@@ -389,8 +415,8 @@ __global__ __launch_bounds__(kGemvThreads) void down_rows_kernel(DownParams p) {
 
 int gemv_group_tokens() { return kGuNB; }
 
-// GEMV-path shapes: bf16, H a multiple of 512 up to 2048 (weight rows in whole kilobytes, at most
-// four per row held per lane), I and I_s multiples of 512 up to 1024.
+// GEMV-path shapes: H a multiple of 512 up to 2048 (weight rows in chunks of 512 weights, at
+// most four per row held per lane), I and I_s multiples of 512 up to 1024.
 bool gemv_supported(int H, int I, int Is) {
     const int Imax = I > Is ? I : Is;
     return H % 512 == 0 && H <= 2048 && I % 512 == 0 && (Is == 0 || Is % 512 == 0) &&
@@ -408,15 +434,24 @@ bool down_rows_supported(int H, int I, int Is) {
 // dynamic LDS limit)
 size_t down_rows_lds(int slots) { return (size_t)slots * kDownRows * sizeof(float); }
 
-hipError_t launch_gateup_gemv(const GateUpParams &p, int grid, hipStream_t s) {
+template <int FMT>
+hipError_t launch_gateup_gemv_fmt(const GateUpParams &p, int grid, hipStream_t s) {
     switch (p.H / 512) {
-    case 1: launch_k(gateup_gemv_kernel<1>, grid, kGemvThreads, 0, s, p); break;
-    case 2: launch_k(gateup_gemv_kernel<2>, grid, kGemvThreads, 0, s, p); break;
-    case 3: launch_k(gateup_gemv_kernel<3>, grid, kGemvThreads, 0, s, p); break;
-    case 4: launch_k(gateup_gemv_kernel<4>, grid, kGemvThreads, 0, s, p); break;
+    case 1: launch_k(gateup_gemv_kernel<FMT, 1>, grid, kGemvThreads, 0, s, p); break;
+    case 2: launch_k(gateup_gemv_kernel<FMT, 2>, grid, kGemvThreads, 0, s, p); break;
+    case 3: launch_k(gateup_gemv_kernel<FMT, 3>, grid, kGemvThreads, 0, s, p); break;
+    case 4: launch_k(gateup_gemv_kernel<FMT, 4>, grid, kGemvThreads, 0, s, p); break;
     default: return hipErrorInvalidValue;  // a caller bug: the plan checks gemv_supported
     }
     return hipGetLastError();
+}
+
+// dtype: 1 bf16, 2 FP8 E4M3, 3 MXFP4 weights (bf16 activations)
+hipError_t launch_gateup_gemv(const GateUpParams &p, int dtype, int grid, hipStream_t s) {
+    if (dtype == 1) return launch_gateup_gemv_fmt<kBF16>(p, grid, s);
+    if (dtype == 2) return launch_gateup_gemv_fmt<kFP8>(p, grid, s);
+    if (dtype == 3) return launch_gateup_gemv_fmt<kMXFP4>(p, grid, s);
+    return hipErrorInvalidValue;
 }
 
 // dtype: 1 bf16, 2 FP8 E4M3, 3 MXFP4 weights (bf16 activations)

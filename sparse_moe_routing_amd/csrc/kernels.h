@@ -158,7 +158,7 @@ bool down_rows_supported(int H, int I, int Is);
 int gemv_group_tokens();  // tokens per expert group of the vector-ALU kernels
 
 size_t down_rows_lds(int slots);
-hipError_t launch_gateup_gemv(const GateUpParams &p, int grid, hipStream_t s);
+hipError_t launch_gateup_gemv(const GateUpParams &p, int dtype, int grid, hipStream_t s);
 hipError_t launch_down_rows(const DownParams &p, int dtype, hipStream_t s);  // 1 bf16, 2 FP8, 3 MXFP4
 int wide_rows_per_down_unit();    // rows of y per down_wide unit
 int wide_rows_per_gateup_unit();  // intermediate rows per gateup_wide unit

@@ -113,8 +113,8 @@ struct Plan {
     bool wide = false;           // T > 64: gateup_wide + down_wide + combine, 64-token groups
     bool big = false;            // wide, bf16 or FP8, T >= kBigMinTokens: gateup_big for gateup_wide
     bool down_big = false;       // wide, bf16 or FP8, H a multiple of 512, T <= 256 or big
-    bool gemv = false;           // split, bf16: gateup_gemv in place of gateup
-    bool down_rows = false;      // split, bf16: down_rows in place of down
+    bool gemv = false;           // split, bf16 activations: gateup_gemv in place of gateup
+    bool down_rows = false;      // split, bf16 activations: down_rows in place of down
     int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;
     size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
@@ -195,7 +195,7 @@ Plan make_plan(const moe_ctx *c, int T) {
     // gemv_max_tokens (0 unless MOE_GEMV_MAX_TOKENS sets it: the matrix-core gate/up kernel is as
     // fast or faster from 3 tokens up, and one gate/up kernel for every decode T keeps a token's
     // bits independent of its batch)
-    p.gemv = cfg.dtype == MOE_BF16 && T <= c->gemv_max_tokens && gemv_supported(H, I, Is);
+    p.gemv = cfg.dtype != MOE_F32 && T <= c->gemv_max_tokens && gemv_supported(H, I, Is);
     p.down_rows = cfg.dtype != MOE_F32 && T <= kSplitMaxTokens && down_rows_supported(H, I, Is);
     int ng_x = group_rows(c, T);  // x-tile rows of the split and fused expert kernels
     if ((p.gemv || p.down_rows) && ng_x > gemv_group_tokens()) ng_x = gemv_group_tokens();
@@ -524,7 +524,7 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         gp.gu_mx = mx ? static_cast<const uint8_t *>(c->w.gate_up_scale) : nullptr;
         gp.sgu_mx = mx ? static_cast<const uint8_t *>(c->w.shared_gate_up_scale) : nullptr;
         if (p.gemv)
-            L.step("gateup_gemv", [&] { return launch_gateup_gemv(gp, c->num_cus, L.stream); });
+            L.step("gateup_gemv", [&] { return launch_gateup_gemv(gp, expert_kdt(c), c->num_cus, L.stream); });
         else if (p.big)
             L.step("gateup_big", [&] { return launch_gateup_big(gp, expert_kdt(c), p.gu_grid, L.stream); });
         else if (p.wide)

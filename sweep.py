@@ -1,9 +1,10 @@
 """Token-count sweep of the MoE layer on one MI355X.
 
     python sweep.py [--tokens 1-64,192,768,4097] [--steps 200] [--warmup 20] [--skewed]
+                    [--dtype bf16|fp8|mxfp4] [--paths default,gemv,mfma]
 
 For every T, one step is one moe_forward over T synthetic tokens with the decode shapes (H 2048,
-256 experts, top-8, expert and shared intermediate 512, bf16), timed as in bench.py: cold weights
+256 experts, top-8, expert and shared intermediate 512; bf16, FP8 or MXFP4 expert weights), timed as in bench.py: cold weights
 (each step takes the next of several independent weight sets), activations resident in HBM,
 K steps between two synchronisations. Printed per T: the kernel plan, wall microseconds per
 step, tokens/s, the distinct experts touched (U, from the library's own routing), the step's
@@ -49,6 +50,8 @@ def main():
     ap.add_argument("--pool", type=int, default=8)
     ap.add_argument("--skewed", action="store_true",
                     help="per-expert router bias ~ N(0, 2) (the verify workload's routing)")
+    ap.add_argument("--dtype", default="bf16", choices=("bf16", "fp8", "mxfp4"),
+                    help="expert weight format (bf16 activations and router throughout)")
     ap.add_argument("--paths", default="default",
                     help="comma list of decode expert paths to time per T: default (the "
                          "library's plan), gemv (vector-ALU gate/up and down), mfma "
@@ -61,7 +64,8 @@ def main():
         sys.exit(1)
     binding.load()
     Ts = parse_tokens(args.tokens)
-    base = inputs.BY_NAME["verify_skewed_t192" if args.skewed else "decode_b1_t4"]
+    base = inputs.BY_NAME[("verify_skewed_t192" if args.skewed else "decode_b1_t4") +
+                          ("" if args.dtype == "bf16" else "_" + args.dtype)]
     w = dataclasses.replace(base, name="sweep", tokens=max(Ts))
     H = w.hidden
     sets = bench.make_sets(w, args.sets, torch)

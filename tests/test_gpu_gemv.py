@@ -186,3 +186,60 @@ def test_gemv_out_of_range_ids_add_nothing(orc):
     torch.cuda.synchronize()
     assert_close(y.cpu().numpy(), orc.forward(lay, ids_o, np.where(bad, 0.0, w_o), g_o),
                  "out-of-range ids")
+
+
+# ------------------------------------------------------------------ quantized weights (FP8, MXFP4)
+# The vector-ALU gate/up widens each lane's stored weights to the same eight bf16 operands the
+# bf16 kernel reads at that lane, so on weights a bf16 context holds exactly (every MXFP4 weight;
+# FP8 under power-of-two row scales) its outputs are the bf16 kernel's bits.
+from test_gpu_parity import quantized_pair, quantized_small_layer  # noqa: E402
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_gemv_quantized_equals_bf16_of_decoded_weights_bitwise(fmt):
+    torch = _torch()
+    H, E, I, Is, Tmax = 1024, 16, 512, 512, 64
+    q, b = quantized_pair(fmt, H, E, I, Is, Tmax, seed=51 if fmt == "fp8" else 52)
+    tq, tb = binding.device_weights(q), binding.device_weights(b)
+    with gemv_limit(64):
+        mq = binding.MoeLayer(H, E, I, Is, Tmax, fmt, tq)
+        mb = binding.MoeLayer(H, E, I, Is, Tmax, "bf16", tb)
+    for T in (1, 4, 19, 32, 64):
+        assert mq.plan(T)[-2:] == ["gateup_gemv", "down_rows"], (fmt, T, mq.plan(T))
+        x = tb["x"][:T].contiguous()
+        yq = mq.forward(x)
+        yb = mb.forward(x)
+        torch.cuda.synchronize()
+        assert torch.isfinite(yb).all(), (fmt, T)
+        diff = (yq != yb).nonzero()
+        assert diff.numel() == 0, (fmt, T, diff[:5].tolist())
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("shape", [(1024, 32, 512, 512), (2048, 16, 1024, 512), (512, 64, 512, 0)],
+                         ids=lambda s: f"H{s[0]}-E{s[1]}-I{s[2]}-Is{s[3]}")
+def test_gemv_quantized_oracle(orc, fmt, shape):
+    """Quantized layers of normal draws on the vector-ALU path against the oracle, every output,
+    from the oracle's routing, at ragged token counts."""
+    torch = _torch()
+    H, E, I, Is = shape
+    layer = quantized_small_layer(fmt, H, E, I, Is or I, 64, seed=H + E + I + Is)
+    if not Is:  # no shared expert: its weights and gate row dropped
+        for k in ("shared_gate_up", "shared_down", "shared_gate_up_scale", "shared_down_scale"):
+            layer[k] = None
+        layer["shared_inter"] = 0
+        layer["router_w"] = layer["router_w"][:E]
+    t = binding.device_weights(layer)
+    with gemv_limit(64):
+        m = binding.MoeLayer(H, E, I, Is, 64, fmt, t)
+    ws = m.workspace(64)
+    for T in (1, 4, 20, 47, 64):
+        assert m.plan(T)[-2:] == ["gateup_gemv", "down_rows"], (fmt, shape, T, m.plan(T))
+        lay = dict(layer)
+        lay["x"] = layer["x"][:T]
+        z_o = orc.logits(lay["x"], layer["router_w"], None)
+        ids_o, w_o, g_o = orc.select(z_o, E, Is > 0)
+        y = m.forward(t["x"][:T].contiguous(), routing=routing_device(ids_o, w_o, g_o), ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:m.state_bytes()].view(torch.int32).abs().sum()) == 0
+        assert_close(y.cpu().numpy(), orc.forward(lay, ids_o, w_o, g_o), f"{fmt} {shape} T={T}")
