@@ -74,6 +74,35 @@ __device__ __forceinline__ uint4 load16_stream(const void *p) {
     return uint4{v.x, v.y, v.z, v.w};
 }
 
+// Buffer loads. A buffer resource (wave-uniform, four scalar registers) covers `bytes` bytes from
+// `base`; a load whose offset lies past them returns zero and makes no memory access. A kernel that
+// keeps a fixed number of loads in flight (so that the compiler's wait counts stay exact) issues
+// its loads with nothing to read this way - with `bytes` = 0, or an offset past the range - instead
+// of re-reading some cached address: thousands of waves re-reading one line all queue on the one
+// L2 channel that holds it. The fourth descriptor word is the data-format field the gfx9-family
+// parts take for untyped (raw) buffer access; offsets are 32-bit, so a resource covers < 4 GiB.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+constexpr int kBufNT = 2;  // cache-policy bit of a non-temporal (streamed) load
+__device__ __forceinline__ uint4 bload16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kBufNT));
+}
+__device__ __forceinline__ u32x2_t bload8_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kBufNT));
+}
+__device__ __forceinline__ uint32_t bload4_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kBufNT);
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
 // Expert-weight storage formats. A weight "piece" is the Op::kPerLane elements one lane feeds to
 // one matrix-core fragment (16 bytes of operand data). WeightFmt<Op, false> stores the operand
 // type itself; WeightFmt<OpBF16, true> stores OCP FP8 E4M3 codes (8 bytes per piece) that are
@@ -138,8 +167,6 @@ __device__ __forceinline__ int mx_piece_pos(int p, int b) {
 // upper half of the row's pieces swaps pairs, so that one LDS instruction's 8 pieces are 8
 // distinct bank groups.
 __device__ __forceinline__ int fp8_piece_pos(int p) { return p ^ ((p >> 3) & 1); }
-
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <class Op, bool kFp8>
 struct WeightFmt {

@@ -123,26 +123,30 @@ struct WaveShare {
 // row scales) the outputs are the same bits.
 enum { kBF16 = 0, kFP8 = 1, kMXFP4 = 2 };
 
-// The stored piece of row `row` (element offset of the row in its matrix) and chunk c for this
-// lane; `dummy` (cached, never used) in place of a piece past the range.
+constexpr uint32_t kPast = 0x80000000u;  // an offset past every resource here (each < 2 GiB)
+
+// The stored piece (chunk c, this lane) of row `row` of a matrix of rows of `cols` weights, read
+// through the buffer resource rw (MXFP4: its scale bytes through rs). `in` false: nothing to read
+// (a load past the resource: no memory access, the same count of loads in flight).
 template <int FMT>
-__device__ __forceinline__ uint4 load_piece(const void *mat, const uint8_t *mx, size_t row, int cols,
-                                            int c, int lane, bool in, const void *dummy) {
-    const unsigned char *d = static_cast<const unsigned char *>(dummy);
+__device__ __forceinline__ uint4 load_piece(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rs,
+                                            uint32_t row, int cols, int c, int lane, bool in) {
     if constexpr (FMT == kBF16) {
-        const unsigned char *a = static_cast<const unsigned char *>(mat) + (row * cols + 512 * c + 8 * lane) * 2;
-        return load16_stream(in ? a : d);
+        return bload16_stream(rw, in ? (row * cols + 512 * c + 8 * lane) * 2 : kPast);
     } else if constexpr (FMT == kFP8) {
-        const unsigned char *a = static_cast<const unsigned char *>(mat) + row * cols + 512 * c + 8 * lane;
-        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(in ? a : d));
+        const u32x2_t v = bload8_stream(rw, in ? row * cols + 512 * c + 8 * lane : kPast);
         return uint4{v.x, v.y, 0u, 0u};
     } else {
-        const unsigned char *a = static_cast<const unsigned char *>(mat) + row * (cols / 2) + 256 * c + 4 * lane;
-        const uint8_t *sb = mx + row * (cols / 32) + 16 * c + lane / 4;
-        const uint32_t v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(in ? a : d));
-        const uint8_t *sp = in ? sb : d;  // one load from a selected address
-        return uint4{v, (uint32_t)*sp, 0u, 0u};
+        const uint32_t v = bload4_stream(rw, in ? row * (cols / 2) + 256 * c + 4 * lane : kPast);
+        const uint32_t sb = bload1(rs, in ? row * (cols / 32) + 16 * c + lane / 4 : kPast);
+        return uint4{v, sb, 0u, 0u};
     }
+}
+
+// Bytes of a stored row of `cols` weights.
+template <int FMT>
+__host__ __device__ constexpr uint32_t row_bytes(int cols) {
+    return FMT == kBF16 ? 2 * cols : FMT == kFP8 ? cols : cols / 2;
 }
 
 // The eight bf16 operands of a stored piece.
@@ -177,30 +181,30 @@ __device__ __forceinline__ void gateup_gemv_waves(const GateUpParams &p, int gw,
             slot[t] = shared ? p.T * kTopK + start + m : p.perm[start + m];
             tok[t] = shared ? slot[t] - p.T * kTopK : slot[t] >> 3;
         }
-        const void *gu = shared ? p.sgu : p.gate_up;
-        const uint8_t *gmx = shared ? p.sgu_mx : p.gu_mx;
-        const size_t row0 = shared ? 0 : (size_t)e * 2 * Ie;  // the expert's first row
-        // a unit past the wave's range reads the first token's x row in place of the weights
-        // (hot in cache, never used): every iteration issues the same loads, so the compiler's
-        // wait counts stay exact and two units stay in flight
-        const uint16_t *dummy = x + (size_t)tok[0] * p.H + 8 * lane;
-        // the weights of unit j: gate rows 2j, 2j + 1, up rows Ie + 2j, Ie + 2j + 1
-        // FP8: lane l also reads the scale of row l & 3 of the unit, a vector load in the same
-        // queue as the weights (scalar loads of the scales would each wait for every scalar
-        // load in flight)
-        const float *gsc = shared ? p.sgu_scale : p.gu_scale + row0;
+        // the expert's [2 Ie][H] matrix (rows: gate, then up) and its FP8 row scales or MXFP4
+        // scale bytes; a unit past the wave's range issues its loads past the resources (no
+        // memory access): every iteration issues the same loads, so the compiler's wait counts
+        // stay exact and two units stay in flight
+        const unsigned char *gu = static_cast<const unsigned char *>(shared ? p.sgu : p.gate_up) +
+                                  (shared ? 0 : (size_t)e * 2 * Ie * row_bytes<FMT>(p.H));
+        const auto rw = buffer_rsrc(gu, 2 * Ie * row_bytes<FMT>(p.H));
+        const auto rs = FMT == kMXFP4 ? buffer_rsrc((shared ? p.sgu_mx : p.gu_mx + (size_t)e * 2 * Ie * (p.H / 32)),
+                                                    2 * Ie * (p.H / 32))
+                        : FMT == kFP8 ? buffer_rsrc(shared ? p.sgu_scale : p.gu_scale + (size_t)e * 2 * Ie, 8 * Ie)
+                                      : rw;
+        // the weights of unit j: gate rows 2j, 2j + 1, up rows Ie + 2j, Ie + 2j + 1; FP8: lane l
+        // also reads the scale of row l & 3 of the unit, in the same queue as the weights
+        // (scalar loads of the scales would each wait for every scalar load in flight)
         auto load_w = [&](uint4 (&w)[4][KC], float &sc, int j) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const size_t row = row0 + (r < 2 ? 0 : Ie) + 2 * j + (r & 1);
+                const uint32_t row = (r < 2 ? 0 : Ie) + 2 * j + (r & 1);
 #pragma unroll
-                for (int c = 0; c < KC; ++c)
-                    w[r][c] = load_piece<FMT>(gu, gmx, row, p.H, c, lane, j < j1, dummy);
+                for (int c = 0; c < KC; ++c) w[r][c] = load_piece<FMT>(rw, rs, row, p.H, c, lane, j < j1);
             }
             if constexpr (FMT == kFP8) {
                 const int r = lane & 3;
-                const float *a = gsc + ((r < 2 ? 0 : Ie) + 2 * j + (r & 1));
-                sc = *(j < j1 ? a : reinterpret_cast<const float *>(dummy));
+                sc = __uint_as_float(bload4(rs, j < j1 ? ((r < 2 ? 0 : Ie) + 2 * j + (r & 1)) * 4 : kPast));
             }
         };
         uint4 xr[kGuNB][KC];
@@ -281,52 +285,69 @@ __device__ __forceinline__ void down_rows_block(const DownParams &p, int blk, fl
     const int ng = p.num_groups[0];
     const uint16_t *hg = reinterpret_cast<const uint16_t *>(p.h);
 
+    // the weight (and scale) arrays as integers, chosen between as integers: a choice between two
+    // parameter pointers otherwise becomes a two-entry table in scratch memory
+    const uintptr_t w_rt = (uintptr_t)p.down, w_sh = (uintptr_t)p.sdn;
+    const uintptr_t s_rt = FMT == kMXFP4 ? (uintptr_t)p.dn_mx : (uintptr_t)p.dn_scale;
+    const uintptr_t s_sh = FMT == kMXFP4 ? (uintptr_t)p.sdn_mx : (uintptr_t)p.sdn_scale;
     struct Stage {
         uint4 w[kDownRows][KD];   // bf16: 4 words; FP8: words x, y; MXFP4: word x, scale byte y
         uint4 hh[kDnNB][KD], hl[kDnNB][KD];
         float s0, s1;             // FP8: the scales of rows lane / 16 and lane / 16 + 4
+        int slot[kDnNB];          // the members' row slots (wave-uniform)
     };
-    auto slot_of = [&](int e, int start, int m) {
-        return e == p.E ? p.T * kTopK + start + m : p.perm[start + m];
-    };
-    // Group gi's kDownRows rows of its down weight (with FP8 row scales). Every weight load is
-    // issued whatever the group, so that the compiler's wait counts stay exact and kRing groups
-    // stay in flight: past the last group or past a narrower expert's chunks the lanes all read
-    // the same bytes at the start of h (one cached line), and the compute step never uses them.
+    // Group gi's kDownRows rows of its down weight (with FP8 row scales), read through buffer
+    // resources over just those rows. Every weight load is issued whatever the group, so that the
+    // compiler's wait counts stay exact and kRing groups stay in flight: past the last group the
+    // resources are empty and past a narrower expert's chunks the offsets lie beyond them, so
+    // those loads make no memory access (the compute step never uses them).
     auto load_w = [&](Stage &st, int gi) {
         const bool ok = gi < ng;
         const int4 grp = p.groups[ok ? gi : 0];
-        const int e = grp.x;
+        const int e = ok ? grp.x : p.E;
         const bool shared = e == p.E;
         const int Ie = shared ? p.Is : p.I;
         const int kd = ok ? Ie / 512 : 0;
-        const void *base = shared ? p.sdn : p.down;
-        const uint8_t *mx = shared ? p.sdn_mx : p.dn_mx;
+        const size_t row0 = (shared ? 0 : (size_t)e * p.H) + r0;  // first row, of [E][H]
+        const uintptr_t wbase = (shared ? w_sh : w_rt) + row0 * row_bytes<FMT>(Ie);
+        const auto rw = buffer_rsrc(reinterpret_cast<const void *>(wbase), ok ? kDownRows * row_bytes<FMT>(Ie) : 0);
+        // MXFP4: the rows' scale bytes; FP8: their fp32 scales
+        const uint32_t srow = FMT == kMXFP4 ? Ie / 32 : 4;
+        const auto rs = buffer_rsrc(reinterpret_cast<const void *>((shared ? s_sh : s_rt) + row0 * srow),
+                                    ok && FMT != kBF16 ? kDownRows * srow : 0);
 #pragma unroll
-        for (int r = 0; r < kDownRows; ++r) {
-            const size_t row = (shared ? 0 : (size_t)e * p.H) + r0 + r;  // row of [E][H]
+        for (int r = 0; r < kDownRows; ++r)
 #pragma unroll
-            for (int c = 0; c < KD; ++c) st.w[r][c] = load_piece<FMT>(base, mx, row, Ie, c, lane, c < kd, hg);
-        }
+            for (int c = 0; c < KD; ++c) st.w[r][c] = load_piece<FMT>(rw, rs, r, Ie, c, lane, c < kd);
         if constexpr (FMT == kFP8) {
-            const float *sp = ok ? (shared ? p.sdn_scale : p.dn_scale + (size_t)e * p.H) + r0 + (lane >> 4)
-                                 : reinterpret_cast<const float *>(hg);
-            st.s0 = sp[0];
-            st.s1 = sp[ok ? 4 : 0];
+            st.s0 = __uint_as_float(bload4(rs, (lane >> 4) * 4));
+            st.s1 = __uint_as_float(bload4(rs, ((lane >> 4) + 4) * 4));
         }
     };
     // The h rows of the group's members: only those the group has (a uniform condition; dummy
-    // reads for the absent members measured 2.5 us of the T = 4 down pass). A stage issues these
-    // before its weight loads, which are unconditional, so the wait counts still cover the ring.
+    // reads for the absent members measured 2.5 us of the T = 4 down pass). The members' slots
+    // are read first, all at once and unconditionally (past the members: a repeat of the last
+    // one), so that a group's scalar reads make one round trip, not one per member. A stage
+    // issues these before its weight loads, which are unconditional, so the wait counts still
+    // cover the ring.
     auto load_h = [&](Stage &st, int gi) {
         const bool ok = gi < ng;
         const int4 grp = p.groups[ok ? gi : 0];
-        const int e = grp.x, start = grp.y, n = ok ? grp.z : 0;
-        const int kd = ok ? (e == p.E ? p.Is : p.I) / 512 : 0;
+        const int n = ok ? grp.z : 0;
+        const int kd = ok ? (grp.x == p.E ? p.Is : p.I) / 512 : 0;
+        const bool routed = ok && grp.x != p.E;
+#pragma unroll
+        for (int m = 0; m < kDnNB; ++m) {
+            const int mm = min(m, n - 1);
+            // one unconditional load per member (perm[0] where unused), so that the four reads
+            // go out together
+            const int pv = p.perm[routed ? grp.y + mm : 0];
+            st.slot[m] = routed ? pv : p.T * kTopK + grp.y + mm;
+        }
 #pragma unroll
         for (int m = 0; m < kDnNB; ++m) {
             if (m >= n) break;  // uniform
-            const uint16_t *hs = hg + (size_t)slot_of(e, start, m) * p.Imax + 8 * lane;
+            const uint16_t *hs = hg + (size_t)st.slot[m] * p.Imax + 8 * lane;
 #pragma unroll
             for (int c = 0; c < KD; ++c) {
                 if (c >= kd) break;  // uniform
@@ -367,12 +388,25 @@ __device__ __forceinline__ void down_rows_block(const DownParams &p, int blk, fl
     };
     auto compute = [&](const Stage &st, int gi) {  // no vector-memory loads: the stage holds them
         const int4 grp = p.groups[gi];
-        const int e = grp.x, start = grp.y, n = grp.z;  // n <= kDnNB (the plan's group size)
-        const int kd = (e == p.E ? p.Is : p.I) / 512;
+        const int n = grp.z;  // n <= kDnNB (the plan's group size)
+        const int kd = (grp.x == p.E ? p.Is : p.I) / 512;
 #pragma unroll
         for (int m = 0; m < kDnNB; ++m)
-            if (m < n) emit(st.w, st.hh[m], st.hl[m], kd, st.s0, st.s1, slot_of(e, start, m));
+            if (m < n) emit(st.w, st.hh[m], st.hl[m], kd, st.s0, st.s1, st.slot[m]);
     };
+    // The combine's operands, requested before the weight stream so that they are in registers
+    // when the products are: thread i < 8 T owns row r = i % 8 of token t = i / 8 (8 T <= the
+    // block's threads; the launch checks it)
+    const int ct = tid / kDownRows, cr = tid - ct * kDownRows;
+    const bool cact = ct < p.T;
+    int cid[kTopK];
+    float cw[kTopK], cg = 0.f;
+#pragma unroll
+    for (int k = 0; k < kTopK; ++k) {
+        cid[k] = cact ? p.ids[ct * kTopK + k] : -1;
+        cw[k] = cact ? p.w[ct * kTopK + k] : 0.f;
+    }
+    if (cact && p.g) cg = p.g[ct];
     // a ring of kRing groups per wave: group k + kRing is requested right after group k is done
     Stage st[kRing];
 #pragma unroll
@@ -393,16 +427,13 @@ __device__ __forceinline__ void down_rows_block(const DownParams &p, int blk, fl
     // y rows r0 .. r0 + kDownRows - 1: the eight ranks in rank order (weighted; a pair whose id
     // lies outside [0, E) was dropped by the bucketing and adds nothing), then the gated shared
     // slot
-    for (int i = tid; i < p.T * kDownRows; i += NW * kWave) {
-        const int t = i / kDownRows, r = i - t * kDownRows;
+    if (cact) {
         float acc = 0.f;
 #pragma unroll
-        for (int k = 0; k < kTopK; ++k) {
-            const int e = p.ids[t * kTopK + k];
-            if (e >= 0 && e < p.E) acc += p.w[t * kTopK + k] * obuf[(t * kTopK + k) * kDownRows + r];
-        }
-        if (p.g) acc += p.g[t] * obuf[(p.T * kTopK + t) * kDownRows + r];
-        p.y[(size_t)t * p.H + r0 + r] = acc;
+        for (int k = 0; k < kTopK; ++k)
+            if (cid[k] >= 0 && cid[k] < p.E) acc += cw[k] * obuf[(ct * kTopK + k) * kDownRows + cr];
+        if (p.g) acc += cg * obuf[(p.T * kTopK + ct) * kDownRows + cr];
+        p.y[(size_t)ct * p.H + r0 + cr] = acc;
     }
 }
 
@@ -462,7 +493,8 @@ void launch_down_rows_fmt(const DownParams &p, int grid, size_t lds, hipStream_t
 }
 
 hipError_t launch_down_rows(const DownParams &p, int dtype, hipStream_t s) {
-    if (p.H % kDownRows || p.Imax > 1024) return hipErrorInvalidValue;  // a caller bug
+    // a caller bug: the plan checks down_rows_supported and T <= 64
+    if (p.H % kDownRows || p.Imax > 1024 || p.T * kDownRows > kGemvThreads) return hipErrorInvalidValue;
     const size_t lds = down_rows_lds(p.T * kTopK + (p.g ? p.T : 0));
     const int grid = p.H / kDownRows;
     if (dtype == 1) launch_down_rows_fmt<kBF16>(p, grid, lds, s);
