@@ -228,8 +228,10 @@ def test_route_fused(orc, name):
 
 
 # ----------------------------------------------------------------------------- bucketing
-@pytest.mark.parametrize("T", [1, 2, 4, 19, 20, 32, 46, 47, 64, 65, 192, 768, 4097, 8192])
+@pytest.mark.parametrize("T", [1, 2, 4, 7, 8, 9, 19, 20, 32, 46, 47, 64, 65, 192, 768, 4097, 8192])
 def test_bucket_exact(orc, T):
+    """Counts, offsets and pair order equal to a stable counting sort (one wave takes up to 64
+    pairs, T <= 8; a block barrier pass above)."""
     torch = _torch()
     layer, m, _ = get_layer("decode_b1_t4", max_tokens=8192)
     E = m.num_experts
