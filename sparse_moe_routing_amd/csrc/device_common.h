@@ -144,11 +144,13 @@ __device__ __forceinline__ uint4 e2m1x8_to_bf16x8(uint32_t w, float s) {
                  e2m1x2_to_bf16x2<2>(w, s), e2m1x2_to_bf16x2<3>(w, s)};
 }
 
-// Wait states between the matrix instructions of one chunk and the FP4 conversions of the next:
-// a matrix instruction still reads its A/B registers for several cycles after it issues, and the
-// scaled FP4 conversions may be allocated those registers; without this gap the last matrix
-// steps before a conversion block read the new values (measured on gfx950: exactly those steps'
-// products were wrong). The scheduling barriers keep every instruction on its side.
+// Wait states between the matrix instructions of one chunk and the scaled conversions (FP4, FP8)
+// of the next: a matrix instruction still reads its A/B registers for several cycles after it
+// issues, and the conversions may be allocated those registers; without this gap the last matrix
+// steps before a conversion block read the new values (measured on gfx950 for the FP4 ones:
+// exactly those steps' products were wrong). The FP8 conversions are the same instruction family
+// and passed as built, but nothing but register allocation kept them clear, so they take the guard
+// too (about 1 % of an FP8 round). The scheduling barriers keep every instruction on its side.
 __device__ __forceinline__ void mfma_operand_guard() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");

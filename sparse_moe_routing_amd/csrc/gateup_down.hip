@@ -166,6 +166,7 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(GateUpParams p) {
                     continue;
                 }
                 unsigned char *buf = stage + (d % kStageBufs) * kStage;  // a wave's LDS ops stay in order
+                if constexpr (kFp8) mfma_operand_guard();  // the FP8 conversions as the MXFP4 ones
 #pragma unroll
                 for (int a = 0; a < kLoads; ++a) {
                     if constexpr (kFp8) {  // 16 codes widened to two bf16 pieces (exact)
@@ -421,6 +422,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
                     }
                     continue;
                 }
+                if constexpr (kFp8) mfma_operand_guard();  // the FP8 conversions as the MXFP4 ones
 #pragma unroll
                 for (int r = 0; r < kLoads; ++r) {
                     if constexpr (kFp8) {  // 16 codes widened to two bf16 pieces (exact)

@@ -115,6 +115,7 @@ __device__ __forceinline__ void stage_w(unsigned char *buf,
             *reinterpret_cast<uint4 *>(buf + rr * 256 + ((mx_piece_pos(pb + k, 0) ^ rr) & 15) * 16) =
                 e2m1x8_to_bf16x8(w4[k], sf);
     } else {
+        if constexpr (W::k8) mfma_operand_guard();  // the FP8 conversions as the MXFP4 ones
 #pragma unroll
         for (int a = 0; a < W::kLoads; ++a) {
             const int rr = W::kRowStep * a + W::row(lane);
@@ -570,6 +571,7 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
         // the 16 rows of an operand read fall on 16 distinct 16-byte bank groups), refill the ring,
         // then the two steps' operands in matrix-core order
         auto half = [&](uint4 (&r)[kRT][2], int hh, int c, const unsigned char *xb) {
+            if constexpr (kFp8) mfma_operand_guard();  // the FP8 conversions as the MXFP4 ones
             if (rows_ok) {
 #pragma unroll
                 for (int t = 0; t < kRT; ++t)
@@ -819,6 +821,7 @@ __global__ __launch_bounds__(kDBThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             for (int s2 = 0; s2 < kWPieces / 4; ++s2) {
                 const int po = col * 128 + (((2 * s2 + (q >> 1)) ^ ((col >> 1) & 7)) * 16) + (q & 1) * 8;
                 uint4 a[kDBTiles];
+                mfma_operand_guard();  // these conversions write operand registers of the last step
 #pragma unroll
                 for (int t = 0; t < kDBTiles; ++t) {
                     const uint2 cd = *reinterpret_cast<const uint2 *>(wst + t * kBigTile + po);

@@ -520,3 +520,26 @@ def test_workload_recipe_shapes():
     assert list(back) == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 0.0]
     q = inputs.tie_quantize(np.array([[0.1, -0.1, 0.375, 0.125, 1.3]], np.float32), np.array([0]))
     assert list(q[0]) == [0.0, 0.0, 0.5, 0.0, 1.25] and np.signbit(q[0, 1])
+
+
+def test_oracle_under_sanitizers(plant_dir):
+    """Every oracle entry point (bf16, FP8 and MXFP4 forwards, logits, selection, bucketing, the
+    format decoders) runs clean under AddressSanitizer and UndefinedBehaviorSanitizer: the oracle
+    source is compiled into tests/sanitize_oracle.c's driver with both sanitizers (serial: no
+    OpenMP runtime in the sanitized build), any invalid access or undefined operation aborts."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not available")
+    here = os.path.dirname(os.path.abspath(__file__))
+    exe = os.path.join(plant_dir, "sanitize_oracle")
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-Wall", "-Wextra", "-Werror", "-Wno-unused-parameter",
+           "-Wno-unknown-pragmas", os.path.join(here, "sanitize_oracle.c"),
+           os.path.join(os.path.dirname(here), "oracle", "moe_oracle.c"), "-o", exe, "-lm"]
+    subprocess.run(cmd, check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.startswith("checksum ") and "ERROR" not in r.stderr, r.stderr
