@@ -187,8 +187,91 @@ __device__ void write_tables(const BucketParams &bp, int cnt, S &s) {
     }
 }
 
+// The whole bucketing of n <= 64 pairs by one wave (lane l holds pair l), with no block barrier
+// and the tables of the block form. Lane l finds the pairs of its own id among the nine ballots
+// of chunk_counts (its rank among them is its stable position); the first pair of each id enters
+// the id's count and group count into a per-expert LDS histogram (the wave's LDS operations take
+// effect in issue order, so no barrier is needed), and a wave scan over the experts (four per
+// lane) turns both into exclusive offsets: the expert's first slot and first group.
+template <class S>
+__device__ void bucket_wave(const BucketParams &bp, int n, int lane, S &s) {
+    const int e = lane < n ? s.ids[lane] : -1;
+    const bool ok = e >= 0 && e < bp.E;
+    uint64_t eq = __ballot(ok);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const uint64_t one = __ballot(ok && ((e >> b) & 1));
+        eq &= ((e >> b) & 1) ? one : ~one;
+    }
+    const int rank = __popcll(eq & ((1ull << lane) - 1ull));
+    const int cnt = __popcll(eq);
+    const bool first = ok && rank == 0;
+    const int ngrp = (cnt + bp.NG - 1) / bp.NG;
+    // Lanes exchange values through LDS here: each exchange is fenced at wavefront scope around a
+    // wave barrier, without which the compiler may forward a lane's own earlier store to its load.
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s.a[4 * lane + k] = s.b[4 * lane + k] = 0;  // experts 4l .. 4l + 3
+    wave_sync();
+    if (first) {
+        s.a[e] = cnt;
+        s.b[e] = ngrp;
+    }
+    wave_sync();
+    int c4[4], g4[4], cs = 0, gs = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        c4[k] = s.a[4 * lane + k];
+        g4[k] = s.b[4 * lane + k];
+        cs += c4[k];
+        gs += g4[k];
+    }
+    const int ci = wave_inclusive_sum(cs), gi = wave_inclusive_sum(gs);
+    int co[4], go[4];
+    co[0] = ci - cs;
+    go[0] = gi - gs;
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+        co[k] = co[k - 1] + c4[k - 1];
+        go[k] = go[k - 1] + g4[k - 1];
+    }
+    wave_sync();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        s.a[4 * lane + k] = co[k];
+        s.b[4 * lane + k] = go[k];
+    }
+    wave_sync();
+    const int nsh = bp.has_shared ? (bp.T + bp.NG - 1) / bp.NG : 0;
+    if (ok) {
+        const int off = s.a[e];
+        bp.perm[off + rank] = lane;
+        if (first) {
+            const int gb = nsh + s.b[e];
+            for (int gg = 0; gg < ngrp; ++gg)
+                bp.groups[gb + gg] = make_int4(e, off + gg * bp.NG, min(bp.NG, cnt - gg * bp.NG), 0);
+        }
+    }
+    if (lane < nsh) bp.groups[lane] = make_int4(bp.E, lane * bp.NG, min(bp.NG, bp.T - lane * bp.NG), 0);
+    const int ctot = __builtin_amdgcn_readlane(ci, kWave - 1), gtot = __builtin_amdgcn_readlane(gi, kWave - 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (4 * lane + k < bp.E) {
+            bp.counts[4 * lane + k] = c4[k];
+            bp.offsets[4 * lane + k] = co[k];
+        }
+    if (lane == 0) {
+        bp.offsets[bp.E] = ctot;
+        bp.num_groups[0] = nsh + gtot;
+    }
+}
+
 // Selection of T <= 64 tokens (one wave per token, 16 waves) and, optionally, the whole
-// bucketing pass, by one block of 1024 threads.
+// bucketing pass, by one block of 1024 threads (up to 64 pairs: by one wave).
 template <bool kDev = false>
 __device__ void select_bucket_block(const SelectParams &sp, const BucketParams &bp, bool do_select,
                                     bool do_bucket, BucketShared &s) {
@@ -205,6 +288,10 @@ __device__ void select_bucket_block(const SelectParams &sp, const BucketParams &
     if (!do_bucket) return;  // uniform over the block
     __syncthreads();
     const int n = T * kTopK;
+    if (n <= kWave) {  // uniform
+        if (wave == 0) bucket_wave(bp, n, lane, s);
+        return;
+    }
     const int cnt = chunk_counts(s, n, bp.E);
     write_tables(bp, cnt, s);  // ends with a barrier; s.a[e] = offset of expert e
     chunk_scatter(s, n, bp.E, 0, bp.perm, [&](int e) { return s.a[e]; });
