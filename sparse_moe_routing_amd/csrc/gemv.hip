@@ -33,7 +33,8 @@ constexpr int kGemvThreads = kGemvWaves * kWave;
 // tokens per expert group on this path (the plan's group size): the gate/up kernel keeps
 // their activations in registers, the down kernel their h rows
 constexpr int kGuNB = 4;
-constexpr int kDnNB = 4;
+constexpr int kDnNB = 4;      // members whose h rows a ring stage holds
+constexpr int kDnMaxNB = 8;   // members a down_rows group may have (the rest load h when computed)
 constexpr int kDownRows = 8;
 
 __device__ __forceinline__ float dot8(const uint4 &w, const uint4 &x, float c) {
@@ -386,13 +387,30 @@ __device__ __forceinline__ void down_rows_block(const DownParams &p, int blk, fl
             obuf[slot * kDownRows + 4 + g] = v1;
         }
     };
-    auto compute = [&](const Stage &st, int gi) {  // no vector-memory loads: the stage holds them
+    // The stage holds the first kDnNB members' h rows; a group with more members (up to
+    // kDnMaxNB, the plan's group size: expert groups of 8 tokens keep a hot expert's weights
+    // from being read once per 4 of its tokens) loads the others' h rows here, against the
+    // weights already in registers.
+    auto compute = [&](const Stage &st, int gi) {
         const int4 grp = p.groups[gi];
-        const int n = grp.z;  // n <= kDnNB (the plan's group size)
+        const int n = grp.z;  // n <= kDnMaxNB
         const int kd = (grp.x == p.E ? p.Is : p.I) / 512;
 #pragma unroll
         for (int m = 0; m < kDnNB; ++m)
             if (m < n) emit(st.w, st.hh[m], st.hl[m], kd, st.s0, st.s1, st.slot[m]);
+        // members past the stage (uniform; rare in near-uniform routing): their h loads queue
+        // behind the ring's, so each waits for the stages in flight
+        for (int m = kDnNB; m < n; ++m) {
+            const int slot = grp.x == p.E ? p.T * kTopK + grp.y + m : p.perm[grp.y + m];
+            const uint16_t *hs = hg + (size_t)slot * p.Imax + 8 * lane;
+            uint4 hh[KD], hl[KD];
+#pragma unroll
+            for (int c = 0; c < KD; ++c) {
+                hh[c] = c < kd ? load16(hs + 512 * c) : uint4{0u, 0u, 0u, 0u};
+                hl[c] = c < kd ? load16(hs + p.plane + 512 * c) : uint4{0u, 0u, 0u, 0u};
+            }
+            emit(st.w, hh, hl, kd, st.s0, st.s1, slot);
+        }
     };
     // The combine's operands, requested before the weight stream so that they are in registers
     // when the products are: thread i < 8 T owns row r = i % 8 of token t = i / 8 (8 T <= the
@@ -445,6 +463,7 @@ __global__ __launch_bounds__(kGemvThreads) void down_rows_kernel(DownParams p) {
 
 
 int gemv_group_tokens() { return kGuNB; }
+int down_rows_group_tokens() { return kDnMaxNB; }
 
 // GEMV-path shapes: H a multiple of 512 up to 2048 (weight rows in chunks of 512 weights, at
 // most four per row held per lane), I and I_s multiples of 512 up to 1024.

@@ -155,7 +155,8 @@ hipError_t launch_down_big(const DownParams &p, int dtype, int grid, hipStream_t
 // Decode expert stage on the vector ALUs (gemv.hip): bf16 shapes gemv_supported accepts.
 bool gemv_supported(int H, int I, int Is);
 bool down_rows_supported(int H, int I, int Is);
-int gemv_group_tokens();  // tokens per expert group of the vector-ALU kernels
+int gemv_group_tokens();       // tokens per expert group of the vector-ALU gate/up kernel
+int down_rows_group_tokens();  // tokens per expert group down_rows takes
 
 size_t down_rows_lds(int slots);
 hipError_t launch_gateup_gemv(const GateUpParams &p, int dtype, int grid, hipStream_t s);

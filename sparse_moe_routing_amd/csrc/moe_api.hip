@@ -188,17 +188,18 @@ Plan make_plan(const moe_ctx *c, int T) {
     const int chunk = act_dtype(cfg.dtype) == MOE_BF16 ? 128 : 64;
     const bool chunk_ok = I % chunk == 0 && Is % chunk == 0;
     p.wide = T > kSplitMaxTokens && chunk_ok;
-    // bf16 decode rounds (T <= 64) end with down_rows (vector-ALU down products of the rows a
-    // block owns, combined in the block: no per-slot buffer, no arrival counters; measured
-    // faster than the matrix-core down kernel at every T from 1 to 32), whose groups hold at most
-    // 4 tokens (their h rows stay in registers); the vector-ALU gate/up kernel is used up to
-    // gemv_max_tokens (0 unless MOE_GEMV_MAX_TOKENS sets it: the matrix-core gate/up kernel is as
-    // fast or faster from 3 tokens up, and one gate/up kernel for every decode T keeps a token's
-    // bits independent of its batch)
+    // bf16 / FP8 / MXFP4 decode rounds (T <= 64) end with down_rows (vector-ALU down products of
+    // the rows a block owns, combined in the block: no per-slot buffer, no arrival counters;
+    // measured faster than the matrix-core down kernel at every T from 1 to 32), whose groups
+    // hold at most 8 tokens; the vector-ALU gate/up kernel (groups of at most 4: the tokens' x
+    // rows stay in registers) is used up to gemv_max_tokens (0 unless MOE_GEMV_MAX_TOKENS sets
+    // it: the matrix-core gate/up kernel is as fast or faster from 3 tokens up, and one gate/up
+    // kernel for every decode T keeps a token's bits independent of its batch)
     p.gemv = cfg.dtype != MOE_F32 && T <= c->gemv_max_tokens && gemv_supported(H, I, Is);
     p.down_rows = cfg.dtype != MOE_F32 && T <= kSplitMaxTokens && down_rows_supported(H, I, Is);
     int ng_x = group_rows(c, T);  // x-tile rows of the split and fused expert kernels
-    if ((p.gemv || p.down_rows) && ng_x > gemv_group_tokens()) ng_x = gemv_group_tokens();
+    if (p.gemv && ng_x > gemv_group_tokens()) ng_x = gemv_group_tokens();
+    if (p.down_rows && ng_x > down_rows_group_tokens()) ng_x = down_rows_group_tokens();
     p.NG = p.wide ? wide_group_tokens() : ng_x;
     p.n_chunks = p.small ? 0 : (T + kHistChunk - 1) / kHistChunk;
     const int pairs = T * 8;

@@ -243,3 +243,27 @@ def test_gemv_quantized_oracle(orc, fmt, shape):
         torch.cuda.synchronize()
         assert int(ws[:m.state_bytes()].view(torch.int32).abs().sum()) == 0
         assert_close(y.cpu().numpy(), orc.forward(lay, ids_o, w_o, g_o), f"{fmt} {shape} T={T}")
+
+
+def test_down_rows_groups_past_the_stage(orc):
+    """The default decode plan (matrix-core gate/up, down_rows) with groups of up to 8 tokens:
+    with 8 experts every token selects all of them, so every group past T = 4 has members beyond
+    the four whose h rows a ring stage holds; every output against the oracle."""
+    torch = _torch()
+    H, E, I, Is = 1024, 8, 512, 512
+    layer = small_layer(H, E, I, Is, 64, seed=88)
+    t = binding.device_weights(layer)
+    m = binding.MoeLayer(H, E, I, Is, 64, "bf16", t)
+    ws = m.workspace(64)
+    for T in (5, 8, 9, 17, 33, 64):
+        assert m.plan(T)[-2:] == ["gateup", "down_rows"], (T, m.plan(T))
+        lay = dict(layer)
+        lay["x"] = layer["x"][:T]
+        z_o = orc.logits(lay["x"], layer["router_w"], None)
+        ids_o, w_o, g_o = orc.select(z_o, E, True)
+        y = m.forward(t["x"][:T].contiguous(), routing=routing_device(ids_o, w_o, g_o), ws=ws)
+        y_int = m.forward(t["x"][:T].contiguous(), ws=ws)
+        torch.cuda.synchronize()
+        y_o = orc.forward(lay, ids_o, w_o, g_o)
+        assert_close(y.cpu().numpy(), y_o, f"E=8 T={T}")
+        assert_close(y_int.cpu().numpy(), y_o, f"E=8 T={T} (from x)")  # every token: all 8
