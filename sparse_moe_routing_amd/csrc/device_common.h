@@ -150,7 +150,9 @@ __device__ __forceinline__ uint4 e2m1x8_to_bf16x8(uint32_t w, float s) {
 // steps before a conversion block read the new values (measured on gfx950 for the FP4 ones:
 // exactly those steps' products were wrong). The FP8 conversions are the same instruction family
 // and passed as built, but nothing but register allocation kept them clear, so they take the guard
-// too (about 1 % of an FP8 round). The scheduling barriers keep every instruction on its side.
+// too (about 1 % of an FP8 round), except in the large-T gate/up kernel, where any such barrier
+// makes the compiler spill; bitwise tests against bf16 contexts holding the decoded weights pin
+// every path. The scheduling barriers keep every instruction on its side.
 __device__ __forceinline__ void mfma_operand_guard() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");

@@ -571,7 +571,10 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(2, 
         // the 16 rows of an operand read fall on 16 distinct 16-byte bank groups), refill the ring,
         // then the two steps' operands in matrix-core order
         auto half = [&](uint4 (&r)[kRT][2], int hh, int c, const unsigned char *xb) {
-            if constexpr (kFp8) mfma_operand_guard();  // the FP8 conversions as the MXFP4 ones
+            // (no operand guard before these FP8 conversions: any wait-state barrier here, even
+            // the bare s_nop sequence, makes the compiler spill 176 bytes per lane and doubles the
+            // kernel's time at T = 8192; the conversions' bits are pinned instead by the bitwise
+            // test against a bf16 context holding the decoded weights, which runs this kernel)
             if (rows_ok) {
 #pragma unroll
                 for (int t = 0; t < kRT; ++t)
