@@ -199,3 +199,34 @@ def test_create_without_gpu_reports_hip_error(lib):
     st, ctx = create(lib, good_config(), fake_weights())
     assert st in (binding.MOE_ERR_HIP, binding.MOE_ERR_UNSUPPORTED)
     assert not ctx.value
+
+
+@pytest.mark.slow
+def test_no_kernel_spills_to_scratch(tmp_path):
+    """Every gfx950 kernel of the library keeps its state in registers: the device code of each
+    source, compiled with the library's flags, declares no private (scratch) segment. A spill in a
+    streaming kernel has cost 2x at large T (the wait-state barrier case), so it is a build check."""
+    import glob
+    import shutil
+    import subprocess
+    from sparse_moe_routing_amd import build as lib_build
+    try:
+        cc = lib_build.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    # -Werror off here only: hipcc adds a link flag that a device-only compile leaves unused
+    flags = [f for f in lib_build.compile_flags() if f not in ("-fPIC", "-Werror")]
+    srcs = sorted(glob.glob(os.path.join(lib_build.CSRC, "*.hip")))
+    assert srcs
+    bad = []
+    for src in srcs:
+        out = tmp_path / (os.path.basename(src) + ".s")
+        cmd = [cc, *flags, "--cuda-device-only", "-S", src, "-o", str(out)]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        text = out.read_text()
+        for name, size in re.findall(r"\.name:\s+(\S+)\n(?:(?!\.name:).)*?\.private_segment_fixed_size:\s+(\d+)",
+                                     text, re.S):
+            if int(size) > 0:
+                bad.append((os.path.basename(src), name, int(size)))
+    assert not bad, bad
