@@ -199,7 +199,12 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.down_rows = cfg.dtype != MOE_F32 && T <= kSplitMaxTokens && down_rows_supported(H, I, Is);
     int ng_x = group_rows(c, T);  // x-tile rows of the split and fused expert kernels
     if (p.gemv && ng_x > gemv_group_tokens()) ng_x = gemv_group_tokens();
-    if (p.down_rows && ng_x > down_rows_group_tokens()) ng_x = down_rows_group_tokens();
+    // down_rows groups: at most 4 tokens up to 16 (an 8-token x tile halves the matrix-core
+    // gate/up kernel's blocks per CU: 2-4 us slower at T = 5..11), at most 8 above (a hot
+    // expert's weights are then read once per 8 of its tokens: skewed T = 64 162 -> 152 us,
+    // near-uniform T = 64 260 -> 255 us)
+    const int dr_group = T <= 16 ? gemv_group_tokens() : down_rows_group_tokens();
+    if (p.down_rows && ng_x > dr_group) ng_x = dr_group;
     p.NG = p.wide ? wide_group_tokens() : ng_x;
     p.n_chunks = p.small ? 0 : (T + kHistChunk - 1) / kHistChunk;
     const int pairs = T * 8;
