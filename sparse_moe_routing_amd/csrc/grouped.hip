@@ -1,0 +1,312 @@
+// grouped.hip - expert-stationary gate/up for prefill-sized rounds.
+//
+// At T = 8192 tokens each of the 256 experts draws ~256 (token, rank) pairs. The 64-token-group
+// kernels read an expert's weight slice once per group, about four times per call, and most of
+// the repeats come from beyond L2. Here a unit is (tile of up to 256 tokens of one expert, 128
+// intermediate rows): the block holds the fp32 products of the 256 weight rows (gate and up of
+// those 128 rows) with the tile's 256 token columns, so every weight line is read once per tile
+// and the tile's x rows once per 128 intermediate rows. The units of one tile (its 128-row
+// slices) are numbered next to each other and run side by side on one XCD, which then reads the
+// tile's gathered x rows from its own L2.
+//
+// Operands are staged in LDS in 64-element K slabs: one slab is 256 weight rows and 256 token
+// rows of 128 bytes each (bf16), double-buffered. x rows and bf16 weights are loaded straight into
+// LDS (buffer loads with the LDS flag: no registers held while in flight), whole 128-byte lines,
+// 8 rows per load instruction; FP8 codes come through registers to be widened. The next slab's
+// loads are in flight during the current slab's matrix instructions; one block barrier per slab.
+// Eight waves, two per SIMD: wave w multiplies weight rows 128 (w % 2) .. + 128 (four 16-row gate
+// tiles and the four matching up tiles, so h = silu(gate) * up is formed in its registers) by
+// token columns 64 (w / 2) .. + 64 (four 16-token tiles); a wave whose columns hold no token of
+// a ragged tile skips its matrix instructions. Operand fragments are read from LDS one k step
+// ahead of the matrix instructions that use them.
+//
+// Per output element the arithmetic is that of the 64-token-group kernels: the same matrix
+// instruction, the same k order (k step kappa covers elements 32 kappa .. 32 kappa + 31, lane
+// group q holding 32 kappa + 8 q .. + 7; the steps accumulate in increasing kappa), the same row
+// scales for FP8 weights (after the K loop), the same SiLU and hi/lo split of h; a token's bits do
+// not depend on which of them ran it.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kGWaves = 8;                      // two waves per SIMD
+constexpr int kGThreads = kGWaves * kWave;
+constexpr int kGTok = 256;                      // tokens per tile
+constexpr int kGRows = 128;                     // intermediate rows per unit
+constexpr int kGWRows = 2 * kGRows;             // weight rows per unit (gate, then up)
+constexpr int kGRowB = 128;                     // bytes of one staged row (64 bf16)
+constexpr int kGSlab = kGRowB / 2;              // K elements per slab
+constexpr int kGWBytes = kGWRows * kGRowB;      // weight part of a slab buffer (32 KB)
+constexpr int kGBuf = kGWBytes + kGTok * kGRowB;  // one slab buffer (64 KB)
+constexpr int kGSegs = kGWBytes / 1024 / kGWaves; // 1 KB segments per wave per stage part (4)
+constexpr int kGTT = kGTok / 4 / kTile;         // token tiles per wave (4)
+constexpr int kGRT = 8;                         // weight tiles per wave (4 gate, 4 up)
+constexpr int kGXcds = 8;                       // XCDs of the chip, each with its own L2
+
+__device__ __forceinline__ uint4 lds_read16(const unsigned char *p) {
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+// Byte position of 16-byte piece pc (0..7) of staged row r: rows 2m and 2m + 1 rotate their
+// pieces by m, so that the 16 rows one operand read touches fall on 16 distinct bank groups. The
+// rotation depends on r % 16 only, so rows 16 apart keep their pieces' order: a fragment of any
+// 16-row tile sits at the lane's own offset plus a constant.
+__device__ __forceinline__ int gpos(int r, int pc) { return r * kGRowB + ((pc ^ (r >> 1)) & 7) * 16; }
+constexpr int kGTileB = kTile * kGRowB;  // bytes of 16 staged rows
+
+// The two slab buffers (each a weight part and an x part) are separate objects, so that the
+// compiler can tell loads straight into one (buffer loads with the LDS flag) from operand reads of
+// the other; otherwise it waits for every such load before any LDS read.
+__shared__ __align__(16) unsigned char g_wslab0[kGWBytes], g_wslab1[kGWBytes];
+__shared__ __align__(16) unsigned char g_xslab0[kGBuf - kGWBytes], g_xslab1[kGBuf - kGWBytes];
+template <int B>
+__device__ __forceinline__ unsigned char *wslab() { return B ? g_wslab1 : g_wslab0; }
+template <int B>
+__device__ __forceinline__ unsigned char *xslab() { return B ? g_xslab1 : g_xslab0; }
+
+// 16 bytes per lane from buffer offset off into LDS: lane l writes bytes 16 l .. 16 l + 15 of the
+// 1 KB segment at seg (wave-uniform).
+template <int kAux>
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, unsigned char *seg, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)seg, 16, (int)off, 0, 0, kAux);
+}
+
+template <bool kFp8>
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_grp_kernel(GateUpParams p) {
+    using Op = OpBF16;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 15, q = lane >> 4;
+    const int rg = wave & 1, th = (wave >> 1) & 3;  // (the mask bounds the LDS offsets for the compiler)
+
+    // unit of this block: blocks b, b + 8, ... run on one XCD and take one contiguous eighth of
+    // the units, in order (a tile's slices next to each other)
+    const int S = p.S;
+    const int nunits = p.num_groups[0] * S;
+    const int per = (nunits + kGXcds - 1) / kGXcds;
+    const int idx = blockIdx.x / kGXcds;
+    const int u = (blockIdx.x % kGXcds) * per + idx;
+    if (idx >= per || u >= nunits) return;  // uniform over the block
+    const int gi = u / S, j = u - gi * S;
+    const int4 grp = p.groups[gi];
+    const int e = grp.x, start = grp.y, n = grp.z;
+    const bool shared = e == p.E;
+    const int Ie = shared ? p.Is : p.I;
+    if (j * kGRows >= Ie) return;  // uniform (Ie is a multiple of kGRows)
+    const int i0 = j * kGRows + rg * (kGRows / 2);  // the wave's first intermediate row
+
+    constexpr int kWB = kFp8 ? 1 : 2;  // bytes per stored weight
+    const size_t wrow = (size_t)p.H * kWB;
+    const unsigned char *wbase = reinterpret_cast<const unsigned char *>(shared ? p.sgu : p.gate_up) +
+                                 (shared ? 0 : (size_t)e * 2 * Ie * wrow);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wbase, (uint32_t)(2 * Ie * wrow));
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.x, (uint32_t)((size_t)p.T * p.H * 2));
+    // weight row of stage row R: tile t = R / 16 % 8 of wave group R / 128 (gate t < 4, up above)
+    auto wrow_of = [&](int R) {
+        const int t = (R >> 4) & 7;
+        return (t < 4 ? 0 : Ie) + j * kGRows + (R >> 7) * (kGRows / 2) + (t & 3) * kTile + (R & 15);
+    };
+    // Straight-to-LDS loads (x rows; bf16 weights): wave w fills the 1 KB segments 4 w + a (stage
+    // rows 32 w + 8 a .. + 8) of both parts of a slab buffer; lane l writes position l % 8 of row
+    // l / 8 of its segment, i.e. it loads the piece the row's rotation puts there.
+    uint32_t xoff[kGSegs], woff[kFp8 ? 1 : kGSegs];
+#pragma unroll
+    for (int a = 0; a < kGSegs; ++a) {
+        const int R = 8 * kGSegs * wave + 8 * a + (lane >> 3);
+        const int pc = ((lane & 7) ^ (R >> 1)) & 7;
+        const int m = R < n ? R : 0;  // token rows past the tile repeat row 0 (columns dropped)
+        const int tok = shared ? start + m : (p.perm[start + m] >> 3);
+        xoff[a] = (uint32_t)((size_t)tok * p.H * 2) + pc * 16;
+        if constexpr (!kFp8) woff[a] = (uint32_t)(wrow_of(R) * wrow) + pc * 16;
+    }
+    auto issue = [&](unsigned char *wbuf, unsigned char *xbuf, int st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int a = 0; a < kGSegs; ++a)
+            lds_load16<0>(rx, xbuf + (kGSegs * wave + a) * 1024, xoff[a] + st * kGRowB);
+        if constexpr (!kFp8) {
+#pragma unroll
+            for (int a = 0; a < kGSegs; ++a)
+                lds_load16<kBufNT>(rw, wbuf + (kGSegs * wave + a) * 1024, woff[a] + st * kGRowB);
+        }
+    };
+    // FP8 codes go through registers (widened while staged): thread tid takes 16-byte piece lp of
+    // the 128-byte code line of stage rows 64 a + lr (two slabs per line), line L in register set
+    // L % 2, requested two slabs ahead of its first slab.
+    constexpr int kW = kFp8 ? kGWRows / (kGThreads / 8) : 1;  // line loads per thread (4)
+    const int lr = tid >> 3, lp = tid & 7;
+    uint32_t w8off[kW];
+    if constexpr (kFp8) {
+#pragma unroll
+        for (int a = 0; a < kW; ++a) w8off[a] = (uint32_t)(wrow_of(kGThreads / 8 * a + lr) * wrow) + lp * 16;
+    }
+    uint4 wa[kW], wb[kW];
+    auto load_w8 = [&](uint4 (&wr)[kW], int line) __attribute__((always_inline)) {
+        if constexpr (kFp8) {
+#pragma unroll
+            for (int a = 0; a < kW; ++a) wr[a] = bload16_stream(rw, w8off[a] + line * kGRowB);
+        }
+    };
+    const int st_off8a = gpos(lr, 2 * (lp & 3)), st_off8b = gpos(lr, 2 * (lp & 3) + 1);
+    auto store_w8 = [&](unsigned char *b, const uint4 (&wr)[kW], int st) __attribute__((always_inline)) {
+        if constexpr (kFp8) {
+#pragma unroll
+            for (int a = 0; a < kW; ++a) {
+                // piece lp holds codes 16 lp .. + 15 of the line: slab lp / 4, bf16 pieces
+                // 2 (lp % 4) and 2 (lp % 4) + 1 of it (exact widening)
+                if ((lp >> 2) == (st & 1)) {
+                    const int r0 = a * (kGThreads / 8) * kGRowB;
+                    *reinterpret_cast<uint4 *>(b + r0 + st_off8a) = e4m3x8_to_bf16x8(wr[a].x, wr[a].y);
+                    *reinterpret_cast<uint4 *>(b + r0 + st_off8b) = e4m3x8_to_bf16x8(wr[a].z, wr[a].w);
+                }
+            }
+        }
+    };
+
+    f32x4_t acc[kGRT][kGTT];
+#pragma unroll
+    for (int t = 0; t < kGRT; ++t)
+#pragma unroll
+        for (int tt = 0; tt < kGTT; ++tt) acc[t][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // token tiles of this wave that hold tokens (uniform)
+    int nt_w = (n - th * (kGTok / 4) + kTile - 1) / kTile;
+    nt_w = nt_w < 0 ? 0 : nt_w > kGTT ? kGTT : nt_w;
+
+    // Operand reads run one k step ahead of the matrix instructions: while k step s's 32
+    // instructions run, step s + 1's fragments are read into the other register set (the last
+    // step of a slab is multiplied after the barrier, from registers).
+    const int rd_off[2] = {gpos(col, q), gpos(col, 4 + q)};
+    auto rd = [&](uint4 (&a)[kGRT], uint4 (&b)[kGTT], const unsigned char *wbuf, const unsigned char *xbuf,
+                  int s) __attribute__((always_inline)) {
+        const unsigned char *wb_ = wbuf + rg * kGRT * kGTileB;
+        const unsigned char *xb_ = xbuf + th * kGTT * kGTileB;
+#pragma unroll
+        for (int t = 0; t < kGRT; ++t) a[t] = lds_read16(wb_ + t * kGTileB + rd_off[s]);
+#pragma unroll
+        for (int tt = 0; tt < kGTT; ++tt) b[tt] = lds_read16(xb_ + tt * kGTileB + rd_off[s]);
+    };
+    auto mm = [&](const uint4 (&a)[kGRT], const uint4 (&b)[kGTT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tt = 0; tt < kGTT; ++tt)
+#pragma unroll
+            for (int t = 0; t < kGRT; ++t) Op::mma(acc[t][tt], a[t], b[tt]);
+    };
+    uint4 a0[kGRT], b0[kGTT], a1[kGRT], b1[kGTT];
+
+    const int nslab = p.H / kGSlab;  // a multiple of 4
+    // slab st (in buffer B = st % 2): request slab st + 1 into the other buffer (read by slab
+    // st - 1, a barrier ago) and, FP8, the code line two slabs ahead; k step 0 of slab st into a0
+    // / b0 while slab st - 1's k step 1 is multiplied, k step 1 into a1 / b1 while k step 0 is
+    // multiplied; FP8: widen slab st + 1's codes into the other buffer; wait for this wave's
+    // straight-to-LDS loads, barrier
+    auto slab = [&](auto bsel, int st, uint4 (&wn)[kW], const uint4 (&ws)[kW]) __attribute__((always_inline)) {
+        constexpr int B = decltype(bsel)::value;
+        if (st + 1 < nslab) issue(wslab<1 - B>(), xslab<1 - B>(), st + 1);
+        // an FP8 line requested after this slab's straight-to-LDS loads (uniform)
+        const bool line = kFp8 && st + 2 < nslab && B == 0;
+        if (line) load_w8(wn, (st + 2) >> 1);
+        if (nt_w > 0) {
+            rd(a0, b0, wslab<B>(), xslab<B>(), 0);
+            if (st > 0) mm(a1, b1);
+            rd(a1, b1, wslab<B>(), xslab<B>(), 1);
+            mm(a0, b0);
+        }
+        if constexpr (kFp8) {
+            if (st + 1 < nslab) {
+                mfma_operand_guard();  // the scaled conversions after the matrix steps
+                store_w8(wslab<1 - B>(), ws, st + 1);
+            }
+        }
+        static_assert(!kFp8 || kW == 4, "vmcnt below");
+        if (line) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): all but the line just requested
+        else __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
+        __syncthreads();
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    load_w8(wa, 0);  // FP8: line 0 (slabs 0 and 1) in set a
+    issue(wslab<0>(), xslab<0>(), 0);
+    store_w8(wslab<0>(), wa, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int st = 0; st < nslab; st += 4) {  // FP8: line L in set L % 2
+        slab(B0{}, st, wb, wa);
+        slab(B1{}, st + 1, wb, wb);
+        slab(B0{}, st + 2, wa, wb);
+        slab(B1{}, st + 3, wa, wa);
+    }
+    if (nt_w > 0) mm(a1, b1);  // k step 1 of the last slab
+    if (nt_w == 0) return;
+
+    if constexpr (kFp8) {  // the rows' dequantization scales (gate rows, then up rows)
+        const float *sc = shared ? p.sgu_scale : p.gu_scale + (size_t)e * 2 * Ie;
+#pragma unroll
+        for (int t = 0; t < kGRT; ++t)
+#pragma unroll
+            for (int tt = 0; tt < kGTT; ++tt)
+                if (tt < nt_w)
+                    scale_rows(acc[t][tt], sc + (t < 4 ? 0 : Ie) + i0 + kTile * (t & 3) + 4 * q);
+    }
+    uint16_t *hp = reinterpret_cast<uint16_t *>(p.h);
+#pragma unroll
+    for (int tt = 0; tt < kGTT; ++tt) {
+        const int m = th * (kGTok / 4) + tt * kTile + col;  // token row of this lane's column
+        if (tt >= nt_w || m >= n) continue;
+        const int slot = shared ? p.T * kTopK + start + m : p.perm[start + m];
+#pragma unroll
+        for (int g2 = 0; g2 < kGRT / 2; ++g2) {
+            const f32x4_t ga = acc[g2][tt], up = acc[kGRT / 2 + g2][tt];
+            float hv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hv[r] = ga[r] / (1.0f + expf(-ga[r])) * up[r];
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hi[r] = f32_to_bf16_bits(hv[r]);
+                lo[r] = f32_to_bf16_bits(hv[r] - bf16_bits_to_f32(hi[r]));
+            }
+            const size_t off = (size_t)slot * p.Imax + i0 + g2 * kTile + 4 * q;
+            *reinterpret_cast<uint2 *>(hp + off) = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+            *reinterpret_cast<uint2 *>(hp + p.plane + off) =
+                uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+        }
+    }
+}
+
+}  // namespace
+
+int grp_tile_tokens() { return kGTok; }
+int grp_rows_per_gateup_unit() { return kGRows; }
+size_t gateup_grp_lds() { return 0; }  // static LDS (two slab buffers)
+
+bool gateup_grp_supported(int H, int I, int Is, int dtype, long x_bytes) {
+    if (dtype != 1 && dtype != 2) return false;
+    if (H % (4 * kGSlab) || I % kGRows || Is % kGRows) return false;  // slabs in fours
+    const long wbytes = 2L * (I > Is ? I : Is) * H * (dtype == 2 ? 1 : 2);
+    return wbytes < (1L << 31) && x_bytes < (1L << 31);
+}
+
+hipError_t prepare_grouped_kernels() {
+    hipError_t err;
+    const void *k[] = {reinterpret_cast<const void *>(&gateup_grp_kernel<false>),
+                       reinterpret_cast<const void *>(&gateup_grp_kernel<true>)};
+    for (const void *f : k)
+        if ((err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)gateup_grp_lds())) != hipSuccess)
+            return err;
+    return hipSuccess;
+}
+
+// dtype: 1 bf16, 2 bf16 activations with FP8 E4M3 weights. p.groups: tiles of at most
+// grp_tile_tokens() tokens; p.S: grp_rows_per_gateup_unit()-row slices of Imax; grid: a multiple
+// of 8 holding every unit (8 * ceil(max tiles * S / 8)).
+hipError_t launch_gateup_grp(const GateUpParams &p, int dtype, int grid, hipStream_t s) {
+    if (grid % kGXcds || p.NG != kGTok) return hipErrorInvalidValue;  // a caller bug
+    if (dtype == 2) launch_k(gateup_grp_kernel<true>, grid, kGThreads, gateup_grp_lds(), s, p);
+    else launch_k(gateup_grp_kernel<false>, grid, kGThreads, gateup_grp_lds(), s, p);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -54,6 +54,9 @@ struct BucketParams {
     int32_t *hist;       // [n_chunks][E] (multi-block path); becomes per-chunk bases
     int4 *groups;        // [max_groups]: {expert (E = shared), start, n, 0}
     int32_t *num_groups; // [1]
+    int NG2;             // > 0: a second table of groups of up to NG2 tokens (same order)
+    int4 *groups2;       // [max_groups for NG2]
+    int32_t *num_groups2;  // [1]
 };
 
 // Expert stage: gate/up + SwiGLU + down for (group, slice chunk) units.
@@ -152,6 +155,13 @@ int big_rows_per_gateup_unit();   // intermediate rows per gateup_big unit
 hipError_t launch_gateup_big(const GateUpParams &p, int dtype, int grid, hipStream_t s);  // bf16 / FP8
 int big_rows_per_down_unit();     // rows of y per down_big unit
 hipError_t launch_down_big(const DownParams &p, int dtype, int grid, hipStream_t s);  // bf16 / FP8
+// Expert-stationary gate/up for prefill-sized rounds (grouped.hip): bf16 / FP8 weights, tiles of
+// up to grp_tile_tokens() tokens of one expert (the second group table).
+int grp_tile_tokens();
+int grp_rows_per_gateup_unit();
+bool gateup_grp_supported(int H, int I, int Is, int dtype, long x_bytes);
+hipError_t prepare_grouped_kernels();
+hipError_t launch_gateup_grp(const GateUpParams &p, int dtype, int grid, hipStream_t s);
 // Decode expert stage on the vector ALUs (gemv.hip): bf16 shapes gemv_supported accepts.
 bool gemv_supported(int H, int I, int Is);
 bool down_rows_supported(int H, int I, int Is);

@@ -40,6 +40,7 @@ struct moe_ctx {
     int num_cus;
     int s;         // intermediate slice width of the expert kernel
     int gemv_max_tokens;  // decode rounds up to this T run the vector-ALU expert kernels
+    int grp_min_tokens;   // rounds from this T run the expert-stationary gate/up (0: never)
     void *scratch; // device address of the static scratch array on this context's device
 };
 
@@ -74,6 +75,7 @@ constexpr int kHistChunk = 16;
 constexpr int kSelBucketMaxTokens = 256;
 constexpr int kSplitMaxTokens = 64;   // 8-token groups up to here, 64-token groups above
 constexpr int kBigMinTokens = 1536;     // bf16 from here: gateup_big in place of gateup_wide
+constexpr int kGrpMinTokens = 1536;     // bf16 / FP8 from here: gateup_grp (256-token tiles)
 
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -115,10 +117,13 @@ struct Plan {
     bool down_big = false;       // wide, bf16 or FP8, H a multiple of 512, T <= 256 or big
     bool gemv = false;           // split, bf16 activations: gateup_gemv in place of gateup
     bool down_rows = false;      // split, bf16 activations: down_rows in place of down
+    bool grp = false;            // wide, bf16 or FP8: gateup_grp for the gate/up kernel
+    int NG2 = 0, max_groups2 = 0, grp_grid = 0;
     int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;
     size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
-           o_hist = 0, o_groups = 0, o_ngroups = 0, o_ypart = 0, o_h = 0, total = 0;
+           o_hist = 0, o_groups = 0, o_ngroups = 0, o_groups2 = 0, o_ngroups2 = 0, o_ypart = 0,
+           o_h = 0, total = 0;
 };
 
 // Activation (x, router) element type of a config: bf16 for FP8 expert weights.
@@ -245,6 +250,17 @@ Plan make_plan(const moe_ctx *c, int T) {
             p.gu_grid = (int)(b_units < b_cap ? b_units : b_cap);
             if (p.gu_grid >= 8) p.gu_grid -= p.gu_grid % 8;  // whole rounds over the 8 XCDs
         }
+        // expert-stationary gate/up: tiles of up to 256 tokens of one expert (a second group
+        // table), 8 * ceil(units / 8) blocks of one unit each
+        p.grp = c->grp_min_tokens > 0 && T >= c->grp_min_tokens &&
+                gateup_grp_supported(H, I, Is, expert_kdt(c), (long)T * H * esz);
+        if (p.grp) {
+            p.NG2 = grp_tile_tokens();
+            p.max_groups2 = max_groups_for(c, T, p.NG2);
+            const long units = (long)p.max_groups2 * (Imax / grp_rows_per_gateup_unit());
+            p.grp_grid = (int)((units + 7) / 8 * 8);
+            p.big = false;
+        }
         // down_big with gateup_big and up to 256 tokens (measured: skewed T = 192 51.1 against
         // 53.8 us; T = 768 140.1 against 137.1 us for down_wide). The big pair from 1536 tokens:
         // T = 2048 step 527 against 611 us, T = 1024 430 against 403 us.
@@ -290,6 +306,8 @@ Plan make_plan(const moe_ctx *c, int T) {
     p.o_hist = take((size_t)p.n_chunks * E * 4);
     p.o_groups = take((size_t)p.max_groups * 16);
     p.o_ngroups = take(16);
+    p.o_groups2 = take((size_t)p.max_groups2 * 16);
+    p.o_ngroups2 = take(p.grp ? 16 : 0);
     const bool per_slot = p.split || p.wide;  // [slots][H] weighted outputs and an h buffer
     p.o_ypart = take(p.down_rows ? 0 : per_slot ? (size_t)p.slots * H * 4
                                                 : (size_t)p.n_sc * p.slots * H * 4);
@@ -371,6 +389,9 @@ BucketParams bucket_params(const moe_ctx *c, const Plan &p, char *ws, const int3
     bp.hist = reinterpret_cast<int32_t *>(ws + p.o_hist);
     bp.groups = reinterpret_cast<int4 *>(ws + p.o_groups);
     bp.num_groups = reinterpret_cast<int32_t *>(ws + p.o_ngroups);
+    bp.NG2 = p.NG2;
+    bp.groups2 = p.grp ? reinterpret_cast<int4 *>(ws + p.o_groups2) : nullptr;
+    bp.num_groups2 = p.grp ? reinterpret_cast<int32_t *>(ws + p.o_ngroups2) : nullptr;
     return bp;
 }
 
@@ -531,6 +552,15 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
         gp.sgu_mx = mx ? static_cast<const uint8_t *>(c->w.shared_gate_up_scale) : nullptr;
         if (p.gemv)
             L.step("gateup_gemv", [&] { return launch_gateup_gemv(gp, expert_kdt(c), c->num_cus, L.stream); });
+        else if (p.grp)
+            L.step("gateup_grp", [&] {
+                GateUpParams g2 = gp;
+                g2.groups = reinterpret_cast<const int4 *>(ws + p.o_groups2);
+                g2.num_groups = reinterpret_cast<const int32_t *>(ws + p.o_ngroups2);
+                g2.S = p.Imax / grp_rows_per_gateup_unit();
+                g2.NG = p.NG2;
+                return launch_gateup_grp(g2, expert_kdt(c), p.grp_grid, L.stream);
+            });
         else if (p.big)
             L.step("gateup_big", [&] { return launch_gateup_big(gp, expert_kdt(c), p.gu_grid, L.stream); });
         else if (p.wide)
@@ -690,6 +720,7 @@ hipError_t raise_lds_caps(const moe_ctx *c, const Plan &p_max) {
     }
     if (!g_wide_ready) {
         if ((err = prepare_wide_kernels()) != hipSuccess) return err;
+        if ((err = prepare_grouped_kernels()) != hipSuccess) return err;
         g_wide_ready = true;
     }
     return hipSuccess;
@@ -771,6 +802,16 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
             return MOE_ERR_INVALID_ARG;
         }
         c->gemv_max_tokens = (int)v;
+    }
+    c->grp_min_tokens = kGrpMinTokens;
+    if (const char *env = getenv("MOE_GRP_MIN_TOKENS")) {  // 0: never
+        char *end = nullptr;
+        const long v = strtol(env, &end, 10);
+        if (end == env || *end != '\0' || v < 0 || (v > 0 && v <= kSplitMaxTokens) || v > (1L << 30)) {
+            delete c;
+            return MOE_ERR_INVALID_ARG;
+        }
+        c->grp_min_tokens = (int)v;
     }
     const int Is = cfg->shared_inter;
     c->s = (cfg->inter % 64 == 0 && Is % 64 == 0) ? 64 : (cfg->inter % 32 == 0 && Is % 32 == 0) ? 32 : 16;

@@ -185,6 +185,27 @@ __device__ void write_tables(const BucketParams &bp, int cnt, S &s) {
         bp.offsets[bp.E] = s.tot[0];
         bp.num_groups[0] = nsh + s.tot[1];
     }
+    if (bp.NG2 > 0) {  // uniform: the second table, groups of up to NG2 tokens
+        __syncthreads();  // every thread has read its scans
+        const int ng2 = (c + bp.NG2 - 1) / bp.NG2;
+        if (tid < 256) {
+            s.a[tid] = 0;
+            s.b[tid] = ng2;
+        }
+        scan_experts(s);
+        const int gbase2 = tid < 256 ? s.b[tid] : 0;
+        const int nsh2 = bp.has_shared ? (bp.T + bp.NG2 - 1) / bp.NG2 : 0;
+        if (own)
+            for (int gg = 0; gg < ng2; ++gg)
+                bp.groups2[nsh2 + gbase2 + gg] =
+                    make_int4(tid, off + gg * bp.NG2, min(bp.NG2, c - gg * bp.NG2), 0);
+        if (tid < nsh2)
+            bp.groups2[tid] = make_int4(bp.E, tid * bp.NG2, min(bp.NG2, bp.T - tid * bp.NG2), 0);
+        if (tid == 0) bp.num_groups2[0] = nsh2 + s.tot[1];
+        __syncthreads();  // every thread has read s.b
+        if (tid < 256) s.a[tid] = off;  // as after the first table: the experts' offsets
+        __syncthreads();
+    }
 }
 
 // The whole bucketing of n <= 64 pairs by one wave (lane l holds pair l), with no block barrier
