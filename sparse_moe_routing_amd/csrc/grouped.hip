@@ -1,24 +1,25 @@
 // grouped.hip - expert-stationary gate/up for prefill-sized rounds.
 //
-// At T = 8192 tokens each of the 256 experts draws ~256 (token, rank) pairs. The 64-token-group
-// kernels read an expert's weight slice once per group, about four times per call, and most of
-// the repeats come from beyond L2. Here a unit is (tile of up to 256 tokens of one expert, 128
-// intermediate rows): the block holds the fp32 products of the 256 weight rows (gate and up of
-// those 128 rows) with the tile's 256 token columns, so every weight line is read once per tile
-// and the tile's x rows once per 128 intermediate rows. The units of one tile (its 128-row
-// slices) are numbered next to each other and run side by side on one XCD, which then reads the
-// tile's gathered x rows from its own L2.
+// At T = 8192 tokens each of the 256 experts draws 256 +- 16 (token, rank) pairs. The
+// 64-token-group kernels read an expert's weight slice once per group, about four times per call,
+// and most of the repeats come from beyond L2. Here a unit is (tile of up to 320 tokens of one
+// expert, 128 intermediate rows): the block holds the fp32 products of the 256 weight rows (gate
+// and up of those 128 rows) with the tile's 320 token columns, so every weight line is read once
+// per tile (once per call for almost every expert at T = 8192) and the tile's x rows once per 128
+// intermediate rows. The units of one tile (its 128-row slices) are numbered next to each other
+// and run side by side on one XCD, which then reads the tile's gathered x rows from its own L2.
+// The time of a unit is mostly the streaming of its 1 MB of weights, whatever its token count,
+// so the tile size is set by the number of units, not by the matrix work.
 //
-// Operands are staged in LDS in 64-element K slabs: one slab is 256 weight rows and 256 token
+// Operands are staged in LDS in 64-element K slabs: one slab is 256 weight rows and 320 token
 // rows of 128 bytes each (bf16), double-buffered. x rows and bf16 weights are loaded straight into
 // LDS (buffer loads with the LDS flag: no registers held while in flight), whole 128-byte lines,
 // 8 rows per load instruction; FP8 codes come through registers to be widened. The next slab's
 // loads are in flight during the current slab's matrix instructions; one block barrier per slab.
 // Eight waves, two per SIMD: wave w multiplies weight rows 128 (w % 2) .. + 128 (four 16-row gate
 // tiles and the four matching up tiles, so h = silu(gate) * up is formed in its registers) by
-// token columns 64 (w / 2) .. + 64 (four 16-token tiles); a wave whose columns hold no token of
-// a ragged tile skips its matrix instructions. Operand fragments are read from LDS one k step
-// ahead of the matrix instructions that use them.
+// token columns 80 (w / 2) .. + 80 (five 16-token tiles); a wave whose columns hold no token of
+// the tile skips its matrix instructions.
 //
 // Per output element the arithmetic is that of the 64-token-group kernels: the same matrix
 // instruction, the same k order (k step kappa covers elements 32 kappa .. 32 kappa + 31, lane
@@ -34,15 +35,16 @@ namespace {
 
 constexpr int kGWaves = 8;                      // two waves per SIMD
 constexpr int kGThreads = kGWaves * kWave;
-constexpr int kGTok = 256;                      // tokens per tile
+constexpr int kGTok = 320;                      // tokens per tile
 constexpr int kGRows = 128;                     // intermediate rows per unit
 constexpr int kGWRows = 2 * kGRows;             // weight rows per unit (gate, then up)
 constexpr int kGRowB = 128;                     // bytes of one staged row (64 bf16)
 constexpr int kGSlab = kGRowB / 2;              // K elements per slab
 constexpr int kGWBytes = kGWRows * kGRowB;      // weight part of a slab buffer (32 KB)
-constexpr int kGBuf = kGWBytes + kGTok * kGRowB;  // one slab buffer (64 KB)
-constexpr int kGSegs = kGWBytes / 1024 / kGWaves; // 1 KB segments per wave per stage part (4)
-constexpr int kGTT = kGTok / 4 / kTile;         // token tiles per wave (4)
+constexpr int kGXBytes = kGTok * kGRowB;        // x part of a slab buffer (40 KB)
+constexpr int kGSegs = kGWBytes / 1024 / kGWaves; // 1 KB weight segments per wave (4)
+constexpr int kGXSegs = kGXBytes / 1024 / kGWaves; // 1 KB x segments per wave (5)
+constexpr int kGTT = kGTok / 4 / kTile;         // token tiles per wave (5)
 constexpr int kGRT = 8;                         // weight tiles per wave (4 gate, 4 up)
 constexpr int kGXcds = 8;                       // XCDs of the chip, each with its own L2
 
@@ -61,7 +63,7 @@ constexpr int kGTileB = kTile * kGRowB;  // bytes of 16 staged rows
 // compiler can tell loads straight into one (buffer loads with the LDS flag) from operand reads of
 // the other; otherwise it waits for every such load before any LDS read.
 __shared__ __align__(16) unsigned char g_wslab0[kGWBytes], g_wslab1[kGWBytes];
-__shared__ __align__(16) unsigned char g_xslab0[kGBuf - kGWBytes], g_xslab1[kGBuf - kGWBytes];
+__shared__ __align__(16) unsigned char g_xslab0[kGXBytes], g_xslab1[kGXBytes];
 template <int B>
 __device__ __forceinline__ unsigned char *wslab() { return B ? g_wslab1 : g_wslab0; }
 template <int B>
@@ -109,23 +111,33 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int t = (R >> 4) & 7;
         return (t < 4 ? 0 : Ie) + j * kGRows + (R >> 7) * (kGRows / 2) + (t & 3) * kTile + (R & 15);
     };
-    // Straight-to-LDS loads (x rows; bf16 weights): wave w fills the 1 KB segments 4 w + a (stage
-    // rows 32 w + 8 a .. + 8) of both parts of a slab buffer; lane l writes position l % 8 of row
-    // l / 8 of its segment, i.e. it loads the piece the row's rotation puts there.
-    uint32_t xoff[kGSegs], woff[kFp8 ? 1 : kGSegs];
+    // Straight-to-LDS loads (x rows; bf16 weights): wave w fills the 1 KB segments 5 w + a of the
+    // x part (token rows 40 w + 8 a .. + 8) and 4 w + a of the weight part (stage rows
+    // 32 w + 8 a .. + 8) of a slab buffer; lane l writes position l % 8 of row l / 8 of its
+    // segment, i.e. it loads the piece the row's rotation puts there.
+    uint32_t xoff[kGXSegs], woff[kFp8 ? 1 : kGSegs];
 #pragma unroll
-    for (int a = 0; a < kGSegs; ++a) {
-        const int R = 8 * kGSegs * wave + 8 * a + (lane >> 3);
+    for (int a = 0; a < kGXSegs; ++a) {
+        const int R = 8 * kGXSegs * wave + 8 * a + (lane >> 3);
         const int pc = ((lane & 7) ^ (R >> 1)) & 7;
         const int m = R < n ? R : 0;  // token rows past the tile repeat row 0 (columns dropped)
         const int tok = shared ? start + m : (p.perm[start + m] >> 3);
         xoff[a] = (uint32_t)((size_t)tok * p.H * 2) + pc * 16;
-        if constexpr (!kFp8) woff[a] = (uint32_t)(wrow_of(R) * wrow) + pc * 16;
     }
+    if constexpr (!kFp8) {
+#pragma unroll
+        for (int a = 0; a < kGSegs; ++a) {
+            const int R = 8 * kGSegs * wave + 8 * a + (lane >> 3);
+            woff[a] = (uint32_t)(wrow_of(R) * wrow) + (((lane & 7) ^ (R >> 1)) & 7) * 16;
+        }
+    }
+    // (x segments wholly past the tile's tokens are not loaded: their columns are dropped; a
+    // ragged tile then streams little more than its weights)
     auto issue = [&](unsigned char *wbuf, unsigned char *xbuf, int st) __attribute__((always_inline)) {
 #pragma unroll
-        for (int a = 0; a < kGSegs; ++a)
-            lds_load16<0>(rx, xbuf + (kGSegs * wave + a) * 1024, xoff[a] + st * kGRowB);
+        for (int a = 0; a < kGXSegs; ++a)
+            if (8 * (kGXSegs * wave + a) < n)  // uniform
+                lds_load16<0>(rx, xbuf + (kGXSegs * wave + a) * 1024, xoff[a] + st * kGRowB);
         if constexpr (!kFp8) {
 #pragma unroll
             for (int a = 0; a < kGSegs; ++a)
@@ -171,12 +183,10 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
         for (int tt = 0; tt < kGTT; ++tt) acc[t][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // token tiles of this wave that hold tokens (uniform)
-    int nt_w = (n - th * (kGTok / 4) + kTile - 1) / kTile;
+    int nt_w = (n - th * kGTT * kTile + kTile - 1) / kTile;
     nt_w = nt_w < 0 ? 0 : nt_w > kGTT ? kGTT : nt_w;
 
-    // Operand reads run one k step ahead of the matrix instructions: while k step s's 32
-    // instructions run, step s + 1's fragments are read into the other register set (the last
-    // step of a slab is multiplied after the barrier, from registers).
+    // a k step: the wave's operand fragments (8 weight, 5 token) are read, then multiplied
     const int rd_off[2] = {gpos(col, q), gpos(col, 4 + q)};
     auto rd = [&](uint4 (&a)[kGRT], uint4 (&b)[kGTT], const unsigned char *wbuf, const unsigned char *xbuf,
                   int s) __attribute__((always_inline)) {
@@ -193,13 +203,12 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
             for (int t = 0; t < kGRT; ++t) Op::mma(acc[t][tt], a[t], b[tt]);
     };
-    uint4 a0[kGRT], b0[kGTT], a1[kGRT], b1[kGTT];
+    uint4 a0[kGRT], b0[kGTT];
 
     const int nslab = p.H / kGSlab;  // a multiple of 4
     // slab st (in buffer B = st % 2): request slab st + 1 into the other buffer (read by slab
-    // st - 1, a barrier ago) and, FP8, the code line two slabs ahead; k step 0 of slab st into a0
-    // / b0 while slab st - 1's k step 1 is multiplied, k step 1 into a1 / b1 while k step 0 is
-    // multiplied; FP8: widen slab st + 1's codes into the other buffer; wait for this wave's
+    // st - 1, a barrier ago) and, FP8, the code line two slabs ahead; multiply the slab's two k
+    // steps; FP8: widen slab st + 1's codes into the other buffer; wait for this wave's
     // straight-to-LDS loads, barrier
     auto slab = [&](auto bsel, int st, uint4 (&wn)[kW], const uint4 (&ws)[kW]) __attribute__((always_inline)) {
         constexpr int B = decltype(bsel)::value;
@@ -208,10 +217,11 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const bool line = kFp8 && st + 2 < nslab && B == 0;
         if (line) load_w8(wn, (st + 2) >> 1);
         if (nt_w > 0) {
-            rd(a0, b0, wslab<B>(), xslab<B>(), 0);
-            if (st > 0) mm(a1, b1);
-            rd(a1, b1, wslab<B>(), xslab<B>(), 1);
-            mm(a0, b0);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                rd(a0, b0, wslab<B>(), xslab<B>(), s);
+                mm(a0, b0);
+            }
         }
         if constexpr (kFp8) {
             if (st + 1 < nslab) {
@@ -237,7 +247,6 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         slab(B0{}, st + 2, wa, wb);
         slab(B1{}, st + 3, wa, wa);
     }
-    if (nt_w > 0) mm(a1, b1);  // k step 1 of the last slab
     if (nt_w == 0) return;
 
     if constexpr (kFp8) {  // the rows' dequantization scales (gate rows, then up rows)
@@ -252,7 +261,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     uint16_t *hp = reinterpret_cast<uint16_t *>(p.h);
 #pragma unroll
     for (int tt = 0; tt < kGTT; ++tt) {
-        const int m = th * (kGTok / 4) + tt * kTile + col;  // token row of this lane's column
+        const int m = (th * kGTT + tt) * kTile + col;  // token row of this lane's column
         if (tt >= nt_w || m >= n) continue;
         const int slot = shared ? p.T * kTopK + start + m : p.perm[start + m];
 #pragma unroll

@@ -557,10 +557,14 @@ def test_fp8_batch_invariance_bitwise():
     torch.cuda.synchronize()
     assert m.plan(32)[-1] == "down_rows" and m.plan(200)[-3:] == ["gateup_wide", "down_big", "combine"]
     assert m.plan(300)[-3:] == ["gateup_wide", "down_wide", "combine"]
-    assert m.plan(1600)[-3:] == ["gateup_grp", "down_big", "combine"]
+    assert m.plan(1600)[-3:] == ["gateup_big", "down_big", "combine"]
     assert torch.equal(y32[:4], y4)
     assert torch.equal(y300[:32], y200[:32]) and torch.equal(y300[288:300], y200[:12])
     assert torch.equal(y1600[:32], y200[:32]) and torch.equal(y1600[1568:], y200[:32])
+    y3200 = m.forward(torch.cat([x] * 100).contiguous())  # the expert-stationary gate/up
+    torch.cuda.synchronize()
+    assert m.plan(3200)[-3:] == ["gateup_grp", "down_big", "combine"]
+    assert torch.equal(y3200[:32], y200[:32]) and torch.equal(y3200[3168:], y200[:32])
     assert_close(y200[:32].cpu().numpy(), y32.cpu().numpy(), "fp8 regimes")
 
 
@@ -585,7 +589,7 @@ def test_mxfp4_batch_invariance_bitwise():
 
 
 GRP_SHAPES = [  # (format, H, E, I, Is, T): T >= 1536 runs the expert-stationary gate/up
-    ("bf16", 1024, 16, 256, 384, 1600),   # ~800 pairs per expert: four tiles, a ragged last one
+    ("bf16", 1024, 16, 256, 384, 1600),   # ~800 pairs per expert: three tiles, a ragged last one
     ("fp8", 1024, 16, 384, 128, 1600),    # shared expert narrower than the routed ones
     ("bf16", 512, 64, 128, 0, 3000),      # no shared expert; ~375 pairs per expert: two tiles
 ]
@@ -593,10 +597,11 @@ GRP_SHAPES = [  # (format, H, E, I, Is, T): T >= 1536 runs the expert-stationary
 
 @pytest.mark.parametrize("shape", GRP_SHAPES, ids=lambda s: f"{s[0]}-H{s[1]}-E{s[2]}-I{s[3]}-Is{s[4]}-T{s[5]}")
 def test_grouped_gateup_shapes(orc, shape):
-    """The expert-stationary gate/up (tiles of up to 256 tokens of one expert, 128 intermediate
-    rows per unit) gives y bit for bit equal to the 64-token-group gate/up of a context that never
-    plans it (MOE_GRP_MIN_TOKENS=0), and matches the oracle on sampled tokens, among them the
-    tokens of the most loaded expert's last tile."""
+    """The expert-stationary gate/up (tiles of up to 320 tokens of one expert, 128 intermediate
+    rows per unit; planned from MOE_GRP_MIN_TOKENS tokens, 1536 here) gives y bit for bit equal to
+    the 64-token-group gate/up of a context that never plans it (MOE_GRP_MIN_TOKENS=0), and
+    matches the oracle on sampled tokens, among them the tokens of the most loaded expert's last
+    tile."""
     import os
     torch = _torch()
     fmt, H, E, I, Is, T = shape
@@ -605,10 +610,11 @@ def test_grouped_gateup_shapes(orc, shape):
     else:
         layer = quantized_small_layer(fmt, H, E, I, Is, T, seed=1536 + H + E + I + Is)
     t = binding.device_weights(layer)
-    m = binding.MoeLayer(H, E, I, Is, T, fmt, t)
     saved = os.environ.get("MOE_GRP_MIN_TOKENS")
-    os.environ["MOE_GRP_MIN_TOKENS"] = "0"
     try:
+        os.environ["MOE_GRP_MIN_TOKENS"] = "1536"
+        m = binding.MoeLayer(H, E, I, Is, T, fmt, t)
+        os.environ["MOE_GRP_MIN_TOKENS"] = "0"
         m0 = binding.MoeLayer(H, E, I, Is, T, fmt, t)
     finally:
         if saved is None:
@@ -620,7 +626,7 @@ def test_grouped_gateup_shapes(orc, shape):
     z_o = orc.logits(layer["x"], layer["router_w"], None)
     ids_o, w_o, g_o = orc.select(z_o, E, Is > 0)
     counts = np.bincount(ids_o.ravel(), minlength=E)
-    assert counts.max() > 256  # experts with more than one tile
+    assert counts.max() > 320  # experts with more than one tile
     x = t["x"].contiguous()
     routing = routing_device(ids_o, w_o, g_o)
     y = m.forward(x, routing=routing)
@@ -632,7 +638,7 @@ def test_grouped_gateup_shapes(orc, shape):
     # most loaded expert's last (ragged) tile
     e_max = int(counts.argmax())
     toks = np.nonzero((ids_o == e_max).any(1))[0]
-    rows = sorted(set(range(0, T, 16)) | {0, T - 1} | set(toks[(len(toks) // 256) * 256:].tolist()))
+    rows = sorted(set(range(0, T, 16)) | {0, T - 1} | set(toks[(len(toks) // 320) * 320:].tolist()))
     y_o = forward_sample(orc, layer, rows, ids_o[rows], w_o[rows], None if g_o is None else g_o[rows])
     assert_close(y.cpu().numpy()[rows], y_o, f"{shape}")
 
@@ -957,8 +963,10 @@ def test_call_errors_and_empty():
     assert m.plan(65) == m.plan(256) == ["router", "select_bucket"] + wide_db
     chained = ["router", "select_hist", "bucket_scan", "bucket_scatter"]
     assert m.plan(257) == m.plan(1535) == chained + wide
-    big = ["gateup_grp", "down_big", "combine"]  # bf16 from 1536 tokens
-    assert m.plan(1536) == m.plan(8192) == chained + big
+    big = ["gateup_big", "down_big", "combine"]  # bf16 from 1536 tokens
+    assert m.plan(1536) == m.plan(3071) == chained + big
+    grp = ["gateup_grp", "down_big", "combine"]  # from 3072 tokens
+    assert m.plan(3072) == m.plan(8192) == chained + grp
     assert m.plan(200, routing_given=True) == ["select_bucket"] + wide_db
     assert m.plan(300, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
     assert tiny.plan(200) == ["router", "select_bucket", "expert", "combine"]
