@@ -76,9 +76,19 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, unsigned ch
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)seg, 16, (int)off, 0, 0, kAux);
 }
 
-template <bool kFp8>
+// Weight formats of the kernel: bf16 (loaded straight into LDS); FP8 E4M3 codes with a scale per
+// row (applied to the products); MXFP4 E2M1 codes with an E8M0 scale per 32 (applied while
+// widening). Codes come through registers: a 128-byte code line per row feeds kLineSlabs slabs.
+enum { kGBf16 = 0, kGFp8 = 1, kGMx = 2 };
+template <int kFmt>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_grp_kernel(GateUpParams p) {
     using Op = OpBF16;
+    constexpr bool kCodes = kFmt != kGBf16;
+    constexpr int kLineSlabs = kFmt == kGMx ? 4 : kFmt == kGFp8 ? 2 : 1;  // slabs per code line
+    constexpr int kPeriod = kFmt == kGMx ? 8 : 4;  // slabs per unrolled loop step
+    // code lines are requested kAhead slabs before their first slab is staged, into kSets
+    // register sets (MXFP4: one set, a slab ahead - its lines cover four slabs)
+    constexpr int kAhead = kFmt == kGMx ? 1 : 2, kSets = kFmt == kGMx ? 1 : 2;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, q = lane >> 4;
@@ -100,8 +110,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     if (j * kGRows >= Ie) return;  // uniform (Ie is a multiple of kGRows)
     const int i0 = j * kGRows + rg * (kGRows / 2);  // the wave's first intermediate row
 
-    constexpr int kWB = kFp8 ? 1 : 2;  // bytes per stored weight
-    const size_t wrow = (size_t)p.H * kWB;
+    const size_t wrow = kFmt == kGMx ? (size_t)p.H / 2 : kFmt == kGFp8 ? (size_t)p.H : (size_t)p.H * 2;
     const unsigned char *wbase = reinterpret_cast<const unsigned char *>(shared ? p.sgu : p.gate_up) +
                                  (shared ? 0 : (size_t)e * 2 * Ie * wrow);
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wbase, (uint32_t)(2 * Ie * wrow));
@@ -115,7 +124,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     // x part (token rows 40 w + 8 a .. + 8) and 4 w + a of the weight part (stage rows
     // 32 w + 8 a .. + 8) of a slab buffer; lane l writes position l % 8 of row l / 8 of its
     // segment, i.e. it loads the piece the row's rotation puts there.
-    uint32_t xoff[kGXSegs], woff[kFp8 ? 1 : kGSegs];
+    uint32_t xoff[kGXSegs], woff[kCodes ? 1 : kGSegs];
 #pragma unroll
     for (int a = 0; a < kGXSegs; ++a) {
         const int R = 8 * kGXSegs * wave + 8 * a + (lane >> 3);
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int tok = shared ? start + m : (p.perm[start + m] >> 3);
         xoff[a] = (uint32_t)((size_t)tok * p.H * 2) + pc * 16;
     }
-    if constexpr (!kFp8) {
+    if constexpr (!kCodes) {
 #pragma unroll
         for (int a = 0; a < kGSegs; ++a) {
             const int R = 8 * kGSegs * wave + 8 * a + (lane >> 3);
@@ -138,40 +147,70 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         for (int a = 0; a < kGXSegs; ++a)
             if (8 * (kGXSegs * wave + a) < n)  // uniform
                 lds_load16<0>(rx, xbuf + (kGXSegs * wave + a) * 1024, xoff[a] + st * kGRowB);
-        if constexpr (!kFp8) {
+        if constexpr (!kCodes) {
 #pragma unroll
             for (int a = 0; a < kGSegs; ++a)
                 lds_load16<kBufNT>(rw, wbuf + (kGSegs * wave + a) * 1024, woff[a] + st * kGRowB);
         }
     };
-    // FP8 codes go through registers (widened while staged): thread tid takes 16-byte piece lp of
-    // the 128-byte code line of stage rows 64 a + lr (two slabs per line), line L in register set
-    // L % 2, requested two slabs ahead of its first slab.
-    constexpr int kW = kFp8 ? kGWRows / (kGThreads / 8) : 1;  // line loads per thread (4)
+    // Codes go through registers (widened while staged): thread tid takes 16-byte piece lp of the
+    // 128-byte code line of stage rows 64 a + lr (and, MXFP4, the scale byte of that piece's 32
+    // codes), line L in register set L % kSets.
+    constexpr int kW = kCodes ? kGWRows / (kGThreads / 8) : 1;  // line loads per thread (4)
     const int lr = tid >> 3, lp = tid & 7;
-    uint32_t w8off[kW];
-    if constexpr (kFp8) {
+    const int srow = p.H / 32;  // MXFP4 scale bytes per row
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(kFmt == kGMx ? (shared ? p.sgu_mx : p.gu_mx + (size_t)e * 2 * Ie * srow) : nullptr,
+                    kFmt == kGMx ? (uint32_t)(2 * Ie * srow) : 0u);
+    uint32_t w8off[kW], soff[kW];
+    if constexpr (kCodes) {
 #pragma unroll
-        for (int a = 0; a < kW; ++a) w8off[a] = (uint32_t)(wrow_of(kGThreads / 8 * a + lr) * wrow) + lp * 16;
+        for (int a = 0; a < kW; ++a) {
+            const int row = wrow_of(kGThreads / 8 * a + lr);
+            w8off[a] = (uint32_t)(row * wrow) + lp * 16;
+            soff[a] = (uint32_t)(row * srow) + lp;
+        }
     }
-    uint4 wa[kW], wb[kW];
-    auto load_w8 = [&](uint4 (&wr)[kW], int line) __attribute__((always_inline)) {
-        if constexpr (kFp8) {
+    struct Line {
+        uint4 c[kW];
+        uint32_t s[kFmt == kGMx ? kW : 1];
+    };
+    Line wa, wb;
+    auto load_line = [&](Line &L, int line) __attribute__((always_inline)) {
+        if constexpr (kCodes) {
 #pragma unroll
-            for (int a = 0; a < kW; ++a) wr[a] = bload16_stream(rw, w8off[a] + line * kGRowB);
+            for (int a = 0; a < kW; ++a) L.c[a] = bload16_stream(rw, w8off[a] + line * kGRowB);
+            if constexpr (kFmt == kGMx) {
+#pragma unroll
+                for (int a = 0; a < kW; ++a) L.s[a] = bload1(rs, soff[a] + line * 8);
+            }
         }
     };
-    const int st_off8a = gpos(lr, 2 * (lp & 3)), st_off8b = gpos(lr, 2 * (lp & 3) + 1);
-    auto store_w8 = [&](unsigned char *b, const uint4 (&wr)[kW], int st) __attribute__((always_inline)) {
-        if constexpr (kFp8) {
+    // FP8: piece lp holds codes 16 lp .. + 15 of the line, i.e. bf16 pieces 2 (lp % 4) and
+    // 2 (lp % 4) + 1 of slab lp / 4; MXFP4: codes 32 lp .. + 31, bf16 pieces 4 (lp % 2) .. + 3 of
+    // slab lp / 2 (exact widening; the MXFP4 block scale multiplies as it widens)
+    constexpr int kPcs = kFmt == kGMx ? 4 : 2;  // bf16 pieces per code piece
+    const int pc0 = kFmt == kGMx ? 4 * (lp & 1) : 2 * (lp & 3);
+    const int my_slab = kFmt == kGMx ? lp >> 1 : lp >> 2;  // slab (within the line) of the piece
+    int st_off[kPcs];
 #pragma unroll
-            for (int a = 0; a < kW; ++a) {
-                // piece lp holds codes 16 lp .. + 15 of the line: slab lp / 4, bf16 pieces
-                // 2 (lp % 4) and 2 (lp % 4) + 1 of it (exact widening)
-                if ((lp >> 2) == (st & 1)) {
-                    const int r0 = a * (kGThreads / 8) * kGRowB;
-                    *reinterpret_cast<uint4 *>(b + r0 + st_off8a) = e4m3x8_to_bf16x8(wr[a].x, wr[a].y);
-                    *reinterpret_cast<uint4 *>(b + r0 + st_off8b) = e4m3x8_to_bf16x8(wr[a].z, wr[a].w);
+    for (int k = 0; k < kPcs; ++k) st_off[k] = gpos(lr, pc0 + k);
+    auto store_line = [&](unsigned char *b, const Line &L, int st) __attribute__((always_inline)) {
+        if constexpr (kCodes) {
+            if (my_slab == st % kLineSlabs) {
+#pragma unroll
+                for (int a = 0; a < kW; ++a) {
+                    unsigned char *row = b + a * (kGThreads / 8) * kGRowB;
+                    const uint32_t w4[4] = {L.c[a].x, L.c[a].y, L.c[a].z, L.c[a].w};
+                    if constexpr (kFmt == kGMx) {
+                        const float sf = e8m0_to_f32(L.s[a]);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            *reinterpret_cast<uint4 *>(row + st_off[k]) = e2m1x8_to_bf16x8(w4[k], sf);
+                    } else {
+                        *reinterpret_cast<uint4 *>(row + st_off[0]) = e4m3x8_to_bf16x8(w4[0], w4[1]);
+                        *reinterpret_cast<uint4 *>(row + st_off[1]) = e4m3x8_to_bf16x8(w4[2], w4[3]);
+                    }
                 }
             }
         }
@@ -205,51 +244,60 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     };
     uint4 a0[kGRT], b0[kGTT];
 
-    const int nslab = p.H / kGSlab;  // a multiple of 4
-    // slab st (in buffer B = st % 2): request slab st + 1 into the other buffer (read by slab
-    // st - 1, a barrier ago) and, FP8, the code line two slabs ahead; multiply the slab's two k
-    // steps; FP8: widen slab st + 1's codes into the other buffer; wait for this wave's
-    // straight-to-LDS loads, barrier
-    auto slab = [&](auto bsel, int st, uint4 (&wn)[kW], const uint4 (&ws)[kW]) __attribute__((always_inline)) {
-        constexpr int B = decltype(bsel)::value;
+    const int nslab = p.H / kGSlab;  // a multiple of kPeriod
+    // slab st0 + i (in buffer B = i % 2; st0 a multiple of kPeriod, so slab st0 + i's code line
+    // is in set (i / kLineSlabs) % kSets): request slab st + 1 into the other buffer (read by slab
+    // st - 1, a barrier ago) and, when slab st + kAhead starts a code line, that line; multiply
+    // the slab's two k steps; widen slab st + 1's codes into the other buffer; wait for this
+    // wave's loads (but a line requested two slabs ahead), barrier
+    auto slab = [&](auto ic, int st0) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int B = i & 1;
+        constexpr bool kReq = kCodes && (i + kAhead) % kLineSlabs == 0;
+        constexpr bool kNextInB = ((i + kAhead) / kLineSlabs) % kSets, kStageFromB = ((i + 1) / kLineSlabs) % kSets;
+        const int st = st0 + i;
         if (st + 1 < nslab) issue(wslab<1 - B>(), xslab<1 - B>(), st + 1);
-        // an FP8 line requested after this slab's straight-to-LDS loads (uniform)
-        const bool line = kFp8 && st + 2 < nslab && B == 0;
-        if (line) load_w8(wn, (st + 2) >> 1);
+        const bool req = kReq && st + kAhead < nslab;  // a line requested after this slab's LDS loads
+        if (req) load_line(kNextInB ? wb : wa, (st + kAhead) / kLineSlabs);
         if (nt_w > 0) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                rd(a0, b0, wslab<B>(), xslab<B>(), s);
+            for (int s2 = 0; s2 < 2; ++s2) {
+                rd(a0, b0, wslab<B>(), xslab<B>(), s2);
                 mm(a0, b0);
             }
         }
-        if constexpr (kFp8) {
+        if constexpr (kCodes) {
             if (st + 1 < nslab) {
                 mfma_operand_guard();  // the scaled conversions after the matrix steps
-                store_w8(wslab<1 - B>(), ws, st + 1);
+                store_line(wslab<1 - B>(), kStageFromB ? wb : wa, st + 1);
             }
         }
-        static_assert(!kFp8 || kW == 4, "vmcnt below");
-        if (line) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): all but the line just requested
-        else __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0)
+        constexpr int kLineLoads = kFmt == kGMx ? 2 * kW : kW;
+        static_assert(!kCodes || kLineLoads == 4 || kLineLoads == 8, "vmcnt below");
+        if (req && kAhead == 2) __builtin_amdgcn_s_waitcnt(kLineLoads == 8 ? 0x0F78 : 0x0F74);  // all but the line
+        else __builtin_amdgcn_s_waitcnt(0x0F70);                                  // vmcnt(0)
         __syncthreads();
     };
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    load_w8(wa, 0);  // FP8: line 0 (slabs 0 and 1) in set a
+    load_line(wa, 0);
     issue(wslab<0>(), xslab<0>(), 0);
-    store_w8(wslab<0>(), wa, 0);
+    store_line(wslab<0>(), wa, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    for (int st = 0; st < nslab; st += 4) {  // FP8: line L in set L % 2
-        slab(B0{}, st, wb, wa);
-        slab(B1{}, st + 1, wb, wb);
-        slab(B0{}, st + 2, wa, wb);
-        slab(B1{}, st + 3, wa, wa);
+    for (int st0 = 0; st0 < nslab; st0 += kPeriod) {
+        slab(std::integral_constant<int, 0>{}, st0);
+        slab(std::integral_constant<int, 1>{}, st0);
+        slab(std::integral_constant<int, 2>{}, st0);
+        slab(std::integral_constant<int, 3>{}, st0);
+        if constexpr (kPeriod == 8) {
+            slab(std::integral_constant<int, 4>{}, st0);
+            slab(std::integral_constant<int, 5>{}, st0);
+            slab(std::integral_constant<int, 6>{}, st0);
+            slab(std::integral_constant<int, 7>{}, st0);
+        }
     }
     if (nt_w == 0) return;
 
-    if constexpr (kFp8) {  // the rows' dequantization scales (gate rows, then up rows)
+    if constexpr (kFmt == kGFp8) {  // the rows' dequantization scales (gate rows, then up rows)
         const float *sc = shared ? p.sgu_scale : p.gu_scale + (size_t)e * 2 * Ie;
 #pragma unroll
         for (int t = 0; t < kGRT; ++t)
@@ -290,17 +338,19 @@ int grp_tile_tokens() { return kGTok; }
 int grp_rows_per_gateup_unit() { return kGRows; }
 size_t gateup_grp_lds() { return 0; }  // static LDS (two slab buffers)
 
+// dtype: 1 bf16, 2 FP8 E4M3, 3 MXFP4 weights (bf16 activations)
 bool gateup_grp_supported(int H, int I, int Is, int dtype, long x_bytes) {
-    if (dtype != 1 && dtype != 2) return false;
-    if (H % (4 * kGSlab) || I % kGRows || Is % kGRows) return false;  // slabs in fours
-    const long wbytes = 2L * (I > Is ? I : Is) * H * (dtype == 2 ? 1 : 2);
+    if (dtype < 1 || dtype > 3) return false;
+    if (H % ((dtype == 3 ? 8 : 4) * kGSlab) || I % kGRows || Is % kGRows) return false;  // whole loop steps
+    const long wbytes = 2L * (I > Is ? I : Is) * H * (dtype == 1 ? 2 : 1);
     return wbytes < (1L << 31) && x_bytes < (1L << 31);
 }
 
 hipError_t prepare_grouped_kernels() {
     hipError_t err;
-    const void *k[] = {reinterpret_cast<const void *>(&gateup_grp_kernel<false>),
-                       reinterpret_cast<const void *>(&gateup_grp_kernel<true>)};
+    const void *k[] = {reinterpret_cast<const void *>(&gateup_grp_kernel<kGBf16>),
+                       reinterpret_cast<const void *>(&gateup_grp_kernel<kGFp8>),
+                       reinterpret_cast<const void *>(&gateup_grp_kernel<kGMx>)};
     for (const void *f : k)
         if ((err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)gateup_grp_lds())) != hipSuccess)
@@ -308,13 +358,14 @@ hipError_t prepare_grouped_kernels() {
     return hipSuccess;
 }
 
-// dtype: 1 bf16, 2 bf16 activations with FP8 E4M3 weights. p.groups: tiles of at most
+// dtype: 1 bf16, 2 FP8 E4M3, 3 MXFP4 weights (bf16 activations). p.groups: tiles of at most
 // grp_tile_tokens() tokens; p.S: grp_rows_per_gateup_unit()-row slices of Imax; grid: a multiple
 // of 8 holding every unit (8 * ceil(max tiles * S / 8)).
 hipError_t launch_gateup_grp(const GateUpParams &p, int dtype, int grid, hipStream_t s) {
     if (grid % kGXcds || p.NG != kGTok) return hipErrorInvalidValue;  // a caller bug
-    if (dtype == 2) launch_k(gateup_grp_kernel<true>, grid, kGThreads, gateup_grp_lds(), s, p);
-    else launch_k(gateup_grp_kernel<false>, grid, kGThreads, gateup_grp_lds(), s, p);
+    if (dtype == 3) launch_k(gateup_grp_kernel<kGMx>, grid, kGThreads, gateup_grp_lds(), s, p);
+    else if (dtype == 2) launch_k(gateup_grp_kernel<kGFp8>, grid, kGThreads, gateup_grp_lds(), s, p);
+    else launch_k(gateup_grp_kernel<kGBf16>, grid, kGThreads, gateup_grp_lds(), s, p);
     return hipGetLastError();
 }
 

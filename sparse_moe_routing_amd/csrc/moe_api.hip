@@ -75,10 +75,10 @@ constexpr int kHistChunk = 16;
 constexpr int kSelBucketMaxTokens = 256;
 constexpr int kSplitMaxTokens = 64;   // 8-token groups up to here, 64-token groups above
 constexpr int kBigMinTokens = 1536;     // bf16 from here: gateup_big in place of gateup_wide
-// bf16 / FP8 from here: gateup_grp (256-token tiles; measured against gateup_big: T = 2048 277 vs
-// 258 us, 3072 277 vs 293, 4096 289 vs 340, 8192 425 vs 562 (bf16); FP8 2048 247 vs 220, 3072
-// 252 vs 278)
-constexpr int kGrpMinTokens = 3072;
+// bf16 / FP8 from here: gateup_grp (320-token tiles) in place of gateup_big; measured, gateup_grp
+// against gateup_big: bf16 T = 3072 296 vs 286 us, 4096 299 vs 332, 6144 327 vs 433, 8192 349 vs
+// 538; FP8 3072 293 vs 274, 4096 303 vs 330, 8192 399 vs 592
+constexpr int kGrpMinTokens = 3584;
 
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }

@@ -561,10 +561,10 @@ def test_fp8_batch_invariance_bitwise():
     assert torch.equal(y32[:4], y4)
     assert torch.equal(y300[:32], y200[:32]) and torch.equal(y300[288:300], y200[:12])
     assert torch.equal(y1600[:32], y200[:32]) and torch.equal(y1600[1568:], y200[:32])
-    y3200 = m.forward(torch.cat([x] * 100).contiguous())  # the expert-stationary gate/up
+    y3616 = m.forward(torch.cat([x] * 113).contiguous())  # the expert-stationary gate/up
     torch.cuda.synchronize()
-    assert m.plan(3200)[-3:] == ["gateup_grp", "down_big", "combine"]
-    assert torch.equal(y3200[:32], y200[:32]) and torch.equal(y3200[3168:], y200[:32])
+    assert m.plan(3616)[-3:] == ["gateup_grp", "down_big", "combine"]
+    assert torch.equal(y3616[:32], y200[:32]) and torch.equal(y3616[3584:], y200[:32])
     assert_close(y200[:32].cpu().numpy(), y32.cpu().numpy(), "fp8 regimes")
 
 
@@ -578,13 +578,16 @@ def test_mxfp4_batch_invariance_bitwise():
     y4 = m.forward(x[:4].contiguous())
     y200 = m.forward(torch.cat([x] * 7)[:200].contiguous())
     y1600 = m.forward(torch.cat([x] * 50).contiguous())
+    y3616 = m.forward(torch.cat([x] * 113).contiguous())
     torch.cuda.synchronize()
     for T in (4, 32):
         assert m.plan(T)[-2:] == ["gateup", "down_rows"], (T, m.plan(T))
     for T in (200, 1600):
         assert m.plan(T)[-3:] == ["gateup_wide", "down_wide", "combine"], (T, m.plan(T))
+    assert m.plan(3616)[-3:] == ["gateup_grp", "down_wide", "combine"], m.plan(3616)
     assert torch.equal(y32[:4], y4)
     assert torch.equal(y1600[:32], y200[:32]) and torch.equal(y1600[1568:], y200[:32])
+    assert torch.equal(y3616[:32], y200[:32]) and torch.equal(y3616[3584:], y200[:32])
     assert_close(y200[:32].cpu().numpy(), y32.cpu().numpy(), "mxfp4 regimes")
 
 
@@ -592,6 +595,7 @@ GRP_SHAPES = [  # (format, H, E, I, Is, T): T >= 1536 runs the expert-stationary
     ("bf16", 1024, 16, 256, 384, 1600),   # ~800 pairs per expert: three tiles, a ragged last one
     ("fp8", 1024, 16, 384, 128, 1600),    # shared expert narrower than the routed ones
     ("bf16", 512, 64, 128, 0, 3000),      # no shared expert; ~375 pairs per expert: two tiles
+    ("mxfp4", 1024, 16, 256, 256, 1600),  # block-scaled codes widened with their scales
 ]
 
 
@@ -787,14 +791,15 @@ def quantized_pair(fmt, H, E, I, Is, T, seed):
 def test_quantized_equals_bf16_of_decoded_weights_bitwise(fmt):
     """FP8 (power-of-two row scales) and MXFP4 (scale bytes over 2^36) against a bf16 context
     holding the decoded weights: y bit for bit at T = 4, 32 (8-token groups), 200, 300 (64-token
-    groups, both down kernels) and 1600 (the large-T kernels where the format has them)."""
+    groups, both down kernels), 1600 (the large-T kernels where the format has them) and 3616 (the
+    expert-stationary gate/up)."""
     torch = _torch()
-    H, E, I, Is, Tmax = 1024, 16, 512, 512, 1600
+    H, E, I, Is, Tmax = 1024, 16, 512, 512, 3616
     q, b = quantized_pair(fmt, H, E, I, Is, Tmax, seed=41 if fmt == "fp8" else 42)
     tq, tb = binding.device_weights(q), binding.device_weights(b)
     mq = binding.MoeLayer(H, E, I, Is, Tmax, fmt, tq)
     mb = binding.MoeLayer(H, E, I, Is, Tmax, "bf16", tb)
-    for T in (4, 32, 200, 300, 1600):
+    for T in (4, 32, 200, 300, 1600, 3616):
         x = tb["x"][:T].contiguous()
         yq = mq.forward(x)
         yb = mb.forward(x)
@@ -964,9 +969,9 @@ def test_call_errors_and_empty():
     chained = ["router", "select_hist", "bucket_scan", "bucket_scatter"]
     assert m.plan(257) == m.plan(1535) == chained + wide
     big = ["gateup_big", "down_big", "combine"]  # bf16 from 1536 tokens
-    assert m.plan(1536) == m.plan(3071) == chained + big
-    grp = ["gateup_grp", "down_big", "combine"]  # from 3072 tokens
-    assert m.plan(3072) == m.plan(8192) == chained + grp
+    assert m.plan(1536) == m.plan(3583) == chained + big
+    grp = ["gateup_grp", "down_big", "combine"]  # from 3584 tokens
+    assert m.plan(3584) == m.plan(8192) == chained + grp
     assert m.plan(200, routing_given=True) == ["select_bucket"] + wide_db
     assert m.plan(300, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
     assert tiny.plan(200) == ["router", "select_bucket", "expert", "combine"]
