@@ -127,7 +127,7 @@ def kernel_bytes(w, U, name):
     esz, wsz, ssz = sizes(w)
     H, I, Is, T = w.hidden, w.inter, w.shared_inter, w.tokens
     name = {"gateup_wide": "gateup", "gateup_big": "gateup", "gateup_grp": "gateup", "gateup_gemv": "gateup",
-            "down_wide": "down", "down_big": "down", "down_rows": "down"}.get(name, name)
+            "down_wide": "down", "down_big": "down", "down_grp": "down", "down_rows": "down"}.get(name, name)
     if name == "gateup":
         return 2 * wsz * H * Is + 2 * ssz * Is + U * (2 * wsz * H * I + 2 * ssz * I) + esz * T * H
     if name == "down":
@@ -305,7 +305,7 @@ def measure(w, args, torch, log_prefix):
     mean_U = float(np.mean([U[c] for c in used]))
     stage = {}
     for name in ("gateup", "down", "gateup_wide", "gateup_big", "gateup_grp", "gateup_gemv", "down_wide",
-                 "down_big", "down_rows", "expert"):
+                 "down_big", "down_grp", "down_rows", "expert"):
         if name in per_kernel:
             us = float(np.mean(per_kernel[name])) * 1e3
             b = float(np.mean([kernel_bytes(w, U[c], name) for c in used]))

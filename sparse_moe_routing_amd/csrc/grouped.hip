@@ -332,6 +332,219 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
 }
 
+// down_grp_kernel - the down product of the same tiles: unit = (tile of up to 320 tokens of one
+// expert, 256 rows of y), so an expert's down rows are read once per tile and a tile's h once per
+// 256 rows of y. K (the expert's intermediate rows) goes in slabs of 32 elements: 256 down rows
+// and the tile's 320 hi and 320 lo h rows of 64 bytes each, double-buffered, bf16 weights and h
+// loaded straight into LDS (a slab of 128 bytes per row would not fit twice), FP8 codes through
+// registers. Eight waves: wave w multiplies y rows 128 (w % 2) .. + 128 (eight 16-row tiles) by
+// token columns 80 (w / 2) .. + 80 (five tiles). Per output element the steps, planes and their
+// order are those of the 64-token-group down kernels: per k step the hi plane, then the lo plane,
+// into one accumulator; FP8 row scales after the K loop; the routing weight (or the shared gate)
+// times the product goes to the (token, rank) slot's row of the per-slot buffer.
+constexpr int kDRows = 256;                    // rows of y per unit
+constexpr int kDRowB = 64;                     // bytes of a staged row (32 bf16)
+constexpr int kDSlab = kDRowB / 2;             // K elements per slab (one k step)
+constexpr int kDWBytes = kDRows * kDRowB;      // weight part of a slab buffer (16 KB)
+constexpr int kDHBytes = 2 * kGTok * kDRowB;   // h part: hi rows, then lo rows (40 KB)
+constexpr int kDWSegs = kDWBytes / 1024 / kGWaves;  // 1 KB weight segments per wave (2)
+constexpr int kDHSegs = kDHBytes / 1024 / kGWaves;  // 1 KB h segments per wave (5)
+constexpr int kDRT = kDRows / 2 / kTile;       // row tiles per wave (8)
+__shared__ __align__(16) unsigned char g_dw0[kDWBytes], g_dw1[kDWBytes];
+__shared__ __align__(16) unsigned char g_dh0[kDHBytes], g_dh1[kDHBytes];
+template <int B>
+__device__ __forceinline__ unsigned char *dwslab() { return B ? g_dw1 : g_dw0; }
+template <int B>
+__device__ __forceinline__ unsigned char *dhslab() { return B ? g_dh1 : g_dh0; }
+
+// Byte position of 16-byte piece pc (0..3) of staged 64-byte row r: rows 4m .. 4m + 3 rotate their
+// pieces by m, so that the 16 rows one operand read touches fall on 16 distinct bank groups; the
+// rotation depends on r % 16 only.
+__device__ __forceinline__ int dpos(int r, int pc) { return r * kDRowB + ((pc ^ (r >> 2)) & 3) * 16; }
+constexpr int kDTileB = kTile * kDRowB;  // bytes of 16 staged rows
+
+template <int kFmt>
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_grp_kernel(DownParams p) {
+    using Op = OpBF16;
+    constexpr bool kCodes = kFmt != kGBf16;
+    static_assert(kFmt != kGMx, "MXFP4 down weights run the 64-token-group kernel");
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 15, q = lane >> 4;
+    const int rg = wave & 1, th = (wave >> 1) & 3;  // (the masks bound the LDS offsets for the compiler)
+
+    // unit: blocks b, b + 8, ... run on one XCD and take one contiguous eighth of the units, in
+    // order (a tile's row blocks next to each other: they read the same h rows)
+    const int nrb = p.H / kDRows;
+    const int nunits = p.num_groups[0] * nrb;
+    const int per = (nunits + kGXcds - 1) / kGXcds;
+    const int idx = blockIdx.x / kGXcds;
+    const int u = (blockIdx.x % kGXcds) * per + idx;
+    if (idx >= per || u >= nunits) return;  // uniform over the block
+    const int gi = u / nrb, rb = u - gi * nrb;
+    const int4 grp = p.groups[gi];
+    const int e = grp.x, start = grp.y, n = grp.z;
+    const bool shared = e == p.E;
+    const int Ie = shared ? p.Is : p.I;
+    const int row0 = rb * kDRows;  // the unit's first row of y
+
+    const size_t wrow = kFmt == kGFp8 ? (size_t)Ie : (size_t)Ie * 2;  // bytes per down row
+    const unsigned char *wbase = reinterpret_cast<const unsigned char *>(shared ? p.sdn : p.down) +
+                                 (shared ? 0 : (size_t)e * p.H * wrow) + (size_t)row0 * wrow;
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wbase, (uint32_t)(kDRows * wrow));
+    const __amdgpu_buffer_rsrc_t rh = buffer_rsrc(p.h, (uint32_t)(2 * p.plane * 2));
+    // Straight-to-LDS loads: wave w fills h segments 5 w + a (h stage rows 80 w + 16 a .. + 16:
+    // rows < 320 the hi plane of token row r, rows >= 320 the lo plane of token row r - 320) and
+    // bf16 weight segments 2 w + a (down rows 32 w + 16 a .. + 16); lane l writes position l % 4 of
+    // row l / 4 of its segment, i.e. it loads the piece the row's rotation puts there.
+    uint32_t hoff[kDHSegs], woff[kCodes ? 1 : kDWSegs];
+#pragma unroll
+    for (int a = 0; a < kDHSegs; ++a) {
+        const int R = 16 * (kDHSegs * wave + a) + (lane >> 2);
+        const int pc = ((lane & 3) ^ (R >> 2)) & 3;
+        const int pl = R >= kGTok, r = R - pl * kGTok;
+        const int m = r < n ? r : 0;  // token rows past the tile repeat row 0 (columns dropped)
+        const int slot = shared ? p.T * kTopK + start + m : p.perm[start + m];
+        hoff[a] = (uint32_t)(((size_t)pl * p.plane + (size_t)slot * p.Imax) * 2) + pc * 16;
+    }
+    if constexpr (!kCodes) {
+#pragma unroll
+        for (int a = 0; a < kDWSegs; ++a) {
+            const int R = 16 * (kDWSegs * wave + a) + (lane >> 2);
+            woff[a] = (uint32_t)(R * wrow) + (((lane & 3) ^ (R >> 2)) & 3) * 16;
+        }
+    }
+    auto issue = [&](unsigned char *wbuf, unsigned char *hbuf, int st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int a = 0; a < kDHSegs; ++a) {
+            const int R0 = 16 * (kDHSegs * wave + a);
+            if ((R0 >= kGTok ? R0 - kGTok : R0) < n)  // uniform: segments past the tile not loaded
+                lds_load16<0>(rh, hbuf + (kDHSegs * wave + a) * 1024, hoff[a] + st * kDRowB);
+        }
+        if constexpr (!kCodes) {
+#pragma unroll
+            for (int a = 0; a < kDWSegs; ++a)
+                lds_load16<kBufNT>(rw, wbuf + (kDWSegs * wave + a) * 1024, woff[a] + st * kDRowB);
+        }
+    };
+    // FP8 codes through registers: thread tid takes 16-byte piece lp (codes 16 lp .. + 15, i.e.
+    // bf16 pieces 2 (lp % 2), 2 (lp % 2) + 1 of slab lp / 2) of the 128-byte code line (four slabs)
+    // of down rows 64 a + lr; one register set, a line requested a slab ahead of its first slab.
+    constexpr int kLineSlabs = 4;
+    constexpr int kW = kCodes ? kDRows / (kGThreads / 8) : 1;  // line loads per thread (4)
+    const int lr = tid >> 3, lp = tid & 7;
+    uint32_t w8off[kW];
+    if constexpr (kCodes) {
+#pragma unroll
+        for (int a = 0; a < kW; ++a) w8off[a] = (uint32_t)((kGThreads / 8 * a + lr) * wrow) + lp * 16;
+    }
+    uint4 wl[kW];
+    auto load_line = [&](int line) __attribute__((always_inline)) {
+        if constexpr (kCodes) {
+#pragma unroll
+            for (int a = 0; a < kW; ++a) wl[a] = bload16_stream(rw, w8off[a] + line * 128);
+        }
+    };
+    const int st_off8a = dpos(lr, 2 * (lp & 1)), st_off8b = dpos(lr, 2 * (lp & 1) + 1);
+    auto store_line = [&](unsigned char *b, int st) __attribute__((always_inline)) {
+        if constexpr (kCodes) {
+            if ((lp >> 1) == st % kLineSlabs) {
+#pragma unroll
+                for (int a = 0; a < kW; ++a) {
+                    unsigned char *row = b + a * (kGThreads / 8) * kDRowB;
+                    *reinterpret_cast<uint4 *>(row + st_off8a) = e4m3x8_to_bf16x8(wl[a].x, wl[a].y);
+                    *reinterpret_cast<uint4 *>(row + st_off8b) = e4m3x8_to_bf16x8(wl[a].z, wl[a].w);
+                }
+            }
+        }
+    };
+
+    f32x4_t acc[kDRT][kGTT];
+#pragma unroll
+    for (int t = 0; t < kDRT; ++t)
+#pragma unroll
+        for (int tt = 0; tt < kGTT; ++tt) acc[t][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int nt_w = (n - th * kGTT * kTile + kTile - 1) / kTile;
+    nt_w = nt_w < 0 ? 0 : nt_w > kGTT ? kGTT : nt_w;
+
+    // a slab (one k step): the wave's 8 weight and 5 + 5 h fragments are read, then multiplied,
+    // hi plane then lo plane per accumulator
+    const int rd_off = dpos(col, q);
+    auto compute = [&](const unsigned char *wbuf, const unsigned char *hbuf) __attribute__((always_inline)) {
+        const unsigned char *wb_ = wbuf + rg * kDRT * kDTileB;
+        const unsigned char *hb_ = hbuf + th * kGTT * kDTileB;
+        uint4 a[kDRT], bh[kGTT], bl[kGTT];
+#pragma unroll
+        for (int t = 0; t < kDRT; ++t) a[t] = lds_read16(wb_ + t * kDTileB + rd_off);
+#pragma unroll
+        for (int tt = 0; tt < kGTT; ++tt) {
+            bh[tt] = lds_read16(hb_ + tt * kDTileB + rd_off);
+            bl[tt] = lds_read16(hb_ + kGTok * kDRowB + tt * kDTileB + rd_off);
+        }
+#pragma unroll
+        for (int tt = 0; tt < kGTT; ++tt) {
+#pragma unroll
+            for (int t = 0; t < kDRT; ++t) Op::mma(acc[t][tt], a[t], bh[tt]);
+#pragma unroll
+            for (int t = 0; t < kDRT; ++t) Op::mma(acc[t][tt], a[t], bl[tt]);
+        }
+    };
+
+    const int nslab = Ie / kDSlab;  // a multiple of 4 (Ie a multiple of 128)
+    // slab st (buffer B = st % 2): request slab st + 1 into the other buffer (read by slab st - 1,
+    // a barrier ago) and, FP8, at the last slab of a code line the next line; multiply; FP8: widen
+    // slab st + 1's codes into the other buffer; wait for this wave's loads, barrier
+    auto slab = [&](auto ic, int st0) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int B = i & 1;
+        const int st = st0 + i;
+        if (st + 1 < nslab) issue(dwslab<1 - B>(), dhslab<1 - B>(), st + 1);
+        if constexpr (kCodes && (i + 1) % kLineSlabs == 0)
+            if (st + 1 < nslab) load_line((st + 1) / kLineSlabs);
+        if (nt_w > 0) compute(dwslab<B>(), dhslab<B>());
+        if constexpr (kCodes) {
+            if (st + 1 < nslab) {
+                mfma_operand_guard();  // the scaled conversions after the matrix steps
+                store_line(dwslab<1 - B>(), st + 1);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+    };
+    load_line(0);
+    issue(dwslab<0>(), dhslab<0>(), 0);
+    store_line(dwslab<0>(), 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int st0 = 0; st0 < nslab; st0 += 4) {
+        slab(std::integral_constant<int, 0>{}, st0);
+        slab(std::integral_constant<int, 1>{}, st0);
+        slab(std::integral_constant<int, 2>{}, st0);
+        slab(std::integral_constant<int, 3>{}, st0);
+    }
+    if (nt_w == 0) return;
+
+    if constexpr (kFmt == kGFp8) {  // the output rows' dequantization scales
+        const float *sc = (shared ? p.sdn_scale : p.dn_scale + (size_t)e * p.H) + row0 + rg * kDRT * kTile + 4 * q;
+#pragma unroll
+        for (int t = 0; t < kDRT; ++t)
+#pragma unroll
+            for (int tt = 0; tt < kGTT; ++tt) scale_rows(acc[t][tt], sc + t * kTile);
+    }
+#pragma unroll
+    for (int tt = 0; tt < kGTT; ++tt) {
+        const int m = (th * kGTT + tt) * kTile + col;
+        if (tt >= nt_w || m >= n) continue;
+        const int slot = shared ? p.T * kTopK + start + m : p.perm[start + m];
+        const float wt = shared ? p.g[start + m] : p.w[slot];
+        // lane holds rows 4q + r of each of the wave's 16-row tiles for its token column
+#pragma unroll
+        for (int t = 0; t < kDRT; ++t)
+            *reinterpret_cast<float4 *>(p.ybuf + (size_t)slot * p.H + row0 + (rg * kDRT + t) * kTile + 4 * q) =
+                make_float4(wt * acc[t][tt][0], wt * acc[t][tt][1], wt * acc[t][tt][2], wt * acc[t][tt][3]);
+    }
+}
+
 }  // namespace
 
 int grp_tile_tokens() { return kGTok; }
@@ -345,6 +558,21 @@ bool gateup_grp_supported(int H, int I, int Is, int dtype, long x_bytes) {
     const long wbytes = 2L * (I > Is ? I : Is) * H * (dtype == 1 ? 2 : 1);
     return wbytes < (1L << 31) && x_bytes < (1L << 31);
 }
+
+// dtype: 1 bf16, 2 FP8 E4M3 down weights
+bool down_grp_supported(int H, int I, int Is, int dtype, size_t h_bytes) {
+    if (dtype != 1 && dtype != 2) return false;
+    if (H % kDRows || I % 128 || Is % 128) return false;  // slabs in fours
+    return (size_t)kDRows * (I > Is ? I : Is) * 2 < (1u << 31) && h_bytes < (1u << 31);
+}
+
+hipError_t launch_down_grp(const DownParams &p, int dtype, int grid, hipStream_t s) {
+    if (grid % kGXcds || p.NG != kGTok || p.H % kDRows) return hipErrorInvalidValue;  // a caller bug
+    if (dtype == 2) launch_k(down_grp_kernel<kGFp8>, grid, kGThreads, 0, s, p);
+    else launch_k(down_grp_kernel<kGBf16>, grid, kGThreads, 0, s, p);
+    return hipGetLastError();
+}
+int grp_rows_per_down_unit() { return kDRows; }
 
 hipError_t prepare_grouped_kernels() {
     hipError_t err;

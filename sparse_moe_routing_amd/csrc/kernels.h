@@ -162,6 +162,10 @@ int grp_rows_per_gateup_unit();
 bool gateup_grp_supported(int H, int I, int Is, int dtype, long x_bytes);
 hipError_t prepare_grouped_kernels();
 hipError_t launch_gateup_grp(const GateUpParams &p, int dtype, int grid, hipStream_t s);
+// its down product over the same tiles (bf16 / FP8 down weights), rows of y per unit
+bool down_grp_supported(int H, int I, int Is, int dtype, size_t h_bytes);
+int grp_rows_per_down_unit();
+hipError_t launch_down_grp(const DownParams &p, int dtype, int grid, hipStream_t s);
 // Decode expert stage on the vector ALUs (gemv.hip): bf16 shapes gemv_supported accepts.
 bool gemv_supported(int H, int I, int Is);
 bool down_rows_supported(int H, int I, int Is);

@@ -120,8 +120,9 @@ struct Plan {
     bool down_big = false;       // wide, bf16 or FP8, H a multiple of 512, T <= 256 or big
     bool gemv = false;           // split, bf16 activations: gateup_gemv in place of gateup
     bool down_rows = false;      // split, bf16 activations: down_rows in place of down
-    bool grp = false;            // wide, bf16 or FP8: gateup_grp for the gate/up kernel
-    int NG2 = 0, max_groups2 = 0, grp_grid = 0;
+    bool grp = false;            // wide, bf16 / FP8 / MXFP4: gateup_grp for the gate/up kernel
+    bool down_grp = false;       // with grp, bf16 / FP8: down_grp over the same tiles
+    int NG2 = 0, max_groups2 = 0, grp_grid = 0, down_grp_grid = 0;
     int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;
     size_t o_state = 0, o_zpart = 0, o_ids = 0, o_w = 0, o_g = 0, o_counts = 0, o_offsets = 0, o_perm = 0,
@@ -263,6 +264,10 @@ Plan make_plan(const moe_ctx *c, int T) {
             const long units = (long)p.max_groups2 * (Imax / grp_rows_per_gateup_unit());
             p.grp_grid = (int)((units + 7) / 8 * 8);
             p.big = false;
+            const size_t h_bytes = (size_t)2 * (T * 8 + (Is > 0 ? T : 0)) * Imax * 2;
+            p.down_grp = down_grp_supported(H, I, Is, expert_kdt(c), h_bytes);
+            const long d_units = (long)p.max_groups2 * (H / grp_rows_per_down_unit());
+            p.down_grp_grid = (int)((d_units + 7) / 8 * 8);
         }
         // down_big with gateup_big and up to 256 tokens (measured: skewed T = 192 51.1 against
         // 53.8 us; T = 768 140.1 against 137.1 us for down_wide). The big pair from 1536 tokens:
@@ -605,7 +610,15 @@ int forward_impl(const moe_ctx *c, const void *x, int32_t T, const int32_t *ids_
             if (n_kernels) *n_kernels = L.count;
             return hip_status(L.err);
         }
-        if (p.down_big) {
+        if (p.down_grp) {
+            L.step("down_grp", [&] {
+                DownParams d2 = dp;
+                d2.groups = reinterpret_cast<const int4 *>(ws + p.o_groups2);
+                d2.num_groups = reinterpret_cast<const int32_t *>(ws + p.o_ngroups2);
+                d2.NG = p.NG2;
+                return launch_down_grp(d2, expert_kdt(c), p.down_grp_grid, L.stream);
+            });
+        } else if (p.down_big) {
             L.step("down_big", [&] { return launch_down_big(dp, expert_kdt(c), p.down_grid, L.stream); });
         } else if (p.wide) {
             L.step("down_wide", [&] {

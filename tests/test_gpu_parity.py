@@ -538,7 +538,7 @@ def test_batch_invariance_bitwise():
     # T >= 1536: the large-T gate/up and down kernels, the same bits as the 64-token groups
     y4097 = m.forward(torch.cat([x] * 129)[:4097].contiguous())
     torch.cuda.synchronize()
-    assert m.plan(4097)[4:6] == ["gateup_grp", "down_big"]
+    assert m.plan(4097)[4:6] == ["gateup_grp", "down_grp"]
     assert torch.equal(y4097[:32], y384[:32]) and torch.equal(y4097[4064:4096], y384[:32])
 
 
@@ -563,7 +563,7 @@ def test_fp8_batch_invariance_bitwise():
     assert torch.equal(y1600[:32], y200[:32]) and torch.equal(y1600[1568:], y200[:32])
     y3616 = m.forward(torch.cat([x] * 113).contiguous())  # the expert-stationary gate/up
     torch.cuda.synchronize()
-    assert m.plan(3616)[-3:] == ["gateup_grp", "down_big", "combine"]
+    assert m.plan(3616)[-3:] == ["gateup_grp", "down_grp", "combine"]
     assert torch.equal(y3616[:32], y200[:32]) and torch.equal(y3616[3584:], y200[:32])
     assert_close(y200[:32].cpu().numpy(), y32.cpu().numpy(), "fp8 regimes")
 
@@ -601,11 +601,11 @@ GRP_SHAPES = [  # (format, H, E, I, Is, T): T >= 1536 runs the expert-stationary
 
 @pytest.mark.parametrize("shape", GRP_SHAPES, ids=lambda s: f"{s[0]}-H{s[1]}-E{s[2]}-I{s[3]}-Is{s[4]}-T{s[5]}")
 def test_grouped_gateup_shapes(orc, shape):
-    """The expert-stationary gate/up (tiles of up to 320 tokens of one expert, 128 intermediate
-    rows per unit; planned from MOE_GRP_MIN_TOKENS tokens, 1536 here) gives y bit for bit equal to
-    the 64-token-group gate/up of a context that never plans it (MOE_GRP_MIN_TOKENS=0), and
-    matches the oracle on sampled tokens, among them the tokens of the most loaded expert's last
-    tile."""
+    """The expert-stationary gate/up and down kernels (tiles of up to 320 tokens of one expert;
+    planned from MOE_GRP_MIN_TOKENS tokens, 1536 here; the down kernel for bf16 and FP8 weights)
+    give y bit for bit equal to the 64-token-group kernels of a context that never plans them
+    (MOE_GRP_MIN_TOKENS=0), and match the oracle on sampled tokens, among them the tokens of the
+    most loaded expert's last tile."""
     import os
     torch = _torch()
     fmt, H, E, I, Is, T = shape
@@ -970,7 +970,7 @@ def test_call_errors_and_empty():
     assert m.plan(257) == m.plan(1535) == chained + wide
     big = ["gateup_big", "down_big", "combine"]  # bf16 from 1536 tokens
     assert m.plan(1536) == m.plan(3583) == chained + big
-    grp = ["gateup_grp", "down_big", "combine"]  # from 3584 tokens
+    grp = ["gateup_grp", "down_grp", "combine"]  # from 3584 tokens
     assert m.plan(3584) == m.plan(8192) == chained + grp
     assert m.plan(200, routing_given=True) == ["select_bucket"] + wide_db
     assert m.plan(300, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
