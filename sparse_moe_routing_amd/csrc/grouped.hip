@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // 256 rows of y. K (the expert's intermediate rows) goes in slabs of 32 elements: 256 down rows
 // and the tile's 320 hi and 320 lo h rows of 64 bytes each, double-buffered, bf16 weights and h
 // loaded straight into LDS (a slab of 128 bytes per row would not fit twice), FP8 codes through
-// registers. Eight waves: wave w multiplies y rows 128 (w % 2) .. + 128 (eight 16-row tiles) by
+// registers (FP8, MXFP4). Eight waves: wave w multiplies y rows 128 (w % 2) .. + 128 (eight 16-row tiles) by
 // token columns 80 (w / 2) .. + 80 (five tiles). Per output element the steps, planes and their
 // order are those of the 64-token-group down kernels: per k step the hi plane, then the lo plane,
 // into one accumulator; FP8 row scales after the K loop; the routing weight (or the shared gate)
@@ -367,7 +367,7 @@ template <int kFmt>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_grp_kernel(DownParams p) {
     using Op = OpBF16;
     constexpr bool kCodes = kFmt != kGBf16;
-    static_assert(kFmt != kGMx, "MXFP4 down weights run the 64-token-group kernel");
+    constexpr int kLineSlabs = kFmt == kGMx ? 8 : 4;  // slabs per 128-byte code line
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, q = lane >> 4;
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int Ie = shared ? p.Is : p.I;
     const int row0 = rb * kDRows;  // the unit's first row of y
 
-    const size_t wrow = kFmt == kGFp8 ? (size_t)Ie : (size_t)Ie * 2;  // bytes per down row
+    const size_t wrow = kFmt == kGMx ? (size_t)Ie / 2 : kFmt == kGFp8 ? (size_t)Ie : (size_t)Ie * 2;
     const unsigned char *wbase = reinterpret_cast<const unsigned char *>(shared ? p.sdn : p.down) +
                                  (shared ? 0 : (size_t)e * p.H * wrow) + (size_t)row0 * wrow;
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wbase, (uint32_t)(kDRows * wrow));
@@ -427,33 +427,58 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 lds_load16<kBufNT>(rw, wbuf + (kDWSegs * wave + a) * 1024, woff[a] + st * kDRowB);
         }
     };
-    // FP8 codes through registers: thread tid takes 16-byte piece lp (codes 16 lp .. + 15, i.e.
-    // bf16 pieces 2 (lp % 2), 2 (lp % 2) + 1 of slab lp / 2) of the 128-byte code line (four slabs)
-    // of down rows 64 a + lr; one register set, a line requested a slab ahead of its first slab.
-    constexpr int kLineSlabs = 4;
+    // Codes through registers: thread tid takes 16-byte piece lp of the 128-byte code line of down
+    // rows 64 a + lr - FP8: codes 16 lp .. + 15, bf16 pieces 2 (lp % 2), 2 (lp % 2) + 1 of slab
+    // lp / 2; MXFP4: codes 32 lp .. + 31 with their scale byte, the four bf16 pieces of slab lp -
+    // one register set, a line requested a slab ahead of its first slab.
     constexpr int kW = kCodes ? kDRows / (kGThreads / 8) : 1;  // line loads per thread (4)
     const int lr = tid >> 3, lp = tid & 7;
-    uint32_t w8off[kW];
+    const int srow = Ie / 32;  // MXFP4 scale bytes per row
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
+        kFmt == kGMx ? (shared ? p.sdn_mx : p.dn_mx + (size_t)e * p.H * srow) + (size_t)row0 * srow : nullptr,
+        kFmt == kGMx ? (uint32_t)(kDRows * srow) : 0u);
+    uint32_t w8off[kW], soff[kW];
     if constexpr (kCodes) {
 #pragma unroll
-        for (int a = 0; a < kW; ++a) w8off[a] = (uint32_t)((kGThreads / 8 * a + lr) * wrow) + lp * 16;
+        for (int a = 0; a < kW; ++a) {
+            w8off[a] = (uint32_t)((kGThreads / 8 * a + lr) * wrow) + lp * 16;
+            soff[a] = (uint32_t)((kGThreads / 8 * a + lr) * srow) + lp;
+        }
     }
     uint4 wl[kW];
+    uint32_t wsc[kFmt == kGMx ? kW : 1];
     auto load_line = [&](int line) __attribute__((always_inline)) {
         if constexpr (kCodes) {
 #pragma unroll
             for (int a = 0; a < kW; ++a) wl[a] = bload16_stream(rw, w8off[a] + line * 128);
+            if constexpr (kFmt == kGMx) {
+#pragma unroll
+                for (int a = 0; a < kW; ++a) wsc[a] = bload1(rs, soff[a] + line * 8);
+            }
         }
     };
-    const int st_off8a = dpos(lr, 2 * (lp & 1)), st_off8b = dpos(lr, 2 * (lp & 1) + 1);
+    constexpr int kPcs = kFmt == kGMx ? 4 : 2;  // bf16 pieces per code piece
+    const int pc0 = kFmt == kGMx ? 0 : 2 * (lp & 1);
+    const int my_slab = kFmt == kGMx ? lp : lp >> 1;
+    int st_off[kPcs];
+#pragma unroll
+    for (int k = 0; k < kPcs; ++k) st_off[k] = dpos(lr, pc0 + k);
     auto store_line = [&](unsigned char *b, int st) __attribute__((always_inline)) {
         if constexpr (kCodes) {
-            if ((lp >> 1) == st % kLineSlabs) {
+            if (my_slab == st % kLineSlabs) {
 #pragma unroll
                 for (int a = 0; a < kW; ++a) {
                     unsigned char *row = b + a * (kGThreads / 8) * kDRowB;
-                    *reinterpret_cast<uint4 *>(row + st_off8a) = e4m3x8_to_bf16x8(wl[a].x, wl[a].y);
-                    *reinterpret_cast<uint4 *>(row + st_off8b) = e4m3x8_to_bf16x8(wl[a].z, wl[a].w);
+                    const uint32_t w4[4] = {wl[a].x, wl[a].y, wl[a].z, wl[a].w};
+                    if constexpr (kFmt == kGMx) {
+                        const float sf = e8m0_to_f32(wsc[a]);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            *reinterpret_cast<uint4 *>(row + st_off[k]) = e2m1x8_to_bf16x8(w4[k], sf);
+                    } else {
+                        *reinterpret_cast<uint4 *>(row + st_off[0]) = e4m3x8_to_bf16x8(w4[0], w4[1]);
+                        *reinterpret_cast<uint4 *>(row + st_off[1]) = e4m3x8_to_bf16x8(w4[2], w4[3]);
+                    }
                 }
             }
         }
@@ -490,7 +515,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
     };
 
-    const int nslab = Ie / kDSlab;  // a multiple of 4 (Ie a multiple of 128)
+    const int nslab = Ie / kDSlab;  // a multiple of kLineSlabs
     // slab st (buffer B = st % 2): request slab st + 1 into the other buffer (read by slab st - 1,
     // a barrier ago) and, FP8, at the last slab of a code line the next line; multiply; FP8: widen
     // slab st + 1's codes into the other buffer; wait for this wave's loads, barrier
@@ -516,11 +541,17 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     store_line(dwslab<0>(), 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    for (int st0 = 0; st0 < nslab; st0 += 4) {
+    for (int st0 = 0; st0 < nslab; st0 += kLineSlabs) {
         slab(std::integral_constant<int, 0>{}, st0);
         slab(std::integral_constant<int, 1>{}, st0);
         slab(std::integral_constant<int, 2>{}, st0);
         slab(std::integral_constant<int, 3>{}, st0);
+        if constexpr (kLineSlabs == 8) {
+            slab(std::integral_constant<int, 4>{}, st0);
+            slab(std::integral_constant<int, 5>{}, st0);
+            slab(std::integral_constant<int, 6>{}, st0);
+            slab(std::integral_constant<int, 7>{}, st0);
+        }
     }
     if (nt_w == 0) return;
 
@@ -559,16 +590,18 @@ bool gateup_grp_supported(int H, int I, int Is, int dtype, long x_bytes) {
     return wbytes < (1L << 31) && x_bytes < (1L << 31);
 }
 
-// dtype: 1 bf16, 2 FP8 E4M3 down weights
+// dtype: 1 bf16, 2 FP8 E4M3, 3 MXFP4 down weights
 bool down_grp_supported(int H, int I, int Is, int dtype, size_t h_bytes) {
-    if (dtype != 1 && dtype != 2) return false;
-    if (H % kDRows || I % 128 || Is % 128) return false;  // slabs in fours
+    if (dtype < 1 || dtype > 3) return false;
+    const int m = dtype == 3 ? 256 : 128;  // whole loop steps (code lines)
+    if (H % kDRows || I % m || Is % m) return false;
     return (size_t)kDRows * (I > Is ? I : Is) * 2 < (1u << 31) && h_bytes < (1u << 31);
 }
 
 hipError_t launch_down_grp(const DownParams &p, int dtype, int grid, hipStream_t s) {
     if (grid % kGXcds || p.NG != kGTok || p.H % kDRows) return hipErrorInvalidValue;  // a caller bug
-    if (dtype == 2) launch_k(down_grp_kernel<kGFp8>, grid, kGThreads, 0, s, p);
+    if (dtype == 3) launch_k(down_grp_kernel<kGMx>, grid, kGThreads, 0, s, p);
+    else if (dtype == 2) launch_k(down_grp_kernel<kGFp8>, grid, kGThreads, 0, s, p);
     else launch_k(down_grp_kernel<kGBf16>, grid, kGThreads, 0, s, p);
     return hipGetLastError();
 }

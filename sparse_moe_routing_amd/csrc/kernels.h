@@ -162,7 +162,7 @@ int grp_rows_per_gateup_unit();
 bool gateup_grp_supported(int H, int I, int Is, int dtype, long x_bytes);
 hipError_t prepare_grouped_kernels();
 hipError_t launch_gateup_grp(const GateUpParams &p, int dtype, int grid, hipStream_t s);
-// its down product over the same tiles (bf16 / FP8 down weights), rows of y per unit
+// its down product over the same tiles (bf16 / FP8 / MXFP4 down weights), rows of y per unit
 bool down_grp_supported(int H, int I, int Is, int dtype, size_t h_bytes);
 int grp_rows_per_down_unit();
 hipError_t launch_down_grp(const DownParams &p, int dtype, int grid, hipStream_t s);

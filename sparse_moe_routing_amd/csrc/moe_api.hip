@@ -121,7 +121,7 @@ struct Plan {
     bool gemv = false;           // split, bf16 activations: gateup_gemv in place of gateup
     bool down_rows = false;      // split, bf16 activations: down_rows in place of down
     bool grp = false;            // wide, bf16 / FP8 / MXFP4: gateup_grp for the gate/up kernel
-    bool down_grp = false;       // with grp, bf16 / FP8: down_grp over the same tiles
+    bool down_grp = false;       // with grp: down_grp over the same tiles
     int NG2 = 0, max_groups2 = 0, grp_grid = 0, down_grp_grid = 0;
     int Imax = 0, gu_grid = 1, down_grid = 1, gu_S = 1;
     size_t gu_lds = 0, down_lds = 0;

@@ -584,7 +584,7 @@ def test_mxfp4_batch_invariance_bitwise():
         assert m.plan(T)[-2:] == ["gateup", "down_rows"], (T, m.plan(T))
     for T in (200, 1600):
         assert m.plan(T)[-3:] == ["gateup_wide", "down_wide", "combine"], (T, m.plan(T))
-    assert m.plan(3616)[-3:] == ["gateup_grp", "down_wide", "combine"], m.plan(3616)
+    assert m.plan(3616)[-3:] == ["gateup_grp", "down_grp", "combine"], m.plan(3616)
     assert torch.equal(y32[:4], y4)
     assert torch.equal(y1600[:32], y200[:32]) and torch.equal(y1600[1568:], y200[:32])
     assert torch.equal(y3616[:32], y200[:32]) and torch.equal(y3616[3584:], y200[:32])
