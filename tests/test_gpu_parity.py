@@ -899,11 +899,13 @@ def test_out_of_range_ids_add_nothing(orc, name, Ts):
         assert_close(y.cpu().numpy(), y_o, f"{name} T={T} out-of-range ids")
 
 
-@pytest.mark.parametrize("dtype,H", [("bf16", 384), ("f32", 384), ("f32", 448)])
+@pytest.mark.parametrize("dtype,H", [("bf16", 384), ("f32", 384), ("f32", 448), ("bf16", 512), ("bf16", 4096)])
 def test_large_t_router_forms(orc, dtype, H):
-    """T > 256 routes through the token-tile-blocked router: the LDS-staged form for an even
-    number of k steps per quarter (fp32 H = 384) and the form that reads operands straight from
-    global memory for an odd number (bf16 H = 384: 3 steps; fp32 H = 448: 7 steps). Logits,
+    """T > 256 routes through the large-T routers: bf16 with H a multiple of 256 the block form
+    (all row tiles of a quarter per block; H = 512: 17 router rows in two tiles spread over four
+    row groups, most of them empty; H = 4096: runs of two k steps), else the token-tile-blocked
+    form - LDS-staged for an even number of k steps per quarter (fp32 H = 384), operands straight
+    from global memory for an odd number (bf16 H = 384: 3 steps; fp32 H = 448: 7 steps). Logits,
     ids and y against the oracle on every token."""
     torch = _torch()
     E, I, T = 16, 128, 300
