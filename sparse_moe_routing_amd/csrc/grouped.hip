@@ -357,10 +357,12 @@ __device__ __forceinline__ unsigned char *dwslab() { return B ? g_dw1 : g_dw0; }
 template <int B>
 __device__ __forceinline__ unsigned char *dhslab() { return B ? g_dh1 : g_dh0; }
 
-// Byte position of 16-byte piece pc (0..3) of staged 64-byte row r: rows 4m .. 4m + 3 rotate their
-// pieces by m, so that the 16 rows one operand read touches fall on 16 distinct bank groups; the
-// rotation depends on r % 16 only.
-__device__ __forceinline__ int dpos(int r, int pc) { return r * kDRowB + ((pc ^ (r >> 2)) & 3) * 16; }
+// Byte position of 16-byte piece pc (0..3) of staged 64-byte row r: rows 2m, 2m + 1 (one 128-byte
+// line) rotate their pieces by m % 4, so that an operand read (16 rows x one piece per 16 lanes)
+// has no bank conflicts; the rotation depends on r % 8 only. (Rotating rows 4m .. 4m + 3 by m
+// instead costs 4 conflict cycles per read: a read probe gives 126 against 140 bytes per clock
+// and CU, and the conflict counter 4 per read instruction, against 0.)
+__device__ __forceinline__ int dpos(int r, int pc) { return r * kDRowB + ((pc ^ (r >> 1)) & 3) * 16; }
 constexpr int kDTileB = kTile * kDRowB;  // bytes of 16 staged rows
 
 template <int kFmt>
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
     for (int a = 0; a < kDHSegs; ++a) {
         const int R = 16 * (kDHSegs * wave + a) + (lane >> 2);
-        const int pc = ((lane & 3) ^ (R >> 2)) & 3;
+        const int pc = ((lane & 3) ^ (R >> 1)) & 3;
         const int pl = R >= kGTok, r = R - pl * kGTok;
         const int m = r < n ? r : 0;  // token rows past the tile repeat row 0 (columns dropped)
         const int slot = shared ? p.T * kTopK + start + m : p.perm[start + m];
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
         for (int a = 0; a < kDWSegs; ++a) {
             const int R = 16 * (kDWSegs * wave + a) + (lane >> 2);
-            woff[a] = (uint32_t)(R * wrow) + (((lane & 3) ^ (R >> 2)) & 3) * 16;
+            woff[a] = (uint32_t)(R * wrow) + (((lane & 3) ^ (R >> 1)) & 3) * 16;
         }
     }
     auto issue = [&](unsigned char *wbuf, unsigned char *hbuf, int st) __attribute__((always_inline)) {
