@@ -41,6 +41,7 @@ struct moe_ctx {
     int s;         // intermediate slice width of the expert kernel
     int gemv_max_tokens;  // decode rounds up to this T run the vector-ALU expert kernels
     int grp_min_tokens;   // rounds from this T run the expert-stationary gate/up (0: never)
+    int down_grp_min_tokens;  // ... and, from this T (and with that gate/up), its down (0: never)
     void *scratch; // device address of the static scratch array on this context's device
 };
 
@@ -79,6 +80,13 @@ constexpr int kBigMinTokens = 1536;     // bf16 from here: gateup_big in place o
 // against gateup_big: bf16 T = 3072 296 vs 286 us, 4096 299 vs 332, 6144 327 vs 433, 8192 349 vs
 // 538; FP8 3072 293 vs 274, 4096 303 vs 330, 8192 399 vs 592
 constexpr int kGrpMinTokens = 3584;
+// its down product (down_grp) from these T, with that gate/up (below them the gate/up's tiles
+// are followed by down_big, or by down_wide for MXFP4, on the 64-token groups); measured on one
+// box, step us with down_grp against without: bf16 T = 4097 754 vs 704, 6144 920 vs 905, 7168
+// 984 vs 991, 8192 1053 vs 1078; FP8 6144 927 vs 889, 7168 985 vs 972, 8192 1034 vs 1051;
+// MXFP4 (against down_wide) 4097 803 vs 787, 5120 904 vs 917, 8192 1083 vs 1241
+constexpr int kDownGrpMinTokens = 7680;
+constexpr int kDownGrpMinTokensMx = 4608;
 
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -265,7 +273,8 @@ Plan make_plan(const moe_ctx *c, int T) {
             p.grp_grid = (int)((units + 7) / 8 * 8);
             p.big = false;
             const size_t h_bytes = (size_t)2 * (T * 8 + (Is > 0 ? T : 0)) * Imax * 2;
-            p.down_grp = down_grp_supported(H, I, Is, expert_kdt(c), h_bytes);
+            p.down_grp = c->down_grp_min_tokens > 0 && T >= c->down_grp_min_tokens &&
+                         down_grp_supported(H, I, Is, expert_kdt(c), h_bytes);
             const long d_units = (long)p.max_groups2 * (H / grp_rows_per_down_unit());
             p.down_grp_grid = (int)((d_units + 7) / 8 * 8);
         }
@@ -828,6 +837,16 @@ int moe_create(const moe_config *cfg, const moe_weights *weights, moe_ctx **out)
             return MOE_ERR_INVALID_ARG;
         }
         c->grp_min_tokens = (int)v;
+    }
+    c->down_grp_min_tokens = cfg->dtype == MOE_MXFP4 ? kDownGrpMinTokensMx : kDownGrpMinTokens;
+    if (const char *env = getenv("MOE_DOWN_GRP_MIN_TOKENS")) {  // 0: never
+        char *end = nullptr;
+        const long v = strtol(env, &end, 10);
+        if (end == env || *end != '\0' || v < 0 || (v > 0 && v <= kSplitMaxTokens) || v > (1L << 30)) {
+            delete c;
+            return MOE_ERR_INVALID_ARG;
+        }
+        c->down_grp_min_tokens = (int)v;
     }
     const int Is = cfg->shared_inter;
     c->s = (cfg->inter % 64 == 0 && Is % 64 == 0) ? 64 : (cfg->inter % 32 == 0 && Is % 32 == 0) ? 32 : 16;

@@ -1,7 +1,7 @@
 """Token-count sweep of the MoE layer on one MI355X.
 
     python sweep.py [--tokens 1-64,192,768,4097] [--steps 200] [--warmup 20] [--skewed]
-                    [--dtype bf16|fp8|mxfp4] [--paths default,gemv,mfma,grp,nogrp]
+                    [--dtype bf16|fp8|mxfp4] [--paths default,gemv,mfma,grp,nogrp,nodgrp]
 
 For every T, one step is one moe_forward over T synthetic tokens with the decode shapes (H 2048,
 256 experts, top-8, expert and shared intermediate 512; bf16, FP8 or MXFP4 expert weights), timed as in bench.py: cold weights
@@ -56,7 +56,8 @@ def main():
                     help="comma list of expert paths to time per T: default (the library's "
                          "plan), gemv (vector-ALU decode gate/up), mfma (matrix-core decode "
                          "gate/up), grp (the expert-stationary gate/up from T = 65), nogrp "
-                         "(never the expert-stationary gate/up)")
+                         "(never the expert-stationary kernels), nodgrp (the expert-stationary "
+                         "gate/up but never its down product)")
     args = ap.parse_args()
     import torch
     from sparse_moe_routing_amd import binding, inputs
@@ -76,14 +77,16 @@ def main():
             for _ in range(args.pool)]
     stream = torch.cuda.current_stream()
     # contexts over the same weight sets per path: the plan boundaries are read from
-    # MOE_GEMV_MAX_TOKENS (vector-ALU gate/up up to that T) and MOE_GRP_MIN_TOKENS (the
-    # expert-stationary gate/up from that T) when a context is created
+    # MOE_GEMV_MAX_TOKENS (vector-ALU gate/up up to that T), MOE_GRP_MIN_TOKENS (the
+    # expert-stationary gate/up from that T) and MOE_DOWN_GRP_MIN_TOKENS (its down product from
+    # that T) when a context is created
     knobs = {"default": {}, "gemv": {"MOE_GEMV_MAX_TOKENS": "64"},
              "mfma": {"MOE_GEMV_MAX_TOKENS": "0"}, "grp": {"MOE_GRP_MIN_TOKENS": "65"},
-             "nogrp": {"MOE_GRP_MIN_TOKENS": "0"}}
+             "nogrp": {"MOE_GRP_MIN_TOKENS": "0"}, "nodgrp": {"MOE_DOWN_GRP_MIN_TOKENS": "0"}}
     path_sets = {}
     for name in args.paths.split(","):
-        saved = {k: os.environ.pop(k, None) for k in ("MOE_GEMV_MAX_TOKENS", "MOE_GRP_MIN_TOKENS")}
+        saved = {k: os.environ.pop(k, None)
+                 for k in ("MOE_GEMV_MAX_TOKENS", "MOE_GRP_MIN_TOKENS", "MOE_DOWN_GRP_MIN_TOKENS")}
         os.environ.update(knobs[name])
         path_sets[name] = [(binding.MoeLayer(H, w.num_experts, w.inter, w.shared_inter, w.tokens,
                                              w.dtype, t), t) for _, t in sets]

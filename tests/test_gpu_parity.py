@@ -537,9 +537,12 @@ def test_batch_invariance_bitwise():
     assert_close(y200[:32].cpu().numpy(), y32.cpu().numpy(), "regimes")
     # T >= 1536: the large-T gate/up and down kernels, the same bits as the 64-token groups
     y4097 = m.forward(torch.cat([x] * 129)[:4097].contiguous())
+    y7712 = m.forward(torch.cat([x] * 241).contiguous())
     torch.cuda.synchronize()
-    assert m.plan(4097)[4:6] == ["gateup_grp", "down_grp"]
+    assert m.plan(4097)[4:6] == ["gateup_grp", "down_big"]
+    assert m.plan(7712)[4:6] == ["gateup_grp", "down_grp"]
     assert torch.equal(y4097[:32], y384[:32]) and torch.equal(y4097[4064:4096], y384[:32])
+    assert torch.equal(y7712[:32], y384[:32]) and torch.equal(y7712[7680:], y384[:32])
 
 
 def test_fp8_batch_invariance_bitwise():
@@ -562,9 +565,12 @@ def test_fp8_batch_invariance_bitwise():
     assert torch.equal(y300[:32], y200[:32]) and torch.equal(y300[288:300], y200[:12])
     assert torch.equal(y1600[:32], y200[:32]) and torch.equal(y1600[1568:], y200[:32])
     y3616 = m.forward(torch.cat([x] * 113).contiguous())  # the expert-stationary gate/up
+    y7712 = m.forward(torch.cat([x] * 241).contiguous())  # ... and its down product
     torch.cuda.synchronize()
-    assert m.plan(3616)[-3:] == ["gateup_grp", "down_grp", "combine"]
+    assert m.plan(3616)[-3:] == ["gateup_grp", "down_big", "combine"]
+    assert m.plan(7712)[-3:] == ["gateup_grp", "down_grp", "combine"]
     assert torch.equal(y3616[:32], y200[:32]) and torch.equal(y3616[3584:], y200[:32])
+    assert torch.equal(y7712[:32], y200[:32]) and torch.equal(y7712[7680:], y200[:32])
     assert_close(y200[:32].cpu().numpy(), y32.cpu().numpy(), "fp8 regimes")
 
 
@@ -579,15 +585,18 @@ def test_mxfp4_batch_invariance_bitwise():
     y200 = m.forward(torch.cat([x] * 7)[:200].contiguous())
     y1600 = m.forward(torch.cat([x] * 50).contiguous())
     y3616 = m.forward(torch.cat([x] * 113).contiguous())
+    y4640 = m.forward(torch.cat([x] * 145).contiguous())
     torch.cuda.synchronize()
     for T in (4, 32):
         assert m.plan(T)[-2:] == ["gateup", "down_rows"], (T, m.plan(T))
     for T in (200, 1600):
         assert m.plan(T)[-3:] == ["gateup_wide", "down_wide", "combine"], (T, m.plan(T))
-    assert m.plan(3616)[-3:] == ["gateup_grp", "down_grp", "combine"], m.plan(3616)
+    assert m.plan(3616)[-3:] == ["gateup_grp", "down_wide", "combine"], m.plan(3616)
+    assert m.plan(4640)[-3:] == ["gateup_grp", "down_grp", "combine"], m.plan(4640)
     assert torch.equal(y32[:4], y4)
     assert torch.equal(y1600[:32], y200[:32]) and torch.equal(y1600[1568:], y200[:32])
     assert torch.equal(y3616[:32], y200[:32]) and torch.equal(y3616[3584:], y200[:32])
+    assert torch.equal(y4640[:32], y200[:32]) and torch.equal(y4640[4608:], y200[:32])
     assert_close(y200[:32].cpu().numpy(), y32.cpu().numpy(), "mxfp4 regimes")
 
 
@@ -602,7 +611,7 @@ GRP_SHAPES = [  # (format, H, E, I, Is, T): T >= 1536 runs the expert-stationary
 @pytest.mark.parametrize("shape", GRP_SHAPES, ids=lambda s: f"{s[0]}-H{s[1]}-E{s[2]}-I{s[3]}-Is{s[4]}-T{s[5]}")
 def test_grouped_gateup_shapes(orc, shape):
     """The expert-stationary gate/up and down kernels (tiles of up to 320 tokens of one expert;
-    planned from MOE_GRP_MIN_TOKENS tokens, 1536 here; the down kernel for bf16 and FP8 weights)
+    planned from MOE_GRP_MIN_TOKENS and MOE_DOWN_GRP_MIN_TOKENS tokens, 1536 here)
     give y bit for bit equal to the 64-token-group kernels of a context that never plans them
     (MOE_GRP_MIN_TOKENS=0), and match the oracle on sampled tokens, among them the tokens of the
     most loaded expert's last tile."""
@@ -614,18 +623,20 @@ def test_grouped_gateup_shapes(orc, shape):
     else:
         layer = quantized_small_layer(fmt, H, E, I, Is, T, seed=1536 + H + E + I + Is)
     t = binding.device_weights(layer)
-    saved = os.environ.get("MOE_GRP_MIN_TOKENS")
+    knobs = ("MOE_GRP_MIN_TOKENS", "MOE_DOWN_GRP_MIN_TOKENS")
+    saved = {k: os.environ.get(k) for k in knobs}
     try:
-        os.environ["MOE_GRP_MIN_TOKENS"] = "1536"
+        os.environ["MOE_GRP_MIN_TOKENS"] = os.environ["MOE_DOWN_GRP_MIN_TOKENS"] = "1536"
         m = binding.MoeLayer(H, E, I, Is, T, fmt, t)
         os.environ["MOE_GRP_MIN_TOKENS"] = "0"
         m0 = binding.MoeLayer(H, E, I, Is, T, fmt, t)
     finally:
-        if saved is None:
-            os.environ.pop("MOE_GRP_MIN_TOKENS")
-        else:
-            os.environ["MOE_GRP_MIN_TOKENS"] = saved
-    assert "gateup_grp" in m.plan(T), m.plan(T)
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert "gateup_grp" in m.plan(T) and "down_grp" in m.plan(T), m.plan(T)
     assert "gateup_grp" not in m0.plan(T), m0.plan(T)
     z_o = orc.logits(layer["x"], layer["router_w"], None)
     ids_o, w_o, g_o = orc.select(z_o, E, Is > 0)
@@ -974,8 +985,10 @@ def test_call_errors_and_empty():
     assert m.plan(257) == m.plan(1535) == chained + wide
     big = ["gateup_big", "down_big", "combine"]  # bf16 from 1536 tokens
     assert m.plan(1536) == m.plan(3583) == chained + big
-    grp = ["gateup_grp", "down_grp", "combine"]  # from 3584 tokens
-    assert m.plan(3584) == m.plan(8192) == chained + grp
+    grp_db = ["gateup_grp", "down_big", "combine"]  # from 3584 tokens
+    assert m.plan(3584) == m.plan(7679) == chained + grp_db
+    grp = ["gateup_grp", "down_grp", "combine"]  # from 7680 tokens
+    assert m.plan(7680) == m.plan(8192) == chained + grp
     assert m.plan(200, routing_given=True) == ["select_bucket"] + wide_db
     assert m.plan(300, routing_given=True) == ["select_hist", "bucket_scan", "bucket_scatter"] + wide
     assert tiny.plan(200) == ["router", "select_bucket", "expert", "combine"]
