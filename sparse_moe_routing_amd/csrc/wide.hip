@@ -32,8 +32,11 @@ constexpr int kWThreads = kWWaves * kWave;
 constexpr int kDownTiles = 2;                 // 16-row tiles of the down weight per wave
 constexpr int kWPieces = 16;                  // 16-byte pieces per row per chunk (256 bytes)
 constexpr int kWStage = kTile * kWPieces * 16;  // one wave's 16 x 256-byte weight chunk
-constexpr int kXRow = kWPieces * 16 + 16;     // LDS row of a staged token chunk (+16 B: no bank
-                                              // conflicts across the 16 rows of an operand read)
+// LDS row of a staged token chunk: 256 bytes plus 16. On gfx950 an operand read of 16 such rows
+// still costs 4 bank-conflict cycles (conflict counter and a read probe); a conflict-free
+// rotation of 256-byte rows measured no faster in these kernels and needs registers the wide
+// gate/up kernel does not have at 4 waves per SIMD.
+constexpr int kXRow = kWPieces * 16 + 16;
 
 __device__ __forceinline__ uint4 lds_read16(const unsigned char *p) {
     return *reinterpret_cast<const uint4 *>(p);
