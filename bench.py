@@ -13,6 +13,9 @@ dominant kernel's roofline (algorithmic bytes per launch over its event-timed av
 and the oracle's CPU throughput on a bounded sample of the same workload (all threads and one).
 The metric is quoted at T=4, 32 and 192, so the same line carries `sub_results` for the T=32
 decode round and the skewed T=192 verify round, each timed the same way after the main one.
+Next to the 8 TB/s specification each result reports `read_ceiling_gbs`: this GPU's measured rate
+for reading the step's byte count once, cold (the calibration kernel of libmoe_probe.so, built
+next to libmoe.so), and the step's HBM rate as a fraction of it.
 """
 from __future__ import annotations
 
@@ -237,6 +240,45 @@ def cpu_baseline(w, m_t, seconds):
                          "sample": f"{r_one} batches of {T_one} tokens, {el_one:.1f} s"}}
 
 
+def read_ceiling(torch, nbytes, steps, stream):
+    """This GPU's streaming-read rate for the step's byte count (GB/s), or None without the
+    calibration library: libmoe_probe.so's kernel reads `nbytes` once per launch (grid-stride,
+    16-byte non-temporal loads, one 512-thread block per compute unit), cycling over six such
+    regions so that every read is cold as the weight sets are, `steps` launches back to back
+    after five warm-up ones, synchronized on both sides - the same clock as the step's value."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_moe_routing_amd", "libmoe_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.moe_probe_read.restype = ctypes.c_int
+    n = int(nbytes) // 256 * 256
+    regions = 6
+    buf = torch.ones(regions * n // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    blocks = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    s = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch(i):
+        rc = lib.moe_probe_read(ctypes.c_void_p(buf.data_ptr() + (i % regions) * n), n, blocks,
+                                ctypes.c_void_p(sink.data_ptr()), s)
+        if rc:
+            raise RuntimeError(f"moe_probe_read failed ({rc})")
+
+    for i in range(5):
+        launch(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        launch(5 + i)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    del buf
+    return n / dt / 1e9
+
+
 def measure(w, args, torch, log_prefix):
     """Warm-up, then K timed steps of plain moe_forward calls (wall clock, synchronized on both
     sides), then the same K steps once more with per-kernel events. Returns (result dict, the
@@ -314,12 +356,16 @@ def measure(w, args, torch, log_prefix):
     achieved = stage[dom]["gbs"]
     step_b = float(np.mean([step_bytes(w, U[c]) for c in used]))
     gpu_step_us = float(np.median(step_ms)) * 1e3
+    ceiling = read_ceiling(torch, step_b, args.steps, stream)
     log(f"[{log_prefix}] per-kernel mean us: " + ", ".join(
         f"{k}={np.mean(v) * 1e3:.2f}" for k, v in per_kernel.items()))
     log(f"[{log_prefix}] wall {ms_per_step * 1e3:.2f} us/step (host enqueue "
         f"{(t_enq - t0) * 1e6 / args.steps:.1f} us/step), event-timed step median "
         f"{gpu_step_us:.2f} us, mean U {mean_U:.1f}, step bytes {step_b / 1e6:.1f} MB -> "
         f"{step_b / (ms_per_step * 1e-3) / 1e9:.0f} GB/s wall")
+    if ceiling is not None:
+        log(f"[{log_prefix}] streaming-read ceiling for {step_b / 1e6:.1f} MB cold: {ceiling:.0f} GB/s "
+            f"-> the step at {step_b / (ms_per_step * 1e-3) / 1e9 / ceiling * 100:.1f} % of it")
     res = {
         "value": value, "unit": "tokens/s", "ms_per_step": ms_per_step, "dtype": w.dtype,
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": w.num_experts,
@@ -332,6 +378,11 @@ def measure(w, args, torch, log_prefix):
         "mean_distinct_experts": mean_U,
         "host_enqueue_us_per_step": (t_enq - t0) * 1e6 / args.steps,
         "event_step_us_median": gpu_step_us,
+        "event_step_us_p10_p90": [float(np.percentile(step_ms, 10)) * 1e3,
+                                  float(np.percentile(step_ms, 90)) * 1e3],
+        "read_ceiling_gbs": ceiling,
+        "hbm_frac_of_read_ceiling": (None if ceiling is None else
+                                     step_b / (ms_per_step * 1e-3) / 1e9 / ceiling),
         "per_kernel_us": {k: float(np.mean(v)) * 1e3 for k, v in per_kernel.items()},
         "expert_stage_gbs": {k: v["gbs"] for k, v in stage.items()},
         "roofline": {"scope": "kernel", "kernel": dom, "bound": "hbm", "achieved": achieved,
@@ -386,9 +437,10 @@ def main():
         "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
     }
-    for k in ("config", "hbm_gbs_step", "hbm_frac_step", "step_bytes", "mean_distinct_experts",
-              "host_enqueue_us_per_step", "event_step_us_median", "per_kernel_us",
-              "expert_stage_gbs", "roofline"):
+    for k in ("config", "hbm_gbs_step", "hbm_frac_step", "read_ceiling_gbs",
+              "hbm_frac_of_read_ceiling", "step_bytes", "mean_distinct_experts",
+              "host_enqueue_us_per_step", "event_step_us_median", "event_step_us_p10_p90",
+              "per_kernel_us", "expert_stage_gbs", "roofline"):
         result[k] = main_res[k]
     if subs:
         result["sub_results"] = subs

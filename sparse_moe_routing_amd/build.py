@@ -4,6 +4,8 @@
 
 Every .hip file under csrc/ is compiled to an object in _build/ (in parallel), then linked into
 sparse_moe_routing_amd/libmoe.so. Packed fp32 instructions are disabled for all device code.
+The benchmark's streaming-read calibration kernel (probe/read_probe.hip) is built next to it as
+libmoe_probe.so, a library of its own: libmoe.so does not contain or call it.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PROBE_SRC = os.path.join(PKG, "probe", "read_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
 ARCH = "gfx950"
 
 
@@ -64,6 +68,12 @@ def build(verbose: bool = False) -> str:
     if r.returncode:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + f".tmp{os.getpid()}"
+    cmd = [cc, *compile_flags(), "-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n" + r.stdout + r.stderr)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -910,6 +910,43 @@ def test_out_of_range_ids_add_nothing(orc, name, Ts):
         assert_close(y.cpu().numpy(), y_o, f"{name} T={T} out-of-range ids")
 
 
+@pytest.mark.parametrize("name,G", [("decode_b8_t32", 8), ("verify_skewed_t192", 4),
+                                    ("decode_b8_t32_fp8", 8)])
+def test_expert_shards_sum_to_full_layer(orc, name, G):
+    """Expert parallelism, its one-GPU part: G contexts each hold E/G experts (contiguous ids;
+    the first one also the shared expert) at the layer's real shapes, each computes its partial y
+    from the global routing (its own pairs with local ids, every other pair's id out of range), and
+    the partial ys summed over the shards equal the oracle's y within the tolerance - the sum an
+    all-reduce of y would form."""
+    torch = _torch()
+    layer, m, t = get_layer(name)
+    w = layer["workload"]
+    E, H, I, Is, T = w.num_experts, w.hidden, w.inter, w.shared_inter, w.tokens
+    z_o, ids_o, w_o, g_o = orc.route(layer)
+    y_o = orc.forward(layer, ids_o, w_o, g_o)
+    n = E // G
+    x = t["x"].contiguous()
+    total = torch.zeros((T, H), dtype=torch.float64, device="cuda")
+    for s in range(G):
+        lo = s * n
+        rows = t["router_w"][lo:lo + n]
+        if s == 0:
+            rows = torch.cat([rows, t["router_w"][E:E + 1]])
+        wts = {"router_w": rows.contiguous(), "router_bias": None}
+        for k in ("gate_up", "down", "gate_up_scale", "down_scale"):
+            wts[k] = None if t.get(k) is None else t[k][lo:lo + n].contiguous()
+        for k in ("shared_gate_up", "shared_down", "shared_gate_up_scale", "shared_down_scale"):
+            wts[k] = t.get(k) if s == 0 else None
+        shard = binding.MoeLayer(H, n, I, Is if s == 0 else 0, T, w.dtype, wts)
+        local = (ids_o >= lo) & (ids_o < lo + n)
+        ids_s = np.where(local, ids_o - lo, -1).astype(np.int32)
+        y_s = shard.forward(x, routing=routing_device(ids_s, w_o, g_o if s == 0 else None))
+        torch.cuda.synchronize()
+        total += y_s.double()
+        shard.close()
+    assert_close(total.cpu().numpy(), y_o, f"{name}: sum over {G} expert shards")
+
+
 @pytest.mark.parametrize("dtype,H", [("bf16", 384), ("f32", 384), ("f32", 448), ("bf16", 512), ("bf16", 4096)])
 def test_large_t_router_forms(orc, dtype, H):
     """T > 256 routes through the large-T routers: from T = 3072 bf16 with H a multiple of 256 the

@@ -44,6 +44,19 @@ def test_no_oracle_code_in_the_library():
     assert b"oracle_" not in data
 
 
+def test_read_probe_is_a_library_of_its_own(lib):
+    """The benchmark's streaming-read calibration kernel is built as libmoe_probe.so, exports
+    moe_probe_read and rejects a misaligned size on the host; libmoe.so carries no such symbol."""
+    path = os.path.join(ROOT, "sparse_moe_routing_amd", "libmoe_probe.so")
+    probe = ctypes.CDLL(path)
+    probe.moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    probe.moe_probe_read.restype = ctypes.c_int
+    assert probe.moe_probe_read(ctypes.c_void_p(16), 17, 1, ctypes.c_void_p(16), None) != 0
+    assert probe.moe_probe_read(None, 16, 1, ctypes.c_void_p(16), None) != 0
+    assert not hasattr(lib, "moe_probe_read")
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4):
         assert lib.moe_status_str(st)
