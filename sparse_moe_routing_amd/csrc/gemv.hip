@@ -17,8 +17,8 @@
 //   kNB at a time with the weights kept in registers. The grid's waves split the group list:
 //   with fewer groups than waves each group's units are cut into contiguous runs, one per wave
 //   (a wave loads its group's activations once); otherwise each wave takes whole groups.
-// down_rows_kernel - a block owns 4 consecutive rows of y for every token: its waves take the
-//   groups in turn, read those 4 rows of each group's down weight (4 x I bf16; the next group's
+// down_rows_kernel - a block owns 8 consecutive rows of y for every token: its waves take the
+//   groups in turn, read those 8 rows of each group's down weight (8 x I weights; the next group's
 //   rows and h are requested before the current one is computed), multiply them by the group's
 //   h and keep every (slot, row) product in LDS; the block then sums each token's eight ranks in
 //   rank order, weighted, plus its gated shared slot into y. Every output element has one writer

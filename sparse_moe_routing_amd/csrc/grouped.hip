@@ -1,4 +1,4 @@
-// grouped.hip - expert-stationary gate/up for prefill-sized rounds.
+// grouped.hip - expert-stationary gate/up and down for prefill-sized rounds.
 //
 // At T = 8192 tokens each of the 256 experts draws 256 +- 16 (token, rank) pairs. The
 // 64-token-group kernels read an expert's weight slice once per group, about four times per call,
@@ -14,7 +14,8 @@
 // Operands are staged in LDS in 64-element K slabs: one slab is 256 weight rows and 320 token
 // rows of 128 bytes each (bf16), double-buffered. x rows and bf16 weights are loaded straight into
 // LDS (buffer loads with the LDS flag: no registers held while in flight), whole 128-byte lines,
-// 8 rows per load instruction; FP8 codes come through registers to be widened. The next slab's
+// 8 rows per load instruction; FP8 and MXFP4 codes come through registers to be widened (MXFP4
+// with its block scale). The next slab's
 // loads are in flight during the current slab's matrix instructions; one block barrier per slab.
 // Eight waves, two per SIMD: wave w multiplies weight rows 128 (w % 2) .. + 128 (four 16-row gate
 // tiles and the four matching up tiles, so h = silu(gate) * up is formed in its registers) by

@@ -1,22 +1,33 @@
 // moe_api.hip - the C ABI of libmoe (include/moe.h): validation, workspace layout, kernel plans.
 //
-// Call sequence of moe_forward (all on the caller's stream, no host synchronisation):
-//   router        T > 64: partial logits (matrix cores)
-//   route_fused   T <= 16 from x: router partials; the last block selects and buckets
-//   route_tiles   16 < T <= 64 from x: as route_fused per 16-token tile; the last tile buckets
-//   route_small   T <= 64, routing given: the whole bucketing pass, one block
-//   select_hist   T > 64: per 16-token chunk, fold + top-8 + softmax + gate
-//                 + expert histogram
-//   bucket_scan   per-expert chunk bases, counts, offsets, expert-group table
+// Call sequence of moe_forward (all on the caller's stream, no host synchronisation); which
+// kernels a T gets is the plan (make_plan), with the boundaries measured on MI355X:
+//   route_fused    T <= 16 from x: router partials; the last block selects and buckets
+//   route_tiles    16 < T <= 64 from x: as route_fused per 16-token tile; the last tile buckets
+//   route_small    T <= 64, routing given: the whole bucketing pass, one block
+//   router         T > 64: partial logits (matrix cores; router.hip picks the per-wave, the
+//                  LDS-staged or, from 3072 bf16 tokens, the block form)
+//   select_bucket  64 < T <= 256: per 16-token chunk fold + top-8 + softmax + gate; the last
+//                  chunk block buckets all pairs
+//   select_hist    T > 256: the same per chunk, plus the chunk's expert histogram
+//   bucket_scan    per-expert chunk bases, counts, offsets, the 64-token group table (and the
+//                  320-token tile table for the expert-stationary kernels)
 //   bucket_scatter the stable scatter of pair indices
-//   gateup        T <= 64: gate/up + SwiGLU into h per (8-token expert group, 32 inter. rows)
-//   down          T <= 64: down product per (expert group, 64 rows of y), weighted per slot;
-//                 the last unit of each 64-row block sums the slots into y
-//   gateup_wide   T > 64: as gateup for 64-token expert groups (wide.hip)
-//   down_wide     T > 64: as down for 64-token groups, slot outputs only
-//   combine       sum of the weighted slot outputs (or partials) into y
-//   expert        shapes outside the chunked kernels: fused gate/up + SwiGLU + down per (group,
-//                 intermediate slice chunk), then combine
+//   gateup         T <= 64: gate/up + SwiGLU into h per (<= 8-token expert group, 32 inter.
+//                  rows), matrix cores (gateup_gemv: the vector-ALU form, opt-in)
+//   down_rows      T <= 64: vector-ALU down product per 8 rows of y over every group, the
+//                  eight ranks and the gated shared slot summed into y in the block
+//   down           T <= 64 shapes down_rows does not take: matrix-core down per (group, 64 rows
+//                  of y); the last unit of each 64-row block sums the slots into y
+//   gateup_wide    T > 64: as gateup for 64-token expert groups (wide.hip)
+//   gateup_big     bf16 / FP8, 1536 <= T < 3584: 64-token groups, whole-line weight staging
+//   gateup_grp     T >= 3584: expert-stationary, tiles of <= 320 tokens (grouped.hip)
+//   down_wide / down_big / down_grp  T > 64: the down product into per-slot rows, on the
+//                  64-token groups (down_big: bf16 / FP8 at T <= 256 and 1536 <= T < 7680) or
+//                  on the tiles (down_grp: bf16 / FP8 from 7680, MXFP4 from 4608 tokens)
+//   combine        T > 64: the weighted slot outputs of each token summed in rank order into y
+//   expert         shapes outside the chunked kernels: fused gate/up + SwiGLU + down per (group,
+//                  intermediate slice chunk), then combine
 #include <stdlib.h>
 #include <string.h>
 

@@ -1,4 +1,6 @@
-// router.hip - the standalone router kernels (large T).
+// router.hip - the standalone router kernels (T > 64): the per-wave form, its LDS-staged variant
+// (an even number of k steps per quarter) and, for long bf16 rounds, the block form. All of them
+// keep the summation order of router_core.h, so a token's logits do not depend on the kernel.
 #include "router_core.h"
 
 namespace moe {
