@@ -947,6 +947,71 @@ def test_expert_shards_sum_to_full_layer(orc, name, G):
     assert_close(total.cpu().numpy(), y_o, f"{name}: sum over {G} expert shards")
 
 
+def random_configs(seed):
+    """Seeded layer shapes for every (weight format, plan regime) pair: decode (T <= 64), the
+    64-token-group kernels (65..400), the large-T pair (1536..1700) and the expert-stationary
+    kernels (3584..3700, their down product planned from 3584 here); fp32 layers in the first
+    two. Weights stay under ~40 M elements so that drawing them and the oracle stay quick."""
+    rng = np.random.default_rng(seed)
+    out = []
+    pairs = [(f, r) for f in ("bf16", "fp8", "mxfp4") for r in ("decode", "mid", "big", "grp")]
+    pairs += [("f32", "decode"), ("f32", "mid")]
+    for fmt, regime in pairs:
+        while True:
+            H = int(rng.choice([256, 512, 768, 1024, 2048]))
+            E = int(rng.choice([8, 16, 32, 64]))
+            I = int(rng.choice([256, 512] if fmt == "mxfp4" else [128, 256, 384, 512]))
+            Is = int(rng.choice([0, I, 512 if fmt == "mxfp4" else 256]))
+            if fmt in ("fp8", "mxfp4") and Is == 0:
+                Is = I
+            if E * 3 * I * H + 3 * Is * H <= 40_000_000:
+                break
+        lo, hi = {"decode": (1, 65), "mid": (65, 400), "big": (1536, 1700), "grp": (3584, 3700)}[regime]
+        out.append((fmt, H, E, I, Is, int(rng.integers(lo, hi)), regime))
+    return out
+
+
+@pytest.mark.parametrize("cfg", random_configs(2026),
+                         ids=lambda c: f"{c[0]}-H{c[1]}-E{c[2]}-I{c[3]}-Is{c[4]}-T{c[5]}")
+def test_random_shapes_against_oracle(orc, cfg):
+    """Seeded random shapes, weight formats and token counts: logits on every token and y from
+    the oracle's routing (every token up to 300, else 256 random ones plus the last 32) against
+    the oracle, whatever kernels the plan picks for the shape."""
+    import os
+    torch = _torch()
+    fmt, H, E, I, Is, T, regime = cfg
+    seed = H + 7 * E + 11 * I + 13 * Is + T
+    if fmt in ("fp8", "mxfp4"):
+        layer = quantized_small_layer(fmt, H, E, I, Is, T, seed=seed)
+    else:
+        layer = small_layer(fmt, H, E, I, Is, T, seed=seed)
+    t = binding.device_weights(layer)
+    saved = os.environ.get("MOE_DOWN_GRP_MIN_TOKENS")
+    try:
+        os.environ["MOE_DOWN_GRP_MIN_TOKENS"] = "3584"
+        m = binding.MoeLayer(H, E, I, Is, T, fmt, t)
+    finally:
+        if saved is None:
+            os.environ.pop("MOE_DOWN_GRP_MIN_TOKENS", None)
+        else:
+            os.environ["MOE_DOWN_GRP_MIN_TOKENS"] = saved
+    plan = m.plan(T, routing_given=True)
+    if regime == "grp" and H % (512 if fmt == "mxfp4" else 256) == 0:
+        assert "gateup_grp" in plan, plan
+    z, _, _, _ = m.route(x=t["x"])
+    z_o = orc.logits(layer["x"], layer["router_w"], None)
+    ids_o, w_o, g_o = orc.select(z_o, E, Is > 0)
+    y = m.forward(t["x"], routing=routing_device(ids_o, w_o, g_o))
+    torch.cuda.synchronize()
+    assert_close(z.cpu().numpy(), z_o, f"{cfg} logits")
+    rng = np.random.default_rng(seed)
+    rows = np.arange(T) if T <= 300 else np.unique(np.concatenate(
+        [rng.choice(T, 256, replace=False), np.arange(T - 32, T)]))
+    y_o = orc.forward(layer, ids_o, w_o, g_o, tokens=rows.astype(np.int32))
+    assert_close(y.cpu().numpy()[rows], y_o, f"{cfg} plan {plan}")
+    m.close()
+
+
 @pytest.mark.parametrize("dtype,H", [("bf16", 384), ("f32", 384), ("f32", 448), ("bf16", 512), ("bf16", 4096)])
 def test_large_t_router_forms(orc, dtype, H):
     """T > 256 routes through the large-T routers: from T = 3072 bf16 with H a multiple of 256 the
