@@ -1012,6 +1012,47 @@ def test_random_shapes_against_oracle(orc, cfg):
     m.close()
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_every_token_on_the_same_experts(orc, fmt):
+    """The most skewed routing there is: every token picks the same eight experts (in a random
+    order per token, random weights), so eight groups or tiles carry all T tokens and the other
+    experts none - at T = 40 (8-token groups), 200 (64-token groups), 1600 (large-T pair) and 3700
+    (the expert-stationary kernels, their down product planned from 3584 here). y on sampled
+    tokens against the oracle."""
+    import os
+    torch = _torch()
+    H, E, I, Is, Tmax = 512, 32, 256, 256, 3700
+    layer = (small_layer("bf16", H, E, I, Is, Tmax, seed=88) if fmt == "bf16"
+             else quantized_small_layer(fmt, H, E, I, Is, Tmax, seed=88))
+    t = binding.device_weights(layer)
+    saved = os.environ.get("MOE_DOWN_GRP_MIN_TOKENS")
+    try:
+        os.environ["MOE_DOWN_GRP_MIN_TOKENS"] = "3584"
+        m = binding.MoeLayer(H, E, I, Is, Tmax, fmt, t)
+    finally:
+        if saved is None:
+            os.environ.pop("MOE_DOWN_GRP_MIN_TOKENS", None)
+        else:
+            os.environ["MOE_DOWN_GRP_MIN_TOKENS"] = saved
+    rng = np.random.default_rng(89)
+    hot = rng.permutation(E)[:8]
+    for T in (40, 200, 1600, 3700):
+        ids = np.stack([rng.permutation(hot) for _ in range(T)]).astype(np.int32)
+        w = rng.random((T, 8)).astype(np.float32)
+        w /= w.sum(1, keepdims=True)
+        g = rng.random(T).astype(np.float32)
+        lay = dict(layer)
+        lay["x"] = layer["x"][:T]
+        y = m.forward(t["x"][:T].contiguous(), routing=routing_device(ids, w, g))
+        torch.cuda.synchronize()
+        rows = np.arange(T) if T <= 200 else np.unique(np.concatenate(
+            [rng.choice(T, 200, replace=False), np.arange(T - 16, T)]))
+        y_o = orc.forward(lay, ids, w.astype(np.float64), g.astype(np.float64),
+                          tokens=rows.astype(np.int32))
+        assert_close(y.cpu().numpy()[rows], y_o, f"{fmt} T={T} plan {m.plan(T, routing_given=True)}")
+    m.close()
+
+
 @pytest.mark.parametrize("dtype,H", [("bf16", 384), ("f32", 384), ("f32", 448), ("bf16", 512), ("bf16", 4096)])
 def test_large_t_router_forms(orc, dtype, H):
     """T > 256 routes through the large-T routers: from T = 3072 bf16 with H a multiple of 256 the
