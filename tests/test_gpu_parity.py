@@ -1095,6 +1095,42 @@ def test_token_permutation_equivariance():
     assert torch.equal(yp, y[perm])
 
 
+def test_side_stream_matches_default_stream():
+    """Every kernel of a call runs on the caller's stream: the same calls on a second stream (same
+    priority), with the inputs written on that stream just before, give y bit for bit equal to the
+    default stream's, at a decode, a 64-token-group and a large-T round."""
+    torch = _torch()
+    layer, m, t = get_layer("decode_b8_t32")
+    base = t["x"]
+    for T in (32, 200, 4097):
+        x0 = torch.cat([base] * ((T + 31) // 32))[:T].contiguous()
+        y0 = m.forward(x0)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side):
+            x1 = torch.empty_like(x0)
+            x1.copy_(x0)  # enqueued on the side stream, right before the layer's kernels
+            y1 = m.forward(x1, stream=side)
+        side.synchronize()
+        assert torch.equal(y0, y1), T
+
+
+def test_largest_round_is_batch_invariant():
+    """A 16384-token round (twice the prefill chunk; a context sized for it) gives each token the
+    bits of the 8192-token round: the expert-stationary kernels at both sizes."""
+    torch = _torch()
+    layer, _, t = get_layer("prefill_t8192")
+    w = layer["workload"]
+    m = binding.MoeLayer(w.hidden, w.num_experts, w.inter, w.shared_inter, 16384, w.dtype, t)
+    x = t["x"].contiguous()
+    y8 = m.forward(x)
+    y16 = m.forward(torch.cat([x, x]).contiguous())
+    torch.cuda.synchronize()
+    assert m.plan(16384)[-3:] == ["gateup_grp", "down_grp", "combine"], m.plan(16384)
+    assert torch.equal(y16[:8192], y8) and torch.equal(y16[8192:], y8)
+    m.close()
+
+
 def test_call_errors_and_empty():
     torch = _torch()
     layer, m, t = get_layer("decode_b1_t4", max_tokens=8192)
