@@ -1115,6 +1115,41 @@ def test_side_stream_matches_default_stream():
         assert torch.equal(y0, y1), T
 
 
+@pytest.mark.parametrize("name", ["decode_b1_t4", "decode_b8_t32", "verify_skewed_t192"])
+def test_graph_capture_replays(name):
+    """A call captured in a HIP graph (it enqueues no memset and no allocation: the workspace's
+    state words are cleared by the calls themselves) replays to the eager result bit for bit, five
+    times with eager calls in between; the no-allocation entry point too, up to 64 tokens."""
+    torch = _torch()
+    layer, m, t = get_layer(name)
+    T = layer["x"].shape[0]
+    x = t["x"].contiguous()
+    ws = m.workspace(T)
+    y_e = m.forward(x, ws=ws)
+    torch.cuda.synchronize()
+    for mode in (("ws", "noalloc") if T <= 64 else ("ws",)):
+        y = torch.empty_like(y_e)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                if mode == "ws":
+                    m.forward(x, y=y, ws=ws)
+                else:
+                    m.forward_noalloc(x, y=y)
+        torch.cuda.synchronize()
+        for r in range(5):
+            y.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_e), (mode, r)
+            y2 = m.forward(x, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y2, y_e), (mode, r)
+        del g
+
+
 def test_largest_round_is_batch_invariant():
     """A 16384-token round (twice the prefill chunk; a context sized for it) gives each token the
     bits of the 8192-token round: the expert-stationary kernels at both sizes."""
