@@ -51,13 +51,28 @@ struct BucketParams {
     int32_t *counts;     // [E]
     int32_t *offsets;    // [E+1]
     int32_t *perm;       // [T*8]
-    int32_t *hist;       // [n_chunks][E] (multi-block path); becomes per-chunk bases
+    int32_t *hist;       // the chunks' expert histograms (multi-block path), then per-chunk
+                         // bases: [n_chunks][E], or [E][n_chunks] above kScanOneBlockChunks
+                         // chunks (hist_at)
     int4 *groups;        // [max_groups]: {expert (E = shared), start, n, 0}
     int32_t *num_groups; // [1]
     int NG2;             // > 0: a second table of groups of up to NG2 tokens (same order)
     int4 *groups2;       // [max_groups for NG2]
     int32_t *num_groups2;  // [1]
 };
+
+// Chunk histograms: the one-block scan (up to this many chunks) reads a chunk's row of E counts
+// with consecutive threads, so they are stored chunk-major; the multi-block scan gives each expert
+// a wave that reads the expert's counts over all chunks, so above it they are stored
+// expert-major (one contiguous run per expert instead of one cache line per chunk). Measured
+// (bucket_scan, us, one block against the multi-block form): 32 chunks (T = 512) 4.2 vs 4.3,
+// 48 chunks 4.9 vs 4.3, 64 chunks 4.9 vs 4.1, 257 chunks 15.1 vs 6.6; 512 chunks 13.9 (20.7 with
+// the chunk-major columns).
+constexpr int kScanOneBlockChunks = 32;
+__host__ __device__ inline size_t hist_at(const BucketParams &bp, int chunk, int e) {
+    return bp.n_chunks > kScanOneBlockChunks ? (size_t)e * bp.n_chunks + chunk
+                                             : (size_t)chunk * bp.E + e;
+}
 
 // Expert stage: gate/up + SwiGLU + down for (group, slice chunk) units.
 struct ExpertParams {

@@ -419,7 +419,7 @@ __global__ __launch_bounds__(1024) void select_hist_kernel(SelectParams sp, Buck
     if (!do_hist) return;
     __syncthreads();
     const int cnt = chunk_counts(s, nt * kTopK, bp.E);
-    if (tid < bp.E) bp.hist[(size_t)blockIdx.x * bp.E + tid] = cnt;
+    if (tid < bp.E) bp.hist[hist_at(bp, blockIdx.x, tid)] = cnt;
 }
 
 // 64 < T <= 256: per 16-token chunk (one wave per token) the selection (optional); the chunk's
@@ -524,6 +524,7 @@ __global__ __launch_bounds__(kScanWaves * kWave) void bucket_scan_kernel(BucketP
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int e = blockIdx.x * kScanWaves + wave;
     if (e < bp.E) {  // uniform over the wave
+        int32_t *col = bp.hist + (size_t)e * bp.n_chunks;  // the expert's counts, chunk order
         const int per = (bp.n_chunks + kWave - 1) / kWave;
         const int c0 = min(lane * per, bp.n_chunks), c1 = min(c0 + per, bp.n_chunks);
         constexpr int kB = 8;  // loads issued together (clamped past the end, dropped)
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(kScanWaves * kWave) void bucket_scan_kernel(BucketP
         for (int c = c0; c < c1; c += kB) {
             int v[kB];
 #pragma unroll
-            for (int j = 0; j < kB; ++j) v[j] = bp.hist[(size_t)min(c + j, c1 - 1) * bp.E + e];
+            for (int j = 0; j < kB; ++j) v[j] = col[min(c + j, c1 - 1)];
 #pragma unroll
             for (int j = 0; j < kB; ++j) sum += c + j < c1 ? v[j] : 0;
         }
@@ -540,11 +541,11 @@ __global__ __launch_bounds__(kScanWaves * kWave) void bucket_scan_kernel(BucketP
         for (int c = c0; c < c1; c += kB) {
             int v[kB];
 #pragma unroll
-            for (int j = 0; j < kB; ++j) v[j] = bp.hist[(size_t)min(c + j, c1 - 1) * bp.E + e];
+            for (int j = 0; j < kB; ++j) v[j] = col[min(c + j, c1 - 1)];
 #pragma unroll
             for (int j = 0; j < kB; ++j) {
                 if (c + j < c1) {
-                    bp.hist[(size_t)(c + j) * bp.E + e] = base;
+                    col[c + j] = base;
                     base += v[j];
                 }
             }
@@ -573,9 +574,8 @@ __global__ __launch_bounds__(512) void bucket_scatter_kernel(BucketParams bp) {
     __syncthreads();
     chunk_counts(s, nt * kTopK, bp.E);
     __syncthreads();
-    const int32_t *chunk_base = bp.hist + (size_t)blockIdx.x * bp.E;
     chunk_scatter(s, nt * kTopK, bp.E, t0 * kTopK, bp.perm,
-                  [&](int e) { return bp.offsets[e] + chunk_base[e]; });
+                  [&](int e) { return bp.offsets[e] + bp.hist[hist_at(bp, blockIdx.x, e)]; });
 }
 
 hipError_t launch_route_small(const SelectParams &sp, const BucketParams &bp, bool do_select,
@@ -625,10 +625,7 @@ hipError_t launch_select_bucket(const SelectParams &sp, const BucketParams &bp, 
 }
 
 hipError_t launch_bucket_scan(const BucketParams &bp, int *arrivals, hipStream_t s) {
-    // measured: one block at T = 768 (48 chunks) 4.9 us against 8.9 us; at T = 8192 (512 chunks)
-    // 26.0 us against 20.8 us
-    constexpr int kScanOneBlockChunks = 288;
-    if (bp.n_chunks <= kScanOneBlockChunks)
+    if (bp.n_chunks <= kScanOneBlockChunks)  // the boundary and its measurements: kernels.h
         launch_k(bucket_scan_one_kernel, 1, 1024, 0, s, bp);
     else
         launch_k(bucket_scan_kernel, (bp.E + kScanWaves - 1) / kScanWaves, kScanWaves * kWave, 0, s,
